@@ -1,0 +1,190 @@
+"""Benchmark: tiled, software-pipelined GEMM on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--variant k=v,...]
+
+A step is one C = A x B of the workload (default bf16 M = N = K = 4096,
+N(0,1) operands rounded to bf16, fp32 output) through the C ABI, with A, B
+and C already resident in HBM.  Prints ONE JSON line with the throughput, a
+roofline record for the kernel (achieved vs MI355X dense peak, from HIP
+events on the launch stream) and the CPU oracle's rate on a bounded sample of
+the same workload.
+
+Extra modes (not used by the default run):
+    --ladder   time every compiled variant of the workload's dtype (one JSON
+               line each, then the summary line)
+    --sweep    time the default plan on the bf16 shape sweep
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published dense peaks (TFLOP/s or TOP/s) and HBM bandwidth (GB/s)
+PEAK_TFLOPS = {"bf16": 2500.0, "i8": 5000.0, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+METRIC = "GEMM TFLOPS (TOPS int8) and % of MI355X MFMA peak, bf16 M=N=K=4096"
+
+
+def parse_variant(text, lib):
+    if not text:
+        return None
+    v = lib.Variant()
+    for kv in text.split(","):
+        k, val = kv.split("=")
+        setattr(v, k.strip(), int(val))
+    return v
+
+
+def algorithmic_bytes(w):
+    esz = {"f32": 4, "bf16": 2, "i8": 1}[w.dtype]
+    return (w.M * w.K + w.K * w.N) * esz + w.M * w.N * 4
+
+
+def time_plan(lib, torch, w, A, B, C, variant, steps, warmup):
+    """Per-launch kernel durations (ms) from HIP events on the launch stream,
+    plus the wall time of the whole timed region."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        lib.gemm(A, B, out=C, variant=variant)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        lib.gemm(A, B, out=C, variant=variant)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return per, wall
+
+
+def cpu_baseline(w, A_cpu, B_cpu, budget_s=12.0):
+    """The oracle (fp64 / int64 triple loop, OpenMP) on a row sample of the
+    same operands: rows are taken until about `budget_s` of CPU work."""
+    import numpy as np
+
+    import oracle
+    from tiled_software_pipelined_amd import inputs
+    Bo = inputs.as_oracle_array(B_cpu)
+    rows = 8
+    t = 0.0
+    done_rows = 0
+    total_t = 0.0
+    while True:
+        Ao = inputs.as_oracle_array(A_cpu[done_rows:done_rows + rows])
+        t0 = time.perf_counter()
+        oracle.gemm(Ao, Bo, w.dtype)
+        t = time.perf_counter() - t0
+        done_rows += rows
+        total_t += t
+        if total_t >= budget_s or done_rows >= w.M:
+            break
+        left = budget_s - total_t
+        rows = int(min(w.M - done_rows, max(8, rows * min(4.0, left / max(t, 1e-3)))))
+    flops = 2.0 * done_rows * w.N * w.K
+    return {"value": flops / total_t / 1e12, "unit": "TFLOPS" if w.dtype != "i8" else "TOPS",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "first %d of %d rows of A times all of B (%s %dx%dx%d), %.1f s" % (
+                done_rows, w.M, w.dtype, w.M, w.N, w.K, total_t)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="bf16_4096")
+    ap.add_argument("--variant", default="")
+    ap.add_argument("--ladder", action="store_true")
+    ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this GEMM path runs on one GPU only (--gpus %d requested); "
+              "sharding across GPUs is not built" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from tiled_software_pipelined_amd import inputs, lib
+
+    w = inputs.workloads()[args.workload]
+    dev = torch.device("cuda:0")
+    A_cpu, B_cpu = w.operands()
+    A = A_cpu.to(dev)
+    B = B_cpu.to(dev)
+    out_dtype = torch.int32 if w.dtype == "i8" else torch.float32
+    C = torch.empty((w.M, w.N), dtype=out_dtype, device=dev)
+    torch.cuda.synchronize()
+
+    if args.ladder:
+        code = {"f32": lib.F32, "bf16": lib.BF16, "i8": lib.I8}[w.dtype]
+        for v in lib.variants(code):
+            per, _ = time_plan(lib, torch, w, A, B, C, v, max(5, args.steps // 5), 3)
+            ms = sorted(per)[len(per) // 2]
+            p = lib.plan_for(w.M, w.N, w.K, code, w.K, w.N, w.N, v)
+            print(json.dumps({"mode": "ladder", "workload": w.name, "kernel": p.name,
+                              "median_ms": ms, "tflops": w.flops / ms / 1e9,
+                              "frac_peak": w.flops / ms / 1e9 / PEAK_TFLOPS[w.dtype]}), flush=True)
+    if args.sweep:
+        for name, sw in inputs.workloads().items():
+            if not name.startswith("bf16_sweep"):
+                continue
+            a, b = sw.operands()
+            a, b = a.to(dev), b.to(dev)
+            c = torch.empty((sw.M, sw.N), dtype=torch.float32, device=dev)
+            per, _ = time_plan(lib, torch, sw, a, b, c, None, max(10, args.steps // 2), 5)
+            ms = sorted(per)[len(per) // 2]
+            ideal_ms = max(sw.flops / (PEAK_TFLOPS["bf16"] * 1e9), algorithmic_bytes(sw) / (PEAK_HBM_GBS * 1e6))
+            print(json.dumps({"mode": "sweep", "workload": name, "median_ms": ms,
+                              "tflops": sw.flops / ms / 1e9, "frac_roofline": ideal_ms / ms,
+                              "kernel": lib.plan_for(sw.M, sw.N, sw.K, lib.BF16, sw.K, sw.N, sw.N).name}),
+                  flush=True)
+            del a, b, c
+
+    variant = parse_variant(args.variant, lib)
+    per, wall = time_plan(lib, torch, w, A, B, C, variant, args.steps, args.warmup)
+    code = {"f32": lib.F32, "bf16": lib.BF16, "i8": lib.I8}[w.dtype]
+    plan = lib.plan_for(w.M, w.N, w.K, code, w.K, w.N, w.N, variant)
+    ms_step = wall * 1e3 / args.steps
+    kernel_ms = sum(per) / len(per)
+    value = w.flops * args.steps / wall / 1e12
+    achieved = w.flops / (kernel_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TOPS" if w.dtype == "i8" else "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": "%s GEMM M=%d N=%d K=%d" % (w.dtype, w.M, w.N, w.K),
+                   "operands": w.kind, "seed": w.seed, "kernel": plan.name,
+                   "grid": plan.info().grid, "frac_of_peak": round(value / peak, 4)},
+        "roofline": {"bound": "mfma" if w.dtype != "f32" else "alu", "achieved": round(achieved, 2),
+                     "peak": peak, "unit": "TFLOP/s" if w.dtype != "i8" else "TOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel_ms_mean": round(kernel_ms, 5),
+                     "kernel_ms_min": round(min(per), 5)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        rec["cpu_baseline"] = cpu_baseline(w, A_cpu, B_cpu)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,170 @@
+/*
+ * tgemm.h -- C ABI of libtgemm, a tiled, software-pipelined GEMM for AMD
+ * MI355X (gfx950).
+ *
+ * Operation.  C = A x B, the general matrix product defined in
+ * "4.1 CUDA GEMM算子性能优化" (CUDA GEMM operator optimisation), section 1.1:
+ * A is M x K, B is K x N, C is M x N, 2*M*N*K flops (section 1.3).  All three
+ * matrices are row-major with leading dimensions in elements, the indexing of
+ * that page's naive kernel (section 3.1):
+ *
+ *     C[i*ldc + j] = sum_{k < K} A[i*lda + k] * B[k*ldb + j],  i < M, j < N.
+ *
+ * C is overwritten (no alpha/beta, no transposes).  Elements of C outside the
+ * M x N window are never written.  K = 0 writes zeros; M = 0 or N = 0 does
+ * nothing.  A and B must not overlap C.
+ *
+ * Types (operand -> output):
+ *   TGEMM_F32  : float    x float    -> float   (fp32 vector fused multiply-add,
+ *                one fma chain per output in increasing k)
+ *   TGEMM_BF16 : bf16     x bf16     -> float   (matrix cores, fp32 accumulate)
+ *   TGEMM_I8   : int8     x int8     -> int32   (matrix cores, exact int32
+ *                accumulate; exact while |C| < 2^31, i.e. K <= 131072)
+ * bf16 operands are passed as their raw 16-bit patterns.
+ *
+ * The K loop is software-pipelined as the "流水化 GPU 内核" (pipelining GPU
+ * kernels) skill, Step 3, and the GEMM page, sections 9-10, describe: tiles of
+ * A and B move global -> LDS through a ring of 1-4 stages while the matrix
+ * cores work on an earlier stage.
+ *
+ * Ownership.  The caller owns A, B, C and the stream.  The library allocates
+ * no device memory and never copies or pads inputs.  A plan holds only host
+ * metadata; it is immutable after creation, so one plan may be run
+ * concurrently on several streams.
+ *
+ * Errors.  gemm_plan* return NULL and record a message (tgemm_last_error) on
+ * invalid arguments.  gemm_run returns TGEMM_OK once the kernel is enqueued,
+ * a negative TGEMM_E_* code for a rejected call (nothing is enqueued), or
+ * TGEMM_E_HIP if the launch itself failed.  Faults during execution surface
+ * at the caller's next synchronisation on the stream.  The error message is
+ * thread-local.
+ */
+#ifndef TGEMM_H
+#define TGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tgemm_dtype {
+    TGEMM_F32 = 0,
+    TGEMM_BF16 = 1,
+    TGEMM_I8 = 2
+} tgemm_dtype;
+
+#define TGEMM_OK 0
+#define TGEMM_E_ARG (-1)     /* invalid argument (sizes, leading dims, dtype) */
+#define TGEMM_E_NULL (-2)    /* NULL plan or matrix pointer with non-empty work */
+#define TGEMM_E_ALIGN (-3)   /* pointer not aligned to its element size */
+#define TGEMM_E_ARCH (-4)    /* current device is not gfx950 */
+#define TGEMM_E_VARIANT (-5) /* requested variant not available for this plan */
+#define TGEMM_E_HIP (-6)     /* HIP runtime call failed (message has detail) */
+
+/* Kernel families (the steps of the optimisation ladder, one variable per
+ * step, as the SM80 cp.async / ldmatrix ablation plan, section 1, and the
+ * GEMM page, sections 3-10, order them). */
+#define TGEMM_KERNEL_AUTO 0      /* let the plan choose (the default) */
+#define TGEMM_KERNEL_NAIVE 1     /* one thread per C element, no LDS (section 3.1) */
+#define TGEMM_KERNEL_TILED 2     /* LDS block tiling + register / matrix-core tiles */
+
+/* Global -> LDS loaders (the "流水化 GPU 内核" skill, Step 2: register-staged
+ * vs asynchronous copy). */
+#define TGEMM_LOADER_VGPR 1      /* loads into registers, then ds_write */
+#define TGEMM_LOADER_DIRECT 2    /* global_load_lds_dwordx4 straight into LDS */
+
+/* LDS layouts (GEMM page, section 8.5). */
+#define TGEMM_LDS_PLAIN 1
+#define TGEMM_LDS_XOR 2          /* 16-byte chunk index XOR-swizzled by row */
+
+/* Access width of global loads, LDS writes and LDS fragment reads
+ * (GEMM page, section 7: 128-bit vector accesses). */
+#define TGEMM_ACCESS_WIDE 1      /* 16-byte accesses */
+#define TGEMM_ACCESS_NARROW 2    /* 4-byte global loads / LDS accesses */
+
+/* Register tiling (GEMM page, sections 5-6). */
+#define TGEMM_FRAG_REUSE 1       /* each fragment read once per k step, reused across the wave tile */
+#define TGEMM_FRAG_PER_MMA 2     /* both fragments re-read for every matrix-core instruction */
+
+/* Workgroup order (GEMM page, section 2.3). */
+#define TGEMM_ORDER_ROW_MAJOR (-1)
+
+/* Variant description.  Zero-initialise and set the fields you want; a zero
+ * field means "the plan's default" (every TGEMM_* value above is non-zero).  Only combinations the library was built
+ * with are accepted (TGEMM_E_VARIANT otherwise; gemm_variant_count /
+ * gemm_variant_get enumerate them). */
+typedef struct tgemm_variant {
+    int32_t kernel;     /* TGEMM_KERNEL_* */
+    int32_t tile_m;     /* workgroup tile rows (BM) */
+    int32_t tile_n;     /* workgroup tile columns (BN) */
+    int32_t tile_k;     /* K step per stage (BK), in elements */
+    int32_t stages;     /* LDS stages in the ring: 1 (no pipelining) .. 4 */
+    int32_t loader;     /* TGEMM_LOADER_* */
+    int32_t lds_layout; /* TGEMM_LDS_* */
+    int32_t access;     /* TGEMM_ACCESS_* */
+    int32_t frag;       /* TGEMM_FRAG_* */
+    int32_t wg_group;   /* TGEMM_ORDER_ROW_MAJOR, or g >= 1: XCD-aware order grouped by g tile rows */
+} tgemm_variant;
+
+typedef struct tgemm_plan tgemm_plan;
+
+/* Create a plan for an M x N x K product of the given type with the given
+ * leading dimensions (elements).  Requires M, N, K >= 0, lda >= K, ldb >= N,
+ * ldc >= N (each leading dimension >= 1).  Does not touch the device.  The
+ * plan picks the fastest variant built for this shape.  Returns NULL on error. */
+tgemm_plan* gemm_plan(int64_t M, int64_t N, int64_t K, int32_t dtype,
+                      int64_t lda, int64_t ldb, int64_t ldc);
+
+/* As gemm_plan, with an explicit variant (NULL = default).  Used by the
+ * ablation harness to time one rung of the ladder. */
+tgemm_plan* gemm_plan_variant(int64_t M, int64_t N, int64_t K, int32_t dtype,
+                              int64_t lda, int64_t ldb, int64_t ldc,
+                              const tgemm_variant* variant);
+
+/* Enqueue C = A x B on `stream` (a hipStream_t; NULL = the null stream) on
+ * the current HIP device.  A, B, C are device pointers (or any pointers the
+ * device can access) aligned to their element size.  A pointer that is
+ * element-aligned but not 16-byte aligned, or a leading dimension whose rows
+ * are not 16-byte aligned, makes that operand use the guarded narrow loader
+ * (slower, same results).  Returns TGEMM_OK or a TGEMM_E_* code. */
+int gemm_run(const tgemm_plan* plan, const void* A, const void* B, void* C,
+             void* stream);
+
+/* Free a plan (NULL is allowed). */
+void gemm_destroy(tgemm_plan* plan);
+
+/* Last error message of this thread ("" if none). */
+const char* tgemm_last_error(void);
+
+/* What a plan will launch. */
+typedef struct tgemm_plan_info {
+    int64_t M, N, K, lda, ldb, ldc;
+    int32_t dtype;
+    tgemm_variant variant;   /* fully resolved (no zero/default fields) */
+    int32_t grid;            /* workgroups launched */
+    int32_t threads;         /* threads per workgroup */
+    int32_t lds_bytes;       /* LDS per workgroup */
+    int32_t loads_per_stage; /* global->LDS instructions per wave per stage */
+    int32_t a_guarded;       /* A uses the guarded narrow loader for every tile */
+    int32_t b_guarded;       /* B uses the guarded narrow loader for every tile */
+    char name[96];           /* kernel name, e.g. "bf16_t256x256x64_s2_direct_xor_wide_reuse" */
+} tgemm_plan_info;
+
+/* Fill *info for `plan`.  Returns TGEMM_OK or TGEMM_E_NULL. */
+int gemm_plan_get_info(const tgemm_plan* plan, tgemm_plan_info* info);
+
+/* Enumerate the variants compiled into the library for `dtype`.
+ * gemm_variant_count returns how many; gemm_variant_get copies the i-th one
+ * (0 <= i < count) and returns TGEMM_OK, or TGEMM_E_ARG for a bad index. */
+int gemm_variant_count(int32_t dtype);
+int gemm_variant_get(int32_t dtype, int32_t index, tgemm_variant* out);
+
+/* Library version string. */
+const char* tgemm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TGEMM_H */

@@ -1,0 +1,118 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/tgemm.h declares, validates plans and picks variants."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tgemm.h")
+
+tl = pytest.importorskip("tiled_software_pipelined_amd.lib")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w\s\*]*?\b(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if not n.startswith("TGEMM")))
+
+
+def test_header_declares_the_abi():
+    names = _declared_functions()
+    for n in ("gemm_plan", "gemm_run", "gemm_destroy"):
+        assert n in names
+    assert set(names) == set(tl.EXPORTS)
+
+
+@pytest.mark.parametrize("name", _declared_functions())
+def test_library_exports_symbol(name):
+    lib = ctypes.CDLL(tl.LIB_PATH)
+    assert hasattr(lib, name)
+
+
+def test_version():
+    assert "gfx950" in tl.version()
+
+
+@pytest.mark.parametrize("args", [
+    (-1, 4, 4, tl.F32, 4, 4, 4),          # negative M
+    (4, 4, 4, 7, 4, 4, 4),                # unknown dtype
+    (4, 4, 8, tl.BF16, 7, 4, 4),          # lda < K
+    (4, 8, 4, tl.BF16, 4, 7, 8),          # ldb < N
+    (4, 8, 4, tl.BF16, 4, 8, 7),          # ldc < N
+    (4, 4, 200000, tl.I8, 200000, 4, 4),  # int8 K beyond exact int32 range
+    (2 ** 31, 4, 4, tl.F32, 4, 4, 4),     # too large
+])
+def test_plan_rejects_invalid(args):
+    with pytest.raises(tl.TgemmError):
+        tl.Plan(*args)
+    assert tl.last_error() != ""
+
+
+def test_plan_run_rejects_null_plan():
+    assert tl._lib.gemm_run(None, None, None, None, None) == -2
+    assert "NULL" in tl.last_error()
+
+
+def test_run_with_empty_output_is_a_noop_without_device():
+    # M = 0: nothing to do, returns before touching the device
+    p = tl.Plan(0, 16, 16, tl.BF16)
+    p.run_ptr(0, 0, 0)
+
+
+def test_destroy_null_is_allowed():
+    tl._lib.gemm_destroy(None)
+
+
+@pytest.mark.parametrize("dtype", [tl.F32, tl.BF16, tl.I8])
+def test_variants_enumerate(dtype):
+    vs = tl.variants(dtype)
+    assert len(vs) >= 3
+    kinds = {v.kernel for v in vs}
+    assert kinds == {tl.KERNEL_NAIVE, tl.KERNEL_TILED}
+    for v in vs:
+        p = tl.Plan(512, 512, 512, dtype, variant=v)
+        got = p.info().variant
+        for f in ("kernel", "tile_m", "tile_n", "tile_k", "stages", "loader", "lds_layout", "access", "frag"):
+            assert getattr(got, f) == getattr(v, f)
+
+
+def test_bad_variant_rejected():
+    v = tl.Variant(kernel=tl.KERNEL_TILED, tile_m=96)
+    with pytest.raises(tl.TgemmError):
+        tl.Plan(256, 256, 256, tl.BF16, variant=v)
+
+
+def test_default_choice_by_shape():
+    big = tl.Plan(4096, 4096, 4096, tl.BF16).info()
+    assert (big.variant.tile_m, big.variant.tile_n) == (256, 256)
+    assert big.variant.loader == tl.LOADER_DIRECT and big.grid == 256
+    small = tl.Plan(512, 512, 512, tl.BF16).info()
+    assert (small.variant.tile_m, small.variant.tile_n) == (128, 128) and small.grid == 16
+    f = tl.Plan(256, 256, 256, tl.F32).info()
+    assert f.variant.tile_k == 8 and f.grid == 4
+
+
+def test_unaligned_leading_dimension_uses_guarded_register_loader():
+    # ragged workload: B rows of 4097 bf16 = 8194 bytes are not 16-byte aligned
+    info = tl.Plan(4095, 4097, 4104, tl.BF16).info()
+    assert info.b_guarded == 1 and info.a_guarded == 0
+    assert info.variant.loader == tl.LOADER_VGPR
+    assert info.grid == 16 * 17
+
+
+def test_lds_budget_of_stage_ring():
+    # 128 x 128 x 32 bf16: 8 KiB of A + 8 KiB of B per stage (the SM80 ablation
+    # plan's stage table, section 1.4): S = 2, 3, 4 -> 32, 48, 64 KiB
+    for s, kib in ((2, 32), (3, 48), (4, 64)):
+        v = tl.Variant(kernel=tl.KERNEL_TILED, tile_m=128, tile_n=128, tile_k=32, stages=s,
+                       loader=tl.LOADER_DIRECT)
+        assert tl.Plan(4096, 4096, 4096, tl.BF16, variant=v).info().lds_bytes == kib * 1024
+
+
+def test_loads_per_stage_match_tile_bytes():
+    info = tl.Plan(4096, 4096, 4096, tl.BF16).info()
+    # 256 x 64 + 64 x 256 bf16 = 64 KiB per slice, 256 threads, 16 B per load
+    assert info.loads_per_stage == 65536 // 256 // 16

@@ -1,0 +1,28 @@
+// bf16 kernel variants compiled into libtgemm.  Order matters: for a given
+// set of requested fields the first matching entry wins.
+#include "tg_kernels.hpp"
+
+namespace tg {
+
+void register_bf16(void (*add)(const KernelEntry&)) {
+    typedef TraitsBF16 T;
+    // production tiles
+    add(mfma_entry<T, 256, 256, 64, 2, 2, 2, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 1>(1));
+    add(mfma_entry<T, 256, 256, 32, 2, 2, 3, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 1>(1));
+    add(mfma_entry<T, 256, 256, 32, 2, 2, 4, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 1>(1));
+    add(mfma_entry<T, 256, 256, 64, 2, 4, 2, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2>(1));
+    add(mfma_entry<T, 256, 128, 64, 2, 2, 2, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 1>(1));
+    add(mfma_entry<T, 256, 256, 64, 2, 2, 2, LD_VGPR, LY_XOR, AC_WIDE, FR_REUSE, 1>(1));
+    // the 128 x 128 x 32 ladder, one change per step
+    add(mfma_entry<T, 128, 128, 32, 2, 2, 3, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2>(1));
+    add(mfma_entry<T, 128, 128, 32, 2, 2, 4, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2>(1));
+    add(mfma_entry<T, 128, 128, 32, 2, 2, 2, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2>(1));
+    add(mfma_entry<T, 128, 128, 32, 2, 2, 2, LD_VGPR, LY_XOR, AC_WIDE, FR_REUSE, 2>(1));
+    add(mfma_entry<T, 128, 128, 32, 2, 2, 1, LD_VGPR, LY_XOR, AC_WIDE, FR_REUSE, 2>(1));
+    add(mfma_entry<T, 128, 128, 32, 2, 2, 1, LD_VGPR, LY_PLAIN, AC_WIDE, FR_REUSE, 2>(1));
+    add(mfma_entry<T, 128, 128, 32, 2, 2, 1, LD_VGPR, LY_PLAIN, AC_NARROW, FR_REUSE, 2>(1));
+    add(mfma_entry<T, 128, 128, 32, 2, 2, 1, LD_VGPR, LY_PLAIN, AC_NARROW, FR_PER_MMA, 2>(1));
+    add(naive_entry<1>());
+}
+
+}  // namespace tg

@@ -1,0 +1,18 @@
+// int8 kernel variants compiled into libtgemm (same bytes per slice as the
+// bf16 ones: BK doubles because an element is one byte).
+#include "tg_kernels.hpp"
+
+namespace tg {
+
+void register_i8(void (*add)(const KernelEntry&)) {
+    typedef TraitsI8 T;
+    add(mfma_entry<T, 256, 256, 128, 2, 2, 2, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 1>(2));
+    add(mfma_entry<T, 256, 256, 128, 2, 2, 2, LD_VGPR, LY_XOR, AC_WIDE, FR_REUSE, 1>(2));
+    add(mfma_entry<T, 128, 128, 64, 2, 2, 3, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2>(2));
+    add(mfma_entry<T, 128, 128, 64, 2, 2, 2, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2>(2));
+    add(mfma_entry<T, 128, 128, 64, 2, 2, 2, LD_VGPR, LY_XOR, AC_WIDE, FR_REUSE, 2>(2));
+    add(mfma_entry<T, 128, 128, 64, 2, 2, 1, LD_VGPR, LY_PLAIN, AC_NARROW, FR_PER_MMA, 2>(2));
+    add(naive_entry<2>());
+}
+
+}  // namespace tg

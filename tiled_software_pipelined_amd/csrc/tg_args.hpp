@@ -1,0 +1,54 @@
+// Kernel argument block and the registry record that describes one compiled
+// kernel variant to the host library.
+#pragma once
+
+#include <stdint.h>
+
+namespace tg {
+
+// Passed by value to every GEMM kernel.  Row-major operands, leading
+// dimensions in elements; sizes already validated by the host.
+struct GemmArgs {
+    const void* A;
+    const void* B;
+    void* C;
+    int32_t M, N, K;
+    int32_t tiles_m, tiles_n;  // ceil(M / BM), ceil(N / BN)
+    int64_t lda, ldb, ldc;
+    int32_t wg_group;          // <= 0: row-major workgroup order
+    int32_t a_guard;           // 1: every A tile through the guarded element loader
+    int32_t b_guard;           // 1: every B tile through the guarded element loader
+};
+
+typedef void (*KernelFn)(GemmArgs);
+
+enum Family { FAM_NAIVE = 1, FAM_TILED = 2 };
+enum Loader { LD_VGPR = 1, LD_DIRECT = 2 };
+enum Layout { LY_PLAIN = 1, LY_XOR = 2 };
+enum Access { AC_WIDE = 1, AC_NARROW = 2 };
+enum Frag { FR_REUSE = 1, FR_PER_MMA = 2 };
+
+struct KernelEntry {
+    int dtype;       // TGEMM_* dtype
+    int family;      // Family
+    int bm, bn, bk;  // tile (naive: threads per block in x/y, bk = 1)
+    int stages;
+    int loader;      // Loader
+    int layout;      // Layout
+    int access;      // Access
+    int frag;        // Frag
+    int threads;     // threads per workgroup
+    int lds_bytes;   // static LDS per workgroup
+    int loads_per_stage;  // global->LDS instructions per wave per stage
+    int guard_ok;    // accepts a_guard / b_guard = 1
+    int tail_ok;     // handles K not a multiple of bk
+    KernelFn fn;
+    char name[96];
+};
+
+// Filled by each instantiation unit; the host library concatenates them.
+void register_bf16(void (*add)(const KernelEntry&));
+void register_i8(void (*add)(const KernelEntry&));
+void register_f32(void (*add)(const KernelEntry&));
+
+}  // namespace tg

@@ -1,0 +1,76 @@
+// Device-side building blocks shared by the libtgemm kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tg_args.hpp"
+
+namespace tg {
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
+typedef int16_t i16x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+#define TG_LDS __attribute__((address_space(3)))
+
+// Wait until at most N vector-memory instructions of this wave are still
+// outstanding and every LDS access of this wave has completed, then meet the
+// other waves of the workgroup at the barrier.  Written as one asm statement
+// with a memory clobber so that the compiler neither moves LDS accesses
+// across it nor widens it into vmcnt(0) (which the fenced __syncthreads()
+// does and which would drain every stage in flight).  Waiting for the LDS
+// reads matters: after the barrier another wave may start a copy into the
+// slot those reads came from.
+template <int N>
+__device__ __forceinline__ void wait_vm_then_barrier() {
+    static_assert(N >= 0 && N <= 63, "vmcnt is a 6-bit counter on gfx9");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Wait for this wave's LDS writes, then barrier (register-staged loaders).
+__device__ __forceinline__ void wait_lds_then_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Wait for every outstanding memory instruction of this wave, then barrier.
+__device__ __forceinline__ void wait_all_then_barrier() {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Workgroup -> output tile.  The hardware hands workgroup b to XCD b mod 8;
+// with wg_group > 0 the id is first re-ranked so that consecutive ids run on
+// one XCD (and share its L2), then tiles are walked in groups of wg_group
+// tile rows, column by column, so that one XCD's workgroups reuse the same
+// A row panels and B column panels (the block-order effect on L2 hit rate of
+// "4.1 CUDA GEMM算子性能优化", section 2.3).
+__device__ __forceinline__ void tile_of_workgroup(const GemmArgs& g, int& tm, int& tn) {
+    const int b = blockIdx.x;
+    if (g.wg_group <= 0) {
+        tm = b / g.tiles_n;
+        tn = b - tm * g.tiles_n;
+        return;
+    }
+    const int total = g.tiles_m * g.tiles_n;
+    int r = b;
+    if ((total & 7) == 0) r = (b & 7) * (total >> 3) + (b >> 3);
+    const int per_group = g.wg_group * g.tiles_n;
+    const int group = r / per_group;
+    const int first_m = group * g.wg_group;
+    const int rows = min(g.tiles_m - first_m, g.wg_group);
+    const int in_group = r - group * per_group;
+    tm = first_m + in_group % rows;
+    tn = in_group / rows;
+}
+
+}  // namespace tg

@@ -1,0 +1,196 @@
+// fp32 GEMM on the vector ALUs (no matrix cores): the register-tiled
+// outer-product kernel of "4.1 CUDA GEMM算子性能优化", sections 4-9, laid out
+// for 64-wide waves.
+//
+// Workgroup tile 128 x 128, K slice 8, 256 threads = 4 waves in a 2 x 2 grid,
+// each wave 64 x 64.  Lane l of a wave is (lr, lc) = (l / 8, l % 8) in an
+// 8 x 8 lane grid and owns an 8 x 8 block of C split into 4 x 4 quarters 32
+// rows / columns apart, so that the 16-byte fragment reads of one wave cover
+// 8 distinct, contiguous 16-byte words of LDS (the others are broadcasts).
+// A is stored transposed in LDS (As[k][m], section 7.3) so that both
+// fragments are 16-byte reads.
+//
+// Every C element is one fused multiply-add chain in increasing k, started
+// from zero: acc = fma(a_ik, b_kj, acc).  The K tail is zero-filled, and
+// fma(0, b, acc) = acc, so the result equals the sequential single-precision
+// fma chain bit for bit.
+//
+// STAGES = 1: load slice, barrier, compute, barrier.  STAGES = 2: the
+// register-staged double buffer of section 9.5 (issue the loads of slice t+1,
+// compute slice t, store slice t+1 to the other buffer, one barrier).
+#pragma once
+
+#include "tg_device.hpp"
+
+namespace tg {
+
+template <int STAGES>
+struct F32Gemm {
+    static constexpr int BM = 128, BN = 128, BK = 8, NT = 256;
+    static constexpr int A_BYTES = BK * BM * 4;
+    static constexpr int B_BYTES = BK * BN * 4;
+    static constexpr int SLOT = A_BYTES + B_BYTES;
+    static constexpr int LDS_BYTES = STAGES * SLOT;
+    static constexpr int N_LD = 2;
+    static_assert(STAGES == 1 || STAGES == 2, "register-staged: 1 or 2 slots");
+
+    struct Staged {
+        f32x4 a, b;
+    };
+
+    // Thread t loads A[m0 + t/2][k0 + 4 (t%2) .. +3] and B[k0 + t/32][n0 + 4 (t%32) .. +3].
+    __device__ static __forceinline__ void load(Staged& r, const GemmArgs& g, int m0, int n0, int k0,
+                                                bool guard_a, bool guard_b) {
+        const float* A = static_cast<const float*>(g.A);
+        const float* B = static_cast<const float*>(g.B);
+        const int t = threadIdx.x;
+        {
+            const float* rowp = A + (int64_t)min(m0 + (t >> 1), g.M - 1) * g.lda;
+            const int kc = k0 + 4 * (t & 1);
+            if (!guard_a) {
+                r.a = *reinterpret_cast<const f32x4*>(rowp + kc);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) r.a[e] = kc + e < g.K ? rowp[kc + e] : 0.0f;
+            }
+        }
+        {
+            const int gk = k0 + (t >> 5);
+            const int nc = n0 + 4 * (t & 31);
+            if (!guard_b) {
+                r.b = *reinterpret_cast<const f32x4*>(B + (int64_t)gk * g.ldb + min(nc, g.N - 4));
+            } else {
+                const float* rowp = B + (int64_t)gk * g.ldb;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) r.b[e] = (gk < g.K && nc + e < g.N) ? rowp[nc + e] : 0.0f;
+            }
+        }
+    }
+
+    __device__ static __forceinline__ void store(TG_LDS char* slot, const Staged& r) {
+        const int t = threadIdx.x;
+        TG_LDS float* As = reinterpret_cast<TG_LDS float*>(slot);
+        TG_LDS float* Bs = reinterpret_cast<TG_LDS float*>(slot + A_BYTES);
+        const int row = t >> 1, kq = 4 * (t & 1);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) As[(kq + e) * BM + row] = r.a[e];
+        *reinterpret_cast<TG_LDS f32x4*>(Bs + (t >> 5) * BN + 4 * (t & 31)) = r.b;
+    }
+
+    __device__ static __forceinline__ void compute(const TG_LDS char* slot, float (&c)[8][8], int am,
+                                                   int bn) {
+        const TG_LDS float* As = reinterpret_cast<const TG_LDS float*>(slot);
+        const TG_LDS float* Bs = reinterpret_cast<const TG_LDS float*>(slot + A_BYTES);
+#pragma unroll
+        for (int k = 0; k < BK; ++k) {
+            const f32x4 a0 = *reinterpret_cast<const TG_LDS f32x4*>(As + k * BM + am);
+            const f32x4 a1 = *reinterpret_cast<const TG_LDS f32x4*>(As + k * BM + am + 32);
+            const f32x4 b0 = *reinterpret_cast<const TG_LDS f32x4*>(Bs + k * BN + bn);
+            const f32x4 b1 = *reinterpret_cast<const TG_LDS f32x4*>(Bs + k * BN + bn + 32);
+            const float a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+            const float b[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) c[i][j] = __builtin_fmaf(a[i], b[j], c[i][j]);
+        }
+    }
+
+    __device__ static void run(const GemmArgs& g) {
+        __shared__ __attribute__((aligned(1024))) char smem_raw[LDS_BYTES];
+        TG_LDS char* smem = (TG_LDS char*)(smem_raw);
+        int tm, tn;
+        tile_of_workgroup(g, tm, tn);
+        const int m0 = tm * BM, n0 = tn * BN;
+        const int wave = wave_id(), lane = lane_id();
+        const int lr = lane >> 3, lc = lane & 7;
+        const int am = (wave >> 1) * 64 + 4 * lr;  // first of this thread's rows in the tile
+        const int bn = (wave & 1) * 64 + 4 * lc;   // first of its columns
+
+        float c[8][8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) c[i][j] = 0.0f;
+
+        const int tiles = (g.K + BK - 1) / BK;
+        const int full = g.K / BK;
+        const bool ga = g.a_guard != 0, gb = g.b_guard != 0;
+        if constexpr (STAGES == 1) {
+            for (int t = 0; t < tiles; ++t) {
+                Staged r;
+                load(r, g, m0, n0, t * BK, ga || t >= full, gb || t >= full);
+                store(smem, r);
+                wait_lds_then_barrier();
+                compute(smem, c, am, bn);
+                wait_lds_then_barrier();
+            }
+        } else {
+            if (tiles > 0) {
+                Staged r;
+                load(r, g, m0, n0, 0, ga || full == 0, gb || full == 0);
+                store(smem, r);
+                wait_lds_then_barrier();
+            }
+            for (int t = 0; t < tiles; ++t) {
+                const int nxt = t + 1;
+                Staged r;
+                if (nxt < tiles) load(r, g, m0, n0, nxt * BK, ga || nxt >= full, gb || nxt >= full);
+                compute(smem + (t & 1) * SLOT, c, am, bn);
+                if (nxt < tiles) store(smem + (nxt & 1) * SLOT, r);
+                wait_lds_then_barrier();
+            }
+        }
+
+        float* C = static_cast<float*>(g.C);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int row = m0 + am + (i & 3) + 32 * (i >> 2);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int col = n0 + bn + (j & 3) + 32 * (j >> 2);
+                if (row < g.M && col < g.N) C[(int64_t)row * g.ldc + col] = c[i][j];
+            }
+        }
+    }
+};
+
+// One thread per C element, no LDS: the naive kernel of section 3.1 (the
+// ladder's anchor).  fp32 accumulation as one fma chain in increasing k
+// (int32 sums for int8).
+template <int DT>
+struct NaiveGemm {
+    static constexpr int BM = 16, BN = 16, NT = 256;
+    __device__ static void run(const GemmArgs& g) {
+        int tm, tn;
+        tile_of_workgroup(g, tm, tn);
+        const int row = tm * BM + (threadIdx.x >> 4);
+        const int col = tn * BN + (threadIdx.x & 15);
+        if (row >= g.M || col >= g.N) return;
+        if constexpr (DT == 0) {  // fp32
+            const float* A = static_cast<const float*>(g.A) + (int64_t)row * g.lda;
+            const float* B = static_cast<const float*>(g.B) + col;
+            float acc = 0.0f;
+            for (int k = 0; k < g.K; ++k) acc = __builtin_fmaf(A[k], B[(int64_t)k * g.ldb], acc);
+            static_cast<float*>(g.C)[(int64_t)row * g.ldc + col] = acc;
+        } else if constexpr (DT == 1) {  // bf16 bits
+            const uint16_t* A = static_cast<const uint16_t*>(g.A) + (int64_t)row * g.lda;
+            const uint16_t* B = static_cast<const uint16_t*>(g.B) + col;
+            float acc = 0.0f;
+            for (int k = 0; k < g.K; ++k) {
+                const float a = __uint_as_float((uint32_t)A[k] << 16);
+                const float b = __uint_as_float((uint32_t)B[(int64_t)k * g.ldb] << 16);
+                acc = __builtin_fmaf(a, b, acc);
+            }
+            static_cast<float*>(g.C)[(int64_t)row * g.ldc + col] = acc;
+        } else {  // int8
+            const int8_t* A = static_cast<const int8_t*>(g.A) + (int64_t)row * g.lda;
+            const int8_t* B = static_cast<const int8_t*>(g.B) + col;
+            int32_t acc = 0;
+            for (int k = 0; k < g.K; ++k) acc += (int32_t)A[k] * (int32_t)B[(int64_t)k * g.ldb];
+            static_cast<int32_t*>(g.C)[(int64_t)row * g.ldc + col] = acc;
+        }
+    }
+};
+
+}  // namespace tg

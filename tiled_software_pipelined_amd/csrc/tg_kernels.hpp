@@ -1,0 +1,96 @@
+// Kernel entry points and registry records for the kernel templates.
+#pragma once
+
+#include <stdio.h>
+
+#include "tg_f32.hpp"
+#include "tg_mfma.hpp"
+
+namespace tg {
+
+// WAVES: waves per SIMD the kernel is compiled for (1 lets a wave use the
+// whole 512-entry register file, VGPRs plus AGPRs).
+template <class Kern, int WAVES>
+__global__ __launch_bounds__(Kern::NT) __attribute__((amdgpu_waves_per_eu(WAVES, WAVES)))
+void gemm_kernel(GemmArgs g) {
+    Kern::run(g);
+}
+
+static const char* dtype_tag(int dt) { return dt == 0 ? "f32" : dt == 1 ? "bf16" : "i8"; }
+
+template <class Tr, int BM, int BN, int BK, int WM, int WN, int S, int LD, int LY, int AC, int FR,
+          int WAVES>
+KernelEntry mfma_entry(int dtype) {
+    typedef MfmaGemm<Tr, BM, BN, BK, WM, WN, S, LD, LY, AC, FR> K;
+    KernelEntry e{};
+    e.dtype = dtype;
+    e.family = FAM_TILED;
+    e.bm = BM;
+    e.bn = BN;
+    e.bk = BK;
+    e.stages = S;
+    e.loader = LD;
+    e.layout = LY;
+    e.access = AC;
+    e.frag = FR;
+    e.threads = K::NT;
+    e.lds_bytes = K::LDS_BYTES;
+    e.loads_per_stage = AC == AC_WIDE ? K::N_LD : K::A_DW + K::B_DW;
+    e.guard_ok = LD == LD_VGPR;
+    e.tail_ok = 1;
+    e.fn = gemm_kernel<K, WAVES>;
+    snprintf(e.name, sizeof e.name, "%s_t%dx%dx%d_w%dx%d_s%d_%s_%s_%s_%s", dtype_tag(dtype), BM, BN,
+             BK, WM, WN, S, LD == LD_DIRECT ? "direct" : "vgpr", LY == LY_XOR ? "xor" : "plain",
+             AC == AC_WIDE ? "wide" : "narrow", FR == FR_REUSE ? "reuse" : "permma");
+    return e;
+}
+
+template <int DT>
+KernelEntry naive_entry() {
+    typedef NaiveGemm<DT> K;
+    KernelEntry e{};
+    e.dtype = DT;
+    e.family = FAM_NAIVE;
+    e.bm = K::BM;
+    e.bn = K::BN;
+    e.bk = 1;
+    e.stages = 1;
+    e.loader = LD_VGPR;
+    e.layout = LY_PLAIN;
+    e.access = AC_NARROW;
+    e.frag = FR_PER_MMA;
+    e.threads = K::NT;
+    e.lds_bytes = 0;
+    e.loads_per_stage = 0;
+    e.guard_ok = 1;
+    e.tail_ok = 1;
+    e.fn = gemm_kernel<K, 4>;
+    snprintf(e.name, sizeof e.name, "%s_naive", dtype_tag(DT));
+    return e;
+}
+
+template <int S>
+KernelEntry f32_entry() {
+    typedef F32Gemm<S> K;
+    KernelEntry e{};
+    e.dtype = 0;
+    e.family = FAM_TILED;
+    e.bm = K::BM;
+    e.bn = K::BN;
+    e.bk = K::BK;
+    e.stages = S;
+    e.loader = LD_VGPR;
+    e.layout = LY_PLAIN;
+    e.access = AC_WIDE;
+    e.frag = FR_REUSE;
+    e.threads = K::NT;
+    e.lds_bytes = K::LDS_BYTES;
+    e.loads_per_stage = K::N_LD;
+    e.guard_ok = 1;
+    e.tail_ok = 1;
+    e.fn = gemm_kernel<K, 2>;
+    snprintf(e.name, sizeof e.name, "f32_t128x128x8_w2x2_s%d_vgpr_plain_wide_reuse", S);
+    return e;
+}
+
+}  // namespace tg

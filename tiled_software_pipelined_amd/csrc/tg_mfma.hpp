@@ -1,0 +1,454 @@
+// Matrix-core (MFMA) GEMM kernel family for gfx950: bf16 x bf16 -> fp32 and
+// int8 x int8 -> int32.
+//
+// One workgroup computes one BM x BN tile of C.  Its waves form a
+// WAVES_M x WAVES_N grid; each wave owns a (BM/WAVES_M) x (BN/WAVES_N) block
+// made of 32 x 32 matrix-core tiles ("4.1 CUDA GEMM算子性能优化", sections 4-6:
+// block, warp and thread tiling, with the wave as the unit on this GPU).  The
+// K loop walks BK-wide slices of A and B through a ring of STAGES LDS slots
+// (same page, sections 9-10; the "流水化 GPU 内核" skill, Step 3: prologue,
+// steady loop, epilogue):
+//
+//   prologue : start the loads of slices 0 .. STAGES-2
+//   slice t  : wait for slice t, barrier, start slice t+STAGES-1 into the slot
+//              slice t-1 just left, then multiply slice t out of LDS
+//
+// so that the global->LDS copy of later slices overlaps the matrix-core work
+// on slice t.  Two loaders are built (the skill's Step 2 choice):
+//   LD_VGPR   : 16-byte loads into registers, written to LDS after the
+//               multiply of the current slice (register-staged double buffer,
+//               GEMM page section 9.5);
+//   LD_DIRECT : global_load_lds_dwordx4, which writes LDS without passing
+//               through registers (the asynchronous copy of section 10).
+//
+// Operand fragments come from LDS with 16-byte reads (A, K-contiguous) and
+// the gfx950 transposing reads ds_read_b64_tr_b16 / _tr_b8 (B, which is
+// N-contiguous in memory but must be K-contiguous in each lane).  With
+// LY_XOR the 16-byte chunks of every LDS row are permuted by an XOR of the
+// row index so that the lanes of one read hit distinct banks (section 8.5).
+//
+// Edges: rows of A past M and columns of B past N are loaded from a clamped,
+// valid address (they only feed C elements that are never stored); the last,
+// partial K slice is loaded element by element with zero fill (the skill's
+// pitfall list: boundary tiles need a guarded fallback); an operand whose rows
+// are not 16-byte aligned is loaded element by element for every slice.
+#pragma once
+
+#include "tg_device.hpp"
+
+namespace tg {
+
+struct TraitsBF16 {
+    typedef uint16_t T;
+    typedef float Out;
+    typedef f32x16 Acc;
+    static constexpr int ESZ = 2;
+    static constexpr int MK = 16;  // K of one v_mfma_f32_32x32x16_bf16
+    __device__ static __forceinline__ Acc mma(i32x4 a, i32x4 b, Acc c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+};
+
+struct TraitsI8 {
+    typedef int8_t T;
+    typedef int32_t Out;
+    typedef i32x16 Acc;
+    static constexpr int ESZ = 1;
+    static constexpr int MK = 32;  // K of one v_mfma_i32_32x32x32_i8
+    __device__ static __forceinline__ Acc mma(i32x4 a, i32x4 b, Acc c) {
+        return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+    }
+};
+
+template <class Tr, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int LOADER,
+          int LAYOUT, int ACCESS, int FRAG>
+struct MfmaGemm {
+    typedef typename Tr::T T;
+    typedef typename Tr::Out Out;
+    typedef typename Tr::Acc Acc;
+
+    static constexpr int NT = 64 * WAVES_M * WAVES_N;
+    static constexpr int ESZ = Tr::ESZ;
+    static constexpr int CE = 16 / ESZ;      // elements per 16-byte chunk
+    static constexpr int KB = BK * ESZ;      // bytes of one A row of a slice
+    static constexpr int CA = KB / 16;       // 16-byte chunks per A row
+    static constexpr int NB = BN * ESZ;      // bytes of one B row of a slice
+    static constexpr int CB = NB / 16;       // 16-byte chunks per B row
+    static constexpr int A_BYTES = BM * KB;
+    static constexpr int B_BYTES = BK * NB;
+    static constexpr int SLOT = A_BYTES + B_BYTES;
+    static constexpr int LDS_BYTES = STAGES * SLOT;
+    static constexpr int WTM = BM / WAVES_M;
+    static constexpr int WTN = BN / WAVES_N;
+    static constexpr int FM = WTM / 32;
+    static constexpr int FN = WTN / 32;
+    static constexpr int KSUB = BK / Tr::MK;  // matrix-core K steps per slice
+    static constexpr int A_PER = BM * CA / NT;  // 16-byte A chunks per thread per slice
+    static constexpr int B_PER = BK * CB / NT;
+    static constexpr int N_LD = A_PER + B_PER;  // loads per thread (= per wave) per slice
+    static constexpr bool XOR = LAYOUT == LY_XOR;
+    static constexpr bool WIDE = ACCESS == AC_WIDE;
+    static constexpr bool DIRECT = LOADER == LD_DIRECT;
+    // narrow (4-byte) accesses
+    static constexpr int A_DW = BM * KB / 4 / NT;  // A dwords per thread per slice
+    static constexpr int B_DW = BK * NB / 4 / NT;
+
+    static_assert(BM % (32 * WAVES_M) == 0 && BN % (32 * WAVES_N) == 0, "wave tile");
+    static_assert(BK % Tr::MK == 0, "slice must hold whole matrix-core steps");
+    static_assert((BM * CA) % NT == 0 && (BK * CB) % NT == 0, "even 16-byte split");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS per CU");
+    static_assert(!DIRECT || (STAGES >= 2 && WIDE), "direct loads need a ring and 16-byte chunks");
+    static_assert(DIRECT || STAGES <= 2, "register-staged loader: 1 or 2 slots");
+    static_assert(WIDE || (!XOR && !DIRECT), "narrow accesses use the plain layout");
+    static_assert(FRAG == FR_REUSE || !WIDE, "per-instruction fragment reloads only on the narrow rung");
+    static_assert(N_LD * (STAGES > 2 ? STAGES - 2 : 0) <= 63, "vmcnt range");
+
+    // ---- LDS layout --------------------------------------------------------
+    // A: row r of a slice at r*KB; its 16-byte chunks permuted by an XOR so
+    // that the 32 rows read by one 16-byte fragment read spread over the
+    // banks.  Rows that share one 128-byte window use distinct offsets.
+    static constexpr int A_ROWS_PER_WIN = KB >= 128 ? 1 : 128 / KB;
+    __device__ static __forceinline__ int a_chunk(int row, int c) {
+        if constexpr (XOR) return c ^ ((row / A_ROWS_PER_WIN) & (CA - 1));
+        else return c;
+    }
+    // B: row k at k*NB.  A transposing read covers (8/ESZ) consecutive rows
+    // per 16-lane group; XOR the chunk index so those rows (and the
+    // neighbouring group's columns) land on distinct banks.
+    static constexpr int B_RPG = 8 / ESZ;  // rows per 16-lane group of one transposing read
+    __device__ static __forceinline__ int b_chunk(int k, int c) {
+        if constexpr (XOR) return c ^ (((k % B_RPG) * (16 / B_RPG)) & (CB - 1));
+        else return c;
+    }
+
+    // ---- global loads --------------------------------------------------------
+    // Elements [start, start + CE) of one row, zero where index >= limit.
+    __device__ static __forceinline__ i32x4 load_chunk_guarded(const T* rowp, int start, int limit) {
+        union { i32x4 v; T e[CE]; } u;
+#pragma unroll
+        for (int e = 0; e < CE; ++e) {
+            const int idx = start + e;
+            u.e[e] = idx < limit ? rowp[idx] : T(0);
+        }
+        return u.v;
+    }
+
+    struct Staged {
+        i32x4 a[WIDE ? A_PER : 1];
+        i32x4 b[WIDE ? B_PER : 1];
+        int32_t ad[WIDE ? 1 : A_DW];
+        int32_t bd[WIDE ? 1 : B_DW];
+    };
+
+    // Register-staged load of slice k0 (guard_a/guard_b: element loads with
+    // zero fill at k >= K, and at n >= N for B).
+    __device__ static __forceinline__ void load_regs(Staged& r, const GemmArgs& g, int m0, int n0,
+                                                     int k0, bool guard_a, bool guard_b) {
+        const T* A = static_cast<const T*>(g.A);
+        const T* B = static_cast<const T*>(g.B);
+        const int tid = threadIdx.x;
+        if constexpr (WIDE) {
+#pragma unroll
+            for (int q = 0; q < A_PER; ++q) {
+                const int p = q * NT + tid;
+                const int row = p / CA, c = p % CA;
+                const T* rowp = A + (int64_t)min(m0 + row, g.M - 1) * g.lda;
+                const int kc = k0 + c * CE;
+                if (!guard_a) r.a[q] = *reinterpret_cast<const i32x4*>(rowp + kc);
+                else r.a[q] = load_chunk_guarded(rowp, kc, g.K);
+            }
+#pragma unroll
+            for (int q = 0; q < B_PER; ++q) {
+                const int p = q * NT + tid;
+                const int k = p / CB, c = p % CB;
+                const int gk = k0 + k;
+                const int nc = n0 + c * CE;
+                if (!guard_b) {
+                    r.b[q] = *reinterpret_cast<const i32x4*>(B + (int64_t)gk * g.ldb + min(nc, g.N - CE));
+                } else if (gk < g.K) {
+                    r.b[q] = load_chunk_guarded(B + (int64_t)gk * g.ldb, nc, g.N);
+                } else {
+                    r.b[q] = i32x4{0, 0, 0, 0};
+                }
+            }
+        } else {
+            constexpr int EPD = 4 / ESZ;  // elements per dword
+#pragma unroll
+            for (int q = 0; q < A_DW; ++q) {
+                const int p = q * NT + tid;
+                const int row = p / (KB / 4), d = p % (KB / 4);
+                const T* rowp = A + (int64_t)min(m0 + row, g.M - 1) * g.lda;
+                const int kc = k0 + d * EPD;
+                if (!guard_a) {
+                    r.ad[q] = *reinterpret_cast<const int32_t*>(rowp + kc);
+                } else {
+                    union { int32_t v; T e[EPD]; } u;
+#pragma unroll
+                    for (int e = 0; e < EPD; ++e) u.e[e] = kc + e < g.K ? rowp[kc + e] : T(0);
+                    r.ad[q] = u.v;
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < B_DW; ++q) {
+                const int p = q * NT + tid;
+                const int k = p / (NB / 4), d = p % (NB / 4);
+                const int gk = k0 + k;
+                const int nc = n0 + d * EPD;
+                if (!guard_b) {
+                    r.bd[q] = *reinterpret_cast<const int32_t*>(B + (int64_t)gk * g.ldb + min(nc, g.N - EPD));
+                } else {
+                    union { int32_t v; T e[EPD]; } u;
+                    const T* rowp = B + (int64_t)gk * g.ldb;
+#pragma unroll
+                    for (int e = 0; e < EPD; ++e) u.e[e] = (gk < g.K && nc + e < g.N) ? rowp[nc + e] : T(0);
+                    r.bd[q] = u.v;
+                }
+            }
+        }
+    }
+
+    __device__ static __forceinline__ void store_regs(TG_LDS char* slot, const Staged& r) {
+        const int tid = threadIdx.x;
+        if constexpr (WIDE) {
+#pragma unroll
+            for (int q = 0; q < A_PER; ++q) {
+                const int p = q * NT + tid;
+                const int row = p / CA, c = p % CA;
+                *reinterpret_cast<TG_LDS i32x4*>(slot + row * KB + a_chunk(row, c) * 16) = r.a[q];
+            }
+#pragma unroll
+            for (int q = 0; q < B_PER; ++q) {
+                const int p = q * NT + tid;
+                const int k = p / CB, c = p % CB;
+                *reinterpret_cast<TG_LDS i32x4*>(slot + A_BYTES + k * NB + b_chunk(k, c) * 16) = r.b[q];
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < A_DW; ++q)
+                *reinterpret_cast<TG_LDS int32_t*>(slot + (q * NT + tid) * 4) = r.ad[q];
+#pragma unroll
+            for (int q = 0; q < B_DW; ++q)
+                *reinterpret_cast<TG_LDS int32_t*>(slot + A_BYTES + (q * NT + tid) * 4) = r.bd[q];
+        }
+    }
+
+    // Direct global->LDS copy of slice k0 into `slot`.  Lane l of each
+    // instruction lands at (wave base + 16 l), so the XOR layout is produced
+    // by choosing which global chunk each lane fetches.
+    __device__ static __forceinline__ void issue_direct(TG_LDS char* slot, const GemmArgs& g, int m0,
+                                                        int n0, int k0, int wave) {
+        const T* A = static_cast<const T*>(g.A);
+        const T* B = static_cast<const T*>(g.B);
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int q = 0; q < A_PER; ++q) {
+            const int p = q * NT + tid;
+            const int row = p / CA, pc = p % CA;
+            const int c = a_chunk(row, pc);  // XOR is its own inverse
+            const T* src = A + (int64_t)min(m0 + row, g.M - 1) * g.lda + k0 + c * CE;
+            __builtin_amdgcn_global_load_lds(src, slot + (q * NT + wave * 64) * 16, 16, 0, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < B_PER; ++q) {
+            const int p = q * NT + tid;
+            const int k = p / CB, pc = p % CB;
+            const int c = b_chunk(k, pc);
+            const T* src = B + (int64_t)(k0 + k) * g.ldb + min(n0 + c * CE, g.N - CE);
+            __builtin_amdgcn_global_load_lds(src, slot + A_BYTES + (q * NT + wave * 64) * 16, 16, 0, 0);
+        }
+    }
+
+    // ---- fragments -----------------------------------------------------------
+    // A fragment of 32 x 32 tile row block at `row0`, K step s: lane l holds
+    // row row0 + l%32, bytes [16 (l/32), +16) of the step's 32-byte K span.
+    __device__ static __forceinline__ i32x4 read_a(const TG_LDS char* slot, int row0, int s, int lane) {
+        const int row = row0 + (lane & 31);
+        const int c = 2 * s + (lane >> 5);
+        if constexpr (WIDE) {
+            return *reinterpret_cast<const TG_LDS i32x4*>(slot + row * KB + a_chunk(row, c) * 16);
+        } else {
+            const volatile TG_LDS int32_t* p =
+                reinterpret_cast<const volatile TG_LDS int32_t*>(slot + row * KB + c * 16);
+            return i32x4{p[0], p[1], p[2], p[3]};
+        }
+    }
+
+    // B fragment of the 32-column block at `col0`, K step s: lane l holds
+    // column col0 + l%32 and K rows s*MK + (MK/2)(l/32) + e.  Transposing
+    // reads: in each 16-lane group, input lane j points at row kb + j/(8/ESZ)
+    // and 8 bytes of columns; output lane i receives column nb + i of 8/ESZ
+    // consecutive rows.
+    __device__ static __forceinline__ i32x4 read_b(const TG_LDS char* bslot, int col0, int s, int lane) {
+        if constexpr (WIDE) {
+            const int grp = lane >> 4, j = lane & 15;
+            const int nb = col0 + 16 * (grp & 1);
+            if constexpr (ESZ == 2) {
+                const int kb = s * 16 + 8 * (grp >> 1);
+                const int row0 = kb + (j >> 2);
+                const int byte = (nb + 4 * (j & 3)) * 2;
+                const int c = byte >> 4, w = byte & 15;
+                const TG_LDS char* p0 = bslot + row0 * NB + b_chunk(row0, c) * 16 + w;
+                const TG_LDS char* p1 = bslot + (row0 + 4) * NB + b_chunk(row0 + 4, c) * 16 + w;
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (TG_LDS i16x4*)(p0));
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (TG_LDS i16x4*)(p1));
+                const i32x2 l2 = __builtin_bit_cast(i32x2, lo);
+                const i32x2 h2 = __builtin_bit_cast(i32x2, hi);
+                return i32x4{l2.x, l2.y, h2.x, h2.y};
+            } else {
+                const int kb = s * 32 + 16 * (grp >> 1);
+                const int row0 = kb + (j >> 1);
+                const int byte = nb + 8 * (j & 1);
+                const int c = byte >> 4, w = byte & 15;
+                const TG_LDS char* p0 = bslot + row0 * NB + b_chunk(row0, c) * 16 + w;
+                const TG_LDS char* p1 = bslot + (row0 + 8) * NB + b_chunk(row0 + 8, c) * 16 + w;
+                const i32x2 lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((TG_LDS i32x2*)(p0));
+                const i32x2 hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((TG_LDS i32x2*)(p1));
+                return i32x4{lo.x, lo.y, hi.x, hi.y};
+            }
+        } else {
+            constexpr int PER = 16 / ESZ;  // K values per lane
+            union { i32x4 v; T e[PER]; } u;
+            const int col = col0 + (lane & 31);
+            const int kb = s * Tr::MK + PER * (lane >> 5);
+            const volatile TG_LDS T* base = reinterpret_cast<const volatile TG_LDS T*>(bslot);
+#pragma unroll
+            for (int e = 0; e < PER; ++e) u.e[e] = base[(kb + e) * BN + col];
+            return u.v;
+        }
+    }
+
+    // Multiply one slice held in `slot` into the accumulators.
+    __device__ static __forceinline__ void compute(const TG_LDS char* slot, Acc (&acc)[FM][FN],
+                                                   int wm0, int wn0, int lane) {
+        const TG_LDS char* bslot = slot + A_BYTES;
+#pragma unroll
+        for (int s = 0; s < KSUB; ++s) {
+            if constexpr (FRAG == FR_REUSE) {
+                i32x4 a[FM], b[FN];
+#pragma unroll
+                for (int i = 0; i < FM; ++i) a[i] = read_a(slot, wm0 + 32 * i, s, lane);
+#pragma unroll
+                for (int j = 0; j < FN; ++j) b[j] = read_b(bslot, wn0 + 32 * j, s, lane);
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) acc[i][j] = Tr::mma(a[i], b[j], acc[i][j]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) {
+                        const i32x4 a = read_a(slot, wm0 + 32 * i, s, lane);
+                        const i32x4 b = read_b(bslot, wn0 + 32 * j, s, lane);
+                        acc[i][j] = Tr::mma(a, b, acc[i][j]);
+                    }
+            }
+        }
+    }
+
+    // Wait until this wave's copies of slice t are in LDS (`ahead` later
+    // slices may stay in flight), then barrier.
+    __device__ static __forceinline__ void wait_slice(int ahead) {
+        if constexpr (STAGES >= 4) {
+            if (ahead >= 2) { wait_vm_then_barrier<2 * N_LD>(); return; }
+        }
+        if constexpr (STAGES >= 3) {
+            if (ahead >= 1) { wait_vm_then_barrier<N_LD>(); return; }
+        }
+        wait_vm_then_barrier<0>();
+    }
+
+    __device__ static void run(const GemmArgs& g) {
+        __shared__ __attribute__((aligned(1024))) char smem_raw[LDS_BYTES];
+        TG_LDS char* smem = (TG_LDS char*)(smem_raw);
+
+        const int lane = lane_id();
+        const int wave = wave_id();
+        int tm, tn;
+        tile_of_workgroup(g, tm, tn);
+        const int m0 = tm * BM, n0 = tn * BN;
+        const int wm0 = (wave / WAVES_N) * WTM;
+        const int wn0 = (wave % WAVES_N) * WTN;
+
+        Acc acc[FM][FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+
+        const int tiles = (g.K + BK - 1) / BK;
+        const int full = g.K / BK;  // slices with no K tail
+        const bool ga = g.a_guard != 0, gb = g.b_guard != 0;
+
+        if constexpr (DIRECT) {
+            // Prologue: slices 0 .. STAGES-2 in flight.
+#pragma unroll
+            for (int s = 0; s < STAGES - 1; ++s)
+                if (s < full) issue_direct(smem + s * SLOT, g, m0, n0, s * BK, wave);
+            for (int t = 0; t < full; ++t) {
+                wait_slice(min(STAGES - 2, full - 1 - t));
+                const int nxt = t + STAGES - 1;
+                if (nxt < full) issue_direct(smem + (nxt % STAGES) * SLOT, g, m0, n0, nxt * BK, wave);
+                compute(smem + (t % STAGES) * SLOT, acc, wm0, wn0, lane);
+            }
+            if (full < tiles) {
+                // K tail: element loads with zero fill into the next slot
+                // (no copy is in flight and nobody reads that slot any more).
+                Staged r;
+                load_regs(r, g, m0, n0, full * BK, true, true);
+                store_regs(smem + (full % STAGES) * SLOT, r);
+                wait_lds_then_barrier();
+                compute(smem + (full % STAGES) * SLOT, acc, wm0, wn0, lane);
+            }
+        } else if constexpr (STAGES == 1) {
+            for (int t = 0; t < tiles; ++t) {
+                const bool tail = t >= full;
+                Staged r;
+                load_regs(r, g, m0, n0, t * BK, ga || tail, gb || tail);
+                store_regs(smem, r);
+                wait_lds_then_barrier();
+                compute(smem, acc, wm0, wn0, lane);
+                wait_lds_then_barrier();  // all reads done before the next overwrite
+            }
+        } else {
+            // Register-staged double buffer: one barrier per slice.
+            if (tiles > 0) {
+                Staged r;
+                load_regs(r, g, m0, n0, 0, ga || full == 0, gb || full == 0);
+                store_regs(smem, r);
+                wait_lds_then_barrier();
+            }
+            for (int t = 0; t < tiles; ++t) {
+                const int nxt = t + 1;
+                Staged r;
+                if (nxt < tiles) load_regs(r, g, m0, n0, nxt * BK, ga || nxt >= full, gb || nxt >= full);
+                compute(smem + (t & 1) * SLOT, acc, wm0, wn0, lane);
+                if (nxt < tiles) store_regs(smem + (nxt & 1) * SLOT, r);
+                wait_lds_then_barrier();
+            }
+        }
+
+        // Epilogue: accumulators -> C.  Register r of tile (i, j) in lane l is
+        // row 8 (r/4) + 4 (l/32) + r%4, column l%32 of that 32 x 32 tile.
+        Out* C = static_cast<Out*>(g.C);
+        const bool inside = (m0 + BM <= g.M) && (n0 + BN <= g.N);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = m0 + wm0 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    const int col = n0 + wn0 + 32 * j + (lane & 31);
+                    if (inside || (row < g.M && col < g.N))
+                        C[(int64_t)row * g.ldc + col] = static_cast<Out>(acc[i][j][r]);
+                }
+    }
+};
+
+}  // namespace tg

@@ -1,0 +1,378 @@
+// libtgemm host side: plans, variant registry, launch (the C ABI of
+// include/tgemm.h).
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "tg_args.hpp"
+#include "tgemm.h"
+
+using tg::KernelEntry;
+
+struct tgemm_plan {
+    int64_t M, N, K, lda, ldb, ldc;
+    int32_t dtype;
+    const KernelEntry* entry;     // what runs when the operands allow it
+    const KernelEntry* fallback;  // register-staged entry used when an operand needs the guarded loader
+    int32_t wg_group;
+    int32_t a_guard, b_guard;     // leading-dimension based (pointer alignment is checked per run)
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+void set_err(const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+}
+
+std::vector<KernelEntry> g_reg[3];
+std::once_flag g_reg_once;
+
+void add_entry(const KernelEntry& e) { g_reg[e.dtype].push_back(e); }
+
+void init_registry() {
+    std::call_once(g_reg_once, [] {
+        tg::register_f32(add_entry);
+        tg::register_bf16(add_entry);
+        tg::register_i8(add_entry);
+    });
+}
+
+int elem_size(int dtype) { return dtype == TGEMM_F32 ? 4 : dtype == TGEMM_BF16 ? 2 : 1; }
+
+// Bytes moved per 16-byte chunk / per narrow access by an entry's loader.
+int access_bytes(const KernelEntry& e) {
+    if (e.family == tg::FAM_NAIVE) return 0;
+    return e.access == tg::AC_WIDE ? 16 : 4;
+}
+
+// Leading-dimension checks: can every row of the operand be read with
+// `bytes`-wide aligned accesses?  (Pointer alignment is checked at run time.)
+void ld_guards(const KernelEntry& e, int64_t N, int64_t lda, int64_t ldb, int32_t* ga, int32_t* gb) {
+    const int bytes = access_bytes(e);
+    if (bytes == 0) {
+        *ga = *gb = 0;
+        return;
+    }
+    const int esz = elem_size(e.dtype);
+    const int per = bytes / esz;  // elements per access
+    *ga = (lda * esz) % bytes != 0;
+    *gb = (ldb * esz) % bytes != 0 || N % per != 0 || N < per;
+}
+
+bool field_ok(int want, int have) { return want == 0 || want == have; }
+
+bool matches(const KernelEntry& e, const tgemm_variant& v) {
+    if (v.kernel == TGEMM_KERNEL_NAIVE && e.family != tg::FAM_NAIVE) return false;
+    if (v.kernel == TGEMM_KERNEL_TILED && e.family != tg::FAM_TILED) return false;
+    return field_ok(v.tile_m, e.bm) && field_ok(v.tile_n, e.bn) && field_ok(v.tile_k, e.bk) &&
+           field_ok(v.stages, e.stages) && field_ok(v.loader, e.loader) &&
+           field_ok(v.lds_layout, e.layout) && field_ok(v.access, e.access) && field_ok(v.frag, e.frag);
+}
+
+const KernelEntry* find_entry(int dtype, const tgemm_variant& v) {
+    for (const KernelEntry& e : g_reg[dtype])
+        if (matches(e, v)) return &e;
+    return nullptr;
+}
+
+// Default choice for a shape: the largest tile that still gives the GPU
+// (256 compute units) at least half a workgroup per unit, else 128 x 128.
+const KernelEntry* default_entry(int dtype, int64_t M, int64_t N) {
+    tgemm_variant v{};
+    v.kernel = TGEMM_KERNEL_TILED;
+    if (dtype == TGEMM_F32) return find_entry(dtype, v);
+    const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
+    v.loader = TGEMM_LOADER_DIRECT;
+    v.access = TGEMM_ACCESS_WIDE;
+    v.frag = TGEMM_FRAG_REUSE;
+    v.lds_layout = TGEMM_LDS_XOR;
+    if (big >= 128) {
+        v.tile_m = 256;
+        v.tile_n = 256;
+        v.stages = 2;
+    } else {
+        v.tile_m = 128;
+        v.tile_n = 128;
+        v.stages = 3;
+    }
+    return find_entry(dtype, v);
+}
+
+// A register-staged entry with the same tile (else any wide one) for
+// operands that need guarded loads.
+const KernelEntry* guard_capable(const KernelEntry* e) {
+    if (e->guard_ok) return e;
+    for (const KernelEntry& c : g_reg[e->dtype])
+        if (c.guard_ok && c.family == e->family && c.bm == e->bm && c.bn == e->bn && c.bk == e->bk &&
+            c.access == tg::AC_WIDE && c.stages == 2)
+            return &c;
+    for (const KernelEntry& c : g_reg[e->dtype])
+        if (c.guard_ok && c.family == tg::FAM_TILED && c.access == tg::AC_WIDE && c.stages == 2) return &c;
+    return nullptr;
+}
+
+void entry_to_variant(const KernelEntry& e, int32_t wg_group, tgemm_variant* v) {
+    memset(v, 0, sizeof *v);
+    v->kernel = e.family == tg::FAM_NAIVE ? TGEMM_KERNEL_NAIVE : TGEMM_KERNEL_TILED;
+    v->tile_m = e.bm;
+    v->tile_n = e.bn;
+    v->tile_k = e.bk;
+    v->stages = e.stages;
+    v->loader = e.loader;
+    v->lds_layout = e.layout;
+    v->access = e.access;
+    v->frag = e.frag;
+    v->wg_group = wg_group;
+}
+
+// Per-device gfx950 check, cached.
+std::mutex g_arch_mu;
+int g_arch_ok[64];  // 0 unknown, 1 gfx950, -1 other
+
+int check_arch() {
+    int dev = 0;
+    const hipError_t gerr = hipGetDevice(&dev);
+    if (gerr != hipSuccess) {
+        set_err("hipGetDevice failed: %s", hipGetErrorString(gerr));
+        return TGEMM_E_HIP;
+    }
+    if (dev < 0 || dev >= 64) {
+        set_err("device index %d out of range", dev);
+        return TGEMM_E_ARCH;
+    }
+    std::lock_guard<std::mutex> lk(g_arch_mu);
+    if (g_arch_ok[dev] == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            set_err("hipGetDeviceProperties failed");
+            return TGEMM_E_HIP;
+        }
+        g_arch_ok[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+        if (g_arch_ok[dev] < 0) set_err("device %d is %s, libtgemm is built for gfx950 only", dev, prop.gcnArchName);
+    }
+    return g_arch_ok[dev] > 0 ? TGEMM_OK : TGEMM_E_ARCH;
+}
+
+__global__ void zero_fill_4byte(uint32_t* C, int M, int N, int64_t ldc) {
+    const int64_t total = (int64_t)M * N;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = i / N, c = i - r * N;
+        C[r * ldc + c] = 0u;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tgemm_version(void) { return "tgemm 0.1 (gfx950)"; }
+
+const char* tgemm_last_error(void) { return g_err.c_str(); }
+
+tgemm_plan* gemm_plan_variant(int64_t M, int64_t N, int64_t K, int32_t dtype, int64_t lda, int64_t ldb,
+                              int64_t ldc, const tgemm_variant* variant) {
+    init_registry();
+    if (dtype != TGEMM_F32 && dtype != TGEMM_BF16 && dtype != TGEMM_I8) {
+        set_err("unknown dtype %d", dtype);
+        return nullptr;
+    }
+    if (M < 0 || N < 0 || K < 0) {
+        set_err("negative size M=%lld N=%lld K=%lld", (long long)M, (long long)N, (long long)K);
+        return nullptr;
+    }
+    if (M > INT_MAX || N > INT_MAX || K > INT_MAX) {
+        set_err("sizes must be below 2^31");
+        return nullptr;
+    }
+    if (lda < 1 || ldb < 1 || ldc < 1 || lda < K || ldb < N || ldc < N) {
+        set_err("leading dimensions too small: lda=%lld (K=%lld) ldb=%lld (N=%lld) ldc=%lld (N=%lld)",
+                (long long)lda, (long long)K, (long long)ldb, (long long)N, (long long)ldc, (long long)N);
+        return nullptr;
+    }
+    if (dtype == TGEMM_I8 && K > 131072) {
+        set_err("int8: K=%lld may overflow the int32 accumulator (K <= 131072)", (long long)K);
+        return nullptr;
+    }
+    tgemm_variant v{};
+    if (variant) v = *variant;
+    if (v.wg_group < -1) {
+        set_err("wg_group must be -1, 0 or positive");
+        return nullptr;
+    }
+    const KernelEntry* e = nullptr;
+    if (v.kernel == TGEMM_KERNEL_AUTO && v.tile_m == 0 && v.tile_n == 0 && v.tile_k == 0 && v.stages == 0 &&
+        v.loader == 0 && v.lds_layout == 0 && v.access == 0 && v.frag == 0) {
+        e = default_entry(dtype, M, N);
+    } else {
+        e = find_entry(dtype, v);
+    }
+    if (!e) {
+        set_err("no compiled variant matches the request (see gemm_variant_get)");
+        return nullptr;
+    }
+    int32_t ga = 0, gb = 0;
+    ld_guards(*e, N, lda, ldb, &ga, &gb);
+    const KernelEntry* fb = guard_capable(e);
+    if ((ga || gb) && !e->guard_ok) {
+        if (!fb) {
+            set_err("variant %s cannot load unaligned operands and has no fallback", e->name);
+            return nullptr;
+        }
+        e = fb;
+        ld_guards(*e, N, lda, ldb, &ga, &gb);
+    }
+    const int64_t tiles_m = (M + e->bm - 1) / e->bm, tiles_n = (N + e->bn - 1) / e->bn;
+    if (tiles_m * tiles_n > INT_MAX) {
+        set_err("too many tiles");
+        return nullptr;
+    }
+    tgemm_plan* p = new tgemm_plan;
+    p->M = M;
+    p->N = N;
+    p->K = K;
+    p->lda = lda;
+    p->ldb = ldb;
+    p->ldc = ldc;
+    p->dtype = dtype;
+    p->entry = e;
+    p->fallback = fb ? fb : e;
+    p->wg_group = v.wg_group == 0 ? (e->family == tg::FAM_NAIVE ? -1 : 4) : v.wg_group;
+    p->a_guard = ga;
+    p->b_guard = gb;
+    g_err.clear();
+    return p;
+}
+
+tgemm_plan* gemm_plan(int64_t M, int64_t N, int64_t K, int32_t dtype, int64_t lda, int64_t ldb,
+                      int64_t ldc) {
+    return gemm_plan_variant(M, N, K, dtype, lda, ldb, ldc, nullptr);
+}
+
+void gemm_destroy(tgemm_plan* plan) { delete plan; }
+
+int gemm_run(const tgemm_plan* p, const void* A, const void* B, void* C, void* stream) {
+    if (!p) {
+        set_err("NULL plan");
+        return TGEMM_E_NULL;
+    }
+    if (p->M == 0 || p->N == 0) return TGEMM_OK;
+    if (!C || (p->K > 0 && (!A || !B))) {
+        set_err("NULL matrix pointer");
+        return TGEMM_E_NULL;
+    }
+    const int esz = elem_size(p->dtype);
+    if (((uintptr_t)A % esz) || ((uintptr_t)B % esz) || ((uintptr_t)C % 4)) {
+        set_err("pointer not aligned to its element size");
+        return TGEMM_E_ALIGN;
+    }
+    int rc = check_arch();
+    if (rc != TGEMM_OK) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (p->K == 0) {
+        const int64_t total = p->M * p->N;
+        const int blocks = (int)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
+        hipLaunchKernelGGL(zero_fill_4byte, dim3(blocks), dim3(256), 0, s, static_cast<uint32_t*>(C),
+                           (int)p->M, (int)p->N, p->ldc);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess) {
+            set_err("launch failed: %s", hipGetErrorString(err));
+            return TGEMM_E_HIP;
+        }
+        return TGEMM_OK;
+    }
+    const KernelEntry* e = p->entry;
+    int32_t ga = p->a_guard, gb = p->b_guard;
+    const int bytes = access_bytes(*e);
+    if (bytes) {
+        if ((uintptr_t)A % bytes) ga = 1;
+        if ((uintptr_t)B % bytes) gb = 1;
+    }
+    if ((ga || gb) && !e->guard_ok) {
+        e = p->fallback;
+        int32_t fa = 0, fbg = 0;
+        ld_guards(*e, p->N, p->lda, p->ldb, &fa, &fbg);
+        const int fbytes = access_bytes(*e);
+        ga = fa || (fbytes && (uintptr_t)A % fbytes);
+        gb = fbg || (fbytes && (uintptr_t)B % fbytes);
+    }
+    tg::GemmArgs g;
+    g.A = A;
+    g.B = B;
+    g.C = C;
+    g.M = (int32_t)p->M;
+    g.N = (int32_t)p->N;
+    g.K = (int32_t)p->K;
+    g.tiles_m = (int32_t)((p->M + e->bm - 1) / e->bm);
+    g.tiles_n = (int32_t)((p->N + e->bn - 1) / e->bn);
+    g.lda = p->lda;
+    g.ldb = p->ldb;
+    g.ldc = p->ldc;
+    g.wg_group = p->wg_group;
+    g.a_guard = ga;
+    g.b_guard = gb;
+    void* args[] = {&g};
+    const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(e->fn),
+                                           dim3((unsigned)(g.tiles_m * g.tiles_n)), dim3(e->threads), args, 0, s);
+    if (err != hipSuccess) {
+        set_err("launch of %s failed: %s", e->name, hipGetErrorString(err));
+        return TGEMM_E_HIP;
+    }
+    return TGEMM_OK;
+}
+
+int gemm_plan_get_info(const tgemm_plan* p, tgemm_plan_info* info) {
+    if (!p || !info) {
+        set_err("NULL plan or info");
+        return TGEMM_E_NULL;
+    }
+    memset(info, 0, sizeof *info);
+    const KernelEntry& e = *p->entry;
+    info->M = p->M;
+    info->N = p->N;
+    info->K = p->K;
+    info->lda = p->lda;
+    info->ldb = p->ldb;
+    info->ldc = p->ldc;
+    info->dtype = p->dtype;
+    entry_to_variant(e, p->wg_group, &info->variant);
+    info->grid = (int32_t)(((p->M + e.bm - 1) / e.bm) * ((p->N + e.bn - 1) / e.bn));
+    info->threads = e.threads;
+    info->lds_bytes = e.lds_bytes;
+    info->loads_per_stage = e.loads_per_stage;
+    info->a_guarded = p->a_guard;
+    info->b_guarded = p->b_guard;
+    snprintf(info->name, sizeof info->name, "%s", e.name);
+    return TGEMM_OK;
+}
+
+int gemm_variant_count(int32_t dtype) {
+    init_registry();
+    if (dtype < 0 || dtype > 2) return 0;
+    return (int)g_reg[dtype].size();
+}
+
+int gemm_variant_get(int32_t dtype, int32_t index, tgemm_variant* out) {
+    init_registry();
+    if (dtype < 0 || dtype > 2 || !out || index < 0 || index >= (int32_t)g_reg[dtype].size()) {
+        set_err("bad dtype or index");
+        return TGEMM_E_ARG;
+    }
+    entry_to_variant(g_reg[dtype][index], 0, out);
+    return TGEMM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,220 @@
+"""Python binding of libtgemm (argument marshalling only).
+
+Every step of the product runs in the HIP kernels of ``libtgemm.so``; this
+module checks tensor arguments, caches plans and calls the C ABI of
+``include/tgemm.h`` with raw device pointers and torch's current stream.
+There is no CPU fallback: if the library is missing, importing this module
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtgemm.so")
+
+# dtype codes of the C ABI
+F32, BF16, I8 = 0, 1, 2
+DTYPE_NAMES = {F32: "f32", BF16: "bf16", I8: "i8"}
+
+OK = 0
+ERRORS = {-1: "TGEMM_E_ARG", -2: "TGEMM_E_NULL", -3: "TGEMM_E_ALIGN", -4: "TGEMM_E_ARCH",
+          -5: "TGEMM_E_VARIANT", -6: "TGEMM_E_HIP"}
+
+# variant field values (include/tgemm.h)
+KERNEL_AUTO, KERNEL_NAIVE, KERNEL_TILED = 0, 1, 2
+LOADER_VGPR, LOADER_DIRECT = 1, 2
+LDS_PLAIN, LDS_XOR = 1, 2
+ACCESS_WIDE, ACCESS_NARROW = 1, 2
+FRAG_REUSE, FRAG_PER_MMA = 1, 2
+ORDER_ROW_MAJOR = -1
+
+
+class Variant(ctypes.Structure):
+    """Mirror of ``tgemm_variant``; zero fields mean "default"."""
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "kernel", "tile_m", "tile_n", "tile_k", "stages", "loader", "lds_layout", "access", "frag",
+        "wg_group")]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+    def __repr__(self):
+        return "Variant(%s)" % ", ".join("%s=%d" % kv for kv in self.as_dict().items() if kv[1])
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("lda", ctypes.c_int64), ("ldb", ctypes.c_int64), ("ldc", ctypes.c_int64),
+                ("dtype", ctypes.c_int32), ("variant", Variant), ("grid", ctypes.c_int32),
+                ("threads", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
+                ("loads_per_stage", ctypes.c_int32), ("a_guarded", ctypes.c_int32),
+                ("b_guarded", ctypes.c_int32), ("name", ctypes.c_char * 96)]
+
+
+EXPORTS = ("gemm_plan", "gemm_plan_variant", "gemm_run", "gemm_destroy", "tgemm_last_error",
+           "gemm_plan_get_info", "gemm_variant_count", "gemm_variant_get", "tgemm_version")
+
+
+def _load():
+    # Load torch first: its HIP runtime (libamdhip64, SONAME libamdhip64.so.7)
+    # is then the one libtgemm binds to, so device memory, streams and the
+    # kernel launches all belong to one runtime in this process.
+    import torch  # noqa: F401
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libtgemm.so is not built (%s); run "
+                          "`python -m tiled_software_pipelined_amd.build`" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+    lib.gemm_plan.argtypes = [i64, i64, i64, i32, i64, i64, i64]
+    lib.gemm_plan.restype = vp
+    lib.gemm_plan_variant.argtypes = [i64, i64, i64, i32, i64, i64, i64, ctypes.POINTER(Variant)]
+    lib.gemm_plan_variant.restype = vp
+    lib.gemm_run.argtypes = [vp, vp, vp, vp, vp]
+    lib.gemm_run.restype = ctypes.c_int
+    lib.gemm_destroy.argtypes = [vp]
+    lib.gemm_destroy.restype = None
+    lib.tgemm_last_error.argtypes = []
+    lib.tgemm_last_error.restype = ctypes.c_char_p
+    lib.gemm_plan_get_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]
+    lib.gemm_plan_get_info.restype = ctypes.c_int
+    lib.gemm_variant_count.argtypes = [i32]
+    lib.gemm_variant_count.restype = ctypes.c_int
+    lib.gemm_variant_get.argtypes = [i32, i32, ctypes.POINTER(Variant)]
+    lib.gemm_variant_get.restype = ctypes.c_int
+    lib.tgemm_version.argtypes = []
+    lib.tgemm_version.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+class TgemmError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__("%s: %s" % (ERRORS.get(code, code), msg))
+        self.code = code
+
+
+def last_error() -> str:
+    return _lib.tgemm_last_error().decode()
+
+
+def version() -> str:
+    return _lib.tgemm_version().decode()
+
+
+def variants(dtype: int):
+    """The variants compiled into the library for a dtype code."""
+    out = []
+    for i in range(_lib.gemm_variant_count(dtype)):
+        v = Variant()
+        if _lib.gemm_variant_get(dtype, i, ctypes.byref(v)) != OK:
+            raise TgemmError(-1, last_error())
+        out.append(v)
+    return out
+
+
+class Plan:
+    """A ``tgemm_plan`` (host metadata only; never touches the GPU)."""
+
+    def __init__(self, M, N, K, dtype, lda=None, ldb=None, ldc=None, variant: Variant | None = None):
+        lda = K if lda is None else lda
+        ldb = N if ldb is None else ldb
+        ldc = N if ldc is None else ldc
+        self.M, self.N, self.K, self.dtype = int(M), int(N), int(K), int(dtype)
+        self.lda, self.ldb, self.ldc = int(lda), int(ldb), int(ldc)
+        if variant is None:
+            h = _lib.gemm_plan(M, N, K, dtype, lda, ldb, ldc)
+        else:
+            h = _lib.gemm_plan_variant(M, N, K, dtype, lda, ldb, ldc, ctypes.byref(variant))
+        if not h:
+            raise TgemmError(-1, last_error())
+        self._h = h
+
+    def info(self) -> PlanInfo:
+        info = PlanInfo()
+        rc = _lib.gemm_plan_get_info(self._h, ctypes.byref(info))
+        if rc != OK:
+            raise TgemmError(rc, last_error())
+        return info
+
+    @property
+    def name(self) -> str:
+        return self.info().name.decode()
+
+    def run_ptr(self, A: int, B: int, C: int, stream: int = 0) -> None:
+        """Enqueue on raw device pointers (the caller keeps the buffers alive)."""
+        rc = _lib.gemm_run(self._h, ctypes.c_void_p(A), ctypes.c_void_p(B), ctypes.c_void_p(C),
+                           ctypes.c_void_p(stream))
+        if rc != OK:
+            raise TgemmError(rc, last_error())
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            _lib.gemm_destroy(h)
+            self._h = None
+
+
+_cache: dict = {}
+_cache_lock = threading.Lock()
+
+
+def _torch_dtype_code(t):
+    import torch
+    m = {torch.float32: F32, torch.bfloat16: BF16, torch.int8: I8}
+    if t.dtype not in m:
+        raise TypeError("unsupported dtype %s (float32, bfloat16, int8)" % t.dtype)
+    return m[t.dtype]
+
+
+def _ld(t, name):
+    if t.dim() != 2:
+        raise ValueError("%s must be 2-D" % name)
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError("%s must be row-major with unit column stride" % name)
+    return max(int(t.stride(0)), int(t.shape[1]), 1) if t.shape[0] > 1 else max(int(t.shape[1]), 1)
+
+
+def plan_for(M, N, K, dtype, lda, ldb, ldc, variant: Variant | None = None) -> Plan:
+    key = (M, N, K, dtype, lda, ldb, ldc, None if variant is None else tuple(variant.as_dict().items()))
+    with _cache_lock:
+        p = _cache.get(key)
+        if p is None:
+            p = Plan(M, N, K, dtype, lda, ldb, ldc, variant)
+            _cache[key] = p
+    return p
+
+
+def gemm(A, B, out=None, variant: Variant | None = None):
+    """C = A @ B on the current CUDA/HIP stream.
+
+    A: (M, K), B: (K, N) torch tensors on the GPU, both float32, both bfloat16
+    or both int8, row-major (row stride may exceed the row length).  Returns
+    C (M, N): float32 for float32/bfloat16 inputs, int32 for int8 inputs.
+    ``out`` may be a preallocated row-major C (its row stride is used as ldc).
+    """
+    import torch
+    if not (A.is_cuda and B.is_cuda):
+        raise ValueError("A and B must be GPU tensors")
+    if A.dtype != B.dtype:
+        raise TypeError("A and B must have the same dtype")
+    code = _torch_dtype_code(A)
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ: %d vs %d" % (K, K2))
+    out_dtype = torch.int32 if code == I8 else torch.float32
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=A.device)
+    elif out.dtype != out_dtype or tuple(out.shape) != (M, N) or out.device != A.device:
+        raise ValueError("out must be a %s tensor of shape (%d, %d) on %s" % (out_dtype, M, N, A.device))
+    lda, ldb, ldc = _ld(A, "A"), _ld(B, "B"), _ld(out, "out")
+    p = plan_for(M, N, K, code, lda, ldb, ldc, variant)
+    stream = torch.cuda.current_stream(A.device).cuda_stream
+    with torch.cuda.device(A.device):
+        p.run_ptr(A.data_ptr(), B.data_ptr(), out.data_ptr(), stream)
+    return out
