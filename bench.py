@@ -106,6 +106,9 @@ def main():
     ap.add_argument("--ladder", action="store_true")
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
+                    help="also run a plain device copy of MIB MiB (a reference for the HBM "
+                         "byte counters when profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this GEMM path runs on one GPU only (--gpus %d requested); "
@@ -148,6 +151,15 @@ def main():
                               "kernel": lib.plan_for(sw.M, sw.N, sw.K, lib.BF16, sw.K, sw.N, sw.N).name}),
                   flush=True)
             del a, b, c
+
+    if args.calib_copy:
+        nbytes = args.calib_copy << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     variant = parse_variant(args.variant, lib)
     per, wall = time_plan(lib, torch, w, A, B, C, variant, args.steps, args.warmup)

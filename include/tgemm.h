@@ -105,6 +105,8 @@ typedef struct tgemm_variant {
     int32_t access;     /* TGEMM_ACCESS_* */
     int32_t frag;       /* TGEMM_FRAG_* */
     int32_t wg_group;   /* TGEMM_ORDER_ROW_MAJOR, or g >= 1: XCD-aware order grouped by g tile rows */
+    int32_t waves_m;    /* waves per workgroup along M */
+    int32_t waves_n;    /* waves per workgroup along N */
 } tgemm_variant;
 
 typedef struct tgemm_plan tgemm_plan;

@@ -75,7 +75,8 @@ def test_variants_enumerate(dtype):
     for v in vs:
         p = tl.Plan(512, 512, 512, dtype, variant=v)
         got = p.info().variant
-        for f in ("kernel", "tile_m", "tile_n", "tile_k", "stages", "loader", "lds_layout", "access", "frag"):
+        for f in ("kernel", "tile_m", "tile_n", "tile_k", "stages", "loader", "lds_layout", "access", "frag",
+                  "waves_m", "waves_n"):
             assert getattr(got, f) == getattr(v, f)
 
 

@@ -37,6 +37,7 @@ struct KernelEntry {
     int layout;      // Layout
     int access;      // Access
     int frag;        // Frag
+    int wm, wn;      // wave grid
     int threads;     // threads per workgroup
     int lds_bytes;   // static LDS per workgroup
     int loads_per_stage;  // global->LDS instructions per wave per stage

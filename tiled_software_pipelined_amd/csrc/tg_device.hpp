@@ -42,6 +42,30 @@ __device__ __forceinline__ void wait_all_then_barrier() {
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// One 16-byte-per-lane copy global -> LDS that bypasses the registers
+// (global_load_lds_dwordx4).  Lane l reads `base + voff` and its 16 bytes
+// land at LDS byte `lds + 16 l`; `lds` and `base` must be wave-uniform.
+// Issued from asm so that the compiler does not treat the LDS write as
+// aliasing every later LDS read (it would otherwise wait for the copy to
+// finish before each read and serialise the pipeline); completion is tracked
+// explicitly with wait_vm_then_barrier.  M0 is written here: the kernels that
+// use this issue every LDS copy through it and nothing else of theirs uses
+// M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void copy16_to_lds(uint32_t lds, uint32_t voff, const void* base) {
+    // make the wave-uniform operands scalar (they are, but the compiler may
+    // not be able to prove it)
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    const uint64_t sb = ((uint64_t)hi << 32) | lo;
+    const uint32_t sl = __builtin_amdgcn_readfirstlane(lds);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(sl), "v"(voff), "s"(sb)
+                 : "m0");
+}
+#pragma clang diagnostic pop
+
 __device__ __forceinline__ int wave_id() {
     return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }

@@ -33,6 +33,8 @@ KernelEntry mfma_entry(int dtype) {
     e.layout = LY;
     e.access = AC;
     e.frag = FR;
+    e.wm = WM;
+    e.wn = WN;
     e.threads = K::NT;
     e.lds_bytes = K::LDS_BYTES;
     e.loads_per_stage = AC == AC_WIDE ? K::N_LD : K::A_DW + K::B_DW;
@@ -59,6 +61,8 @@ KernelEntry naive_entry() {
     e.layout = LY_PLAIN;
     e.access = AC_NARROW;
     e.frag = FR_PER_MMA;
+    e.wm = 4;
+    e.wn = 1;
     e.threads = K::NT;
     e.lds_bytes = 0;
     e.loads_per_stage = 0;
@@ -83,6 +87,8 @@ KernelEntry f32_entry() {
     e.layout = LY_PLAIN;
     e.access = AC_WIDE;
     e.frag = FR_REUSE;
+    e.wm = 2;
+    e.wn = 2;
     e.threads = K::NT;
     e.lds_bytes = K::LDS_BYTES;
     e.loads_per_stage = K::N_LD;

@@ -106,9 +106,14 @@ struct MfmaGemm {
 
     // ---- LDS layout --------------------------------------------------------
     // A: row r of a slice at r*KB; its 16-byte chunks permuted by an XOR so
-    // that the 32 rows read by one 16-byte fragment read spread over the
-    // banks.  Rows that share one 128-byte window use distinct offsets.
-    static constexpr int A_ROWS_PER_WIN = KB >= 128 ? 1 : 128 / KB;
+    // that the rows read by one 16-byte fragment read spread over the banks.
+    // gfx950's LDS serves 64 banks x 4 bytes = one 256-byte window per cycle
+    // (16 lanes of a 16-byte read): the 16 rows such a group reads must land
+    // on 16 distinct 16-byte offsets of that window.  Rows that share one
+    // window differ by their row offset; consecutive windows get distinct
+    // XOR keys.
+    static constexpr int LDS_WINDOW = 256;
+    static constexpr int A_ROWS_PER_WIN = KB >= LDS_WINDOW ? 1 : LDS_WINDOW / KB;
     __device__ static __forceinline__ int a_chunk(int row, int c) {
         if constexpr (XOR) return c ^ ((row / A_ROWS_PER_WIN) & (CA - 1));
         else return c;
@@ -233,30 +238,58 @@ struct MfmaGemm {
         }
     }
 
-    // Direct global->LDS copy of slice k0 into `slot`.  Lane l of each
-    // instruction lands at (wave base + 16 l), so the XOR layout is produced
-    // by choosing which global chunk each lane fetches.
-    __device__ static __forceinline__ void issue_direct(TG_LDS char* slot, const GemmArgs& g, int m0,
-                                                        int n0, int k0, int wave) {
-        const T* A = static_cast<const T*>(g.A);
-        const T* B = static_cast<const T*>(g.B);
+    // Direct global->LDS copies.  Lane l of each instruction lands at
+    // (wave base + 16 l), so the XOR layout is produced by choosing which
+    // global chunk each lane fetches.  The per-lane byte offsets from the
+    // slice's (wave-uniform) base address never change along K, so they are
+    // computed once: A chunk q of this thread sits at row r, logical chunk c
+    // -> r*lda + c*16 bytes from A's slice base (rows past M clamped to the
+    // last row); B chunk q at row k, chunk c -> k*ldb + (column clamped to
+    // the last full chunk) bytes from B's slice base.  The host only picks
+    // this loader when these offsets fit in 32 bits.
+    struct DirectOffsets {
+        uint32_t a[A_PER];
+        uint32_t b[B_PER];
+    };
+
+    __device__ static __forceinline__ void direct_offsets(DirectOffsets& o, const GemmArgs& g, int m0,
+                                                          int n0) {
         const int tid = threadIdx.x;
 #pragma unroll
         for (int q = 0; q < A_PER; ++q) {
             const int p = q * NT + tid;
             const int row = p / CA, pc = p % CA;
             const int c = a_chunk(row, pc);  // XOR is its own inverse
-            const T* src = A + (int64_t)min(m0 + row, g.M - 1) * g.lda + k0 + c * CE;
-            __builtin_amdgcn_global_load_lds(src, slot + (q * NT + wave * 64) * 16, 16, 0, 0);
+            const int r = min(m0 + row, g.M - 1) - m0;
+            o.a[q] = (uint32_t)((int64_t)r * g.lda * ESZ + c * 16);
         }
 #pragma unroll
         for (int q = 0; q < B_PER; ++q) {
             const int p = q * NT + tid;
             const int k = p / CB, pc = p % CB;
             const int c = b_chunk(k, pc);
-            const T* src = B + (int64_t)(k0 + k) * g.ldb + min(n0 + c * CE, g.N - CE);
-            __builtin_amdgcn_global_load_lds(src, slot + A_BYTES + (q * NT + wave * 64) * 16, 16, 0, 0);
+            const int col = min(n0 + c * CE, g.N - CE) - n0;
+            o.b[q] = (uint32_t)((int64_t)k * g.ldb * ESZ + col * ESZ);
         }
+    }
+
+    // Issue copy number i (0 <= i < N_LD) of one slice into `slot`.
+    __device__ static __forceinline__ void issue_direct_one(int i, TG_LDS char* slot, const DirectOffsets& o,
+                                                            const char* abase, const char* bbase,
+                                                            int wave) {
+        const uint32_t lds = (uint32_t)(uintptr_t)slot;
+        if (i < A_PER) {
+            copy16_to_lds(lds + (i * NT + wave * 64) * 16, o.a[i], abase);
+        } else {
+            const int q = i - A_PER;
+            copy16_to_lds(lds + A_BYTES + (q * NT + wave * 64) * 16, o.b[q], bbase);
+        }
+    }
+
+    __device__ static __forceinline__ void issue_direct(TG_LDS char* slot, const DirectOffsets& o,
+                                                        const char* abase, const char* bbase, int wave) {
+#pragma unroll
+        for (int i = 0; i < N_LD; ++i) issue_direct_one(i, slot, o, abase, bbase, wave);
     }
 
     // ---- fragments -----------------------------------------------------------
@@ -279,35 +312,32 @@ struct MfmaGemm {
     // reads: in each 16-lane group, input lane j points at row kb + j/(8/ESZ)
     // and 8 bytes of columns; output lane i receives column nb + i of 8/ESZ
     // consecutive rows.
+    // Half h (0: first, 1: second 8/ESZ K rows of the lane's run) of the B
+    // fragment: one transposing read.
+    __device__ static __forceinline__ i32x2 read_b_half(const TG_LDS char* bslot, int col0, int s, int lane,
+                                                        int h) {
+        const int grp = lane >> 4, j = lane & 15;
+        const int nb = col0 + 16 * (grp & 1);
+        if constexpr (ESZ == 2) {
+            const int row = s * 16 + 8 * (grp >> 1) + (j >> 2) + 4 * h;
+            const int byte = (nb + 4 * (j & 3)) * 2;
+            const int c = byte >> 4, w = byte & 15;
+            const TG_LDS char* p = bslot + row * NB + b_chunk(row, c) * 16 + w;
+            return __builtin_bit_cast(i32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((TG_LDS i16x4*)(p)));
+        } else {
+            const int row = s * 32 + 16 * (grp >> 1) + (j >> 1) + 8 * h;
+            const int byte = nb + 8 * (j & 1);
+            const int c = byte >> 4, w = byte & 15;
+            const TG_LDS char* p = bslot + row * NB + b_chunk(row, c) * 16 + w;
+            return __builtin_amdgcn_ds_read_tr8_b64_v2i32((TG_LDS i32x2*)(p));
+        }
+    }
+
     __device__ static __forceinline__ i32x4 read_b(const TG_LDS char* bslot, int col0, int s, int lane) {
         if constexpr (WIDE) {
-            const int grp = lane >> 4, j = lane & 15;
-            const int nb = col0 + 16 * (grp & 1);
-            if constexpr (ESZ == 2) {
-                const int kb = s * 16 + 8 * (grp >> 1);
-                const int row0 = kb + (j >> 2);
-                const int byte = (nb + 4 * (j & 3)) * 2;
-                const int c = byte >> 4, w = byte & 15;
-                const TG_LDS char* p0 = bslot + row0 * NB + b_chunk(row0, c) * 16 + w;
-                const TG_LDS char* p1 = bslot + (row0 + 4) * NB + b_chunk(row0 + 4, c) * 16 + w;
-                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (TG_LDS i16x4*)(p0));
-                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (TG_LDS i16x4*)(p1));
-                const i32x2 l2 = __builtin_bit_cast(i32x2, lo);
-                const i32x2 h2 = __builtin_bit_cast(i32x2, hi);
-                return i32x4{l2.x, l2.y, h2.x, h2.y};
-            } else {
-                const int kb = s * 32 + 16 * (grp >> 1);
-                const int row0 = kb + (j >> 1);
-                const int byte = nb + 8 * (j & 1);
-                const int c = byte >> 4, w = byte & 15;
-                const TG_LDS char* p0 = bslot + row0 * NB + b_chunk(row0, c) * 16 + w;
-                const TG_LDS char* p1 = bslot + (row0 + 8) * NB + b_chunk(row0 + 8, c) * 16 + w;
-                const i32x2 lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((TG_LDS i32x2*)(p0));
-                const i32x2 hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((TG_LDS i32x2*)(p1));
-                return i32x4{lo.x, lo.y, hi.x, hi.y};
-            }
+            const i32x2 lo = read_b_half(bslot, col0, s, lane, 0);
+            const i32x2 hi = read_b_half(bslot, col0, s, lane, 1);
+            return i32x4{lo.x, lo.y, hi.x, hi.y};
         } else {
             constexpr int PER = 16 / ESZ;  // K values per lane
             union { i32x4 v; T e[PER]; } u;
@@ -320,23 +350,154 @@ struct MfmaGemm {
         }
     }
 
-    // Multiply one slice held in `slot` into the accumulators.
-    __device__ static __forceinline__ void compute(const TG_LDS char* slot, Acc (&acc)[FM][FN],
+    struct Frags {
+        i32x4 a[FM];
+        i32x4 b[FN];
+    };
+
+    __device__ static __forceinline__ void read_frags(Frags& f, const TG_LDS char* slot, int s, int wm0,
+                                                      int wn0, int lane) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) f.a[i] = read_a(slot, wm0 + 32 * i, s, lane);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) f.b[j] = read_b(slot + A_BYTES, wn0 + 32 * j, s, lane);
+    }
+
+    // ---- interleaved K step (direct loader) -------------------------------
+    // One K step issues its FM*FN matrix-core instructions one at a time and
+    // puts the step's memory instructions (fragment reads for the next K
+    // step, copies for a later slice) between them, fenced so the compiler
+    // keeps the order: with one wave per SIMD nothing else keeps the matrix
+    // core busy while a burst of LDS instructions is being issued.
+    static constexpr int NM = FM * FN;      // matrix-core instructions per K step
+    static constexpr int NR = FM + 2 * FN;  // LDS reads per K step (A: 1 each, B: 2 each)
+
+    // Read number r of K step s of `slot` into f, in the order the matrix
+    // instructions consume them: a0, b0 (two halves), ..., b(FN-1), a1, ...
+    __device__ static __forceinline__ void read_op(Frags& f, const TG_LDS char* slot, int s, int r,
                                                    int wm0, int wn0, int lane) {
+        if (r == 0) {
+            f.a[0] = read_a(slot, wm0, s, lane);
+        } else if (r <= 2 * FN) {
+            const int j = (r - 1) >> 1, h = (r - 1) & 1;
+            const i32x2 v = read_b_half(slot + A_BYTES, wn0 + 32 * j, s, lane, h);
+            if (h == 0) {
+                f.b[j].x = v.x;
+                f.b[j].y = v.y;
+            } else {
+                f.b[j].z = v.x;
+                f.b[j].w = v.y;
+            }
+        } else {
+            const int i = r - 2 * FN;
+            f.a[i] = read_a(slot, wm0 + 32 * i, s, lane);
+        }
+    }
+
+    // Memory instructions put after matrix instruction k when `total` of
+    // them are spread evenly over matrix instructions [first, NM).
+    __device__ static constexpr int mem_begin(int k, int first, int total) {
+        return k < first ? 0 : ((k - first) * total + (NM - first) - 1) / (NM - first);
+    }
+
+    // Matrix step on `cur` with reads of (rslot, rs) into `nxt` interleaved.
+    // BARRIER: before the reads, meet the other waves once this wave's slot
+    // reads are done and at most `ahead` later slices' copies are in flight
+    // (after matrix instruction BAR_AT); then, if DMA, issue the N_LD copies
+    // of slice (copy_slot, ca, cb) after the reads.
+    template <bool READS, bool BARRIER, bool DMA>
+    __device__ static __forceinline__ void kstep(Acc (&acc)[FM][FN], const Frags& cur, Frags& nxt,
+                                                 const TG_LDS char* rslot, int rs, int ahead,
+                                                 TG_LDS char* copy_slot, const DirectOffsets& off,
+                                                 const char* ca, const char* cb, int wm0, int wn0,
+                                                 int lane, int wave) {
+        constexpr int BAR_AT = BARRIER ? (NM >= 8 ? 2 : 1) : 0;
+        constexpr int NREAD = READS ? NR : 0;
+        constexpr int TOTAL = NREAD + (DMA ? N_LD : 0);
+#pragma unroll
+        for (int k = 0; k < NM; ++k) {
+            const int i = k / FN, j = k % FN;
+            acc[i][j] = Tr::mma(cur.a[i], cur.b[j], acc[i][j]);
+            if (BARRIER && k == BAR_AT - 1) wait_slice(ahead);
+#pragma unroll
+            for (int m = mem_begin(k, BAR_AT, TOTAL); m < mem_begin(k + 1, BAR_AT, TOTAL); ++m) {
+                if (m < NREAD) read_op(nxt, rslot, rs, m, wm0, wn0, lane);
+                else issue_direct_one(m - NREAD, copy_slot, off, ca, cb, wave);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // One slice t from `cur_slot`.  NEXT: slice t+1 exists (barrier in the
+    // last K step, then its first fragments are read); DMA: also start the
+    // copy of slice t+STAGES into this slot after that barrier.
+    template <bool NEXT, bool DMA>
+    __device__ static __forceinline__ void slice_direct(Acc (&acc)[FM][FN], Frags (&f)[2],
+                                                        const TG_LDS char* cur_slot,
+                                                        const TG_LDS char* next_slot, int ahead,
+                                                        TG_LDS char* copy_slot, const DirectOffsets& off,
+                                                        const char* ca, const char* cb, int wm0, int wn0,
+                                                        int lane, int wave) {
+#pragma unroll
+        for (int s = 0; s + 1 < KSUB; ++s)
+            kstep<true, false, false>(acc, f[s & 1], f[(s + 1) & 1], cur_slot, s + 1, 0, copy_slot, off, ca,
+                                      cb, wm0, wn0, lane, wave);
+        constexpr int L = KSUB - 1;
+        kstep<NEXT, NEXT, DMA>(acc, f[L & 1], f[(L + 1) & 1], next_slot, 0, ahead, copy_slot, off, ca, cb, wm0,
+                               wn0, lane, wave);
+    }
+
+    struct NoHook {
+        __device__ void operator()(int) const {}
+    };
+
+    // Issues K step s's share of the copies of the next slice (if `on`).
+    struct DirectHook {
+        TG_LDS char* slot;
+        const DirectOffsets& off;
+        const char* abase;
+        const char* bbase;
+        int wave;
+        bool on;
+        __device__ __forceinline__ void operator()(int s) const {
+            constexpr int PER = (N_LD + KSUB - 1) / KSUB;
+            if (!on) return;
+#pragma unroll
+            for (int i = 0; i < PER; ++i)
+                if (s * PER + i < N_LD) issue_direct_one(s * PER + i, slot, off, abase, bbase, wave);
+        }
+    };
+
+    // Multiply one slice held in `slot` into the accumulators.  With
+    // fragment reuse the reads are software-pipelined one K step ahead
+    // (register double buffer, "4.1 CUDA GEMM算子性能优化" section 9.2): the
+    // fragments of step s+1 are requested before the matrix-core work of
+    // step s, which hides the LDS latency behind it.  hook(s) runs between
+    // the two and issues this step's share of the next slice's copies.
+    template <class Hook = NoHook>
+    __device__ static __forceinline__ void compute(const TG_LDS char* slot, Acc (&acc)[FM][FN],
+                                                   int wm0, int wn0, int lane, Hook hook = Hook()) {
         const TG_LDS char* bslot = slot + A_BYTES;
+        if constexpr (FRAG == FR_REUSE) {
+            Frags f[2];
+            read_frags(f[0], slot, 0, wm0, wn0, lane);
 #pragma unroll
-        for (int s = 0; s < KSUB; ++s) {
-            if constexpr (FRAG == FR_REUSE) {
-                i32x4 a[FM], b[FN];
-#pragma unroll
-                for (int i = 0; i < FM; ++i) a[i] = read_a(slot, wm0 + 32 * i, s, lane);
-#pragma unroll
-                for (int j = 0; j < FN; ++j) b[j] = read_b(bslot, wn0 + 32 * j, s, lane);
+            for (int s = 0; s < KSUB; ++s) {
+                if (s + 1 < KSUB) read_frags(f[(s + 1) & 1], slot, s + 1, wm0, wn0, lane);
+                hook(s);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
-                    for (int j = 0; j < FN; ++j) acc[i][j] = Tr::mma(a[i], b[j], acc[i][j]);
-            } else {
+                    for (int j = 0; j < FN; ++j) acc[i][j] = Tr::mma(f[s & 1].a[i], f[s & 1].b[j], acc[i][j]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            return;
+        }
+#pragma unroll
+        for (int s = 0; s < KSUB; ++s) {
+            hook(s);
+            {
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -386,19 +547,53 @@ struct MfmaGemm {
         const bool ga = g.a_guard != 0, gb = g.b_guard != 0;
 
         if constexpr (DIRECT) {
-            // Prologue: slices 0 .. STAGES-2 in flight.
+            DirectOffsets off;
+            direct_offsets(off, g, m0, n0);
+            // wave-uniform byte addresses of slice 0 of this tile's A rows / B columns
+            const char* abase = static_cast<const char*>(g.A) + (int64_t)m0 * g.lda * ESZ;
+            const char* bbase = static_cast<const char*>(g.B) + (int64_t)n0 * ESZ;
+            const int64_t astep = (int64_t)BK * ESZ;          // A base advance per slice
+            const int64_t bstep = (int64_t)BK * g.ldb * ESZ;  // B base advance per slice
+            auto issue_slice = [&](int sl) {
+                issue_direct(smem + (sl % STAGES) * SLOT, off, abase + sl * astep, bbase + sl * bstep, wave);
+            };
+            // Prologue: slices 0 .. STAGES-2 in flight; once slice 0 is in
+            // LDS (barrier), start slice STAGES-1 and read the fragments of
+            // slice 0's first K step.
+            Frags f[2];
 #pragma unroll
             for (int s = 0; s < STAGES - 1; ++s)
-                if (s < full) issue_direct(smem + s * SLOT, g, m0, n0, s * BK, wave);
-            for (int t = 0; t < full; ++t) {
-                wait_slice(min(STAGES - 2, full - 1 - t));
-                const int nxt = t + STAGES - 1;
-                if (nxt < full) issue_direct(smem + (nxt % STAGES) * SLOT, g, m0, n0, nxt * BK, wave);
-                compute(smem + (t % STAGES) * SLOT, acc, wm0, wn0, lane);
+                if (s < full) issue_slice(s);
+            if (full > 0) {
+                wait_slice(min(STAGES - 2, full - 1));
+                if (STAGES - 1 < full) issue_slice(STAGES - 1);
+                read_frags(f[0], smem, 0, wm0, wn0, lane);
             }
+            // Steady state.  Slice t is multiplied from slot t % STAGES with
+            // the fragment reads one K step ahead.  The single barrier of the
+            // slice sits inside its last K step: by then this wave's reads of
+            // the slot are complete, so after the barrier (a) no wave reads
+            // the slot any more and the copy of slice t+STAGES may overwrite
+            // it, and (b) every wave's copy of slice t+1 has landed, so the
+            // first fragments of slice t+1 are read while the last K step of
+            // slice t still runs on the matrix cores.
+            int t = 0;
+            for (; t + STAGES < full; ++t)
+                slice_direct<true, true>(acc, f, smem + (t % STAGES) * SLOT, smem + ((t + 1) % STAGES) * SLOT,
+                                         STAGES - 2, smem + (t % STAGES) * SLOT, off,
+                                         abase + (t + STAGES) * astep, bbase + (t + STAGES) * bstep, wm0, wn0,
+                                         lane, wave);
+            for (; t + 1 < full; ++t)
+                slice_direct<true, false>(acc, f, smem + (t % STAGES) * SLOT, smem + ((t + 1) % STAGES) * SLOT,
+                                          min(STAGES - 2, full - 2 - t), smem, off, abase, bbase, wm0, wn0, lane,
+                                          wave);
+            if (t < full)
+                slice_direct<false, false>(acc, f, smem + (t % STAGES) * SLOT, smem, 0, smem, off, abase, bbase,
+                                           wm0, wn0, lane, wave);
             if (full < tiles) {
-                // K tail: element loads with zero fill into the next slot
-                // (no copy is in flight and nobody reads that slot any more).
+                // K tail: element loads with zero fill into slot full % STAGES.
+                // No copy is in flight (the last wait drained them) and every
+                // wave passed the barrier that ended its reads of that slot.
                 Staged r;
                 load_regs(r, g, m0, n0, full * BK, true, true);
                 store_regs(smem + (full % STAGES) * SLOT, r);

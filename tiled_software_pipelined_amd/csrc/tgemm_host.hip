@@ -79,7 +79,8 @@ bool matches(const KernelEntry& e, const tgemm_variant& v) {
     if (v.kernel == TGEMM_KERNEL_TILED && e.family != tg::FAM_TILED) return false;
     return field_ok(v.tile_m, e.bm) && field_ok(v.tile_n, e.bn) && field_ok(v.tile_k, e.bk) &&
            field_ok(v.stages, e.stages) && field_ok(v.loader, e.loader) &&
-           field_ok(v.lds_layout, e.layout) && field_ok(v.access, e.access) && field_ok(v.frag, e.frag);
+           field_ok(v.lds_layout, e.layout) && field_ok(v.access, e.access) && field_ok(v.frag, e.frag) &&
+           field_ok(v.waves_m, e.wm) && field_ok(v.waves_n, e.wn);
 }
 
 const KernelEntry* find_entry(int dtype, const tgemm_variant& v) {
@@ -136,6 +137,8 @@ void entry_to_variant(const KernelEntry& e, int32_t wg_group, tgemm_variant* v) 
     v->access = e.access;
     v->frag = e.frag;
     v->wg_group = wg_group;
+    v->waves_m = e.wm;
+    v->waves_n = e.wn;
 }
 
 // Per-device gfx950 check, cached.
@@ -215,7 +218,8 @@ tgemm_plan* gemm_plan_variant(int64_t M, int64_t N, int64_t K, int32_t dtype, in
     }
     const KernelEntry* e = nullptr;
     if (v.kernel == TGEMM_KERNEL_AUTO && v.tile_m == 0 && v.tile_n == 0 && v.tile_k == 0 && v.stages == 0 &&
-        v.loader == 0 && v.lds_layout == 0 && v.access == 0 && v.frag == 0) {
+        v.loader == 0 && v.lds_layout == 0 && v.access == 0 && v.frag == 0 && v.waves_m == 0 &&
+        v.waves_n == 0) {
         e = default_entry(dtype, M, N);
     } else {
         e = find_entry(dtype, v);

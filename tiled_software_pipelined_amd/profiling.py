@@ -1,0 +1,219 @@
+"""Counter layer: rocprofv3 kernel trace + hardware counters for one workload.
+
+    python -m tiled_software_pipelined_amd.profiling --workload bf16_4096 --out gpurun_out/prof_bf16 \\
+        [--variant k=v,...] [--summary profiles/<name>.md]
+
+Runs bench.py under rocprofv3 several times (one kernel-trace pass, then one
+process per counter group so that no hardware block is over-subscribed) and
+writes a Markdown summary: mean kernel duration, achieved TFLOP/s, matrix-core
+busy fraction, LDS bank-conflict rate, LDS instruction mix, L2 hit rate and
+the HBM bytes per launch.  FETCH_SIZE / WRITE_SIZE are converted to bytes by
+the ratio the same counters read for a plain device copy of known size, run
+in the same process (bench.py --calib-copy).
+
+Needs a GPU and rocprofv3; every pass runs under its own time limit.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import os
+import shlex
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# one rocprofv3 process per group: at most 8 SQ and 4 TCC counters each
+GROUPS = [
+    ["SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES",
+     "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_WAIT_INST_LDS"],
+    ["SQ_LDS_BANK_CONFLICT", "SQ_LDS_ADDR_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_UNALIGNED_STALL",
+     "SQ_ACTIVE_INST_LDS", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_INSTS_LDS_LOAD"],
+    ["FETCH_SIZE"],
+    ["WRITE_SIZE"],
+    ["TCC_HIT_sum", "TCC_MISS_sum"],
+]
+CALIB_MIB = 256
+
+
+def _bench_cmd(args, steps, warmup, calib=False):
+    cmd = ["python3", os.path.join(ROOT, "bench.py"), "--workload", args.workload, "--steps",
+           str(steps), "--warmup", str(warmup), "--no-cpu"]
+    if args.variant:
+        cmd += ["--variant", args.variant]
+    if calib:
+        cmd += ["--calib-copy", str(CALIB_MIB)]
+    return cmd
+
+
+def _run(cmd, limit, log):
+    print("+", " ".join(shlex.quote(c) for c in cmd), flush=True)
+    with open(log, "a") as f:
+        f.write("+ " + " ".join(shlex.quote(c) for c in cmd) + "\n")
+        f.flush()
+        r = subprocess.run(["timeout", "-s", "KILL", str(limit)] + cmd, stdout=f, stderr=subprocess.STDOUT)
+    # rocprofv3 may end with a segfault after the program's results are written
+    return r.returncode
+
+
+def _read_csv(path):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _find(d, pattern):
+    hits = sorted(glob.glob(os.path.join(d, "**", pattern), recursive=True))
+    return hits[0] if hits else None
+
+
+def _is_gemm(name):
+    return "gemm_kernel" in name
+
+
+def _is_copy(name):
+    n = name.lower()
+    return ("copy" in n or "elementwise" in n) and "gemm" not in n
+
+
+def collect(args):
+    out = os.path.abspath(args.out)
+    os.makedirs(out, exist_ok=True)
+    log = os.path.join(out, "profiling.log")
+    env_prefix = []
+    cmds = {}
+    # pass 0: kernel trace + stats
+    tdir = os.path.join(out, "trace")
+    cmd = ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d", tdir, "-o", "trace",
+           "--"] + _bench_cmd(args, args.steps, args.warmup)
+    cmds["trace"] = cmd
+    _run(env_prefix + cmd, 240, log)
+    for i, grp in enumerate(GROUPS):
+        pdir = os.path.join(out, "pmc%d" % i)
+        cmd = ["rocprofv3", "--pmc"] + grp + ["--output-format", "csv", "-d", pdir, "-o", "pmc", "--"] + \
+            _bench_cmd(args, 3, 1, calib=True)
+        cmds["pmc%d" % i] = cmd
+        _run(env_prefix + cmd, 120, log)
+    return cmds
+
+
+def summarize(args, cmds):
+    out = os.path.abspath(args.out)
+    res = {"counters": {}, "copy": {}}
+    stats = _find(os.path.join(out, "trace"), "*kernel_stats.csv")
+    if stats:
+        for row in _read_csv(stats):
+            if _is_gemm(row["Name"]):
+                res["kernel"] = row["Name"]
+                res["calls"] = int(row["Calls"])
+                res["avg_ns"] = float(row["AverageNs"])
+                res["min_ns"] = float(row["MinNs"])
+                res["max_ns"] = float(row["MaxNs"])
+    for i in range(len(GROUPS)):
+        f = _find(os.path.join(out, "pmc%d" % i), "*counter_collection.csv")
+        if not f:
+            continue
+        gsum, gcnt, csum, ccnt = {}, {}, {}, {}
+        for row in _read_csv(f):
+            name = row.get("Kernel_Name", "")
+            cn = row["Counter_Name"]
+            val = float(row["Counter_Value"])
+            if _is_gemm(name):
+                gsum[cn] = gsum.get(cn, 0.0) + val
+                gcnt[cn] = gcnt.get(cn, 0) + 1
+            elif _is_copy(name):
+                csum[cn] = csum.get(cn, 0.0) + val
+                ccnt[cn] = ccnt.get(cn, 0) + 1
+        # rows are per dispatch (and per counter); average over dispatches
+        for cn in gsum:
+            res["counters"][cn] = gsum[cn] / gcnt[cn]
+        for cn in csum:
+            res["copy"][cn] = csum[cn] / ccnt[cn]
+    return res
+
+
+def render(args, cmds, res):
+    from tiled_software_pipelined_amd import inputs
+    w = inputs.workloads()[args.workload]
+    esz = {"f32": 4, "bf16": 2, "i8": 1}[w.dtype]
+    alg_bytes = (w.M * w.K + w.K * w.N) * esz + w.M * w.N * 4
+    lines = ["# rocprofv3 summary: %s" % args.workload, ""]
+    lines.append("Workload: %s GEMM M=%d N=%d K=%d (%s operands, seed %d); variant: %s." % (
+        w.dtype, w.M, w.N, w.K, w.kind, w.seed, args.variant or "default plan"))
+    lines.append("")
+    lines.append("Commands (run from the repository root):")
+    lines.append("")
+    lines.append("```")
+    lines.append("python -m tiled_software_pipelined_amd.profiling --workload %s --out %s%s" % (
+        args.workload, args.out, (" --variant " + args.variant) if args.variant else ""))
+    for k, c in cmds.items():
+        lines.append("# %s: %s" % (k, " ".join(shlex.quote(x) for x in c).replace(ROOT + "/", "")))
+    lines.append("```")
+    lines.append("")
+    if "avg_ns" in res:
+        t = res["avg_ns"] * 1e-9
+        lines.append("| quantity | value |")
+        lines.append("|---|---|")
+        lines.append("| kernel | `%s` |" % res["kernel"])
+        lines.append("| dispatches traced | %d |" % res["calls"])
+        lines.append("| mean / min / max duration | %.2f / %.2f / %.2f us |" % (
+            res["avg_ns"] / 1e3, res["min_ns"] / 1e3, res["max_ns"] / 1e3))
+        lines.append("| achieved (2MNK / mean) | %.1f TFLOP/s |" % (w.flops / t / 1e12))
+        c = res["counters"]
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in c and "SQ_BUSY_CU_CYCLES" in c and c["SQ_BUSY_CU_CYCLES"]:
+            lines.append("| SQ_VALU_MFMA_BUSY_CYCLES / SQ_BUSY_CU_CYCLES | %.3f |" % (
+                c["SQ_VALU_MFMA_BUSY_CYCLES"] / c["SQ_BUSY_CU_CYCLES"]))
+        if "SQ_LDS_BANK_CONFLICT" in c and c.get("SQ_LDS_IDX_ACTIVE"):
+            lines.append("| SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE | %.3f |" % (
+                c["SQ_LDS_BANK_CONFLICT"] / c["SQ_LDS_IDX_ACTIVE"]))
+        if c.get("TCC_HIT_sum") is not None and c.get("TCC_MISS_sum") is not None:
+            tot = c["TCC_HIT_sum"] + c["TCC_MISS_sum"]
+            if tot:
+                lines.append("| L2 hit rate | %.3f |" % (c["TCC_HIT_sum"] / tot))
+        cp = res["copy"]
+        calib = CALIB_MIB << 20
+        for cn in ("FETCH_SIZE", "WRITE_SIZE"):
+            if cn in c and cp.get(cn):
+                scale = calib / cp[cn]  # bytes per counter unit, from the copy
+                lines.append("| %s per launch (scaled by copy: %.1f B/unit) | %.1f MiB |" % (
+                    cn, scale, c[cn] * scale / 2 ** 20))
+        if "FETCH_SIZE" in c and "WRITE_SIZE" in c and cp.get("FETCH_SIZE") and cp.get("WRITE_SIZE"):
+            traffic = c["FETCH_SIZE"] * calib / cp["FETCH_SIZE"] + c["WRITE_SIZE"] * calib / cp["WRITE_SIZE"]
+            lines.append("| HBM traffic per launch / algorithmic bytes | %.1f MiB / %.1f MiB |" % (
+                traffic / 2 ** 20, alg_bytes / 2 ** 20))
+        lines.append("")
+        lines.append("Raw counter means per dispatch:")
+        lines.append("")
+        lines.append("| counter | GEMM kernel | copy kernel (%d MiB) |" % CALIB_MIB)
+        lines.append("|---|---|---|")
+        for cn in sorted(set(c) | set(cp)):
+            lines.append("| %s | %s | %s |" % (cn, "%.4g" % c[cn] if cn in c else "",
+                                               "%.4g" % cp[cn] if cn in cp else ""))
+    return "\n".join(lines) + "\n"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workload", default="bf16_4096")
+    ap.add_argument("--variant", default="")
+    ap.add_argument("--out", default="gpurun_out/prof")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--summary", default="")
+    ap.add_argument("--summarize-only", action="store_true")
+    args = ap.parse_args()
+    sys.path.insert(0, ROOT)
+    os.environ.setdefault("TMPDIR", "/tmp")
+    cmds = {} if args.summarize_only else collect(args)
+    res = summarize(args, cmds)
+    text = render(args, cmds, res)
+    path = args.summary or os.path.join(args.out, "summary.md")
+    os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+    with open(path, "w") as f:
+        f.write(text)
+    print(text, flush=True)
+
+
+if __name__ == "__main__":
+    main()
