@@ -136,20 +136,37 @@ def main():
             print(json.dumps({"mode": "ladder", "workload": w.name, "kernel": p.name,
                               "median_ms": ms, "tflops": w.flops / ms / 1e9,
                               "frac_peak": w.flops / ms / 1e9 / PEAK_TFLOPS[w.dtype]}), flush=True)
+        # workgroup order (the last rung): the default plan with each order
+        for grp in (lib.ORDER_ROW_MAJOR, 1, 2, 4, 8):
+            dv = lib.plan_for(w.M, w.N, w.K, code, w.K, w.N, w.N).info().variant
+            dv.wg_group = grp
+            per, _ = time_plan(lib, torch, w, A, B, C, dv, max(5, args.steps // 5), 3)
+            ms = sorted(per)[len(per) // 2]
+            print(json.dumps({"mode": "ladder", "workload": w.name,
+                              "kernel": lib.plan_for(w.M, w.N, w.K, code, w.K, w.N, w.N, dv).name,
+                              "wg_group": grp, "median_ms": ms, "tflops": w.flops / ms / 1e9,
+                              "frac_peak": w.flops / ms / 1e9 / PEAK_TFLOPS[w.dtype]}), flush=True)
     if args.sweep:
+        # heatmap: every bf16 sweep shape x (128x128x32 tile at 2, 3, 4 stages,
+        # and the default plan)
+        stage_vs = [("s%d" % st, lib.Variant(kernel=lib.KERNEL_TILED, tile_m=128, tile_n=128, tile_k=32,
+                                            stages=st, loader=lib.LOADER_DIRECT, waves_m=2, waves_n=2))
+                    for st in (2, 3, 4)] + [("default", None)]
         for name, sw in inputs.workloads().items():
             if not name.startswith("bf16_sweep"):
                 continue
             a, b = sw.operands()
             a, b = a.to(dev), b.to(dev)
             c = torch.empty((sw.M, sw.N), dtype=torch.float32, device=dev)
-            per, _ = time_plan(lib, torch, sw, a, b, c, None, max(10, args.steps // 2), 5)
-            ms = sorted(per)[len(per) // 2]
             ideal_ms = max(sw.flops / (PEAK_TFLOPS["bf16"] * 1e9), algorithmic_bytes(sw) / (PEAK_HBM_GBS * 1e6))
-            print(json.dumps({"mode": "sweep", "workload": name, "median_ms": ms,
-                              "tflops": sw.flops / ms / 1e9, "frac_roofline": ideal_ms / ms,
-                              "kernel": lib.plan_for(sw.M, sw.N, sw.K, lib.BF16, sw.K, sw.N, sw.N).name}),
-                  flush=True)
+            for label, v in stage_vs:
+                per, _ = time_plan(lib, torch, sw, a, b, c, v, max(10, args.steps // 2), 5)
+                ms = sorted(per)[len(per) // 2]
+                kname = lib.plan_for(sw.M, sw.N, sw.K, lib.BF16, sw.K, sw.N, sw.N, v).name
+                print(json.dumps({"mode": "sweep", "workload": name, "plan": label, "kernel": kname,
+                                  "median_ms": ms, "tflops": sw.flops / ms / 1e9,
+                                  "frac_peak": sw.flops / ms / 1e9 / PEAK_TFLOPS["bf16"],
+                                  "frac_roofline": ideal_ms / ms}), flush=True)
             del a, b, c
 
     if args.calib_copy:
@@ -170,6 +187,13 @@ def main():
     value = w.flops * args.steps / wall / 1e12
     achieved = w.flops / (kernel_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
+    # HBM bytes per launch measured by the counter layer on these exact
+    # kernel sources (profiles/*.md); null when none matches
+    from tiled_software_pipelined_amd import provenance
+    prof = provenance.find_profile(plan.name, w.name)
+    traffic = None
+    if prof and prof.get("traffic_bytes") not in (None, "null"):
+        traffic = int(float(prof["traffic_bytes"]))
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -188,7 +212,9 @@ def main():
                    "grid": plan.info().grid, "frac_of_peak": round(value / peak, 4)},
         "roofline": {"bound": "mfma" if w.dtype != "f32" else "alu", "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s" if w.dtype != "i8" else "TOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "traffic_unit": "bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-scaled)",
+                     "traffic_source": prof["path"] if prof else None,
                      "kernel_ms_mean": round(kernel_ms, 5),
                      "kernel_ms_min": round(min(per), 5)},
         "cpu_baseline": None,

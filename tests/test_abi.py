@@ -90,8 +90,10 @@ def test_default_choice_by_shape():
     big = tl.Plan(4096, 4096, 4096, tl.BF16).info()
     assert (big.variant.tile_m, big.variant.tile_n) == (256, 256)
     assert big.variant.loader == tl.LOADER_DIRECT and big.grid == 256
+    mid = tl.Plan(1024, 1024, 512, tl.BF16).info()
+    assert (mid.variant.tile_m, mid.variant.tile_n) == (128, 128) and mid.grid == 64
     small = tl.Plan(512, 512, 512, tl.BF16).info()
-    assert (small.variant.tile_m, small.variant.tile_n) == (128, 128) and small.grid == 16
+    assert (small.variant.tile_m, small.variant.tile_n) == (64, 64) and small.grid == 64
     f = tl.Plan(256, 256, 256, tl.F32).info()
     assert f.variant.tile_k == 8 and f.grid == 4
 

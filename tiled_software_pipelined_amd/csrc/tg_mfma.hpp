@@ -394,16 +394,17 @@ struct MfmaGemm {
         }
     }
 
-    // Memory instructions put after matrix instruction k when `total` of
-    // them are spread evenly over matrix instructions [first, NM).
+    // Memory instructions [mem_begin(k), mem_begin(k+1)) follow matrix
+    // instruction k when `total` of them are spread evenly over matrix
+    // instructions first .. NM-1 (0 <= first < NM).
     __device__ static constexpr int mem_begin(int k, int first, int total) {
-        return k < first ? 0 : ((k - first) * total + (NM - first) - 1) / (NM - first);
+        return k <= first ? 0 : ((k - first) * total + (NM - first) - 1) / (NM - first);
     }
 
     // Matrix step on `cur` with reads of (rslot, rs) into `nxt` interleaved.
     // BARRIER: before the reads, meet the other waves once this wave's slot
     // reads are done and at most `ahead` later slices' copies are in flight
-    // (after matrix instruction BAR_AT); then, if DMA, issue the N_LD copies
+    // (after matrix instruction BAR_K); then, if DMA, issue the N_LD copies
     // of slice (copy_slot, ca, cb) after the reads.
     template <bool READS, bool BARRIER, bool DMA>
     __device__ static __forceinline__ void kstep(Acc (&acc)[FM][FN], const Frags& cur, Frags& nxt,
@@ -411,16 +412,19 @@ struct MfmaGemm {
                                                  TG_LDS char* copy_slot, const DirectOffsets& off,
                                                  const char* ca, const char* cb, int wm0, int wn0,
                                                  int lane, int wave) {
-        constexpr int BAR_AT = BARRIER ? (NM >= 8 ? 2 : 1) : 0;
+        // the barrier follows matrix instruction BAR_K; the memory
+        // instructions start after it
+        constexpr int BAR_K = (BARRIER && NM >= 8) ? 1 : 0;
+        static_assert(BAR_K < NM, "barrier inside the K step");
         constexpr int NREAD = READS ? NR : 0;
         constexpr int TOTAL = NREAD + (DMA ? N_LD : 0);
 #pragma unroll
         for (int k = 0; k < NM; ++k) {
             const int i = k / FN, j = k % FN;
             acc[i][j] = Tr::mma(cur.a[i], cur.b[j], acc[i][j]);
-            if (BARRIER && k == BAR_AT - 1) wait_slice(ahead);
+            if (BARRIER && k == BAR_K) wait_slice(ahead);
 #pragma unroll
-            for (int m = mem_begin(k, BAR_AT, TOTAL); m < mem_begin(k + 1, BAR_AT, TOTAL); ++m) {
+            for (int m = mem_begin(k, BAR_K, TOTAL); m < mem_begin(k + 1, BAR_K, TOTAL); ++m) {
                 if (m < NREAD) read_op(nxt, rslot, rs, m, wm0, wn0, lane);
                 else issue_direct_one(m - NREAD, copy_slot, off, ca, cb, wave);
             }

@@ -90,23 +90,31 @@ const KernelEntry* find_entry(int dtype, const tgemm_variant& v) {
 }
 
 // Default choice for a shape: the largest tile that still gives the GPU
-// (256 compute units) at least half a workgroup per unit, else 128 x 128.
-const KernelEntry* default_entry(int dtype, int64_t M, int64_t N) {
+// (256 compute units) at least half a workgroup per unit; small problems
+// step down to 128 x 128 and then 64 x 64 tiles.  Short K (a few slices per
+// tile) also takes 128 x 128: with one wave of 256 x 256 tiles every
+// workgroup writes its C tile at the same moment, unoverlapped, and at short
+// K that write is most of the work.
+const KernelEntry* default_entry(int dtype, int64_t M, int64_t N, int64_t K) {
     tgemm_variant v{};
     v.kernel = TGEMM_KERNEL_TILED;
     if (dtype == TGEMM_F32) return find_entry(dtype, v);
-    const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
+    auto wgs = [&](int t) { return ((M + t - 1) / t) * ((N + t - 1) / t); };
     v.loader = TGEMM_LOADER_DIRECT;
     v.access = TGEMM_ACCESS_WIDE;
     v.frag = TGEMM_FRAG_REUSE;
     v.lds_layout = TGEMM_LDS_XOR;
-    if (big >= 128) {
-        v.tile_m = 256;
-        v.tile_n = 256;
+    v.waves_m = 2;
+    v.waves_n = 2;
+    const int64_t short_k = dtype == TGEMM_I8 ? 2048 : 1024;
+    if (wgs(256) >= 128 && K > short_k) {
+        v.tile_m = v.tile_n = 256;
         v.stages = 2;
+    } else if (wgs(128) >= 64) {
+        v.tile_m = v.tile_n = 128;
+        v.stages = 3;
     } else {
-        v.tile_m = 128;
-        v.tile_n = 128;
+        v.tile_m = v.tile_n = 64;
         v.stages = 3;
     }
     return find_entry(dtype, v);
@@ -220,7 +228,7 @@ tgemm_plan* gemm_plan_variant(int64_t M, int64_t N, int64_t K, int32_t dtype, in
     if (v.kernel == TGEMM_KERNEL_AUTO && v.tile_m == 0 && v.tile_n == 0 && v.tile_k == 0 && v.stages == 0 &&
         v.loader == 0 && v.lds_layout == 0 && v.access == 0 && v.frag == 0 && v.waves_m == 0 &&
         v.waves_n == 0) {
-        e = default_entry(dtype, M, N);
+        e = default_entry(dtype, M, N, K);
     } else {
         e = find_entry(dtype, v);
     }
@@ -254,6 +262,8 @@ tgemm_plan* gemm_plan_variant(int64_t M, int64_t N, int64_t K, int32_t dtype, in
     p->dtype = dtype;
     p->entry = e;
     p->fallback = fb ? fb : e;
+    // default: XCD-aware order grouped by 4 tile rows (measured ~4% faster
+    // than row-major for 256 x 256 tiles at 4096^3, with less L2-miss traffic)
     p->wg_group = v.wg_group == 0 ? (e->family == tg::FAM_NAIVE ? -1 : 4) : v.wg_group;
     p->a_guard = ga;
     p->b_guard = gb;

@@ -154,7 +154,7 @@ class Plan:
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h:
+        if h and _lib is not None:  # module globals are gone at interpreter exit
             _lib.gemm_destroy(h)
             self._h = None
 

@@ -77,24 +77,26 @@ def _is_copy(name):
     return ("copy" in n or "elementwise" in n) and "gemm" not in n
 
 
+def build_cmds(args):
+    """The rocprofv3 command of every pass (kernel trace, then one per counter group)."""
+    out = os.path.abspath(args.out)
+    cmds = {"trace": ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d",
+                      os.path.join(out, "trace"), "-o", "trace", "--"] +
+                     _bench_cmd(args, args.steps, args.warmup)}
+    for i, grp in enumerate(GROUPS):
+        cmds["pmc%d" % i] = ["rocprofv3", "--pmc"] + grp + ["--output-format", "csv", "-d",
+                                                            os.path.join(out, "pmc%d" % i), "-o", "pmc",
+                                                            "--"] + _bench_cmd(args, 3, 1, calib=True)
+    return cmds
+
+
 def collect(args):
     out = os.path.abspath(args.out)
     os.makedirs(out, exist_ok=True)
     log = os.path.join(out, "profiling.log")
-    env_prefix = []
-    cmds = {}
-    # pass 0: kernel trace + stats
-    tdir = os.path.join(out, "trace")
-    cmd = ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d", tdir, "-o", "trace",
-           "--"] + _bench_cmd(args, args.steps, args.warmup)
-    cmds["trace"] = cmd
-    _run(env_prefix + cmd, 240, log)
-    for i, grp in enumerate(GROUPS):
-        pdir = os.path.join(out, "pmc%d" % i)
-        cmd = ["rocprofv3", "--pmc"] + grp + ["--output-format", "csv", "-d", pdir, "-o", "pmc", "--"] + \
-            _bench_cmd(args, 3, 1, calib=True)
-        cmds["pmc%d" % i] = cmd
-        _run(env_prefix + cmd, 120, log)
+    cmds = build_cmds(args)
+    for name, cmd in cmds.items():
+        _run(cmd, 240 if name == "trace" else 120, log)
     return cmds
 
 
@@ -133,12 +135,33 @@ def summarize(args, cmds):
     return res
 
 
+def _plan_name(args, w):
+    from tiled_software_pipelined_amd import lib
+    v = None
+    if args.variant:
+        v = lib.Variant()
+        for kv in args.variant.split(","):
+            k, val = kv.split("=")
+            setattr(v, k.strip(), int(val))
+    code = {"f32": lib.F32, "bf16": lib.BF16, "i8": lib.I8}[w.dtype]
+    return lib.Plan(w.M, w.N, w.K, code, variant=v).name
+
+
 def render(args, cmds, res):
-    from tiled_software_pipelined_amd import inputs
+    from tiled_software_pipelined_amd import inputs, provenance
     w = inputs.workloads()[args.workload]
     esz = {"f32": 4, "bf16": 2, "i8": 1}[w.dtype]
     alg_bytes = (w.M * w.K + w.K * w.N) * esz + w.M * w.N * 4
-    lines = ["# rocprofv3 summary: %s" % args.workload, ""]
+    kname = _plan_name(args, w)
+    c, cp = res["counters"], res["copy"]
+    calib = CALIB_MIB << 20
+    traffic = None
+    if "FETCH_SIZE" in c and "WRITE_SIZE" in c and cp.get("FETCH_SIZE") and cp.get("WRITE_SIZE"):
+        traffic = c["FETCH_SIZE"] * calib / cp["FETCH_SIZE"] + c["WRITE_SIZE"] * calib / cp["WRITE_SIZE"]
+    tag = provenance.profile_tag(kernel=kname, workload=args.workload, source=provenance.source_hash(),
+                                 avg_ns="%.0f" % res.get("avg_ns", 0),
+                                 traffic_bytes="%.0f" % traffic if traffic is not None else "null")
+    lines = [tag, "# rocprofv3 summary: %s, kernel %s" % (args.workload, kname), ""]
     lines.append("Workload: %s GEMM M=%d N=%d K=%d (%s operands, seed %d); variant: %s." % (
         w.dtype, w.M, w.N, w.K, w.kind, w.seed, args.variant or "default plan"))
     lines.append("")
@@ -147,8 +170,9 @@ def render(args, cmds, res):
     lines.append("```")
     lines.append("python -m tiled_software_pipelined_amd.profiling --workload %s --out %s%s" % (
         args.workload, args.out, (" --variant " + args.variant) if args.variant else ""))
-    for k, c in cmds.items():
-        lines.append("# %s: %s" % (k, " ".join(shlex.quote(x) for x in c).replace(ROOT + "/", "")))
+    for k, cmd in cmds.items():
+        text = " ".join(shlex.quote(x) for x in cmd).replace(ROOT + "/", "")
+        lines.append("# %s: %s" % (k, text.replace(os.path.abspath(args.out), args.out)))
     lines.append("```")
     lines.append("")
     if "avg_ns" in res:
@@ -160,10 +184,9 @@ def render(args, cmds, res):
         lines.append("| mean / min / max duration | %.2f / %.2f / %.2f us |" % (
             res["avg_ns"] / 1e3, res["min_ns"] / 1e3, res["max_ns"] / 1e3))
         lines.append("| achieved (2MNK / mean) | %.1f TFLOP/s |" % (w.flops / t / 1e12))
-        c = res["counters"]
         if "SQ_VALU_MFMA_BUSY_CYCLES" in c and "SQ_BUSY_CU_CYCLES" in c and c["SQ_BUSY_CU_CYCLES"]:
-            lines.append("| SQ_VALU_MFMA_BUSY_CYCLES / SQ_BUSY_CU_CYCLES | %.3f |" % (
-                c["SQ_VALU_MFMA_BUSY_CYCLES"] / c["SQ_BUSY_CU_CYCLES"]))
+            lines.append("| SQ_VALU_MFMA_BUSY_CYCLES / (4 SIMDs x SQ_BUSY_CU_CYCLES) | %.3f |" % (
+                c["SQ_VALU_MFMA_BUSY_CYCLES"] / (4.0 * c["SQ_BUSY_CU_CYCLES"])))
         if "SQ_LDS_BANK_CONFLICT" in c and c.get("SQ_LDS_IDX_ACTIVE"):
             lines.append("| SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE | %.3f |" % (
                 c["SQ_LDS_BANK_CONFLICT"] / c["SQ_LDS_IDX_ACTIVE"]))
@@ -171,15 +194,12 @@ def render(args, cmds, res):
             tot = c["TCC_HIT_sum"] + c["TCC_MISS_sum"]
             if tot:
                 lines.append("| L2 hit rate | %.3f |" % (c["TCC_HIT_sum"] / tot))
-        cp = res["copy"]
-        calib = CALIB_MIB << 20
         for cn in ("FETCH_SIZE", "WRITE_SIZE"):
             if cn in c and cp.get(cn):
                 scale = calib / cp[cn]  # bytes per counter unit, from the copy
                 lines.append("| %s per launch (scaled by copy: %.1f B/unit) | %.1f MiB |" % (
                     cn, scale, c[cn] * scale / 2 ** 20))
-        if "FETCH_SIZE" in c and "WRITE_SIZE" in c and cp.get("FETCH_SIZE") and cp.get("WRITE_SIZE"):
-            traffic = c["FETCH_SIZE"] * calib / cp["FETCH_SIZE"] + c["WRITE_SIZE"] * calib / cp["WRITE_SIZE"]
+        if traffic is not None:
             lines.append("| HBM traffic per launch / algorithmic bytes | %.1f MiB / %.1f MiB |" % (
                 traffic / 2 ** 20, alg_bytes / 2 ** 20))
         lines.append("")
@@ -205,7 +225,7 @@ def main():
     args = ap.parse_args()
     sys.path.insert(0, ROOT)
     os.environ.setdefault("TMPDIR", "/tmp")
-    cmds = {} if args.summarize_only else collect(args)
+    cmds = build_cmds(args) if args.summarize_only else collect(args)
     res = summarize(args, cmds)
     text = render(args, cmds, res)
     path = args.summary or os.path.join(args.out, "summary.md")
