@@ -42,8 +42,8 @@ def parse_variant(text, lib):
 
 
 def algorithmic_bytes(w):
-    esz = {"f32": 4, "bf16": 2, "i8": 1}[w.dtype]
-    return (w.M * w.K + w.K * w.N) * esz + w.M * w.N * 4
+    from tiled_software_pipelined_amd import metrics
+    return metrics.algorithmic_bytes(w.M, w.N, w.K, {"f32": 4, "bf16": 2, "i8": 1}[w.dtype], 4)
 
 
 def time_plan(lib, torch, w, A, B, C, variant, steps, warmup):
@@ -116,7 +116,7 @@ def main():
         sys.exit(2)
 
     import torch
-    from tiled_software_pipelined_amd import inputs, lib
+    from tiled_software_pipelined_amd import inputs, lib, metrics
 
     w = inputs.workloads()[args.workload]
     dev = torch.device("cuda:0")
@@ -158,7 +158,8 @@ def main():
             a, b = sw.operands()
             a, b = a.to(dev), b.to(dev)
             c = torch.empty((sw.M, sw.N), dtype=torch.float32, device=dev)
-            ideal_ms = max(sw.flops / (PEAK_TFLOPS["bf16"] * 1e9), algorithmic_bytes(sw) / (PEAK_HBM_GBS * 1e6))
+            ideal_ms = 1e3 * metrics.roofline_time(sw.M, sw.N, sw.K, 2, 4, PEAK_TFLOPS["bf16"] * 1e12,
+                                                   PEAK_HBM_GBS * 1e9)
             for label, v in stage_vs:
                 per, _ = time_plan(lib, torch, sw, a, b, c, v, max(10, args.steps // 2), 5)
                 ms = sorted(per)[len(per) // 2]
@@ -184,8 +185,8 @@ def main():
     plan = lib.plan_for(w.M, w.N, w.K, code, w.K, w.N, w.N, variant)
     ms_step = wall * 1e3 / args.steps
     kernel_ms = sum(per) / len(per)
-    value = w.flops * args.steps / wall / 1e12
-    achieved = w.flops / (kernel_ms * 1e-3) / 1e12
+    value = metrics.tflops(w.M, w.N, w.K, wall / args.steps)
+    achieved = metrics.tflops(w.M, w.N, w.K, kernel_ms * 1e-3)
     peak = PEAK_TFLOPS[w.dtype]
     # HBM bytes per launch measured by the counter layer on these exact
     # kernel sources (profiles/*.md); null when none matches

@@ -148,10 +148,10 @@ def _plan_name(args, w):
 
 
 def render(args, cmds, res):
-    from tiled_software_pipelined_amd import inputs, provenance
+    from tiled_software_pipelined_amd import inputs, metrics, provenance
     w = inputs.workloads()[args.workload]
     esz = {"f32": 4, "bf16": 2, "i8": 1}[w.dtype]
-    alg_bytes = (w.M * w.K + w.K * w.N) * esz + w.M * w.N * 4
+    alg_bytes = metrics.algorithmic_bytes(w.M, w.N, w.K, esz, 4)
     kname = _plan_name(args, w)
     c, cp = res["counters"], res["copy"]
     calib = CALIB_MIB << 20
