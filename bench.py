@@ -128,24 +128,39 @@ def main():
     torch.cuda.synchronize()
 
     if args.ladder:
+        # Every compiled variant of this dtype, then the default plan under each
+        # workgroup order.  Timed round-robin (a few launches of each variant per
+        # round, many rounds) so that clock and thermal drift during the run
+        # spreads over all variants instead of favouring the ones timed first.
         code = {"f32": lib.F32, "bf16": lib.BF16, "i8": lib.I8}[w.dtype]
-        for v in lib.variants(code):
-            per, _ = time_plan(lib, torch, w, A, B, C, v, max(5, args.steps // 5), 3)
-            ms = sorted(per)[len(per) // 2]
-            p = lib.plan_for(w.M, w.N, w.K, code, w.K, w.N, w.N, v)
-            print(json.dumps({"mode": "ladder", "workload": w.name, "kernel": p.name,
-                              "median_ms": ms, "tflops": w.flops / ms / 1e9,
-                              "frac_peak": w.flops / ms / 1e9 / PEAK_TFLOPS[w.dtype]}), flush=True)
-        # workgroup order (the last rung): the default plan with each order
+        entries = [(v, None) for v in lib.variants(code)]
         for grp in (lib.ORDER_ROW_MAJOR, 1, 2, 4, 8):
             dv = lib.plan_for(w.M, w.N, w.K, code, w.K, w.N, w.N).info().variant
             dv.wg_group = grp
-            per, _ = time_plan(lib, torch, w, A, B, C, dv, max(5, args.steps // 5), 3)
-            ms = sorted(per)[len(per) // 2]
-            print(json.dumps({"mode": "ladder", "workload": w.name,
-                              "kernel": lib.plan_for(w.M, w.N, w.K, code, w.K, w.N, w.N, dv).name,
-                              "wg_group": grp, "median_ms": ms, "tflops": w.flops / ms / 1e9,
-                              "frac_peak": w.flops / ms / 1e9 / PEAK_TFLOPS[w.dtype]}), flush=True)
+            entries.append((dv, grp))
+        slow = [i for i, (v, _) in enumerate(entries) if v.kernel == lib.KERNEL_NAIVE]
+        per_round = {i: (1 if i in slow else 3) for i in range(len(entries))}
+        rounds = max(4, args.steps // 3)
+        times = {i: [] for i in range(len(entries))}
+        for i, (v, _) in enumerate(entries):  # warm every kernel once
+            lib.gemm(A, B, out=C, variant=v)
+        torch.cuda.synchronize()
+        for r in range(rounds):
+            for i, (v, _) in enumerate(entries):
+                if i in slow and r >= 2:
+                    continue
+                per, _ = time_plan(lib, torch, w, A, B, C, v, per_round[i], 0)
+                times[i] += per
+        for i, (v, grp) in enumerate(entries):
+            t = sorted(times[i])
+            ms = t[len(t) // 2]
+            rec = {"mode": "ladder", "workload": w.name,
+                   "kernel": lib.plan_for(w.M, w.N, w.K, code, w.K, w.N, w.N, v).name,
+                   "median_ms": ms, "p10_ms": t[len(t) // 10], "launches": len(t),
+                   "tflops": w.flops / ms / 1e9, "frac_peak": w.flops / ms / 1e9 / PEAK_TFLOPS[w.dtype]}
+            if grp is not None:
+                rec["wg_group"] = grp
+            print(json.dumps(rec), flush=True)
     if args.sweep:
         # heatmap: every bf16 sweep shape x (128x128x32 tile at 2, 3, 4 stages,
         # and the default plan)

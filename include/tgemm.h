@@ -76,16 +76,23 @@ typedef enum tgemm_dtype {
 
 /* LDS layouts (GEMM page, section 8.5). */
 #define TGEMM_LDS_PLAIN 1
-#define TGEMM_LDS_XOR 2          /* 16-byte chunk index XOR-swizzled by row */
+#define TGEMM_LDS_XOR 2          /* 16-byte chunk index XOR-swizzled by row; for the fp32
+                                    kernels: each lane's outputs split in quarters 32 apart */
 
 /* Access width of global loads, LDS writes and LDS fragment reads
- * (GEMM page, section 7: 128-bit vector accesses). */
+ * (GEMM page, section 7: 128-bit vector accesses).  For the fp32 kernels it
+ * selects the A fragment read: WIDE = A transposed in LDS, two 16-byte reads;
+ * NARROW = A row-major in LDS, eight 4-byte reads. */
 #define TGEMM_ACCESS_WIDE 1      /* 16-byte accesses */
 #define TGEMM_ACCESS_NARROW 2    /* 4-byte global loads / LDS accesses */
 
 /* Register tiling (GEMM page, sections 5-6). */
 #define TGEMM_FRAG_REUSE 1       /* each fragment read once per k step, reused across the wave tile */
 #define TGEMM_FRAG_PER_MMA 2     /* both fragments re-read for every matrix-core instruction */
+
+/* C write-back (the SIMT ladder's coalesced write-back step). */
+#define TGEMM_STORE_VECTOR 1     /* 16-byte row pieces */
+#define TGEMM_STORE_SCALAR 2     /* one element per store */
 
 /* Workgroup order (GEMM page, section 2.3). */
 #define TGEMM_ORDER_ROW_MAJOR (-1)
@@ -107,6 +114,7 @@ typedef struct tgemm_variant {
     int32_t wg_group;   /* TGEMM_ORDER_ROW_MAJOR, or g >= 1: XCD-aware order grouped by g tile rows */
     int32_t waves_m;    /* waves per workgroup along M */
     int32_t waves_n;    /* waves per workgroup along N */
+    int32_t store;      /* TGEMM_STORE_* (fp32 kernels; matrix-core kernels report 0) */
 } tgemm_variant;
 
 typedef struct tgemm_plan tgemm_plan;

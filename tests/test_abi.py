@@ -76,7 +76,7 @@ def test_variants_enumerate(dtype):
         p = tl.Plan(512, 512, 512, dtype, variant=v)
         got = p.info().variant
         for f in ("kernel", "tile_m", "tile_n", "tile_k", "stages", "loader", "lds_layout", "access", "frag",
-                  "waves_m", "waves_n"):
+                  "waves_m", "waves_n", "store"):
             assert getattr(got, f) == getattr(v, f)
 
 
@@ -119,3 +119,14 @@ def test_loads_per_stage_match_tile_bytes():
     info = tl.Plan(4096, 4096, 4096, tl.BF16).info()
     # 256 x 64 + 64 x 256 bf16 = 64 KiB per slice, 256 threads, 16 B per load
     assert info.loads_per_stage == 65536 // 256 // 16
+
+
+def test_guard_follows_global_load_width_for_every_variant():
+    # N = 257 leaves a partial 16-byte chunk at the end of every B row: every
+    # tiled variant that loads B in chunks must guard B (found on the fp32
+    # rung whose A-fragment access is narrow but whose B loads are 16 bytes)
+    for dtype in (tl.F32, tl.BF16, tl.I8):
+        for v in tl.variants(dtype):
+            info = tl.Plan(129, 257, 40, dtype, variant=v).info()
+            if info.variant.kernel == tl.KERNEL_TILED:
+                assert info.b_guarded == 1, info.name.decode()

@@ -86,8 +86,9 @@ def _variants(dtype, tiled_only=False):
 
 
 def _vname(v):
-    return "t%dx%dx%d_w%dx%d_s%d_l%d_y%d_a%d_f%d" % (v.tile_m, v.tile_n, v.tile_k, v.waves_m, v.waves_n,
-                                                   v.stages, v.loader, v.lds_layout, v.access, v.frag)
+    return "t%dx%dx%d_w%dx%d_s%d_l%d_y%d_a%d_f%d_st%d" % (v.tile_m, v.tile_n, v.tile_k, v.waves_m, v.waves_n,
+                                                        v.stages, v.loader, v.lds_layout, v.access, v.frag,
+                                                        v.store)
 
 
 # ---------------------------------------------------------------- small shapes

@@ -4,8 +4,15 @@
 namespace tg {
 
 void register_f32(void (*add)(const KernelEntry&)) {
-    add(f32_entry<2>());
-    add(f32_entry<1>());
+    // production: every rung on
+    add(f32_entry<2, true, true, true>());
+    // the SIMT ladder, one change per rung (the SM80 ablation plan, section
+    // 1.5.4): tiling -> + A transposed -> + conflict-free layout ->
+    // + coalesced write-back -> + double buffer
+    add(f32_entry<1, true, true, true>());
+    add(f32_entry<1, true, true, false>());
+    add(f32_entry<1, true, false, false>());
+    add(f32_entry<1, false, false, false>());
     add(naive_entry<0>());
 }
 

@@ -38,6 +38,8 @@ struct KernelEntry {
     int access;      // Access
     int frag;        // Frag
     int wm, wn;      // wave grid
+    int store;       // C store width (fp32 kernels), 0 = not applicable
+    int gload_bytes; // width of the global loads of full chunks (0: element loads only)
     int threads;     // threads per workgroup
     int lds_bytes;   // static LDS per workgroup
     int loads_per_stage;  // global->LDS instructions per wave per stage

@@ -1,30 +1,38 @@
 // fp32 GEMM on the vector ALUs (no matrix cores): the register-tiled
 // outer-product kernel of "4.1 CUDA GEMM算子性能优化", sections 4-9, laid out
-// for 64-wide waves.
+// for 64-wide waves, with the switches of the SIMT ladder of the SM80
+// cp.async / ldmatrix ablation plan (section 1.5.4: tiling -> A transposed in
+// shared memory -> conflict-free layout -> coalesced write-back -> double
+// buffer), one per template parameter:
+//
+//   TRANS_A   A slice stored transposed in LDS (As[k][m], section 7.3), so the
+//             A fragment is two 16-byte reads instead of eight 4-byte reads
+//             of rows BK*4 bytes apart;
+//   QUARTERS  each lane's 8 x 8 outputs split into 4 x 4 quarters 32 rows /
+//             columns apart (section 8.5's sub-block split), so the 16-byte
+//             fragment reads of a wave cover 8 contiguous 16-byte words; off:
+//             one contiguous 8 x 8 block per lane;
+//   VEC_STORE C written as 16-byte row pieces (one instruction writes whole
+//             128-byte row segments); off: one float per store;
+//   STAGES    1: load slice, barrier, compute, barrier.  2: the
+//             register-staged double buffer of section 9.5 (issue the loads of
+//             slice t+1, compute slice t, store slice t+1 to the other
+//             buffer, one barrier).
 //
 // Workgroup tile 128 x 128, K slice 8, 256 threads = 4 waves in a 2 x 2 grid,
-// each wave 64 x 64.  Lane l of a wave is (lr, lc) = (l / 8, l % 8) in an
-// 8 x 8 lane grid and owns an 8 x 8 block of C split into 4 x 4 quarters 32
-// rows / columns apart, so that the 16-byte fragment reads of one wave cover
-// 8 distinct, contiguous 16-byte words of LDS (the others are broadcasts).
-// A is stored transposed in LDS (As[k][m], section 7.3) so that both
-// fragments are 16-byte reads.
+// each wave 64 x 64; lane l of a wave is (lr, lc) = (l / 8, l % 8).
 //
 // Every C element is one fused multiply-add chain in increasing k, started
 // from zero: acc = fma(a_ik, b_kj, acc).  The K tail is zero-filled, and
 // fma(0, b, acc) = acc, so the result equals the sequential single-precision
-// fma chain bit for bit.
-//
-// STAGES = 1: load slice, barrier, compute, barrier.  STAGES = 2: the
-// register-staged double buffer of section 9.5 (issue the loads of slice t+1,
-// compute slice t, store slice t+1 to the other buffer, one barrier).
+// fma chain bit for bit in every variant.
 #pragma once
 
 #include "tg_device.hpp"
 
 namespace tg {
 
-template <int STAGES>
+template <int STAGES, bool TRANS_A, bool QUARTERS, bool VEC_STORE>
 struct F32Gemm {
     static constexpr int BM = 128, BN = 128, BK = 8, NT = 256;
     static constexpr int A_BYTES = BK * BM * 4;
@@ -72,23 +80,42 @@ struct F32Gemm {
         TG_LDS float* As = reinterpret_cast<TG_LDS float*>(slot);
         TG_LDS float* Bs = reinterpret_cast<TG_LDS float*>(slot + A_BYTES);
         const int row = t >> 1, kq = 4 * (t & 1);
+        if constexpr (TRANS_A) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) As[(kq + e) * BM + row] = r.a[e];
+            for (int e = 0; e < 4; ++e) As[(kq + e) * BM + row] = r.a[e];
+        } else {
+            *reinterpret_cast<TG_LDS f32x4*>(As + row * BK + kq) = r.a;
+        }
         *reinterpret_cast<TG_LDS f32x4*>(Bs + (t >> 5) * BN + 4 * (t & 31)) = r.b;
     }
 
-    __device__ static __forceinline__ void compute(const TG_LDS char* slot, float (&c)[8][8], int am,
-                                                   int bn) {
+    // Row (column) offset of this lane's fragment element i within the tile.
+    __device__ static __forceinline__ int frag_off(int base, int idx, int i) {
+        if constexpr (QUARTERS) return base + 4 * idx + (i & 3) + 32 * (i >> 2);
+        else return base + 8 * idx + i;
+    }
+
+    __device__ static __forceinline__ void compute(const TG_LDS char* slot, float (&c)[8][8], int wm, int wn,
+                                                   int lr, int lc) {
         const TG_LDS float* As = reinterpret_cast<const TG_LDS float*>(slot);
         const TG_LDS float* Bs = reinterpret_cast<const TG_LDS float*>(slot + A_BYTES);
 #pragma unroll
         for (int k = 0; k < BK; ++k) {
-            const f32x4 a0 = *reinterpret_cast<const TG_LDS f32x4*>(As + k * BM + am);
-            const f32x4 a1 = *reinterpret_cast<const TG_LDS f32x4*>(As + k * BM + am + 32);
-            const f32x4 b0 = *reinterpret_cast<const TG_LDS f32x4*>(Bs + k * BN + bn);
-            const f32x4 b1 = *reinterpret_cast<const TG_LDS f32x4*>(Bs + k * BN + bn + 32);
-            const float a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-            const float b[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+            float a[8], b[8];
+            if constexpr (TRANS_A) {
+                // rows frag_off(wm, lr, 0..3) and frag_off(wm, lr, 4..7) are each 4 contiguous
+                const f32x4 a0 = *reinterpret_cast<const TG_LDS f32x4*>(As + k * BM + frag_off(wm, lr, 0));
+                const f32x4 a1 = *reinterpret_cast<const TG_LDS f32x4*>(As + k * BM + frag_off(wm, lr, 4));
+                a[0] = a0.x; a[1] = a0.y; a[2] = a0.z; a[3] = a0.w;
+                a[4] = a1.x; a[5] = a1.y; a[6] = a1.z; a[7] = a1.w;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) a[i] = As[frag_off(wm, lr, i) * BK + k];
+            }
+            const f32x4 b0 = *reinterpret_cast<const TG_LDS f32x4*>(Bs + k * BN + frag_off(wn, lc, 0));
+            const f32x4 b1 = *reinterpret_cast<const TG_LDS f32x4*>(Bs + k * BN + frag_off(wn, lc, 4));
+            b[0] = b0.x; b[1] = b0.y; b[2] = b0.z; b[3] = b0.w;
+            b[4] = b1.x; b[5] = b1.y; b[6] = b1.z; b[7] = b1.w;
 #pragma unroll
             for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -104,8 +131,7 @@ struct F32Gemm {
         const int m0 = tm * BM, n0 = tn * BN;
         const int wave = wave_id(), lane = lane_id();
         const int lr = lane >> 3, lc = lane & 7;
-        const int am = (wave >> 1) * 64 + 4 * lr;  // first of this thread's rows in the tile
-        const int bn = (wave & 1) * 64 + 4 * lc;   // first of its columns
+        const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
 
         float c[8][8];
 #pragma unroll
@@ -122,7 +148,7 @@ struct F32Gemm {
                 load(r, g, m0, n0, t * BK, ga || t >= full, gb || t >= full);
                 store(smem, r);
                 wait_lds_then_barrier();
-                compute(smem, c, am, bn);
+                compute(smem, c, wm, wn, lr, lc);
                 wait_lds_then_barrier();
             }
         } else {
@@ -136,20 +162,30 @@ struct F32Gemm {
                 const int nxt = t + 1;
                 Staged r;
                 if (nxt < tiles) load(r, g, m0, n0, nxt * BK, ga || nxt >= full, gb || nxt >= full);
-                compute(smem + (t & 1) * SLOT, c, am, bn);
+                compute(smem + (t & 1) * SLOT, c, wm, wn, lr, lc);
                 if (nxt < tiles) store(smem + (nxt & 1) * SLOT, r);
                 wait_lds_then_barrier();
             }
         }
 
         float* C = static_cast<float*>(g.C);
+        const bool vec_ok = VEC_STORE && (m0 + BM <= g.M) && (n0 + BN <= g.N) && (g.ldc % 4 == 0) &&
+                            ((reinterpret_cast<uintptr_t>(C) & 15) == 0);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int row = m0 + am + (i & 3) + 32 * (i >> 2);
+            const int row = m0 + frag_off(wm, lr, i);
+            if (vec_ok) {
+                // columns frag_off(wn, lc, 0..3) and (4..7) are 4 contiguous each
+                *reinterpret_cast<f32x4*>(C + (int64_t)row * g.ldc + n0 + frag_off(wn, lc, 0)) =
+                    f32x4{c[i][0], c[i][1], c[i][2], c[i][3]};
+                *reinterpret_cast<f32x4*>(C + (int64_t)row * g.ldc + n0 + frag_off(wn, lc, 4)) =
+                    f32x4{c[i][4], c[i][5], c[i][6], c[i][7]};
+            } else {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int col = n0 + bn + (j & 3) + 32 * (j >> 2);
-                if (row < g.M && col < g.N) C[(int64_t)row * g.ldc + col] = c[i][j];
+                for (int j = 0; j < 8; ++j) {
+                    const int col = n0 + frag_off(wn, lc, j);
+                    if (row < g.M && col < g.N) C[(int64_t)row * g.ldc + col] = c[i][j];
+                }
             }
         }
     }

@@ -35,6 +35,7 @@ KernelEntry mfma_entry(int dtype) {
     e.frag = FR;
     e.wm = WM;
     e.wn = WN;
+    e.gload_bytes = AC == AC_WIDE ? 16 : 4;
     e.threads = K::NT;
     e.lds_bytes = K::LDS_BYTES;
     e.loads_per_stage = AC == AC_WIDE ? K::N_LD : K::A_DW + K::B_DW;
@@ -63,6 +64,7 @@ KernelEntry naive_entry() {
     e.frag = FR_PER_MMA;
     e.wm = 4;
     e.wn = 1;
+    e.gload_bytes = 0;
     e.threads = K::NT;
     e.lds_bytes = 0;
     e.loads_per_stage = 0;
@@ -73,9 +75,11 @@ KernelEntry naive_entry() {
     return e;
 }
 
-template <int S>
+// fp32 ladder rungs: access / frag fields encode TRANS_A and QUARTERS, the
+// layout field VEC_STORE (see inst_f32.hip).
+template <int S, bool TA, bool QU, bool VS>
 KernelEntry f32_entry() {
-    typedef F32Gemm<S> K;
+    typedef F32Gemm<S, TA, QU, VS> K;
     KernelEntry e{};
     e.dtype = 0;
     e.family = FAM_TILED;
@@ -84,9 +88,11 @@ KernelEntry f32_entry() {
     e.bk = K::BK;
     e.stages = S;
     e.loader = LD_VGPR;
-    e.layout = LY_PLAIN;
-    e.access = AC_WIDE;
+    e.layout = QU ? LY_XOR : LY_PLAIN;    // conflict-free quarters vs contiguous blocks
+    e.access = TA ? AC_WIDE : AC_NARROW;  // A fragment: 16-byte reads of transposed A vs 4-byte reads
     e.frag = FR_REUSE;
+    e.store = VS ? 1 : 2;                 // TGEMM_STORE_VECTOR / TGEMM_STORE_SCALAR
+    e.gload_bytes = 16;                   // A and B always loaded as float4
     e.wm = 2;
     e.wn = 2;
     e.threads = K::NT;
@@ -95,7 +101,8 @@ KernelEntry f32_entry() {
     e.guard_ok = 1;
     e.tail_ok = 1;
     e.fn = gemm_kernel<K, 2>;
-    snprintf(e.name, sizeof e.name, "f32_t128x128x8_w2x2_s%d_vgpr_plain_wide_reuse", S);
+    snprintf(e.name, sizeof e.name, "f32_t128x128x8_w2x2_s%d_%s_%s_%s", S, TA ? "transA" : "rowA",
+             QU ? "quarters" : "blocks", VS ? "vecstore" : "scalarstore");
     return e;
 }
 

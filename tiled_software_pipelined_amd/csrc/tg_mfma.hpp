@@ -633,7 +633,9 @@ struct MfmaGemm {
         }
 
         // Epilogue: accumulators -> C.  Register r of tile (i, j) in lane l is
-        // row 8 (r/4) + 4 (l/32) + r%4, column l%32 of that 32 x 32 tile.
+        // row 8 (r/4) + 4 (l/32) + r%4, column l%32 of that 32 x 32 tile, so
+        // each store instruction writes two full 128-byte row segments.  C is
+        // written once and never re-read here: non-temporal stores.
         Out* C = static_cast<Out*>(g.C);
         const bool inside = (m0 + BM <= g.M) && (n0 + BN <= g.N);
 #pragma unroll
@@ -645,7 +647,7 @@ struct MfmaGemm {
                     const int row = m0 + wm0 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
                     const int col = n0 + wn0 + 32 * j + (lane & 31);
                     if (inside || (row < g.M && col < g.N))
-                        C[(int64_t)row * g.ldc + col] = static_cast<Out>(acc[i][j][r]);
+                        __builtin_nontemporal_store(static_cast<Out>(acc[i][j][r]), &C[(int64_t)row * g.ldc + col]);
                 }
     }
 };

@@ -52,11 +52,8 @@ void init_registry() {
 
 int elem_size(int dtype) { return dtype == TGEMM_F32 ? 4 : dtype == TGEMM_BF16 ? 2 : 1; }
 
-// Bytes moved per 16-byte chunk / per narrow access by an entry's loader.
-int access_bytes(const KernelEntry& e) {
-    if (e.family == tg::FAM_NAIVE) return 0;
-    return e.access == tg::AC_WIDE ? 16 : 4;
-}
+// Width of an entry's unguarded global loads (0: it only does element loads).
+int access_bytes(const KernelEntry& e) { return e.gload_bytes; }
 
 // Leading-dimension checks: can every row of the operand be read with
 // `bytes`-wide aligned accesses?  (Pointer alignment is checked at run time.)
@@ -80,7 +77,7 @@ bool matches(const KernelEntry& e, const tgemm_variant& v) {
     return field_ok(v.tile_m, e.bm) && field_ok(v.tile_n, e.bn) && field_ok(v.tile_k, e.bk) &&
            field_ok(v.stages, e.stages) && field_ok(v.loader, e.loader) &&
            field_ok(v.lds_layout, e.layout) && field_ok(v.access, e.access) && field_ok(v.frag, e.frag) &&
-           field_ok(v.waves_m, e.wm) && field_ok(v.waves_n, e.wn);
+           field_ok(v.waves_m, e.wm) && field_ok(v.waves_n, e.wn) && field_ok(v.store, e.store);
 }
 
 const KernelEntry* find_entry(int dtype, const tgemm_variant& v) {
@@ -147,6 +144,7 @@ void entry_to_variant(const KernelEntry& e, int32_t wg_group, tgemm_variant* v) 
     v->wg_group = wg_group;
     v->waves_m = e.wm;
     v->waves_n = e.wn;
+    v->store = e.store;
 }
 
 // Per-device gfx950 check, cached.
@@ -227,7 +225,7 @@ tgemm_plan* gemm_plan_variant(int64_t M, int64_t N, int64_t K, int32_t dtype, in
     const KernelEntry* e = nullptr;
     if (v.kernel == TGEMM_KERNEL_AUTO && v.tile_m == 0 && v.tile_n == 0 && v.tile_k == 0 && v.stages == 0 &&
         v.loader == 0 && v.lds_layout == 0 && v.access == 0 && v.frag == 0 && v.waves_m == 0 &&
-        v.waves_n == 0) {
+        v.waves_n == 0 && v.store == 0) {
         e = default_entry(dtype, M, N, K);
     } else {
         e = find_entry(dtype, v);

@@ -36,7 +36,7 @@ class Variant(ctypes.Structure):
     """Mirror of ``tgemm_variant``; zero fields mean "default"."""
     _fields_ = [(n, ctypes.c_int32) for n in (
         "kernel", "tile_m", "tile_n", "tile_k", "stages", "loader", "lds_layout", "access", "frag",
-        "wg_group", "waves_m", "waves_n")]
+        "wg_group", "waves_m", "waves_n", "store")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
