@@ -105,6 +105,15 @@ def test_unaligned_leading_dimension_uses_guarded_register_loader():
     assert info.b_guarded == 1 and info.a_guarded == 0
     assert info.variant.loader == tl.LOADER_VGPR
     assert info.grid == 16 * 17
+    # same tile and wave grid as the aligned default
+    d = tl.Plan(4096, 4096, 4096, tl.BF16).info().variant
+    v = info.variant
+    assert (v.tile_m, v.tile_n, v.tile_k, v.waves_m, v.waves_n) == (d.tile_m, d.tile_n, d.tile_k, d.waves_m,
+                                                                    d.waves_n)
+    # a small unaligned problem keeps a small register-staged tile
+    for dtype in (tl.BF16, tl.I8):
+        v = tl.Plan(150, 131, 101, dtype).info().variant
+        assert v.loader == tl.LOADER_VGPR and (v.tile_m, v.tile_n) == (128, 128), dtype
 
 
 def test_lds_budget_of_stage_ring():

@@ -232,6 +232,69 @@ def test_unaligned_leading_dimensions_and_pointers(dtype):
     _assert_parity(C.cpu(), A2, B2, dtype)
 
 
+def _exact_device_view(t, ld, off):
+    """t copied to the GPU with row stride ld, starting `off` elements into a
+    buffer that ends exactly at t's last element."""
+    rows, cols = t.shape
+    buf = torch.zeros(off + (rows - 1) * ld + cols, dtype=t.dtype)
+    buf.as_strided((rows, cols), (ld, 1), off).copy_(t)
+    return buf.cuda().as_strided((rows, cols), (ld, 1), off)
+
+
+def _run_views(Ad, Bd, variant):
+    out_dtype = torch.int32 if Ad.dtype == torch.int8 else torch.float32
+    C = torch.full((Ad.shape[0], Bd.shape[1]), -7, dtype=out_dtype, device="cuda")
+    tl.gemm(Ad, Bd, out=C, variant=variant)
+    torch.cuda.synchronize()
+    return C.cpu()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "i8"])
+def test_shifted_loads_every_byte_offset(dtype):
+    # Rows that are not 16-byte aligned go through pairs of aligned 16-byte
+    # loads and a funnel shift.  Odd leading dimensions give consecutive rows
+    # every byte offset (all 16 for int8, all 8 even ones for bf16); the
+    # pointer offsets put the first and last pairs against the ends of
+    # exactly sized buffers, where the checked form must fall back to element
+    # loads.  K spans the first, interior, last and partial slices.  Every
+    # register-staged variant must match the oracle and, bit for bit, itself
+    # on 16-byte aligned copies of the same operands.
+    ce = 8 if dtype == "bf16" else 16
+    vs = [v for v in _variants(dtype, tiled_only=True)
+          if v.loader == tl.LOADER_VGPR and v.access == tl.ACCESS_WIDE]
+    assert vs
+    for v in vs:
+        M, N, K = 161, 208, 5 * v.tile_k + 3
+        A = inputs.operand(KIND[dtype], M, K, 61 + K)
+        B = inputs.operand(KIND[dtype], K, N, 62 + K)
+        lda_al = (K + ce - 1) // ce * ce
+        ref = _run_views(_exact_device_view(A, lda_al, 0), _exact_device_view(B, N, 0), v)
+        _assert_parity(ref, A, B, dtype)
+        for (lda, ldb, oa, ob) in [(K, N + 1, 0, 0), (K + 2, N + 3, 1, ce - 1), (lda_al, N, ce // 2, 1),
+                                   (K + 1, N + ce + 1, ce - 1, ce // 2)]:
+            print("shifted", dtype, _vname(v), lda, ldb, oa, ob, flush=True)
+            C = _run_views(_exact_device_view(A, lda, oa), _exact_device_view(B, ldb, ob), v)
+            assert torch.equal(C, ref), (_vname(v), lda, ldb, oa, ob)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "i8"])
+def test_shifted_loads_few_slices(dtype):
+    # one, two and three whole slices (no interior slice, or one), with and
+    # without a partial slice, on every register-staged variant
+    ce = 8 if dtype == "bf16" else 16
+    for v in _variants(dtype, tiled_only=True):
+        if v.loader != tl.LOADER_VGPR or v.access != tl.ACCESS_WIDE:
+            continue
+        for K in (v.tile_k, v.tile_k + 5, 2 * v.tile_k, 2 * v.tile_k + 5, 3 * v.tile_k, 3 * v.tile_k + 5):
+            M, N = 300, 520
+            A = inputs.operand(KIND[dtype], M, K, 71 + K)
+            B = inputs.operand(KIND[dtype], K, N, 72 + K)
+            C = _run_views(_exact_device_view(A, K + 1, 1), _exact_device_view(B, N + 1, ce - 1), v)
+            C_ref, S = _oracle(A, B, dtype)
+            ok, rep = check(C.numpy(), C_ref, S, dtype, K)
+            assert ok, (_vname(v), K, rep)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "i8"])
 def test_K_zero_writes_zeros(dtype):
     A = torch.zeros((70, 0), dtype=inputs.KINDS[KIND[dtype]])

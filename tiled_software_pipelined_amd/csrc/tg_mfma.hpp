@@ -9,9 +9,12 @@
 // (same page, sections 9-10; the "流水化 GPU 内核" skill, Step 3: prologue,
 // steady loop, epilogue):
 //
-//   prologue : start the loads of slices 0 .. STAGES-2
-//   slice t  : wait for slice t, barrier, start slice t+STAGES-1 into the slot
-//              slice t-1 just left, then multiply slice t out of LDS
+//   prologue : start the loads of slices 0 .. STAGES-2; wait for slice 0
+//   slice t  : multiply slice t out of LDS, one matrix-core K step at a time,
+//              reading the fragments of the next K step ahead; inside the
+//              last K step wait for slice t+1, barrier, start slice
+//              t+STAGES into the slot slice t just left and read slice
+//              t+1's first fragments
 //
 // so that the global->LDS copy of later slices overlaps the matrix-core work
 // on slice t.  Two loaders are built (the skill's Step 2 choice):
@@ -31,7 +34,9 @@
 // valid address (they only feed C elements that are never stored); the last,
 // partial K slice is loaded element by element with zero fill (the skill's
 // pitfall list: boundary tiles need a guarded fallback); an operand whose rows
-// are not 16-byte aligned is loaded element by element for every slice.
+// are not 16-byte aligned (odd leading dimension, offset pointer) goes through
+// the register-staged loader, each chunk funnel-shifted out of two aligned
+// 16-byte loads.
 #pragma once
 
 #include "tg_device.hpp"
@@ -128,6 +133,9 @@ struct MfmaGemm {
     }
 
     // ---- global loads --------------------------------------------------------
+    enum { LM_ALIGNED = 0, LM_SHIFTED = 1, LM_SHIFTED_EDGE = 2, LM_ELEMENT = 3 };
+    // the mode of a first or last whole slice
+    static constexpr int edge_mode(int m) { return m == LM_SHIFTED ? LM_SHIFTED_EDGE : m; }
     // Elements [start, start + CE) of one row, zero where index >= limit.
     __device__ static __forceinline__ i32x4 load_chunk_guarded(const T* rowp, int start, int limit) {
         union { i32x4 v; T e[CE]; } u;
@@ -139,6 +147,42 @@ struct MfmaGemm {
         return u.v;
     }
 
+    // 16 bytes starting at p, for an operand whose valid bytes are [beg, end)
+    // and whose rows are not 16-byte aligned: the two aligned 16-byte blocks
+    // that cover them are loaded and the wanted bytes funnel-shifted out of
+    // the pair (2 wide loads and ~15 ALU operations instead of CE element
+    // loads).  CHECK: where the pair would leave [beg, end) the chunk falls
+    // back to element loads, zero past end.  Without CHECK the caller has
+    // shown that the pair lies inside (see staged_loop).
+    template <bool CHECK>
+    __device__ static __forceinline__ i32x4 load_chunk_shifted(const T* p, uintptr_t beg, uintptr_t end) {
+        const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+        const uintptr_t lo = a & ~uintptr_t(15);
+        if (!CHECK || (lo >= beg && lo + 32 <= end)) {
+            const i32x4 x = *reinterpret_cast<const i32x4*>(lo);
+            const i32x4 y = *reinterpret_cast<const i32x4*>(lo + 16);
+            const uint32_t sh = uint32_t(a & 15);
+            // Named scalars, not an array: selects between elements of a
+            // local array are turned into a dynamically indexed stack copy.
+            const bool s8 = sh & 8, s4 = sh & 4;
+            const uint32_t t0 = s8 ? x[2] : x[0], t1 = s8 ? x[3] : x[1], t2 = s8 ? y[0] : x[2];
+            const uint32_t t3 = s8 ? y[1] : x[3], t4 = s8 ? y[2] : y[0], t5 = s8 ? y[3] : y[1];
+            const uint32_t u0 = s4 ? t1 : t0, u1 = s4 ? t2 : t1, u2 = s4 ? t3 : t2;
+            const uint32_t u3 = s4 ? t4 : t3, u4 = s4 ? t5 : t4;
+            const uint32_t b = sh & 3;
+            i32x4 out;
+            out[0] = int32_t(__builtin_amdgcn_alignbyte(u1, u0, b));
+            out[1] = int32_t(__builtin_amdgcn_alignbyte(u2, u1, b));
+            out[2] = int32_t(__builtin_amdgcn_alignbyte(u3, u2, b));
+            out[3] = int32_t(__builtin_amdgcn_alignbyte(u4, u3, b));
+            return out;
+        }
+        union { i32x4 v; T e[CE]; } u;
+#pragma unroll
+        for (int e = 0; e < CE; ++e) u.e[e] = a + (e + 1) * ESZ <= end ? p[e] : T(0);
+        return u.v;
+    }
+
     struct Staged {
         i32x4 a[WIDE ? A_PER : 1];
         i32x4 b[WIDE ? B_PER : 1];
@@ -146,21 +190,35 @@ struct MfmaGemm {
         int32_t bd[WIDE ? 1 : B_DW];
     };
 
-    // Register-staged load of slice k0 (guard_a/guard_b: element loads with
-    // zero fill at k >= K, and at n >= N for B).
-    __device__ static __forceinline__ void load_regs(Staged& r, const GemmArgs& g, int m0, int n0,
-                                                     int k0, bool guard_a, bool guard_b) {
+    // Register-staged load of slice k0.  Per operand, a load mode:
+    //   LM_ALIGNED : 16-byte loads (rows 16-byte aligned, N a multiple of CE);
+    //   LM_SHIFTED : rows not 16-byte aligned, slice inside K: funnel-shifted
+    //                pairs of aligned loads (values at n >= N are whatever
+    //                follows in memory; they only reach C columns that are
+    //                never stored);
+    //   LM_SHIFTED_EDGE : the same with a bounds check per pair, for the
+    //                first and last whole slices;
+    //   LM_ELEMENT : element loads with zero fill at k >= K (and n >= N for
+    //                B): the partial last K slice.
+    template <int MODE_A, int MODE_B>
+    __device__ static __forceinline__ void load_regs(Staged& r, const GemmArgs& g, int m0, int n0, int k0) {
         const T* A = static_cast<const T*>(g.A);
         const T* B = static_cast<const T*>(g.B);
         const int tid = threadIdx.x;
         if constexpr (WIDE) {
+            const uintptr_t a_beg = reinterpret_cast<uintptr_t>(A);
+            const uintptr_t a_end = a_beg + ((int64_t)(g.M - 1) * g.lda + g.K) * ESZ;
+            const uintptr_t b_beg = reinterpret_cast<uintptr_t>(B);
+            const uintptr_t b_end = b_beg + ((int64_t)(g.K - 1) * g.ldb + g.N) * ESZ;
 #pragma unroll
             for (int q = 0; q < A_PER; ++q) {
                 const int p = q * NT + tid;
                 const int row = p / CA, c = p % CA;
                 const T* rowp = A + (int64_t)min(m0 + row, g.M - 1) * g.lda;
                 const int kc = k0 + c * CE;
-                if (!guard_a) r.a[q] = *reinterpret_cast<const i32x4*>(rowp + kc);
+                if constexpr (MODE_A == LM_ALIGNED) r.a[q] = *reinterpret_cast<const i32x4*>(rowp + kc);
+                else if constexpr (MODE_A != LM_ELEMENT)
+                    r.a[q] = load_chunk_shifted<MODE_A == LM_SHIFTED_EDGE>(rowp + kc, a_beg, a_end);
                 else r.a[q] = load_chunk_guarded(rowp, kc, g.K);
             }
 #pragma unroll
@@ -169,12 +227,13 @@ struct MfmaGemm {
                 const int k = p / CB, c = p % CB;
                 const int gk = k0 + k;
                 const int nc = n0 + c * CE;
-                if (!guard_b) {
-                    r.b[q] = *reinterpret_cast<const i32x4*>(B + (int64_t)gk * g.ldb + min(nc, g.N - CE));
-                } else if (gk < g.K) {
-                    r.b[q] = load_chunk_guarded(B + (int64_t)gk * g.ldb, nc, g.N);
+                const T* rowp = B + (int64_t)gk * g.ldb;
+                if constexpr (MODE_B == LM_ALIGNED) {
+                    r.b[q] = *reinterpret_cast<const i32x4*>(rowp + min(nc, g.N - CE));
+                } else if constexpr (MODE_B != LM_ELEMENT) {
+                    r.b[q] = load_chunk_shifted<MODE_B == LM_SHIFTED_EDGE>(rowp + min(nc, g.N - 1), b_beg, b_end);
                 } else {
-                    r.b[q] = i32x4{0, 0, 0, 0};
+                    r.b[q] = gk < g.K ? load_chunk_guarded(rowp, nc, g.N) : i32x4{0, 0, 0, 0};
                 }
             }
         } else {
@@ -185,7 +244,7 @@ struct MfmaGemm {
                 const int row = p / (KB / 4), d = p % (KB / 4);
                 const T* rowp = A + (int64_t)min(m0 + row, g.M - 1) * g.lda;
                 const int kc = k0 + d * EPD;
-                if (!guard_a) {
+                if constexpr (MODE_A == LM_ALIGNED) {
                     r.ad[q] = *reinterpret_cast<const int32_t*>(rowp + kc);
                 } else {
                     union { int32_t v; T e[EPD]; } u;
@@ -200,7 +259,7 @@ struct MfmaGemm {
                 const int k = p / (NB / 4), d = p % (NB / 4);
                 const int gk = k0 + k;
                 const int nc = n0 + d * EPD;
-                if (!guard_b) {
+                if constexpr (MODE_B == LM_ALIGNED) {
                     r.bd[q] = *reinterpret_cast<const int32_t*>(B + (int64_t)gk * g.ldb + min(nc, g.N - EPD));
                 } else {
                     union { int32_t v; T e[EPD]; } u;
@@ -516,6 +575,87 @@ struct MfmaGemm {
 
     // Wait until this wave's copies of slice t are in LDS (`ahead` later
     // slices may stay in flight), then barrier.
+    // K loop of the register-staged loaders: the `full` whole slices with
+    // MODE_A / MODE_B loads, then the partial last slice (if tiles > full)
+    // with element loads.  STAGES == 1: load, store, barrier, multiply,
+    // barrier.  STAGES == 2: the loads of slice t+1 are issued before the
+    // multiply of slice t and written to the other slot after it, one barrier
+    // per slice.
+    //
+    // Shifted pairs need no bounds check on the interior slices 1 .. full-2
+    // (a slice is at least 64 bytes of a row, lda >= K, ldb >= N >= 1): an A
+    // pair starts at k >= BK, so at least 64 bytes past A's first element,
+    // and ends at most 16 bytes past its chunk, whose k < (full-1) BK, so
+    // before the end of row m <= M-1 at K; a B pair lies in a row
+    // BK <= k < K - BK, at least BK rows (64 bytes) from both ends of B.
+    // Only the first and last whole slices take the checked form.
+    template <int MODE_A, int MODE_B>
+    __device__ static __forceinline__ void staged_loop(Acc (&acc)[FM][FN], TG_LDS char* smem, const GemmArgs& g,
+                                                       int m0, int n0, int wm0, int wn0, int lane, int full,
+                                                       int tiles) {
+        constexpr int EA = edge_mode(MODE_A), EB = edge_mode(MODE_B);
+        if constexpr (STAGES == 1) {
+            for (int t = 0; t < full; ++t) {
+                Staged r;
+                if (t == 0 || t == full - 1) load_regs<EA, EB>(r, g, m0, n0, t * BK);
+                else load_regs<MODE_A, MODE_B>(r, g, m0, n0, t * BK);
+                store_regs(smem, r);
+                wait_lds_then_barrier();
+                compute(smem, acc, wm0, wn0, lane);
+                wait_lds_then_barrier();  // all reads done before the next overwrite
+            }
+            if (full < tiles) {
+                Staged r;
+                load_regs<LM_ELEMENT, LM_ELEMENT>(r, g, m0, n0, full * BK);
+                store_regs(smem, r);
+                wait_lds_then_barrier();
+                compute(smem, acc, wm0, wn0, lane);
+            }
+        } else {
+            if (full == 0) {
+                if (tiles > 0) {
+                    Staged r;
+                    load_regs<LM_ELEMENT, LM_ELEMENT>(r, g, m0, n0, 0);
+                    store_regs(smem, r);
+                    wait_lds_then_barrier();
+                    compute(smem, acc, wm0, wn0, lane);
+                }
+                return;
+            }
+            {
+                Staged r;
+                load_regs<EA, EB>(r, g, m0, n0, 0);
+                store_regs(smem, r);
+                wait_lds_then_barrier();
+            }
+            int t = 0;
+            for (; t + 2 < full; ++t) {  // loads slices 1 .. full-2
+                Staged r;
+                load_regs<MODE_A, MODE_B>(r, g, m0, n0, (t + 1) * BK);
+                compute(smem + (t & 1) * SLOT, acc, wm0, wn0, lane);
+                store_regs(smem + ((t + 1) & 1) * SLOT, r);
+                wait_lds_then_barrier();
+            }
+            if (t + 1 < full) {  // loads the last whole slice
+                Staged r;
+                load_regs<EA, EB>(r, g, m0, n0, (t + 1) * BK);
+                compute(smem + (t & 1) * SLOT, acc, wm0, wn0, lane);
+                store_regs(smem + ((t + 1) & 1) * SLOT, r);
+                wait_lds_then_barrier();
+                ++t;
+            }
+            if (full < tiles) {  // loads the partial slice
+                Staged r;
+                load_regs<LM_ELEMENT, LM_ELEMENT>(r, g, m0, n0, full * BK);
+                compute(smem + (t & 1) * SLOT, acc, wm0, wn0, lane);
+                store_regs(smem + ((t + 1) & 1) * SLOT, r);
+                wait_lds_then_barrier();
+                ++t;
+            }
+            compute(smem + (t & 1) * SLOT, acc, wm0, wn0, lane);
+        }
+    }
+
     __device__ static __forceinline__ void wait_slice(int ahead) {
         if constexpr (STAGES >= 4) {
             if (ahead >= 2) { wait_vm_then_barrier<2 * N_LD>(); return; }
@@ -526,7 +666,7 @@ struct MfmaGemm {
         wait_vm_then_barrier<0>();
     }
 
-    __device__ static void run(const GemmArgs& g) {
+    __device__ static __forceinline__ void run(const GemmArgs& g) {
         __shared__ __attribute__((aligned(1024))) char smem_raw[LDS_BYTES];
         TG_LDS char* smem = (TG_LDS char*)(smem_raw);
 
@@ -548,7 +688,6 @@ struct MfmaGemm {
 
         const int tiles = (g.K + BK - 1) / BK;
         const int full = g.K / BK;  // slices with no K tail
-        const bool ga = g.a_guard != 0, gb = g.b_guard != 0;
 
         if constexpr (DIRECT) {
             DirectOffsets off;
@@ -599,36 +738,19 @@ struct MfmaGemm {
                 // No copy is in flight (the last wait drained them) and every
                 // wave passed the barrier that ended its reads of that slot.
                 Staged r;
-                load_regs(r, g, m0, n0, full * BK, true, true);
+                load_regs<LM_ELEMENT, LM_ELEMENT>(r, g, m0, n0, full * BK);
                 store_regs(smem + (full % STAGES) * SLOT, r);
                 wait_lds_then_barrier();
                 compute(smem + (full % STAGES) * SLOT, acc, wm0, wn0, lane);
             }
-        } else if constexpr (STAGES == 1) {
-            for (int t = 0; t < tiles; ++t) {
-                const bool tail = t >= full;
-                Staged r;
-                load_regs(r, g, m0, n0, t * BK, ga || tail, gb || tail);
-                store_regs(smem, r);
-                wait_lds_then_barrier();
-                compute(smem, acc, wm0, wn0, lane);
-                wait_lds_then_barrier();  // all reads done before the next overwrite
-            }
         } else {
-            // Register-staged double buffer: one barrier per slice.
-            if (tiles > 0) {
-                Staged r;
-                load_regs(r, g, m0, n0, 0, ga || full == 0, gb || full == 0);
-                store_regs(smem, r);
-                wait_lds_then_barrier();
-            }
-            for (int t = 0; t < tiles; ++t) {
-                const int nxt = t + 1;
-                Staged r;
-                if (nxt < tiles) load_regs(r, g, m0, n0, nxt * BK, ga || nxt >= full, gb || nxt >= full);
-                compute(smem + (t & 1) * SLOT, acc, wm0, wn0, lane);
-                if (nxt < tiles) store_regs(smem + (nxt & 1) * SLOT, r);
-                wait_lds_then_barrier();
+            // register-staged loaders: one instantiation per pair of load modes
+            if (g.a_guard) {
+                if (g.b_guard) staged_loop<LM_SHIFTED, LM_SHIFTED>(acc, smem, g, m0, n0, wm0, wn0, lane, full, tiles);
+                else staged_loop<LM_SHIFTED, LM_ALIGNED>(acc, smem, g, m0, n0, wm0, wn0, lane, full, tiles);
+            } else {
+                if (g.b_guard) staged_loop<LM_ALIGNED, LM_SHIFTED>(acc, smem, g, m0, n0, wm0, wn0, lane, full, tiles);
+                else staged_loop<LM_ALIGNED, LM_ALIGNED>(acc, smem, g, m0, n0, wm0, wn0, lane, full, tiles);
             }
         }
 

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <cstdlib>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -118,17 +119,28 @@ const KernelEntry* default_entry(int dtype, int64_t M, int64_t N, int64_t K) {
     return find_entry(dtype, v);
 }
 
-// A register-staged entry with the same tile (else any wide one) for
-// operands that need guarded loads.
+// A register-staged entry for operands that need guarded loads: the same
+// tile and wave grid, else the same tile, else the double-buffered wide one
+// whose tile is nearest in size (small tiles keep small problems spread over
+// the GPU).
 const KernelEntry* guard_capable(const KernelEntry* e) {
     if (e->guard_ok) return e;
+    for (int same_waves = 1; same_waves >= 0; --same_waves)
+        for (const KernelEntry& c : g_reg[e->dtype])
+            if (c.guard_ok && c.family == e->family && c.bm == e->bm && c.bn == e->bn && c.bk == e->bk &&
+                c.access == tg::AC_WIDE && c.stages == 2 && (!same_waves || (c.wm == e->wm && c.wn == e->wn)))
+                return &c;
+    const KernelEntry* best = nullptr;
+    int best_d = INT_MAX;
     for (const KernelEntry& c : g_reg[e->dtype])
-        if (c.guard_ok && c.family == e->family && c.bm == e->bm && c.bn == e->bn && c.bk == e->bk &&
-            c.access == tg::AC_WIDE && c.stages == 2)
-            return &c;
-    for (const KernelEntry& c : g_reg[e->dtype])
-        if (c.guard_ok && c.family == tg::FAM_TILED && c.access == tg::AC_WIDE && c.stages == 2) return &c;
-    return nullptr;
+        if (c.guard_ok && c.family == tg::FAM_TILED && c.access == tg::AC_WIDE && c.stages == 2) {
+            const int d = abs(c.bm - e->bm) + abs(c.bn - e->bn);
+            if (d < best_d) {
+                best = &c;
+                best_d = d;
+            }
+        }
+    return best;
 }
 
 void entry_to_variant(const KernelEntry& e, int32_t wg_group, tgemm_variant* v) {
