@@ -104,16 +104,31 @@ def test_unaligned_leading_dimension_uses_guarded_register_loader():
     info = tl.Plan(4095, 4097, 4104, tl.BF16).info()
     assert info.b_guarded == 1 and info.a_guarded == 0
     assert info.variant.loader == tl.LOADER_VGPR
-    assert info.grid == 16 * 17
-    # same tile and wave grid as the aligned default
-    d = tl.Plan(4096, 4096, 4096, tl.BF16).info().variant
-    v = info.variant
-    assert (v.tile_m, v.tile_n, v.tile_k, v.waves_m, v.waves_n) == (d.tile_m, d.tile_n, d.tile_k, d.waves_m,
-                                                                    d.waves_n)
+    # 256 x 256 tiles would be 272 workgroups, one per compute unit: two
+    # rounds, 53 % full; the 128 x 128 register-staged tile wins on rate x fill
+    assert (info.variant.tile_m, info.variant.tile_n) == (128, 128)
+    assert info.grid == 32 * 33
     # a small unaligned problem keeps a small register-staged tile
     for dtype in (tl.BF16, tl.I8):
         v = tl.Plan(150, 131, 101, dtype).info().variant
         assert v.loader == tl.LOADER_VGPR and (v.tile_m, v.tile_n) == (128, 128), dtype
+    # an explicit direct-loader request falls back to the register-staged
+    # kernel with the same tile and wave grid
+    req = tl.Variant(kernel=tl.KERNEL_TILED, tile_m=256, tile_n=256, tile_k=64, waves_n=4,
+                     loader=tl.LOADER_DIRECT)
+    v = tl.Plan(4095, 4097, 4104, tl.BF16, variant=req).info().variant
+    assert (v.loader, v.tile_m, v.tile_n, v.tile_k, v.waves_m, v.waves_n) == (tl.LOADER_VGPR, 256, 256, 64, 2, 4)
+
+
+def test_default_tile_weighs_rate_against_grid_fill():
+    # aligned: 4096 x 4352 is 272 tiles of 256 x 256 (53 % full over two
+    # rounds) against 1088 tiles of 128 x 128 (71 % of three per unit over two
+    # rounds) at 0.72 of the rate: the big tile still wins
+    assert tl.Plan(4096, 4352, 4096, tl.BF16).info().variant.tile_m == 256
+    assert tl.Plan(4096, 4096, 4096, tl.BF16).info().variant.tile_m == 256
+    # guarded 4096 x 4097 (N not a whole number of 16-byte chunks)
+    info = tl.Plan(4096, 4097, 4096, tl.BF16).info()
+    assert info.b_guarded == 1 and info.variant.tile_m == 128
 
 
 def test_lds_budget_of_stage_ring():

@@ -295,6 +295,31 @@ def test_shifted_loads_few_slices(dtype):
             assert ok, (_vname(v), K, rep)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "i8"])
+def test_streaming_and_plain_C_stores_agree(dtype):
+    # C rows 128-byte aligned take non-temporal stores, others plain ones;
+    # both must write the same values and nothing outside the M x N window
+    M, N, K = 300, 256, 192
+    A = inputs.operand(KIND[dtype], M, K, 81)
+    B = inputs.operand(KIND[dtype], K, N, 82)
+    Ad, Bd = _to_device(A), _to_device(B)
+    out_dtype = torch.int32 if dtype == "i8" else torch.float32
+    ref = None
+    for ldc, off in [(N, 0), (N + 1, 0), (N + 32, 0), (N, 1), (N + 5, 3)]:
+        buf = torch.full((off + M * ldc + 64,), -7, dtype=out_dtype, device="cuda")
+        C = buf.as_strided((M, N), (ldc, 1), off)
+        tl.gemm(Ad, Bd, out=C)
+        torch.cuda.synchronize()
+        got = C.cpu().clone()
+        mask = torch.ones(buf.numel(), dtype=torch.bool)
+        mask.as_strided((M, N), (ldc, 1), off).fill_(False)
+        assert (buf.cpu()[mask] == -7).all(), (ldc, off)
+        if ref is None:
+            ref = got
+            _assert_parity(got, A, B, dtype)
+        assert torch.equal(got, ref), (ldc, off)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "i8"])
 def test_K_zero_writes_zeros(dtype):
     A = torch.zeros((70, 0), dtype=inputs.KINDS[KIND[dtype]])

@@ -16,8 +16,9 @@ struct GemmArgs {
     int32_t tiles_m, tiles_n;  // ceil(M / BM), ceil(N / BN)
     int64_t lda, ldb, ldc;
     int32_t wg_group;          // <= 0: row-major workgroup order
-    int32_t a_guard;           // 1: every A tile through the guarded element loader
-    int32_t b_guard;           // 1: every B tile through the guarded element loader
+    int32_t a_guard;           // 1: A rows not 16-byte aligned (register-staged shifted loads)
+    int32_t b_guard;           // 1: B rows not 16-byte aligned or N not a whole number of chunks
+    int32_t c_stream;          // 1: C rows 128-byte aligned: non-temporal (streaming) C stores
 };
 
 typedef void (*KernelFn)(GemmArgs);

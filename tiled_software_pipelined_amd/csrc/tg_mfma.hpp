@@ -656,6 +656,25 @@ struct MfmaGemm {
         }
     }
 
+    template <bool STREAM>
+    __device__ static __forceinline__ void store_c(Out* C, const GemmArgs& g, const Acc (&acc)[FM][FN], int r0,
+                                                   int c0, int lane, bool inside) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = r0 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    const int col = c0 + 32 * j + (lane & 31);
+                    if (inside || (row < g.M && col < g.N)) {
+                        Out* dst = &C[(int64_t)row * g.ldc + col];
+                        if constexpr (STREAM) __builtin_nontemporal_store(static_cast<Out>(acc[i][j][r]), dst);
+                        else *dst = static_cast<Out>(acc[i][j][r]);
+                    }
+                }
+    }
+
     __device__ static __forceinline__ void wait_slice(int ahead) {
         if constexpr (STAGES >= 4) {
             if (ahead >= 2) { wait_vm_then_barrier<2 * N_LD>(); return; }
@@ -756,21 +775,16 @@ struct MfmaGemm {
 
         // Epilogue: accumulators -> C.  Register r of tile (i, j) in lane l is
         // row 8 (r/4) + 4 (l/32) + r%4, column l%32 of that 32 x 32 tile, so
-        // each store instruction writes two full 128-byte row segments.  C is
-        // written once and never re-read here: non-temporal stores.
+        // each store instruction writes two 128-byte row segments.  C is
+        // written once and never re-read here: when its rows are 128-byte
+        // aligned each segment is one whole cache line and the stores are
+        // non-temporal; otherwise every segment straddles two lines, and
+        // ordinary stores let the L2 merge the halves before they reach HBM
+        // (about 20 % faster than streaming the partial lines at 4096^3).
         Out* C = static_cast<Out*>(g.C);
         const bool inside = (m0 + BM <= g.M) && (n0 + BN <= g.N);
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = m0 + wm0 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                    const int col = n0 + wn0 + 32 * j + (lane & 31);
-                    if (inside || (row < g.M && col < g.N))
-                        __builtin_nontemporal_store(static_cast<Out>(acc[i][j][r]), &C[(int64_t)row * g.ldc + col]);
-                }
+        if (g.c_stream) store_c<true>(C, g, acc, m0 + wm0, n0 + wn0, lane, inside);
+        else store_c<false>(C, g, acc, m0 + wm0, n0 + wn0, lane, inside);
     }
 };
 

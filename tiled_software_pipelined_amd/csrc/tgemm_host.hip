@@ -87,34 +87,64 @@ const KernelEntry* find_entry(int dtype, const tgemm_variant& v) {
     return nullptr;
 }
 
-// Default choice for a shape: the largest tile that still gives the GPU
-// (256 compute units) at least half a workgroup per unit; small problems
-// step down to 128 x 128 and then 64 x 64 tiles.  Short K (a few slices per
-// tile) also takes 128 x 128: with one wave of 256 x 256 tiles every
-// workgroup writes its C tile at the same moment, unoverlapped, and at short
-// K that write is most of the work.
-const KernelEntry* default_entry(int dtype, int64_t M, int64_t N, int64_t K) {
+// Default choice for a shape.  Small problems (fewer than half a workgroup
+// per compute unit on 256 x 256 tiles, or short K) take 128 x 128 and then
+// 64 x 64 tiles.  Otherwise the 8-wave 256 x 256 tile and the 128 x 128 tile
+// compete on rate x fill: `rate` is each tile's throughput relative to the
+// 256 x 256 tile on a full GPU (median of interleaved runs at 4096^3),
+// `fill` the fraction of workgroup slots (256 compute units x workgroups
+// resident per unit) busy over the ceil(tiles / slots) rounds the grid
+// takes.  4095 x 4097 makes 272 tiles of 256 x 256: two rounds for one
+// workgroup per unit, 53 % full.  With `guarded` (an operand whose rows are
+// not 16-byte aligned) the candidates are the register-staged tiles.
+// Short K (a few slices per tile) also takes 128 x 128: with one round of
+// 256 x 256 tiles every workgroup writes its C tile at the same moment,
+// unoverlapped, and at short K that write is most of the work.
+struct TileCandidate {
+    int bm, stages, loader, waves_n;
+    double rate;  // relative to the 256 x 256 direct (or register-staged) tile
+    int per_cu;   // workgroups resident per compute unit (LDS / registers)
+};
+
+double fill(int64_t tiles, int per_cu) {
+    const int64_t slots = 256 * (int64_t)per_cu;
+    const int64_t rounds = (tiles + slots - 1) / slots;
+    return (double)tiles / (double)(rounds * slots);
+}
+
+const KernelEntry* default_entry(int dtype, int64_t M, int64_t N, int64_t K, bool guarded) {
     tgemm_variant v{};
     v.kernel = TGEMM_KERNEL_TILED;
     if (dtype == TGEMM_F32) return find_entry(dtype, v);
     auto wgs = [&](int t) { return ((M + t - 1) / t) * ((N + t - 1) / t); };
-    v.loader = TGEMM_LOADER_DIRECT;
     v.access = TGEMM_ACCESS_WIDE;
     v.frag = TGEMM_FRAG_REUSE;
     v.lds_layout = TGEMM_LDS_XOR;
     v.waves_m = 2;
-    v.waves_n = 2;
-    const int64_t short_k = dtype == TGEMM_I8 ? 2048 : 1024;
-    if (wgs(256) >= 128 && K > short_k) {
-        v.tile_m = v.tile_n = 256;
-        v.stages = 2;
-        v.waves_n = 4;  // 8 waves, two per SIMD: 5% faster than 4 at 4096^3
-    } else if (wgs(128) >= 64) {
-        v.tile_m = v.tile_n = 128;
-        v.stages = 3;
+    const bool i8 = dtype == TGEMM_I8;
+    const int64_t short_k = i8 ? 2048 : 1024;
+    // bf16: 256 x 256 direct 111-117 us, 128 x 128 S3 direct 150-165 us;
+    // register-staged 138-140 us vs 160-165 us.  int8: 68 vs 85 us.
+    const TileCandidate big = {256, 2, guarded ? TGEMM_LOADER_VGPR : TGEMM_LOADER_DIRECT, 4, 1.0, 1};
+    const TileCandidate mid = {128, guarded ? 2 : 3, guarded ? TGEMM_LOADER_VGPR : TGEMM_LOADER_DIRECT, 2,
+                               guarded ? 0.86 : (i8 ? 0.80 : 0.72), 3};
+    const TileCandidate* pick;
+    if (wgs(256) >= 128 && K > short_k)
+        pick = big.rate * fill(wgs(256), big.per_cu) >= mid.rate * fill(wgs(128), mid.per_cu) ? &big : &mid;
+    else if (wgs(128) >= 64 || guarded)
+        pick = &mid;
+    else
+        pick = nullptr;  // 64 x 64
+    if (pick) {
+        v.tile_m = v.tile_n = pick->bm;
+        v.stages = pick->stages;
+        v.loader = pick->loader;
+        v.waves_n = pick->waves_n;
     } else {
         v.tile_m = v.tile_n = 64;
         v.stages = 3;
+        v.loader = TGEMM_LOADER_DIRECT;
+        v.waves_n = 2;
     }
     return find_entry(dtype, v);
 }
@@ -236,10 +266,12 @@ tgemm_plan* gemm_plan_variant(int64_t M, int64_t N, int64_t K, int32_t dtype, in
         return nullptr;
     }
     const KernelEntry* e = nullptr;
+    bool default_plan = false;
     if (v.kernel == TGEMM_KERNEL_AUTO && v.tile_m == 0 && v.tile_n == 0 && v.tile_k == 0 && v.stages == 0 &&
         v.loader == 0 && v.lds_layout == 0 && v.access == 0 && v.frag == 0 && v.waves_m == 0 &&
         v.waves_n == 0 && v.store == 0) {
-        e = default_entry(dtype, M, N, K);
+        e = default_entry(dtype, M, N, K, false);
+        default_plan = true;
     } else {
         e = find_entry(dtype, v);
     }
@@ -249,7 +281,8 @@ tgemm_plan* gemm_plan_variant(int64_t M, int64_t N, int64_t K, int32_t dtype, in
     }
     int32_t ga = 0, gb = 0;
     ld_guards(*e, N, lda, ldb, &ga, &gb);
-    const KernelEntry* fb = guard_capable(e);
+    const KernelEntry* fb = default_plan ? default_entry(dtype, M, N, K, true) : nullptr;
+    if (!fb) fb = guard_capable(e);
     if ((ga || gb) && !e->guard_ok) {
         if (!fb) {
             set_err("variant %s cannot load unaligned operands and has no fallback", e->name);
@@ -349,6 +382,7 @@ int gemm_run(const tgemm_plan* p, const void* A, const void* B, void* C, void* s
     g.wg_group = p->wg_group;
     g.a_guard = ga;
     g.b_guard = gb;
+    g.c_stream = (uintptr_t)C % 128 == 0 && (p->ldc * 4) % 128 == 0;
     void* args[] = {&g};
     const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(e->fn),
                                            dim3((unsigned)(g.tiles_m * g.tiles_n)), dim3(e->threads), args, 0, s);
