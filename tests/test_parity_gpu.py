@@ -270,8 +270,11 @@ def test_shifted_loads_every_byte_offset(dtype):
         lda_al = (K + ce - 1) // ce * ce
         ref = _run_views(_exact_device_view(A, lda_al, 0), _exact_device_view(B, N, 0), v)
         _assert_parity(ref, A, B, dtype)
+        # both operands misaligned; then B only and A only, by stride and by pointer
         for (lda, ldb, oa, ob) in [(K, N + 1, 0, 0), (K + 2, N + 3, 1, ce - 1), (lda_al, N, ce // 2, 1),
-                                   (K + 1, N + ce + 1, ce - 1, ce // 2)]:
+                                   (K + 1, N + ce + 1, ce - 1, ce // 2),
+                                   (lda_al, N + 1, 0, 0), (lda_al, N, 0, 1), (lda_al, N + 3, 0, ce - 1),
+                                   (K, N, 0, 0), (lda_al, N, 1, 0), (K + 2, N, ce - 1, 0)]:
             print("shifted", dtype, _vname(v), lda, ldb, oa, ob, flush=True)
             C = _run_views(_exact_device_view(A, lda, oa), _exact_device_view(B, ldb, ob), v)
             assert torch.equal(C, ref), (_vname(v), lda, ldb, oa, ob)
@@ -289,10 +292,12 @@ def test_shifted_loads_few_slices(dtype):
             M, N = 300, 520
             A = inputs.operand(KIND[dtype], M, K, 71 + K)
             B = inputs.operand(KIND[dtype], K, N, 72 + K)
-            C = _run_views(_exact_device_view(A, K + 1, 1), _exact_device_view(B, N + 1, ce - 1), v)
             C_ref, S = _oracle(A, B, dtype)
-            ok, rep = check(C.numpy(), C_ref, S, dtype, K)
-            assert ok, (_vname(v), K, rep)
+            lda_al = (K + ce - 1) // ce * ce
+            for (lda, ldb, oa, ob) in [(K + 1, N + 1, 1, ce - 1), (lda_al, N + 1, 0, 0), (K + 1, N, 0, 0)]:
+                C = _run_views(_exact_device_view(A, lda, oa), _exact_device_view(B, ldb, ob), v)
+                ok, rep = check(C.numpy(), C_ref, S, dtype, K)
+                assert ok, (_vname(v), K, lda, ldb, oa, ob, rep)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "i8"])

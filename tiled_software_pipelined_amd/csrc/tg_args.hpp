@@ -16,8 +16,8 @@ struct GemmArgs {
     int32_t tiles_m, tiles_n;  // ceil(M / BM), ceil(N / BN)
     int64_t lda, ldb, ldc;
     int32_t wg_group;          // <= 0: row-major workgroup order
-    int32_t a_guard;           // 1: A rows not 16-byte aligned (register-staged shifted loads)
-    int32_t b_guard;           // 1: B rows not 16-byte aligned or N not a whole number of chunks
+    int32_t a_guard;           // 1: A rows not 16-byte aligned (kernels with shift_mask bit 0)
+    int32_t b_guard;           // 1: B rows not 16-byte aligned or N not a whole number of chunks (bit 1)
     int32_t c_stream;          // 1: C rows 128-byte aligned: non-temporal (streaming) C stores
 };
 
@@ -44,7 +44,8 @@ struct KernelEntry {
     int threads;     // threads per workgroup
     int lds_bytes;   // static LDS per workgroup
     int loads_per_stage;  // global->LDS instructions per wave per stage
-    int guard_ok;    // accepts a_guard / b_guard = 1
+    int shift_mask;  // operands it can read from rows that are not 16-byte aligned: bit 0 A, bit 1 B
+    int listed;      // 0: only reached as the fallback of a listed entry for such operands
     int tail_ok;     // handles K not a multiple of bk
     KernelFn fn;
     char name[96];

@@ -18,10 +18,12 @@ void gemm_kernel(GemmArgs g) {
 
 static const char* dtype_tag(int dt) { return dt == 0 ? "f32" : dt == 1 ? "bf16" : "i8"; }
 
+// SHIFT: which operands the kernel reads from rows that are not 16-byte
+// aligned (bit 0 A, bit 1 B).  Such kernels are unlisted fallbacks.
 template <class Tr, int BM, int BN, int BK, int WM, int WN, int S, int LD, int LY, int AC, int FR,
-          int WAVES>
+          int WAVES, int SHIFT = 0>
 KernelEntry mfma_entry(int dtype) {
-    typedef MfmaGemm<Tr, BM, BN, BK, WM, WN, S, LD, LY, AC, FR> K;
+    typedef MfmaGemm<Tr, BM, BN, BK, WM, WN, S, LD, LY, AC, FR, SHIFT> K;
     KernelEntry e{};
     e.dtype = dtype;
     e.family = FAM_TILED;
@@ -39,12 +41,14 @@ KernelEntry mfma_entry(int dtype) {
     e.threads = K::NT;
     e.lds_bytes = K::LDS_BYTES;
     e.loads_per_stage = AC == AC_WIDE ? K::N_LD : K::A_DW + K::B_DW;
-    e.guard_ok = LD == LD_VGPR;
+    e.shift_mask = SHIFT;
+    e.listed = SHIFT == 0;
     e.tail_ok = 1;
     e.fn = gemm_kernel<K, WAVES>;
-    snprintf(e.name, sizeof e.name, "%s_t%dx%dx%d_w%dx%d_s%d_%s_%s_%s_%s", dtype_tag(dtype), BM, BN,
+    snprintf(e.name, sizeof e.name, "%s_t%dx%dx%d_w%dx%d_s%d_%s_%s_%s_%s%s", dtype_tag(dtype), BM, BN,
              BK, WM, WN, S, LD == LD_DIRECT ? "direct" : "vgpr", LY == LY_XOR ? "xor" : "plain",
-             AC == AC_WIDE ? "wide" : "narrow", FR == FR_REUSE ? "reuse" : "permma");
+             AC == AC_WIDE ? "wide" : "narrow", FR == FR_REUSE ? "reuse" : "permma",
+             SHIFT == 1 ? "_shiftA" : SHIFT == 2 ? "_shiftB" : SHIFT == 3 ? "_shiftAB" : "");
     return e;
 }
 
@@ -68,7 +72,8 @@ KernelEntry naive_entry() {
     e.threads = K::NT;
     e.lds_bytes = 0;
     e.loads_per_stage = 0;
-    e.guard_ok = 1;
+    e.shift_mask = 3;  // element loads only
+    e.listed = 1;
     e.tail_ok = 1;
     e.fn = gemm_kernel<K, 4>;
     snprintf(e.name, sizeof e.name, "%s_naive", dtype_tag(DT));
@@ -98,7 +103,8 @@ KernelEntry f32_entry() {
     e.threads = K::NT;
     e.lds_bytes = K::LDS_BYTES;
     e.loads_per_stage = K::N_LD;
-    e.guard_ok = 1;
+    e.shift_mask = 3;  // its own guarded element loads
+    e.listed = 1;
     e.tail_ok = 1;
     e.fn = gemm_kernel<K, 2>;
     snprintf(e.name, sizeof e.name, "f32_t128x128x8_w2x2_s%d_%s_%s_%s", S, TA ? "transA" : "rowA",

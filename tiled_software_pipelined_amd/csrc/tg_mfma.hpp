@@ -67,7 +67,7 @@ struct TraitsI8 {
 };
 
 template <class Tr, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int LOADER,
-          int LAYOUT, int ACCESS, int FRAG>
+          int LAYOUT, int ACCESS, int FRAG, int SHIFT = 0>
 struct MfmaGemm {
     typedef typename Tr::T T;
     typedef typename Tr::Out Out;
@@ -108,6 +108,13 @@ struct MfmaGemm {
     static_assert(WIDE || (!XOR && !DIRECT), "narrow accesses use the plain layout");
     static_assert(FRAG == FR_REUSE || !WIDE, "per-instruction fragment reloads only on the narrow rung");
     static_assert(N_LD * (STAGES > 2 ? STAGES - 2 : 0) <= 63, "vmcnt range");
+    static_assert(SHIFT == 0 || (LOADER == LD_VGPR && WIDE), "shifted loads: register-staged, 16-byte chunks");
+    // Shifted chunks complete their pairs from the neighbouring lane after
+    // the multiply when the staged registers are few (the extra block and
+    // shift per chunk then fit); with more chunks per thread the pair is
+    // loaded and shifted at load time instead, which needs no extra
+    // registers across the multiply.
+    static constexpr bool DEFER_SHIFT = A_PER + B_PER <= 4;
 
     // ---- LDS layout --------------------------------------------------------
     // A: row r of a slice at r*KB; its 16-byte chunks permuted by an XOR so
@@ -147,6 +154,33 @@ struct MfmaGemm {
         return u.v;
     }
 
+    // Bytes [sh, sh + 16) of the 32-byte pair x | y (x first in memory).
+    __device__ static __forceinline__ i32x4 funnel(i32x4 x, i32x4 y, uint32_t sh) {
+        // Named scalars, not an array: selects between elements of a local
+        // array are turned into a dynamically indexed stack copy.
+        const bool s8 = sh & 8, s4 = sh & 4;
+        const uint32_t t0 = s8 ? x[2] : x[0], t1 = s8 ? x[3] : x[1], t2 = s8 ? y[0] : x[2];
+        const uint32_t t3 = s8 ? y[1] : x[3], t4 = s8 ? y[2] : y[0], t5 = s8 ? y[3] : y[1];
+        const uint32_t u0 = s4 ? t1 : t0, u1 = s4 ? t2 : t1, u2 = s4 ? t3 : t2;
+        const uint32_t u3 = s4 ? t4 : t3, u4 = s4 ? t5 : t4;
+        const uint32_t b = sh & 3;
+        i32x4 out;
+        out[0] = int32_t(__builtin_amdgcn_alignbyte(u1, u0, b));
+        out[1] = int32_t(__builtin_amdgcn_alignbyte(u2, u1, b));
+        out[2] = int32_t(__builtin_amdgcn_alignbyte(u3, u2, b));
+        out[3] = int32_t(__builtin_amdgcn_alignbyte(u4, u3, b));
+        return out;
+    }
+
+    // The value of `v` in lane + 1 of the same 16-lane row (DPP row_shl:1);
+    // lanes 15, 31, 47, 63 keep `own`.
+    __device__ static __forceinline__ i32x4 from_right_lane(i32x4 v, i32x4 own) {
+        i32x4 out;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) out[d] = __builtin_amdgcn_update_dpp(own[d], v[d], 0x101, 0xf, 0xf, false);
+        return out;
+    }
+
     // 16 bytes starting at p, for an operand whose valid bytes are [beg, end)
     // and whose rows are not 16-byte aligned: the two aligned 16-byte blocks
     // that cover them are loaded and the wanted bytes funnel-shifted out of
@@ -161,21 +195,7 @@ struct MfmaGemm {
         if (!CHECK || (lo >= beg && lo + 32 <= end)) {
             const i32x4 x = *reinterpret_cast<const i32x4*>(lo);
             const i32x4 y = *reinterpret_cast<const i32x4*>(lo + 16);
-            const uint32_t sh = uint32_t(a & 15);
-            // Named scalars, not an array: selects between elements of a
-            // local array are turned into a dynamically indexed stack copy.
-            const bool s8 = sh & 8, s4 = sh & 4;
-            const uint32_t t0 = s8 ? x[2] : x[0], t1 = s8 ? x[3] : x[1], t2 = s8 ? y[0] : x[2];
-            const uint32_t t3 = s8 ? y[1] : x[3], t4 = s8 ? y[2] : y[0], t5 = s8 ? y[3] : y[1];
-            const uint32_t u0 = s4 ? t1 : t0, u1 = s4 ? t2 : t1, u2 = s4 ? t3 : t2;
-            const uint32_t u3 = s4 ? t4 : t3, u4 = s4 ? t5 : t4;
-            const uint32_t b = sh & 3;
-            i32x4 out;
-            out[0] = int32_t(__builtin_amdgcn_alignbyte(u1, u0, b));
-            out[1] = int32_t(__builtin_amdgcn_alignbyte(u2, u1, b));
-            out[2] = int32_t(__builtin_amdgcn_alignbyte(u3, u2, b));
-            out[3] = int32_t(__builtin_amdgcn_alignbyte(u4, u3, b));
-            return out;
+            return funnel(x, y, uint32_t(a & 15));
         }
         union { i32x4 v; T e[CE]; } u;
 #pragma unroll
@@ -183,25 +203,46 @@ struct MfmaGemm {
         return u.v;
     }
 
+    // Registers of one register-staged slice.  For LM_SHIFTED operands with
+    // DEFER_SHIFT, `a` / `b` hold the low aligned block of each chunk's pair
+    // and `*sh` its byte offset; the high block is the next chunk's low block, which lane + 1
+    // holds, except in the lanes at the end of an operand row or of a
+    // 16-lane DPP row: those load it into `ah` / `bh` themselves.  The funnel
+    // shift happens in store_regs, after the multiply, so that the loads'
+    // latency stays hidden behind it as in the aligned case.
+    template <int MODE_A, int MODE_B>
     struct Staged {
+        static constexpr bool SA = DEFER_SHIFT && MODE_A == LM_SHIFTED;
+        static constexpr bool SB = DEFER_SHIFT && MODE_B == LM_SHIFTED;
         i32x4 a[WIDE ? A_PER : 1];
         i32x4 b[WIDE ? B_PER : 1];
+        i32x4 ah[SA ? A_PER : 1];
+        i32x4 bh[SB ? B_PER : 1];
+        uint32_t ash[SA ? A_PER : 1];
+        uint32_t bsh[SB ? B_PER : 1];
         int32_t ad[WIDE ? 1 : A_DW];
         int32_t bd[WIDE ? 1 : B_DW];
     };
 
+    // does this lane load the high block of its shifted pair itself?
+    __device__ static __forceinline__ bool own_high(int c, int chunks_per_row) {
+        return c == chunks_per_row - 1 || (threadIdx.x & 15) == 15;
+    }
+
     // Register-staged load of slice k0.  Per operand, a load mode:
     //   LM_ALIGNED : 16-byte loads (rows 16-byte aligned, N a multiple of CE);
-    //   LM_SHIFTED : rows not 16-byte aligned, slice inside K: funnel-shifted
-    //                pairs of aligned loads (values at n >= N are whatever
-    //                follows in memory; they only reach C columns that are
-    //                never stored);
+    //   LM_SHIFTED : rows not 16-byte aligned, slice inside K: one aligned
+    //                16-byte load per chunk, the pair completed from the
+    //                neighbouring lane and funnel-shifted in store_regs (values
+    //                at n >= N are whatever follows in memory; they only reach
+    //                C columns that are never stored);
     //   LM_SHIFTED_EDGE : the same with a bounds check per pair, for the
     //                first and last whole slices;
     //   LM_ELEMENT : element loads with zero fill at k >= K (and n >= N for
     //                B): the partial last K slice.
     template <int MODE_A, int MODE_B>
-    __device__ static __forceinline__ void load_regs(Staged& r, const GemmArgs& g, int m0, int n0, int k0) {
+    __device__ static __forceinline__ void load_regs(Staged<MODE_A, MODE_B>& r, const GemmArgs& g, int m0, int n0,
+                                                     int k0) {
         const T* A = static_cast<const T*>(g.A);
         const T* B = static_cast<const T*>(g.B);
         const int tid = threadIdx.x;
@@ -216,10 +257,22 @@ struct MfmaGemm {
                 const int row = p / CA, c = p % CA;
                 const T* rowp = A + (int64_t)min(m0 + row, g.M - 1) * g.lda;
                 const int kc = k0 + c * CE;
-                if constexpr (MODE_A == LM_ALIGNED) r.a[q] = *reinterpret_cast<const i32x4*>(rowp + kc);
-                else if constexpr (MODE_A != LM_ELEMENT)
-                    r.a[q] = load_chunk_shifted<MODE_A == LM_SHIFTED_EDGE>(rowp + kc, a_beg, a_end);
-                else r.a[q] = load_chunk_guarded(rowp, kc, g.K);
+                if constexpr (MODE_A == LM_ALIGNED) {
+                    r.a[q] = *reinterpret_cast<const i32x4*>(rowp + kc);
+                } else if constexpr (MODE_A == LM_SHIFTED && !DEFER_SHIFT) {
+                    r.a[q] = load_chunk_shifted<false>(rowp + kc, a_beg, a_end);
+                } else if constexpr (MODE_A == LM_SHIFTED) {
+                    const uintptr_t ad = reinterpret_cast<uintptr_t>(rowp + kc);
+                    const uintptr_t lo = ad & ~uintptr_t(15);
+                    r.a[q] = *reinterpret_cast<const i32x4*>(lo);
+                    r.ash[q] = uint32_t(ad & 15);
+                    r.ah[q] = i32x4{0, 0, 0, 0};
+                    if (own_high(c, CA)) r.ah[q] = *reinterpret_cast<const i32x4*>(lo + 16);
+                } else if constexpr (MODE_A == LM_SHIFTED_EDGE) {
+                    r.a[q] = load_chunk_shifted<true>(rowp + kc, a_beg, a_end);
+                } else {
+                    r.a[q] = load_chunk_guarded(rowp, kc, g.K);
+                }
             }
 #pragma unroll
             for (int q = 0; q < B_PER; ++q) {
@@ -230,8 +283,17 @@ struct MfmaGemm {
                 const T* rowp = B + (int64_t)gk * g.ldb;
                 if constexpr (MODE_B == LM_ALIGNED) {
                     r.b[q] = *reinterpret_cast<const i32x4*>(rowp + min(nc, g.N - CE));
-                } else if constexpr (MODE_B != LM_ELEMENT) {
-                    r.b[q] = load_chunk_shifted<MODE_B == LM_SHIFTED_EDGE>(rowp + min(nc, g.N - 1), b_beg, b_end);
+                } else if constexpr (MODE_B == LM_SHIFTED && !DEFER_SHIFT) {
+                    r.b[q] = load_chunk_shifted<false>(rowp + min(nc, g.N - 1), b_beg, b_end);
+                } else if constexpr (MODE_B == LM_SHIFTED) {
+                    const uintptr_t ad = reinterpret_cast<uintptr_t>(rowp + min(nc, g.N - 1));
+                    const uintptr_t lo = ad & ~uintptr_t(15);
+                    r.b[q] = *reinterpret_cast<const i32x4*>(lo);
+                    r.bsh[q] = uint32_t(ad & 15);
+                    r.bh[q] = i32x4{0, 0, 0, 0};
+                    if (own_high(c, CB)) r.bh[q] = *reinterpret_cast<const i32x4*>(lo + 16);
+                } else if constexpr (MODE_B == LM_SHIFTED_EDGE) {
+                    r.b[q] = load_chunk_shifted<true>(rowp + min(nc, g.N - 1), b_beg, b_end);
                 } else {
                     r.b[q] = gk < g.K ? load_chunk_guarded(rowp, nc, g.N) : i32x4{0, 0, 0, 0};
                 }
@@ -272,20 +334,36 @@ struct MfmaGemm {
         }
     }
 
-    __device__ static __forceinline__ void store_regs(TG_LDS char* slot, const Staged& r) {
+    // Shifted chunks: the high block comes from lane + 1 (the next chunk of
+    // the same row: its low block starts 16 bytes later) unless this lane
+    // loaded it.  Where lane + 1's column was clamped to N - 1, its block is
+    // either the right one or this lane's own, and then every byte past this
+    // lane's low block lies at a column >= N.
+    template <int MODE_A, int MODE_B>
+    __device__ static __forceinline__ void store_regs(TG_LDS char* slot, const Staged<MODE_A, MODE_B>& r) {
         const int tid = threadIdx.x;
         if constexpr (WIDE) {
 #pragma unroll
             for (int q = 0; q < A_PER; ++q) {
                 const int p = q * NT + tid;
                 const int row = p / CA, c = p % CA;
-                *reinterpret_cast<TG_LDS i32x4*>(slot + row * KB + a_chunk(row, c) * 16) = r.a[q];
+                i32x4 v = r.a[q];
+                if constexpr (Staged<MODE_A, MODE_B>::SA) {
+                    const i32x4 nb = from_right_lane(r.a[q], r.ah[q]);
+                    v = funnel(r.a[q], own_high(c, CA) ? r.ah[q] : nb, r.ash[q]);
+                }
+                *reinterpret_cast<TG_LDS i32x4*>(slot + row * KB + a_chunk(row, c) * 16) = v;
             }
 #pragma unroll
             for (int q = 0; q < B_PER; ++q) {
                 const int p = q * NT + tid;
                 const int k = p / CB, c = p % CB;
-                *reinterpret_cast<TG_LDS i32x4*>(slot + A_BYTES + k * NB + b_chunk(k, c) * 16) = r.b[q];
+                i32x4 v = r.b[q];
+                if constexpr (Staged<MODE_A, MODE_B>::SB) {
+                    const i32x4 nb = from_right_lane(r.b[q], r.bh[q]);
+                    v = funnel(r.b[q], own_high(c, CB) ? r.bh[q] : nb, r.bsh[q]);
+                }
+                *reinterpret_cast<TG_LDS i32x4*>(slot + A_BYTES + k * NB + b_chunk(k, c) * 16) = v;
             }
         } else {
 #pragma unroll
@@ -596,17 +674,22 @@ struct MfmaGemm {
         constexpr int EA = edge_mode(MODE_A), EB = edge_mode(MODE_B);
         if constexpr (STAGES == 1) {
             for (int t = 0; t < full; ++t) {
-                Staged r;
-                if (t == 0 || t == full - 1) load_regs<EA, EB>(r, g, m0, n0, t * BK);
-                else load_regs<MODE_A, MODE_B>(r, g, m0, n0, t * BK);
-                store_regs(smem, r);
+                if (t == 0 || t == full - 1) {
+                    Staged<EA, EB> r;
+                    load_regs(r, g, m0, n0, t * BK);
+                    store_regs(smem, r);
+                } else {
+                    Staged<MODE_A, MODE_B> r;
+                    load_regs(r, g, m0, n0, t * BK);
+                    store_regs(smem, r);
+                }
                 wait_lds_then_barrier();
                 compute(smem, acc, wm0, wn0, lane);
                 wait_lds_then_barrier();  // all reads done before the next overwrite
             }
             if (full < tiles) {
-                Staged r;
-                load_regs<LM_ELEMENT, LM_ELEMENT>(r, g, m0, n0, full * BK);
+                Staged<LM_ELEMENT, LM_ELEMENT> r;
+                load_regs(r, g, m0, n0, full * BK);
                 store_regs(smem, r);
                 wait_lds_then_barrier();
                 compute(smem, acc, wm0, wn0, lane);
@@ -614,8 +697,8 @@ struct MfmaGemm {
         } else {
             if (full == 0) {
                 if (tiles > 0) {
-                    Staged r;
-                    load_regs<LM_ELEMENT, LM_ELEMENT>(r, g, m0, n0, 0);
+                    Staged<LM_ELEMENT, LM_ELEMENT> r;
+                    load_regs(r, g, m0, n0, 0);
                     store_regs(smem, r);
                     wait_lds_then_barrier();
                     compute(smem, acc, wm0, wn0, lane);
@@ -623,30 +706,30 @@ struct MfmaGemm {
                 return;
             }
             {
-                Staged r;
-                load_regs<EA, EB>(r, g, m0, n0, 0);
+                Staged<EA, EB> r;
+                load_regs(r, g, m0, n0, 0);
                 store_regs(smem, r);
                 wait_lds_then_barrier();
             }
             int t = 0;
             for (; t + 2 < full; ++t) {  // loads slices 1 .. full-2
-                Staged r;
-                load_regs<MODE_A, MODE_B>(r, g, m0, n0, (t + 1) * BK);
+                Staged<MODE_A, MODE_B> r;
+                load_regs(r, g, m0, n0, (t + 1) * BK);
                 compute(smem + (t & 1) * SLOT, acc, wm0, wn0, lane);
                 store_regs(smem + ((t + 1) & 1) * SLOT, r);
                 wait_lds_then_barrier();
             }
             if (t + 1 < full) {  // loads the last whole slice
-                Staged r;
-                load_regs<EA, EB>(r, g, m0, n0, (t + 1) * BK);
+                Staged<EA, EB> r;
+                load_regs(r, g, m0, n0, (t + 1) * BK);
                 compute(smem + (t & 1) * SLOT, acc, wm0, wn0, lane);
                 store_regs(smem + ((t + 1) & 1) * SLOT, r);
                 wait_lds_then_barrier();
                 ++t;
             }
             if (full < tiles) {  // loads the partial slice
-                Staged r;
-                load_regs<LM_ELEMENT, LM_ELEMENT>(r, g, m0, n0, full * BK);
+                Staged<LM_ELEMENT, LM_ELEMENT> r;
+                load_regs(r, g, m0, n0, full * BK);
                 compute(smem + (t & 1) * SLOT, acc, wm0, wn0, lane);
                 store_regs(smem + ((t + 1) & 1) * SLOT, r);
                 wait_lds_then_barrier();
@@ -756,21 +839,16 @@ struct MfmaGemm {
                 // K tail: element loads with zero fill into slot full % STAGES.
                 // No copy is in flight (the last wait drained them) and every
                 // wave passed the barrier that ended its reads of that slot.
-                Staged r;
-                load_regs<LM_ELEMENT, LM_ELEMENT>(r, g, m0, n0, full * BK);
+                Staged<LM_ELEMENT, LM_ELEMENT> r;
+                load_regs(r, g, m0, n0, full * BK);
                 store_regs(smem + (full % STAGES) * SLOT, r);
                 wait_lds_then_barrier();
                 compute(smem + (full % STAGES) * SLOT, acc, wm0, wn0, lane);
             }
         } else {
-            // register-staged loaders: one instantiation per pair of load modes
-            if (g.a_guard) {
-                if (g.b_guard) staged_loop<LM_SHIFTED, LM_SHIFTED>(acc, smem, g, m0, n0, wm0, wn0, lane, full, tiles);
-                else staged_loop<LM_SHIFTED, LM_ALIGNED>(acc, smem, g, m0, n0, wm0, wn0, lane, full, tiles);
-            } else {
-                if (g.b_guard) staged_loop<LM_ALIGNED, LM_SHIFTED>(acc, smem, g, m0, n0, wm0, wn0, lane, full, tiles);
-                else staged_loop<LM_ALIGNED, LM_ALIGNED>(acc, smem, g, m0, n0, wm0, wn0, lane, full, tiles);
-            }
+            // register-staged loaders: the kernel's own pair of load modes
+            staged_loop<(SHIFT & 1) ? LM_SHIFTED : LM_ALIGNED, (SHIFT & 2) ? LM_SHIFTED : LM_ALIGNED>(
+                acc, smem, g, m0, n0, wm0, wn0, lane, full, tiles);
         }
 
         // Epilogue: accumulators -> C.  Register r of tile (i, j) in lane l is

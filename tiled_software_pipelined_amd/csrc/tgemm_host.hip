@@ -19,8 +19,8 @@ using tg::KernelEntry;
 struct tgemm_plan {
     int64_t M, N, K, lda, ldb, ldc;
     int32_t dtype;
-    const KernelEntry* entry;     // what runs when the operands allow it
-    const KernelEntry* fallback;  // register-staged entry used when an operand needs the guarded loader
+    const KernelEntry* entry;        // what runs when the operands allow it
+    const KernelEntry* fallback[4];  // by misaligned operands (bit 0 A, bit 1 B); [0] = entry
     int32_t wg_group;
     int32_t a_guard, b_guard;     // leading-dimension based (pointer alignment is checked per run)
 };
@@ -83,8 +83,13 @@ bool matches(const KernelEntry& e, const tgemm_variant& v) {
 
 const KernelEntry* find_entry(int dtype, const tgemm_variant& v) {
     for (const KernelEntry& e : g_reg[dtype])
-        if (matches(e, v)) return &e;
+        if (e.listed && matches(e, v)) return &e;
     return nullptr;
+}
+
+// Can entry e read operands whose rows are not 16-byte aligned (ga: A, gb: B)?
+bool accepts(const KernelEntry& e, bool ga, bool gb) {
+    return (!ga || (e.shift_mask & 1)) && (!gb || (e.shift_mask & 2));
 }
 
 // Default choice for a shape.  Small problems (fewer than half a workgroup
@@ -149,21 +154,23 @@ const KernelEntry* default_entry(int dtype, int64_t M, int64_t N, int64_t K, boo
     return find_entry(dtype, v);
 }
 
-// A register-staged entry for operands that need guarded loads: the same
-// tile and wave grid, else the same tile, else the double-buffered wide one
-// whose tile is nearest in size (small tiles keep small problems spread over
-// the GPU).
-const KernelEntry* guard_capable(const KernelEntry* e) {
-    if (e->guard_ok) return e;
+// The kernel that runs in place of e for operands whose rows are not
+// 16-byte aligned (ga: A, gb: B): e itself if it can read them, else a
+// register-staged kernel with shifted loads for just those operands
+// (registry order puts A-only before B-only before both) with the same tile
+// and wave grid, else the same tile, else the nearest tile in size.
+const KernelEntry* guard_capable(const KernelEntry* e, bool ga, bool gb) {
+    if (accepts(*e, ga, gb)) return e;
     for (int same_waves = 1; same_waves >= 0; --same_waves)
         for (const KernelEntry& c : g_reg[e->dtype])
-            if (c.guard_ok && c.family == e->family && c.bm == e->bm && c.bn == e->bn && c.bk == e->bk &&
-                c.access == tg::AC_WIDE && c.stages == 2 && (!same_waves || (c.wm == e->wm && c.wn == e->wn)))
+            if (accepts(c, ga, gb) && c.family == e->family && c.bm == e->bm && c.bn == e->bn &&
+                c.bk == e->bk && c.access == tg::AC_WIDE && c.stages == 2 &&
+                (!same_waves || (c.wm == e->wm && c.wn == e->wn)))
                 return &c;
     const KernelEntry* best = nullptr;
     int best_d = INT_MAX;
     for (const KernelEntry& c : g_reg[e->dtype])
-        if (c.guard_ok && c.family == tg::FAM_TILED && c.access == tg::AC_WIDE && c.stages == 2) {
+        if (accepts(c, ga, gb) && c.family == tg::FAM_TILED && c.access == tg::AC_WIDE && c.stages == 2) {
             const int d = abs(c.bm - e->bm) + abs(c.bn - e->bn);
             if (d < best_d) {
                 best = &c;
@@ -279,16 +286,23 @@ tgemm_plan* gemm_plan_variant(int64_t M, int64_t N, int64_t K, int32_t dtype, in
         set_err("no compiled variant matches the request (see gemm_variant_get)");
         return nullptr;
     }
-    int32_t ga = 0, gb = 0;
-    ld_guards(*e, N, lda, ldb, &ga, &gb);
-    const KernelEntry* fb = default_plan ? default_entry(dtype, M, N, K, true) : nullptr;
-    if (!fb) fb = guard_capable(e);
-    if ((ga || gb) && !e->guard_ok) {
-        if (!fb) {
-            set_err("variant %s cannot load unaligned operands and has no fallback", e->name);
+    // Kernels for every combination of misaligned operands (pointers are
+    // only known per run); the leading dimensions fix which one this plan
+    // starts from.  A default plan falls back to the default register-staged
+    // choice for the shape, an explicit variant to its nearest relative.
+    const KernelEntry* fb[4] = {e, nullptr, nullptr, nullptr};
+    const KernelEntry* base = default_plan ? default_entry(dtype, M, N, K, true) : e;
+    for (int m = 1; m < 4; ++m) {
+        fb[m] = guard_capable(accepts(*e, m & 1, m & 2) ? e : base, m & 1, m & 2);
+        if (!fb[m]) {
+            set_err("variant %s has no fallback for unaligned operands", e->name);
             return nullptr;
         }
-        e = fb;
+    }
+    int32_t ga = 0, gb = 0;
+    ld_guards(*e, N, lda, ldb, &ga, &gb);
+    if (ga || gb) {
+        e = fb[ga | (gb << 1)];
         ld_guards(*e, N, lda, ldb, &ga, &gb);
     }
     const int64_t tiles_m = (M + e->bm - 1) / e->bm, tiles_n = (N + e->bn - 1) / e->bn;
@@ -305,7 +319,7 @@ tgemm_plan* gemm_plan_variant(int64_t M, int64_t N, int64_t K, int32_t dtype, in
     p->ldc = ldc;
     p->dtype = dtype;
     p->entry = e;
-    p->fallback = fb ? fb : e;
+    for (int m = 0; m < 4; ++m) p->fallback[m] = m == 0 ? e : fb[m];
     // default: XCD-aware order grouped by 4 tile rows (measured ~4% faster
     // than row-major for 256 x 256 tiles at 4096^3, with less L2-miss traffic)
     p->wg_group = v.wg_group == 0 ? (e->family == tg::FAM_NAIVE ? -1 : 4) : v.wg_group;
@@ -359,13 +373,17 @@ int gemm_run(const tgemm_plan* p, const void* A, const void* B, void* C, void* s
         if ((uintptr_t)A % bytes) ga = 1;
         if ((uintptr_t)B % bytes) gb = 1;
     }
-    if ((ga || gb) && !e->guard_ok) {
-        e = p->fallback;
+    if (!accepts(*e, ga, gb)) {
+        e = p->fallback[ga | (gb << 1)];
         int32_t fa = 0, fbg = 0;
         ld_guards(*e, p->N, p->lda, p->ldb, &fa, &fbg);
         const int fbytes = access_bytes(*e);
         ga = fa || (fbytes && (uintptr_t)A % fbytes);
         gb = fbg || (fbytes && (uintptr_t)B % fbytes);
+        if (!accepts(*e, ga, gb)) {
+            set_err("no kernel of this plan reads operands at these addresses");
+            return TGEMM_E_ALIGN;
+        }
     }
     tg::GemmArgs g;
     g.A = A;
@@ -421,17 +439,23 @@ int gemm_plan_get_info(const tgemm_plan* p, tgemm_plan_info* info) {
 int gemm_variant_count(int32_t dtype) {
     init_registry();
     if (dtype < 0 || dtype > 2) return 0;
-    return (int)g_reg[dtype].size();
+    int n = 0;
+    for (const KernelEntry& e : g_reg[dtype]) n += e.listed;
+    return n;
 }
 
 int gemm_variant_get(int32_t dtype, int32_t index, tgemm_variant* out) {
     init_registry();
-    if (dtype < 0 || dtype > 2 || !out || index < 0 || index >= (int32_t)g_reg[dtype].size()) {
-        set_err("bad dtype or index");
-        return TGEMM_E_ARG;
+    if (dtype >= 0 && dtype <= 2 && out && index >= 0) {
+        int n = 0;
+        for (const KernelEntry& e : g_reg[dtype])
+            if (e.listed && n++ == index) {
+                entry_to_variant(e, 0, out);
+                return TGEMM_OK;
+            }
     }
-    entry_to_variant(g_reg[dtype][index], 0, out);
-    return TGEMM_OK;
+    set_err("bad dtype or index");
+    return TGEMM_E_ARG;
 }
 
 }  // extern "C"
