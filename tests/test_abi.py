@@ -120,13 +120,17 @@ def test_unaligned_leading_dimension_uses_guarded_register_loader():
     assert (v.loader, v.tile_m, v.tile_n, v.tile_k, v.waves_m, v.waves_n) == (tl.LOADER_VGPR, 256, 256, 64, 2, 4)
 
 
-def test_default_tile_weighs_rate_against_grid_fill():
-    # aligned: 4096 x 4352 is 272 tiles of 256 x 256 (53 % full over two
-    # rounds) against 1088 tiles of 128 x 128 (71 % of three per unit over two
-    # rounds) at 0.72 of the rate: the big tile still wins
-    assert tl.Plan(4096, 4352, 4096, tl.BF16).info().variant.tile_m == 256
-    assert tl.Plan(4096, 4096, 4096, tl.BF16).info().variant.tile_m == 256
-    # guarded 4096 x 4097 (N not a whole number of 16-byte chunks)
+def test_default_tile_follows_the_round_model():
+    # measured (interleaved, bf16, K = 4096): 256 x 256 faster at 4096^2,
+    # 5120^2 and 3072^2; 128 x 128 faster at 4096 x 4352 and 4096 x 4608
+    # (272 / 288 big tiles: a second, nearly empty round)
+    for (M, N, want) in [(4096, 4096, 256), (5120, 5120, 256), (3072, 3072, 256), (4096, 4352, 128),
+                         (4096, 4608, 128)]:
+        assert tl.Plan(M, N, 4096, tl.BF16).info().variant.tile_m == want, (M, N)
+    # unaligned B: 4096^2 keeps the 256 x 256 register-staged kernel, the
+    # 272-tile 4096 x 4097 takes the 128 x 128 one
+    big = tl.Plan(4096, 4096, 4096, tl.BF16, ldb=4097).info()
+    assert big.b_guarded == 1 and big.variant.tile_m == 256 and big.variant.loader == tl.LOADER_VGPR
     info = tl.Plan(4096, 4097, 4096, tl.BF16).info()
     assert info.b_guarded == 1 and info.variant.tile_m == 128
 

@@ -95,26 +95,24 @@ bool accepts(const KernelEntry& e, bool ga, bool gb) {
 // Default choice for a shape.  Small problems (fewer than half a workgroup
 // per compute unit on 256 x 256 tiles, or short K) take 128 x 128 and then
 // 64 x 64 tiles.  Otherwise the 8-wave 256 x 256 tile and the 128 x 128 tile
-// compete on rate x fill: `rate` is each tile's throughput relative to the
-// 256 x 256 tile on a full GPU (median of interleaved runs at 4096^3),
-// `fill` the fraction of workgroup slots (256 compute units x workgroups
-// resident per unit) busy over the ceil(tiles / slots) rounds the grid
-// takes.  4095 x 4097 makes 272 tiles of 256 x 256: two rounds for one
-// workgroup per unit, 53 % full.  With `guarded` (an operand whose rows are
-// not 16-byte aligned) the candidates are the register-staged tiles.
-// Short K (a few slices per tile) also takes 128 x 128: with one round of
-// 256 x 256 tiles every workgroup writes its C tile at the same moment,
-// unoverlapped, and at short K that write is most of the work.
-struct TileCandidate {
-    int bm, stages, loader, waves_n;
-    double rate;  // relative to the 256 x 256 direct (or register-staged) tile
-    int per_cu;   // workgroups resident per compute unit (LDS / registers)
-};
-
-double fill(int64_t tiles, int per_cu) {
-    const int64_t slots = 256 * (int64_t)per_cu;
-    const int64_t rounds = (tiles + slots - 1) / slots;
-    return (double)tiles / (double)(rounds * slots);
+// compete on a time model fitted to interleaved runs of both at seven
+// shapes (within about 5 %), in units of one full round of 256 x 256 tiles:
+//  - 256 x 256 (one workgroup per compute unit): whole rounds of 256
+//    workgroups, plus a partial last round of f x 256 workgroups that
+//    takes 0.62 + 0.38 f of a full one (the idle units leave clock and
+//    memory bandwidth to the busy ones: measured 0.65 at f = 1/16, 0.82 at
+//    f = 9/16);
+//  - 128 x 128 (three per unit): ceil(tiles / 256) tiles on the busiest
+//    unit, each `mid_tile` of a 256 x 256 round.
+// So 4096 x 4096 keeps 256 x 256 (1 vs 4 x 0.33) and 4096 x 4352 (272 big
+// tiles, 1088 small ones) takes 128 x 128 (1.64 vs 5 x 0.33).  With
+// `guarded` (an operand whose rows are not 16-byte aligned) the candidates
+// are the register-staged tiles.  Short K also takes 128 x 128: with one
+// round of 256 x 256 tiles every workgroup writes its C tile at the same
+// moment, unoverlapped, and at short K that write is most of the work.
+double big_rounds(int64_t tiles) {
+    const int64_t full = tiles / 256, rest = tiles % 256;
+    return (double)full + (rest ? 0.62 + 0.38 * (double)rest / 256.0 : 0.0);
 }
 
 const KernelEntry* default_entry(int dtype, int64_t M, int64_t N, int64_t K, bool guarded) {
@@ -128,29 +126,21 @@ const KernelEntry* default_entry(int dtype, int64_t M, int64_t N, int64_t K, boo
     v.waves_m = 2;
     const bool i8 = dtype == TGEMM_I8;
     const int64_t short_k = i8 ? 2048 : 1024;
-    // bf16: 256 x 256 direct 111-117 us, 128 x 128 S3 direct 150-165 us;
-    // register-staged 138-140 us vs 160-165 us.  int8: 68 vs 85 us.
-    const TileCandidate big = {256, 2, guarded ? TGEMM_LOADER_VGPR : TGEMM_LOADER_DIRECT, 4, 1.0, 1};
-    const TileCandidate mid = {128, guarded ? 2 : 3, guarded ? TGEMM_LOADER_VGPR : TGEMM_LOADER_DIRECT, 2,
-                               guarded ? 0.86 : (i8 ? 0.80 : 0.72), 3};
-    const TileCandidate* pick;
+    // one 128 x 128 tile per unit, relative to a round of 256 x 256 tiles, at
+    // 4096^3: bf16 direct 146 / 4 us vs 113 us; int8 85 / 4 vs 68 us;
+    // register-staged, B rows unaligned: 221 / 4 vs 212 us
+    const double mid_tile = guarded ? 0.26 : (i8 ? 0.31 : 0.325);
+    int pick;  // tile edge
     if (wgs(256) >= 128 && K > short_k)
-        pick = big.rate * fill(wgs(256), big.per_cu) >= mid.rate * fill(wgs(128), mid.per_cu) ? &big : &mid;
+        pick = big_rounds(wgs(256)) <= mid_tile * (double)((wgs(128) + 255) / 256) ? 256 : 128;
     else if (wgs(128) >= 64 || guarded)
-        pick = &mid;
+        pick = 128;
     else
-        pick = nullptr;  // 64 x 64
-    if (pick) {
-        v.tile_m = v.tile_n = pick->bm;
-        v.stages = pick->stages;
-        v.loader = pick->loader;
-        v.waves_n = pick->waves_n;
-    } else {
-        v.tile_m = v.tile_n = 64;
-        v.stages = 3;
-        v.loader = TGEMM_LOADER_DIRECT;
-        v.waves_n = 2;
-    }
+        pick = 64;
+    v.tile_m = v.tile_n = pick;
+    v.waves_n = pick == 256 ? 4 : 2;
+    v.stages = pick == 256 || guarded ? 2 : 3;
+    v.loader = guarded ? TGEMM_LOADER_VGPR : TGEMM_LOADER_DIRECT;
     return find_entry(dtype, v);
 }
 
