@@ -25,6 +25,8 @@ void register_bf16(void (*add)(const KernelEntry&)) {
     add(mfma_entry<T, 128, 128, 32, 2, 2, 4, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2>(1));
     add(mfma_entry<T, 128, 128, 32, 2, 2, 2, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2>(1));
     add(mfma_entry<T, 128, 128, 32, 2, 2, 2, LD_VGPR, LY_XOR, AC_WIDE, FR_REUSE, 2>(1));
+    // the asynchronous copy with a single buffer: no overlap to gain
+    add(mfma_entry<T, 128, 128, 32, 2, 2, 1, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2>(1));
     add(mfma_entry<T, 128, 128, 32, 2, 2, 1, LD_VGPR, LY_XOR, AC_WIDE, FR_REUSE, 2>(1));
     add(mfma_entry<T, 128, 128, 32, 2, 2, 1, LD_VGPR, LY_PLAIN, AC_WIDE, FR_REUSE, 2>(1));
     add(mfma_entry<T, 128, 128, 32, 2, 2, 1, LD_VGPR, LY_PLAIN, AC_NARROW, FR_REUSE, 2>(1));

@@ -103,7 +103,7 @@ struct MfmaGemm {
     static_assert(BK % Tr::MK == 0, "slice must hold whole matrix-core steps");
     static_assert((BM * CA) % NT == 0 && (BK * CB) % NT == 0, "even 16-byte split");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS per CU");
-    static_assert(!DIRECT || (STAGES >= 2 && WIDE), "direct loads need a ring and 16-byte chunks");
+    static_assert(!DIRECT || WIDE, "direct loads move 16-byte chunks");
     static_assert(DIRECT || STAGES <= 2, "register-staged loader: 1 or 2 slots");
     static_assert(WIDE || (!XOR && !DIRECT), "narrow accesses use the plain layout");
     static_assert(FRAG == FR_REUSE || !WIDE, "per-instruction fragment reloads only on the narrow rung");
@@ -802,6 +802,24 @@ struct MfmaGemm {
             auto issue_slice = [&](int sl) {
                 issue_direct(smem + (sl % STAGES) * SLOT, off, abase + sl * astep, bbase + sl * bstep, wave);
             };
+            if constexpr (STAGES == 1) {
+                // One slot: the copy of slice t+1 may only start once every
+                // wave has finished reading slice t, so nothing overlaps -
+                // the asynchronous copy without a second buffer.
+                for (int t = 0; t < full; ++t) {
+                    issue_slice(t);
+                    wait_all_then_barrier();
+                    compute(smem, acc, wm0, wn0, lane);
+                    wait_lds_then_barrier();
+                }
+                if (full < tiles) {
+                    Staged<LM_ELEMENT, LM_ELEMENT> r;
+                    load_regs(r, g, m0, n0, full * BK);
+                    store_regs(smem, r);
+                    wait_lds_then_barrier();
+                    compute(smem, acc, wm0, wn0, lane);
+                }
+            } else {
             // Prologue: slices 0 .. STAGES-2 in flight; once slice 0 is in
             // LDS (barrier), start slice STAGES-1 and read the fragments of
             // slice 0's first K step.
@@ -844,6 +862,7 @@ struct MfmaGemm {
                 store_regs(smem + (full % STAGES) * SLOT, r);
                 wait_lds_then_barrier();
                 compute(smem + (full % STAGES) * SLOT, acc, wm0, wn0, lane);
+            }
             }
         } else {
             // register-staged loaders: the kernel's own pair of load modes

@@ -95,8 +95,9 @@ bool accepts(const KernelEntry& e, bool ga, bool gb) {
 // Default choice for a shape.  Small problems (fewer than half a workgroup
 // per compute unit on 256 x 256 tiles, or short K) take 128 x 128 and then
 // 64 x 64 tiles.  Otherwise the 8-wave 256 x 256 tile and the 128 x 128 tile
-// compete on a time model fitted to interleaved runs of both at seven
-// shapes (within about 5 %), in units of one full round of 256 x 256 tiles:
+// compete on a time model fitted to interleaved runs of both at six
+// aligned shapes and two with unaligned B rows (within about 5 %), in units
+// of one full round of 256 x 256 tiles:
 //  - 256 x 256 (one workgroup per compute unit): whole rounds of 256
 //    workgroups, plus a partial last round of f x 256 workgroups that
 //    takes 0.62 + 0.38 f of a full one (the idle units leave clock and
@@ -139,7 +140,10 @@ const KernelEntry* default_entry(int dtype, int64_t M, int64_t N, int64_t K, boo
         pick = 64;
     v.tile_m = v.tile_n = pick;
     v.waves_n = pick == 256 ? 4 : 2;
-    v.stages = pick == 256 || guarded ? 2 : 3;
+    // 128 x 128 direct: a 4-slot ring from K = 4096 (4-13 % faster than 3
+    // slots at 2048^2 x 4096, 4096 x 4352 x 4096, 1024^2 x 8192 and 2048^2 x
+    // 8192); 3 below (equal to 4 at K <= 1024, where the prologue dominates)
+    v.stages = pick == 256 || guarded ? 2 : (K >= 4096 ? 4 : 3);
     v.loader = guarded ? TGEMM_LOADER_VGPR : TGEMM_LOADER_DIRECT;
     return find_entry(dtype, v);
 }
