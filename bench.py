@@ -18,6 +18,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import statistics
 import os
 import sys
 import time
@@ -96,6 +97,38 @@ def cpu_baseline(w, A_cpu, B_cpu, budget_s=12.0):
                 done_rows, w.M, w.dtype, w.M, w.N, w.K, total_t)}
 
 
+def lds_probe(torch, lib, workgroups=2048, reps=2048, rounds=8, launches=3):
+    """LDS read throughput per instruction form and address pattern, timed
+    round-robin.  Each workgroup of 256 threads reads 64 bytes per thread per
+    iteration: pattern "linear" is conflict-free for every width (the forms
+    differ by instruction alone), "swizzled" reads 16-byte pieces of
+    256-byte rows whose chunks are XOR-permuted by the row index."""
+    out = torch.empty(workgroups * lib.LDS_PROBE_THREADS, dtype=torch.int32, device="cuda:0")
+    nbytes = workgroups * lib.LDS_PROBE_THREADS * 64 * reps
+    cases = [(k, p) for p in range(2) for k in range(4)]
+    times = {c: [] for c in cases}
+    for k, p in cases:
+        lib.lds_read_probe(k, p, 16, out)  # warm-up
+    torch.cuda.synchronize()
+    for _ in range(rounds):
+        for k, p in cases:
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(launches)]
+            for e0, e1 in ev:
+                e0.record()
+                lib.lds_read_probe(k, p, reps, out)
+                e1.record()
+            torch.cuda.synchronize()
+            times[(k, p)] += [e0.elapsed_time(e1) for e0, e1 in ev]
+    for k, p in cases:
+        ms = statistics.median(times[(k, p)])
+        tbs = nbytes / (ms * 1e-3) / 1e12
+        print(json.dumps({"mode": "lds_probe", "instruction": lib.LDS_PROBE_KINDS[k],
+                          "pattern": lib.LDS_PROBE_PATTERNS[p], "workgroups": workgroups, "reps": reps,
+                          "bytes": nbytes, "median_ms": round(ms, 4), "TB_per_s": round(tbs, 2),
+                          "bytes_per_clk_per_cu_at_2p4GHz": round(tbs * 1e12 / 256 / 2.4e9, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -105,6 +138,9 @@ def main():
     ap.add_argument("--variant", default="")
     ap.add_argument("--ladder", action="store_true")
     ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--lds-probe", action="store_true",
+                    help="time the LDS read-path probe: the same bytes through ds_read_b32 / b64 / "
+                         "b128 / b64_tr_b16 (one JSON line per instruction form)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of MIB MiB (a reference for the HBM "
@@ -117,6 +153,10 @@ def main():
 
     import torch
     from tiled_software_pipelined_amd import inputs, lib, metrics
+
+    if args.lds_probe:
+        lds_probe(torch, lib)
+        return
 
     w = inputs.workloads()[args.workload]
     dev = torch.device("cuda:0")

@@ -156,8 +156,9 @@ typedef struct tgemm_plan_info {
     int32_t threads;         /* threads per workgroup */
     int32_t lds_bytes;       /* LDS per workgroup */
     int32_t loads_per_stage; /* global->LDS instructions per wave per stage */
-    int32_t a_guarded;       /* A uses the guarded narrow loader for every tile */
-    int32_t b_guarded;       /* B uses the guarded narrow loader for every tile */
+    int32_t a_guarded;       /* A rows are not 16-byte aligned: a register-staged kernel with
+                                shifted loads reads A (pointer alignment is checked per run) */
+    int32_t b_guarded;       /* the same for B (also when N is not a whole number of 16-byte chunks) */
     char name[96];           /* kernel name, e.g. "bf16_t256x256x64_s2_direct_xor_wide_reuse" */
 } tgemm_plan_info;
 
@@ -172,6 +173,32 @@ int gemm_variant_get(int32_t dtype, int32_t index, tgemm_variant* out);
 
 /* Library version string. */
 const char* tgemm_version(void);
+
+/* LDS read-path probe (a measurement harness, not part of the GEMM).
+ * Launches `workgroups` workgroups of 256 threads on `stream`; each fills a
+ * 16 KiB LDS block with pattern(i) = i * 2654435761 ^ (i >> 7) for dword i
+ * (mod 2^32), then for `reps` iterations reads 64 bytes per lane through
+ *   kind 0: 16 x ds_read_b32       kind 1: 8 x ds_read_b64
+ *   kind 2:  4 x ds_read_b128      kind 3: 8 x ds_read_b64_tr_b16
+ * at the addresses of
+ *   pattern 0 (linear, conflict-free at every width): instruction j of lane
+ *     l of wave w reads W bytes (W = its width) at w * 4096 + j * 64 W + l W;
+ *   pattern 1 (256-byte rows, 16-byte chunks XOR-permuted by row): four 16-byte
+ *     pieces, piece c of lane l of wave w in iteration r at
+ *     row * 256 + ((chunk ^ (row & 15)) * 16), row = (l & 31) + 32 (c & 1),
+ *     chunk = ((l >> 5) + 2 (c >> 1) + 4 ((r + w) & 3)) & 15, each read as
+ *     16 / W instructions at increasing offsets.
+ * Each thread keeps acc = rotl16(acc, 1) ^ fold16(XOR of the dwords it read
+ * in the iteration), fold16(x) = (x ^ x >> 16) & 0xffff, and writes it to
+ * out[workgroup * 256 + thread]; the XOR over one workgroup's 256 values
+ * does not depend on the kind (the transposing read only moves 16-bit
+ * elements between the lanes of a 16-lane group).  out: device memory of
+ * workgroups * 256 uint32 values, owned by the caller.  Returns TGEMM_OK,
+ * TGEMM_E_ARG (kind outside 0..3, pattern outside 0..1, reps < 0,
+ * workgroups < 1), TGEMM_E_NULL, TGEMM_E_ALIGN (out not 4-byte aligned) or
+ * TGEMM_E_HIP (launch failed). */
+int tgemm_lds_read_probe(int32_t kind, int32_t pattern, int32_t reps, int32_t workgroups, uint32_t* out,
+                         void* stream);
 
 #ifdef __cplusplus
 }

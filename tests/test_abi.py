@@ -138,6 +138,18 @@ def test_default_tile_follows_the_round_model():
     assert info.b_guarded == 1 and info.variant.tile_m == 128
 
 
+@pytest.mark.parametrize("dtype", [tl.F32, tl.BF16, tl.I8])
+def test_default_plan_exists_for_every_shape_class(dtype):
+    # every branch of the default choice must name a compiled kernel, for
+    # aligned and unaligned leading dimensions
+    sizes = [1, 7, 64, 127, 128, 129, 512, 1000, 2048, 4095, 4096, 4097, 8192]
+    for M in sizes:
+        for N in sizes:
+            for K in (1, 33, 1024, 1025, 4096, 4104, 8192):
+                for pad in (0, 1):
+                    tl.Plan(M, N, K, dtype, lda=K + pad, ldb=N + pad, ldc=N)
+
+
 def test_lds_budget_of_stage_ring():
     # 128 x 128 x 32 bf16: 8 KiB of A + 8 KiB of B per stage (the SM80 ablation
     # plan's stage table, section 1.4): S = 2, 3, 4 -> 32, 48, 64 KiB

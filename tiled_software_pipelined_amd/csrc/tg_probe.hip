@@ -1,0 +1,143 @@
+// LDS read-path probe: the same bytes read from LDS through four instruction
+// forms, to attribute the gain of wide fragment reads separately from the
+// GEMM, where matrix-core time hides it ("4.1 CUDA GEMM算子性能优化",
+// section 8: wide shared-memory reads and their bank behaviour; the
+// "流水化 GPU 内核" skill: ldmatrix-style reads cut instructions, not bytes).
+//
+// Every workgroup fills a 16 KiB LDS block (64 rows of 256 bytes, one
+// 64-bank window per row) with a fixed pattern, then each lane reads 64
+// bytes per iteration as
+//   kind 0: 16 x ds_read_b32        kind 1: 8 x ds_read_b64
+//   kind 2:  4 x ds_read_b128       kind 3: 8 x ds_read_b64_tr_b16
+// from one of two address patterns:
+//   pattern 0 (linear): instruction j of a wave reads 64 consecutive
+//     W-byte slots (W = its width), lane l the l-th - conflict-free for
+//     every width, so the kinds differ by instruction form alone;
+//   pattern 1 (swizzled): four 16-byte pieces in 256-byte rows whose
+//     16-byte chunks are permuted by an XOR with the row index, the kind of
+//     layout the GEMM's operands use; each piece is read as 16 / W
+//     instructions.
+// Each lane folds what it read into a 16-bit checksum, so that the host can
+// check every read happened and returned the right bytes (the transposing
+// read only permutes 16-bit elements within a 16-lane group; the XOR over a
+// workgroup does not see the permutation).
+#include <hip/hip_runtime.h>
+
+#include "tg_device.hpp"
+#include "tgemm.h"
+
+namespace tg {
+
+constexpr int PROBE_THREADS = 256;
+constexpr int PROBE_ROW = 256;
+constexpr int PROBE_ROWS = 64;
+constexpr int PROBE_DWORDS = PROBE_ROW * PROBE_ROWS / 4;
+
+__device__ __forceinline__ uint32_t probe_pattern(uint32_t i) { return i * 2654435761u ^ (i >> 7); }
+
+// pattern 1: byte address of 16-byte piece c (0..3) of lane l of wave w in
+// iteration r
+__device__ __forceinline__ uint32_t probe_addr(int l, int w, int r, int c) {
+    const int row = (l & 31) + 32 * (c & 1);
+    const int chunk = ((l >> 5) + 2 * (c >> 1) + 4 * ((r + w) & 3)) & 15;
+    return row * PROBE_ROW + (chunk ^ (row & 15)) * 16;
+}
+
+__device__ __forceinline__ uint32_t fold16(uint32_t x) { return (x ^ (x >> 16)) & 0xffffu; }
+
+template <int KIND, int PATTERN>
+__global__ __launch_bounds__(PROBE_THREADS) void lds_read_probe(uint32_t* out, int reps) {
+    __shared__ __attribute__((aligned(16))) uint32_t lds[PROBE_DWORDS];
+    for (int i = threadIdx.x; i < PROBE_DWORDS; i += PROBE_THREADS) lds[i] = probe_pattern(i);
+    __syncthreads();
+    const uint32_t base = (uint32_t)(uintptr_t)(TG_LDS char*)(lds);
+    const int l = lane_id(), w = wave_id();
+    // pattern 0: this lane's slot in the wave's 4 KiB quarter; instruction j
+    // adds j * 64 * W (an immediate offset)
+    constexpr int W = KIND == 0 ? 4 : KIND == 2 ? 16 : 8;
+    const uint32_t lin = base + w * 4096 + l * W;
+    uint32_t acc = 0;
+    for (int r = 0; r < reps; ++r) {
+        uint32_t a[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) a[c] = base + probe_addr(l, w, r, c);
+        uint32_t f = 0;
+        if constexpr (KIND == 0) {
+            uint32_t v[16];
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    if constexpr (PATTERN == 0)
+                        asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(v[4 * c + d]) : "v"(lin), "n"(256 * (4 * c + d)));
+                    else
+                        asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(v[4 * c + d]) : "v"(a[c]), "n"(4 * d));
+                }
+            // the wait names every result, so no use of one moves above it
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]),
+                           "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]), "+v"(v[12]), "+v"(v[13]),
+                           "+v"(v[14]), "+v"(v[15]));
+#pragma unroll
+            for (int i = 0; i < 16; ++i) f ^= v[i];
+        } else if constexpr (KIND == 2) {
+            i32x4 v[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                if constexpr (PATTERN == 0)
+                    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v[c]) : "v"(lin), "n"(1024 * c));
+                else
+                    asm volatile("ds_read_b128 %0, %1" : "=v"(v[c]) : "v"(a[c]));
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]));
+#pragma unroll
+            for (int c = 0; c < 4; ++c) f ^= uint32_t(v[c][0] ^ v[c][1] ^ v[c][2] ^ v[c][3]);
+        } else {
+            i32x2 v[8];
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t ad = PATTERN == 0 ? lin : a[c];
+                    if constexpr (KIND == 1) {
+                        if constexpr (PATTERN == 0)
+                            asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(v[2 * c + h]) : "v"(ad), "n"(512 * (2 * c + h)));
+                        else
+                            asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(v[2 * c + h]) : "v"(ad), "n"(8 * h));
+                    } else {
+                        if constexpr (PATTERN == 0)
+                            asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                                         : "=v"(v[2 * c + h])
+                                         : "v"(ad), "n"(512 * (2 * c + h)));
+                        else
+                            asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                                         : "=v"(v[2 * c + h])
+                                         : "v"(ad), "n"(8 * h));
+                    }
+                }
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]),
+                           "+v"(v[7]));
+#pragma unroll
+            for (int i = 0; i < 8; ++i) f ^= uint32_t(v[i][0] ^ v[i][1]);
+        }
+        acc = (((acc << 1) | (acc >> 15)) & 0xffffu) ^ fold16(f);
+    }
+    out[(int64_t)blockIdx.x * PROBE_THREADS + threadIdx.x] = acc;
+}
+
+}  // namespace tg
+
+extern "C" int tgemm_lds_read_probe(int32_t kind, int32_t pattern, int32_t reps, int32_t workgroups, uint32_t* out,
+                                    void* stream) {
+    if (kind < 0 || kind > 3 || pattern < 0 || pattern > 1 || reps < 0 || workgroups < 1) return TGEMM_E_ARG;
+    if (!out) return TGEMM_E_NULL;
+    if ((uintptr_t)out % 4) return TGEMM_E_ALIGN;
+    static void (*const fns[2][4])(uint32_t*, int) = {
+        {tg::lds_read_probe<0, 0>, tg::lds_read_probe<1, 0>, tg::lds_read_probe<2, 0>, tg::lds_read_probe<3, 0>},
+        {tg::lds_read_probe<0, 1>, tg::lds_read_probe<1, 1>, tg::lds_read_probe<2, 1>, tg::lds_read_probe<3, 1>}};
+    void* args[] = {&out, &reps};
+    const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(fns[pattern][kind]), dim3((unsigned)workgroups),
+                                           dim3(tg::PROBE_THREADS), args, 0, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? TGEMM_OK : TGEMM_E_HIP;
+}

@@ -140,10 +140,11 @@ const KernelEntry* default_entry(int dtype, int64_t M, int64_t N, int64_t K, boo
         pick = 64;
     v.tile_m = v.tile_n = pick;
     v.waves_n = pick == 256 ? 4 : 2;
-    // 128 x 128 direct: a 4-slot ring from K = 4096 (4-13 % faster than 3
-    // slots at 2048^2 x 4096, 4096 x 4352 x 4096, 1024^2 x 8192 and 2048^2 x
-    // 8192); 3 below (equal to 4 at K <= 1024, where the prologue dominates)
-    v.stages = pick == 256 || guarded ? 2 : (K >= 4096 ? 4 : 3);
+    // bf16 128 x 128 direct: a 4-slot ring from K = 4096 (4-13 % faster than
+    // 3 slots at 2048^2 x 4096, 4096 x 4352 x 4096, 1024^2 x 8192 and 2048^2
+    // x 8192); 3 below (equal to 4 at K <= 1024, where the prologue
+    // dominates) and for the other tiles and int8
+    v.stages = pick == 256 || guarded ? 2 : (pick == 128 && !i8 && K >= 4096 ? 4 : 3);
     v.loader = guarded ? TGEMM_LOADER_VGPR : TGEMM_LOADER_DIRECT;
     return find_entry(dtype, v);
 }

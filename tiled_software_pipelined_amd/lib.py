@@ -55,7 +55,8 @@ class PlanInfo(ctypes.Structure):
 
 
 EXPORTS = ("gemm_plan", "gemm_plan_variant", "gemm_run", "gemm_destroy", "tgemm_last_error",
-           "gemm_plan_get_info", "gemm_variant_count", "gemm_variant_get", "tgemm_version")
+           "gemm_plan_get_info", "gemm_variant_count", "gemm_variant_get", "tgemm_version",
+           "tgemm_lds_read_probe")
 
 
 def _load():
@@ -86,6 +87,8 @@ def _load():
     lib.gemm_variant_get.restype = ctypes.c_int
     lib.tgemm_version.argtypes = []
     lib.tgemm_version.restype = ctypes.c_char_p
+    lib.tgemm_lds_read_probe.argtypes = [i32, i32, i32, i32, vp, vp]
+    lib.tgemm_lds_read_probe.restype = ctypes.c_int
     return lib
 
 
@@ -104,6 +107,27 @@ def last_error() -> str:
 
 def version() -> str:
     return _lib.tgemm_version().decode()
+
+
+LDS_PROBE_KINDS = ("ds_read_b32", "ds_read_b64", "ds_read_b128", "ds_read_b64_tr_b16")
+LDS_PROBE_PATTERNS = ("linear", "swizzled")
+LDS_PROBE_THREADS = 256
+
+
+def lds_read_probe(kind: int, pattern: int, reps: int, out):
+    """Launch the LDS read-path probe on the current stream: one workgroup
+    per 256 entries of ``out`` (a uint32-compatible int32 GPU tensor)."""
+    import torch
+    if not out.is_cuda or out.dtype != torch.int32 or out.numel() % LDS_PROBE_THREADS or not out.is_contiguous():
+        raise ValueError("out must be a contiguous int32 GPU tensor of 256 * workgroups entries")
+    wgs = out.numel() // LDS_PROBE_THREADS
+    stream = torch.cuda.current_stream(out.device).cuda_stream
+    with torch.cuda.device(out.device):
+        rc = _lib.tgemm_lds_read_probe(kind, pattern, reps, wgs, out.data_ptr(), stream)
+    if rc != OK:
+        raise TgemmError(rc, "tgemm_lds_read_probe(kind=%d, pattern=%d, reps=%d, workgroups=%d)" % (
+            kind, pattern, reps, wgs))
+    return out
 
 
 def variants(dtype: int):
