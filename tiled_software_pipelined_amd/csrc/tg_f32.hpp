@@ -95,31 +95,64 @@ struct F32Gemm {
         else return base + 8 * idx + i;
     }
 
-    __device__ static __forceinline__ void compute(const TG_LDS char* slot, float (&c)[8][8], int wm, int wn,
-                                                   int lr, int lc) {
+    struct Frag {
+        float a[8], b[8];
+    };
+
+    __device__ static __forceinline__ void read_frag(Frag& f, const TG_LDS char* slot, int k, int wm, int wn,
+                                                     int lr, int lc) {
         const TG_LDS float* As = reinterpret_cast<const TG_LDS float*>(slot);
         const TG_LDS float* Bs = reinterpret_cast<const TG_LDS float*>(slot + A_BYTES);
+        if constexpr (TRANS_A) {
+            // rows frag_off(wm, lr, 0..3) and frag_off(wm, lr, 4..7) are each 4 contiguous
+            const f32x4 a0 = *reinterpret_cast<const TG_LDS f32x4*>(As + k * BM + frag_off(wm, lr, 0));
+            const f32x4 a1 = *reinterpret_cast<const TG_LDS f32x4*>(As + k * BM + frag_off(wm, lr, 4));
+            f.a[0] = a0.x; f.a[1] = a0.y; f.a[2] = a0.z; f.a[3] = a0.w;
+            f.a[4] = a1.x; f.a[5] = a1.y; f.a[6] = a1.z; f.a[7] = a1.w;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) f.a[i] = As[frag_off(wm, lr, i) * BK + k];
+        }
+        const f32x4 b0 = *reinterpret_cast<const TG_LDS f32x4*>(Bs + k * BN + frag_off(wn, lc, 0));
+        const f32x4 b1 = *reinterpret_cast<const TG_LDS f32x4*>(Bs + k * BN + frag_off(wn, lc, 4));
+        f.b[0] = b0.x; f.b[1] = b0.y; f.b[2] = b0.z; f.b[3] = b0.w;
+        f.b[4] = b1.x; f.b[5] = b1.y; f.b[6] = b1.z; f.b[7] = b1.w;
+    }
+
+    // End of one outer-product step: an empty asm that takes every
+    // accumulator in and out and clobbers memory, so that this step's FMAs
+    // stay before it, the next step's after it, and the LDS reads issued for
+    // the step after next cannot be hoisted above it (neither the FMAs nor
+    // plain LDS loads are ordered by a scheduling barrier alone).
+    __device__ static __forceinline__ void step_fence(float (&c)[8][8]) {
+#pragma unroll
+        for (int i = 0; i < 8; i += 2)
+            asm volatile(""
+                         : "+v"(c[i][0]), "+v"(c[i][1]), "+v"(c[i][2]), "+v"(c[i][3]), "+v"(c[i][4]),
+                           "+v"(c[i][5]), "+v"(c[i][6]), "+v"(c[i][7]), "+v"(c[i + 1][0]), "+v"(c[i + 1][1]),
+                           "+v"(c[i + 1][2]), "+v"(c[i + 1][3]), "+v"(c[i + 1][4]), "+v"(c[i + 1][5]),
+                           "+v"(c[i + 1][6]), "+v"(c[i + 1][7])
+                         :
+                         : "memory");
+    }
+
+    // The slice's BK outer products, each lane's 8 x 8 block at a time.  The
+    // fragments of step k+1 are read while the 64 FMAs of step k issue, and a
+    // fence per step keeps the compiler from hoisting the reads of the whole
+    // slice ahead (which took 219 registers and limited a SIMD to 2 waves).
+    __device__ static __forceinline__ void compute(const TG_LDS char* slot, float (&c)[8][8], int wm, int wn,
+                                                   int lr, int lc) {
+        Frag f[2];
+        read_frag(f[0], slot, 0, wm, wn, lr, lc);
 #pragma unroll
         for (int k = 0; k < BK; ++k) {
-            float a[8], b[8];
-            if constexpr (TRANS_A) {
-                // rows frag_off(wm, lr, 0..3) and frag_off(wm, lr, 4..7) are each 4 contiguous
-                const f32x4 a0 = *reinterpret_cast<const TG_LDS f32x4*>(As + k * BM + frag_off(wm, lr, 0));
-                const f32x4 a1 = *reinterpret_cast<const TG_LDS f32x4*>(As + k * BM + frag_off(wm, lr, 4));
-                a[0] = a0.x; a[1] = a0.y; a[2] = a0.z; a[3] = a0.w;
-                a[4] = a1.x; a[5] = a1.y; a[6] = a1.z; a[7] = a1.w;
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) a[i] = As[frag_off(wm, lr, i) * BK + k];
-            }
-            const f32x4 b0 = *reinterpret_cast<const TG_LDS f32x4*>(Bs + k * BN + frag_off(wn, lc, 0));
-            const f32x4 b1 = *reinterpret_cast<const TG_LDS f32x4*>(Bs + k * BN + frag_off(wn, lc, 4));
-            b[0] = b0.x; b[1] = b0.y; b[2] = b0.z; b[3] = b0.w;
-            b[4] = b1.x; b[5] = b1.y; b[6] = b1.z; b[7] = b1.w;
+            if (k + 1 < BK) read_frag(f[(k + 1) & 1], slot, k + 1, wm, wn, lr, lc);
+            const Frag& x = f[k & 1];
 #pragma unroll
             for (int i = 0; i < 8; ++i)
 #pragma unroll
-                for (int j = 0; j < 8; ++j) c[i][j] = __builtin_fmaf(a[i], b[j], c[i][j]);
+                for (int j = 0; j < 8; ++j) c[i][j] = __builtin_fmaf(x.a[i], x.b[j], c[i][j]);
+            step_fence(c);
         }
     }
 
@@ -158,6 +191,7 @@ struct F32Gemm {
                 store(smem, r);
                 wait_lds_then_barrier();
             }
+#pragma nounroll
             for (int t = 0; t < tiles; ++t) {
                 const int nxt = t + 1;
                 Staged r;
