@@ -67,6 +67,35 @@ def time_plan(lib, torch, w, A, B, C, variant, steps, warmup):
     return per, wall
 
 
+def time_graph(lib, torch, A, B, C, variant, per_graph=20, replays=10):
+    """Per-launch time (ms) from replaying a HIP graph of `per_graph`
+    launches: no host work inside the timed interval, so short kernels are
+    timed at the GPU's own cadence rather than the launch path's.  Returns
+    (median ms per launch, whether every replay reproduced the eager C)."""
+    lib.gemm(A, B, out=C, variant=variant)
+    torch.cuda.synchronize()
+    eager = C.clone()
+    side = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for _ in range(per_graph):
+            lib.gemm(A, B, out=C, variant=variant)
+    same = True
+    per = []
+    for _ in range(replays):
+        C.zero_()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) / per_graph)
+        same = same and bool(torch.equal(C, eager))
+    del graph
+    return statistics.median(per), same
+
+
 def cpu_baseline(w, A_cpu, B_cpu, budget_s=12.0):
     """The oracle (fp64 / int64 triple loop, OpenMP) on a row sample of the
     same operands: rows are taken until about `budget_s` of CPU work."""
@@ -203,7 +232,10 @@ def main():
             print(json.dumps(rec), flush=True)
     if args.sweep:
         # heatmap: every bf16 sweep shape x (128x128x32 tile at 2, 3, 4 stages,
-        # and the default plan)
+        # and the default plan).  The per-launch time is taken from HIP-graph
+        # replay (the smallest shapes run for a few microseconds, less than
+        # the host's launch path, so eager timing would measure the host);
+        # the eager per-launch median is reported beside it.
         stage_vs = [("s%d" % st, lib.Variant(kernel=lib.KERNEL_TILED, tile_m=128, tile_n=128, tile_k=32,
                                             stages=st, loader=lib.LOADER_DIRECT, waves_m=2, waves_n=2))
                     for st in (2, 3, 4)] + [("default", None)]
@@ -217,10 +249,14 @@ def main():
                                                    PEAK_HBM_GBS * 1e9)
             for label, v in stage_vs:
                 per, _ = time_plan(lib, torch, sw, a, b, c, v, max(10, args.steps // 2), 5)
-                ms = sorted(per)[len(per) // 2]
+                eager_ms = sorted(per)[len(per) // 2]
+                ms, same = time_graph(lib, torch, a, b, c, v)
+                if not same:
+                    raise RuntimeError("graph replay of %s (%s) did not reproduce the eager result" % (name, label))
                 kname = lib.plan_for(sw.M, sw.N, sw.K, lib.BF16, sw.K, sw.N, sw.N, v).name
                 print(json.dumps({"mode": "sweep", "workload": name, "plan": label, "kernel": kname,
-                                  "median_ms": ms, "tflops": sw.flops / ms / 1e9,
+                                  "median_ms": ms, "eager_median_ms": eager_ms, "tflops": sw.flops / ms / 1e9,
+                                  "eager_tflops": sw.flops / eager_ms / 1e9,
                                   "frac_peak": sw.flops / ms / 1e9 / PEAK_TFLOPS["bf16"],
                                   "frac_roofline": ideal_ms / ms}), flush=True)
             del a, b, c

@@ -94,8 +94,13 @@ def test_default_choice_by_shape():
     mid = tl.Plan(1024, 1024, 512, tl.BF16).info()
     assert (mid.variant.tile_m, mid.variant.tile_n) == (128, 128) and mid.grid == 64
     assert mid.variant.stages == 3
-    # long K on the 128 x 128 tile: the deeper ring
+    # long K on the 128 x 128 tile: the deeper ring; on the 64 x 64 tile the
+    # 8-slot ring
     assert tl.Plan(2048, 2048, 4096, tl.BF16).info().variant.stages == 4
+    for dtype in (tl.BF16, tl.I8):
+        small = tl.Plan(512, 512, 4096, dtype).info().variant
+        assert (small.tile_m, small.stages) == (64, 8), dtype
+        assert tl.Plan(512, 512, 1024, dtype).info().variant.stages == 3
     small = tl.Plan(512, 512, 512, tl.BF16).info()
     assert (small.variant.tile_m, small.variant.tile_n) == (64, 64) and small.grid == 64
     f = tl.Plan(256, 256, 256, tl.F32).info()

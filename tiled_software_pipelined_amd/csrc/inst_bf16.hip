@@ -20,6 +20,9 @@ void register_bf16(void (*add)(const KernelEntry&)) {
     add(mfma_entry<T, 256, 256, 64, 2, 4, 2, LD_VGPR, LY_XOR, AC_WIDE, FR_REUSE, 2>(1));
     // small problems: more workgroups per CU count
     add(mfma_entry<T, 64, 64, 64, 2, 2, 3, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 4>(1));
+    // a deep ring for small grids (about one workgroup per compute unit),
+    // where each slice's load latency is exposed unless many are in flight
+    add(mfma_entry<T, 64, 64, 64, 2, 2, 8, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 4>(1));
     // the 128 x 128 x 32 ladder, one change per step
     add(mfma_entry<T, 128, 128, 32, 2, 2, 3, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2>(1));
     add(mfma_entry<T, 128, 128, 32, 2, 2, 4, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2>(1));

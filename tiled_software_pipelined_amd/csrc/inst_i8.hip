@@ -15,6 +15,7 @@ void register_i8(void (*add)(const KernelEntry&)) {
     add(mfma_entry<T, 128, 128, 64, 2, 2, 2, LD_VGPR, LY_XOR, AC_WIDE, FR_REUSE, 2>(2));
     add(mfma_entry<T, 128, 128, 64, 2, 2, 1, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2>(2));
     add(mfma_entry<T, 64, 64, 128, 2, 2, 3, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 4>(2));
+    add(mfma_entry<T, 64, 64, 128, 2, 2, 8, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 4>(2));
     add(mfma_entry<T, 128, 128, 64, 2, 2, 1, LD_VGPR, LY_PLAIN, AC_NARROW, FR_PER_MMA, 2>(2));
     add(naive_entry<2>());
     // unlisted: the register-staged defaults reading rows that are not

@@ -758,14 +758,25 @@ struct MfmaGemm {
                 }
     }
 
+    // Wait until at most `ahead` slices' copies (issued after the one needed
+    // next) are still in flight, then barrier.  The wait count is an
+    // immediate, so the runtime `ahead` (0 .. STAGES-2) selects among
+    // compile-time instances.
+    template <int A>
+    __device__ static __forceinline__ void wait_ahead(int ahead) {
+        if constexpr (A > 0) {
+            if (ahead >= A) {
+                wait_vm_then_barrier<A * N_LD>();
+                return;
+            }
+            wait_ahead<A - 1>(ahead);
+        } else {
+            wait_vm_then_barrier<0>();
+        }
+    }
+
     __device__ static __forceinline__ void wait_slice(int ahead) {
-        if constexpr (STAGES >= 4) {
-            if (ahead >= 2) { wait_vm_then_barrier<2 * N_LD>(); return; }
-        }
-        if constexpr (STAGES >= 3) {
-            if (ahead >= 1) { wait_vm_then_barrier<N_LD>(); return; }
-        }
-        wait_vm_then_barrier<0>();
+        wait_ahead<(STAGES > 2 ? STAGES - 2 : 0)>(ahead);
     }
 
     __device__ static __forceinline__ void run(const GemmArgs& g) {

@@ -145,6 +145,10 @@ const KernelEntry* default_entry(int dtype, int64_t M, int64_t N, int64_t K, boo
     // x 8192); 3 below (equal to 4 at K <= 1024, where the prologue
     // dominates) and for the other tiles and int8
     v.stages = pick == 256 || guarded ? 2 : (pick == 128 && !i8 && K >= 4096 ? 4 : 3);
+    // 64 x 64 tiles (grids of about one workgroup per compute unit): an
+    // 8-slot ring from K = 2048 (6-20 % faster than 3 slots at 512^2 x
+    // 2048..8192, 768^2 x 4096 and 512 x 1024 x 8192, timed by graph replay)
+    if (pick == 64 && K >= 2048) v.stages = 8;
     v.loader = guarded ? TGEMM_LOADER_VGPR : TGEMM_LOADER_DIRECT;
     return find_entry(dtype, v);
 }
