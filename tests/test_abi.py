@@ -155,6 +155,22 @@ def test_default_plan_exists_for_every_shape_class(dtype):
                     tl.Plan(M, N, K, dtype, lda=K + pad, ldb=N + pad, ldc=N)
 
 
+def test_huge_leading_dimension_leaves_the_direct_loader():
+    # the direct loader's per-lane offsets are 32-bit: (BM-1)*lda*2 bytes
+    # must fit.  lda = 8.5M bf16 overflows them on a 256-row tile.
+    req = tl.Variant(kernel=tl.KERNEL_TILED, tile_m=256, tile_n=256, tile_k=64, waves_n=4,
+                     loader=tl.LOADER_DIRECT)
+    assert tl.Plan(256, 256, 512, tl.BF16, variant=req).info().variant.loader == tl.LOADER_DIRECT
+    v = tl.Plan(256, 256, 512, tl.BF16, lda=8_500_000, variant=req).info().variant
+    assert v.loader == tl.LOADER_VGPR and (v.tile_m, v.tile_n) == (256, 256)
+    # a huge ldb (B offsets reach (BK-1)*ldb)
+    v = tl.Plan(4096, 4096, 4096, tl.BF16, ldb=40_000_000).info().variant
+    assert v.loader == tl.LOADER_VGPR
+    # the default plan of a small shape too
+    v = tl.Plan(512, 512, 512, tl.BF16, lda=40_000_000).info().variant
+    assert v.loader == tl.LOADER_VGPR
+
+
 def test_lds_budget_of_stage_ring():
     # 128 x 128 x 32 bf16: 8 KiB of A + 8 KiB of B per stage (the SM80 ablation
     # plan's stage table, section 1.4): S = 2, 3, 4 -> 32, 48, 64 KiB

@@ -325,6 +325,26 @@ def test_streaming_and_plain_C_stores_agree(dtype):
         assert torch.equal(got, ref), (ldc, off)
 
 
+def test_huge_leading_dimension():
+    # lda = 8.5M bf16 (17 MB rows, a 4.35 GB A): the direct loader's 32-bit
+    # per-lane offsets would wrap on a 256-row tile, so the plan takes the
+    # register-staged kernel; only the first K columns of each row are set
+    M, N, K, lda = 256, 256, 512, 8_500_000
+    A = inputs.operand("bf16_normal", M, K, 97)
+    B = inputs.operand("bf16_normal", K, N, 98)
+    big = torch.empty((M, lda), dtype=torch.bfloat16, device="cuda")
+    big[:, :K].copy_(A.cuda())
+    Bd = B.cuda()
+    C = torch.full((M, N), -7.0, dtype=torch.float32, device="cuda")
+    req = tl.Variant(kernel=tl.KERNEL_TILED, tile_m=256, tile_n=256, tile_k=64, waves_n=4,
+                     loader=tl.LOADER_DIRECT)
+    assert tl.plan_for(M, N, K, tl.BF16, lda, N, N, req).info().variant.loader == tl.LOADER_VGPR
+    tl.gemm(big[:, :K], Bd, out=C, variant=req)
+    torch.cuda.synchronize()
+    del big
+    _assert_parity(C.cpu(), A, B, "bf16")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "i8"])
 def test_K_zero_writes_zeros(dtype):
     A = torch.zeros((70, 0), dtype=inputs.KINDS[KIND[dtype]])

@@ -504,8 +504,8 @@ struct MfmaGemm {
     // One K step issues its FM*FN matrix-core instructions one at a time and
     // puts the step's memory instructions (fragment reads for the next K
     // step, copies for a later slice) between them, fenced so the compiler
-    // keeps the order: with one wave per SIMD nothing else keeps the matrix
-    // core busy while a burst of LDS instructions is being issued.
+    // keeps the order: with one or two waves per SIMD little else keeps the
+    // matrix core busy while a burst of LDS instructions is being issued.
     static constexpr int NM = FM * FN;      // matrix-core instructions per K step
     static constexpr int NR = FM + 2 * FN;  // LDS reads per K step (A: 1 each, B: 2 each)
 
@@ -588,36 +588,15 @@ struct MfmaGemm {
                                wn0, lane, wave);
     }
 
-    struct NoHook {
-        __device__ void operator()(int) const {}
-    };
-
-    // Issues K step s's share of the copies of the next slice (if `on`).
-    struct DirectHook {
-        TG_LDS char* slot;
-        const DirectOffsets& off;
-        const char* abase;
-        const char* bbase;
-        int wave;
-        bool on;
-        __device__ __forceinline__ void operator()(int s) const {
-            constexpr int PER = (N_LD + KSUB - 1) / KSUB;
-            if (!on) return;
-#pragma unroll
-            for (int i = 0; i < PER; ++i)
-                if (s * PER + i < N_LD) issue_direct_one(s * PER + i, slot, off, abase, bbase, wave);
-        }
-    };
-
     // Multiply one slice held in `slot` into the accumulators.  With
     // fragment reuse the reads are software-pipelined one K step ahead
     // (register double buffer, "4.1 CUDA GEMM算子性能优化" section 9.2): the
     // fragments of step s+1 are requested before the matrix-core work of
-    // step s, which hides the LDS latency behind it.  hook(s) runs between
-    // the two and issues this step's share of the next slice's copies.
-    template <class Hook = NoHook>
+    // step s, which hides the LDS latency behind it.  (The register-staged
+    // loops and the K tail use this; the direct ring's steady state runs
+    // slice_direct, which also interleaves the copies.)
     __device__ static __forceinline__ void compute(const TG_LDS char* slot, Acc (&acc)[FM][FN],
-                                                   int wm0, int wn0, int lane, Hook hook = Hook()) {
+                                                   int wm0, int wn0, int lane) {
         const TG_LDS char* bslot = slot + A_BYTES;
         if constexpr (FRAG == FR_REUSE) {
             Frags f[2];
@@ -625,7 +604,6 @@ struct MfmaGemm {
 #pragma unroll
             for (int s = 0; s < KSUB; ++s) {
                 if (s + 1 < KSUB) read_frags(f[(s + 1) & 1], slot, s + 1, wm0, wn0, lane);
-                hook(s);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
@@ -637,22 +615,17 @@ struct MfmaGemm {
         }
 #pragma unroll
         for (int s = 0; s < KSUB; ++s) {
-            hook(s);
-            {
 #pragma unroll
-                for (int i = 0; i < FM; ++i)
+            for (int i = 0; i < FM; ++i)
 #pragma unroll
-                    for (int j = 0; j < FN; ++j) {
-                        const i32x4 a = read_a(slot, wm0 + 32 * i, s, lane);
-                        const i32x4 b = read_b(bslot, wn0 + 32 * j, s, lane);
-                        acc[i][j] = Tr::mma(a, b, acc[i][j]);
-                    }
-            }
+                for (int j = 0; j < FN; ++j) {
+                    const i32x4 a = read_a(slot, wm0 + 32 * i, s, lane);
+                    const i32x4 b = read_b(bslot, wn0 + 32 * j, s, lane);
+                    acc[i][j] = Tr::mma(a, b, acc[i][j]);
+                }
         }
     }
 
-    // Wait until this wave's copies of slice t are in LDS (`ahead` later
-    // slices may stay in flight), then barrier.
     // K loop of the register-staged loaders: the `full` whole slices with
     // MODE_A / MODE_B loads, then the partial last slice (if tiles > full)
     // with element loads.  STAGES == 1: load, store, barrier, multiply,

@@ -70,6 +70,17 @@ void ld_guards(const KernelEntry& e, int64_t N, int64_t lda, int64_t ldb, int32_
     *gb = (ldb * esz) % bytes != 0 || N % per != 0 || N < per;
 }
 
+// The direct loader addresses each lane's 16 bytes as a wave-uniform base
+// plus a 32-bit byte offset from the slice's first row: up to (BM-1)*lda
+// elements into A and (BK-1)*ldb + BN into B.  Larger leading dimensions
+// need a register-staged kernel (64-bit addresses).
+bool direct_fits(const KernelEntry& e, int64_t lda, int64_t ldb) {
+    if (e.loader != tg::LD_DIRECT) return true;
+    const int64_t esz = elem_size(e.dtype);
+    const int64_t lim = INT64_C(0xffffffff);
+    return ((int64_t)(e.bm - 1) * lda + e.bk) * esz <= lim && ((int64_t)(e.bk - 1) * ldb + e.bn) * esz <= lim;
+}
+
 bool field_ok(int want, int have) { return want == 0 || want == have; }
 
 bool matches(const KernelEntry& e, const tgemm_variant& v) {
@@ -284,6 +295,22 @@ tgemm_plan* gemm_plan_variant(int64_t M, int64_t N, int64_t K, int32_t dtype, in
     if (!e) {
         set_err("no compiled variant matches the request (see gemm_variant_get)");
         return nullptr;
+    }
+    if (!direct_fits(*e, lda, ldb)) {
+        // leading dimensions too large for the direct loader's 32-bit
+        // offsets: the register-staged kernel of the same tile, else the
+        // register-staged default for the shape
+        tgemm_variant r{};
+        entry_to_variant(*e, 0, &r);
+        r.loader = TGEMM_LOADER_VGPR;
+        r.stages = 2;
+        r.wg_group = 0;
+        const KernelEntry* rs = find_entry(dtype, r);
+        e = rs ? rs : default_entry(dtype, M, N, K, true);
+        if (!e || !direct_fits(*e, lda, ldb)) {
+            set_err("no kernel addresses leading dimensions lda=%lld ldb=%lld", (long long)lda, (long long)ldb);
+            return nullptr;
+        }
     }
     // Kernels for every combination of misaligned operands (pointers are
     // only known per run); the leading dimensions fix which one this plan
