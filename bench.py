@@ -10,16 +10,20 @@ events on the launch stream) and the CPU oracle's rate on a bounded sample of
 the same workload.
 
 Extra modes (not used by the default run):
-    --ladder   time every compiled variant of the workload's dtype (one JSON
-               line each, then the summary line)
-    --sweep    time the default plan on the bf16 shape sweep
+    --ladder     time every listed variant of the workload's dtype, round-robin
+                 (one JSON line each, then the summary line)
+    --sweep      the bf16 shape sweep: the 128x128x32 tile at 2 / 3 / 4 stages
+                 and the default plan per shape, timed by HIP-graph replay
+                 (eager per-launch times beside them)
+    --lds-probe  LDS read throughput of ds_read_b32 / b64 / b128 / b64_tr_b16
+    --gpus N     N > 1 exits: this path runs on one GPU
 """
 from __future__ import annotations
 
 import argparse
 import json
-import statistics
 import os
+import statistics
 import sys
 import time
 

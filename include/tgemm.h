@@ -122,7 +122,10 @@ typedef struct tgemm_plan tgemm_plan;
 /* Create a plan for an M x N x K product of the given type with the given
  * leading dimensions (elements).  Requires M, N, K >= 0, lda >= K, ldb >= N,
  * ldc >= N (each leading dimension >= 1).  Does not touch the device.  The
- * plan picks the fastest variant built for this shape.  Returns NULL on error. */
+ * plan picks the variant for this shape (tile size by a measured time model
+ * of the grid, ring depth by K) and, for each combination of operands whose
+ * rows may turn out unaligned at run time, the kernel that reads them.
+ * Returns NULL on error (tgemm_last_error says why). */
 tgemm_plan* gemm_plan(int64_t M, int64_t N, int64_t K, int32_t dtype,
                       int64_t lda, int64_t ldb, int64_t ldc);
 
@@ -136,8 +139,14 @@ tgemm_plan* gemm_plan_variant(int64_t M, int64_t N, int64_t K, int32_t dtype,
  * the current HIP device.  A, B, C are device pointers (or any pointers the
  * device can access) aligned to their element size.  A pointer that is
  * element-aligned but not 16-byte aligned, or a leading dimension whose rows
- * are not 16-byte aligned, makes that operand use the guarded narrow loader
- * (slower, same results).  Returns TGEMM_OK or a TGEMM_E_* code. */
+ * are not 16-byte aligned, makes the run use a register-staged kernel that
+ * reads that operand as shifted pairs of aligned 16-byte blocks (slower,
+ * same results); so does a leading dimension too large for the direct
+ * loader's 32-bit lane offsets (from the plan on).  Nothing outside
+ * [A, A + ((M-1)*lda + K) elements) or the corresponding range of B is read.
+ * C outside its M x N window is not written.  The launch is asynchronous:
+ * execution errors surface at the stream's next synchronisation.  Returns
+ * TGEMM_OK or a TGEMM_E_* code. */
 int gemm_run(const tgemm_plan* plan, const void* A, const void* B, void* C,
              void* stream);
 
