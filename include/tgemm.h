@@ -168,7 +168,10 @@ typedef struct tgemm_plan_info {
     int32_t a_guarded;       /* A rows are not 16-byte aligned: a register-staged kernel with
                                 shifted loads reads A (pointer alignment is checked per run) */
     int32_t b_guarded;       /* the same for B (also when N is not a whole number of 16-byte chunks) */
-    char name[96];           /* kernel name, e.g. "bf16_t256x256x64_s2_direct_xor_wide_reuse" */
+    char name[96];           /* kernel name, e.g. "bf16_t256x256x64_w2x4_s2_direct_xor_wide_reuse" */
+    int64_t n_main;          /* columns the kernel above covers: N, or for a split plan the first
+                                N - r, the last r (<= 16) going to the thin kernel `rem_name` */
+    char rem_name[96];       /* split plans: the kernel of the last columns; else "" */
 } tgemm_plan_info;
 
 /* Fill *info for `plan`.  Returns TGEMM_OK or TGEMM_E_NULL. */

@@ -112,10 +112,12 @@ def test_unaligned_leading_dimension_uses_guarded_register_loader():
     info = tl.Plan(4095, 4097, 4104, tl.BF16).info()
     assert info.b_guarded == 1 and info.a_guarded == 0
     assert info.variant.loader == tl.LOADER_VGPR
-    # 256 x 256 tiles would be 272 workgroups, one per compute unit: two
-    # rounds, 53 % full; the 128 x 128 register-staged tile wins on rate x fill
-    assert (info.variant.tile_m, info.variant.tile_n) == (128, 128)
-    assert info.grid == 32 * 33
+    # split: the first 4096 columns on 256 x 256 tiles (one round of 256
+    # workgroups; 4097 columns would need 272 of them, or 1056 of 128 x 128),
+    # the last column on the thin kernel
+    assert (info.variant.tile_m, info.variant.tile_n) == (256, 256)
+    assert info.grid == 16 * 16 and info.n_main == 4096
+    assert b"thin" in info.rem_name
     # a small unaligned problem keeps a small register-staged tile
     for dtype in (tl.BF16, tl.I8):
         v = tl.Plan(150, 131, 101, dtype).info().variant
@@ -135,12 +137,34 @@ def test_default_tile_follows_the_round_model():
     for (M, N, want) in [(4096, 4096, 256), (5120, 5120, 256), (3072, 3072, 256), (4096, 4352, 128),
                          (4096, 4608, 128)]:
         assert tl.Plan(M, N, 4096, tl.BF16).info().variant.tile_m == want, (M, N)
-    # unaligned B: 4096^2 keeps the 256 x 256 register-staged kernel, the
-    # 272-tile 4096 x 4097 takes the 128 x 128 one
+    # unaligned B: 4096^2 keeps the 256 x 256 register-staged kernel
     big = tl.Plan(4096, 4096, 4096, tl.BF16, ldb=4097).info()
     assert big.b_guarded == 1 and big.variant.tile_m == 256 and big.variant.loader == tl.LOADER_VGPR
+    # 4096 x 4097 splits off its last column (272 big tiles or 1056 small
+    # ones would need a second round); with a padded, aligned ldb the main
+    # part is the direct-loader kernel
     info = tl.Plan(4096, 4097, 4096, tl.BF16).info()
-    assert info.b_guarded == 1 and info.variant.tile_m == 128
+    assert info.b_guarded == 1 and info.variant.tile_m == 256 and info.n_main == 4096
+    info = tl.Plan(4096, 4097, 4096, tl.BF16, ldb=4104).info()
+    assert info.n_main == 4096 and info.variant.loader == tl.LOADER_DIRECT and b"thin" in info.rem_name
+    # 4096 x 4352 leaves no thin remainder: no split
+    info = tl.Plan(4096, 4352, 4096, tl.BF16).info()
+    assert info.n_main == 4352 and info.rem_name == b""
+
+
+def test_thin_products_use_the_thin_kernel():
+    # N <= 16 with rows the direct loader cannot read (N not a whole number of
+    # 16-byte pieces, or an unaligned ldb): the thin kernel of the smallest
+    # width that covers N; with aligned rows the direct-loader tile
+    for dtype in (tl.BF16, tl.I8):
+        for N, ldb, width in [(1, 1, 1), (7, 7, 8), (16, 17, 16), (3, 64, 4)]:
+            info = tl.Plan(4096, N, 4096, dtype, ldb=ldb).info()
+            assert b"thin" in info.name and info.n_main == N, (dtype, N, ldb)
+            assert info.variant.tile_n == width and info.grid == 4096 // (8 if width == 16 else 16)
+        assert b"thin" not in tl.Plan(4096, 16, 4096, dtype, ldb=32).info().name
+        assert b"thin" not in tl.Plan(4096, 17, 4096, dtype, ldb=17).info().name
+    # fp32 keeps its one-fma-chain-per-output kernel
+    assert b"thin" not in tl.Plan(4096, 4, 4096, tl.F32).info().name
 
 
 @pytest.mark.parametrize("dtype", [tl.F32, tl.BF16, tl.I8])

@@ -33,6 +33,8 @@ CASES = [
     ("i8_uniform", 520, 264, 1000, 0),
     ("f32_uniform", 200, 136, 96, 0),     # vector-FMA path
     ("bf16_normal", 70, 90, 0, 0),        # K = 0: the fill kernel
+    ("bf16_normal", 4096, 4097, 256, 0),  # split plan: tiled kernel + thin kernel
+    ("i8_uniform", 2000, 9, 700, 1),      # thin kernel
 ]
 
 

@@ -325,6 +325,40 @@ def test_streaming_and_plain_C_stores_agree(dtype):
         assert torch.equal(got, ref), (ldc, off)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "i8"])
+def test_thin_kernel(dtype):
+    # N <= 16: the thin kernel (rows per wave, lanes along K, a cross-lane
+    # sum) where rows are unaligned, the direct-loader tile where they are
+    # aligned; offset pointers and K tails
+    ce = 8 if dtype == "bf16" else 16
+    for (M, N, K) in [(1, 1, 1), (5, 3, 7), (17, 16, 9), (33, 8, 1029), (1000, 1, 4104), (64, 16, 64),
+                      (130, 5, 520)]:
+        A = inputs.operand(KIND[dtype], M, K, 101 + K)
+        B = inputs.operand(KIND[dtype], K, N, 102 + K)
+        lda_al = (K + ce - 1) // ce * ce
+        C_ref, S = _oracle(A, B, dtype)
+        # rows the direct loader cannot read take the thin kernel
+        assert b"thin" in tl.plan_for(M, N, K, DT[dtype], K + 1, N + 3, N).info().name
+        for (lda, oa, ldb, ob) in [(lda_al, 0, N, 0), (K + 1, 1, N + 3, 1), (lda_al, ce - 1, N, 0), (K, 0, N, 0)]:
+            C = _run_views(_exact_device_view(A, lda, oa), _exact_device_view(B, ldb, ob), None)
+            ok, rep = check(C.numpy(), C_ref, S, dtype, K)
+            assert ok, ((M, N, K), lda, oa, ldb, ob, rep)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "i8"])
+def test_split_plans(dtype):
+    # the main tiled kernel on the first N - r columns, the thin kernel on
+    # the last r, with aligned and unaligned B and exactly sized buffers
+    for (M, N, K, ldb) in [(4096, 4097, 256, 4097), (4096, 4097, 256, 4112), (4095, 4100, 300, 4100)]:
+        info = tl.plan_for(M, N, K, DT[dtype], K, ldb, N).info()
+        assert info.n_main < N and b"thin" in info.rem_name, (M, N, K, ldb)
+        A = inputs.operand(KIND[dtype], M, K, 111 + K)
+        B = inputs.operand(KIND[dtype], K, N, 112 + K)
+        print("split", dtype, M, N, K, ldb, info.name.decode(), flush=True)
+        C = _run_views(_exact_device_view(A, K, 0), _exact_device_view(B, ldb, 0), None)
+        _assert_parity(C, A, B, dtype)
+
+
 def test_huge_leading_dimension():
     # lda = 8.5M bf16 (17 MB rows, a 4.35 GB A): the direct loader's 32-bit
     # per-lane offsets would wrap on a 256-row tile, so the plan takes the

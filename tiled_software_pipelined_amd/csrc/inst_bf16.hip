@@ -35,6 +35,12 @@ void register_bf16(void (*add)(const KernelEntry&)) {
     add(mfma_entry<T, 128, 128, 32, 2, 2, 1, LD_VGPR, LY_PLAIN, AC_NARROW, FR_REUSE, 2>(1));
     add(mfma_entry<T, 128, 128, 32, 2, 2, 1, LD_VGPR, LY_PLAIN, AC_NARROW, FR_PER_MMA, 2>(1));
     add(naive_entry<1>());
+    // unlisted: thin products (N <= 16) and split-plan remainders
+    add(thin_entry<1, 1>());
+    add(thin_entry<1, 2>());
+    add(thin_entry<1, 4>());
+    add(thin_entry<1, 8>());
+    add(thin_entry<1, 16>());
     // unlisted: the register-staged defaults reading rows that are not
     // 16-byte aligned (A only, B only, both)
     add(mfma_entry<T, 256, 256, 64, 2, 4, 2, LD_VGPR, LY_XOR, AC_WIDE, FR_REUSE, 2, 1>(1));

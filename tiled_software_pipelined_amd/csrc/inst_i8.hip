@@ -18,6 +18,12 @@ void register_i8(void (*add)(const KernelEntry&)) {
     add(mfma_entry<T, 64, 64, 128, 2, 2, 8, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 4>(2));
     add(mfma_entry<T, 128, 128, 64, 2, 2, 1, LD_VGPR, LY_PLAIN, AC_NARROW, FR_PER_MMA, 2>(2));
     add(naive_entry<2>());
+    // unlisted: thin products (N <= 16) and split-plan remainders
+    add(thin_entry<2, 1>());
+    add(thin_entry<2, 2>());
+    add(thin_entry<2, 4>());
+    add(thin_entry<2, 8>());
+    add(thin_entry<2, 16>());
     // unlisted: the register-staged defaults reading rows that are not
     // 16-byte aligned (A only, B only, both)
     add(mfma_entry<T, 256, 256, 128, 2, 4, 2, LD_VGPR, LY_XOR, AC_WIDE, FR_REUSE, 2, 1>(2));

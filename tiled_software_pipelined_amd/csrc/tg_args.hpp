@@ -23,7 +23,10 @@ struct GemmArgs {
 
 typedef void (*KernelFn)(GemmArgs);
 
-enum Family { FAM_NAIVE = 1, FAM_TILED = 2 };
+// Widest N the thin kernel (and the remainder of a split plan) takes.
+constexpr int THIN_N_MAX = 16;
+
+enum Family { FAM_NAIVE = 1, FAM_TILED = 2, FAM_THIN = 3 };
 enum Loader { LD_VGPR = 1, LD_DIRECT = 2 };
 enum Layout { LY_PLAIN = 1, LY_XOR = 2 };
 enum Access { AC_WIDE = 1, AC_NARROW = 2 };

@@ -5,6 +5,7 @@
 
 #include "tg_f32.hpp"
 #include "tg_mfma.hpp"
+#include "tg_thin.hpp"
 
 namespace tg {
 
@@ -77,6 +78,37 @@ KernelEntry naive_entry() {
     e.tail_ok = 1;
     e.fn = gemm_kernel<K, 4>;
     snprintf(e.name, sizeof e.name, "%s_naive", dtype_tag(DT));
+    return e;
+}
+
+// The thin-N kernel (N <= NB <= THIN_N_MAX, bf16 / int8): unlisted, chosen
+// by the planner for thin products and for the narrow remainder of a split
+// plan (the smallest NB that covers N).
+template <int DT, int NB>
+KernelEntry thin_entry() {
+    typedef ThinGemm<DT, NB> K;
+    KernelEntry e{};
+    e.dtype = DT;
+    e.family = FAM_THIN;
+    e.bm = K::BM;
+    e.bn = K::BN;
+    e.bk = K::KC;  // K per chunk
+    e.stages = 2;
+    e.loader = LD_VGPR;
+    e.layout = LY_PLAIN;
+    e.access = AC_WIDE;
+    e.frag = FR_REUSE;
+    e.wm = K::NT / 64;
+    e.wn = 1;
+    e.gload_bytes = 16;  // A rows in whole pieces when 16-byte aligned; B by element
+    e.threads = K::NT;
+    e.lds_bytes = K::LDS_BYTES;
+    e.loads_per_stage = K::ROWS + K::BPT;
+    e.shift_mask = 3;  // element loads wherever a row is not aligned
+    e.listed = 0;
+    e.tail_ok = 1;
+    e.fn = gemm_kernel<K, 2>;
+    snprintf(e.name, sizeof e.name, "%s_thin_n%d", dtype_tag(DT), NB);
     return e;
 }
 

@@ -23,6 +23,8 @@ struct tgemm_plan {
     const KernelEntry* fallback[4];  // by misaligned operands (bit 0 A, bit 1 B); [0] = entry
     int32_t wg_group;
     int32_t a_guard, b_guard;     // leading-dimension based (pointer alignment is checked per run)
+    int64_t n_main;               // columns the entry's grid covers (N unless split)
+    tgemm_plan* rem;              // split plans: the last N - n_main columns (thin kernel), else NULL
 };
 
 namespace {
@@ -127,6 +129,23 @@ double big_rounds(int64_t tiles) {
     return (double)full + (rest ? 0.62 + 0.38 * (double)rest / 256.0 : 0.0);
 }
 
+// Time of entry e on an M x N grid in units of one full round of the
+// 256 x 256 direct tile (the same model; register-staged rounds are 1.9
+// times as long: 212 vs 112 us at 4096^3), or a negative value where the
+// model does not apply (other tiles).
+double model_rounds(const KernelEntry& e, int64_t M, int64_t N) {
+    if (e.family != tg::FAM_TILED) return -1.0;
+    const bool staged = e.loader == tg::LD_VGPR;
+    const double round = staged ? 1.9 : 1.0;
+    const int64_t tiles = ((M + e.bm - 1) / e.bm) * ((N + e.bn - 1) / e.bn);
+    if (e.bm == 256 && e.bn == 256) return round * big_rounds(tiles);
+    if (e.bm == 128 && e.bn == 128) {
+        const double mid = staged ? 0.26 : (e.dtype == TGEMM_I8 ? 0.31 : 0.325);
+        return round * mid * (double)((tiles + 255) / 256);
+    }
+    return -1.0;
+}
+
 const KernelEntry* default_entry(int dtype, int64_t M, int64_t N, int64_t K, bool guarded) {
     tgemm_variant v{};
     v.kernel = TGEMM_KERNEL_TILED;
@@ -137,6 +156,18 @@ const KernelEntry* default_entry(int dtype, int64_t M, int64_t N, int64_t K, boo
     v.lds_layout = TGEMM_LDS_XOR;
     v.waves_m = 2;
     const bool i8 = dtype == TGEMM_I8;
+    if (N <= tg::THIN_N_MAX && guarded) {
+        // a few columns whose rows cannot go through the direct loader: the
+        // thin kernel with the fewest columns that cover N (the register-
+        // staged tiles would leave each workgroup waiting on one slice at a
+        // time: 4096 x 1 x 4096 in 11 us against 95 us).  With aligned rows
+        // the direct-loader tiles are as fast or faster (4096 x 16 x 4096:
+        // 17.7 us against 23.8).
+        const KernelEntry* best = nullptr;
+        for (const KernelEntry& e : g_reg[dtype])
+            if (e.family == tg::FAM_THIN && e.bn >= N && (!best || e.bn < best->bn)) best = &e;
+        if (best) return best;
+    }
     const int64_t short_k = i8 ? 2048 : 1024;
     // one 128 x 128 tile per unit, relative to a round of 256 x 256 tiles, at
     // 4096^3: bf16 direct 146 / 4 us vs 113 us; int8 85 / 4 vs 68 us;
@@ -252,9 +283,15 @@ const char* tgemm_version(void) { return "tgemm 0.1 (gfx950)"; }
 
 const char* tgemm_last_error(void) { return g_err.c_str(); }
 
-tgemm_plan* gemm_plan_variant(int64_t M, int64_t N, int64_t K, int32_t dtype, int64_t lda, int64_t ldb,
-                              int64_t ldc, const tgemm_variant* variant) {
-    init_registry();
+}  // extern "C"
+
+extern "C" void gemm_destroy(tgemm_plan* plan);
+
+namespace {
+
+// One plan for the whole M x N x K product (no split).
+tgemm_plan* make_plan(int64_t M, int64_t N, int64_t K, int32_t dtype, int64_t lda, int64_t ldb, int64_t ldc,
+                      const tgemm_variant* variant, bool* is_default) {
     if (dtype != TGEMM_F32 && dtype != TGEMM_BF16 && dtype != TGEMM_I8) {
         set_err("unknown dtype %d", dtype);
         return nullptr;
@@ -351,8 +388,55 @@ tgemm_plan* gemm_plan_variant(int64_t M, int64_t N, int64_t K, int32_t dtype, in
     p->wg_group = v.wg_group == 0 ? (e->family == tg::FAM_NAIVE ? -1 : 4) : v.wg_group;
     p->a_guard = ga;
     p->b_guard = gb;
+    p->n_main = N;
+    p->rem = nullptr;
+    if (is_default) *is_default = default_plan;
     g_err.clear();
     return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+// A default plan whose tile leaves a last column of at most THIN_N_MAX
+// columns may split: the tiled kernel on the first N - r columns and the
+// thin kernel on the last r, launched one after the other on the stream.
+// It does when the time model gives the main part fewer rounds than the
+// whole (4095 x 4097: 1056 tiles of 128 x 128, five on the busiest compute
+// unit, against 256 tiles of 256 x 256 in one round plus one column).
+tgemm_plan* gemm_plan_variant(int64_t M, int64_t N, int64_t K, int32_t dtype, int64_t lda, int64_t ldb,
+                              int64_t ldc, const tgemm_variant* variant) {
+    init_registry();
+    bool is_default = false;
+    tgemm_plan* p = make_plan(M, N, K, dtype, lda, ldb, ldc, variant, &is_default);
+    if (!p || !is_default || dtype == TGEMM_F32 || K == 0 || M == 0) return p;
+    const KernelEntry& e = *p->entry;
+    const int64_t r = N % e.bn;
+    if (e.family != tg::FAM_TILED || r == 0 || r > tg::THIN_N_MAX || N <= e.bn) return p;
+    const double t_full = model_rounds(e, M, N);
+    if (t_full < 0) return p;
+    tgemm_plan* main = make_plan(M, N - r, K, dtype, lda, ldb, ldc, nullptr, nullptr);
+    if (!main) {
+        g_err.clear();
+        return p;
+    }
+    const double t_main = model_rounds(*main->entry, M, N - r);
+    if (t_main < 0 || t_main >= t_full) {
+        gemm_destroy(main);
+        return p;
+    }
+    tgemm_plan* rem = make_plan(M, r, K, dtype, lda, ldb, ldc, nullptr, nullptr);
+    if (!rem) {
+        gemm_destroy(main);
+        g_err.clear();
+        return p;
+    }
+    gemm_destroy(p);
+    main->N = N;  // the user's shape; the grid covers n_main
+    main->rem = rem;
+    g_err.clear();
+    return main;
 }
 
 tgemm_plan* gemm_plan(int64_t M, int64_t N, int64_t K, int32_t dtype, int64_t lda, int64_t ldb,
@@ -360,7 +444,11 @@ tgemm_plan* gemm_plan(int64_t M, int64_t N, int64_t K, int32_t dtype, int64_t ld
     return gemm_plan_variant(M, N, K, dtype, lda, ldb, ldc, nullptr);
 }
 
-void gemm_destroy(tgemm_plan* plan) { delete plan; }
+void gemm_destroy(tgemm_plan* plan) {
+    if (!plan) return;
+    gemm_destroy(plan->rem);
+    delete plan;
+}
 
 int gemm_run(const tgemm_plan* p, const void* A, const void* B, void* C, void* stream) {
     if (!p) {
@@ -402,7 +490,7 @@ int gemm_run(const tgemm_plan* p, const void* A, const void* B, void* C, void* s
     if (!accepts(*e, ga, gb)) {
         e = p->fallback[ga | (gb << 1)];
         int32_t fa = 0, fbg = 0;
-        ld_guards(*e, p->N, p->lda, p->ldb, &fa, &fbg);
+        ld_guards(*e, p->n_main, p->lda, p->ldb, &fa, &fbg);
         const int fbytes = access_bytes(*e);
         ga = fa || (fbytes && (uintptr_t)A % fbytes);
         gb = fbg || (fbytes && (uintptr_t)B % fbytes);
@@ -416,10 +504,10 @@ int gemm_run(const tgemm_plan* p, const void* A, const void* B, void* C, void* s
     g.B = B;
     g.C = C;
     g.M = (int32_t)p->M;
-    g.N = (int32_t)p->N;
+    g.N = (int32_t)p->n_main;
     g.K = (int32_t)p->K;
     g.tiles_m = (int32_t)((p->M + e->bm - 1) / e->bm);
-    g.tiles_n = (int32_t)((p->N + e->bn - 1) / e->bn);
+    g.tiles_n = (int32_t)((p->n_main + e->bn - 1) / e->bn);
     g.lda = p->lda;
     g.ldb = p->ldb;
     g.ldc = p->ldc;
@@ -434,6 +522,9 @@ int gemm_run(const tgemm_plan* p, const void* A, const void* B, void* C, void* s
         set_err("launch of %s failed: %s", e->name, hipGetErrorString(err));
         return TGEMM_E_HIP;
     }
+    if (p->rem)  // the last N - n_main columns, after the main part on the same stream
+        return gemm_run(p->rem, A, static_cast<const char*>(B) + p->n_main * esz,
+                        static_cast<char*>(C) + p->n_main * 4, stream);
     return TGEMM_OK;
 }
 
@@ -452,7 +543,9 @@ int gemm_plan_get_info(const tgemm_plan* p, tgemm_plan_info* info) {
     info->ldc = p->ldc;
     info->dtype = p->dtype;
     entry_to_variant(e, p->wg_group, &info->variant);
-    info->grid = (int32_t)(((p->M + e.bm - 1) / e.bm) * ((p->N + e.bn - 1) / e.bn));
+    info->grid = (int32_t)(((p->M + e.bm - 1) / e.bm) * ((p->n_main + e.bn - 1) / e.bn));
+    info->n_main = p->n_main;
+    if (p->rem) snprintf(info->rem_name, sizeof info->rem_name, "%s", p->rem->entry->name);
     info->threads = e.threads;
     info->lds_bytes = e.lds_bytes;
     info->loads_per_stage = e.loads_per_stage;
