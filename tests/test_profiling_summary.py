@@ -1,0 +1,52 @@
+"""CPU: the rocprofv3 summary arithmetic (per-launch sums over a plan's
+kernels, counter means per dispatch, HBM bytes scaled by the copy kernel's
+reading) on synthetic CSV files in the layout rocprofv3 writes."""
+import csv
+import os
+import types
+
+from tiled_software_pipelined_amd import profiling
+
+
+def _write(path, header, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+def test_split_plan_sums_its_kernels(tmp_path):
+    out = tmp_path / "prof"
+    main = "void tg::gemm_kernel<tg::MfmaGemm<...>, 2>(tg::GemmArgs)"
+    thin = "void tg::gemm_kernel<tg::ThinGemm<1, 1>, 2>(tg::GemmArgs)"
+    _write(str(out / "trace" / "x" / "trace_kernel_stats.csv"),
+           ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"],
+           [[main, 25, 25 * 200000, 200000, 90, 190000, 230000, 1], [thin, 25, 25 * 15000, 15000, 7, 14000, 17000, 1],
+            ["elementwise_copy", 3, 300, 100, 3, 90, 110, 1]])
+    # FETCH_SIZE (group 2) and WRITE_SIZE (group 3): two dispatches of each
+    # GEMM kernel, one of the copy
+    rows = []
+    for name, vals in ((main, (1000.0, 1200.0)), (thin, (100.0, 100.0))):
+        for v in vals:
+            rows.append([name, "FETCH_SIZE", v])
+    rows.append(["elementwise_copy_kernel", "FETCH_SIZE", 2.0 ** 28 / 2048.0])  # 2 KiB per unit
+    _write(str(out / "pmc2" / "x" / "pmc_counter_collection.csv"), ["Kernel_Name", "Counter_Name", "Counter_Value"],
+           rows)
+    rows = [[main, "WRITE_SIZE", 500.0], [main, "WRITE_SIZE", 500.0], [thin, "WRITE_SIZE", 4.0],
+            ["elementwise_copy_kernel", "WRITE_SIZE", 2.0 ** 28 / 1024.0]]  # 1 KiB per unit
+    _write(str(out / "pmc3" / "x" / "pmc_counter_collection.csv"), ["Kernel_Name", "Counter_Name", "Counter_Value"],
+           rows)
+    args = types.SimpleNamespace(out=str(out), workload="bf16_4096", variant="", steps=20, warmup=5)
+    res = profiling.summarize(args, {})
+    assert [k["name"] for k in res["kernels"]] == [main, thin]
+    assert res["avg_ns"] == 215000 and res["min_ns"] == 204000 and res["calls"] == 25
+    # counters: each kernel's mean per dispatch, added over the plan's kernels
+    assert res["counters"]["FETCH_SIZE"] == 1100.0 + 100.0
+    assert res["counters"]["WRITE_SIZE"] == 500.0 + 4.0
+    # bytes per counter unit = the calibration copy's size / its reading
+    calib = profiling.CALIB_MIB << 20
+    fetch_scale = calib / res["copy"]["FETCH_SIZE"]
+    write_scale = calib / res["copy"]["WRITE_SIZE"]
+    assert fetch_scale == calib / (2.0 ** 28 / 2048.0)
+    assert write_scale == calib / (2.0 ** 28 / 1024.0)

@@ -101,17 +101,26 @@ def collect(args):
 
 
 def summarize(args, cmds):
+    """Per-launch figures of the GEMM.  A plan may launch more than one
+    kernel per GEMM (a split plan: the tiled kernel, then the thin kernel on
+    the last columns); durations and counters are then the sum over its
+    kernels of each kernel's mean per dispatch, and `kernels` lists them."""
     out = os.path.abspath(args.out)
-    res = {"counters": {}, "copy": {}}
+    res = {"counters": {}, "copy": {}, "kernels": []}
     stats = _find(os.path.join(out, "trace"), "*kernel_stats.csv")
     if stats:
-        for row in _read_csv(stats):
-            if _is_gemm(row["Name"]):
-                res["kernel"] = row["Name"]
-                res["calls"] = int(row["Calls"])
-                res["avg_ns"] = float(row["AverageNs"])
-                res["min_ns"] = float(row["MinNs"])
-                res["max_ns"] = float(row["MaxNs"])
+        rows = [r for r in _read_csv(stats) if _is_gemm(r["Name"])]
+        # the most-called kernel first (all kernels of a plan run once per GEMM)
+        rows.sort(key=lambda r: (-int(r["Calls"]), -float(r["TotalDurationNs"]) if "TotalDurationNs" in r else 0))
+        for r in rows:
+            res["kernels"].append({"name": r["Name"], "calls": int(r["Calls"]), "avg_ns": float(r["AverageNs"]),
+                                   "min_ns": float(r["MinNs"]), "max_ns": float(r["MaxNs"])})
+        if rows:
+            res["kernel"] = rows[0]["Name"]
+            res["calls"] = int(rows[0]["Calls"])
+            res["avg_ns"] = sum(k["avg_ns"] for k in res["kernels"])
+            res["min_ns"] = sum(k["min_ns"] for k in res["kernels"])
+            res["max_ns"] = sum(k["max_ns"] for k in res["kernels"])
     for i in range(len(GROUPS)):
         f = _find(os.path.join(out, "pmc%d" % i), "*counter_collection.csv")
         if not f:
@@ -122,14 +131,16 @@ def summarize(args, cmds):
             cn = row["Counter_Name"]
             val = float(row["Counter_Value"])
             if _is_gemm(name):
-                gsum[cn] = gsum.get(cn, 0.0) + val
-                gcnt[cn] = gcnt.get(cn, 0) + 1
+                key = (name, cn)
+                gsum[key] = gsum.get(key, 0.0) + val
+                gcnt[key] = gcnt.get(key, 0) + 1
             elif _is_copy(name):
                 csum[cn] = csum.get(cn, 0.0) + val
                 ccnt[cn] = ccnt.get(cn, 0) + 1
-        # rows are per dispatch (and per counter); average over dispatches
-        for cn in gsum:
-            res["counters"][cn] = gsum[cn] / gcnt[cn]
+        # rows are per dispatch (and per counter): average over each kernel's
+        # dispatches, then add the plan's kernels
+        for (name, cn) in gsum:
+            res["counters"][cn] = res["counters"].get(cn, 0.0) + gsum[(name, cn)] / gcnt[(name, cn)]
         for cn in csum:
             res["copy"][cn] = csum[cn] / ccnt[cn]
     return res
@@ -179,9 +190,11 @@ def render(args, cmds, res):
         t = res["avg_ns"] * 1e-9
         lines.append("| quantity | value |")
         lines.append("|---|---|")
-        lines.append("| kernel | `%s` |" % res["kernel"])
+        for k in res["kernels"]:
+            lines.append("| kernel | `%s`: %d dispatches, mean %.2f us |" % (k["name"], k["calls"],
+                                                                        k["avg_ns"] / 1e3))
         lines.append("| dispatches traced | %d |" % res["calls"])
-        lines.append("| mean / min / max duration | %.2f / %.2f / %.2f us |" % (
+        lines.append("| mean / min / max duration per GEMM | %.2f / %.2f / %.2f us |" % (
             res["avg_ns"] / 1e3, res["min_ns"] / 1e3, res["max_ns"] / 1e3))
         lines.append("| achieved (2MNK / mean) | %.1f TFLOP/s |" % (w.flops / t / 1e12))
         if "SQ_VALU_MFMA_BUSY_CYCLES" in c and "SQ_BUSY_CU_CYCLES" in c and c["SQ_BUSY_CU_CYCLES"]:
