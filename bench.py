@@ -189,7 +189,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # the shader clock takes tens of milliseconds of load to ramp up from idle
+    # (the first 50 launches of bf16 4096^3 average 134 us, later ones 115)
+    ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--workload", default="bf16_4096")
     ap.add_argument("--variant", default="")
     ap.add_argument("--ladder", action="store_true")

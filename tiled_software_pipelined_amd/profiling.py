@@ -231,8 +231,10 @@ def main():
     ap.add_argument("--workload", default="bf16_4096")
     ap.add_argument("--variant", default="")
     ap.add_argument("--out", default="gpurun_out/prof")
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the trace pass runs the same timed region as the default bench run
+    # (its kernel means then describe the same, clock-ramped, steady state)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--summary", default="")
     ap.add_argument("--summarize-only", action="store_true")
     args = ap.parse_args()
