@@ -16,6 +16,8 @@ Extra modes (not used by the default run):
                  and the default plan per shape, timed by HIP-graph replay
                  (eager per-launch times beside them)
     --lds-probe  LDS read throughput of ds_read_b32 / b64 / b128 / b64_tr_b16
+    --mfma-probe matrix-core rate and clock for bf16 / int8 operand bits
+                 (the workloads' random operands, all ones, all zeros)
     --gpus N     N > 1 exits: this path runs on one GPU
 """
 from __future__ import annotations
@@ -185,6 +187,48 @@ def lds_probe(torch, lib, workgroups=2048, reps=2048, rounds=8, launches=3):
                           "bytes_per_clk_per_cu_at_2p4GHz": round(tbs * 1e12 / 256 / 2.4e9, 1)}), flush=True)
 
 
+def mfma_ceiling(torch, lib, dtype, source, reps=None, workgroups=256, launches=3):
+    """The matrix-core rate probe (one wave per SIMD, 16 independent
+    accumulators, no memory traffic) on operand bits drawn as `source`:
+    "random" = the GEMM workloads' distribution (bf16 N(0,1), int8 uniform),
+    "ones", "zeros".  Returns (TFLOP/s or TOP/s, mean clock in GHz from the
+    shader-clock / real-time tick ratio, median ms)."""
+    from tiled_software_pipelined_amd import inputs
+    kind = lib.RATE_PROBE_KINDS.index(dtype)
+    nbytes = workgroups * lib.RATE_PROBE_THREADS * 8 * 16
+    if dtype == "bf16":
+        if source == "random":
+            ops = inputs.operand("bf16_normal", nbytes // 2 // 2048, 2048, 77)
+        else:
+            ops = torch.full((nbytes // 2,), 1.0 if source == "ones" else 0.0, dtype=torch.bfloat16)
+    else:
+        if source == "random":
+            ops = inputs.operand("i8_uniform", nbytes // 4096, 4096, 78)
+        else:
+            ops = torch.full((nbytes,), 1 if source == "ones" else 0, dtype=torch.int8)
+    ops = ops.contiguous().view(-1).to("cuda:0")
+    out = torch.empty(workgroups * lib.RATE_PROBE_THREADS, dtype=torch.int32, device="cuda:0")
+    clocks = torch.empty(2 * workgroups, dtype=torch.int64, device="cuda:0")
+    # about 20 ms per launch at the nominal clock (both instructions take 32
+    # cycles per wave)
+    reps = reps or int(20e-3 * 2.4e9 / (16 * 32))
+    lib.mfma_rate_probe(kind, reps // 10, ops, out, clocks)
+    torch.cuda.synchronize()
+    ms, ghz = [], []
+    for _ in range(launches):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        lib.mfma_rate_probe(kind, reps, ops, out, clocks)
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+        c = clocks.view(-1, 2).double().cpu()
+        ghz.append(float((c[:, 0] / c[:, 1]).mean()) * 0.1)
+    med = statistics.median(ms)
+    ops_total = float(lib.RATE_PROBE_OPS_PER_INST[dtype]) * 16 * reps * 4 * workgroups
+    return ops_total / (med * 1e-3) / 1e12, statistics.median(ghz), med
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -199,6 +243,9 @@ def main():
     ap.add_argument("--lds-probe", action="store_true",
                     help="time the LDS read-path probe: the same bytes through ds_read_b32 / b64 / "
                          "b128 / b64_tr_b16 (one JSON line per instruction form)")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="matrix-core rate and clock for bf16 / int8 with random, all-ones and all-zero "
+                         "operand bits (one JSON line each)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of MIB MiB (a reference for the HBM "
@@ -214,6 +261,15 @@ def main():
 
     if args.lds_probe:
         lds_probe(torch, lib)
+        return
+    if args.mfma_probe:
+        for dt in ("bf16", "i8"):
+            for src in ("random", "ones", "zeros"):
+                rate, ghz, ms = mfma_ceiling(torch, lib, dt, src)
+                print(json.dumps({"mode": "mfma_probe", "dtype": dt, "operands": src,
+                                  "rate": round(rate, 1), "unit": "TFLOP/s" if dt == "bf16" else "TOP/s",
+                                  "frac_peak": round(rate / PEAK_TFLOPS[dt], 4), "clock_ghz": round(ghz, 3),
+                                  "median_ms": round(ms, 3)}), flush=True)
         return
 
     w = inputs.workloads()[args.workload]
@@ -343,6 +399,14 @@ def main():
                                "kernel_ms_min: per-launch events in a pass after it"},
         "cpu_baseline": None,
     }
+    if w.dtype in ("bf16", "i8"):
+        # the rate the matrix cores sustain on this machine for the workload's
+        # operand distribution with no memory traffic at all (the power
+        # budget lowers the clock below nominal for random operands)
+        rate, ghz, _ = mfma_ceiling(torch, lib, w.dtype, "random")
+        rec["roofline"]["measured_ceiling"] = {
+            "value": round(rate, 1), "clock_ghz": round(ghz, 3), "frac": round(achieved / rate, 4),
+            "source": "matrix-core rate probe, random %s operands, no memory traffic" % w.dtype}
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(w, A_cpu, B_cpu)
     print(json.dumps(rec), flush=True)

@@ -212,6 +212,36 @@ const char* tgemm_version(void);
 int tgemm_lds_read_probe(int32_t kind, int32_t pattern, int32_t reps, int32_t workgroups, uint32_t* out,
                          void* stream);
 
+/* Matrix-core rate probe (a measurement harness, not part of the GEMM): the
+ * rate at which the chip sustains the matrix-core instruction of a GEMM type
+ * for given operand bits, with no memory traffic.  The dense peak of the
+ * datasheet assumes the nominal clock; the clock the power budget allows
+ * depends on the operands (the "4.1 CUDA GEMM算子性能优化" page, section 2:
+ * the roofline's compute ceiling is the one to measure against).
+ *   kind 0: v_mfma_f32_32x32x16_bf16 (32768 flops per wave instruction)
+ *   kind 1: v_mfma_i32_32x32x32_i8   (65536 ops per wave instruction)
+ * Launches `workgroups` workgroups of 256 threads (4 waves, one per SIMD
+ * while workgroups <= 256 compute units) on `stream`.  Thread t (global
+ * index workgroup * 256 + thread) loads operands[8t .. 8t+3] (16 bytes each)
+ * as A registers a[0..3] and operands[8t+4 .. 8t+7] as B registers b[0..3],
+ * then runs `reps` iterations of 16 independent accumulators,
+ * acc[i] += mma(a[i % 4], b[(i / 4) % 4]), i = 0..15 (16 * reps matrix
+ * instructions per wave).  Operand layout of one instruction: lane l holds
+ * row (A) / column (B) l % 32 and K elements 8 (l / 32) .. +7 (bf16) or
+ * 16 (l / 32) .. +15 (int8); accumulator register r of lane l is row
+ * 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.
+ * out[t] = the sum of the thread's 256 accumulator registers (bf16: fp32
+ * bits of a sum taken in increasing i, then r; int8: the int32 sum mod 2^32).
+ * clocks[2 w], clocks[2 w + 1]: shader-clock ticks (s_memtime) and 100 MHz
+ * real-time ticks (s_memrealtime) that wave 0 of workgroup w spent in the
+ * loop.  operands (workgroups * 256 * 8 16-byte entries), out (workgroups *
+ * 256 uint32) and clocks (2 * workgroups uint64) are device memory owned by
+ * the caller.  Returns TGEMM_OK, TGEMM_E_ARG (kind outside 0..1, reps < 0,
+ * workgroups < 1), TGEMM_E_NULL, TGEMM_E_ALIGN (operands not 16-byte, out
+ * not 4-byte or clocks not 8-byte aligned) or TGEMM_E_HIP (launch failed). */
+int tgemm_mfma_rate_probe(int32_t kind, int32_t reps, int32_t workgroups, const void* operands, uint32_t* out,
+                          uint64_t* clocks, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -16,6 +16,8 @@ void register_bf16(void (*add)(const KernelEntry&)) {
     add(mfma_entry<T, 256, 128, 32, 2, 2, 2, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2>(1));
     add(mfma_entry<T, 128, 256, 32, 2, 2, 2, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2>(1));
     add(mfma_entry<T, 256, 256, 32, 2, 4, 2, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2>(1));
+    add(mfma_entry<T, 256, 256, 32, 2, 4, 3, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2>(1));
+    add(mfma_entry<T, 256, 256, 32, 2, 4, 4, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2>(1));
     add(mfma_entry<T, 256, 256, 64, 2, 2, 2, LD_VGPR, LY_XOR, AC_WIDE, FR_REUSE, 1>(1));
     add(mfma_entry<T, 256, 256, 64, 2, 4, 2, LD_VGPR, LY_XOR, AC_WIDE, FR_REUSE, 2>(1));
     // small problems: more workgroups per CU count

@@ -23,6 +23,8 @@
 // workgroup does not see the permutation).
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "tg_device.hpp"
 #include "tgemm.h"
 
@@ -126,6 +128,73 @@ __global__ __launch_bounds__(PROBE_THREADS) void lds_read_probe(uint32_t* out, i
     out[(int64_t)blockIdx.x * PROBE_THREADS + threadIdx.x] = acc;
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core rate probe: the matrix-core instruction of each GEMM type
+// issued back to back with no memory traffic, to measure the rate the chip
+// sustains for given operand bits (the dense peak assumes the nominal clock;
+// the clock the power budget allows depends on what the operands toggle).
+//
+// Each of the 4 waves of a workgroup loads 4 A and 4 B operand registers
+// (16 bytes each) per lane, then runs `reps` iterations of 16 independent
+// accumulators, acc[i] += mma(a[i % 4], b[(i / 4) % 4]).  Wave 0 records the
+// shader-clock ticks (s_memtime) and the 100 MHz real-time ticks
+// (s_memrealtime) around the loop; their ratio is the clock.
+constexpr int RATE_THREADS = 256;
+constexpr int RATE_ACC = 16;
+
+template <int KIND>
+__global__ __launch_bounds__(RATE_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mfma_rate_probe(const i32x4* operands, uint32_t* out, uint64_t* clocks, int reps) {
+    const int64_t t = (int64_t)blockIdx.x * RATE_THREADS + threadIdx.x;
+    i32x4 a[4], b[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        a[q] = operands[t * 8 + q];
+        b[q] = operands[t * 8 + 4 + q];
+    }
+    typedef typename std::conditional<KIND == 0, f32x16, i32x16>::type Acc;
+    Acc acc[RATE_ACC];
+#pragma unroll
+    for (int i = 0; i < RATE_ACC; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] = 0;
+    const uint64_t c0 = __builtin_amdgcn_s_memtime();
+    const uint64_t w0 = __builtin_amdgcn_s_memrealtime();
+    for (int it = 0; it < reps; ++it) {
+#pragma unroll
+        for (int i = 0; i < RATE_ACC; ++i) {
+            if constexpr (KIND == 0)
+                acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[i & 3]),
+                                                                 __builtin_bit_cast(bf16x8, b[(i >> 2) & 3]),
+                                                                 acc[i], 0, 0, 0);
+            else
+                acc[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i & 3], b[(i >> 2) & 3], acc[i], 0, 0, 0);
+        }
+    }
+    const uint64_t c1 = __builtin_amdgcn_s_memtime();
+    const uint64_t w1 = __builtin_amdgcn_s_memrealtime();
+    // fold every accumulator register so that no matrix instruction is dead
+    if constexpr (KIND == 0) {
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < RATE_ACC; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s += acc[i][r];
+        out[t] = __builtin_bit_cast(uint32_t, s);
+    } else {
+        uint32_t s = 0;
+#pragma unroll
+        for (int i = 0; i < RATE_ACC; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s += (uint32_t)acc[i][r];
+        out[t] = s;
+    }
+    if (threadIdx.x == 0) {
+        clocks[2 * blockIdx.x] = c1 - c0;
+        clocks[2 * blockIdx.x + 1] = w1 - w0;
+    }
+}
+
 }  // namespace tg
 
 extern "C" int tgemm_lds_read_probe(int32_t kind, int32_t pattern, int32_t reps, int32_t workgroups, uint32_t* out,
@@ -139,5 +208,19 @@ extern "C" int tgemm_lds_read_probe(int32_t kind, int32_t pattern, int32_t reps,
     void* args[] = {&out, &reps};
     const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(fns[pattern][kind]), dim3((unsigned)workgroups),
                                            dim3(tg::PROBE_THREADS), args, 0, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? TGEMM_OK : TGEMM_E_HIP;
+}
+
+extern "C" int tgemm_mfma_rate_probe(int32_t kind, int32_t reps, int32_t workgroups, const void* operands,
+                                     uint32_t* out, uint64_t* clocks, void* stream) {
+    if (kind < 0 || kind > 1 || reps < 0 || workgroups < 1) return TGEMM_E_ARG;
+    if (!operands || !out || !clocks) return TGEMM_E_NULL;
+    if ((uintptr_t)operands % 16 || (uintptr_t)out % 4 || (uintptr_t)clocks % 8) return TGEMM_E_ALIGN;
+    static void (*const fns[2])(const tg::i32x4*, uint32_t*, uint64_t*, int) = {tg::mfma_rate_probe<0>,
+                                                                                tg::mfma_rate_probe<1>};
+    const tg::i32x4* ops = static_cast<const tg::i32x4*>(operands);
+    void* args[] = {&ops, &out, &clocks, &reps};
+    const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(fns[kind]), dim3((unsigned)workgroups),
+                                           dim3(tg::RATE_THREADS), args, 0, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? TGEMM_OK : TGEMM_E_HIP;
 }

@@ -57,7 +57,7 @@ class PlanInfo(ctypes.Structure):
 
 EXPORTS = ("gemm_plan", "gemm_plan_variant", "gemm_run", "gemm_destroy", "tgemm_last_error",
            "gemm_plan_get_info", "gemm_variant_count", "gemm_variant_get", "tgemm_version",
-           "tgemm_lds_read_probe")
+           "tgemm_lds_read_probe", "tgemm_mfma_rate_probe")
 
 
 def _load():
@@ -90,6 +90,8 @@ def _load():
     lib.tgemm_version.restype = ctypes.c_char_p
     lib.tgemm_lds_read_probe.argtypes = [i32, i32, i32, i32, vp, vp]
     lib.tgemm_lds_read_probe.restype = ctypes.c_int
+    lib.tgemm_mfma_rate_probe.argtypes = [i32, i32, i32, vp, vp, vp, vp]
+    lib.tgemm_mfma_rate_probe.restype = ctypes.c_int
     return lib
 
 
@@ -129,6 +131,36 @@ def lds_read_probe(kind: int, pattern: int, reps: int, out):
         raise TgemmError(rc, "tgemm_lds_read_probe(kind=%d, pattern=%d, reps=%d, workgroups=%d)" % (
             kind, pattern, reps, wgs))
     return out
+
+
+RATE_PROBE_KINDS = ("bf16", "i8")
+RATE_PROBE_THREADS = 256
+RATE_PROBE_OPS_PER_INST = {"bf16": 2 * 32 * 32 * 16, "i8": 2 * 32 * 32 * 32}
+
+
+def mfma_rate_probe(kind: int, reps: int, operands, out, clocks):
+    """Launch the matrix-core rate probe on the current stream.
+
+    operands: contiguous GPU tensor of workgroups * 256 * 8 16-byte entries
+    (any dtype; its bytes are the operand registers), out: int32 GPU tensor
+    of workgroups * 256 entries, clocks: int64 GPU tensor of 2 * workgroups
+    entries (shader-clock and real-time ticks per workgroup)."""
+    import torch
+    if not out.is_cuda or out.dtype != torch.int32 or out.numel() % RATE_PROBE_THREADS or not out.is_contiguous():
+        raise ValueError("out must be a contiguous int32 GPU tensor of 256 * workgroups entries")
+    wgs = out.numel() // RATE_PROBE_THREADS
+    if (not operands.is_cuda or not operands.is_contiguous()
+            or operands.numel() * operands.element_size() != wgs * RATE_PROBE_THREADS * 8 * 16):
+        raise ValueError("operands must be a contiguous GPU tensor of workgroups * 256 * 8 * 16 bytes")
+    if not clocks.is_cuda or clocks.dtype != torch.int64 or clocks.numel() != 2 * wgs or not clocks.is_contiguous():
+        raise ValueError("clocks must be a contiguous int64 GPU tensor of 2 * workgroups entries")
+    stream = torch.cuda.current_stream(out.device).cuda_stream
+    with torch.cuda.device(out.device):
+        rc = _lib.tgemm_mfma_rate_probe(kind, reps, wgs, operands.data_ptr(), out.data_ptr(), clocks.data_ptr(),
+                                        stream)
+    if rc != OK:
+        raise TgemmError(rc, "tgemm_mfma_rate_probe(kind=%d, reps=%d, workgroups=%d)" % (kind, reps, wgs))
+    return out, clocks
 
 
 def variants(dtype: int):
