@@ -18,6 +18,9 @@ Extra modes (not used by the default run):
     --lds-probe  LDS read throughput of ds_read_b32 / b64 / b128 / b64_tr_b16
     --mfma-probe matrix-core rate and clock for bf16 / int8 operand bits
                  (the workloads' random operands, all ones, all zeros)
+    --soak S     run the workload's GEMM, then the matrix-core probe on random
+                 operands of its type, back to back for S seconds each while
+                 sampling socket power and shader clocks (amd-smi)
     --gpus N     N > 1 exits: this path runs on one GPU
 """
 from __future__ import annotations
@@ -229,6 +232,90 @@ def mfma_ceiling(torch, lib, dtype, source, reps=None, workgroups=256, launches=
     return ops_total / (med * 1e-3) / 1e12, statistics.median(ghz), med
 
 
+class PowerSampler:
+    """Samples socket power (W) and the per-XCD shader clocks (MHz) with
+    amd-smi in a child process every `period` seconds while active."""
+
+    def __init__(self, period=0.25):
+        import shutil
+        import threading
+        self.exe = shutil.which("amd-smi")
+        self.period = period
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._loop, daemon=True)
+
+    def _one(self):
+        import subprocess
+        r = subprocess.run([self.exe, "metric", "-p", "-c", "--json"], capture_output=True, text=True, timeout=10)
+        d = json.loads(r.stdout)
+        g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+        watts = float(g["power"]["socket_power"]["value"])
+        clocks = [float(v["clk"]["value"]) for k, v in sorted(g["clock"].items()) if k.startswith("gfx_")]
+        return watts, clocks
+
+    def _loop(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._one())
+            except Exception:  # noqa: BLE001 - a missing or failing tool leaves no sample
+                pass
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.exe:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self.exe:
+            self._thread.join()
+
+    def summary(self, skip=2):
+        s = self.samples[skip:] if len(self.samples) > skip + 2 else self.samples
+        if not s:
+            return None
+        watts = statistics.mean(w for w, _ in s)
+        per_xcd = [statistics.mean(c[i] for _, c in s) for i in range(len(s[0][1]))]
+        return {"socket_w": round(watts, 1), "gfx_mhz_per_xcd": [round(c) for c in per_xcd],
+                "gfx_mhz_mean": round(statistics.mean(per_xcd)), "samples": len(s)}
+
+
+def soak(torch, lib, w, A, B, C, seconds):
+    """The default plan back to back for `seconds`, then the matrix-core
+    probe on random operands of the workload's type for as long, each with
+    power and clock samples: energy per operation of the GEMM against the
+    same chip's energy per operation of the matrix cores alone."""
+    lines = []
+    with PowerSampler() as ps:
+        n = 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(200):
+                lib.gemm(A, B, out=C)
+            torch.cuda.synchronize()
+            n += 200
+        dt = time.perf_counter() - t0
+    rate = w.flops * n / dt / 1e12
+    lines.append({"mode": "soak", "what": "gemm " + w.name, "launches": n, "seconds": round(dt, 2),
+                  "rate": round(rate, 1), "power": ps.summary()})
+    if w.dtype in ("bf16", "i8"):
+        with PowerSampler() as ps:
+            t0 = time.perf_counter()
+            reps = 0
+            while time.perf_counter() - t0 < seconds:
+                r, ghz, ms = mfma_ceiling(torch, lib, w.dtype, "random", launches=3)
+                reps += 1
+        lines.append({"mode": "soak", "what": "matrix-core probe, random %s operands" % w.dtype,
+                      "rate": round(r, 1), "clock_ghz": round(ghz, 3), "power": ps.summary()})
+    for rec in lines:
+        p = rec.get("power")
+        if p:
+            rec["pj_per_op"] = round(p["socket_w"] / (rec["rate"] * 1e12) * 1e12, 3)
+        print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -246,6 +333,9 @@ def main():
     ap.add_argument("--mfma-probe", action="store_true",
                     help="matrix-core rate and clock for bf16 / int8 with random, all-ones and all-zero "
                          "operand bits (one JSON line each)")
+    ap.add_argument("--soak", type=float, default=0.0, metavar="S",
+                    help="GEMM and matrix-core probe back to back for S seconds each, with socket "
+                         "power and shader clocks sampled by amd-smi")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of MIB MiB (a reference for the HBM "
@@ -345,6 +435,10 @@ def main():
                                   "frac_peak": sw.flops / ms / 1e9 / PEAK_TFLOPS["bf16"],
                                   "frac_roofline": ideal_ms / ms}), flush=True)
             del a, b, c
+
+    if args.soak:
+        soak(torch, lib, w, A, B, C, args.soak)
+        return
 
     if args.calib_copy:
         nbytes = args.calib_copy << 20
