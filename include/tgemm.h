@@ -156,6 +156,34 @@ void gemm_destroy(tgemm_plan* plan);
 /* Last error message of this thread ("" if none). */
 const char* tgemm_last_error(void);
 
+/* Run with a caller-owned device workspace.  Operands whose rows are not
+ * 16-byte aligned (a leading dimension that is not a whole number of
+ * 16-byte chunks, or a pointer that is not 16-byte aligned) are first copied
+ * on `stream` into the workspace with 16-byte aligned rows (leading
+ * dimension rounded up to 8 bf16, 16 int8 or 4 fp32 elements; each copy
+ * starts on a 256-byte boundary; the padding columns are written as zero),
+ * then the plan's product runs on the copies with the direct global->LDS
+ * loader.  Padding the misaligned operand is the pages' remedy besides a
+ * guarded narrow loader (the "流水化 GPU 内核" skill's pitfall list; the SM80
+ * ablation plan, section 1.4, note 2).  The result meets the same accuracy
+ * as gemm_run's; it is the same bit for bit wherever both paths use
+ * matrix-core or fp32 tiles (every such kernel accumulates each output in
+ * increasing k), and may differ in the last bits on columns that one path
+ * gives to the thin kernel.
+ *
+ * gemm_workspace_bytes returns the bytes this needs for these pointers: 0
+ * when no operand is misaligned, for K, M or N = 0, and for plans that carry
+ * no repack (explicit variants, products with N <= 16, which read their
+ * operands about once anyway).  gemm_run_ws behaves exactly like gemm_run
+ * when that is 0, when `workspace` is NULL or when `workspace_bytes` is
+ * smaller.  The workspace must be 256-byte aligned (TGEMM_E_ALIGN otherwise),
+ * must not overlap A, B or C, and must stay allocated until the stream has
+ * run the product; its contents are overwritten, so runs that share one
+ * workspace must be ordered on one stream.  Returns as gemm_run. */
+int64_t gemm_workspace_bytes(const tgemm_plan* plan, const void* A, const void* B);
+int gemm_run_ws(const tgemm_plan* plan, const void* A, const void* B, void* C, void* workspace,
+                int64_t workspace_bytes, void* stream);
+
 /* What a plan will launch. */
 typedef struct tgemm_plan_info {
     int64_t M, N, K, lda, ldb, ldc;

@@ -220,3 +220,38 @@ def test_guard_follows_global_load_width_for_every_variant():
             info = tl.Plan(129, 257, 40, dtype, variant=v).info()
             if info.variant.kernel == tl.KERNEL_TILED:
                 assert info.b_guarded == 1, info.name.decode()
+
+
+def _ru(x, m):
+    return (x + m - 1) // m * m
+
+
+@pytest.mark.parametrize("dtype,esz", [(tl.F32, 4), (tl.BF16, 2), (tl.I8, 1)])
+def test_workspace_bytes(dtype, esz):
+    # host-only: the addresses are numbers, nothing is dereferenced
+    al = 1 << 20
+    M, N, K = 4095, 4097, 4104
+    per = 16 // esz
+    p = tl.Plan(M, N, K, dtype, K, N, N)
+    bytes_a = _ru(M * _ru(K, per) * esz, 256)
+    bytes_b = _ru(K * _ru(N, per) * esz, 256)
+    a_al = (K * esz) % 16 == 0
+    # leading dimensions: B rows (N = 4097) are never aligned; A rows at K = 4104 are for bf16 / fp32
+    assert p.workspace_bytes(al, al) == (0 if a_al else bytes_a) + bytes_b
+    # a pointer that is not 16-byte aligned adds its operand (its rows keep lda = K when aligned)
+    assert p.workspace_bytes(al + esz, al) == (_ru(M * K * esz, 256) if a_al else bytes_a) + bytes_b
+    q = tl.Plan(1024, 1024, 512, dtype)
+    assert q.workspace_bytes(al, al) == 0
+    assert q.workspace_bytes(al, al + esz) == _ru(512 * 1024 * esz, 256)
+    # no repack for explicit variants, thin products, or empty work
+    v = tl.variants(dtype)[0]
+    assert tl.Plan(M, N, K, dtype, variant=v).workspace_bytes(al, al) == 0
+    assert tl.Plan(4096, 9, 4096, dtype, 4096, 9, 9).workspace_bytes(al, al) == 0
+    assert tl.Plan(64, 64, 0, dtype, 1, 64, 64).workspace_bytes(al + 1, al + 1) == 0
+    assert tl.Plan(0, 64, 64, dtype).workspace_bytes(al + 1, al + 1) == 0
+
+
+def test_run_ws_without_workspace_falls_back_to_run():
+    # M = 0: both return before touching the device
+    p = tl.Plan(0, 16, 16, tl.BF16)
+    p.run_ws_ptr(0, 0, 0, 0, 0)

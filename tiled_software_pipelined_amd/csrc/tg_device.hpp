@@ -66,6 +66,26 @@ __device__ __forceinline__ void copy16_to_lds(uint32_t lds, uint32_t voff, const
 }
 #pragma clang diagnostic pop
 
+// Bytes [sh, sh + 16) of the 32-byte pair x | y (x first in memory),
+// 0 <= sh < 16: how a 16-byte piece at any byte offset is cut out of the
+// two aligned 16-byte blocks that cover it.
+__device__ __forceinline__ i32x4 funnel16(i32x4 x, i32x4 y, uint32_t sh) {
+    // Named scalars, not an array: selects between elements of a local
+    // array are turned into a dynamically indexed stack copy.
+    const bool s8 = sh & 8, s4 = sh & 4;
+    const uint32_t t0 = s8 ? x[2] : x[0], t1 = s8 ? x[3] : x[1], t2 = s8 ? y[0] : x[2];
+    const uint32_t t3 = s8 ? y[1] : x[3], t4 = s8 ? y[2] : y[0], t5 = s8 ? y[3] : y[1];
+    const uint32_t u0 = s4 ? t1 : t0, u1 = s4 ? t2 : t1, u2 = s4 ? t3 : t2;
+    const uint32_t u3 = s4 ? t4 : t3, u4 = s4 ? t5 : t4;
+    const uint32_t b = sh & 3;
+    i32x4 out;
+    out[0] = int32_t(__builtin_amdgcn_alignbyte(u1, u0, b));
+    out[1] = int32_t(__builtin_amdgcn_alignbyte(u2, u1, b));
+    out[2] = int32_t(__builtin_amdgcn_alignbyte(u3, u2, b));
+    out[3] = int32_t(__builtin_amdgcn_alignbyte(u4, u3, b));
+    return out;
+}
+
 __device__ __forceinline__ int wave_id() {
     return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }

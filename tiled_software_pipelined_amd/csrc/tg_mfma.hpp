@@ -154,23 +154,7 @@ struct MfmaGemm {
         return u.v;
     }
 
-    // Bytes [sh, sh + 16) of the 32-byte pair x | y (x first in memory).
-    __device__ static __forceinline__ i32x4 funnel(i32x4 x, i32x4 y, uint32_t sh) {
-        // Named scalars, not an array: selects between elements of a local
-        // array are turned into a dynamically indexed stack copy.
-        const bool s8 = sh & 8, s4 = sh & 4;
-        const uint32_t t0 = s8 ? x[2] : x[0], t1 = s8 ? x[3] : x[1], t2 = s8 ? y[0] : x[2];
-        const uint32_t t3 = s8 ? y[1] : x[3], t4 = s8 ? y[2] : y[0], t5 = s8 ? y[3] : y[1];
-        const uint32_t u0 = s4 ? t1 : t0, u1 = s4 ? t2 : t1, u2 = s4 ? t3 : t2;
-        const uint32_t u3 = s4 ? t4 : t3, u4 = s4 ? t5 : t4;
-        const uint32_t b = sh & 3;
-        i32x4 out;
-        out[0] = int32_t(__builtin_amdgcn_alignbyte(u1, u0, b));
-        out[1] = int32_t(__builtin_amdgcn_alignbyte(u2, u1, b));
-        out[2] = int32_t(__builtin_amdgcn_alignbyte(u3, u2, b));
-        out[3] = int32_t(__builtin_amdgcn_alignbyte(u4, u3, b));
-        return out;
-    }
+    __device__ static __forceinline__ i32x4 funnel(i32x4 x, i32x4 y, uint32_t sh) { return funnel16(x, y, sh); }
 
     // The value of `v` in lane + 1 of the same 16-lane row (DPP row_shl:1);
     // lanes 15, 31, 47, 63 keep `own`.

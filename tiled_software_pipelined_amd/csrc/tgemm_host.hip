@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "tg_args.hpp"
+#include "tg_pack.hpp"
 #include "tgemm.h"
 
 using tg::KernelEntry;
@@ -25,6 +26,9 @@ struct tgemm_plan {
     int32_t a_guard, b_guard;     // leading-dimension based (pointer alignment is checked per run)
     int64_t n_main;               // columns the entry's grid covers (N unless split)
     tgemm_plan* rem;              // split plans: the last N - n_main columns (thin kernel), else NULL
+    tgemm_plan* packed;           // default plans: the same product on operands repacked with
+                                  // 16-byte aligned rows (gemm_run_ws), else NULL
+    int64_t lda_p, ldb_p;         // leading dimensions of `packed`
 };
 
 namespace {
@@ -390,6 +394,9 @@ tgemm_plan* make_plan(int64_t M, int64_t N, int64_t K, int32_t dtype, int64_t ld
     p->b_guard = gb;
     p->n_main = N;
     p->rem = nullptr;
+    p->packed = nullptr;
+    p->lda_p = lda;
+    p->ldb_p = ldb;
     if (is_default) *is_default = default_plan;
     g_err.clear();
     return p;
@@ -405,11 +412,11 @@ extern "C" {
 // It does when the time model gives the main part fewer rounds than the
 // whole (4095 x 4097: 1056 tiles of 128 x 128, five on the busiest compute
 // unit, against 256 tiles of 256 x 256 in one round plus one column).
-tgemm_plan* gemm_plan_variant(int64_t M, int64_t N, int64_t K, int32_t dtype, int64_t lda, int64_t ldb,
-                              int64_t ldc, const tgemm_variant* variant) {
-    init_registry();
+static tgemm_plan* split_plan(int64_t M, int64_t N, int64_t K, int32_t dtype, int64_t lda, int64_t ldb,
+                              int64_t ldc, const tgemm_variant* variant, bool* default_out) {
     bool is_default = false;
     tgemm_plan* p = make_plan(M, N, K, dtype, lda, ldb, ldc, variant, &is_default);
+    if (default_out) *default_out = is_default;
     if (!p || !is_default || dtype == TGEMM_F32 || K == 0 || M == 0) return p;
     const KernelEntry& e = *p->entry;
     const int64_t r = N % e.bn;
@@ -439,6 +446,38 @@ tgemm_plan* gemm_plan_variant(int64_t M, int64_t N, int64_t K, int32_t dtype, in
     return main;
 }
 
+// Round a leading dimension up to whole 16-byte rows unless it already is.
+static int64_t aligned_ld(int64_t ld, int64_t cols, int esz) {
+    if ((ld * esz) % 16 == 0) return ld;
+    const int64_t per = 16 / esz;
+    return (cols + per - 1) / per * per;
+}
+
+// A default plan also carries the plan for the same product on operands
+// repacked into 16-byte aligned rows (gemm_run_ws), when that plan runs a
+// tiled kernel on more than THIN_N_MAX columns (for thinner products the
+// product itself moves about as many bytes as the repack would).
+tgemm_plan* gemm_plan_variant(int64_t M, int64_t N, int64_t K, int32_t dtype, int64_t lda, int64_t ldb,
+                              int64_t ldc, const tgemm_variant* variant) {
+    init_registry();
+    bool is_default = false;
+    tgemm_plan* p = split_plan(M, N, K, dtype, lda, ldb, ldc, variant, &is_default);
+    if (!p || !is_default || M == 0 || N <= tg::THIN_N_MAX || K == 0) return p;
+    const int esz = elem_size(dtype);
+    const int64_t lda_p = aligned_ld(lda, K, esz), ldb_p = aligned_ld(ldb, N, esz);
+    tgemm_plan* q = split_plan(M, N, K, dtype, lda_p, ldb_p, ldc, nullptr, nullptr);
+    if (!q || q->entry->family != tg::FAM_TILED) {
+        gemm_destroy(q);
+        g_err.clear();
+        return p;
+    }
+    p->packed = q;
+    p->lda_p = lda_p;
+    p->ldb_p = ldb_p;
+    g_err.clear();
+    return p;
+}
+
 tgemm_plan* gemm_plan(int64_t M, int64_t N, int64_t K, int32_t dtype, int64_t lda, int64_t ldb,
                       int64_t ldc) {
     return gemm_plan_variant(M, N, K, dtype, lda, ldb, ldc, nullptr);
@@ -447,6 +486,7 @@ tgemm_plan* gemm_plan(int64_t M, int64_t N, int64_t K, int32_t dtype, int64_t ld
 void gemm_destroy(tgemm_plan* plan) {
     if (!plan) return;
     gemm_destroy(plan->rem);
+    gemm_destroy(plan->packed);
     delete plan;
 }
 
@@ -526,6 +566,72 @@ int gemm_run(const tgemm_plan* p, const void* A, const void* B, void* C, void* s
         return gemm_run(p->rem, A, static_cast<const char*>(B) + p->n_main * esz,
                         static_cast<char*>(C) + p->n_main * 4, stream);
     return TGEMM_OK;
+}
+
+// Which operands gemm_run_ws repacks for these pointers (bit 0 A, bit 1 B)
+// and the workspace bytes that takes: an operand is repacked when its rows
+// are not 16-byte aligned (leading dimension or pointer), each copy starting
+// on a 256-byte boundary of the workspace.
+static int64_t pack_need(const tgemm_plan* p, const void* A, const void* B, int* mask) {
+    *mask = 0;
+    if (!p || !p->packed || p->M == 0 || p->N == 0 || p->K == 0) return 0;
+    const int esz = elem_size(p->dtype);
+    const bool ma = (p->lda * esz) % 16 != 0 || (uintptr_t)A % 16 != 0;
+    const bool mb = (p->ldb * esz) % 16 != 0 || (uintptr_t)B % 16 != 0;
+    int64_t need = 0;
+    if (ma) need += (p->M * p->lda_p * esz + 255) / 256 * 256;
+    if (mb) need += (p->K * p->ldb_p * esz + 255) / 256 * 256;
+    *mask = (ma ? 1 : 0) | (mb ? 2 : 0);
+    return need;
+}
+
+int64_t gemm_workspace_bytes(const tgemm_plan* p, const void* A, const void* B) {
+    int mask = 0;
+    return pack_need(p, A, B, &mask);
+}
+
+int gemm_run_ws(const tgemm_plan* p, const void* A, const void* B, void* C, void* workspace,
+                int64_t workspace_bytes, void* stream) {
+    int mask = 0;
+    const int64_t need = pack_need(p, A, B, &mask);
+    if (need == 0 || !workspace || workspace_bytes < need) return gemm_run(p, A, B, C, stream);
+    if ((uintptr_t)workspace % 256) {
+        set_err("workspace not 256-byte aligned");
+        return TGEMM_E_ALIGN;
+    }
+    if (!C || !A || !B) {
+        set_err("NULL matrix pointer");
+        return TGEMM_E_NULL;
+    }
+    const int esz = elem_size(p->dtype);
+    if (((uintptr_t)A % esz) || ((uintptr_t)B % esz) || ((uintptr_t)C % 4)) {
+        set_err("pointer not aligned to its element size");
+        return TGEMM_E_ALIGN;
+    }
+    int rc = check_arch();
+    if (rc != TGEMM_OK) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    const void* a = A;
+    const void* b = B;
+    if (mask & 1) {
+        const hipError_t err = tg::launch_pack(A, ws, p->M, p->K * esz, p->lda * esz, p->lda_p * esz, s);
+        if (err != hipSuccess) {
+            set_err("repack of A failed: %s", hipGetErrorString(err));
+            return TGEMM_E_HIP;
+        }
+        a = ws;
+        ws += (p->M * p->lda_p * esz + 255) / 256 * 256;
+    }
+    if (mask & 2) {
+        const hipError_t err = tg::launch_pack(B, ws, p->K, p->N * esz, p->ldb * esz, p->ldb_p * esz, s);
+        if (err != hipSuccess) {
+            set_err("repack of B failed: %s", hipGetErrorString(err));
+            return TGEMM_E_HIP;
+        }
+        b = ws;
+    }
+    return gemm_run(p->packed, a, b, C, stream);
 }
 
 int gemm_plan_get_info(const tgemm_plan* p, tgemm_plan_info* info) {

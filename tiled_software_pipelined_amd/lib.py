@@ -57,7 +57,7 @@ class PlanInfo(ctypes.Structure):
 
 EXPORTS = ("gemm_plan", "gemm_plan_variant", "gemm_run", "gemm_destroy", "tgemm_last_error",
            "gemm_plan_get_info", "gemm_variant_count", "gemm_variant_get", "tgemm_version",
-           "tgemm_lds_read_probe", "tgemm_mfma_rate_probe")
+           "tgemm_lds_read_probe", "tgemm_mfma_rate_probe", "gemm_workspace_bytes", "gemm_run_ws")
 
 
 def _load():
@@ -90,6 +90,10 @@ def _load():
     lib.tgemm_version.restype = ctypes.c_char_p
     lib.tgemm_lds_read_probe.argtypes = [i32, i32, i32, i32, vp, vp]
     lib.tgemm_lds_read_probe.restype = ctypes.c_int
+    lib.gemm_workspace_bytes.argtypes = [vp, vp, vp]
+    lib.gemm_workspace_bytes.restype = i64
+    lib.gemm_run_ws.argtypes = [vp, vp, vp, vp, vp, i64, vp]
+    lib.gemm_run_ws.restype = ctypes.c_int
     lib.tgemm_mfma_rate_probe.argtypes = [i32, i32, i32, vp, vp, vp, vp]
     lib.tgemm_mfma_rate_probe.restype = ctypes.c_int
     return lib
@@ -209,6 +213,17 @@ class Plan:
         if rc != OK:
             raise TgemmError(rc, last_error())
 
+    def workspace_bytes(self, A: int, B: int) -> int:
+        """Workspace bytes gemm_run_ws uses to repack misaligned operands at these addresses."""
+        return int(_lib.gemm_workspace_bytes(self._h, ctypes.c_void_p(A), ctypes.c_void_p(B)))
+
+    def run_ws_ptr(self, A: int, B: int, C: int, ws: int, ws_bytes: int, stream: int = 0) -> None:
+        """gemm_run_ws on raw device pointers (the caller keeps the buffers alive)."""
+        rc = _lib.gemm_run_ws(self._h, ctypes.c_void_p(A), ctypes.c_void_p(B), ctypes.c_void_p(C),
+                              ctypes.c_void_p(ws), ws_bytes, ctypes.c_void_p(stream))
+        if rc != OK:
+            raise TgemmError(rc, last_error())
+
     def __del__(self):
         h = getattr(self, "_h", None)
         if h and _lib is not None:  # module globals are gone at interpreter exit
@@ -246,13 +261,17 @@ def plan_for(M, N, K, dtype, lda, ldb, ldc, variant: Variant | None = None) -> P
     return p
 
 
-def gemm(A, B, out=None, variant: Variant | None = None):
+def gemm(A, B, out=None, variant: Variant | None = None, workspace: bool = True):
     """C = A @ B on the current CUDA/HIP stream.
 
     A: (M, K), B: (K, N) torch tensors on the GPU, both float32, both bfloat16
     or both int8, row-major (row stride may exceed the row length).  Returns
     C (M, N): float32 for float32/bfloat16 inputs, int32 for int8 inputs.
     ``out`` may be a preallocated row-major C (its row stride is used as ldc).
+    With ``workspace`` (default plans only), operands whose rows are not
+    16-byte aligned are repacked into a device buffer taken from torch's
+    allocator on the current stream (gemm_run_ws); otherwise the kernels that
+    read such rows in place run (gemm_run).
     """
     import torch
     if not (A.is_cuda and B.is_cuda):
@@ -273,5 +292,13 @@ def gemm(A, B, out=None, variant: Variant | None = None):
     p = plan_for(M, N, K, code, lda, ldb, ldc, variant)
     stream = torch.cuda.current_stream(A.device).cuda_stream
     with torch.cuda.device(A.device):
-        p.run_ptr(A.data_ptr(), B.data_ptr(), out.data_ptr(), stream)
+        need = p.workspace_bytes(A.data_ptr(), B.data_ptr()) if workspace and variant is None else 0
+        if need > 0:
+            # stream-ordered: the block returns to torch's pool for this
+            # stream when `ws` is dropped, after the work queued here
+            ws = torch.empty(need + 256, dtype=torch.uint8, device=A.device)
+            base = (ws.data_ptr() + 255) // 256 * 256
+            p.run_ws_ptr(A.data_ptr(), B.data_ptr(), out.data_ptr(), base, need, stream)
+        else:
+            p.run_ptr(A.data_ptr(), B.data_ptr(), out.data_ptr(), stream)
     return out
