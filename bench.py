@@ -462,7 +462,9 @@ def main():
     # HBM bytes per launch measured by the counter layer on these exact
     # kernel sources (profiles/*.md); null when none matches
     from tiled_software_pipelined_amd import provenance
-    prof = provenance.find_profile(plan.name, w.name)
+    # the kernel that ran (the repacked plan's when operand rows were misaligned)
+    kname = plan.kernel_for(A.data_ptr(), B.data_ptr(), workspace=variant is None)
+    prof = provenance.find_profile(kname, w.name)
     traffic = None
     if prof and prof.get("traffic_bytes") not in (None, "null"):
         traffic = int(float(prof["traffic_bytes"]))
@@ -480,7 +482,7 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": "%s GEMM M=%d N=%d K=%d" % (w.dtype, w.M, w.N, w.K),
-                   "operands": w.kind, "seed": w.seed, "kernel": plan.name,
+                   "operands": w.kind, "seed": w.seed, "kernel": kname,
                    "grid": plan.info().grid, "frac_of_peak": round(value / peak, 4)},
         "roofline": {"bound": "mfma" if w.dtype != "f32" else "alu", "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s" if w.dtype != "i8" else "TOP/s",
@@ -493,7 +495,7 @@ def main():
                                "kernel_ms_min: per-launch events in a pass after it"},
         "cpu_baseline": None,
     }
-    if w.dtype in ("bf16", "i8"):
+    if w.dtype in ("bf16", "i8") and not args.calib_copy:
         # the rate the matrix cores sustain on this machine for the workload's
         # operand distribution with no memory traffic at all (the power
         # budget lowers the clock below nominal for random operands)

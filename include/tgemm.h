@@ -200,6 +200,8 @@ typedef struct tgemm_plan_info {
     int64_t n_main;          /* columns the kernel above covers: N, or for a split plan the first
                                 N - r, the last r (<= 16) going to the thin kernel `rem_name` */
     char rem_name[96];       /* split plans: the kernel of the last columns; else "" */
+    char packed_name[96];    /* the kernel gemm_run_ws runs on repacked operands (its plan's
+                                `name`); "" for plans that carry no repack */
 } tgemm_plan_info;
 
 /* Fill *info for `plan`.  Returns TGEMM_OK or TGEMM_E_NULL. */

@@ -652,6 +652,7 @@ int gemm_plan_get_info(const tgemm_plan* p, tgemm_plan_info* info) {
     info->grid = (int32_t)(((p->M + e.bm - 1) / e.bm) * ((p->n_main + e.bn - 1) / e.bn));
     info->n_main = p->n_main;
     if (p->rem) snprintf(info->rem_name, sizeof info->rem_name, "%s", p->rem->entry->name);
+    if (p->packed) snprintf(info->packed_name, sizeof info->packed_name, "%s", p->packed->entry->name);
     info->threads = e.threads;
     info->lds_bytes = e.lds_bytes;
     info->loads_per_stage = e.loads_per_stage;

@@ -52,7 +52,7 @@ class PlanInfo(ctypes.Structure):
                 ("threads", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
                 ("loads_per_stage", ctypes.c_int32), ("a_guarded", ctypes.c_int32),
                 ("b_guarded", ctypes.c_int32), ("name", ctypes.c_char * 96), ("n_main", ctypes.c_int64),
-                ("rem_name", ctypes.c_char * 96)]
+                ("rem_name", ctypes.c_char * 96), ("packed_name", ctypes.c_char * 96)]
 
 
 EXPORTS = ("gemm_plan", "gemm_plan_variant", "gemm_run", "gemm_destroy", "tgemm_last_error",
@@ -205,6 +205,14 @@ class Plan:
     @property
     def name(self) -> str:
         return self.info().name.decode()
+
+    def kernel_for(self, A: int, B: int, workspace: bool = True) -> str:
+        """Name of the main kernel that runs for operands at these addresses:
+        the repacked plan's when the binding would use a workspace."""
+        info = self.info()
+        if workspace and self.workspace_bytes(A, B) > 0:
+            return info.packed_name.decode()
+        return info.name.decode()
 
     def run_ptr(self, A: int, B: int, C: int, stream: int = 0) -> None:
         """Enqueue on raw device pointers (the caller keeps the buffers alive)."""
