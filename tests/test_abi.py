@@ -93,7 +93,13 @@ def test_default_choice_by_shape():
     assert big.variant.loader == tl.LOADER_DIRECT and big.grid == 256
     mid = tl.Plan(1024, 1024, 512, tl.BF16).info()
     assert (mid.variant.tile_m, mid.variant.tile_n) == (128, 128) and mid.grid == 64
-    assert mid.variant.stages == 3
+    assert mid.variant.stages == 4
+    assert tl.Plan(1024, 1024, 256, tl.BF16).info().variant.stages == 3
+    # one round of 256 x 256 tiles from K = 512 (int8: 1024); several rounds
+    # at short K stay on 128 x 128
+    for M, K, dt, edge in [(4096, 512, tl.BF16, 256), (4096, 256, tl.BF16, 128), (3072, 512, tl.BF16, 256),
+                           (6144, 512, tl.BF16, 128), (4096, 1024, tl.I8, 256), (4096, 512, tl.I8, 128)]:
+        assert tl.Plan(M, M, K, dt).info().variant.tile_m == edge, (M, K, dt)
     # long K on the 128 x 128 tile: the deeper ring; on the 64 x 64 tile the
     # 8-slot ring
     assert tl.Plan(2048, 2048, 4096, tl.BF16).info().variant.stages == 4

@@ -11,6 +11,7 @@ void register_i8(void (*add)(const KernelEntry&)) {
     add(mfma_entry<T, 256, 256, 128, 2, 2, 2, LD_VGPR, LY_XOR, AC_WIDE, FR_REUSE, 1>(2));
     add(mfma_entry<T, 256, 256, 128, 2, 4, 2, LD_VGPR, LY_XOR, AC_WIDE, FR_REUSE, 2>(2));
     add(mfma_entry<T, 128, 128, 64, 2, 2, 3, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2>(2));
+    add(mfma_entry<T, 128, 128, 64, 2, 2, 4, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2>(2));
     add(mfma_entry<T, 128, 128, 64, 2, 2, 2, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2>(2));
     add(mfma_entry<T, 128, 128, 64, 2, 2, 2, LD_VGPR, LY_XOR, AC_WIDE, FR_REUSE, 2>(2));
     add(mfma_entry<T, 128, 128, 64, 2, 2, 1, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2>(2));

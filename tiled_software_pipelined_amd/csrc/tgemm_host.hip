@@ -177,20 +177,30 @@ const KernelEntry* default_entry(int dtype, int64_t M, int64_t N, int64_t K, boo
     // 4096^3: bf16 direct 146 / 4 us vs 113 us; int8 85 / 4 vs 68 us;
     // register-staged, B rows unaligned: 221 / 4 vs 212 us
     const double mid_tile = guarded ? 0.26 : (i8 ? 0.31 : 0.325);
+    // Below short_k, a single round of 256 x 256 tiles (128 to 256 of them)
+    // still wins from K = 512 (int8: 1024), where the K loop outweighs the
+    // one unoverlapped C write: bf16 4096^2 x 512 26.0 vs 27.2 us (128 x 128,
+    // 4 slots), x 1024 38.3 vs 41.6; 3072^2 x 512 19.8 vs 21.9; int8 4096^2 x
+    // 1024 28.0 vs 30.9, x 2048 41.3 vs 47.3.  With more than one round
+    // (6144^2 x 512: 68.1 vs 57.4) the 128 x 128 tiles overlap their writes.
+    const int64_t one_round_k = i8 ? 1024 : 512;
     int pick;  // tile edge
     if (wgs(256) >= 128 && K > short_k)
         pick = big_rounds(wgs(256)) <= mid_tile * (double)((wgs(128) + 255) / 256) ? 256 : 128;
+    else if (!guarded && wgs(256) >= 128 && wgs(256) <= 256 && K >= one_round_k)
+        pick = 256;
     else if (wgs(128) >= 64 || guarded)
         pick = 128;
     else
         pick = 64;
     v.tile_m = v.tile_n = pick;
     v.waves_n = pick == 256 ? 4 : 2;
-    // bf16 128 x 128 direct: a 4-slot ring from K = 4096 (4-13 % faster than
-    // 3 slots at 2048^2 x 4096, 4096 x 4352 x 4096, 1024^2 x 8192 and 2048^2
-    // x 8192); 3 below (equal to 4 at K <= 1024, where the prologue
-    // dominates) and for the other tiles and int8
-    v.stages = pick == 256 || guarded ? 2 : (pick == 128 && !i8 && K >= 4096 ? 4 : 3);
+    // 128 x 128 direct: a 4-slot ring from K = 512 for bf16 (4-13 % faster
+    // than 3 slots at 2048^2 x 4096, 4096 x 4352 x 4096, 1024^2 x 8192 and
+    // 2048^2 x 8192; 3-8 % at 2048^2 x 1024..2048, 6144^2 and 8192^2 x 512)
+    // and from K = 1024 for int8 (2048^2 x 4096 24.3 vs 25.4 us, 6144^2 x
+    // 1024 57.0 vs 60.9; equal at 2048^2 x 8192); 3 below
+    v.stages = pick == 256 || guarded ? 2 : (pick == 128 && K >= (i8 ? 1024 : 512) ? 4 : 3);
     // 64 x 64 tiles (grids of about one workgroup per compute unit): an
     // 8-slot ring from K = 2048 (6-20 % faster than 3 slots at 512^2 x
     // 2048..8192, 768^2 x 4096 and 512 x 1024 x 8192, timed by graph replay)
