@@ -191,31 +191,31 @@ def lds_probe(torch, lib, workgroups=2048, reps=2048, rounds=8, launches=3):
 
 
 def mfma_ceiling(torch, lib, dtype, source, reps=None, workgroups=256, launches=3):
-    """The matrix-core rate probe (one wave per SIMD, 16 independent
-    accumulators, no memory traffic) on operand bits drawn as `source`:
-    "random" = the GEMM workloads' distribution (bf16 N(0,1), int8 uniform),
-    "ones", "zeros".  Returns (TFLOP/s or TOP/s, mean clock in GHz from the
-    shader-clock / real-time tick ratio, median ms)."""
+    """The rate probe (no memory traffic) on operand bits drawn as `source`:
+    "random" = the GEMM workloads' distribution (bf16 N(0,1), int8 uniform,
+    fp32 uniform[-1, 1)), "ones", "zeros".  bf16 / int8: the matrix
+    instruction, one wave per SIMD, 16 independent accumulators; fp32:
+    v_fmac_f32, with `workgroups` / 256 x 4 waves per SIMD.  Returns
+    (TFLOP/s or TOP/s, mean clock in GHz from the shader-clock / real-time
+    tick ratio, median ms)."""
     from tiled_software_pipelined_amd import inputs
     kind = lib.RATE_PROBE_KINDS.index(dtype)
     nbytes = workgroups * lib.RATE_PROBE_THREADS * 8 * 16
-    if dtype == "bf16":
-        if source == "random":
-            ops = inputs.operand("bf16_normal", nbytes // 2 // 2048, 2048, 77)
-        else:
-            ops = torch.full((nbytes // 2,), 1.0 if source == "ones" else 0.0, dtype=torch.bfloat16)
+    if source == "random":
+        kinds = {"bf16": ("bf16_normal", 2), "i8": ("i8_uniform", 1), "f32": ("f32_uniform", 4)}
+        kname, esz = kinds[dtype]
+        ops = inputs.operand(kname, nbytes // esz // 2048, 2048, 77 + kind)
     else:
-        if source == "random":
-            ops = inputs.operand("i8_uniform", nbytes // 4096, 4096, 78)
-        else:
-            ops = torch.full((nbytes,), 1 if source == "ones" else 0, dtype=torch.int8)
+        tdt = {"bf16": torch.bfloat16, "i8": torch.int8, "f32": torch.float32}[dtype]
+        esz = {"bf16": 2, "i8": 1, "f32": 4}[dtype]
+        ops = torch.full((nbytes // esz,), 1 if source == "ones" else 0, dtype=tdt)
     ops = ops.contiguous().view(-1).to("cuda:0")
     out = torch.empty(workgroups * lib.RATE_PROBE_THREADS, dtype=torch.int32, device="cuda:0")
     clocks = torch.empty(2 * workgroups, dtype=torch.int64, device="cuda:0")
-    # about 20 ms per launch at the nominal clock (both instructions take 32
-    # cycles per wave)
-    reps = reps or int(20e-3 * 2.4e9 / (16 * 32))
-    lib.mfma_rate_probe(kind, reps // 10, ops, out, clocks)
+    per_iter = float(lib.RATE_PROBE_OPS_PER_INST[dtype]) * 16 * 4 * workgroups  # ops per loop iteration
+    # about 20 ms per launch at the datasheet peak
+    reps = reps or max(1, int(20e-3 * PEAK_TFLOPS[dtype] * 1e12 / per_iter))
+    lib.mfma_rate_probe(kind, max(1, reps // 10), ops, out, clocks)
     torch.cuda.synchronize()
     ms, ghz = [], []
     for _ in range(launches):
@@ -228,8 +228,11 @@ def mfma_ceiling(torch, lib, dtype, source, reps=None, workgroups=256, launches=
         c = clocks.view(-1, 2).double().cpu()
         ghz.append(float((c[:, 0] / c[:, 1]).mean()) * 0.1)
     med = statistics.median(ms)
-    ops_total = float(lib.RATE_PROBE_OPS_PER_INST[dtype]) * 16 * reps * 4 * workgroups
-    return ops_total / (med * 1e-3) / 1e12, statistics.median(ghz), med
+    return per_iter * reps / (med * 1e-3) / 1e12, statistics.median(ghz), med
+
+
+# waves per SIMD of the fp32 rate probe and the workgroups that give them
+F32_PROBE_WAVES = {4: 1024, 8: 2048}
 
 
 class PowerSampler:
@@ -353,13 +356,14 @@ def main():
         lds_probe(torch, lib)
         return
     if args.mfma_probe:
-        for dt in ("bf16", "i8"):
-            for src in ("random", "ones", "zeros"):
-                rate, ghz, ms = mfma_ceiling(torch, lib, dt, src)
-                print(json.dumps({"mode": "mfma_probe", "dtype": dt, "operands": src,
-                                  "rate": round(rate, 1), "unit": "TFLOP/s" if dt == "bf16" else "TOP/s",
-                                  "frac_peak": round(rate / PEAK_TFLOPS[dt], 4), "clock_ghz": round(ghz, 3),
-                                  "median_ms": round(ms, 3)}), flush=True)
+        cases = [(dt, src, 256, 1) for dt in ("bf16", "i8") for src in ("random", "ones", "zeros")]
+        cases += [("f32", src, wgs, w) for src in ("random", "ones") for w, wgs in F32_PROBE_WAVES.items()]
+        for dt, src, wgs, waves in cases:
+            rate, ghz, ms = mfma_ceiling(torch, lib, dt, src, workgroups=wgs)
+            print(json.dumps({"mode": "mfma_probe", "dtype": dt, "operands": src, "waves_per_simd": waves,
+                              "rate": round(rate, 1), "unit": "TOP/s" if dt == "i8" else "TFLOP/s",
+                              "frac_peak": round(rate / PEAK_TFLOPS[dt], 4), "clock_ghz": round(ghz, 3),
+                              "median_ms": round(ms, 3)}), flush=True)
         return
 
     w = inputs.workloads()[args.workload]
@@ -495,14 +499,17 @@ def main():
                                "kernel_ms_min: per-launch events in a pass after it"},
         "cpu_baseline": None,
     }
-    if w.dtype in ("bf16", "i8") and not args.calib_copy:
-        # the rate the matrix cores sustain on this machine for the workload's
-        # operand distribution with no memory traffic at all (the power
-        # budget lowers the clock below nominal for random operands)
-        rate, ghz, _ = mfma_ceiling(torch, lib, w.dtype, "random")
+    if not args.calib_copy:
+        # the rate the arithmetic units sustain on this machine for the
+        # workload's operand distribution with no memory traffic at all (the
+        # power budget lowers the clock below nominal for random operands;
+        # the fp32 rate grows with the waves per SIMD, 8 at most)
+        wgs = 256 if w.dtype != "f32" else F32_PROBE_WAVES[8]
+        rate, ghz, _ = mfma_ceiling(torch, lib, w.dtype, "random", workgroups=wgs)
+        unit = "matrix-core" if w.dtype != "f32" else "v_fmac_f32 (8 waves per SIMD)"
         rec["roofline"]["measured_ceiling"] = {
             "value": round(rate, 1), "clock_ghz": round(ghz, 3), "frac": round(achieved / rate, 4),
-            "source": "matrix-core rate probe, random %s operands, no memory traffic" % w.dtype}
+            "source": "%s rate probe, random %s operands, no memory traffic" % (unit, w.dtype)}
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(w, A_cpu, B_cpu)
     print(json.dumps(rec), flush=True)

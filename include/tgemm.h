@@ -250,6 +250,8 @@ int tgemm_lds_read_probe(int32_t kind, int32_t pattern, int32_t reps, int32_t wo
  * the roofline's compute ceiling is the one to measure against).
  *   kind 0: v_mfma_f32_32x32x16_bf16 (32768 flops per wave instruction)
  *   kind 1: v_mfma_i32_32x32x32_i8   (65536 ops per wave instruction)
+ *   kind 2: v_fmac_f32, the fp32 vector fused multiply-add (128 flops per
+ *           wave instruction), the ALU of the fp32 path
  * Launches `workgroups` workgroups of 256 threads (4 waves, one per SIMD
  * while workgroups <= 256 compute units) on `stream`.  Thread t (global
  * index workgroup * 256 + thread) loads operands[8t .. 8t+3] (16 bytes each)
@@ -262,11 +264,17 @@ int tgemm_lds_read_probe(int32_t kind, int32_t pattern, int32_t reps, int32_t wo
  * 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.
  * out[t] = the sum of the thread's 256 accumulator registers (bf16: fp32
  * bits of a sum taken in increasing i, then r; int8: the int32 sum mod 2^32).
+ * Kind 2 instead reads the same 128 bytes as 16 floats x[0..15] (A
+ * registers) and y[0..15] (B registers) and runs `reps` iterations of
+ * acc[i] = fma(x[i], y[i], acc[i]), i = 0..15, from acc = 0; out[t] = fp32
+ * bits of acc[0] + ... + acc[15] summed in increasing i.  It is built for up
+ * to 8 waves per SIMD: `workgroups` / 256 compute units sets the waves that
+ * share a SIMD (up to 8 workgroups of 4 waves per unit).
  * clocks[2 w], clocks[2 w + 1]: shader-clock ticks (s_memtime) and 100 MHz
  * real-time ticks (s_memrealtime) that wave 0 of workgroup w spent in the
  * loop.  operands (workgroups * 256 * 8 16-byte entries), out (workgroups *
  * 256 uint32) and clocks (2 * workgroups uint64) are device memory owned by
- * the caller.  Returns TGEMM_OK, TGEMM_E_ARG (kind outside 0..1, reps < 0,
+ * the caller.  Returns TGEMM_OK, TGEMM_E_ARG (kind outside 0..2, reps < 0,
  * workgroups < 1), TGEMM_E_NULL, TGEMM_E_ALIGN (operands not 16-byte, out
  * not 4-byte or clocks not 8-byte aligned) or TGEMM_E_HIP (launch failed). */
 int tgemm_mfma_rate_probe(int32_t kind, int32_t reps, int32_t workgroups, const void* operands, uint32_t* out,

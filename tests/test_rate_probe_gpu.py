@@ -1,11 +1,12 @@
-"""GPU: the matrix-core rate probe executes the instructions its definition names.
+"""GPU: the rate probe executes the instructions its definition names.
 
 The probe (tgemm_mfma_rate_probe, include/tgemm.h) sums every accumulator
 register of each thread after `reps` iterations of 16 independent
-matrix-core instructions.  With small integer operands every product and sum
-is exact, so each thread's sum is recomputed here from the operand bytes and
-the instruction's operand / result lane layout: a dropped or repeated
-instruction, a wrong operand register or a wrong layout changes it.
+matrix-core instructions (kinds 0, 1) or fp32 fma chains (kind 2).  With
+small integer operands every product and sum is exact, so each thread's sum
+is recomputed here from the operand bytes and the instruction's operand /
+result lane layout: a dropped or repeated instruction, a wrong operand
+register or a wrong layout changes it.
 """
 import numpy as np
 import pytest
@@ -27,9 +28,12 @@ def _gpu():
 
 
 def _operands(kind, workgroups, seed):
-    """Small integers: bf16 in [-3, 3], int8 in [-8, 8]; shape (threads, 8, H)."""
+    """Small integers: bf16 / fp32 in [-3, 3], int8 in [-8, 8]; shape (threads, 8, H)."""
     g = np.random.default_rng(seed)
     threads = workgroups * 256
+    if kind == 2:
+        vals = g.integers(-3, 4, size=(threads, 8, 4)).astype(np.float32)
+        return vals, torch.from_numpy(vals.reshape(-1).copy())
     if kind == 0:
         vals = g.integers(-3, 4, size=(threads, 8, 8)).astype(np.float32)
         bits = (vals.view(np.uint32) >> 16).astype(np.uint16)  # exact: small integers
@@ -39,7 +43,12 @@ def _operands(kind, workgroups, seed):
 
 
 def _expected(kind, vals, reps):
-    """Per-thread sum of the 16 accumulators' registers after `reps` iterations."""
+    """Per-thread sum of the 16 accumulators' registers after `reps` iterations
+    (kind 2: of the 16 fma chains, acc_i = reps * x_i * y_i)."""
+    if kind == 2:
+        x = vals[:, 0:4, :].reshape(vals.shape[0], 16).astype(np.int64)
+        y = vals[:, 4:8, :].reshape(vals.shape[0], 16).astype(np.int64)
+        return (x * y).sum(axis=1) * reps
     H = 8 if kind == 0 else 16  # K elements per lane
     out = np.zeros(vals.shape[0], dtype=np.int64)
     lane = np.arange(64)
@@ -59,7 +68,7 @@ def _expected(kind, vals, reps):
     return out
 
 
-@pytest.mark.parametrize("kind", [0, 1])
+@pytest.mark.parametrize("kind", [0, 1, 2])
 @pytest.mark.parametrize("reps", [0, 1, 3])
 def test_rate_probe_checksum(kind, reps):
     wgs = 3
@@ -71,7 +80,7 @@ def test_rate_probe_checksum(kind, reps):
     torch.cuda.synchronize()
     got = out.cpu().numpy()
     exp = _expected(kind, vals, reps)
-    if kind == 0:
+    if kind in (0, 2):
         got = got.view(np.float32).astype(np.int64)
     else:
         exp = exp.astype(np.int32).astype(np.int64)
@@ -102,7 +111,7 @@ def test_rate_probe_rejects_bad_arguments():
     clocks = torch.empty(2, dtype=torch.int64, device="cuda:0")
     ops = torch.empty(256 * 8 * 8, dtype=torch.int16, device="cuda:0")
     with pytest.raises(Exception):
-        tl.mfma_rate_probe(2, 1, ops, out, clocks)
+        tl.mfma_rate_probe(3, 1, ops, out, clocks)
     with pytest.raises(Exception):
         tl.mfma_rate_probe(0, -1, ops, out, clocks)
     with pytest.raises(ValueError):

@@ -195,6 +195,45 @@ void mfma_rate_probe(const i32x4* operands, uint32_t* out, uint64_t* clocks, int
     }
 }
 
+// The fp32 vector counterpart: 16 independent v_fmac_f32 chains per thread,
+// every operand in a VGPR, acc[i] = fma(x[i], y[i], acc[i]) with x the 16
+// floats of the thread's A registers and y those of its B registers.  Built
+// for up to 8 waves per SIMD, so that the number of workgroups per compute
+// unit sets how many waves share a SIMD.
+__global__ __launch_bounds__(RATE_THREADS) __attribute__((amdgpu_waves_per_eu(1, 8)))
+void fma_rate_probe(const i32x4* operands, uint32_t* out, uint64_t* clocks, int reps) {
+    const int64_t t = (int64_t)blockIdx.x * RATE_THREADS + threadIdx.x;
+    float x[16], y[16], acc[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const f32x4 a = __builtin_bit_cast(f32x4, operands[t * 8 + q]);
+        const f32x4 b = __builtin_bit_cast(f32x4, operands[t * 8 + 4 + q]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[4 * q + e] = a[e];
+            y[4 * q + e] = b[e];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    const uint64_t c0 = __builtin_amdgcn_s_memtime();
+    const uint64_t w0 = __builtin_amdgcn_s_memrealtime();
+    for (int it = 0; it < reps; ++it) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] = __builtin_fmaf(x[i], y[i], acc[i]);
+    }
+    const uint64_t c1 = __builtin_amdgcn_s_memtime();
+    const uint64_t w1 = __builtin_amdgcn_s_memrealtime();
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += acc[i];
+    out[t] = __builtin_bit_cast(uint32_t, s);
+    if (threadIdx.x == 0) {
+        clocks[2 * blockIdx.x] = c1 - c0;
+        clocks[2 * blockIdx.x + 1] = w1 - w0;
+    }
+}
+
 }  // namespace tg
 
 extern "C" int tgemm_lds_read_probe(int32_t kind, int32_t pattern, int32_t reps, int32_t workgroups, uint32_t* out,
@@ -213,11 +252,11 @@ extern "C" int tgemm_lds_read_probe(int32_t kind, int32_t pattern, int32_t reps,
 
 extern "C" int tgemm_mfma_rate_probe(int32_t kind, int32_t reps, int32_t workgroups, const void* operands,
                                      uint32_t* out, uint64_t* clocks, void* stream) {
-    if (kind < 0 || kind > 1 || reps < 0 || workgroups < 1) return TGEMM_E_ARG;
+    if (kind < 0 || kind > 2 || reps < 0 || workgroups < 1) return TGEMM_E_ARG;
     if (!operands || !out || !clocks) return TGEMM_E_NULL;
     if ((uintptr_t)operands % 16 || (uintptr_t)out % 4 || (uintptr_t)clocks % 8) return TGEMM_E_ALIGN;
-    static void (*const fns[2])(const tg::i32x4*, uint32_t*, uint64_t*, int) = {tg::mfma_rate_probe<0>,
-                                                                                tg::mfma_rate_probe<1>};
+    static void (*const fns[3])(const tg::i32x4*, uint32_t*, uint64_t*, int) = {
+        tg::mfma_rate_probe<0>, tg::mfma_rate_probe<1>, tg::fma_rate_probe};
     const tg::i32x4* ops = static_cast<const tg::i32x4*>(operands);
     void* args[] = {&ops, &out, &clocks, &reps};
     const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(fns[kind]), dim3((unsigned)workgroups),

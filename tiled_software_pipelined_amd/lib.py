@@ -137,9 +137,9 @@ def lds_read_probe(kind: int, pattern: int, reps: int, out):
     return out
 
 
-RATE_PROBE_KINDS = ("bf16", "i8")
+RATE_PROBE_KINDS = ("bf16", "i8", "f32")
 RATE_PROBE_THREADS = 256
-RATE_PROBE_OPS_PER_INST = {"bf16": 2 * 32 * 32 * 16, "i8": 2 * 32 * 32 * 32}
+RATE_PROBE_OPS_PER_INST = {"bf16": 2 * 32 * 32 * 16, "i8": 2 * 32 * 32 * 32, "f32": 2 * 64}
 
 
 def mfma_rate_probe(kind: int, reps: int, operands, out, clocks):
