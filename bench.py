@@ -18,6 +18,8 @@ Extra modes (not used by the default run):
     --lds-probe  LDS read throughput of ds_read_b32 / b64 / b128 / b64_tr_b16
     --mfma-probe matrix-core rate and clock for bf16 / int8 operand bits
                  (the workloads' random operands, all ones, all zeros)
+    --cold       per-launch kernel time with the caches cold: a 512 MiB buffer is
+                 written before every launch, evicting L2 and MALL (one JSON line)
     --soak S     run the workload's GEMM, then the matrix-core probe on random
                  operands of its type, back to back for S seconds each while
                  sampling socket power and shader clocks (amd-smi)
@@ -319,6 +321,29 @@ def soak(torch, lib, w, A, B, C, seconds):
         print(json.dumps(rec), flush=True)
 
 
+def cold_timing(torch, lib, w, A, B, C, variant, launches=30):
+    """Kernel time per launch with cold caches: before each launch a 512 MiB
+    buffer is filled (more than the 256 MB MALL and the 8 x 4 MB of L2), so
+    A and B start in HBM; HIP events bracket the GEMM alone."""
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    for _ in range(20):
+        lib.gemm(A, B, out=C, variant=variant)
+    per = []
+    for _ in range(launches):
+        scratch.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        lib.gemm(A, B, out=C, variant=variant)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1))
+    ms = statistics.median(per)
+    print(json.dumps({"mode": "cold", "workload": w.name, "launches": launches, "median_ms": round(ms, 5),
+                      "min_ms": round(min(per), 5), "rate": round(w.flops / ms / 1e9, 1),
+                      "unit": "TOP/s" if w.dtype == "i8" else "TFLOP/s"}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -336,6 +361,8 @@ def main():
     ap.add_argument("--mfma-probe", action="store_true",
                     help="matrix-core rate and clock for bf16 / int8 with random, all-ones and all-zero "
                          "operand bits (one JSON line each)")
+    ap.add_argument("--cold", action="store_true",
+                    help="per-launch kernel time with L2 and MALL evicted before every launch")
     ap.add_argument("--soak", type=float, default=0.0, metavar="S",
                     help="GEMM and matrix-core probe back to back for S seconds each, with socket "
                          "power and shader clocks sampled by amd-smi")
@@ -442,6 +469,9 @@ def main():
 
     if args.soak:
         soak(torch, lib, w, A, B, C, args.soak)
+        return
+    if args.cold:
+        cold_timing(torch, lib, w, A, B, C, parse_variant(args.variant, lib))
         return
 
     if args.calib_copy:
