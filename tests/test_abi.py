@@ -110,7 +110,7 @@ def test_default_choice_by_shape():
     small = tl.Plan(512, 512, 512, tl.BF16).info()
     assert (small.variant.tile_m, small.variant.tile_n) == (64, 64) and small.grid == 64
     f = tl.Plan(256, 256, 256, tl.F32).info()
-    assert f.variant.tile_k == 8 and f.grid == 4
+    assert f.variant.tile_k == 16 and f.grid == 4
 
 
 def test_unaligned_leading_dimension_uses_guarded_register_loader():

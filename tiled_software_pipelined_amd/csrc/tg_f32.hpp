@@ -19,8 +19,9 @@
 //             slice t+1, compute slice t, store slice t+1 to the other
 //             buffer, one barrier).
 //
-// Workgroup tile 128 x 128, K slice 8, 256 threads = 4 waves in a 2 x 2 grid,
-// each wave 64 x 64; lane l of a wave is (lr, lc) = (l / 8, l % 8).
+// Workgroup tile 128 x 128, K slice BK (8, or 16 in the default kernel), 256
+// threads = 4 waves in a 2 x 2 grid, each wave 64 x 64; lane l of a wave is
+// (lr, lc) = (l / 8, l % 8).
 //
 // Every C element is one fused multiply-add chain in increasing k, started
 // from zero: acc = fma(a_ik, b_kj, acc).  The K tail is zero-filled, and
@@ -32,61 +33,71 @@
 
 namespace tg {
 
-template <int STAGES, bool TRANS_A, bool QUARTERS, bool VEC_STORE>
+template <int STAGES, bool TRANS_A, bool QUARTERS, bool VEC_STORE, int BK_ = 8>
 struct F32Gemm {
-    static constexpr int BM = 128, BN = 128, BK = 8, NT = 256;
+    static constexpr int BM = 128, BN = 128, BK = BK_, NT = 256;
     static constexpr int A_BYTES = BK * BM * 4;
     static constexpr int B_BYTES = BK * BN * 4;
     static constexpr int SLOT = A_BYTES + B_BYTES;
     static constexpr int LDS_BYTES = STAGES * SLOT;
-    static constexpr int N_LD = 2;
+    static constexpr int PER = BK / 8;        // 16-byte pieces of A and of B per thread per slice
+    static constexpr int N_LD = 2 * PER;
+    static constexpr int AQ = BK / 4;         // pieces per A row of a slice
     static_assert(STAGES == 1 || STAGES == 2, "register-staged: 1 or 2 slots");
+    static_assert(BK % 8 == 0, "whole pieces per thread");
 
     struct Staged {
-        f32x4 a, b;
+        f32x4 a[PER], b[PER];
     };
 
-    // Thread t loads A[m0 + t/2][k0 + 4 (t%2) .. +3] and B[k0 + t/32][n0 + 4 (t%32) .. +3].
+    // Piece p = q NT + t (q < PER) of the slice: A[m0 + p / AQ][k0 + 4 (p % AQ) .. +3]
+    // and B[k0 + p / 32][n0 + 4 (p % 32) .. +3].
     __device__ static __forceinline__ void load(Staged& r, const GemmArgs& g, int m0, int n0, int k0,
                                                 bool guard_a, bool guard_b) {
         const float* A = static_cast<const float*>(g.A);
         const float* B = static_cast<const float*>(g.B);
-        const int t = threadIdx.x;
-        {
-            const float* rowp = A + (int64_t)min(m0 + (t >> 1), g.M - 1) * g.lda;
-            const int kc = k0 + 4 * (t & 1);
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int p = q * NT + threadIdx.x;
+            const float* rowp = A + (int64_t)min(m0 + p / AQ, g.M - 1) * g.lda;
+            const int kc = k0 + 4 * (p % AQ);
             if (!guard_a) {
-                r.a = *reinterpret_cast<const f32x4*>(rowp + kc);
+                r.a[q] = *reinterpret_cast<const f32x4*>(rowp + kc);
             } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) r.a[e] = kc + e < g.K ? rowp[kc + e] : 0.0f;
+                for (int e = 0; e < 4; ++e) r.a[q][e] = kc + e < g.K ? rowp[kc + e] : 0.0f;
             }
         }
-        {
-            const int gk = k0 + (t >> 5);
-            const int nc = n0 + 4 * (t & 31);
-            if (!guard_b) {
-                r.b = *reinterpret_cast<const f32x4*>(B + (int64_t)gk * g.ldb + min(nc, g.N - 4));
-            } else {
-                const float* rowp = B + (int64_t)gk * g.ldb;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) r.b[e] = (gk < g.K && nc + e < g.N) ? rowp[nc + e] : 0.0f;
+        for (int q = 0; q < PER; ++q) {
+            const int p = q * NT + threadIdx.x;
+            const int gk = k0 + (p >> 5);
+            const int nc = n0 + 4 * (p & 31);
+            if (!guard_b) {
+                r.b[q] = *reinterpret_cast<const f32x4*>(B + (int64_t)gk * g.ldb + min(nc, g.N - 4));
+            } else {
+                const float* rowp = B + (int64_t)min(gk, g.K - 1) * g.ldb;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) r.b[q][e] = (gk < g.K && nc + e < g.N) ? rowp[nc + e] : 0.0f;
             }
         }
     }
 
     __device__ static __forceinline__ void store(TG_LDS char* slot, const Staged& r) {
-        const int t = threadIdx.x;
         TG_LDS float* As = reinterpret_cast<TG_LDS float*>(slot);
         TG_LDS float* Bs = reinterpret_cast<TG_LDS float*>(slot + A_BYTES);
-        const int row = t >> 1, kq = 4 * (t & 1);
-        if constexpr (TRANS_A) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) As[(kq + e) * BM + row] = r.a[e];
-        } else {
-            *reinterpret_cast<TG_LDS f32x4*>(As + row * BK + kq) = r.a;
+        for (int q = 0; q < PER; ++q) {
+            const int p = q * NT + threadIdx.x;
+            const int row = p / AQ, kq = 4 * (p % AQ);
+            if constexpr (TRANS_A) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) As[(kq + e) * BM + row] = r.a[q][e];
+            } else {
+                *reinterpret_cast<TG_LDS f32x4*>(As + row * BK + kq) = r.a[q];
+            }
+            *reinterpret_cast<TG_LDS f32x4*>(Bs + (p >> 5) * BN + 4 * (p & 31)) = r.b[q];
         }
-        *reinterpret_cast<TG_LDS f32x4*>(Bs + (t >> 5) * BN + 4 * (t & 31)) = r.b;
     }
 
     // Row (column) offset of this lane's fragment element i within the tile.

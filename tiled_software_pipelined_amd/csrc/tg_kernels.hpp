@@ -114,9 +114,9 @@ KernelEntry thin_entry() {
 
 // fp32 ladder rungs: access / frag fields encode TRANS_A and QUARTERS, the
 // layout field VEC_STORE (see inst_f32.hip).
-template <int S, bool TA, bool QU, bool VS>
+template <int S, bool TA, bool QU, bool VS, int BK = 8>
 KernelEntry f32_entry() {
-    typedef F32Gemm<S, TA, QU, VS> K;
+    typedef F32Gemm<S, TA, QU, VS, BK> K;
     KernelEntry e{};
     e.dtype = 0;
     e.family = FAM_TILED;
@@ -139,7 +139,7 @@ KernelEntry f32_entry() {
     e.listed = 1;
     e.tail_ok = 1;
     e.fn = gemm_kernel<K, 2>;
-    snprintf(e.name, sizeof e.name, "f32_t128x128x8_w2x2_s%d_%s_%s_%s", S, TA ? "transA" : "rowA",
+    snprintf(e.name, sizeof e.name, "f32_t128x128x%d_w2x2_s%d_%s_%s_%s", BK, S, TA ? "transA" : "rowA",
              QU ? "quarters" : "blocks", VS ? "vecstore" : "scalarstore");
     return e;
 }
