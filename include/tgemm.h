@@ -202,6 +202,8 @@ typedef struct tgemm_plan_info {
     char rem_name[96];       /* split plans: the kernel of the last columns; else "" */
     char packed_name[96];    /* the kernel gemm_run_ws runs on repacked operands (its plan's
                                 `name`); "" for plans that carry no repack */
+    int32_t waves_per_simd;  /* occupancy the kernel is compiled for: its registers (VGPRs + AGPRs,
+                                512 per SIMD lane) leave room for at least this many waves per SIMD */
 } tgemm_plan_info;
 
 /* Fill *info for `plan`.  Returns TGEMM_OK or TGEMM_E_NULL. */

@@ -50,3 +50,17 @@ def test_split_plan_sums_its_kernels(tmp_path):
     write_scale = calib / res["copy"]["WRITE_SIZE"]
     assert fetch_scale == calib / (2.0 ** 28 / 2048.0)
     assert write_scale == calib / (2.0 ** 28 / 1024.0)
+
+
+def test_kernel_resources_from_trace():
+    rows = [{"Kernel_Name": "void tg::gemm_kernel<tg::MfmaGemm<...>, 2>(tg::GemmArgs)", "LDS_Block_Size": "131072",
+             "Scratch_Size": "0", "Workgroup_Size_X": "512", "Workgroup_Size_Y": "1", "Workgroup_Size_Z": "1"},
+            {"Kernel_Name": "tg::pack_rows(char const*, char*, long, long, long, long)", "LDS_Block_Size": "0",
+             "Scratch_Size": "0", "Workgroup_Size_X": "256", "Workgroup_Size_Y": "1", "Workgroup_Size_Z": "1"},
+            {"Kernel_Name": "elementwise_copy_kernel", "LDS_Block_Size": "0", "Scratch_Size": "0",
+             "Workgroup_Size_X": "128", "Workgroup_Size_Y": "1", "Workgroup_Size_Z": "1"}]
+    res = profiling.kernel_resources(rows)
+    assert set(res) == {rows[0]["Kernel_Name"], rows[1]["Kernel_Name"]}
+    main = res[rows[0]["Kernel_Name"]]
+    assert main["lds_bytes"] == 131072 and main["wg_per_cu_by_lds"] == 1 and main["threads"] == 512
+    assert res[rows[1]["Kernel_Name"]]["wg_per_cu_by_lds"] is None

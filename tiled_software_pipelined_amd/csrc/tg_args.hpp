@@ -50,6 +50,7 @@ struct KernelEntry {
     int shift_mask;  // operands it can read from rows that are not 16-byte aligned: bit 0 A, bit 1 B
     int listed;      // 0: only reached as the fallback of a listed entry for such operands
     int tail_ok;     // handles K not a multiple of bk
+    int waves_per_simd;  // occupancy the kernel is compiled for (its registers allow at least this)
     KernelFn fn;
     char name[96];
 };

@@ -45,6 +45,7 @@ KernelEntry mfma_entry(int dtype) {
     e.shift_mask = SHIFT;
     e.listed = SHIFT == 0;
     e.tail_ok = 1;
+    e.waves_per_simd = WAVES;
     e.fn = gemm_kernel<K, WAVES>;
     snprintf(e.name, sizeof e.name, "%s_t%dx%dx%d_w%dx%d_s%d_%s_%s_%s_%s%s", dtype_tag(dtype), BM, BN,
              BK, WM, WN, S, LD == LD_DIRECT ? "direct" : "vgpr", LY == LY_XOR ? "xor" : "plain",
@@ -76,6 +77,7 @@ KernelEntry naive_entry() {
     e.shift_mask = 3;  // element loads only
     e.listed = 1;
     e.tail_ok = 1;
+    e.waves_per_simd = 4;
     e.fn = gemm_kernel<K, 4>;
     snprintf(e.name, sizeof e.name, "%s_naive", dtype_tag(DT));
     return e;
@@ -107,6 +109,7 @@ KernelEntry thin_entry() {
     e.shift_mask = 3;  // element loads wherever a row is not aligned
     e.listed = 0;
     e.tail_ok = 1;
+    e.waves_per_simd = 2;
     e.fn = gemm_kernel<K, 2>;
     snprintf(e.name, sizeof e.name, "%s_thin_n%d", dtype_tag(DT), NB);
     return e;
@@ -138,6 +141,7 @@ KernelEntry f32_entry() {
     e.shift_mask = 3;  // its own guarded element loads
     e.listed = 1;
     e.tail_ok = 1;
+    e.waves_per_simd = 2;
     e.fn = gemm_kernel<K, 2>;
     snprintf(e.name, sizeof e.name, "f32_t128x128x%d_w2x2_s%d_%s_%s_%s", BK, S, TA ? "transA" : "rowA",
              QU ? "quarters" : "blocks", VS ? "vecstore" : "scalarstore");

@@ -665,6 +665,7 @@ int gemm_plan_get_info(const tgemm_plan* p, tgemm_plan_info* info) {
     if (p->packed) snprintf(info->packed_name, sizeof info->packed_name, "%s", p->packed->entry->name);
     info->threads = e.threads;
     info->lds_bytes = e.lds_bytes;
+    info->waves_per_simd = e.waves_per_simd;
     info->loads_per_stage = e.loads_per_stage;
     info->a_guarded = p->a_guard;
     info->b_guarded = p->b_guard;

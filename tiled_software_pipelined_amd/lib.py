@@ -52,7 +52,8 @@ class PlanInfo(ctypes.Structure):
                 ("threads", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
                 ("loads_per_stage", ctypes.c_int32), ("a_guarded", ctypes.c_int32),
                 ("b_guarded", ctypes.c_int32), ("name", ctypes.c_char * 96), ("n_main", ctypes.c_int64),
-                ("rem_name", ctypes.c_char * 96), ("packed_name", ctypes.c_char * 96)]
+                ("rem_name", ctypes.c_char * 96), ("packed_name", ctypes.c_char * 96),
+                ("waves_per_simd", ctypes.c_int32)]
 
 
 EXPORTS = ("gemm_plan", "gemm_plan_variant", "gemm_run", "gemm_destroy", "tgemm_last_error",

@@ -123,6 +123,9 @@ def summarize(args, cmds):
             res["avg_ns"] = sum(k["avg_ns"] for k in res["kernels"])
             res["min_ns"] = sum(k["min_ns"] for k in res["kernels"])
             res["max_ns"] = sum(k["max_ns"] for k in res["kernels"])
+    trace = _find(os.path.join(out, "trace"), "*kernel_trace.csv")
+    if trace:
+        res["resources"] = kernel_resources(_read_csv(trace))
     for i in range(len(GROUPS)):
         f = _find(os.path.join(out, "pmc%d" % i), "*counter_collection.csv")
         if not f:
@@ -150,6 +153,28 @@ def summarize(args, cmds):
     return res
 
 
+LDS_PER_CU = 160 * 1024      # bytes of LDS per compute unit
+
+
+def kernel_resources(trace_rows):
+    """Per GEMM kernel, from its first dispatch in a rocprofv3 kernel trace:
+    LDS bytes per workgroup (and how many workgroups fit a compute unit's
+    160 KiB), scratch bytes per lane (0: no register spills) and threads per
+    workgroup."""
+    out = {}
+    for r in trace_rows:
+        name = r.get("Kernel_Name", "")
+        if not _is_gemm(name) or name in out:
+            continue
+        lds = int(float(r.get("LDS_Block_Size", 0) or 0))
+        threads = 1
+        for d in ("X", "Y", "Z"):
+            threads *= int(float(r.get("Workgroup_Size_" + d, 1) or 1))
+        out[name] = {"lds_bytes": lds, "scratch": int(float(r.get("Scratch_Size", 0) or 0)), "threads": threads,
+                     "wg_per_cu_by_lds": LDS_PER_CU // lds if lds else None}
+    return out
+
+
 def _plan_name(args, w):
     from tiled_software_pipelined_amd import lib
     v = None
@@ -163,6 +188,28 @@ def _plan_name(args, w):
     # the leading dimensions decide whether the repacked plan's kernel runs
     aligned = 1 << 20
     return lib.Plan(w.M, w.N, w.K, code, variant=v).kernel_for(aligned, aligned, workspace=v is None)
+
+
+def _plan_occupancy(args, w):
+    """(waves-per-SIMD target, threads, LDS bytes, workgroups per CU, waves
+    per SIMD) of the plan's main kernel: the registers allow the target, the
+    LDS allows 160 KiB / LDS workgroups per CU."""
+    from tiled_software_pipelined_amd import lib
+    v = None
+    if args.variant:
+        v = lib.Variant()
+        for kv in args.variant.split(","):
+            k, val = kv.split("=")
+            setattr(v, k.strip(), int(val))
+    code = {"f32": lib.F32, "bf16": lib.BF16, "i8": lib.I8}[w.dtype]
+    info = lib.Plan(w.M, w.N, w.K, code, variant=v).info()
+    if not info.threads or not info.waves_per_simd:
+        return None
+    waves_per_wg = (info.threads + 63) // 64
+    by_regs = 4 * info.waves_per_simd // waves_per_wg
+    by_lds = LDS_PER_CU // info.lds_bytes if info.lds_bytes else by_regs
+    wg = min(by_regs, by_lds)
+    return (info.waves_per_simd, info.threads, info.lds_bytes, wg, wg * waves_per_wg / 4.0)
 
 
 def render(args, cmds, res):
@@ -201,6 +248,17 @@ def render(args, cmds, res):
             lines.append("| kernel | `%s`: %d dispatches, mean %.2f us |" % (k["name"], k["calls"],
                                                                         k["avg_ns"] / 1e3))
         lines.append("| dispatches traced | %d |" % res["calls"])
+        for kn, rr in res.get("resources", {}).items():
+            short = kn.split("(")[0].replace("void ", "")
+            lines.append("| resources of `%s` | LDS %d B per workgroup (%s per CU of 160 KiB), %d threads, "
+                         "scratch %d B per lane |" % (
+                             short, rr["lds_bytes"],
+                             rr["wg_per_cu_by_lds"] if rr["wg_per_cu_by_lds"] is not None else "no LDS limit",
+                             rr["threads"], rr["scratch"]))
+        occ = _plan_occupancy(args, w)
+        if occ:
+            lines.append("| occupancy of the main kernel | compiled for %d waves per SIMD (registers); "
+                         "%d threads and %d B of LDS per workgroup: %d per CU, %.1f waves per SIMD |" % occ)
         lines.append("| mean / min / max duration per GEMM | %.2f / %.2f / %.2f us |" % (
             res["avg_ns"] / 1e3, res["min_ns"] / 1e3, res["max_ns"] / 1e3))
         lines.append("| achieved (2MNK / mean) | %.1f TFLOP/s |" % (w.flops / t / 1e12))
