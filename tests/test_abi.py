@@ -100,6 +100,10 @@ def test_default_choice_by_shape():
     for M, K, dt, edge in [(4096, 512, tl.BF16, 256), (4096, 256, tl.BF16, 128), (3072, 512, tl.BF16, 256),
                            (6144, 512, tl.BF16, 128), (4096, 1024, tl.I8, 256), (4096, 512, tl.I8, 128)]:
         assert tl.Plan(M, M, K, dt).info().variant.tile_m == edge, (M, K, dt)
+    # 128 x 128 tiles filling at most half the CUs: half tiles, wide along the longer side
+    for M, N, tile in [(512, 4096, (64, 128)), (4096, 512, (128, 64))]:
+        v = tl.Plan(M, N, 4096, tl.BF16).info().variant
+        assert (v.tile_m, v.tile_n, v.stages) == tile + (4,), (M, N)
     # long K on the 128 x 128 tile: the deeper ring; on the 64 x 64 tile the
     # 8-slot ring
     assert tl.Plan(2048, 2048, 4096, tl.BF16).info().variant.stages == 4

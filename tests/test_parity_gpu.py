@@ -422,7 +422,7 @@ def _sample_positions(M, N, n, seed):
 
 FULL = ["bf16_4096", "i8_4096", "f32_4096", "bf16_ragged_4095x4097x4104",
         "bf16_sweep_4096x4096x256", "bf16_sweep_4096x4096x8192", "bf16_sweep_512x512x8192",
-        "f32_256"]
+        "f32_256", "bf16_msplit_512x4096x4096"]
 
 
 @pytest.mark.parametrize("name", FULL)

@@ -25,6 +25,10 @@ void register_bf16(void (*add)(const KernelEntry&)) {
     // a deep ring for small grids (about one workgroup per compute unit),
     // where each slice's load latency is exposed unless many are in flight
     add(mfma_entry<T, 64, 64, 64, 2, 2, 8, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 4>(1));
+    // half tiles: twice the workgroups where 128 x 128 tiles fill at most
+    // half the compute units
+    add(mfma_entry<T, 128, 64, 32, 2, 2, 4, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2>(1));
+    add(mfma_entry<T, 64, 128, 32, 2, 2, 4, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2>(1));
     // the 128 x 128 x 32 ladder, one change per step
     add(mfma_entry<T, 128, 128, 32, 2, 2, 3, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2>(1));
     add(mfma_entry<T, 128, 128, 32, 2, 2, 4, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2>(1));

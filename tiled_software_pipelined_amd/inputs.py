@@ -110,4 +110,7 @@ def workloads() -> dict:
     w["f32_4096"] = Workload("f32_4096", "f32", 4096, 4096, 4096, "f32_uniform", 5000)
     w["bf16_ragged_4095x4097x4104"] = Workload("bf16_ragged_4095x4097x4104", "bf16",
                                                4095, 4097, 4104, "bf16_uniform", 5100)
+    # one GPU's share of bf16 4096^3 split over 8 GPUs by rows of A and C
+    w["bf16_msplit_512x4096x4096"] = Workload("bf16_msplit_512x4096x4096", "bf16", 512, 4096, 4096,
+                                              "bf16_normal", 5200)
     return w
