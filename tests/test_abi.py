@@ -91,10 +91,14 @@ def test_default_choice_by_shape():
     assert (big.variant.tile_m, big.variant.tile_n, big.variant.tile_k) == (256, 256, 64)
     assert (big.variant.waves_m, big.variant.waves_n) == (2, 4)
     assert big.variant.loader == tl.LOADER_DIRECT and big.grid == 256
-    mid = tl.Plan(1024, 1024, 512, tl.BF16).info()
-    assert (mid.variant.tile_m, mid.variant.tile_n) == (128, 128) and mid.grid == 64
+    mid = tl.Plan(2048, 2048, 512, tl.BF16).info()
+    assert (mid.variant.tile_m, mid.variant.tile_n) == (128, 128) and mid.grid == 256
     assert mid.variant.stages == 4
-    assert tl.Plan(1024, 1024, 256, tl.BF16).info().variant.stages == 3
+    assert tl.Plan(2048, 2048, 256, tl.BF16).info().variant.stages == 3
+    # 128 x 128 tiles filling a quarter of the CUs or fewer: 64 x 64
+    for dtype in (tl.BF16, tl.I8):
+        q = tl.Plan(1024, 1024, 4096, dtype).info()
+        assert (q.variant.tile_m, q.variant.tile_n, q.variant.stages, q.grid) == (64, 64, 8, 256), dtype
     # one round of 256 x 256 tiles from K = 512 (int8: 1024); several rounds
     # at short K stay on 128 x 128
     for M, K, dt, edge in [(4096, 512, tl.BF16, 256), (4096, 256, tl.BF16, 128), (3072, 512, tl.BF16, 256),
