@@ -117,8 +117,12 @@ def test_default_choice_by_shape():
         assert tl.Plan(512, 512, 1024, dtype).info().variant.stages == 3
     small = tl.Plan(512, 512, 512, tl.BF16).info()
     assert (small.variant.tile_m, small.variant.tile_n) == (64, 64) and small.grid == 64
+    # fp32: 64 x 64 tiles while 128 x 128 ones would give one per CU or fewer
     f = tl.Plan(256, 256, 256, tl.F32).info()
-    assert f.variant.tile_k == 16 and f.grid == 4
+    assert (f.variant.tile_m, f.variant.tile_k, f.grid) == (64, 16, 16)
+    assert tl.Plan(2048, 2048, 2048, tl.F32).info().variant.tile_m == 64
+    f = tl.Plan(4096, 4096, 4096, tl.F32).info()
+    assert (f.variant.tile_m, f.variant.tile_k, f.grid) == (128, 16, 1024)
 
 
 def test_unaligned_leading_dimension_uses_guarded_register_loader():

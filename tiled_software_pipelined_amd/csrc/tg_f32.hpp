@@ -19,9 +19,12 @@
 //             slice t+1, compute slice t, store slice t+1 to the other
 //             buffer, one barrier).
 //
-// Workgroup tile 128 x 128, K slice BK (8, or 16 in the default kernel), 256
-// threads = 4 waves in a 2 x 2 grid, each wave 64 x 64; lane l of a wave is
-// (lr, lc) = (l / 8, l % 8).
+// Workgroup tile TILE x TILE (128, or 64 for grids too small to fill the
+// compute units), K slice BK (8, or 16 in the default kernel), 256 threads =
+// 4 waves in a 2 x 2 grid, each wave TILE/2 x TILE/2; lane l of a wave is
+// (lr, lc) = (l / 8, l % 8) and owns TM x TM outputs, TM = TILE / 16.  The
+// 64 x 64 tile spreads a product over four times the SIMDs of the 128 x 128
+// one: on the vector ALUs a wave's time is set by its count of FMAs.
 //
 // Every C element is one fused multiply-add chain in increasing k, started
 // from zero: acc = fma(a_ik, b_kj, acc).  The K tail is zero-filled, and
@@ -33,25 +36,28 @@
 
 namespace tg {
 
-template <int STAGES, bool TRANS_A, bool QUARTERS, bool VEC_STORE, int BK_ = 8>
+template <int STAGES, bool TRANS_A, bool QUARTERS, bool VEC_STORE, int BK_ = 8, int TILE = 128>
 struct F32Gemm {
-    static constexpr int BM = 128, BN = 128, BK = BK_, NT = 256;
+    static constexpr int BM = TILE, BN = TILE, BK = BK_, NT = 256;
+    static constexpr int TM = TILE / 16;      // outputs per lane along each side
     static constexpr int A_BYTES = BK * BM * 4;
     static constexpr int B_BYTES = BK * BN * 4;
     static constexpr int SLOT = A_BYTES + B_BYTES;
     static constexpr int LDS_BYTES = STAGES * SLOT;
-    static constexpr int PER = BK / 8;        // 16-byte pieces of A and of B per thread per slice
+    static constexpr int PER = BK * TILE / 4 / NT;  // 16-byte pieces of A and of B per thread per slice
     static constexpr int N_LD = 2 * PER;
     static constexpr int AQ = BK / 4;         // pieces per A row of a slice
+    static constexpr int BQ = BN / 4;         // pieces per B row of a slice
     static_assert(STAGES == 1 || STAGES == 2, "register-staged: 1 or 2 slots");
-    static_assert(BK % 8 == 0, "whole pieces per thread");
+    static_assert(TILE == 128 || TILE == 64, "lane blocks of 8 x 8 or 4 x 4");
+    static_assert(PER >= 1 && (BK * TILE / 4) % NT == 0, "whole pieces per thread");
 
     struct Staged {
         f32x4 a[PER], b[PER];
     };
 
     // Piece p = q NT + t (q < PER) of the slice: A[m0 + p / AQ][k0 + 4 (p % AQ) .. +3]
-    // and B[k0 + p / 32][n0 + 4 (p % 32) .. +3].
+    // and B[k0 + p / BQ][n0 + 4 (p % BQ) .. +3].
     __device__ static __forceinline__ void load(Staged& r, const GemmArgs& g, int m0, int n0, int k0,
                                                 bool guard_a, bool guard_b) {
         const float* A = static_cast<const float*>(g.A);
@@ -71,8 +77,8 @@ struct F32Gemm {
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
             const int p = q * NT + threadIdx.x;
-            const int gk = k0 + (p >> 5);
-            const int nc = n0 + 4 * (p & 31);
+            const int gk = k0 + p / BQ;
+            const int nc = n0 + 4 * (p % BQ);
             if (!guard_b) {
                 r.b[q] = *reinterpret_cast<const f32x4*>(B + (int64_t)gk * g.ldb + min(nc, g.N - 4));
             } else {
@@ -96,18 +102,19 @@ struct F32Gemm {
             } else {
                 *reinterpret_cast<TG_LDS f32x4*>(As + row * BK + kq) = r.a[q];
             }
-            *reinterpret_cast<TG_LDS f32x4*>(Bs + (p >> 5) * BN + 4 * (p & 31)) = r.b[q];
+            *reinterpret_cast<TG_LDS f32x4*>(Bs + (p / BQ) * BN + 4 * (p % BQ)) = r.b[q];
         }
     }
 
     // Row (column) offset of this lane's fragment element i within the tile.
+    // (With TM = 4 both forms are the lane's 4 contiguous rows.)
     __device__ static __forceinline__ int frag_off(int base, int idx, int i) {
         if constexpr (QUARTERS) return base + 4 * idx + (i & 3) + 32 * (i >> 2);
-        else return base + 8 * idx + i;
+        else return base + TM * idx + i;
     }
 
     struct Frag {
-        float a[8], b[8];
+        float a[TM], b[TM];
     };
 
     __device__ static __forceinline__ void read_frag(Frag& f, const TG_LDS char* slot, int k, int wm, int wn,
@@ -115,19 +122,21 @@ struct F32Gemm {
         const TG_LDS float* As = reinterpret_cast<const TG_LDS float*>(slot);
         const TG_LDS float* Bs = reinterpret_cast<const TG_LDS float*>(slot + A_BYTES);
         if constexpr (TRANS_A) {
-            // rows frag_off(wm, lr, 0..3) and frag_off(wm, lr, 4..7) are each 4 contiguous
-            const f32x4 a0 = *reinterpret_cast<const TG_LDS f32x4*>(As + k * BM + frag_off(wm, lr, 0));
-            const f32x4 a1 = *reinterpret_cast<const TG_LDS f32x4*>(As + k * BM + frag_off(wm, lr, 4));
-            f.a[0] = a0.x; f.a[1] = a0.y; f.a[2] = a0.z; f.a[3] = a0.w;
-            f.a[4] = a1.x; f.a[5] = a1.y; f.a[6] = a1.z; f.a[7] = a1.w;
+            // rows frag_off(wm, lr, 4h .. 4h+3) are 4 contiguous for each h
+#pragma unroll
+            for (int h = 0; h < TM / 4; ++h) {
+                const f32x4 a = *reinterpret_cast<const TG_LDS f32x4*>(As + k * BM + frag_off(wm, lr, 4 * h));
+                f.a[4 * h] = a.x; f.a[4 * h + 1] = a.y; f.a[4 * h + 2] = a.z; f.a[4 * h + 3] = a.w;
+            }
         } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) f.a[i] = As[frag_off(wm, lr, i) * BK + k];
+            for (int i = 0; i < TM; ++i) f.a[i] = As[frag_off(wm, lr, i) * BK + k];
         }
-        const f32x4 b0 = *reinterpret_cast<const TG_LDS f32x4*>(Bs + k * BN + frag_off(wn, lc, 0));
-        const f32x4 b1 = *reinterpret_cast<const TG_LDS f32x4*>(Bs + k * BN + frag_off(wn, lc, 4));
-        f.b[0] = b0.x; f.b[1] = b0.y; f.b[2] = b0.z; f.b[3] = b0.w;
-        f.b[4] = b1.x; f.b[5] = b1.y; f.b[6] = b1.z; f.b[7] = b1.w;
+#pragma unroll
+        for (int h = 0; h < TM / 4; ++h) {
+            const f32x4 b = *reinterpret_cast<const TG_LDS f32x4*>(Bs + k * BN + frag_off(wn, lc, 4 * h));
+            f.b[4 * h] = b.x; f.b[4 * h + 1] = b.y; f.b[4 * h + 2] = b.z; f.b[4 * h + 3] = b.w;
+        }
     }
 
     // End of one outer-product step: an empty asm that takes every
@@ -135,23 +144,33 @@ struct F32Gemm {
     // stay before it, the next step's after it, and the LDS reads issued for
     // the step after next cannot be hoisted above it (neither the FMAs nor
     // plain LDS loads are ordered by a scheduling barrier alone).
-    __device__ static __forceinline__ void step_fence(float (&c)[8][8]) {
+    __device__ static __forceinline__ void step_fence(float (&c)[TM][TM]) {
+        if constexpr (TM == 8) {
 #pragma unroll
-        for (int i = 0; i < 8; i += 2)
+            for (int i = 0; i < 8; i += 2)
+                asm volatile(""
+                             : "+v"(c[i][0]), "+v"(c[i][1]), "+v"(c[i][2]), "+v"(c[i][3]), "+v"(c[i][4]),
+                               "+v"(c[i][5]), "+v"(c[i][6]), "+v"(c[i][7]), "+v"(c[i + 1][0]), "+v"(c[i + 1][1]),
+                               "+v"(c[i + 1][2]), "+v"(c[i + 1][3]), "+v"(c[i + 1][4]), "+v"(c[i + 1][5]),
+                               "+v"(c[i + 1][6]), "+v"(c[i + 1][7])
+                             :
+                             : "memory");
+        } else {
             asm volatile(""
-                         : "+v"(c[i][0]), "+v"(c[i][1]), "+v"(c[i][2]), "+v"(c[i][3]), "+v"(c[i][4]),
-                           "+v"(c[i][5]), "+v"(c[i][6]), "+v"(c[i][7]), "+v"(c[i + 1][0]), "+v"(c[i + 1][1]),
-                           "+v"(c[i + 1][2]), "+v"(c[i + 1][3]), "+v"(c[i + 1][4]), "+v"(c[i + 1][5]),
-                           "+v"(c[i + 1][6]), "+v"(c[i + 1][7])
+                         : "+v"(c[0][0]), "+v"(c[0][1]), "+v"(c[0][2]), "+v"(c[0][3]), "+v"(c[1][0]),
+                           "+v"(c[1][1]), "+v"(c[1][2]), "+v"(c[1][3]), "+v"(c[2][0]), "+v"(c[2][1]),
+                           "+v"(c[2][2]), "+v"(c[2][3]), "+v"(c[3][0]), "+v"(c[3][1]), "+v"(c[3][2]),
+                           "+v"(c[3][3])
                          :
                          : "memory");
+        }
     }
 
-    // The slice's BK outer products, each lane's 8 x 8 block at a time.  The
-    // fragments of step k+1 are read while the 64 FMAs of step k issue, and a
+    // The slice's BK outer products, each lane's TM x TM block at a time.  The
+    // fragments of step k+1 are read while the TM^2 FMAs of step k issue, and a
     // fence per step keeps the compiler from hoisting the reads of the whole
     // slice ahead (which took 219 registers and limited a SIMD to 2 waves).
-    __device__ static __forceinline__ void compute(const TG_LDS char* slot, float (&c)[8][8], int wm, int wn,
+    __device__ static __forceinline__ void compute(const TG_LDS char* slot, float (&c)[TM][TM], int wm, int wn,
                                                    int lr, int lc) {
         Frag f[2];
         read_frag(f[0], slot, 0, wm, wn, lr, lc);
@@ -160,9 +179,9 @@ struct F32Gemm {
             if (k + 1 < BK) read_frag(f[(k + 1) & 1], slot, k + 1, wm, wn, lr, lc);
             const Frag& x = f[k & 1];
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int j = 0; j < 8; ++j) c[i][j] = __builtin_fmaf(x.a[i], x.b[j], c[i][j]);
+                for (int j = 0; j < TM; ++j) c[i][j] = __builtin_fmaf(x.a[i], x.b[j], c[i][j]);
             step_fence(c);
         }
     }
@@ -175,13 +194,13 @@ struct F32Gemm {
         const int m0 = tm * BM, n0 = tn * BN;
         const int wave = wave_id(), lane = lane_id();
         const int lr = lane >> 3, lc = lane & 7;
-        const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+        const int wm = (wave >> 1) * (BM / 2), wn = (wave & 1) * (BN / 2);
 
-        float c[8][8];
+        float c[TM][TM];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) c[i][j] = 0.0f;
+            for (int j = 0; j < TM; ++j) c[i][j] = 0.0f;
 
         const int tiles = (g.K + BK - 1) / BK;
         const int full = g.K / BK;
@@ -217,17 +236,17 @@ struct F32Gemm {
         const bool vec_ok = VEC_STORE && (m0 + BM <= g.M) && (n0 + BN <= g.N) && (g.ldc % 4 == 0) &&
                             ((reinterpret_cast<uintptr_t>(C) & 15) == 0);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < TM; ++i) {
             const int row = m0 + frag_off(wm, lr, i);
             if (vec_ok) {
-                // columns frag_off(wn, lc, 0..3) and (4..7) are 4 contiguous each
-                *reinterpret_cast<f32x4*>(C + (int64_t)row * g.ldc + n0 + frag_off(wn, lc, 0)) =
-                    f32x4{c[i][0], c[i][1], c[i][2], c[i][3]};
-                *reinterpret_cast<f32x4*>(C + (int64_t)row * g.ldc + n0 + frag_off(wn, lc, 4)) =
-                    f32x4{c[i][4], c[i][5], c[i][6], c[i][7]};
+                // columns frag_off(wn, lc, 4h .. 4h+3) are 4 contiguous for each h
+#pragma unroll
+                for (int h = 0; h < TM / 4; ++h)
+                    *reinterpret_cast<f32x4*>(C + (int64_t)row * g.ldc + n0 + frag_off(wn, lc, 4 * h)) =
+                        f32x4{c[i][4 * h], c[i][4 * h + 1], c[i][4 * h + 2], c[i][4 * h + 3]};
             } else {
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
+                for (int j = 0; j < TM; ++j) {
                     const int col = n0 + frag_off(wn, lc, j);
                     if (row < g.M && col < g.N) C[(int64_t)row * g.ldc + col] = c[i][j];
                 }

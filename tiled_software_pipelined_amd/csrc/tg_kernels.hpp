@@ -117,9 +117,12 @@ KernelEntry thin_entry() {
 
 // fp32 ladder rungs: access / frag fields encode TRANS_A and QUARTERS, the
 // layout field VEC_STORE (see inst_f32.hip).
-template <int S, bool TA, bool QU, bool VS, int BK = 8>
+template <int S, bool TA, bool QU, bool VS, int BK = 8, int TILE = 128>
 KernelEntry f32_entry() {
-    typedef F32Gemm<S, TA, QU, VS, BK> K;
+    typedef F32Gemm<S, TA, QU, VS, BK, TILE> K;
+    // 8 x 8 outputs per lane take ~140 registers (3 waves per SIMD); 4 x 4
+    // take few enough for 4
+    constexpr int WAVES = TILE == 128 ? 2 : 4;
     KernelEntry e{};
     e.dtype = 0;
     e.family = FAM_TILED;
@@ -141,9 +144,9 @@ KernelEntry f32_entry() {
     e.shift_mask = 3;  // its own guarded element loads
     e.listed = 1;
     e.tail_ok = 1;
-    e.waves_per_simd = 2;
-    e.fn = gemm_kernel<K, 2>;
-    snprintf(e.name, sizeof e.name, "f32_t128x128x%d_w2x2_s%d_%s_%s_%s", BK, S, TA ? "transA" : "rowA",
+    e.waves_per_simd = WAVES;
+    e.fn = gemm_kernel<K, WAVES>;
+    snprintf(e.name, sizeof e.name, "f32_t%dx%dx%d_w2x2_s%d_%s_%s_%s", TILE, TILE, BK, S, TA ? "transA" : "rowA",
              QU ? "quarters" : "blocks", VS ? "vecstore" : "scalarstore");
     return e;
 }

@@ -153,8 +153,16 @@ double model_rounds(const KernelEntry& e, int64_t M, int64_t N) {
 const KernelEntry* default_entry(int dtype, int64_t M, int64_t N, int64_t K, bool guarded) {
     tgemm_variant v{};
     v.kernel = TGEMM_KERNEL_TILED;
-    if (dtype == TGEMM_F32) return find_entry(dtype, v);
     auto wgs = [&](int t) { return ((M + t - 1) / t) * ((N + t - 1) / t); };
+    if (dtype == TGEMM_F32) {
+        // One 128 x 128 tile per compute unit or fewer: 64 x 64 tiles, four
+        // times the workgroups.  A wave's time on the vector ALUs is its
+        // count of FMAs, so spreading the product over more SIMDs is what
+        // pays: 1024^3 60 vs 154 us, 256^3 17 vs 42, 2048^3 239 vs 308;
+        // 4096^3 stays on 128 x 128 (1565 vs 1745).
+        if (wgs(128) <= 256) v.tile_m = v.tile_n = 64;
+        return find_entry(dtype, v);
+    }
     v.access = TGEMM_ACCESS_WIDE;
     v.frag = TGEMM_FRAG_REUSE;
     v.lds_layout = TGEMM_LDS_XOR;
@@ -194,7 +202,7 @@ const KernelEntry* default_entry(int dtype, int64_t M, int64_t N, int64_t K, boo
     else if (wgs(128) > 64 || guarded)
         pick = 128;
     else
-        pick = 64;  // a quarter of the CUs or fewer on 128 x 128 (1024^2 x 4096: 22.3 vs 32.4 us)
+        pick = 64;  // a quarter of the CUs or fewer on 128 x 128 (1024^2 x 4096: 19.4 vs 32.7 us)
     if (pick == 96) {
         // 128 x 128 tiles would fill between a quarter and half of the
         // compute units; half tiles fill them (bf16 512 x 4096 x 4096: 64 x
