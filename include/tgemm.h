@@ -209,6 +209,17 @@ typedef struct tgemm_plan_info {
 /* Fill *info for `plan`.  Returns TGEMM_OK or TGEMM_E_NULL. */
 int gemm_plan_get_info(const tgemm_plan* plan, tgemm_plan_info* info);
 
+/* Occupancy of a plan's main kernel (a diagnostic for profile summaries, not
+ * needed to run a plan): *workgroups_per_cu receives how many of its
+ * workgroups one compute unit holds at once, as the HIP runtime's occupancy
+ * calculator gives it from the kernel's registers, LDS and threads.
+ * packed = 0: the kernel gemm_run launches; packed = 1: the kernel gemm_run_ws
+ * launches after repacking (the same one when the plan has no repacked
+ * form).  Needs the current device to be the gfx950 GPU the plan runs on.
+ * Returns TGEMM_OK, TGEMM_E_NULL for a NULL argument, or a positive
+ * hipError_t from the runtime. */
+int gemm_kernel_occupancy(const tgemm_plan* plan, int32_t packed, int32_t* workgroups_per_cu);
+
 /* Enumerate the variants compiled into the library for `dtype`.
  * gemm_variant_count returns how many; gemm_variant_get copies the i-th one
  * (0 <= i < count) and returns TGEMM_OK, or TGEMM_E_ARG for a bad index. */

@@ -56,6 +56,13 @@ def test_plan_run_rejects_null_plan():
     assert "NULL" in tl.last_error()
 
 
+def test_occupancy_rejects_null_arguments():
+    n = ctypes.c_int32(-1)
+    assert tl._lib.gemm_kernel_occupancy(None, 0, ctypes.byref(n)) == -2 and n.value == -1
+    p = tl.Plan(64, 64, 64, tl.BF16)
+    assert tl._lib.gemm_kernel_occupancy(p._h, 0, None) == -2
+
+
 def test_run_with_empty_output_is_a_noop_without_device():
     # M = 0: nothing to do, returns before touching the device
     p = tl.Plan(0, 16, 16, tl.BF16)

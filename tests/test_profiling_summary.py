@@ -64,3 +64,26 @@ def test_kernel_resources_from_trace():
     main = res[rows[0]["Kernel_Name"]]
     assert main["lds_bytes"] == 131072 and main["wg_per_cu_by_lds"] == 1 and main["threads"] == 512
     assert res[rows[1]["Kernel_Name"]]["wg_per_cu_by_lds"] is None
+
+
+def test_runtime_occupancy_line(tmp_path):
+    # the collected workgroups-per-CU figure is used only for the kernel the
+    # plan runs, with threads and LDS from the trace
+    import json
+
+    out = tmp_path / "prof"
+    os.makedirs(out)
+    args = types.SimpleNamespace(out=str(out), workload="bf16_4096", variant="", steps=20, warmup=5)
+    from tiled_software_pipelined_amd import inputs
+    w = inputs.workloads()["bf16_4096"]
+    kname = profiling._plan_name(args, w)
+    main = "void tg::gemm_kernel<tg::MfmaGemm<...>, 2>(tg::GemmArgs)"
+    res = {"kernel": main, "resources": {main: {"threads": 512, "lds_bytes": 131072, "scratch": 0,
+                                               "wg_per_cu_by_lds": 1}}}
+    assert profiling._runtime_occupancy(args, w, res) is None  # nothing recorded
+    with open(out / profiling.OCC_FILE, "w") as f:
+        json.dump({"kernel": kname, "workgroups_per_cu": 1}, f)
+    assert profiling._runtime_occupancy(args, w, res) == (512, 131072, 1, 2.0)
+    with open(out / profiling.OCC_FILE, "w") as f:
+        json.dump({"kernel": "some_other_kernel", "workgroups_per_cu": 3}, f)
+    assert profiling._runtime_occupancy(args, w, res) is None

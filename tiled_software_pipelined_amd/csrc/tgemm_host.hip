@@ -698,6 +698,23 @@ int gemm_plan_get_info(const tgemm_plan* p, tgemm_plan_info* info) {
     return TGEMM_OK;
 }
 
+int gemm_kernel_occupancy(const tgemm_plan* p, int32_t packed, int32_t* workgroups_per_cu) {
+    if (!p || !workgroups_per_cu) {
+        set_err("NULL plan or output");
+        return TGEMM_E_NULL;
+    }
+    const KernelEntry& e = (packed && p->packed) ? *p->packed->entry : *p->entry;
+    int n = 0;
+    const hipError_t err =
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(e.fn), e.threads, 0);
+    if (err != hipSuccess) {
+        set_err("hipOccupancyMaxActiveBlocksPerMultiprocessor: %s", hipGetErrorString(err));
+        return (int)err;
+    }
+    *workgroups_per_cu = n;
+    return TGEMM_OK;
+}
+
 int gemm_variant_count(int32_t dtype) {
     init_registry();
     if (dtype < 0 || dtype > 2) return 0;

@@ -58,7 +58,8 @@ class PlanInfo(ctypes.Structure):
 
 EXPORTS = ("gemm_plan", "gemm_plan_variant", "gemm_run", "gemm_destroy", "tgemm_last_error",
            "gemm_plan_get_info", "gemm_variant_count", "gemm_variant_get", "tgemm_version",
-           "tgemm_lds_read_probe", "tgemm_mfma_rate_probe", "gemm_workspace_bytes", "gemm_run_ws")
+           "tgemm_lds_read_probe", "tgemm_mfma_rate_probe", "gemm_workspace_bytes", "gemm_run_ws",
+           "gemm_kernel_occupancy")
 
 
 def _load():
@@ -82,6 +83,8 @@ def _load():
     lib.tgemm_last_error.argtypes = []
     lib.tgemm_last_error.restype = ctypes.c_char_p
     lib.gemm_plan_get_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]
+    lib.gemm_kernel_occupancy.argtypes = [vp, i32, ctypes.POINTER(i32)]
+    lib.gemm_kernel_occupancy.restype = ctypes.c_int
     lib.gemm_plan_get_info.restype = ctypes.c_int
     lib.gemm_variant_count.argtypes = [i32]
     lib.gemm_variant_count.restype = ctypes.c_int
@@ -214,6 +217,15 @@ class Plan:
         if workspace and self.workspace_bytes(A, B) > 0:
             return info.packed_name.decode()
         return info.name.decode()
+
+    def occupancy(self, packed: bool = False) -> int:
+        """Workgroups of the main kernel (packed: the repacked plan's) that one
+        compute unit holds at once, from the HIP runtime's calculator (GPU only)."""
+        n = ctypes.c_int32(0)
+        rc = _lib.gemm_kernel_occupancy(self._h, 1 if packed else 0, ctypes.byref(n))
+        if rc != OK:
+            raise TgemmError(rc, last_error())
+        return int(n.value)
 
     def run_ptr(self, A: int, B: int, C: int, stream: int = 0) -> None:
         """Enqueue on raw device pointers (the caller keeps the buffers alive)."""

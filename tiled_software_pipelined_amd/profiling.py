@@ -18,6 +18,7 @@ from __future__ import annotations
 import argparse
 import csv
 import glob
+import json
 import os
 import shlex
 import subprocess
@@ -36,6 +37,8 @@ GROUPS = [
     ["TCC_HIT_sum", "TCC_MISS_sum"],
 ]
 CALIB_MIB = 256
+# the main kernel's workgroups per compute unit, from the HIP runtime
+OCC_FILE = "occupancy.json"
 
 
 def _bench_cmd(args, steps, warmup, calib=False):
@@ -53,7 +56,7 @@ def _run(cmd, limit, log):
     with open(log, "a") as f:
         f.write("+ " + " ".join(shlex.quote(c) for c in cmd) + "\n")
         f.flush()
-        r = subprocess.run(["timeout", "-s", "KILL", str(limit)] + cmd, stdout=f, stderr=subprocess.STDOUT)
+        r = subprocess.run(["timeout", "-s", "KILL", str(limit)] + cmd, stdout=f, stderr=subprocess.STDOUT, cwd=ROOT)
     # rocprofv3 may end with a segfault after the program's results are written
     return r.returncode
 
@@ -99,7 +102,39 @@ def collect(args):
     cmds = build_cmds(args)
     for name, cmd in cmds.items():
         _run(cmd, 240 if name == "trace" else 120, log)
+    # the occupancy query initialises the GPU, so it runs in a child process
+    # of its own (this process starts the profiler runs and touches no GPU)
+    occ = [sys.executable, "-m", "tiled_software_pipelined_amd.profiling", "--workload", args.workload,
+           "--out", out, "--write-occupancy"] + (["--variant", args.variant] if args.variant else [])
+    _run(occ, 120, log)
     return cmds
+
+
+def _plan(args, w):
+    from tiled_software_pipelined_amd import lib
+    v = None
+    if args.variant:
+        v = lib.Variant()
+        for kv in args.variant.split(","):
+            k, val = kv.split("=")
+            setattr(v, k.strip(), int(val))
+    code = {"f32": lib.F32, "bf16": lib.BF16, "i8": lib.I8}[w.dtype]
+    return lib.Plan(w.M, w.N, w.K, code, variant=v), v is None
+
+
+def write_occupancy(args):
+    """Record the HIP runtime's workgroups-per-CU figure for the kernel the
+    profiled runs launch (GPU only)."""
+    from tiled_software_pipelined_amd import inputs
+    w = inputs.workloads()[args.workload]
+    plan, default = _plan(args, w)
+    aligned = 1 << 20
+    packed = default and plan.workspace_bytes(aligned, aligned) > 0
+    rec = {"kernel": _plan_name(args, w), "workgroups_per_cu": plan.occupancy(packed)}
+    os.makedirs(args.out, exist_ok=True)
+    with open(os.path.join(args.out, OCC_FILE), "w") as f:
+        json.dump(rec, f)
+    print(rec, flush=True)
 
 
 def summarize(args, cmds):
@@ -190,6 +225,22 @@ def _plan_name(args, w):
     return lib.Plan(w.M, w.N, w.K, code, variant=v).kernel_for(aligned, aligned, workspace=v is None)
 
 
+def _runtime_occupancy(args, w, res):
+    """(threads, LDS bytes, workgroups per CU, waves per SIMD) of the main
+    kernel as the HIP runtime's calculator gave them during collection, or
+    None.  Threads and LDS come from the kernel trace."""
+    path = os.path.join(args.out, OCC_FILE)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    rr = res.get("resources", {}).get(res.get("kernel", ""))
+    if rec.get("kernel") != _plan_name(args, w) or not rr:
+        return None
+    wg = int(rec["workgroups_per_cu"])
+    return (rr["threads"], rr["lds_bytes"], wg, wg * ((rr["threads"] + 63) // 64) / 4.0)
+
+
 def _plan_occupancy(args, w):
     """(waves-per-SIMD target, threads, LDS bytes, workgroups per CU, waves
     per SIMD) of the plan's main kernel: the registers allow the target, the
@@ -255,7 +306,12 @@ def render(args, cmds, res):
                              short, rr["lds_bytes"],
                              rr["wg_per_cu_by_lds"] if rr["wg_per_cu_by_lds"] is not None else "no LDS limit",
                              rr["threads"], rr["scratch"]))
-        occ = _plan_occupancy(args, w)
+        rocc = _runtime_occupancy(args, w, res)
+        occ = None if rocc else _plan_occupancy(args, w)
+        if rocc:
+            lines.append("| occupancy of the main kernel | %d threads and %d B of LDS per workgroup; the HIP "
+                         "occupancy calculator (registers, LDS, threads): %d workgroups per CU, %.1f waves "
+                         "per SIMD |" % rocc)
         if occ:
             lines.append("| occupancy of the main kernel | compiled for %d waves per SIMD (registers); "
                          "%d threads and %d B of LDS per workgroup: %d per CU, %.1f waves per SIMD |" % occ)
@@ -302,9 +358,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--summary", default="")
     ap.add_argument("--summarize-only", action="store_true")
+    ap.add_argument("--write-occupancy", action="store_true")
     args = ap.parse_args()
     sys.path.insert(0, ROOT)
     os.environ.setdefault("TMPDIR", "/tmp")
+    if args.write_occupancy:
+        write_occupancy(args)
+        return
     cmds = build_cmds(args) if args.summarize_only else collect(args)
     res = summarize(args, cmds)
     text = render(args, cmds, res)
