@@ -114,7 +114,12 @@ def test_default_choice_by_shape():
     # 128 x 128 tiles filling at most half the CUs: half tiles, wide along the longer side
     for M, N, tile in [(512, 4096, (64, 128)), (4096, 512, (128, 64))]:
         v = tl.Plan(M, N, 4096, tl.BF16).info().variant
-        assert (v.tile_m, v.tile_n, v.stages) == tile + (4,), (M, N)
+        assert (v.tile_m, v.tile_n, v.tile_k, v.stages) == tile + (32, 4), (M, N)
+        v = tl.Plan(M, N, 4096, tl.I8).info().variant
+        assert (v.tile_m, v.tile_n, v.tile_k, v.stages) == tile + (64, 4), (M, N)
+    # int8 from K = 2048 only
+    assert tl.Plan(512, 4096, 1024, tl.I8).info().variant.tile_m == 128
+    assert tl.Plan(512, 4096, 1024, tl.BF16).info().variant.tile_m == 64
     # long K on the 128 x 128 tile: the deeper ring; on the 64 x 64 tile the
     # 8-slot ring
     assert tl.Plan(2048, 2048, 4096, tl.BF16).info().variant.stages == 4

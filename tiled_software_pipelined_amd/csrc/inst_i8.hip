@@ -17,6 +17,10 @@ void register_i8(void (*add)(const KernelEntry&)) {
     add(mfma_entry<T, 128, 128, 64, 2, 2, 1, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2>(2));
     add(mfma_entry<T, 64, 64, 128, 2, 2, 3, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 4>(2));
     add(mfma_entry<T, 64, 64, 128, 2, 2, 8, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 4>(2));
+    // half tiles: twice the workgroups where 128 x 128 tiles fill at most
+    // half the compute units
+    add(mfma_entry<T, 128, 64, 64, 2, 2, 4, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2>(2));
+    add(mfma_entry<T, 64, 128, 64, 2, 2, 4, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2>(2));
     add(mfma_entry<T, 128, 128, 64, 2, 2, 1, LD_VGPR, LY_PLAIN, AC_NARROW, FR_PER_MMA, 2>(2));
     add(naive_entry<2>());
     // unlisted: thin products (N <= 16) and split-plan remainders

@@ -8,10 +8,13 @@
 //   TRANS_A   A slice stored transposed in LDS (As[k][m], section 7.3), so the
 //             A fragment is two 16-byte reads instead of eight 4-byte reads
 //             of rows BK*4 bytes apart;
-//   QUARTERS  each lane's 8 x 8 outputs split into 4 x 4 quarters 32 rows /
-//             columns apart (section 8.5's sub-block split), so the 16-byte
-//             fragment reads of a wave cover 8 contiguous 16-byte words; off:
-//             one contiguous 8 x 8 block per lane;
+//   QUARTERS  the conflict-free layout: each lane's 8 x 8 outputs split into
+//             4 x 4 quarters 32 rows / columns apart (section 8.5's sub-block
+//             split), so the 16-byte fragment reads of a wave cover 8
+//             contiguous 16-byte words, and the rows of transposed A padded
+//             (section 8's padding fix) so that the lanes writing one A row
+//             of a slice land on different banks; off: one contiguous 8 x 8
+//             block per lane, unpadded rows;
 //   VEC_STORE C written as 16-byte row pieces (one instruction writes whole
 //             128-byte row segments); off: one float per store;
 //   STAGES    1: load slice, barrier, compute, barrier.  2: the
@@ -40,13 +43,20 @@ template <int STAGES, bool TRANS_A, bool QUARTERS, bool VEC_STORE, int BK_ = 8, 
 struct F32Gemm {
     static constexpr int BM = TILE, BN = TILE, BK = BK_, NT = 256;
     static constexpr int TM = TILE / 16;      // outputs per lane along each side
-    static constexpr int A_BYTES = BK * BM * 4;
+    static constexpr int AQ = BK / 4;         // pieces per A row of a slice
+    // Row stride of transposed A in floats.  The 4 k-rows of one A piece go
+    // to rows kq .. kq+3; AQ lanes with the same m but kq = 0, 4, .. write
+    // each of them.  Padding by 16 / AQ floats (at least 4, to keep 16-byte
+    // reads aligned) moves consecutive kq a quarter (AQ = 4) or half (AQ = 2)
+    // of the 64 banks apart: no conflicts for 8- and 16-deep slices, 2-way
+    // for 32-deep ones.
+    static constexpr int AS_LD = BM + ((TRANS_A && QUARTERS) ? (16 / AQ > 4 ? 16 / AQ : 4) : 0);
+    static constexpr int A_BYTES = TRANS_A ? BK * AS_LD * 4 : BK * BM * 4;
     static constexpr int B_BYTES = BK * BN * 4;
     static constexpr int SLOT = A_BYTES + B_BYTES;
     static constexpr int LDS_BYTES = STAGES * SLOT;
     static constexpr int PER = BK * TILE / 4 / NT;  // 16-byte pieces of A and of B per thread per slice
     static constexpr int N_LD = 2 * PER;
-    static constexpr int AQ = BK / 4;         // pieces per A row of a slice
     static constexpr int BQ = BN / 4;         // pieces per B row of a slice
     static_assert(STAGES == 1 || STAGES == 2, "register-staged: 1 or 2 slots");
     static_assert(TILE == 128 || TILE == 64, "lane blocks of 8 x 8 or 4 x 4");
@@ -98,7 +108,7 @@ struct F32Gemm {
             const int row = p / AQ, kq = 4 * (p % AQ);
             if constexpr (TRANS_A) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) As[(kq + e) * BM + row] = r.a[q][e];
+                for (int e = 0; e < 4; ++e) As[(kq + e) * AS_LD + row] = r.a[q][e];
             } else {
                 *reinterpret_cast<TG_LDS f32x4*>(As + row * BK + kq) = r.a[q];
             }
@@ -125,7 +135,7 @@ struct F32Gemm {
             // rows frag_off(wm, lr, 4h .. 4h+3) are 4 contiguous for each h
 #pragma unroll
             for (int h = 0; h < TM / 4; ++h) {
-                const f32x4 a = *reinterpret_cast<const TG_LDS f32x4*>(As + k * BM + frag_off(wm, lr, 4 * h));
+                const f32x4 a = *reinterpret_cast<const TG_LDS f32x4*>(As + k * AS_LD + frag_off(wm, lr, 4 * h));
                 f.a[4 * h] = a.x; f.a[4 * h + 1] = a.y; f.a[4 * h + 2] = a.z; f.a[4 * h + 3] = a.w;
             }
         } else {

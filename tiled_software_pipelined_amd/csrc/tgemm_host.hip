@@ -197,7 +197,7 @@ const KernelEntry* default_entry(int dtype, int64_t M, int64_t N, int64_t K, boo
         pick = big_rounds(wgs(256)) <= mid_tile * (double)((wgs(128) + 255) / 256) ? 256 : 128;
     else if (!guarded && wgs(256) >= 128 && wgs(256) <= 256 && K >= one_round_k)
         pick = 256;
-    else if (!guarded && !i8 && wgs(128) > 64 && wgs(128) <= 128 && K >= 1024)
+    else if (!guarded && wgs(128) > 64 && wgs(128) <= 128 && K >= (i8 ? 2048 : 1024))
         pick = 96;  // a half tile, 128 x 64 or 64 x 128 (below)
     else if (wgs(128) > 64 || guarded)
         pick = 128;
@@ -207,11 +207,13 @@ const KernelEntry* default_entry(int dtype, int64_t M, int64_t N, int64_t K, boo
         // 128 x 128 tiles would fill between a quarter and half of the
         // compute units; half tiles fill them (bf16 512 x 4096 x 4096: 64 x
         // 128 27.2 us vs 34.3; 1024 x 2048 x 2048: 128 x 64 15.3 vs 19.7;
-        // 2048 x 1024 x 4096: 26.7-27.9 vs 33.2; equal at K = 1024)
+        // 2048 x 1024 x 4096: 26.7-27.9 vs 33.2; equal at K = 1024.  int8
+        // 512 x 4096 x 4096: 17.7 vs 20.3; 2048 x 1024 x 4096: 17.5 vs 20.7;
+        // 1024 x 2048 x 2048: 12.2 vs 12.8; 12.3 vs 11.8 at K = 1024)
         tgemm_variant h = v;
         h.tile_m = N >= M ? 64 : 128;
         h.tile_n = N >= M ? 128 : 64;
-        h.tile_k = 32;
+        h.tile_k = i8 ? 64 : 32;
         h.waves_n = 2;
         h.stages = 4;
         h.loader = TGEMM_LOADER_DIRECT;
