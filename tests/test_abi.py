@@ -69,6 +69,22 @@ def test_run_with_empty_output_is_a_noop_without_device():
     p.run_ptr(0, 0, 0)
 
 
+def test_leading_dimension_of_views():
+    import torch
+    x = torch.zeros(6, 10)
+    assert tl._ld(x, "A") == 10
+    assert tl._ld(x[:, 2:7], "A") == 10      # padded rows: the row stride
+    assert tl._ld(x[:1, :4], "A") == 4       # one row: its length
+    with pytest.raises(ValueError):
+        tl._ld(torch.zeros(8).expand(4, 8), "A")  # every row is the same memory
+    with pytest.raises(ValueError):
+        tl._ld(torch.zeros(20).as_strided((4, 8), (4, 1)), "A")  # rows overlap
+    with pytest.raises(ValueError):
+        tl._ld(x.t(), "A")                   # column-major
+    with pytest.raises(ValueError):
+        tl._ld(torch.zeros(2, 3, 4), "A")
+
+
 def test_destroy_null_is_allowed():
     tl._lib.gemm_destroy(None)
 

@@ -265,10 +265,18 @@ def _torch_dtype_code(t):
 
 
 def _ld(t, name):
+    """Leading dimension (row stride in elements) of a row-major 2-D tensor.
+
+    Rows must not overlap: a row stride below the row length (a broadcast or
+    otherwise aliased view) would make the kernels read past the rows the
+    tensor's storage holds, so it is rejected."""
     if t.dim() != 2:
         raise ValueError("%s must be 2-D" % name)
     if t.shape[1] > 1 and t.stride(1) != 1:
         raise ValueError("%s must be row-major with unit column stride" % name)
+    if t.shape[0] > 1 and t.shape[1] > 0 and t.stride(0) < t.shape[1]:
+        raise ValueError("%s has overlapping rows (row stride %d < %d columns); pass a contiguous copy"
+                         % (name, t.stride(0), t.shape[1]))
     return max(int(t.stride(0)), int(t.shape[1]), 1) if t.shape[0] > 1 else max(int(t.shape[1]), 1)
 
 
@@ -297,6 +305,8 @@ def gemm(A, B, out=None, variant: Variant | None = None, workspace: bool = True)
     import torch
     if not (A.is_cuda and B.is_cuda):
         raise ValueError("A and B must be GPU tensors")
+    if A.device != B.device:
+        raise ValueError("A and B must be on the same device (%s, %s)" % (A.device, B.device))
     if A.dtype != B.dtype:
         raise TypeError("A and B must have the same dtype")
     code = _torch_dtype_code(A)
