@@ -78,6 +78,14 @@ typedef enum tgemm_dtype {
 #define TGEMM_LDS_PLAIN 1
 #define TGEMM_LDS_XOR 2          /* 16-byte chunk index XOR-swizzled by row; for the fp32
                                     kernels: each lane's outputs split in quarters 32 apart */
+#define TGEMM_LDS_XOR_POISON 3   /* debug form of TGEMM_LDS_XOR for the direct-loader ring:
+                                    each lane fills the 16 LDS bytes a direct copy will
+                                    write with all-ones bytes (bf16 NaN, int8 -1) and waits
+                                    for that store before issuing the copy, so a read of a
+                                    slot before its copy lands, or after the copy of a later
+                                    slice began, puts NaN (bf16) or a wrong sum (int8) into
+                                    C.  Same results as TGEMM_LDS_XOR when the ring is
+                                    correct; slower.  Only chosen when requested. */
 
 /* Access width of global loads, LDS writes and LDS fragment reads
  * (GEMM page, section 7: 128-bit vector accesses).  For the fp32 kernels it

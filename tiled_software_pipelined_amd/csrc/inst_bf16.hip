@@ -55,6 +55,12 @@ void register_bf16(void (*add)(const KernelEntry&)) {
     add(mfma_entry<T, 128, 128, 32, 2, 2, 2, LD_VGPR, LY_XOR, AC_WIDE, FR_REUSE, 2, 1>(1));
     add(mfma_entry<T, 128, 128, 32, 2, 2, 2, LD_VGPR, LY_XOR, AC_WIDE, FR_REUSE, 2, 2>(1));
     add(mfma_entry<T, 128, 128, 32, 2, 2, 2, LD_VGPR, LY_XOR, AC_WIDE, FR_REUSE, 2, 3>(1));
+    // debug twins of the direct-loader defaults with poisoned slots: listed
+    // last, so only a request for TGEMM_LDS_XOR_POISON reaches them
+    add(mfma_entry<T, 256, 256, 64, 2, 4, 2, LD_DIRECT, LY_XOR_POISON, AC_WIDE, FR_REUSE, 2>(1));
+    add(mfma_entry<T, 128, 128, 32, 2, 2, 4, LD_DIRECT, LY_XOR_POISON, AC_WIDE, FR_REUSE, 2>(1));
+    add(mfma_entry<T, 64, 128, 32, 2, 2, 4, LD_DIRECT, LY_XOR_POISON, AC_WIDE, FR_REUSE, 2>(1));
+    add(mfma_entry<T, 64, 64, 64, 2, 2, 8, LD_DIRECT, LY_XOR_POISON, AC_WIDE, FR_REUSE, 4>(1));
 }
 
 }  // namespace tg

@@ -37,6 +37,10 @@ void register_i8(void (*add)(const KernelEntry&)) {
     add(mfma_entry<T, 128, 128, 64, 2, 2, 2, LD_VGPR, LY_XOR, AC_WIDE, FR_REUSE, 2, 1>(2));
     add(mfma_entry<T, 128, 128, 64, 2, 2, 2, LD_VGPR, LY_XOR, AC_WIDE, FR_REUSE, 2, 2>(2));
     add(mfma_entry<T, 128, 128, 64, 2, 2, 2, LD_VGPR, LY_XOR, AC_WIDE, FR_REUSE, 2, 3>(2));
+    // debug twins with poisoned slots (only reached by TGEMM_LDS_XOR_POISON)
+    add(mfma_entry<T, 256, 256, 128, 2, 4, 2, LD_DIRECT, LY_XOR_POISON, AC_WIDE, FR_REUSE, 2>(2));
+    add(mfma_entry<T, 128, 128, 64, 2, 2, 4, LD_DIRECT, LY_XOR_POISON, AC_WIDE, FR_REUSE, 2>(2));
+    add(mfma_entry<T, 64, 64, 128, 2, 2, 8, LD_DIRECT, LY_XOR_POISON, AC_WIDE, FR_REUSE, 4>(2));
 }
 
 }  // namespace tg

@@ -28,7 +28,9 @@ constexpr int THIN_N_MAX = 16;
 
 enum Family { FAM_NAIVE = 1, FAM_TILED = 2, FAM_THIN = 3 };
 enum Loader { LD_VGPR = 1, LD_DIRECT = 2 };
-enum Layout { LY_PLAIN = 1, LY_XOR = 2 };
+// LY_XOR_POISON: LY_XOR plus a debug fill of every LDS chunk with all-ones
+// bytes just before its direct copy is issued (see MfmaGemm::issue_direct_one)
+enum Layout { LY_PLAIN = 1, LY_XOR = 2, LY_XOR_POISON = 3 };
 enum Access { AC_WIDE = 1, AC_NARROW = 2 };
 enum Frag { FR_REUSE = 1, FR_PER_MMA = 2 };
 

@@ -48,7 +48,8 @@ KernelEntry mfma_entry(int dtype) {
     e.waves_per_simd = WAVES;
     e.fn = gemm_kernel<K, WAVES>;
     snprintf(e.name, sizeof e.name, "%s_t%dx%dx%d_w%dx%d_s%d_%s_%s_%s_%s%s", dtype_tag(dtype), BM, BN,
-             BK, WM, WN, S, LD == LD_DIRECT ? "direct" : "vgpr", LY == LY_XOR ? "xor" : "plain",
+             BK, WM, WN, S, LD == LD_DIRECT ? "direct" : "vgpr",
+             LY == LY_XOR ? "xor" : LY == LY_XOR_POISON ? "xorpoison" : "plain",
              AC == AC_WIDE ? "wide" : "narrow", FR == FR_REUSE ? "reuse" : "permma",
              SHIFT == 1 ? "_shiftA" : SHIFT == 2 ? "_shiftB" : SHIFT == 3 ? "_shiftAB" : "");
     return e;

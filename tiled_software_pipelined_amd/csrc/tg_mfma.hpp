@@ -92,7 +92,8 @@ struct MfmaGemm {
     static constexpr int A_PER = BM * CA / NT;  // 16-byte A chunks per thread per slice
     static constexpr int B_PER = BK * CB / NT;
     static constexpr int N_LD = A_PER + B_PER;  // loads per thread (= per wave) per slice
-    static constexpr bool XOR = LAYOUT == LY_XOR;
+    static constexpr bool XOR = LAYOUT == LY_XOR || LAYOUT == LY_XOR_POISON;
+    static constexpr bool POISON = LAYOUT == LY_XOR_POISON;
     static constexpr bool WIDE = ACCESS == AC_WIDE;
     static constexpr bool DIRECT = LOADER == LD_DIRECT;
     // narrow (4-byte) accesses
@@ -108,6 +109,7 @@ struct MfmaGemm {
     static_assert(WIDE || (!XOR && !DIRECT), "narrow accesses use the plain layout");
     static_assert(FRAG == FR_REUSE || !WIDE, "per-instruction fragment reloads only on the narrow rung");
     static_assert(N_LD * (STAGES > 2 ? STAGES - 2 : 0) <= 63, "vmcnt range");
+    static_assert(!POISON || (DIRECT && STAGES >= 2), "poisoned slots: the direct-loader ring");
     static_assert(SHIFT == 0 || (LOADER == LD_VGPR && WIDE), "shifted loads: register-staged, 16-byte chunks");
     // Shifted chunks complete their pairs from the neighbouring lane after
     // the multiply when the staged registers are few (the extra block and
@@ -394,17 +396,22 @@ struct MfmaGemm {
         }
     }
 
-    // Issue copy number i (0 <= i < N_LD) of one slice into `slot`.
+    // Issue copy number i (0 <= i < N_LD) of one slice into `slot`.  Lane l
+    // of the copy writes the 16 bytes at its wave's base + 16 l.  POISON
+    // (debug): the lane first stores all-ones bytes there and waits for the
+    // store, so until the copy lands the chunk reads as NaN (bf16) / -1
+    // (int8); every lane poisons only the bytes its own copy overwrites.
     __device__ static __forceinline__ void issue_direct_one(int i, TG_LDS char* slot, const DirectOffsets& o,
                                                             const char* abase, const char* bbase,
                                                             int wave) {
         const uint32_t lds = (uint32_t)(uintptr_t)slot;
-        if (i < A_PER) {
-            copy16_to_lds(lds + (i * NT + wave * 64) * 16, o.a[i], abase);
-        } else {
-            const int q = i - A_PER;
-            copy16_to_lds(lds + A_BYTES + (q * NT + wave * 64) * 16, o.b[q], bbase);
+        const int off = i < A_PER ? (i * NT + wave * 64) * 16 : A_BYTES + ((i - A_PER) * NT + wave * 64) * 16;
+        if constexpr (POISON) {
+            *reinterpret_cast<TG_LDS i32x4*>(slot + off + lane_id() * 16) = i32x4{-1, -1, -1, -1};
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         }
+        if (i < A_PER) copy16_to_lds(lds + off, o.a[i], abase);
+        else copy16_to_lds(lds + off, o.b[i - A_PER], bbase);
     }
 
     __device__ static __forceinline__ void issue_direct(TG_LDS char* slot, const DirectOffsets& o,

@@ -26,7 +26,7 @@ ERRORS = {-1: "TGEMM_E_ARG", -2: "TGEMM_E_NULL", -3: "TGEMM_E_ALIGN", -4: "TGEMM
 # variant field values (include/tgemm.h)
 KERNEL_AUTO, KERNEL_NAIVE, KERNEL_TILED = 0, 1, 2
 LOADER_VGPR, LOADER_DIRECT = 1, 2
-LDS_PLAIN, LDS_XOR = 1, 2
+LDS_PLAIN, LDS_XOR, LDS_XOR_POISON = 1, 2, 3
 ACCESS_WIDE, ACCESS_NARROW = 1, 2
 FRAG_REUSE, FRAG_PER_MMA = 1, 2
 ORDER_ROW_MAJOR = -1
