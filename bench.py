@@ -344,6 +344,16 @@ def cold_timing(torch, lib, w, A, B, C, variant, launches=30):
                       "unit": "TOP/s" if w.dtype == "i8" else "TFLOP/s"}), flush=True)
 
 
+def env_record(torch, lib, dev):
+    """Where the line was measured: device, runtime versions, library
+    version and the hash of the kernel sources it was built from."""
+    from tiled_software_pipelined_amd import provenance
+    p = torch.cuda.get_device_properties(dev)
+    return {"device": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
+            "hip": torch.version.hip, "torch": torch.__version__, "libtgemm": lib.version(),
+            "kernel_sources": provenance.source_hash()}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -528,6 +538,7 @@ def main():
                      "timing": "kernel_ms_mean: HIP events at the two ends of the timed region / steps; "
                                "kernel_ms_min: per-launch events in a pass after it"},
         "cpu_baseline": None,
+        "env": env_record(torch, lib, dev),
     }
     if not args.calib_copy:
         # the rate the arithmetic units sustain on this machine for the

@@ -183,6 +183,24 @@ def test_integer_valued_inputs_are_exact(dtype):
     assert (_run(_as_dtype(P, dtype), _as_dtype(B, dtype)).numpy() == B[perm]).all()
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "i8"])
+def test_permutation_products_every_variant(dtype):
+    # the one-hot lane-layout probe, for every matrix-core variant: with P and
+    # Q permutation matrices each output of P Q holds exactly one product, so a
+    # wrong fragment row / column, K position or output lane moves or drops a
+    # 1 (n = 384: a whole and a ragged 256-wide tile, several slices)
+    rng = np.random.default_rng(7)
+    n = 384
+    P = np.zeros((n, n))
+    P[np.arange(n), rng.permutation(n)] = 1
+    Q = np.zeros((n, n))
+    Q[np.arange(n), rng.permutation(n)] = 1
+    want = P @ Q
+    for v in _variants(dtype, tiled_only=True):
+        C = _run(_as_dtype(P, dtype), _as_dtype(Q, dtype), variant=v).numpy()
+        assert (C == want).all(), _vname(v)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "i8"])
 def test_hadamard(dtype):
     H = np.array([[1]])
