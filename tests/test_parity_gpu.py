@@ -19,7 +19,7 @@ from tiled_software_pipelined_amd import inputs
 
 pytestmark = pytest.mark.gpu
 
-tl = None  # the binding, loaded by the fixture below (it must load on a GPU machine)
+tl = None  # the binding, loaded by the fixture below (it must load wherever a GPU is present)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -27,7 +27,7 @@ def _gpu():
     global tl
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    from tiled_software_pipelined_amd import lib  # must load: no fallback on a GPU machine
+    from tiled_software_pipelined_amd import lib  # must load: there is no fallback
     tl = lib
     yield
 

@@ -1,6 +1,6 @@
 """Counter layer: rocprofv3 kernel trace + hardware counters for one workload.
 
-    python -m tiled_software_pipelined_amd.profiling --workload bf16_4096 --out gpurun_out/prof_bf16 \\
+    python -m tiled_software_pipelined_amd.profiling --workload bf16_4096 --out prof_out/bf16 \\
         [--variant k=v,...] [--summary profiles/<name>.md]
 
 Runs bench.py under rocprofv3 several times (one kernel-trace pass, then one
@@ -351,7 +351,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", default="bf16_4096")
     ap.add_argument("--variant", default="")
-    ap.add_argument("--out", default="gpurun_out/prof")
+    ap.add_argument("--out", default="prof_out/prof")
     # the trace pass runs the same timed region as the default bench run
     # (its kernel means then describe the same, clock-ramped, steady state)
     ap.add_argument("--steps", type=int, default=50)
