@@ -344,6 +344,26 @@ def cold_timing(torch, lib, w, A, B, C, variant, launches=30):
                       "unit": "TOP/s" if w.dtype == "i8" else "TFLOP/s"}), flush=True)
 
 
+NOMINAL_GHZ = 2.4      # the shader clock the datasheet peaks assume
+CLOCKED_LAUNCHES = 20
+
+
+def clocked_rate(torch, lib, plan, A, B, C, variant):
+    """Mean shader clock (GHz) of the plan's tiled kernel over a few launches
+    through gemm_run_clocked, or None when the plan has none to clock or the
+    run repacks operands (the clocked entry runs the plan as gemm_run does)."""
+    slots = plan.clock_slots()
+    if slots == 0 or (variant is None and plan.workspace_bytes(A.data_ptr(), B.data_ptr()) > 0):
+        return None
+    clocks = torch.zeros(CLOCKED_LAUNCHES * slots, dtype=torch.int64, device=A.device)
+    stream = torch.cuda.current_stream().cuda_stream
+    for i in range(CLOCKED_LAUNCHES):
+        plan.run_clocked_ptr(A.data_ptr(), B.data_ptr(), C.data_ptr(), clocks.data_ptr() + 8 * i * slots, slots,
+                             stream)
+    torch.cuda.synchronize()
+    return lib.clock_ghz(clocks.cpu().numpy().view("uint64"))
+
+
 def env_record(torch, lib, dev):
     """Where the line was measured: device, runtime versions, library
     version and the hash of the kernel sources it was built from."""
@@ -540,6 +560,14 @@ def main():
         "cpu_baseline": None,
         "env": env_record(torch, lib, dev),
     }
+    clk = clocked_rate(torch, lib, plan, A, B, C, variant)
+    if clk is not None:
+        ghz = clk
+        at_clock = peak * ghz / NOMINAL_GHZ
+        rec["roofline"]["clock"] = {
+            "ghz": round(ghz, 3), "peak_at_clock": round(at_clock, 1), "frac": round(achieved / at_clock, 4),
+            "source": "s_memtime / s_memrealtime of every workgroup over %d launches right after the timed "
+                      "region; peak scaled from %.1f GHz" % (CLOCKED_LAUNCHES, NOMINAL_GHZ)}
     if not args.calib_copy:
         # the rate the arithmetic units sustain on this machine for the
         # workload's operand distribution with no memory traffic at all (the

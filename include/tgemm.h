@@ -217,6 +217,28 @@ typedef struct tgemm_plan_info {
 /* Fill *info for `plan`.  Returns TGEMM_OK or TGEMM_E_NULL. */
 int gemm_plan_get_info(const tgemm_plan* plan, tgemm_plan_info* info);
 
+/* Shader clock of a run (a diagnostic: the matrix cores' rate scales with
+ * the shader clock, which the power budget lowers under load).
+ * gemm_run_clocked is gemm_run, except that every workgroup of the plan's
+ * tiled kernel (matrix-core or fp32; a split plan's thin remainder is not
+ * clocked) writes four values to clocks[4 w .. 4 w + 3], w its workgroup
+ * index: the shader-clock counter (s_memtime) and the 100 MHz real-time
+ * counter (s_memrealtime) when it starts, then both again once all its
+ * memory instructions, the C stores included, have completed.  Summed over
+ * workgroups, (end - start shader ticks) / (end - start real ticks) x 100 MHz
+ * is the mean shader clock of the run.  The C written is the same as
+ * gemm_run's, bit for bit.
+ * clocks: device memory owned by the caller, 8-byte aligned, clocks_len
+ * values; gemm_clock_slots(plan) values always suffice (it is the largest
+ * grid among the kernels the plan may launch, times 4; 0 for a plan that
+ * launches no tiled kernel, including empty products).
+ * Returns what gemm_run returns, or TGEMM_E_NULL (NULL plan or clocks),
+ * TGEMM_E_ARG (nothing to clock, or clocks_len below what the launched
+ * kernel needs: then nothing is launched) or TGEMM_E_ALIGN. */
+int64_t gemm_clock_slots(const tgemm_plan* plan);
+int gemm_run_clocked(const tgemm_plan* plan, const void* A, const void* B, void* C, uint64_t* clocks,
+                     int64_t clocks_len, void* stream);
+
 /* Occupancy of a plan's main kernel (a diagnostic for profile summaries, not
  * needed to run a plan): *workgroups_per_cu receives how many of its
  * workgroups one compute unit holds at once, as the HIP runtime's occupancy

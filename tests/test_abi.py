@@ -63,6 +63,28 @@ def test_occupancy_rejects_null_arguments():
     assert tl._lib.gemm_kernel_occupancy(p._h, 0, None) == -2
 
 
+def test_clock_slots_and_null_arguments():
+    # host-only: the count covers the largest grid the plan may launch
+    p = tl.Plan(4096, 4096, 4096, tl.BF16)
+    assert p.clock_slots() == 4 * p.info().grid == 4 * 256
+    q = tl.Plan(4096, 4096, 4096, tl.BF16, 4096, 4097, 4096)  # B rows unaligned: register-staged
+    assert q.clock_slots() >= 4 * q.info().grid
+    assert tl.Plan(0, 64, 64, tl.BF16).clock_slots() == 0
+    assert tl.Plan(64, 64, 0, tl.BF16, 1, 64, 64).clock_slots() == 0
+    assert tl._lib.gemm_clock_slots(None) == 0
+    assert tl._lib.gemm_run_clocked(None, None, None, None, None, 0, None) == -2
+    assert tl._lib.gemm_run_clocked(p._h, None, None, None, None, 0, None) == -2
+    # nothing to clock: returns before touching the device
+    assert tl._lib.gemm_run_clocked(tl.Plan(0, 64, 64, tl.BF16)._h, None, None, None, 8, 4, None) == -1
+
+
+def test_clock_ghz_arithmetic():
+    # two workgroups: 2.0e6 and 1.0e6 shader ticks over 1000 and 1000 real ticks (10 us each)
+    c = [[0, 0, 2_000_000, 1000], [5, 7, 1_000_005, 1007]]
+    assert abs(tl.clock_ghz(c) - 3.0e6 / 2000 * 0.1 / 1000 * 1000) < 1e-12
+    assert abs(tl.clock_ghz([[0, 0, 240, 10]]) - 2.4) < 1e-12
+
+
 def test_run_with_empty_output_is_a_noop_without_device():
     # M = 0: nothing to do, returns before touching the device
     p = tl.Plan(0, 16, 16, tl.BF16)

@@ -42,6 +42,35 @@ __device__ __forceinline__ void wait_all_then_barrier() {
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Clock marks of a workgroup (GemmArgs::clocks): the shader-clock counter
+// (s_memtime) and the 100 MHz real-time counter (s_memrealtime).  The end
+// mark is taken once every wave's memory instructions, C stores included,
+// have completed; thread 0 writes [start shader, start real, end shader,
+// end real] to clocks[4 * workgroup ..] with vector stores.
+struct ClockMark {
+    uint64_t c0 = 0, w0 = 0;
+    __device__ __forceinline__ void start(const uint64_t* clocks) {
+        if (clocks) {
+            c0 = __builtin_amdgcn_s_memtime();
+            w0 = __builtin_amdgcn_s_memrealtime();
+        }
+    }
+    __device__ __forceinline__ void finish(uint64_t* clocks) const {
+        if (clocks) {
+            wait_all_then_barrier();
+            const uint64_t c1 = __builtin_amdgcn_s_memtime();
+            const uint64_t w1 = __builtin_amdgcn_s_memrealtime();
+            if (threadIdx.x == 0) {
+                uint64_t* p = clocks + 4 * (uint64_t)blockIdx.x;
+                p[0] = c0;
+                p[1] = w0;
+                p[2] = c1;
+                p[3] = w1;
+            }
+        }
+    }
+};
+
 // One 16-byte-per-lane copy global -> LDS that bypasses the registers
 // (global_load_lds_dwordx4).  Lane l reads `base + voff` and its 16 bytes
 // land at LDS byte `lds + 16 l`; `lds` and `base` must be wave-uniform.

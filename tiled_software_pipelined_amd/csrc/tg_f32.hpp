@@ -199,6 +199,8 @@ struct F32Gemm {
     __device__ static void run(const GemmArgs& g) {
         __shared__ __attribute__((aligned(1024))) char smem_raw[LDS_BYTES];
         TG_LDS char* smem = (TG_LDS char*)(smem_raw);
+        ClockMark clk;
+        clk.start(g.clocks);
         int tm, tn;
         tile_of_workgroup(g, tm, tn);
         const int m0 = tm * BM, n0 = tn * BN;
@@ -262,6 +264,7 @@ struct F32Gemm {
                 }
             }
         }
+        clk.finish(g.clocks);
     }
 };
 

@@ -746,6 +746,8 @@ struct MfmaGemm {
     __device__ static __forceinline__ void run(const GemmArgs& g) {
         __shared__ __attribute__((aligned(1024))) char smem_raw[LDS_BYTES];
         TG_LDS char* smem = (TG_LDS char*)(smem_raw);
+        ClockMark clk;
+        clk.start(g.clocks);
 
         const int lane = lane_id();
         const int wave = wave_id();
@@ -857,6 +859,7 @@ struct MfmaGemm {
         const bool inside = (m0 + BM <= g.M) && (n0 + BN <= g.N);
         if (g.c_stream) store_c<true>(C, g, acc, m0 + wm0, n0 + wn0, lane, inside);
         else store_c<false>(C, g, acc, m0 + wm0, n0 + wn0, lane, inside);
+        clk.finish(g.clocks);
     }
 };
 

@@ -527,7 +527,13 @@ void gemm_destroy(tgemm_plan* plan) {
     delete plan;
 }
 
-int gemm_run(const tgemm_plan* p, const void* A, const void* B, void* C, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// gemm_run with an optional clock buffer for the main kernel's workgroups.
+int run_impl(const tgemm_plan* p, const void* A, const void* B, void* C, uint64_t* clocks, int64_t clocks_len,
+             void* stream) {
     if (!p) {
         set_err("NULL plan");
         return TGEMM_E_NULL;
@@ -576,7 +582,7 @@ int gemm_run(const tgemm_plan* p, const void* A, const void* B, void* C, void* s
             return TGEMM_E_ALIGN;
         }
     }
-    tg::GemmArgs g;
+    tg::GemmArgs g{};  // every field zero, the clock buffer NULL, unless set below
     g.A = A;
     g.B = B;
     g.C = C;
@@ -592,6 +598,16 @@ int gemm_run(const tgemm_plan* p, const void* A, const void* B, void* C, void* s
     g.a_guard = ga;
     g.b_guard = gb;
     g.c_stream = (uintptr_t)C % 128 == 0 && (p->ldc * 4) % 128 == 0;
+    if (clocks && e->family == tg::FAM_TILED) {
+        // the kernel that runs decides the count (a fallback's tile may differ)
+        const int64_t need = 4 * (int64_t)g.tiles_m * g.tiles_n;
+        if (need > clocks_len) {
+            set_err("clock buffer holds %lld values, %s needs %lld", (long long)clocks_len, e->name,
+                    (long long)need);
+            return TGEMM_E_ARG;
+        }
+        g.clocks = clocks;
+    }
     void* args[] = {&g};
     const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(e->fn),
                                            dim3((unsigned)(g.tiles_m * g.tiles_n)), dim3(e->threads), args, 0, s);
@@ -600,9 +616,48 @@ int gemm_run(const tgemm_plan* p, const void* A, const void* B, void* C, void* s
         return TGEMM_E_HIP;
     }
     if (p->rem)  // the last N - n_main columns, after the main part on the same stream
-        return gemm_run(p->rem, A, static_cast<const char*>(B) + p->n_main * esz,
-                        static_cast<char*>(C) + p->n_main * 4, stream);
+        return run_impl(p->rem, A, static_cast<const char*>(B) + p->n_main * esz,
+                        static_cast<char*>(C) + p->n_main * 4, nullptr, 0, stream);
     return TGEMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_run(const tgemm_plan* p, const void* A, const void* B, void* C, void* stream) {
+    return run_impl(p, A, B, C, nullptr, 0, stream);
+}
+
+int64_t gemm_clock_slots(const tgemm_plan* p) {
+    if (!p || p->M == 0 || p->N == 0 || p->K == 0) return 0;
+    // the largest grid among the kernels this plan may launch
+    int64_t most = 0;
+    for (int m = 0; m < 4; ++m) {
+        const KernelEntry* e = m == 0 ? p->entry : p->fallback[m];
+        if (!e || e->family != tg::FAM_TILED) continue;
+        const int64_t n = 4 * ((p->M + e->bm - 1) / e->bm) * ((p->n_main + e->bn - 1) / e->bn);
+        if (n > most) most = n;
+    }
+    return most;
+}
+
+int gemm_run_clocked(const tgemm_plan* p, const void* A, const void* B, void* C, uint64_t* clocks,
+                     int64_t clocks_len, void* stream) {
+    if (!p || !clocks) {
+        set_err("NULL plan or clock buffer");
+        return TGEMM_E_NULL;
+    }
+    const int64_t need = gemm_clock_slots(p);
+    if (need == 0) {
+        set_err("this plan runs no tiled kernel to clock");
+        return TGEMM_E_ARG;
+    }
+    if ((uintptr_t)clocks % 8) {
+        set_err("clock buffer not 8-byte aligned");
+        return TGEMM_E_ALIGN;
+    }
+    return run_impl(p, A, B, C, clocks, clocks_len, stream);
 }
 
 // Which operands gemm_run_ws repacks for these pointers (bit 0 A, bit 1 B)

@@ -59,7 +59,7 @@ class PlanInfo(ctypes.Structure):
 EXPORTS = ("gemm_plan", "gemm_plan_variant", "gemm_run", "gemm_destroy", "tgemm_last_error",
            "gemm_plan_get_info", "gemm_variant_count", "gemm_variant_get", "tgemm_version",
            "tgemm_lds_read_probe", "tgemm_mfma_rate_probe", "gemm_workspace_bytes", "gemm_run_ws",
-           "gemm_kernel_occupancy")
+           "gemm_kernel_occupancy", "gemm_clock_slots", "gemm_run_clocked")
 
 
 def _load():
@@ -85,6 +85,10 @@ def _load():
     lib.gemm_plan_get_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]
     lib.gemm_kernel_occupancy.argtypes = [vp, i32, ctypes.POINTER(i32)]
     lib.gemm_kernel_occupancy.restype = ctypes.c_int
+    lib.gemm_clock_slots.argtypes = [vp]
+    lib.gemm_clock_slots.restype = i64
+    lib.gemm_run_clocked.argtypes = [vp, vp, vp, vp, vp, i64, vp]
+    lib.gemm_run_clocked.restype = ctypes.c_int
     lib.gemm_plan_get_info.restype = ctypes.c_int
     lib.gemm_variant_count.argtypes = [i32]
     lib.gemm_variant_count.restype = ctypes.c_int
@@ -227,6 +231,17 @@ class Plan:
             raise TgemmError(rc, last_error())
         return int(n.value)
 
+    def clock_slots(self) -> int:
+        """Values of the clock buffer gemm_run_clocked needs (0: nothing to clock)."""
+        return int(_lib.gemm_clock_slots(self._h))
+
+    def run_clocked_ptr(self, A: int, B: int, C: int, clocks: int, clocks_len: int, stream: int = 0) -> None:
+        """gemm_run_clocked on raw device pointers."""
+        rc = _lib.gemm_run_clocked(self._h, ctypes.c_void_p(A), ctypes.c_void_p(B), ctypes.c_void_p(C),
+                                   ctypes.c_void_p(clocks), clocks_len, ctypes.c_void_p(stream))
+        if rc != OK:
+            raise TgemmError(rc, last_error())
+
     def run_ptr(self, A: int, B: int, C: int, stream: int = 0) -> None:
         """Enqueue on raw device pointers (the caller keeps the buffers alive)."""
         rc = _lib.gemm_run(self._h, ctypes.c_void_p(A), ctypes.c_void_p(B), ctypes.c_void_p(C),
@@ -278,6 +293,19 @@ def _ld(t, name):
         raise ValueError("%s has overlapping rows (row stride %d < %d columns); pass a contiguous copy"
                          % (name, t.stride(0), t.shape[1]))
     return max(int(t.stride(0)), int(t.shape[1]), 1) if t.shape[0] > 1 else max(int(t.shape[1]), 1)
+
+
+def clock_ghz(clocks) -> float:
+    """Mean shader clock (GHz) of clocked runs: a host array of 4 values per
+    workgroup as gemm_run_clocked writes them (any number of runs stacked);
+    shader ticks over 100 MHz real-time ticks, summed over workgroups."""
+    import numpy as np
+    c = np.asarray(clocks, dtype=np.uint64).reshape(-1, 4).astype(np.float64)
+    shader = float((c[:, 2] - c[:, 0]).sum())
+    real = float((c[:, 3] - c[:, 1]).sum())
+    if real <= 0:
+        raise ValueError("no real-time ticks recorded")
+    return shader / real * 0.1
 
 
 def plan_for(M, N, K, dtype, lda, ldb, ldc, variant: Variant | None = None) -> Plan:
