@@ -68,8 +68,18 @@ struct F32Gemm {
 
     // Piece p = q NT + t (q < PER) of the slice: A[m0 + p / AQ][k0 + 4 (p % AQ) .. +3]
     // and B[k0 + p / BQ][n0 + 4 (p % BQ) .. +3].
+    template <bool GA, bool GB>
+    __device__ static __forceinline__ void load_t(Staged& r, const GemmArgs& g, int m0, int n0, int k0) {
+        load_any(r, g, m0, n0, k0, GA, GB);
+    }
+
     __device__ static __forceinline__ void load(Staged& r, const GemmArgs& g, int m0, int n0, int k0,
                                                 bool guard_a, bool guard_b) {
+        load_any(r, g, m0, n0, k0, guard_a, guard_b);
+    }
+
+    __device__ static __forceinline__ void load_any(Staged& r, const GemmArgs& g, int m0, int n0, int k0,
+                                                    bool guard_a, bool guard_b) {
         const float* A = static_cast<const float*>(g.A);
         const float* B = static_cast<const float*>(g.B);
 #pragma unroll
@@ -233,8 +243,20 @@ struct F32Gemm {
                 store(smem, r);
                 wait_lds_then_barrier();
             }
+            int t = 0;
+            if (!ga && !gb) {
+                // whole slices of aligned operands: no guarded paths in the loop
 #pragma nounroll
-            for (int t = 0; t < tiles; ++t) {
+                for (; t + 1 < full; ++t) {
+                    Staged r;
+                    load_t<false, false>(r, g, m0, n0, (t + 1) * BK);
+                    compute(smem + (t & 1) * SLOT, c, wm, wn, lr, lc);
+                    store(smem + ((t + 1) & 1) * SLOT, r);
+                    wait_lds_then_barrier();
+                }
+            }
+#pragma nounroll
+            for (; t < tiles; ++t) {
                 const int nxt = t + 1;
                 Staged r;
                 if (nxt < tiles) load(r, g, m0, n0, nxt * BK, ga || nxt >= full, gb || nxt >= full);
