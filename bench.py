@@ -349,9 +349,10 @@ CLOCKED_LAUNCHES = 20
 
 
 def clocked_rate(torch, lib, plan, A, B, C, variant):
-    """Mean shader clock (GHz) of the plan's tiled kernel over a few launches
-    through gemm_run_clocked, or None when the plan has none to clock or the
-    run repacks operands (the clocked entry runs the plan as gemm_run does)."""
+    """(mean shader clock in GHz, per-XCD clocks, per-XCD last end in us) of
+    the plan's tiled kernel over a few launches through gemm_run_clocked, or
+    None when the plan has none to clock or the run repacks operands (the
+    clocked entry runs the plan as gemm_run does)."""
     slots = plan.clock_slots()
     if slots == 0 or (variant is None and plan.workspace_bytes(A.data_ptr(), B.data_ptr()) > 0):
         return None
@@ -361,7 +362,16 @@ def clocked_rate(torch, lib, plan, A, B, C, variant):
         plan.run_clocked_ptr(A.data_ptr(), B.data_ptr(), C.data_ptr(), clocks.data_ptr() + 8 * i * slots, slots,
                              stream)
     torch.cuda.synchronize()
-    return lib.clock_ghz(clocks.cpu().numpy().view("uint64"))
+    c = clocks.cpu().numpy().view("uint64").reshape(CLOCKED_LAUNCHES, -1, 4)
+    ghz = lib.clock_ghz(c)
+    # workgroup w runs on XCD w mod 8 (round-robin dispatch); per XCD, the
+    # mean clock and the time from the launch's first start to its last end
+    wg = c.shape[1]
+    xcd = [lib.clock_ghz(c[:, x::8]) if x < wg else None for x in range(8)]
+    start = c[:, :, 1].min(axis=1).astype("int64")
+    span_us = [float(((c[:, x::8, 3].max(axis=1).astype("int64") - start) * 0.01).mean()) if x < wg else None
+               for x in range(8)]
+    return ghz, xcd, span_us
 
 
 def env_record(torch, lib, dev):
@@ -562,12 +572,16 @@ def main():
     }
     clk = clocked_rate(torch, lib, plan, A, B, C, variant)
     if clk is not None:
-        ghz = clk
+        ghz, xcd, span = clk
         at_clock = peak * ghz / NOMINAL_GHZ
         rec["roofline"]["clock"] = {
             "ghz": round(ghz, 3), "peak_at_clock": round(at_clock, 1), "frac": round(achieved / at_clock, 4),
+            "xcd_ghz": [round(x, 3) if x is not None else None for x in xcd],
+            "xcd_last_end_us": [round(x, 2) if x is not None else None for x in span],
             "source": "s_memtime / s_memrealtime of every workgroup over %d launches right after the timed "
-                      "region; peak scaled from %.1f GHz" % (CLOCKED_LAUNCHES, NOMINAL_GHZ)}
+                      "region; peak scaled from %.1f GHz; per XCD (workgroup mod 8): mean clock and time "
+                      "from the launch's first workgroup start to that XCD's last end" % (CLOCKED_LAUNCHES,
+                                                                                          NOMINAL_GHZ)}
     if not args.calib_copy:
         # the rate the arithmetic units sustain on this machine for the
         # workload's operand distribution with no memory traffic at all (the
