@@ -299,10 +299,10 @@ def test_workspace_bytes(dtype, esz):
     # host-only: the addresses are numbers, nothing is dereferenced
     al = 1 << 20
     M, N, K = 4095, 4097, 4104
-    per = 16 // esz
     p = tl.Plan(M, N, K, dtype, K, N, N)
-    bytes_a = _ru(M * _ru(K, per) * esz, 256)
-    bytes_b = _ru(K * _ru(N, per) * esz, 256)
+    # repacked rows are rounded up to whole 128-byte lines
+    bytes_a = _ru(M * _ru(K * esz, 128), 256)
+    bytes_b = _ru(K * _ru(N * esz, 128), 256)
     a_al = (K * esz) % 16 == 0
     # leading dimensions: B rows (N = 4097) are never aligned; A rows at K = 4104 are for bf16 / fp32
     assert p.workspace_bytes(al, al) == (0 if a_al else bytes_a) + bytes_b

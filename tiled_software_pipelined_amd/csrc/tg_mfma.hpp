@@ -225,7 +225,9 @@ struct MfmaGemm {
     //   LM_SHIFTED_EDGE : the same with a bounds check per pair, for the
     //                first and last whole slices;
     //   LM_ELEMENT : element loads with zero fill at k >= K (and n >= N for
-    //                B): the partial last K slice.
+    //                B): the partial last K slice.  In kernels that only
+    //                see 16-byte aligned rows (no SHIFT bit for the operand)
+    //                a chunk wholly inside K (and N) takes one 16-byte load.
     template <int MODE_A, int MODE_B>
     __device__ static __forceinline__ void load_regs(Staged<MODE_A, MODE_B>& r, const GemmArgs& g, int m0, int n0,
                                                      int k0) {
@@ -256,6 +258,9 @@ struct MfmaGemm {
                     if (own_high(c, CA)) r.ah[q] = *reinterpret_cast<const i32x4*>(lo + 16);
                 } else if constexpr (MODE_A == LM_SHIFTED_EDGE) {
                     r.a[q] = load_chunk_shifted<true>(rowp + kc, a_beg, a_end);
+                } else if ((SHIFT & 1) == 0 && kc + CE <= g.K) {
+                    // K tail, a chunk wholly inside K of a 16-byte aligned row
+                    r.a[q] = *reinterpret_cast<const i32x4*>(rowp + kc);
                 } else {
                     r.a[q] = load_chunk_guarded(rowp, kc, g.K);
                 }
@@ -280,6 +285,9 @@ struct MfmaGemm {
                     if (own_high(c, CB)) r.bh[q] = *reinterpret_cast<const i32x4*>(lo + 16);
                 } else if constexpr (MODE_B == LM_SHIFTED_EDGE) {
                     r.b[q] = load_chunk_shifted<true>(rowp + min(nc, g.N - 1), b_beg, b_end);
+                } else if ((SHIFT & 2) == 0 && gk < g.K && nc + CE <= g.N) {
+                    // K tail, a whole chunk of an aligned row that lies inside K
+                    r.b[q] = *reinterpret_cast<const i32x4*>(rowp + nc);
                 } else {
                     r.b[q] = gk < g.K ? load_chunk_guarded(rowp, nc, g.N) : i32x4{0, 0, 0, 0};
                 }
