@@ -143,6 +143,34 @@ def test_short_K_with_deep_rings(dtype):
             assert ok, (_vname(v), K, rep)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "i8"])
+def test_edge_K_across_ring_depths(dtype):
+    # the K edge sweep on every direct-loader ring depth (1-4 and 8 slots,
+    # the production 256 x 256 tile, the half tiles) with ragged M and N:
+    # whole slices only, a partial last slice, fewer slices than the ring
+    # rows 16-byte aligned (A padded to 64 elements per row) so that every
+    # plan runs the requested direct-loader kernel
+    M, N = 129, 272
+    vs = [v for v in _variants(dtype, tiled_only=True)
+          if v.loader == tl.LOADER_DIRECT and v.lds_layout == tl.LDS_XOR]
+    assert {v.stages for v in vs} >= {1, 2, 3, 4, 8}
+    for K in (1, 7, 8, 31, 32, 33, 64, 96, 127, 128, 4104):
+        A = inputs.operand(KIND[dtype], M, K, 17 + K, ld=(K + 63) // 64 * 64)
+        B = inputs.operand(KIND[dtype], K, N, 19 + K)
+        C_ref, S = _oracle(A, B, dtype)
+        first = None
+        for v in vs:
+            name = tl.Plan(M, N, K, DT[dtype], (K + 63) // 64 * 64, N, N, v).name
+            assert "direct" in name, (name, K)
+            C = _run(A, B, variant=v)
+            ok, rep = check(C.numpy(), C_ref, S, dtype, K)
+            assert ok, (_vname(v), K, rep)
+            if first is None:
+                first = C
+            else:
+                assert torch.equal(C, first), (_vname(v), K)
+
+
 def test_fp32_equals_sequential_fma_chain_bitwise():
     for (M, N, K) in [(256, 256, 256), (130, 200, 77)]:
         A = inputs.operand("f32_uniform", M, K, 21 + K)
