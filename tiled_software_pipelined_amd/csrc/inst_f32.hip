@@ -12,6 +12,7 @@ void register_f32(void (*add)(const KernelEntry&)) {
     // 64 x 64 tiles (4 x 4 outputs per lane) for grids that would leave most
     // SIMDs idle on 128 x 128 tiles
     add(f32_entry<2, true, true, true, 16, 64>());
+    add(f32_entry<2, true, true, true, 16, 128, 256>());
     add(f32_entry<2, true, true, true, 32, 64>());
     // the SIMT ladder, one change per rung (the SM80 ablation plan, section
     // 1.5.4): tiling -> + A transposed -> + conflict-free layout ->

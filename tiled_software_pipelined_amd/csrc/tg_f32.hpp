@@ -39,10 +39,11 @@
 
 namespace tg {
 
-template <int STAGES, bool TRANS_A, bool QUARTERS, bool VEC_STORE, int BK_ = 8, int TILE = 128>
+template <int STAGES, bool TRANS_A, bool QUARTERS, bool VEC_STORE, int BK_ = 8, int TILE = 128, int TILE_N = TILE>
 struct F32Gemm {
-    static constexpr int BM = TILE, BN = TILE, BK = BK_, NT = 256;
-    static constexpr int TM = TILE / 16;      // outputs per lane along each side
+    static constexpr int BM = TILE, BN = TILE_N, BK = BK_, NT = 256;
+    static constexpr int TM = BM / 16;        // outputs per lane along M
+    static constexpr int TN = BN / 16;        // outputs per lane along N
     static constexpr int AQ = BK / 4;         // pieces per A row of a slice
     // Row stride of transposed A in floats.  The 4 k-rows of one A piece go
     // to rows kq .. kq+3; AQ lanes with the same m but kq = 0, 4, .. write
@@ -55,15 +56,18 @@ struct F32Gemm {
     static constexpr int B_BYTES = BK * BN * 4;
     static constexpr int SLOT = A_BYTES + B_BYTES;
     static constexpr int LDS_BYTES = STAGES * SLOT;
-    static constexpr int PER = BK * TILE / 4 / NT;  // 16-byte pieces of A and of B per thread per slice
-    static constexpr int N_LD = 2 * PER;
+    static constexpr int PA = BK * BM / 4 / NT;  // 16-byte pieces of A per thread per slice
+    static constexpr int PB = BK * BN / 4 / NT;  // and of B
+    static constexpr int N_LD = PA + PB;
     static constexpr int BQ = BN / 4;         // pieces per B row of a slice
     static_assert(STAGES == 1 || STAGES == 2, "register-staged: 1 or 2 slots");
-    static_assert(TILE == 128 || TILE == 64, "lane blocks of 8 x 8 or 4 x 4");
-    static_assert(PER >= 1 && (BK * TILE / 4) % NT == 0, "whole pieces per thread");
+    static_assert((TM == 4 && TN == 4) || (TM == 8 && TN == 8) || (TM == 8 && TN == 16 && QUARTERS),
+                  "lane blocks of 4 x 4, 8 x 8, or 8 x 16 in the quarter layout");
+    static_assert(PA >= 1 && PB >= 1 && (BK * BM / 4) % NT == 0 && (BK * BN / 4) % NT == 0,
+                  "whole pieces per thread");
 
     struct Staged {
-        f32x4 a[PER], b[PER];
+        f32x4 a[PA], b[PB];
     };
 
     // Piece p = q NT + t (q < PER) of the slice: A[m0 + p / AQ][k0 + 4 (p % AQ) .. +3]
@@ -83,7 +87,7 @@ struct F32Gemm {
         const float* A = static_cast<const float*>(g.A);
         const float* B = static_cast<const float*>(g.B);
 #pragma unroll
-        for (int q = 0; q < PER; ++q) {
+        for (int q = 0; q < PA; ++q) {
             const int p = q * NT + threadIdx.x;
             const float* rowp = A + (int64_t)min(m0 + p / AQ, g.M - 1) * g.lda;
             const int kc = k0 + 4 * (p % AQ);
@@ -95,7 +99,7 @@ struct F32Gemm {
             }
         }
 #pragma unroll
-        for (int q = 0; q < PER; ++q) {
+        for (int q = 0; q < PB; ++q) {
             const int p = q * NT + threadIdx.x;
             const int gk = k0 + p / BQ;
             const int nc = n0 + 4 * (p % BQ);
@@ -113,7 +117,7 @@ struct F32Gemm {
         TG_LDS float* As = reinterpret_cast<TG_LDS float*>(slot);
         TG_LDS float* Bs = reinterpret_cast<TG_LDS float*>(slot + A_BYTES);
 #pragma unroll
-        for (int q = 0; q < PER; ++q) {
+        for (int q = 0; q < PA; ++q) {
             const int p = q * NT + threadIdx.x;
             const int row = p / AQ, kq = 4 * (p % AQ);
             if constexpr (TRANS_A) {
@@ -122,6 +126,10 @@ struct F32Gemm {
             } else {
                 *reinterpret_cast<TG_LDS f32x4*>(As + row * BK + kq) = r.a[q];
             }
+        }
+#pragma unroll
+        for (int q = 0; q < PB; ++q) {
+            const int p = q * NT + threadIdx.x;
             *reinterpret_cast<TG_LDS f32x4*>(Bs + (p / BQ) * BN + 4 * (p % BQ)) = r.b[q];
         }
     }
@@ -134,7 +142,7 @@ struct F32Gemm {
     }
 
     struct Frag {
-        float a[TM], b[TM];
+        float a[TM], b[TN];
     };
 
     __device__ static __forceinline__ void read_frag(Frag& f, const TG_LDS char* slot, int k, int wm, int wn,
@@ -153,7 +161,7 @@ struct F32Gemm {
             for (int i = 0; i < TM; ++i) f.a[i] = As[frag_off(wm, lr, i) * BK + k];
         }
 #pragma unroll
-        for (int h = 0; h < TM / 4; ++h) {
+        for (int h = 0; h < TN / 4; ++h) {
             const f32x4 b = *reinterpret_cast<const TG_LDS f32x4*>(Bs + k * BN + frag_off(wn, lc, 4 * h));
             f.b[4 * h] = b.x; f.b[4 * h + 1] = b.y; f.b[4 * h + 2] = b.z; f.b[4 * h + 3] = b.w;
         }
@@ -164,8 +172,18 @@ struct F32Gemm {
     // stay before it, the next step's after it, and the LDS reads issued for
     // the step after next cannot be hoisted above it (neither the FMAs nor
     // plain LDS loads are ordered by a scheduling barrier alone).
-    __device__ static __forceinline__ void step_fence(float (&c)[TM][TM]) {
-        if constexpr (TM == 8) {
+    __device__ static __forceinline__ void step_fence(float (&c)[TM][TN]) {
+        if constexpr (TN == 16) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                asm volatile(""
+                             : "+v"(c[i][0]), "+v"(c[i][1]), "+v"(c[i][2]), "+v"(c[i][3]), "+v"(c[i][4]),
+                               "+v"(c[i][5]), "+v"(c[i][6]), "+v"(c[i][7]), "+v"(c[i][8]), "+v"(c[i][9]),
+                               "+v"(c[i][10]), "+v"(c[i][11]), "+v"(c[i][12]), "+v"(c[i][13]), "+v"(c[i][14]),
+                               "+v"(c[i][15])
+                             :
+                             : "memory");
+        } else if constexpr (TM == 8) {
 #pragma unroll
             for (int i = 0; i < 8; i += 2)
                 asm volatile(""
@@ -190,7 +208,7 @@ struct F32Gemm {
     // fragments of step k+1 are read while the TM^2 FMAs of step k issue, and a
     // fence per step keeps the compiler from hoisting the reads of the whole
     // slice ahead (which took 219 registers and limited a SIMD to 2 waves).
-    __device__ static __forceinline__ void compute(const TG_LDS char* slot, float (&c)[TM][TM], int wm, int wn,
+    __device__ static __forceinline__ void compute(const TG_LDS char* slot, float (&c)[TM][TN], int wm, int wn,
                                                    int lr, int lc) {
         Frag f[2];
         read_frag(f[0], slot, 0, wm, wn, lr, lc);
@@ -201,7 +219,7 @@ struct F32Gemm {
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int j = 0; j < TM; ++j) c[i][j] = __builtin_fmaf(x.a[i], x.b[j], c[i][j]);
+                for (int j = 0; j < TN; ++j) c[i][j] = __builtin_fmaf(x.a[i], x.b[j], c[i][j]);
             step_fence(c);
         }
     }
@@ -218,11 +236,11 @@ struct F32Gemm {
         const int lr = lane >> 3, lc = lane & 7;
         const int wm = (wave >> 1) * (BM / 2), wn = (wave & 1) * (BN / 2);
 
-        float c[TM][TM];
+        float c[TM][TN];
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int j = 0; j < TM; ++j) c[i][j] = 0.0f;
+            for (int j = 0; j < TN; ++j) c[i][j] = 0.0f;
 
         const int tiles = (g.K + BK - 1) / BK;
         const int full = g.K / BK;
@@ -275,12 +293,12 @@ struct F32Gemm {
             if (vec_ok) {
                 // columns frag_off(wn, lc, 4h .. 4h+3) are 4 contiguous for each h
 #pragma unroll
-                for (int h = 0; h < TM / 4; ++h)
+                for (int h = 0; h < TN / 4; ++h)
                     *reinterpret_cast<f32x4*>(C + (int64_t)row * g.ldc + n0 + frag_off(wn, lc, 4 * h)) =
                         f32x4{c[i][4 * h], c[i][4 * h + 1], c[i][4 * h + 2], c[i][4 * h + 3]};
             } else {
 #pragma unroll
-                for (int j = 0; j < TM; ++j) {
+                for (int j = 0; j < TN; ++j) {
                     const int col = n0 + frag_off(wn, lc, j);
                     if (row < g.M && col < g.N) C[(int64_t)row * g.ldc + col] = c[i][j];
                 }

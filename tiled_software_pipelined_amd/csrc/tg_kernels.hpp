@@ -118,12 +118,12 @@ KernelEntry thin_entry() {
 
 // fp32 ladder rungs: access / frag fields encode TRANS_A and QUARTERS, the
 // layout field VEC_STORE (see inst_f32.hip).
-template <int S, bool TA, bool QU, bool VS, int BK = 8, int TILE = 128>
+template <int S, bool TA, bool QU, bool VS, int BK = 8, int TILE = 128, int TILE_N = TILE>
 KernelEntry f32_entry() {
-    typedef F32Gemm<S, TA, QU, VS, BK, TILE> K;
+    typedef F32Gemm<S, TA, QU, VS, BK, TILE, TILE_N> K;
     // 8 x 8 outputs per lane take ~140 registers (3 waves per SIMD); 4 x 4
     // take few enough for 4
-    constexpr int WAVES = TILE == 128 ? 2 : 4;
+    constexpr int WAVES = TILE == 128 ? 2 : 4;  // 8 x 16 outputs per lane: 2 as well
     KernelEntry e{};
     e.dtype = 0;
     e.family = FAM_TILED;
@@ -147,7 +147,7 @@ KernelEntry f32_entry() {
     e.tail_ok = 1;
     e.waves_per_simd = WAVES;
     e.fn = gemm_kernel<K, WAVES>;
-    snprintf(e.name, sizeof e.name, "f32_t%dx%dx%d_w2x2_s%d_%s_%s_%s", TILE, TILE, BK, S, TA ? "transA" : "rowA",
+    snprintf(e.name, sizeof e.name, "f32_t%dx%dx%d_w2x2_s%d_%s_%s_%s", TILE, TILE_N, BK, S, TA ? "transA" : "rowA",
              QU ? "quarters" : "blocks", VS ? "vecstore" : "scalarstore");
     return e;
 }
