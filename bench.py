@@ -130,6 +130,18 @@ def time_graph(lib, torch, A, B, C, variant, per_graph=20, replays=10):
     return statistics.median(per), same
 
 
+def cpu_model():
+    """The host CPU's model name (Linux), or an empty string."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
 def cpu_baseline(w, A_cpu, B_cpu, budget_s=12.0):
     """The oracle (fp64 / int64 triple loop, OpenMP) on a row sample of the
     same operands: rows are taken until about `budget_s` of CPU work."""
@@ -155,7 +167,7 @@ def cpu_baseline(w, A_cpu, B_cpu, budget_s=12.0):
         rows = int(min(w.M - done_rows, max(8, rows * min(4.0, left / max(t, 1e-3)))))
     flops = 2.0 * done_rows * w.N * w.K
     return {"value": flops / total_t / 1e12, "unit": "TFLOPS" if w.dtype != "i8" else "TOPS",
-            "cores": oracle.num_threads(), "kind": "oracle",
+            "cores": oracle.num_threads(), "cpu_model": cpu_model(), "kind": "oracle",
             "sample": "first %d of %d rows of A times all of B (%s %dx%dx%d), %.1f s" % (
                 done_rows, w.M, w.dtype, w.M, w.N, w.K, total_t)}
 
