@@ -361,10 +361,14 @@ CLOCKED_LAUNCHES = 20
 
 
 def clocked_rate(torch, lib, plan, A, B, C, variant):
-    """(mean shader clock in GHz, per-XCD clocks, per-XCD last end in us) of
-    the plan's tiled kernel over a few launches through gemm_run_clocked, or
-    None when the plan has none to clock or the run repacks operands (the
-    clocked entry runs the plan as gemm_run does)."""
+    """Clock readings of the plan's tiled kernel over a few launches through
+    gemm_run_clocked, or None when the plan has none to clock or the run
+    repacks operands (the clocked entry runs the plan as gemm_run does).
+    Returns a dict: mean shader clock (GHz), per XCD (workgroup w runs on
+    XCD w mod 8) its mean clock and the time from the launch's first
+    workgroup start to that XCD's last end, and the split of the launch into
+    K loop and C write-back (per-workgroup means, and the time from the
+    first start to the last K-loop end vs to the last end)."""
     slots = plan.clock_slots()
     if slots == 0 or (variant is None and plan.workspace_bytes(A.data_ptr(), B.data_ptr()) > 0):
         return None
@@ -374,16 +378,20 @@ def clocked_rate(torch, lib, plan, A, B, C, variant):
         plan.run_clocked_ptr(A.data_ptr(), B.data_ptr(), C.data_ptr(), clocks.data_ptr() + 8 * i * slots, slots,
                              stream)
     torch.cuda.synchronize()
-    c = clocks.cpu().numpy().view("uint64").reshape(CLOCKED_LAUNCHES, -1, 4)
+    nv = lib.CLOCK_VALUES
+    c = clocks.cpu().numpy().view("uint64").reshape(CLOCKED_LAUNCHES, -1, nv)
     ghz = lib.clock_ghz(c)
-    # workgroup w runs on XCD w mod 8 (round-robin dispatch); per XCD, the
-    # mean clock and the time from the launch's first start to its last end
     wg = c.shape[1]
     xcd = [lib.clock_ghz(c[:, x::8]) if x < wg else None for x in range(8)]
     start = c[:, :, 1].min(axis=1).astype("int64")
-    span_us = [float(((c[:, x::8, 3].max(axis=1).astype("int64") - start) * 0.01).mean()) if x < wg else None
+    span_us = [float(((c[:, x::8, 5].max(axis=1).astype("int64") - start) * 0.01).mean()) if x < wg else None
                for x in range(8)]
-    return ghz, xcd, span_us
+    loop_us, store_us = lib.clock_split_us(c)
+    last_loop = float(((c[:, :, 3].max(axis=1).astype("int64") - start) * 0.01).mean())
+    last_end = float(((c[:, :, 5].max(axis=1).astype("int64") - start) * 0.01).mean())
+    return {"ghz": ghz, "xcd_ghz": xcd, "xcd_last_end_us": span_us,
+            "wg_loop_us": float(loop_us.mean()), "wg_store_us": float(store_us.mean()),
+            "last_loop_end_us": last_loop, "last_end_us": last_end}
 
 
 def env_record(torch, lib, dev):
@@ -537,8 +545,10 @@ def main():
 
     variant = parse_variant(args.variant, lib)
     kernel_ms, wall = time_region(lib, torch, A, B, C, variant, args.steps, args.warmup)
-    # after the timed region: per-launch events, for the fastest launch
-    per, _ = time_plan(lib, torch, w, A, B, C, variant, min(args.steps, 20), 0)
+    # after the timed region, one pass with a pair of events around every
+    # launch: the per-launch distribution (median, min, max) of that pass
+    per, _ = time_plan(lib, torch, w, A, B, C, variant, args.steps, 0)
+    per_sorted = sorted(per)
     code = {"f32": lib.F32, "bf16": lib.BF16, "i8": lib.I8}[w.dtype]
     plan = lib.plan_for(w.M, w.N, w.K, code, w.K, w.N, w.N, variant)
     ms_step = wall * 1e3 / args.steps
@@ -573,27 +583,37 @@ def main():
         "roofline": {"bound": "mfma" if w.dtype != "f32" else "alu", "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s" if w.dtype != "i8" else "TOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "traffic_unit": "bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-scaled)",
+                     "traffic_unit": "bytes per launch between L2 and the memory fabric (FETCH_SIZE + "
+                                     "WRITE_SIZE, copy-scaled): L2-miss bytes, which the 256 MB MALL may serve "
+                                     "without reaching HBM",
                      "traffic_source": prof["path"] if prof else None,
                      "kernel_ms_mean": round(kernel_ms, 5),
-                     "kernel_ms_min": round(min(per), 5),
-                     "timing": "kernel_ms_mean: HIP events at the two ends of the timed region / steps; "
-                               "kernel_ms_min: per-launch events in a pass after it"},
+                     "per_launch_ms": {"median": round(per_sorted[len(per_sorted) // 2], 5),
+                                       "min": round(per_sorted[0], 5), "max": round(per_sorted[-1], 5),
+                                       "launches": len(per_sorted)},
+                     "timing": "kernel_ms_mean (used for achieved): HIP events on the launch stream at the two "
+                               "ends of the timed region / steps; per_launch_ms: one further pass of the same "
+                               "number of launches with a pair of events around each launch (the events add "
+                               "their own commands between kernels, so these are slightly longer)"},
         "cpu_baseline": None,
         "env": env_record(torch, lib, dev),
     }
     clk = clocked_rate(torch, lib, plan, A, B, C, variant)
     if clk is not None:
-        ghz, xcd, span = clk
-        at_clock = peak * ghz / NOMINAL_GHZ
+        at_clock = peak * clk["ghz"] / NOMINAL_GHZ
         rec["roofline"]["clock"] = {
-            "ghz": round(ghz, 3), "peak_at_clock": round(at_clock, 1), "frac": round(achieved / at_clock, 4),
-            "xcd_ghz": [round(x, 3) if x is not None else None for x in xcd],
-            "xcd_last_end_us": [round(x, 2) if x is not None else None for x in span],
-            "source": "s_memtime / s_memrealtime of every workgroup over %d launches right after the timed "
-                      "region; peak scaled from %.1f GHz; per XCD (workgroup mod 8): mean clock and time "
-                      "from the launch's first workgroup start to that XCD's last end" % (CLOCKED_LAUNCHES,
-                                                                                          NOMINAL_GHZ)}
+            "ghz": round(clk["ghz"], 3), "peak_at_clock": round(at_clock, 1),
+            "frac": round(achieved / at_clock, 4),
+            "xcd_ghz": [round(x, 3) if x is not None else None for x in clk["xcd_ghz"]],
+            "xcd_last_end_us": [round(x, 2) if x is not None else None for x in clk["xcd_last_end_us"]],
+            "wg_loop_us": round(clk["wg_loop_us"], 2), "wg_store_us": round(clk["wg_store_us"], 2),
+            "last_loop_end_us": round(clk["last_loop_end_us"], 2), "last_end_us": round(clk["last_end_us"], 2),
+            "source": "s_memtime / s_memrealtime of every workgroup (start, end of its K loop, end) over %d "
+                      "launches right after the timed region; peak scaled from %.1f GHz; per XCD (workgroup "
+                      "mod 8): mean clock and time from the launch's first workgroup start to that XCD's last "
+                      "end; wg_loop_us / wg_store_us: per-workgroup means of K loop and C write-back; "
+                      "last_loop_end_us / last_end_us: from the first start to the last K-loop end / last "
+                      "end" % (CLOCKED_LAUNCHES, NOMINAL_GHZ)}
     if not args.calib_copy:
         # the rate the arithmetic units sustain on this machine for the
         # workload's operand distribution with no memory traffic at all (the

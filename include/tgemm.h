@@ -19,18 +19,20 @@
  *                one fma chain per output in increasing k)
  *   TGEMM_BF16 : bf16     x bf16     -> float   (matrix cores, fp32 accumulate)
  *   TGEMM_I8   : int8     x int8     -> int32   (matrix cores, exact int32
- *                accumulate; exact while |C| < 2^31, i.e. K <= 131072)
+ *                accumulate; |C| <= 16384 K stays below 2^31 for every
+ *                input while K <= 131071, the largest K a plan accepts)
  * bf16 operands are passed as their raw 16-bit patterns.
  *
  * The K loop is software-pipelined as the "流水化 GPU 内核" (pipelining GPU
  * kernels) skill, Step 3, and the GEMM page, sections 9-10, describe: tiles of
- * A and B move global -> LDS through a ring of 1-4 stages while the matrix
- * cores work on an earlier stage.
+ * A and B move global -> LDS through a ring of 1-4 stages (8 for the
+ * smallest tiles) while the matrix cores work on an earlier stage.
  *
  * Ownership.  The caller owns A, B, C and the stream.  The library allocates
- * no device memory and never copies or pads inputs.  A plan holds only host
- * metadata; it is immutable after creation, so one plan may be run
- * concurrently on several streams.
+ * no device memory.  gemm_run never copies or pads inputs; gemm_run_ws
+ * copies misaligned operands into the workspace the caller passes.  A plan
+ * holds only host metadata; it is immutable after creation, so one plan may
+ * be run concurrently on several streams.
  *
  * Errors.  gemm_plan* return NULL and record a message (tgemm_last_error) on
  * invalid arguments.  gemm_run returns TGEMM_OK once the kernel is enqueued,
@@ -114,7 +116,7 @@ typedef struct tgemm_variant {
     int32_t tile_m;     /* workgroup tile rows (BM) */
     int32_t tile_n;     /* workgroup tile columns (BN) */
     int32_t tile_k;     /* K step per stage (BK), in elements */
-    int32_t stages;     /* LDS stages in the ring: 1 (no pipelining) .. 4 */
+    int32_t stages;     /* LDS stages in the ring: 1 (no pipelining) .. 4, or 8 (64 x 64 tiles) */
     int32_t loader;     /* TGEMM_LOADER_* */
     int32_t lds_layout; /* TGEMM_LDS_* */
     int32_t access;     /* TGEMM_ACCESS_* */
@@ -221,20 +223,23 @@ int gemm_plan_get_info(const tgemm_plan* plan, tgemm_plan_info* info);
  * the shader clock, which the power budget lowers under load).
  * gemm_run_clocked is gemm_run, except that every workgroup of the plan's
  * tiled kernel (matrix-core or fp32; a split plan's thin remainder is not
- * clocked) writes four values to clocks[4 w .. 4 w + 3], w its workgroup
- * index: the shader-clock counter (s_memtime) and the 100 MHz real-time
- * counter (s_memrealtime) when it starts, then both again once all its
+ * clocked) writes TGEMM_CLOCK_VALUES = 6 values to clocks[6 w .. 6 w + 5],
+ * w its workgroup index: the shader-clock counter (s_memtime) and the
+ * 100 MHz real-time counter (s_memrealtime) when it starts; both again when
+ * its first wave leaves the K loop, before any C store; and both once all its
  * memory instructions, the C stores included, have completed.  Summed over
  * workgroups, (end - start shader ticks) / (end - start real ticks) x 100 MHz
- * is the mean shader clock of the run.  The C written is the same as
- * gemm_run's, bit for bit.
+ * is the mean shader clock of the run, and the middle pair splits each
+ * workgroup's time into its K loop and its C write-back.  The C written is
+ * the same as gemm_run's, bit for bit.
  * clocks: device memory owned by the caller, 8-byte aligned, clocks_len
  * values; gemm_clock_slots(plan) values always suffice (it is the largest
- * grid among the kernels the plan may launch, times 4; 0 for a plan that
+ * grid among the kernels the plan may launch, times 6; 0 for a plan that
  * launches no tiled kernel, including empty products).
  * Returns what gemm_run returns, or TGEMM_E_NULL (NULL plan or clocks),
  * TGEMM_E_ARG (nothing to clock, or clocks_len below what the launched
  * kernel needs: then nothing is launched) or TGEMM_E_ALIGN. */
+#define TGEMM_CLOCK_VALUES 6
 int64_t gemm_clock_slots(const tgemm_plan* plan);
 int gemm_run_clocked(const tgemm_plan* plan, const void* A, const void* B, void* C, uint64_t* clocks,
                      int64_t clocks_len, void* stream);

@@ -43,12 +43,26 @@ def test_version():
     (4, 8, 4, tl.BF16, 4, 7, 8),          # ldb < N
     (4, 8, 4, tl.BF16, 4, 8, 7),          # ldc < N
     (4, 4, 200000, tl.I8, 200000, 4, 4),  # int8 K beyond exact int32 range
+    (4, 4, 131072, tl.I8, 131072, 4, 4),  # 16384 * 131072 = 2^31 wraps int32
     (2 ** 31, 4, 4, tl.F32, 4, 4, 4),     # too large
 ])
 def test_plan_rejects_invalid(args):
     with pytest.raises(tl.TgemmError):
         tl.Plan(*args)
     assert tl.last_error() != ""
+
+
+def test_int8_largest_exact_K_is_accepted():
+    # |C| <= 128 * 128 * K = 2147467264 < 2^31 at K = 131071
+    assert 128 * 128 * 131071 < 2 ** 31 <= 128 * 128 * 131072
+    assert tl.Plan(4, 4, 131071, tl.I8, 131071, 4, 4).K == 131071
+
+
+def test_huge_workgroup_group_is_accepted():
+    # any group of at least tiles_m rows gives one group of all tile rows;
+    # the run clamps it (the GPU test checks the result)
+    v = tl.Variant(kernel=tl.KERNEL_TILED, tile_m=128, tile_n=128, wg_group=1 << 30)
+    assert tl.Plan(512, 512, 64, tl.BF16, variant=v).info().variant.wg_group == 1 << 30
 
 
 def test_plan_run_rejects_null_plan():
@@ -66,9 +80,9 @@ def test_occupancy_rejects_null_arguments():
 def test_clock_slots_and_null_arguments():
     # host-only: the count covers the largest grid the plan may launch
     p = tl.Plan(4096, 4096, 4096, tl.BF16)
-    assert p.clock_slots() == 4 * p.info().grid == 4 * 256
+    assert p.clock_slots() == tl.CLOCK_VALUES * p.info().grid == 6 * 256
     q = tl.Plan(4096, 4096, 4096, tl.BF16, 4096, 4097, 4096)  # B rows unaligned: register-staged
-    assert q.clock_slots() >= 4 * q.info().grid
+    assert q.clock_slots() >= tl.CLOCK_VALUES * q.info().grid
     assert tl.Plan(0, 64, 64, tl.BF16).clock_slots() == 0
     assert tl.Plan(64, 64, 0, tl.BF16, 1, 64, 64).clock_slots() == 0
     assert tl._lib.gemm_clock_slots(None) == 0
@@ -80,9 +94,11 @@ def test_clock_slots_and_null_arguments():
 
 def test_clock_ghz_arithmetic():
     # two workgroups: 2.0e6 and 1.0e6 shader ticks over 1000 and 1000 real ticks (10 us each)
-    c = [[0, 0, 2_000_000, 1000], [5, 7, 1_000_005, 1007]]
+    c = [[0, 0, 1_500_000, 700, 2_000_000, 1000], [5, 7, 900_005, 907, 1_000_005, 1007]]
     assert abs(tl.clock_ghz(c) - 3.0e6 / 2000 * 0.1 / 1000 * 1000) < 1e-12
-    assert abs(tl.clock_ghz([[0, 0, 240, 10]]) - 2.4) < 1e-12
+    assert abs(tl.clock_ghz([[0, 0, 100, 4, 240, 10]]) - 2.4) < 1e-12
+    loop, store = tl.clock_split_us(c)
+    assert list(loop) == [7.0, 9.0] and list(store) == [3.0, 1.0]
 
 
 def test_run_with_empty_output_is_a_noop_without_device():

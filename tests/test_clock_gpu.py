@@ -1,6 +1,7 @@
 """GPU: gemm_run_clocked writes the same C as gemm_run and, per workgroup of
-the tiled kernel, start / end readings of the shader-clock and 100 MHz
-real-time counters from which the run's mean shader clock follows."""
+the tiled kernel, start / K-loop-end / end readings of the shader-clock and
+100 MHz real-time counters from which the run's mean shader clock and its
+split into K loop and C write-back follow."""
 import numpy as np
 import pytest
 import torch
@@ -33,10 +34,10 @@ def test_clocked_run_matches_and_reads_a_plausible_clock(kind, dt, M, N, K):
     out_dtype = torch.int32 if dt == "I8" else torch.float32
     p = tl.Plan(M, N, K, getattr(tl, dt))
     slots = p.clock_slots()
-    assert slots == 4 * p.info().grid
+    assert slots == tl.CLOCK_VALUES * p.info().grid
     C0 = torch.full((M, N), -7, dtype=out_dtype, device="cuda")
     C1 = torch.full((M, N), -5, dtype=out_dtype, device="cuda")
-    clocks = torch.zeros(slots + 4, dtype=torch.int64, device="cuda")
+    clocks = torch.zeros(slots + tl.CLOCK_VALUES, dtype=torch.int64, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
     p.run_ptr(A.data_ptr(), B.data_ptr(), C0.data_ptr(), stream)
     p.run_clocked_ptr(A.data_ptr(), B.data_ptr(), C1.data_ptr(), clocks.data_ptr(), slots, stream)
@@ -44,8 +45,12 @@ def test_clocked_run_matches_and_reads_a_plausible_clock(kind, dt, M, N, K):
     assert torch.equal(C0, C1)
     c = clocks.cpu().numpy().view(np.uint64)
     assert (c[slots:] == 0).all()  # nothing past the slots the plan needs
-    c = c[:slots].reshape(-1, 4)
-    assert (c[:, 2] > c[:, 0]).all() and (c[:, 3] > c[:, 1]).all()
+    c = c[:slots].reshape(-1, tl.CLOCK_VALUES)
+    # start <= K-loop end <= end, for both counters
+    assert (c[:, 2] > c[:, 0]).all() and (c[:, 3] >= c[:, 1]).all()
+    assert (c[:, 4] > c[:, 2]).all() and (c[:, 5] >= c[:, 3]).all() and (c[:, 5] > c[:, 1]).all()
+    loop_us, store_us = tl.clock_split_us(c)
+    assert (loop_us >= 0).all() and (store_us >= 0).all() and loop_us.sum() > 0
     ghz = tl.clock_ghz(c)
     assert 0.3 < ghz < 3.0, ghz
 

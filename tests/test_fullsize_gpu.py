@@ -1,0 +1,133 @@
+"""GPU parity at the workloads' own sizes: every output compared with the oracle.
+
+Each workload (fp32 256^3 and 4096^3, bf16 4096^3, int8 4096^3, the ten bf16
+sweep shapes, the ragged bf16 4095 x 4097 x 4104 and the 512 x 4096 x 4096
+one-GPU share) runs through the C ABI in the launch configuration the
+benchmark times, and all M x N outputs are compared with the oracle computed
+once per workload: int8 exactly, bf16 and fp32 by the per-element gates of
+tests/parity.py, and the fp32 kernels bit for bit with the sequential fp32
+fma chain.  Besides the default plan, each workload also runs the kernels
+whose speed the ladder and the sweep report on it: the 128 x 128 x 32 tile
+at 2, 3 and 4 stages on bf16 4096^3, every loader / ring depth of the sweep
+on every sweep shape, and both unaligned-row paths (repack into a workspace,
+shifted loads in place) on the ragged product.  Every matrix-core result of
+one workload must also be the same bit for bit (pipelining only reorders
+loads: the "流水化 GPU 内核" skill, Step 5; the SM80 ablation plan, section
+1.3).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import check
+from tiled_software_pipelined_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+tl = None
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    global tl
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from tiled_software_pipelined_amd import lib  # must load: there is no fallback
+    tl = lib
+    yield
+
+
+def _variant(**kw):
+    return tl.Variant(kernel=tl.KERNEL_TILED, **kw)
+
+
+def _extra_variants(w):
+    """(label, variant, workspace) of the kernels besides the default plan."""
+    out = []
+    if w.name == "bf16_4096" or w.name.startswith("bf16_sweep"):
+        # the tile of the 4096^3 configuration at 2 / 3 / 4 stages (direct
+        # loader), then the sweep's other loaders on the same tile
+        for st in (2, 3, 4):
+            out.append(("t128x128x32_direct_s%d" % st,
+                        _variant(tile_m=128, tile_n=128, tile_k=32, stages=st, loader=tl.LOADER_DIRECT,
+                                 waves_m=2, waves_n=2), False))
+        out.append(("t128x128x32_vgpr_s2", _variant(tile_m=128, tile_n=128, tile_k=32, stages=2,
+                                                     loader=tl.LOADER_VGPR, lds_layout=tl.LDS_XOR,
+                                                     waves_m=2, waves_n=2), False))
+        out.append(("t128x128x32_direct_s1", _variant(tile_m=128, tile_n=128, tile_k=32, stages=1,
+                                                       loader=tl.LOADER_DIRECT, waves_m=2, waves_n=2), False))
+    if w.name == "i8_4096":
+        for st in (2, 3, 4):
+            out.append(("t128x128x64_direct_s%d" % st,
+                        _variant(tile_m=128, tile_n=128, tile_k=64, stages=st, loader=tl.LOADER_DIRECT,
+                                 waves_m=2, waves_n=2), False))
+    if w.name.startswith("bf16_ragged"):
+        # B's rows (4097 bf16) are not 16-byte aligned: the default run
+        # repacks B into a workspace; without one the shifted-load kernel
+        # reads it in place
+        out.append(("default_in_place", None, False))
+    return out
+
+
+def _run(w, A, B, variant, workspace):
+    out_dtype = torch.int32 if w.dtype == "i8" else torch.float32
+    C = torch.full((w.M, w.N), -7, dtype=out_dtype, device="cuda")
+    tl.gemm(A, B, out=C, variant=variant, workspace=workspace)
+    torch.cuda.synchronize()
+    return C
+
+
+NAMES = sorted(inputs.workloads())
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_workload_in_full(name):
+    w = inputs.workloads()[name]
+    A_cpu, B_cpu = w.operands()
+    print("workload", name, "oracle ...", flush=True)
+    C_ref, S = oracle.gemm(inputs.as_oracle_array(A_cpu), inputs.as_oracle_array(B_cpu), w.dtype)
+    chain = oracle.gemm_f32_fma_chain(A_cpu.numpy(), B_cpu.numpy()) if w.dtype == "f32" else None
+    A, B = A_cpu.cuda(), B_cpu.cuda()
+    runs = [("default", None, True)] + _extra_variants(w)
+    first = None
+    for label, v, ws in runs:
+        kname = tl.plan_for(w.M, w.N, w.K, {"f32": tl.F32, "bf16": tl.BF16, "i8": tl.I8}[w.dtype],
+                            w.K, w.N, w.N, v).kernel_for(A.data_ptr(), B.data_ptr(), workspace=ws and v is None)
+        print("  ", label, kname, flush=True)
+        C = _run(w, A, B, v, ws)
+        Ch = C.cpu().numpy()
+        ok, rep = check(Ch, C_ref, S, w.dtype, w.K)
+        assert ok, (name, label, kname, rep)
+        if w.dtype == "i8":
+            assert np.array_equal(Ch.astype(np.int64), C_ref), (name, label)
+        if chain is not None:
+            bad = int((Ch != chain).sum())
+            assert bad == 0, (name, label, "differs from the fp32 fma chain at %d outputs" % bad)
+        if w.dtype != "f32" and label != "default_in_place":
+            # one matrix-core K order for every tile, ring depth and loader
+            if first is None:
+                first = C
+            else:
+                assert torch.equal(C, first), (name, label)
+        del C
+
+
+def test_in_place_and_repacked_ragged_agree_off_the_thin_columns():
+    # the two unaligned-row paths of the ragged product give the same bits
+    # wherever both run matrix-core tiles (the thin kernel takes the last
+    # column in both plans here)
+    w = inputs.workloads()["bf16_ragged_4095x4097x4104"]
+    A_cpu, B_cpu = w.operands()
+    A, B = A_cpu.cuda(), B_cpu.cuda()
+    p = tl.plan_for(w.M, w.N, w.K, tl.BF16, w.K, w.N, w.N)
+    info = p.info()
+    print("ragged plans:", info.name.decode(), info.rem_name.decode(), info.packed_name.decode(), flush=True)
+    C_ws = _run(w, A, B, None, True)
+    C_in = _run(w, A, B, None, False)
+    # a split plan gives the thin kernel only the N mod (tile width) <= 16
+    # columns past the last whole tile column; the first 4096 columns are
+    # tile columns in every plan of this shape (tile widths 128 and 256)
+    n = w.N - w.N % 128
+    assert n == 4096
+    assert torch.equal(C_ws[:, :n], C_in[:, :n])

@@ -38,6 +38,22 @@ MUTATIONS = [
      "double a = bf16_bits_to_double(A[i * K + k]);"),
     ("fma_chain_unfused", "for (int64_t j = 0; j < N; ++j) c[j] = fmaf(a, b[j], c[j]);",
      "for (int64_t j = 0; j < N; ++j) c[j] = c[j] + a * b[j];"),
+    # the sampled (one dot product per position) functions
+    ("f32_sampled_ldb_ignored", "double q = (double)A[i * lda + k] * (double)B[k * ldb + j];",
+     "double q = (double)A[i * lda + k] * (double)B[k * N + j];"),
+    ("f32_sampled_companion_not_abs", "            s += fabs(q);", "            s += q;"),
+    ("bf16_sampled_drops_last_k",
+     "for (int64_t k = 0; k < K; ++k) {\n            double q = bf16_bits_to_double(A[i * lda + k]) *",
+     "for (int64_t k = 0; k < K - 1; ++k) {\n            double q = bf16_bits_to_double(A[i * lda + k]) *"),
+    ("bf16_sampled_ldb_ignored", "bf16_bits_to_double(B[k * ldb + j]);", "bf16_bits_to_double(B[k * N + j]);"),
+    ("i8_sampled_lda_as_K", "c += (int64_t)A[i * lda + k] * (int64_t)B[k * ldb + j];",
+     "c += (int64_t)A[i * K + k] * (int64_t)B[k * ldb + j];"),
+    ("i8_sampled_ldb_ignored", "c += (int64_t)A[i * lda + k] * (int64_t)B[k * ldb + j];",
+     "c += (int64_t)A[i * lda + k] * (int64_t)B[k * N + j];"),
+    ("fma_chain_sampled_unfused", "c = fmaf(A[i * lda + k], B[k * ldb + j], c);",
+     "c = c + A[i * lda + k] * B[k * ldb + j];"),
+    ("fma_chain_sampled_ldb_ignored", "c = fmaf(A[i * lda + k], B[k * ldb + j], c);",
+     "c = fmaf(A[i * lda + k], B[k * N + j], c);"),
 ]
 
 
@@ -56,6 +72,9 @@ def _pins():
     out.append(pins.test_int8_extremes)
     out.append(lambda: pins.test_fma_chain_exact_emulation(3, 4, 50))
     out.append(pins.test_fma_chain_differs_from_unfused_rounding)
+    for dtype in ("f32", "bf16", "i8"):
+        out.append(lambda d=dtype: pins.test_sampled_brute_force_exact(d))
+    out.append(pins.test_sampled_fma_chain_exact_emulation)
     return out
 
 

@@ -232,28 +232,67 @@ def test_fma_chain_differs_from_unfused_rounding():
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "i8"])
 def test_sampled_matches_full(dtype):
+    # both operands row-padded with a non-zero filler: a sampled function that
+    # ignored lda or ldb would read the filler
     kind = {"f32": "f32_uniform", "bf16": "bf16_normal", "i8": "i8_uniform"}[dtype]
     M, N, K = 67, 45, 130
     A = inputs.as_oracle_array(inputs.operand(kind, M, K, 1, ld=K + 8))
-    B = inputs.as_oracle_array(inputs.operand(kind, K, N, 2))
+    B = inputs.as_oracle_array(inputs.operand(kind, K, N, 2, ld=N + 7))
     C, S = oracle.gemm(A, B, dtype)
     rng = np.random.default_rng(0)
-    rows = rng.integers(0, M, 200)
-    cols = rng.integers(0, N, 200)
+    rows = np.concatenate([rng.integers(0, M, 200), [0, M - 1, M - 1, 0]])
+    cols = np.concatenate([rng.integers(0, N, 200), [0, N - 1, 0, N - 1]])
     Cs, Ss = oracle.gemm_sampled(A, B, rows, cols, dtype)
     np.testing.assert_array_equal(Cs, C[rows, cols])
     if S is not None:
         np.testing.assert_array_equal(Ss, S[rows, cols])
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i8"])
+def test_sampled_brute_force_exact(dtype):
+    # the sampled functions on their own against exact rational sums, with
+    # padded A and B (not only through the full oracle)
+    kind = {"f32": "f32_uniform", "bf16": "bf16_normal", "i8": "i8_uniform"}[dtype]
+    M, N, K = 6, 9, 37
+    A = inputs.operand(kind, M, K, 41, ld=K + 3)
+    B = inputs.operand(kind, K, N, 42, ld=N + 5)
+    Af = A.float().numpy() if dtype == "bf16" else A.numpy()
+    Bf = B.float().numpy() if dtype == "bf16" else B.numpy()
+    Cx, Sx = _exact_product(Af, Bf)
+    rows = np.array([i for i in range(M) for _ in range(N)])
+    cols = np.array([j for _ in range(M) for j in range(N)])
+    Cs, Ss = oracle.gemm_sampled(inputs.as_oracle_array(A), inputs.as_oracle_array(B), rows, cols, dtype)
+    bound_rel = Fraction(K, 2 ** 52)
+    for p in range(rows.shape[0]):
+        i, j = rows[p], cols[p]
+        if dtype == "i8":
+            assert int(Cs[p]) == Cx[i][j]
+        else:
+            assert abs(Fraction(float(Cs[p])) - Cx[i][j]) <= bound_rel * Sx[i][j], (i, j)
+            assert abs(Fraction(float(Ss[p])) - Sx[i][j]) <= bound_rel * Sx[i][j], (i, j)
+
+
 def test_sampled_fma_chain_matches_full():
-    A = inputs.operand("f32_uniform", 20, 77, 3).numpy()
-    B = inputs.operand("f32_uniform", 77, 19, 4).numpy()
+    A = inputs.operand("f32_uniform", 20, 77, 3, ld=80).numpy()
+    B = inputs.operand("f32_uniform", 77, 19, 4, ld=23).numpy()
     C = oracle.gemm_f32_fma_chain(A, B)
     rows = np.array([0, 19, 5, 7])
     cols = np.array([18, 0, 5, 11])
     Cs, _ = oracle.gemm_sampled(A, B, rows, cols, "f32", fma_chain=True)
     np.testing.assert_array_equal(Cs, C[rows, cols])
+
+
+def test_sampled_fma_chain_exact_emulation():
+    A = inputs.operand("f32_uniform", 3, 60, 5, ld=63).numpy()
+    B = inputs.operand("f32_uniform", 60, 4, 6, ld=9).numpy()
+    rows = np.array([0, 2, 1])
+    cols = np.array([3, 0, 2])
+    Cs, _ = oracle.gemm_sampled(A, B, rows, cols, "f32", fma_chain=True)
+    for p in range(3):
+        acc = Fraction(0)
+        for k in range(60):
+            acc = _round_f32(Fraction(float(A[rows[p], k])) * Fraction(float(B[k, cols[p]])) + acc)
+        assert Cs[p] == np.float32(float(acc)), p
 
 
 def test_K_zero_gives_zeros():

@@ -16,8 +16,20 @@ def _write(path, header, rows):
         w.writerows(rows)
 
 
+def _passes(out, rcs, start=0.0):
+    """passes.json as collect() writes it: every pass started at `start`."""
+    import json
+    os.makedirs(str(out), exist_ok=True)
+    with open(str(out / profiling.PASSES_FILE), "w") as f:
+        json.dump({name: {"rc": rc, "start": start} for name, rc in rcs.items()}, f)
+
+
+ALL_OK = {"trace": 0, "pmc0": 0, "pmc1": 0, "pmc2": 0, "pmc3": 0, "pmc4": 0}
+
+
 def test_split_plan_sums_its_kernels(tmp_path):
     out = tmp_path / "prof"
+    _passes(out, ALL_OK)
     main = "void tg::gemm_kernel<tg::MfmaGemm<...>, 2>(tg::GemmArgs)"
     thin = "void tg::gemm_kernel<tg::ThinGemm<1, 1>, 2>(tg::GemmArgs)"
     _write(str(out / "trace" / "x" / "trace_kernel_stats.csv"),
@@ -87,3 +99,45 @@ def test_runtime_occupancy_line(tmp_path):
     with open(out / profiling.OCC_FILE, "w") as f:
         json.dump({"kernel": "some_other_kernel", "workgroups_per_cu": 3}, f)
     assert profiling._runtime_occupancy(args, w, res) is None
+
+
+def _one_fetch_pass(out):
+    main = "void tg::gemm_kernel<tg::MfmaGemm<...>, 2>(tg::GemmArgs)"
+    _write(str(out / "pmc2" / "x" / "pmc_counter_collection.csv"), ["Kernel_Name", "Counter_Name", "Counter_Value"],
+           [[main, "FETCH_SIZE", 1000.0], ["elementwise_copy_kernel", "FETCH_SIZE", 512.0]])
+    return types.SimpleNamespace(out=str(out), workload="bf16_4096", variant="", steps=20, warmup=5)
+
+
+def test_pass_without_record_is_not_used(tmp_path):
+    out = tmp_path / "prof"
+    args = _one_fetch_pass(out)
+    res = profiling.summarize(args, {})
+    assert "FETCH_SIZE" not in res["counters"]
+    assert res["passes"]["pmc2"]["status"].startswith("no record")
+
+
+def test_stale_csv_is_not_used(tmp_path):
+    import time
+    out = tmp_path / "prof"
+    args = _one_fetch_pass(out)
+    _passes(out, {"pmc2": 0}, start=time.time() + 3600)  # the file predates the pass
+    res = profiling.summarize(args, {})
+    assert "FETCH_SIZE" not in res["counters"] and res["passes"]["pmc2"]["status"].startswith("stale")
+
+
+def test_killed_pass_without_csv_is_reported(tmp_path):
+    out = tmp_path / "prof"
+    _passes(out, {"trace": 0, "pmc2": 137})
+    args = types.SimpleNamespace(out=str(out), workload="bf16_4096", variant="", steps=20, warmup=5)
+    res = profiling.summarize(args, {})
+    assert res["passes"]["pmc2"] == {"rc": 137, "csv": None, "status": "no CSV written"}
+    assert res["counters"] == {}
+
+
+def test_fresh_csv_with_nonzero_exit_is_used_and_flagged(tmp_path):
+    out = tmp_path / "prof"
+    args = _one_fetch_pass(out)
+    _passes(out, {"pmc2": 139}, start=0.0)
+    res = profiling.summarize(args, {})
+    assert res["counters"]["FETCH_SIZE"] == 1000.0
+    assert res["passes"]["pmc2"]["status"] == "ok (CSV complete; exit status 139)"

@@ -19,11 +19,15 @@ struct GemmArgs {
     int32_t a_guard;           // 1: A rows not 16-byte aligned (kernels with shift_mask bit 0)
     int32_t b_guard;           // 1: B rows not 16-byte aligned or N not a whole number of chunks (bit 1)
     int32_t c_stream;          // 1: C rows 128-byte aligned: non-temporal (streaming) C stores
-    uint64_t* clocks;          // NULL, or 4 values per workgroup (tiled kernels): shader-clock and
-                               // 100 MHz real-time counters at its start, then at its end
+    uint64_t* clocks;          // NULL, or 6 values per workgroup (tiled kernels): shader-clock and
+                               // 100 MHz real-time counters at its start, at the end of its
+                               // K loop, then at its end
 };
 
 typedef void (*KernelFn)(GemmArgs);
+
+// Values per workgroup in GemmArgs::clocks (TGEMM_CLOCK_VALUES of the C ABI).
+constexpr int CLOCK_VALUES = 6;
 
 // Widest N the thin kernel (and the remainder of a split plan) takes.
 constexpr int THIN_N_MAX = 16;

@@ -43,29 +43,40 @@ __device__ __forceinline__ void wait_all_then_barrier() {
 }
 
 // Clock marks of a workgroup (GemmArgs::clocks): the shader-clock counter
-// (s_memtime) and the 100 MHz real-time counter (s_memrealtime).  The end
-// mark is taken once every wave's memory instructions, C stores included,
-// have completed; thread 0 writes [start shader, start real, end shader,
-// end real] to clocks[4 * workgroup ..] with vector stores.
+// (s_memtime) and the 100 MHz real-time counter (s_memrealtime), read when
+// the workgroup starts, when wave 0 leaves the K loop (before its C stores)
+// and once every wave's memory instructions, the C stores included, have
+// completed.  Thread 0 writes [start shader, start real, loop-end shader,
+// loop-end real, end shader, end real] to clocks[CLOCK_VALUES * workgroup ..]
+// with vector stores.
+
 struct ClockMark {
-    uint64_t c0 = 0, w0 = 0;
+    uint64_t c0 = 0, w0 = 0, c1 = 0, w1 = 0;
     __device__ __forceinline__ void start(const uint64_t* clocks) {
         if (clocks) {
             c0 = __builtin_amdgcn_s_memtime();
             w0 = __builtin_amdgcn_s_memrealtime();
         }
     }
+    __device__ __forceinline__ void loop_end(const uint64_t* clocks) {
+        if (clocks) {
+            c1 = __builtin_amdgcn_s_memtime();
+            w1 = __builtin_amdgcn_s_memrealtime();
+        }
+    }
     __device__ __forceinline__ void finish(uint64_t* clocks) const {
         if (clocks) {
             wait_all_then_barrier();
-            const uint64_t c1 = __builtin_amdgcn_s_memtime();
-            const uint64_t w1 = __builtin_amdgcn_s_memrealtime();
+            const uint64_t c2 = __builtin_amdgcn_s_memtime();
+            const uint64_t w2 = __builtin_amdgcn_s_memrealtime();
             if (threadIdx.x == 0) {
-                uint64_t* p = clocks + 4 * (uint64_t)blockIdx.x;
+                uint64_t* p = clocks + CLOCK_VALUES * (uint64_t)blockIdx.x;
                 p[0] = c0;
                 p[1] = w0;
                 p[2] = c1;
                 p[3] = w1;
+                p[4] = c2;
+                p[5] = w2;
             }
         }
     }
@@ -79,7 +90,10 @@ struct ClockMark {
 // finish before each read and serialise the pipeline); completion is tracked
 // explicitly with wait_vm_then_barrier.  M0 is written here: the kernels that
 // use this issue every LDS copy through it and nothing else of theirs uses
-// M0.
+// M0.  On gfx9-family chips a global/buffer load with LDS=1 that follows a
+// scalar write of M0 needs one wait state in between, which the hardware
+// does not insert and the compiler only inserts between instructions it
+// emits itself, so the asm carries its own s_nop 0.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void copy16_to_lds(uint32_t lds, uint32_t voff, const void* base) {
@@ -90,7 +104,7 @@ __device__ __forceinline__ void copy16_to_lds(uint32_t lds, uint32_t voff, const
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
     const uint64_t sb = ((uint64_t)hi << 32) | lo;
     const uint32_t sl = __builtin_amdgcn_readfirstlane(lds);
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(sl), "v"(voff), "s"(sb)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(sl), "v"(voff), "s"(sb)
                  : "m0");
 }
 #pragma clang diagnostic pop

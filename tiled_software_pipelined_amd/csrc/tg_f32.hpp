@@ -284,6 +284,7 @@ struct F32Gemm {
             }
         }
 
+        clk.loop_end(g.clocks);
         float* C = static_cast<float*>(g.C);
         const bool vec_ok = VEC_STORE && (m0 + BM <= g.M) && (n0 + BN <= g.N) && (g.ldc % 4 == 0) &&
                             ((reinterpret_cast<uintptr_t>(C) & 15) == 0);

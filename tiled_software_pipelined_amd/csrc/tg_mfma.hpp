@@ -863,6 +863,7 @@ struct MfmaGemm {
         // non-temporal; otherwise every segment straddles two lines, and
         // ordinary stores let the L2 merge the halves before they reach HBM
         // (about 20 % faster than streaming the partial lines at 4096^3).
+        clk.loop_end(g.clocks);
         Out* C = static_cast<Out*>(g.C);
         const bool inside = (m0 + BM <= g.M) && (n0 + BN <= g.N);
         if (g.c_stream) store_c<true>(C, g, acc, m0 + wm0, n0 + wn0, lane, inside);

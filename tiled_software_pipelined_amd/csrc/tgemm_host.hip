@@ -350,8 +350,10 @@ tgemm_plan* make_plan(int64_t M, int64_t N, int64_t K, int32_t dtype, int64_t ld
                 (long long)lda, (long long)K, (long long)ldb, (long long)N, (long long)ldc, (long long)N);
         return nullptr;
     }
-    if (dtype == TGEMM_I8 && K > 131072) {
-        set_err("int8: K=%lld may overflow the int32 accumulator (K <= 131072)", (long long)K);
+    // int8: every |product| is at most 128 * 128 = 16384, so |C| <= 16384 K,
+    // which stays below 2^31 (int32) for K <= 131071
+    if (dtype == TGEMM_I8 && K > 131071) {
+        set_err("int8: K=%lld may overflow the int32 accumulator (K <= 131071)", (long long)K);
         return nullptr;
     }
     tgemm_variant v{};
@@ -599,13 +601,15 @@ int run_impl(const tgemm_plan* p, const void* A, const void* B, void* C, uint64_
     g.lda = p->lda;
     g.ldb = p->ldb;
     g.ldc = p->ldc;
-    g.wg_group = p->wg_group;
+    // any group of tiles_m rows or more gives the same order (one group of
+    // every tile row); clamping keeps wg_group * tiles_n within the grid
+    g.wg_group = p->wg_group > g.tiles_m ? g.tiles_m : p->wg_group;
     g.a_guard = ga;
     g.b_guard = gb;
     g.c_stream = (uintptr_t)C % 128 == 0 && (p->ldc * 4) % 128 == 0;
     if (clocks && e->family == tg::FAM_TILED) {
         // the kernel that runs decides the count (a fallback's tile may differ)
-        const int64_t need = 4 * (int64_t)g.tiles_m * g.tiles_n;
+        const int64_t need = tg::CLOCK_VALUES * (int64_t)g.tiles_m * g.tiles_n;
         if (need > clocks_len) {
             set_err("clock buffer holds %lld values, %s needs %lld", (long long)clocks_len, e->name,
                     (long long)need);
@@ -641,7 +645,7 @@ int64_t gemm_clock_slots(const tgemm_plan* p) {
     for (int m = 0; m < 4; ++m) {
         const KernelEntry* e = m == 0 ? p->entry : p->fallback[m];
         if (!e || e->family != tg::FAM_TILED) continue;
-        const int64_t n = 4 * ((p->M + e->bm - 1) / e->bm) * ((p->n_main + e->bn - 1) / e->bn);
+        const int64_t n = tg::CLOCK_VALUES * ((p->M + e->bm - 1) / e->bm) * ((p->n_main + e->bn - 1) / e->bn);
         if (n > most) most = n;
     }
     return most;

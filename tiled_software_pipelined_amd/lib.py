@@ -295,17 +295,29 @@ def _ld(t, name):
     return max(int(t.stride(0)), int(t.shape[1]), 1) if t.shape[0] > 1 else max(int(t.shape[1]), 1)
 
 
+CLOCK_VALUES = 6  # TGEMM_CLOCK_VALUES: values per workgroup written by gemm_run_clocked
+
+
 def clock_ghz(clocks) -> float:
-    """Mean shader clock (GHz) of clocked runs: a host array of 4 values per
-    workgroup as gemm_run_clocked writes them (any number of runs stacked);
-    shader ticks over 100 MHz real-time ticks, summed over workgroups."""
+    """Mean shader clock (GHz) of clocked runs: a host array of CLOCK_VALUES
+    values per workgroup as gemm_run_clocked writes them (any number of runs
+    stacked); shader ticks over 100 MHz real-time ticks from start to end,
+    summed over workgroups."""
     import numpy as np
-    c = np.asarray(clocks, dtype=np.uint64).reshape(-1, 4).astype(np.float64)
-    shader = float((c[:, 2] - c[:, 0]).sum())
-    real = float((c[:, 3] - c[:, 1]).sum())
+    c = np.asarray(clocks, dtype=np.uint64).reshape(-1, CLOCK_VALUES).astype(np.float64)
+    shader = float((c[:, 4] - c[:, 0]).sum())
+    real = float((c[:, 5] - c[:, 1]).sum())
     if real <= 0:
         raise ValueError("no real-time ticks recorded")
     return shader / real * 0.1
+
+
+def clock_split_us(clocks):
+    """Per workgroup of clocked runs: (K-loop microseconds, C write-back
+    microseconds) from the real-time ticks (100 MHz), as two arrays."""
+    import numpy as np
+    c = np.asarray(clocks, dtype=np.uint64).reshape(-1, CLOCK_VALUES).astype(np.int64)
+    return (c[:, 3] - c[:, 1]) * 0.01, (c[:, 5] - c[:, 3]) * 0.01
 
 
 def plan_for(M, N, K, dtype, lda, ldb, ldc, variant: Variant | None = None) -> Plan:

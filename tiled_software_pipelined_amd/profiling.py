@@ -23,6 +23,7 @@ import os
 import shlex
 import subprocess
 import sys
+import time
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -52,12 +53,14 @@ def _bench_cmd(args, steps, warmup, calib=False):
 
 
 def _run(cmd, limit, log):
+    """Run one pass under a time limit; returns its exit status (124/137 or
+    -9: killed at the limit)."""
     print("+", " ".join(shlex.quote(c) for c in cmd), flush=True)
     with open(log, "a") as f:
         f.write("+ " + " ".join(shlex.quote(c) for c in cmd) + "\n")
         f.flush()
         r = subprocess.run(["timeout", "-s", "KILL", str(limit)] + cmd, stdout=f, stderr=subprocess.STDOUT, cwd=ROOT)
-    # rocprofv3 may end with a segfault after the program's results are written
+        f.write("# exit status %d\n" % r.returncode)
     return r.returncode
 
 
@@ -95,13 +98,24 @@ def build_cmds(args):
     return cmds
 
 
+PASSES_FILE = "passes.json"
+
+
 def collect(args):
+    """Run every pass; record each one's exit status and start time in
+    passes.json, so that the summary uses only CSV files written by this
+    collection."""
     out = os.path.abspath(args.out)
     os.makedirs(out, exist_ok=True)
     log = os.path.join(out, "profiling.log")
     cmds = build_cmds(args)
+    passes = {}
     for name, cmd in cmds.items():
-        _run(cmd, 240 if name == "trace" else 120, log)
+        t0 = time.time()
+        rc = _run(cmd, 240 if name == "trace" else 120, log)
+        passes[name] = {"rc": rc, "start": t0}
+        with open(os.path.join(out, PASSES_FILE), "w") as f:
+            json.dump(passes, f)
     # the occupancy query initialises the GPU, so it runs in a child process
     # of its own (this process starts the profiler runs and touches no GPU)
     occ = [sys.executable, "-m", "tiled_software_pipelined_amd.profiling", "--workload", args.workload,
@@ -143,8 +157,35 @@ def summarize(args, cmds):
     the last columns); durations and counters are then the sum over its
     kernels of each kernel's mean per dispatch, and `kernels` lists them."""
     out = os.path.abspath(args.out)
-    res = {"counters": {}, "copy": {}, "kernels": []}
+    res = {"counters": {}, "copy": {}, "kernels": [], "passes": {}}
+    passes = {}
+    if os.path.exists(os.path.join(out, PASSES_FILE)):
+        with open(os.path.join(out, PASSES_FILE)) as f:
+            passes = json.load(f)
+
+    def usable(name, path, rows=None):
+        """A pass's CSV counts only if the pass ran in this collection, the
+        file was written after the pass started and it holds GEMM
+        dispatches; the verdict goes into res["passes"]."""
+        p = passes.get(name)
+        rec = {"rc": p["rc"] if p else None, "csv": os.path.relpath(path, out) if path else None}
+        if p is None:
+            rec["status"] = "no record of this pass in %s" % PASSES_FILE
+        elif not path:
+            rec["status"] = "no CSV written"
+        elif os.path.getmtime(path) < p["start"]:
+            rec["status"] = "stale CSV (older than the pass)"
+        elif rows is not None and not any(_is_gemm(r.get("Kernel_Name", r.get("Name", ""))) for r in rows):
+            rec["status"] = "CSV holds no GEMM dispatch"
+        else:
+            rec["status"] = "ok" if p["rc"] == 0 else "ok (CSV complete; exit status %d)" % p["rc"]
+        res["passes"][name] = rec
+        return rec["status"].startswith("ok")
+
     stats = _find(os.path.join(out, "trace"), "*kernel_stats.csv")
+    stats_rows = _read_csv(stats) if stats else None
+    if not usable("trace", stats, stats_rows):
+        stats = None
     if stats:
         rows = [r for r in _read_csv(stats) if _is_gemm(r["Name"])]
         # the most-called kernel first (all kernels of a plan run once per GEMM)
@@ -163,10 +204,11 @@ def summarize(args, cmds):
         res["resources"] = kernel_resources(_read_csv(trace))
     for i in range(len(GROUPS)):
         f = _find(os.path.join(out, "pmc%d" % i), "*counter_collection.csv")
-        if not f:
+        frows = _read_csv(f) if f else None
+        if not usable("pmc%d" % i, f, frows):
             continue
         gsum, gcnt, cvals = {}, {}, {}
-        for row in _read_csv(f):
+        for row in frows:
             name = row.get("Kernel_Name", "")
             cn = row["Counter_Name"]
             val = float(row["Counter_Value"])
@@ -291,6 +333,12 @@ def render(args, cmds, res):
         lines.append("# %s: %s" % (k, text.replace(os.path.abspath(args.out), args.out)))
     lines.append("```")
     lines.append("")
+    if res.get("passes"):
+        lines.append("| pass | exit status | CSV used |")
+        lines.append("|---|---|---|")
+        for name, rec in res["passes"].items():
+            lines.append("| %s | %s | %s |" % (name, rec["rc"], rec["status"]))
+        lines.append("")
     if "avg_ns" in res:
         t = res["avg_ns"] * 1e-9
         lines.append("| quantity | value |")
@@ -334,7 +382,7 @@ def render(args, cmds, res):
                 lines.append("| %s per launch (scaled by copy: %.1f B/unit) | %.1f MiB |" % (
                     cn, scale, c[cn] * scale / 2 ** 20))
         if traffic is not None:
-            lines.append("| HBM traffic per launch / algorithmic bytes | %.1f MiB / %.1f MiB |" % (
+            lines.append("| L2-miss (fabric) bytes per launch / algorithmic bytes | %.1f MiB / %.1f MiB |" % (
                 traffic / 2 ** 20, alg_bytes / 2 ** 20))
         lines.append("")
         lines.append("Raw counter means per dispatch:")
