@@ -427,6 +427,9 @@ def main():
                     help="GEMM and matrix-core probe back to back for S seconds each, with socket "
                          "power and shader clocks sampled by amd-smi")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--probe-last", action="store_true",
+                    help="run the ceiling probe after the timed region instead of before the warmup "
+                         "(the timed region then starts from whatever clock state the warmup leaves)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of MIB MiB (a reference for the HBM "
                          "byte counters when profiling)")
@@ -544,6 +547,18 @@ def main():
         del src, dst
 
     variant = parse_variant(args.variant, lib)
+    ceiling = None
+    if not args.calib_copy and not args.probe_last:
+        # The rate the arithmetic units sustain on this machine for the
+        # workload's operand distribution with no memory traffic at all (the
+        # power budget lowers the clock below nominal for random operands;
+        # the fp32 rate grows with the waves per SIMD, 8 at most).  Measured
+        # before the warmup steps: it also brings the shader clock out of its
+        # idle state, which otherwise takes tens of milliseconds of load, so
+        # that a short warmup does not leave the timed region on a ramping
+        # clock.
+        ceiling = mfma_ceiling(torch, lib, w.dtype, "random",
+                               workgroups=256 if w.dtype != "f32" else F32_PROBE_WAVES[8])
     kernel_ms, wall = time_region(lib, torch, A, B, C, variant, args.steps, args.warmup)
     # after the timed region, one pass with a pair of events around every
     # launch: the per-launch distribution (median, min, max) of that pass
@@ -615,16 +630,15 @@ def main():
                       "last_loop_end_us / last_end_us: from the first start to the last K-loop end / last "
                       "end" % (CLOCKED_LAUNCHES, NOMINAL_GHZ)}
     if not args.calib_copy:
-        # the rate the arithmetic units sustain on this machine for the
-        # workload's operand distribution with no memory traffic at all (the
-        # power budget lowers the clock below nominal for random operands;
-        # the fp32 rate grows with the waves per SIMD, 8 at most)
-        wgs = 256 if w.dtype != "f32" else F32_PROBE_WAVES[8]
-        rate, ghz, _ = mfma_ceiling(torch, lib, w.dtype, "random", workgroups=wgs)
+        if ceiling is None:
+            ceiling = mfma_ceiling(torch, lib, w.dtype, "random",
+                                   workgroups=256 if w.dtype != "f32" else F32_PROBE_WAVES[8])
+        rate, ghz, _ = ceiling
         unit = "matrix-core" if w.dtype != "f32" else "v_fmac_f32 (8 waves per SIMD)"
         rec["roofline"]["measured_ceiling"] = {
             "value": round(rate, 1), "clock_ghz": round(ghz, 3), "frac": round(achieved / rate, 4),
-            "source": "%s rate probe, random %s operands, no memory traffic" % (unit, w.dtype)}
+            "source": "%s rate probe, random %s operands, no memory traffic; run %s the warmup steps" % (
+                unit, w.dtype, "after the timed region" if args.probe_last else "before")}
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(w, A_cpu, B_cpu)
     print(json.dumps(rec), flush=True)

@@ -104,6 +104,13 @@ typedef enum tgemm_dtype {
 #define TGEMM_STORE_VECTOR 1     /* 16-byte row pieces */
 #define TGEMM_STORE_SCALAR 2     /* one element per store */
 
+/* When the direct loader issues a slice's copies (the skill's Step 3: the
+ * copy of a later stage overlaps the compute of the current one). */
+#define TGEMM_COPY_BURST 1       /* all of them right after the barrier that frees their slot */
+#define TGEMM_COPY_SPREAD 2      /* part of them there, the rest spread over the K steps of the
+                                    next slice (fewer memory instructions between any two
+                                    matrix instructions; a shorter lead for the rest) */
+
 /* Workgroup order (GEMM page, section 2.3). */
 #define TGEMM_ORDER_ROW_MAJOR (-1)
 
@@ -124,7 +131,11 @@ typedef struct tgemm_variant {
     int32_t wg_group;   /* TGEMM_ORDER_ROW_MAJOR, or g >= 1: XCD-aware order grouped by g tile rows */
     int32_t waves_m;    /* waves per workgroup along M */
     int32_t waves_n;    /* waves per workgroup along N */
-    int32_t store;      /* TGEMM_STORE_* (fp32 kernels; matrix-core kernels report 0) */
+    int32_t store;      /* TGEMM_STORE_*: fp32 kernels, and the matrix-core kernels' write-back
+                           (SCALAR: 4-byte stores from the matrix instruction's output layout;
+                           VECTOR: the operands of every matrix instruction swapped, C^T = B^T A^T,
+                           so each lane holds four consecutive columns: 16-byte stores) */
+    int32_t copy_sched; /* TGEMM_COPY_* (matrix-core direct loader; other kernels report BURST) */
 } tgemm_variant;
 
 typedef struct tgemm_plan tgemm_plan;

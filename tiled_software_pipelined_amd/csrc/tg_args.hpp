@@ -59,6 +59,7 @@ struct KernelEntry {
     int listed;      // 0: only reached as the fallback of a listed entry for such operands
     int tail_ok;     // handles K not a multiple of bk
     int waves_per_simd;  // occupancy the kernel is compiled for (its registers allow at least this)
+    int copy_sched;  // TGEMM_COPY_BURST / TGEMM_COPY_SPREAD (direct loader; others report BURST)
     KernelFn fn;
     char name[96];
 };

@@ -22,9 +22,10 @@ static const char* dtype_tag(int dt) { return dt == 0 ? "f32" : dt == 1 ? "bf16"
 // SHIFT: which operands the kernel reads from rows that are not 16-byte
 // aligned (bit 0 A, bit 1 B).  Such kernels are unlisted fallbacks.
 template <class Tr, int BM, int BN, int BK, int WM, int WN, int S, int LD, int LY, int AC, int FR,
-          int WAVES, int SHIFT = 0>
+          int WAVES, int SHIFT = 0, int CST = CST_MFMA, bool SPREAD = false>
 KernelEntry mfma_entry(int dtype) {
-    typedef MfmaGemm<Tr, BM, BN, BK, WM, WN, S, LD, LY, AC, FR, SHIFT> K;
+    static_assert(!SPREAD || LD == LD_DIRECT, "spread copies: the direct loader");
+    typedef MfmaGemm<Tr, BM, BN, BK, WM, WN, S, LD, LY, AC, FR, SHIFT, CST, SPREAD> K;
     KernelEntry e{};
     e.dtype = dtype;
     e.family = FAM_TILED;
@@ -38,6 +39,8 @@ KernelEntry mfma_entry(int dtype) {
     e.frag = FR;
     e.wm = WM;
     e.wn = WN;
+    e.store = CST == CST_SWAP ? 1 : 2;  // TGEMM_STORE_VECTOR / TGEMM_STORE_SCALAR
+    e.copy_sched = SPREAD ? 2 : 1;      // TGEMM_COPY_SPREAD / TGEMM_COPY_BURST
     e.gload_bytes = AC == AC_WIDE ? 16 : 4;
     e.threads = K::NT;
     e.lds_bytes = K::LDS_BYTES;
@@ -47,11 +50,12 @@ KernelEntry mfma_entry(int dtype) {
     e.tail_ok = 1;
     e.waves_per_simd = WAVES;
     e.fn = gemm_kernel<K, WAVES>;
-    snprintf(e.name, sizeof e.name, "%s_t%dx%dx%d_w%dx%d_s%d_%s_%s_%s_%s%s", dtype_tag(dtype), BM, BN,
+    snprintf(e.name, sizeof e.name, "%s_t%dx%dx%d_w%dx%d_s%d_%s_%s_%s_%s%s%s%s", dtype_tag(dtype), BM, BN,
              BK, WM, WN, S, LD == LD_DIRECT ? "direct" : "vgpr",
              LY == LY_XOR ? "xor" : LY == LY_XOR_POISON ? "xorpoison" : "plain",
              AC == AC_WIDE ? "wide" : "narrow", FR == FR_REUSE ? "reuse" : "permma",
-             SHIFT == 1 ? "_shiftA" : SHIFT == 2 ? "_shiftB" : SHIFT == 3 ? "_shiftAB" : "");
+             SHIFT == 1 ? "_shiftA" : SHIFT == 2 ? "_shiftB" : SHIFT == 3 ? "_shiftAB" : "",
+             CST == CST_SWAP ? "_vst" : "", SPREAD ? "_spread" : "");
     return e;
 }
 
@@ -79,6 +83,7 @@ KernelEntry naive_entry() {
     e.listed = 1;
     e.tail_ok = 1;
     e.waves_per_simd = 4;
+    e.copy_sched = 1;
     e.fn = gemm_kernel<K, 4>;
     snprintf(e.name, sizeof e.name, "%s_naive", dtype_tag(DT));
     return e;
@@ -111,6 +116,7 @@ KernelEntry thin_entry() {
     e.listed = 0;
     e.tail_ok = 1;
     e.waves_per_simd = 2;
+    e.copy_sched = 1;
     e.fn = gemm_kernel<K, 2>;
     snprintf(e.name, sizeof e.name, "%s_thin_n%d", dtype_tag(DT), NB);
     return e;
@@ -146,6 +152,7 @@ KernelEntry f32_entry() {
     e.listed = 1;
     e.tail_ok = 1;
     e.waves_per_simd = WAVES;
+    e.copy_sched = 1;
     e.fn = gemm_kernel<K, WAVES>;
     snprintf(e.name, sizeof e.name, "f32_t%dx%dx%d_w2x2_s%d_%s_%s_%s", TILE, TILE_N, BK, S, TA ? "transA" : "rowA",
              QU ? "quarters" : "blocks", VS ? "vecstore" : "scalarstore");

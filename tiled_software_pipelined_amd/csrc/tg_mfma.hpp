@@ -46,6 +46,7 @@ namespace tg {
 struct TraitsBF16 {
     typedef uint16_t T;
     typedef float Out;
+    typedef f32x4 Out4;
     typedef f32x16 Acc;
     static constexpr int ESZ = 2;
     static constexpr int MK = 16;  // K of one v_mfma_f32_32x32x16_bf16
@@ -58,6 +59,7 @@ struct TraitsBF16 {
 struct TraitsI8 {
     typedef int8_t T;
     typedef int32_t Out;
+    typedef i32x4 Out4;
     typedef i32x16 Acc;
     static constexpr int ESZ = 1;
     static constexpr int MK = 32;  // K of one v_mfma_i32_32x32x32_i8
@@ -66,12 +68,32 @@ struct TraitsI8 {
     }
 };
 
+// CST selects the C write-back: CST_MFMA stores from the matrix
+// instruction's own output layout (4-byte stores, each instruction writing
+// two 128-byte row segments); CST_SWAP computes C^T = B^T A^T instead (the
+// operands of every matrix instruction swapped, same products in the same k
+// order), which puts four consecutive columns of one C row in each lane, so
+// that the write-back takes a quarter of the store instructions, 16 bytes
+// each.
+enum CStore { CST_MFMA = 0, CST_SWAP = 1 };
+
+// SPREAD (direct loader): issue each slice's copies in two parts, the
+// second spread over the K steps of the following slice, instead of all of
+// them right after the slice's barrier (see N1 below).
 template <class Tr, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int LOADER,
-          int LAYOUT, int ACCESS, int FRAG, int SHIFT = 0>
+          int LAYOUT, int ACCESS, int FRAG, int SHIFT = 0, int CST = CST_MFMA, bool SPREAD = false>
 struct MfmaGemm {
     typedef typename Tr::T T;
     typedef typename Tr::Out Out;
+    typedef typename Tr::Out4 Out4;
     typedef typename Tr::Acc Acc;
+
+    // one matrix instruction: acc += A-fragment x B-fragment (CST_SWAP:
+    // acc^T += B-fragment^T x A-fragment^T, the transposed tile)
+    __device__ static __forceinline__ Acc mma(i32x4 a, i32x4 b, Acc c) {
+        if constexpr (CST == CST_SWAP) return Tr::mma(b, a, c);
+        else return Tr::mma(a, b, c);
+    }
 
     static constexpr int NT = 64 * WAVES_M * WAVES_N;
     static constexpr int ESZ = Tr::ESZ;
@@ -537,54 +559,88 @@ struct MfmaGemm {
         return k <= first ? 0 : ((k - first) * total + (NM - first) - 1) / (NM - first);
     }
 
+    // Where one slice's direct copies go: the LDS slot and the wave-uniform
+    // A / B addresses of the slice.
+    struct CopyTarget {
+        TG_LDS char* slot;
+        const char* ca;
+        const char* cb;
+    };
+
+    // Copies of slice u are issued in two parts.  Part 1, copies [0, N1),
+    // follows the barrier in the last K step of slice u - STAGES (the
+    // barrier that frees u's slot); part 2, copies [N1, N_LD), is spread
+    // over K steps 0 .. KSUB-2 of slice u - STAGES + 1.  Without SPREAD
+    // part 1 is every copy.  Either way the copies of a slice are issued
+    // before any copy of a later one, so "at most n later slices in flight"
+    // stays vmcnt(n N_LD).
+    static constexpr int N1 = (SPREAD && KSUB > 1) ? (N_LD + KSUB - 1) / KSUB : N_LD;
+    static constexpr int N2 = N_LD - N1;
+    // first copy of part 2 issued in K step s (0 <= s <= KSUB-1)
+    __device__ static constexpr int part2_begin(int s) { return KSUB > 1 ? N1 + (s * N2) / (KSUB - 1) : N_LD; }
+
     // Matrix step on `cur` with reads of (rslot, rs) into `nxt` interleaved.
     // BARRIER: before the reads, meet the other waves once this wave's slot
     // reads are done and at most `ahead` later slices' copies are in flight
-    // (after matrix instruction BAR_K); then, if DMA, issue the N_LD copies
-    // of slice (copy_slot, ca, cb) after the reads.
-    template <bool READS, bool BARRIER, bool DMA>
+    // (after matrix instruction BAR_K); then issue copies [DB, DE) of the
+    // slice `ct` after the reads.
+    template <bool READS, bool BARRIER, int DB, int DE>
     __device__ static __forceinline__ void kstep(Acc (&acc)[FM][FN], const Frags& cur, Frags& nxt,
-                                                 const TG_LDS char* rslot, int rs, int ahead,
-                                                 TG_LDS char* copy_slot, const DirectOffsets& off,
-                                                 const char* ca, const char* cb, int wm0, int wn0,
-                                                 int lane, int wave) {
+                                                 const TG_LDS char* rslot, int rs, int ahead, const CopyTarget& ct,
+                                                 const DirectOffsets& off, int wm0, int wn0, int lane, int wave) {
         // the barrier follows matrix instruction BAR_K; the memory
         // instructions start after it
         constexpr int BAR_K = (BARRIER && NM >= 8) ? 1 : 0;
         static_assert(BAR_K < NM, "barrier inside the K step");
+        static_assert(0 <= DB && DB <= DE && DE <= N_LD, "copy range");
         constexpr int NREAD = READS ? NR : 0;
-        constexpr int TOTAL = NREAD + (DMA ? N_LD : 0);
+        constexpr int TOTAL = NREAD + (DE - DB);
 #pragma unroll
         for (int k = 0; k < NM; ++k) {
             const int i = k / FN, j = k % FN;
-            acc[i][j] = Tr::mma(cur.a[i], cur.b[j], acc[i][j]);
+            acc[i][j] = mma(cur.a[i], cur.b[j], acc[i][j]);
             if (BARRIER && k == BAR_K) wait_slice(ahead);
 #pragma unroll
             for (int m = mem_begin(k, BAR_K, TOTAL); m < mem_begin(k + 1, BAR_K, TOTAL); ++m) {
                 if (m < NREAD) read_op(nxt, rslot, rs, m, wm0, wn0, lane);
-                else issue_direct_one(m - NREAD, copy_slot, off, ca, cb, wave);
+                else issue_direct_one(DB + m - NREAD, ct.slot, off, ct.ca, ct.cb, wave);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
     }
 
-    // One slice t from `cur_slot`.  NEXT: slice t+1 exists (barrier in the
-    // last K step, then its first fragments are read); DMA: also start the
-    // copy of slice t+STAGES into this slot after that barrier.
-    template <bool NEXT, bool DMA>
+    // K steps s .. KSUB-1 of one slice t from `cur_slot`.  PREV: issue part
+    // 2 of the copies of slice t + STAGES - 1 (`prev`) over steps 0 ..
+    // KSUB-2.  NEXT: slice t+1 exists (barrier in the last K step, then its
+    // first fragments are read from `next_slot`); DMA: after that barrier
+    // also issue part 1 of the copies of slice t + STAGES (`next`, into the
+    // slot slice t leaves).
+    template <int S, bool PREV, bool NEXT, bool DMA>
+    __device__ static __forceinline__ void slice_steps(Acc (&acc)[FM][FN], Frags (&f)[2],
+                                                       const TG_LDS char* cur_slot, const TG_LDS char* next_slot,
+                                                       int ahead, const CopyTarget& prev, const CopyTarget& next,
+                                                       const DirectOffsets& off, int wm0, int wn0, int lane,
+                                                       int wave) {
+        if constexpr (S + 1 < KSUB) {
+            constexpr int DB = PREV ? part2_begin(S) : 0, DE = PREV ? part2_begin(S + 1) : 0;
+            kstep<true, false, DB, DE>(acc, f[S & 1], f[(S + 1) & 1], cur_slot, S + 1, 0, prev, off, wm0, wn0,
+                                       lane, wave);
+            slice_steps<S + 1, PREV, NEXT, DMA>(acc, f, cur_slot, next_slot, ahead, prev, next, off, wm0, wn0,
+                                                lane, wave);
+        } else {
+            kstep<NEXT, NEXT, 0, DMA ? N1 : 0>(acc, f[S & 1], f[(S + 1) & 1], next_slot, 0, ahead, next, off,
+                                               wm0, wn0, lane, wave);
+        }
+    }
+
+    template <bool PREV, bool NEXT, bool DMA>
     __device__ static __forceinline__ void slice_direct(Acc (&acc)[FM][FN], Frags (&f)[2],
-                                                        const TG_LDS char* cur_slot,
-                                                        const TG_LDS char* next_slot, int ahead,
-                                                        TG_LDS char* copy_slot, const DirectOffsets& off,
-                                                        const char* ca, const char* cb, int wm0, int wn0,
-                                                        int lane, int wave) {
-#pragma unroll
-        for (int s = 0; s + 1 < KSUB; ++s)
-            kstep<true, false, false>(acc, f[s & 1], f[(s + 1) & 1], cur_slot, s + 1, 0, copy_slot, off, ca,
-                                      cb, wm0, wn0, lane, wave);
-        constexpr int L = KSUB - 1;
-        kstep<NEXT, NEXT, DMA>(acc, f[L & 1], f[(L + 1) & 1], next_slot, 0, ahead, copy_slot, off, ca, cb, wm0,
-                               wn0, lane, wave);
+                                                        const TG_LDS char* cur_slot, const TG_LDS char* next_slot,
+                                                        int ahead, const CopyTarget& prev, const CopyTarget& next,
+                                                        const DirectOffsets& off, int wm0, int wn0, int lane,
+                                                        int wave) {
+        slice_steps<0, PREV, NEXT, DMA>(acc, f, cur_slot, next_slot, ahead, prev, next, off, wm0, wn0, lane,
+                                        wave);
     }
 
     // Multiply one slice held in `slot` into the accumulators.  With
@@ -607,7 +663,7 @@ struct MfmaGemm {
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
-                    for (int j = 0; j < FN; ++j) acc[i][j] = Tr::mma(f[s & 1].a[i], f[s & 1].b[j], acc[i][j]);
+                    for (int j = 0; j < FN; ++j) acc[i][j] = mma(f[s & 1].a[i], f[s & 1].b[j], acc[i][j]);
                 __builtin_amdgcn_sched_barrier(0);
             }
             return;
@@ -620,7 +676,7 @@ struct MfmaGemm {
                 for (int j = 0; j < FN; ++j) {
                     const i32x4 a = read_a(slot, wm0 + 32 * i, s, lane);
                     const i32x4 b = read_b(bslot, wn0 + 32 * j, s, lane);
-                    acc[i][j] = Tr::mma(a, b, acc[i][j]);
+                    acc[i][j] = mma(a, b, acc[i][j]);
                 }
         }
     }
@@ -730,6 +786,36 @@ struct MfmaGemm {
                 }
     }
 
+    // CST_SWAP write-back: register r of tile (i, j) in lane l holds row
+    // 32 i + l%32, column 32 j + 8 (r/4) + 4 (l/32) + r%4, so registers
+    // 4q .. 4q+3 are four consecutive columns of one row: one 16-byte store
+    // where C's rows are 16-byte aligned and the tile lies inside C, element
+    // stores otherwise.  Each instruction writes 32 bytes of each of 32 rows;
+    // the four of one tile complete those rows' 128-byte segments, which the
+    // L2 merges before they are written back (plain, not streaming, stores).
+    __device__ static __forceinline__ void store_c_swapped(Out* C, const GemmArgs& g, const Acc (&acc)[FM][FN],
+                                                           int r0, int c0, int lane, bool inside) {
+        const bool vec = inside && (g.ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(C) & 15) == 0);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int row = r0 + 32 * i + (lane & 31);
+                    const int col = c0 + 32 * j + 8 * q + 4 * (lane >> 5);
+                    Out* dst = &C[(int64_t)row * g.ldc + col];
+                    if (vec) {
+                        *reinterpret_cast<Out4*>(dst) = Out4{acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                                                             acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (row < g.M && col + e < g.N) dst[e] = static_cast<Out>(acc[i][j][4 * q + e]);
+                    }
+                }
+    }
+
     // Wait until at most `ahead` slices' copies (issued after the one needed
     // next) are still in flight, then barrier.  The wait count is an
     // immediate, so the runtime `ahead` (0 .. STAGES-2) selects among
@@ -825,19 +911,37 @@ struct MfmaGemm {
             // it, and (b) every wave's copy of slice t+1 has landed, so the
             // first fragments of slice t+1 are read while the last K step of
             // slice t still runs on the matrix cores.
+            // With SPREAD, part 2 of slice t + STAGES - 1's copies is issued
+            // during slice t; slice STAGES - 1 was issued whole above.
+            auto target = [&](int sl) {
+                return CopyTarget{smem + (sl % STAGES) * SLOT, abase + sl * astep, bbase + sl * bstep};
+            };
+            const CopyTarget none{smem, abase, bbase};
             int t = 0;
-            for (; t + STAGES < full; ++t)
-                slice_direct<true, true>(acc, f, smem + (t % STAGES) * SLOT, smem + ((t + 1) % STAGES) * SLOT,
-                                         STAGES - 2, smem + (t % STAGES) * SLOT, off,
-                                         abase + (t + STAGES) * astep, bbase + (t + STAGES) * bstep, wm0, wn0,
-                                         lane, wave);
+            if (STAGES < full) {
+                slice_direct<false, true, true>(acc, f, smem, smem + SLOT, STAGES - 2, none, target(STAGES), off,
+                                                wm0, wn0, lane, wave);
+                for (t = 1; t + STAGES < full; ++t)
+                    slice_direct<SPREAD, true, true>(acc, f, smem + (t % STAGES) * SLOT,
+                                                     smem + ((t + 1) % STAGES) * SLOT, STAGES - 2,
+                                                     target(t + STAGES - 1), target(t + STAGES), off, wm0, wn0,
+                                                     lane, wave);
+                // the last slice whose part 2 is still to be issued
+                // (t + STAGES == full, so t + 1 < full)
+                if constexpr (SPREAD) {
+                    slice_direct<true, true, false>(acc, f, smem + (t % STAGES) * SLOT,
+                                                    smem + ((t + 1) % STAGES) * SLOT, STAGES - 2,
+                                                    target(t + STAGES - 1), none, off, wm0, wn0, lane, wave);
+                    ++t;
+                }
+            }
             for (; t + 1 < full; ++t)
-                slice_direct<true, false>(acc, f, smem + (t % STAGES) * SLOT, smem + ((t + 1) % STAGES) * SLOT,
-                                          min(STAGES - 2, full - 2 - t), smem, off, abase, bbase, wm0, wn0, lane,
-                                          wave);
+                slice_direct<false, true, false>(acc, f, smem + (t % STAGES) * SLOT, smem + ((t + 1) % STAGES) * SLOT,
+                                                 min(STAGES - 2, full - 2 - t), none, none, off, wm0, wn0, lane,
+                                                 wave);
             if (t < full)
-                slice_direct<false, false>(acc, f, smem + (t % STAGES) * SLOT, smem, 0, smem, off, abase, bbase,
-                                           wm0, wn0, lane, wave);
+                slice_direct<false, false, false>(acc, f, smem + (t % STAGES) * SLOT, smem, 0, none, none, off, wm0,
+                                                  wn0, lane, wave);
             if (full < tiles) {
                 // K tail: element loads with zero fill into slot full % STAGES.
                 // No copy is in flight (the last wait drained them) and every
@@ -866,8 +970,12 @@ struct MfmaGemm {
         clk.loop_end(g.clocks);
         Out* C = static_cast<Out*>(g.C);
         const bool inside = (m0 + BM <= g.M) && (n0 + BN <= g.N);
-        if (g.c_stream) store_c<true>(C, g, acc, m0 + wm0, n0 + wn0, lane, inside);
-        else store_c<false>(C, g, acc, m0 + wm0, n0 + wn0, lane, inside);
+        if constexpr (CST == CST_SWAP) {
+            store_c_swapped(C, g, acc, m0 + wm0, n0 + wn0, lane, inside);
+        } else {
+            if (g.c_stream) store_c<true>(C, g, acc, m0 + wm0, n0 + wn0, lane, inside);
+            else store_c<false>(C, g, acc, m0 + wm0, n0 + wn0, lane, inside);
+        }
         clk.finish(g.clocks);
     }
 };

@@ -29,6 +29,8 @@ LOADER_VGPR, LOADER_DIRECT = 1, 2
 LDS_PLAIN, LDS_XOR, LDS_XOR_POISON = 1, 2, 3
 ACCESS_WIDE, ACCESS_NARROW = 1, 2
 FRAG_REUSE, FRAG_PER_MMA = 1, 2
+STORE_VECTOR, STORE_SCALAR = 1, 2
+COPY_BURST, COPY_SPREAD = 1, 2
 ORDER_ROW_MAJOR = -1
 
 
@@ -36,7 +38,7 @@ class Variant(ctypes.Structure):
     """Mirror of ``tgemm_variant``; zero fields mean "default"."""
     _fields_ = [(n, ctypes.c_int32) for n in (
         "kernel", "tile_m", "tile_n", "tile_k", "stages", "loader", "lds_layout", "access", "frag",
-        "wg_group", "waves_m", "waves_n", "store")]
+        "wg_group", "waves_m", "waves_n", "store", "copy_sched")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
