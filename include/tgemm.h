@@ -205,6 +205,22 @@ int64_t gemm_workspace_bytes(const tgemm_plan* plan, const void* A, const void* 
 int gemm_run_ws(const tgemm_plan* plan, const void* A, const void* B, void* C, void* workspace,
                 int64_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): gemm_run_ws
+ * with the library's own fixed workspace instead of a caller one.  The
+ * workspace is one device array of TGEMM_NOALLOC_MAX_BYTES bytes per GPU,
+ * created with the library's code on that GPU and held until the process
+ * ends; the call itself allocates nothing.  When gemm_workspace_bytes(plan,
+ * A, B) is 0 this is gemm_run; when it is at most TGEMM_NOALLOC_MAX_BYTES
+ * the misaligned operands are repacked into the array and the result is
+ * gemm_run_ws's, bit for bit; larger needs are rejected with TGEMM_E_ARG
+ * (nothing is enqueued; tgemm_last_error gives the bytes needed).  Every call
+ * on one GPU shares that GPU's array and overwrites what it uses, so calls
+ * that overlap on one GPU (other streams, other host threads) race: order
+ * them on one stream.  Returns as gemm_run_ws. */
+#define TGEMM_NOALLOC_MAX_BYTES (64LL << 20)
+int gemm_run_noalloc(const tgemm_plan* plan, const void* A, const void* B, void* C, void* stream);
+
 /* What a plan will launch. */
 typedef struct tgemm_plan_info {
     int64_t M, N, K, lda, ldb, ldc;

@@ -739,6 +739,72 @@ int gemm_run_ws(const tgemm_plan* p, const void* A, const void* B, void* C, void
     return gemm_run(p->packed, a, b, C, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// The workspace of gemm_run_noalloc: a fixed device array, one per GPU the
+// library runs on, held until the process ends.  Its name is a host-side
+// stand-in, not a device address: host code only ever uses the address
+// hipGetSymbolAddress returns for the current device (looked up on the
+// entry point's first call on that device and kept per device).
+static __device__ __align__(256) char scratch[TGEMM_NOALLOC_MAX_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];  // per device; NULL until looked up
+
+int scratch_of_current_device(void** out) {
+    int dev = 0;
+    const hipError_t gerr = hipGetDevice(&dev);
+    if (gerr != hipSuccess) {
+        set_err("hipGetDevice failed: %s", hipGetErrorString(gerr));
+        return TGEMM_E_HIP;
+    }
+    if (dev < 0 || dev >= 64) {
+        set_err("device index %d out of range", dev);
+        return TGEMM_E_ARCH;
+    }
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        const hipError_t err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (err != hipSuccess || !ptr) {
+            set_err("hipGetSymbolAddress of the fixed workspace failed on device %d: %s", dev,
+                    hipGetErrorString(err));
+            return TGEMM_E_HIP;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return TGEMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_run_noalloc(const tgemm_plan* p, const void* A, const void* B, void* C, void* stream) {
+    if (!p) {
+        set_err("NULL plan");
+        return TGEMM_E_NULL;
+    }
+    int mask = 0;
+    const int64_t need = pack_need(p, A, B, &mask);
+    if (need == 0) return gemm_run(p, A, B, C, stream);
+    if (need > TGEMM_NOALLOC_MAX_BYTES) {
+        set_err("repacking these operands needs %lld bytes of workspace; the fixed array of gemm_run_noalloc "
+                "holds %lld (use gemm_run_ws with a caller workspace, or gemm_run)",
+                (long long)need, (long long)TGEMM_NOALLOC_MAX_BYTES);
+        return TGEMM_E_ARG;
+    }
+    int rc = check_arch();
+    if (rc != TGEMM_OK) return rc;
+    void* ws = nullptr;
+    rc = scratch_of_current_device(&ws);
+    if (rc != TGEMM_OK) return rc;
+    return gemm_run_ws(p, A, B, C, ws, need, stream);
+}
+
 int gemm_plan_get_info(const tgemm_plan* p, tgemm_plan_info* info) {
     if (!p || !info) {
         set_err("NULL plan or info");

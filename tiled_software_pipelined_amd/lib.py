@@ -61,7 +61,7 @@ class PlanInfo(ctypes.Structure):
 EXPORTS = ("gemm_plan", "gemm_plan_variant", "gemm_run", "gemm_destroy", "tgemm_last_error",
            "gemm_plan_get_info", "gemm_variant_count", "gemm_variant_get", "tgemm_version",
            "tgemm_lds_read_probe", "tgemm_mfma_rate_probe", "gemm_workspace_bytes", "gemm_run_ws",
-           "gemm_kernel_occupancy", "gemm_clock_slots", "gemm_run_clocked")
+           "gemm_kernel_occupancy", "gemm_clock_slots", "gemm_run_clocked", "gemm_run_noalloc")
 
 
 def _load():
@@ -104,6 +104,8 @@ def _load():
     lib.gemm_workspace_bytes.restype = i64
     lib.gemm_run_ws.argtypes = [vp, vp, vp, vp, vp, i64, vp]
     lib.gemm_run_ws.restype = ctypes.c_int
+    lib.gemm_run_noalloc.argtypes = [vp, vp, vp, vp, vp]
+    lib.gemm_run_noalloc.restype = ctypes.c_int
     lib.tgemm_mfma_rate_probe.argtypes = [i32, i32, i32, vp, vp, vp, vp]
     lib.tgemm_mfma_rate_probe.restype = ctypes.c_int
     return lib
@@ -262,6 +264,14 @@ class Plan:
         if rc != OK:
             raise TgemmError(rc, last_error())
 
+    def run_noalloc_ptr(self, A: int, B: int, C: int, stream: int = 0) -> None:
+        """gemm_run_noalloc on raw device pointers: repacks misaligned operands
+        into the library's fixed device array (no allocation)."""
+        rc = _lib.gemm_run_noalloc(self._h, ctypes.c_void_p(A), ctypes.c_void_p(B), ctypes.c_void_p(C),
+                                   ctypes.c_void_p(stream))
+        if rc != OK:
+            raise TgemmError(rc, last_error())
+
     def __del__(self):
         h = getattr(self, "_h", None)
         if h and _lib is not None:  # module globals are gone at interpreter exit
@@ -298,6 +308,7 @@ def _ld(t, name):
 
 
 CLOCK_VALUES = 6  # TGEMM_CLOCK_VALUES: values per workgroup written by gemm_run_clocked
+NOALLOC_MAX_BYTES = 64 << 20  # TGEMM_NOALLOC_MAX_BYTES: the fixed workspace of gemm_run_noalloc
 
 
 def clock_ghz(clocks) -> float:
