@@ -10,11 +10,14 @@ events on the launch stream) and the CPU oracle's rate on a bounded sample of
 the same workload.
 
 Extra modes (not used by the default run):
-    --ladder     time every listed variant of the workload's dtype, round-robin
-                 (one JSON line each, then the summary line)
-    --sweep      the bf16 shape sweep: the 128x128x32 tile at 2 / 3 / 4 stages
-                 and the default plan per shape, timed by HIP-graph replay
-                 (eager per-launch times beside them)
+    --ladder     the ablation ladder of the workload's type, one change per rung
+                 (TFLOP/s, gain over the rung it changes, bit identity with the
+                 default plan; --ladder-summary writes the table)
+    --variants   time every compiled variant of the workload's type
+    --sweep      the bf16 shape sweep: the 128x128x32 tile with the register-
+                 staged loader (2 slots) and the direct loader (1-4 slots), and
+                 the default plan per shape, timed by HIP-graph replay
+                 (--sweep-summary writes the heatmap)
     --lds-probe  LDS read throughput of ds_read_b32 / b64 / b128 / b64_tr_b16
     --mfma-probe matrix-core rate and clock for bf16 / int8 operand bits
                  (the workloads' random operands, all ones, all zeros)
@@ -404,6 +407,218 @@ def env_record(torch, lib, dev):
             "kernel_sources": provenance.source_hash()}
 
 
+def _round_robin(torch, lib, w, A, B, C, variants, steps, slow):
+    """Median / p10 per-launch ms of every variant, timed round-robin (a few
+    launches of each per round, many rounds) so that clock and thermal drift
+    spreads over all of them.  `slow`: indices timed once per round and only
+    in the first two rounds."""
+    rounds = max(4, steps // 3)
+    times = {i: [] for i in range(len(variants))}
+    for v in variants:  # warm every kernel once
+        lib.gemm(A, B, out=C, variant=v)
+    torch.cuda.synchronize()
+    for r in range(rounds):
+        for i, v in enumerate(variants):
+            if i in slow and r >= 2:
+                continue
+            per, _ = time_plan(lib, torch, w, A, B, C, v, 1 if i in slow else 3, 0)
+            times[i] += per
+    out = []
+    for i in range(len(variants)):
+        t = sorted(times[i])
+        out.append((t[len(t) // 2], t[len(t) // 10], len(t)))
+    return out
+
+
+def run_ladder(torch, lib, w, A, B, C, args):
+    """The ablation ladder of the workload's type (tiled_software_pipelined_amd
+    .ladders): every rung timed round-robin, then one JSON line per rung with
+    TFLOP/s, the gain over the rung it changes one thing of, and whether its
+    C is the same bit for bit as the default plan's (every matrix-core rung
+    and every fp32 rung accumulates each output in increasing k; the oracle
+    check of every rung at this size is tests/test_ladder_gpu.py).  With
+    --ladder-summary PATH also a Markdown table."""
+    from tiled_software_pipelined_amd import ladders
+    code = {"f32": lib.F32, "bf16": lib.BF16, "i8": lib.I8}[w.dtype]
+    rungs = list(ladders.LADDERS[w.dtype])
+    variants = []
+    for r in rungs:
+        variants.append(None if r.fields is None else lib.Variant(**r.fields))
+    labels = [r.label for r in rungs]
+    if w.dtype != "f32":
+        # the default plan under each workgroup order
+        for grp in (lib.ORDER_ROW_MAJOR, 1, 2, 4, 8):
+            dv = lib.plan_for(w.M, w.N, w.K, code, w.K, w.N, w.N).info().variant
+            dv.wg_group = grp
+            variants.append(dv)
+            rungs.append(ladders.Rung("R8g%d" % grp, "default plan, workgroup order %s" % (
+                "row-major" if grp < 0 else "XCD-aware, groups of %d tile rows" % grp), dv.as_dict(),
+                base="R8"))
+            labels.append(rungs[-1].label)
+    ref = torch.empty_like(C)
+    lib.gemm(A, B, out=ref)
+    torch.cuda.synchronize()
+    same = []
+    for v in variants:
+        C.fill_(-7)
+        lib.gemm(A, B, out=C, variant=v)
+        torch.cuda.synchronize()
+        same.append(bool(torch.equal(C, ref)))
+        if not same[-1]:
+            d = (C.double() - ref.double()).abs().max().item()
+            same[-1] = "max |diff| %.3g" % d
+    slow = {i for i, v in enumerate(variants) if v is not None and v.kernel == lib.KERNEL_NAIVE}
+    timing = _round_robin(torch, lib, w, A, B, C, variants, args.steps, slow)
+    unit = "TOP/s" if w.dtype == "i8" else "TFLOP/s"
+    lines = []
+    for i, r in enumerate(rungs):
+        ms, p10, n = timing[i]
+        tf = w.flops / ms / 1e9
+        b = ladders.base_of(rungs, i)
+        gain = None if b is None else 100.0 * (timing[b][0] / ms - 1.0)
+        kname = lib.plan_for(w.M, w.N, w.K, code, w.K, w.N, w.N, variants[i]).name
+        rec = {"mode": "ladder", "workload": w.name, "rung": r.label, "change": r.change, "kernel": kname,
+               "median_ms": round(ms, 5), "p10_ms": round(p10, 5), "launches": n, "rate": round(tf, 1),
+               "unit": unit, "frac_peak": round(tf / PEAK_TFLOPS[w.dtype], 4),
+               "base": None if b is None else rungs[b].label,
+               "gain_vs_base_pct": None if gain is None else round(gain, 1),
+               "same_bits_as_default": same[i]}
+        lines.append(rec)
+        print(json.dumps(rec), flush=True)
+    if args.ladder_summary:
+        write_ladder_summary(args, w, lines, unit)
+
+
+def write_ladder_summary(args, w, lines, unit):
+    import torch
+    from tiled_software_pipelined_amd import lib
+    hdr = ["# Ablation ladder: %s GEMM M=%d N=%d K=%d" % (w.dtype, w.M, w.N, w.K), "",
+           "Command: `python bench.py --workload %s --ladder --steps %d --ladder-summary %s`" % (
+               w.name, args.steps, args.ladder_summary), "",
+           "Device: %s (%s), libtgemm %s.  Every rung timed round-robin in one process (median of the "
+           "per-launch HIP-event times); `gain` is against the rung in `base`, which differs from it in one "
+           "thing; `same bits` compares C with the default plan's bit for bit (each rung's C is also checked "
+           "against the CPU oracle at this size by tests/test_ladder_gpu.py)." % (
+               torch.cuda.get_device_properties(0).name, getattr(torch.cuda.get_device_properties(0),
+                                                                 "gcnArchName", ""), lib.version()), "",
+           "| rung | change | kernel | median us | %s | %% of peak | base | gain | same bits |" % unit,
+           "|---|---|---|---|---|---|---|---|---|"]
+    for r in lines:
+        hdr.append("| %s | %s | `%s` | %.1f | %.1f | %.1f | %s | %s | %s |" % (
+            r["rung"], r["change"], r["kernel"], r["median_ms"] * 1e3, r["rate"], 100 * r["frac_peak"],
+            r["base"] or "", "" if r["gain_vs_base_pct"] is None else "%+.1f %%" % r["gain_vs_base_pct"],
+            "yes" if r["same_bits_as_default"] is True else r["same_bits_as_default"]))
+    os.makedirs(os.path.dirname(os.path.abspath(args.ladder_summary)), exist_ok=True)
+    with open(args.ladder_summary, "w") as f:
+        f.write("\n".join(hdr) + "\n")
+
+
+def run_variants(torch, lib, w, A, B, C, args):
+    """Every compiled variant of the workload's type, timed round-robin (one
+    JSON line each)."""
+    code = {"f32": lib.F32, "bf16": lib.BF16, "i8": lib.I8}[w.dtype]
+    variants = lib.variants(code)
+    slow = {i for i, v in enumerate(variants) if v.kernel == lib.KERNEL_NAIVE}
+    timing = _round_robin(torch, lib, w, A, B, C, variants, args.steps, slow)
+    for i, v in enumerate(variants):
+        ms, p10, n = timing[i]
+        print(json.dumps({"mode": "variants", "workload": w.name,
+                          "kernel": lib.plan_for(w.M, w.N, w.K, code, w.K, w.N, w.N, v).name,
+                          "median_ms": ms, "p10_ms": p10, "launches": n, "rate": w.flops / ms / 1e9,
+                          "frac_peak": w.flops / ms / 1e9 / PEAK_TFLOPS[w.dtype]}), flush=True)
+
+
+SWEEP_VARIANTS = [  # (label, loader, stages) on the 128 x 128 x 32 tile, then the default plan
+    ("direct_s1", 2, 1), ("vgpr_s2", 1, 2), ("direct_s2", 2, 2), ("direct_s3", 2, 3), ("direct_s4", 2, 4),
+    ("default", None, None)]
+
+
+def run_sweep(torch, lib, dev, args, rounds=3):
+    """The bf16 shape sweep: every sweep shape x (the 128 x 128 x 32 tile
+    with the register-staged loader at 2 slots and the direct loader at 1 to
+    4 slots, and the default plan).  Per-launch times come from HIP-graph
+    replay (the smallest shapes run for a few microseconds, less than the
+    host's launch path), interleaved over the variants `rounds` times; the
+    median is reported.  Each variant's C must equal the default plan's bit
+    for bit (the oracle check of every cell is tests/test_fullsize_gpu.py).
+    With --sweep-summary PATH also a Markdown heatmap."""
+    from tiled_software_pipelined_amd import inputs, metrics
+    vs = []
+    for label, loader, st in SWEEP_VARIANTS:
+        v = None if loader is None else lib.Variant(
+            kernel=lib.KERNEL_TILED, tile_m=128, tile_n=128, tile_k=32, stages=st, loader=loader,
+            lds_layout=lib.LDS_XOR, waves_m=2, waves_n=2)
+        vs.append((label, v))
+    cells = []
+    for name, sw in inputs.workloads().items():
+        if not name.startswith("bf16_sweep"):
+            continue
+        a, b = sw.operands()
+        a, b = a.to(dev), b.to(dev)
+        c = torch.empty((sw.M, sw.N), dtype=torch.float32, device=dev)
+        ref = torch.empty_like(c)
+        lib.gemm(a, b, out=ref)
+        torch.cuda.synchronize()
+        ideal_ms = 1e3 * metrics.roofline_time(sw.M, sw.N, sw.K, 2, 4, PEAK_TFLOPS["bf16"] * 1e12,
+                                               PEAK_HBM_GBS * 1e9)
+        times = {label: [] for label, _ in vs}
+        for _ in range(rounds):
+            for label, v in vs:
+                ms, same = time_graph(lib, torch, a, b, c, v)
+                if not same:
+                    raise RuntimeError("graph replay of %s (%s) did not reproduce the eager result" % (name, label))
+                if not torch.equal(c, ref):
+                    raise RuntimeError("%s (%s) differs from the default plan's C" % (name, label))
+                times[label].append(ms)
+        for label, v in vs:
+            ms = statistics.median(times[label])
+            rec = {"mode": "sweep", "workload": name, "M": sw.M, "N": sw.N, "K": sw.K, "plan": label,
+                   "kernel": lib.plan_for(sw.M, sw.N, sw.K, lib.BF16, sw.K, sw.N, sw.N, v).name,
+                   "median_ms": ms, "tflops": sw.flops / ms / 1e9, "frac_peak": sw.flops / ms / 1e9 / PEAK_TFLOPS["bf16"],
+                   "frac_roofline": ideal_ms / ms, "ideal_ms": ideal_ms, "same_bits_as_default": True}
+            cells.append(rec)
+            print(json.dumps(rec), flush=True)
+        del a, b, c, ref
+    if args.sweep_summary:
+        write_sweep_summary(args, cells)
+
+
+def write_sweep_summary(args, cells):
+    import torch
+    from tiled_software_pipelined_amd import lib
+    labels = [l for l, _, _ in SWEEP_VARIANTS]
+    shapes = []
+    for c in cells:
+        if (c["M"], c["K"]) not in shapes:
+            shapes.append((c["M"], c["K"]))
+    get = {(c["M"], c["K"], c["plan"]): c for c in cells}
+    out = ["# bf16 shape sweep by loader and ring depth", "",
+           "Command: `python bench.py --sweep --sweep-summary %s`" % args.sweep_summary, "",
+           "Device: %s, libtgemm %s.  TFLOP/s per cell from HIP-graph replay (20 launches per replay, median "
+           "of 3 interleaved rounds).  The 128 x 128 x 32 tile with the register-staged loader at 2 slots "
+           "(`vgpr_s2`) and the direct global->LDS loader at 1 to 4 slots, and the default plan.  Every "
+           "cell's C equals the default plan's bit for bit; tests/test_fullsize_gpu.py checks every cell "
+           "against the oracle.  `async gain` = vgpr_s2 time / direct_s2 time - 1 (the same ring depth, "
+           "the copy alone changed); `best direct` = the fastest direct ring depth against vgpr_s2.  "
+           "%% roofline = max(2MNK / 2.5 PF, algorithmic bytes / 8 TB/s) / time." % (
+               torch.cuda.get_device_properties(0).name, lib.version()), "",
+           "| M=N | K | " + " | ".join(labels) + " | default kernel | default % roofline | async gain | "
+           "best direct vs vgpr_s2 |",
+           "|---|---|" + "---|" * len(labels) + "---|---|---|---|"]
+    for mn, k in shapes:
+        row = [str(mn), str(k)] + ["%.1f" % get[(mn, k, l)]["tflops"] for l in labels]
+        d = get[(mn, k, "default")]
+        vg = get[(mn, k, "vgpr_s2")]["median_ms"]
+        d2 = get[(mn, k, "direct_s2")]["median_ms"]
+        best = min(get[(mn, k, l)]["median_ms"] for l in ("direct_s2", "direct_s3", "direct_s4"))
+        row += ["`%s`" % d["kernel"], "%.1f" % (100 * d["frac_roofline"]), "%+.1f %%" % (100 * (vg / d2 - 1)),
+                "%+.1f %%" % (100 * (vg / best - 1))]
+        out.append("| " + " | ".join(row) + " |")
+    os.makedirs(os.path.dirname(os.path.abspath(args.sweep_summary)), exist_ok=True)
+    with open(args.sweep_summary, "w") as f:
+        f.write("\n".join(out) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -413,8 +628,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--workload", default="bf16_4096")
     ap.add_argument("--variant", default="")
-    ap.add_argument("--ladder", action="store_true")
-    ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--ladder", action="store_true",
+                    help="the ablation ladder of the workload's type (one JSON line per rung)")
+    ap.add_argument("--ladder-summary", default="", metavar="PATH",
+                    help="with --ladder: also write the rung table as Markdown to PATH")
+    ap.add_argument("--variants", action="store_true",
+                    help="time every compiled variant of the workload's type")
+    ap.add_argument("--sweep", action="store_true",
+                    help="the bf16 shape sweep by loader and ring depth (one JSON line per cell)")
+    ap.add_argument("--sweep-summary", default="", metavar="PATH",
+                    help="with --sweep: also write the heatmap as Markdown to PATH")
     ap.add_argument("--lds-probe", action="store_true",
                     help="time the LDS read-path probe: the same bytes through ds_read_b32 / b64 / "
                          "b128 / b64_tr_b16 (one JSON line per instruction form)")
@@ -466,69 +689,11 @@ def main():
     torch.cuda.synchronize()
 
     if args.ladder:
-        # Every compiled variant of this dtype, then the default plan under each
-        # workgroup order.  Timed round-robin (a few launches of each variant per
-        # round, many rounds) so that clock and thermal drift during the run
-        # spreads over all variants instead of favouring the ones timed first.
-        code = {"f32": lib.F32, "bf16": lib.BF16, "i8": lib.I8}[w.dtype]
-        entries = [(v, None) for v in lib.variants(code)]
-        for grp in (lib.ORDER_ROW_MAJOR, 1, 2, 4, 8):
-            dv = lib.plan_for(w.M, w.N, w.K, code, w.K, w.N, w.N).info().variant
-            dv.wg_group = grp
-            entries.append((dv, grp))
-        slow = [i for i, (v, _) in enumerate(entries) if v.kernel == lib.KERNEL_NAIVE]
-        per_round = {i: (1 if i in slow else 3) for i in range(len(entries))}
-        rounds = max(4, args.steps // 3)
-        times = {i: [] for i in range(len(entries))}
-        for i, (v, _) in enumerate(entries):  # warm every kernel once
-            lib.gemm(A, B, out=C, variant=v)
-        torch.cuda.synchronize()
-        for r in range(rounds):
-            for i, (v, _) in enumerate(entries):
-                if i in slow and r >= 2:
-                    continue
-                per, _ = time_plan(lib, torch, w, A, B, C, v, per_round[i], 0)
-                times[i] += per
-        for i, (v, grp) in enumerate(entries):
-            t = sorted(times[i])
-            ms = t[len(t) // 2]
-            rec = {"mode": "ladder", "workload": w.name,
-                   "kernel": lib.plan_for(w.M, w.N, w.K, code, w.K, w.N, w.N, v).name,
-                   "median_ms": ms, "p10_ms": t[len(t) // 10], "launches": len(t),
-                   "tflops": w.flops / ms / 1e9, "frac_peak": w.flops / ms / 1e9 / PEAK_TFLOPS[w.dtype]}
-            if grp is not None:
-                rec["wg_group"] = grp
-            print(json.dumps(rec), flush=True)
+        run_ladder(torch, lib, w, A, B, C, args)
+    if args.variants:
+        run_variants(torch, lib, w, A, B, C, args)
     if args.sweep:
-        # heatmap: every bf16 sweep shape x (128x128x32 tile at 2, 3, 4 stages,
-        # and the default plan).  The per-launch time is taken from HIP-graph
-        # replay (the smallest shapes run for a few microseconds, less than
-        # the host's launch path, so eager timing would measure the host);
-        # the eager per-launch median is reported beside it.
-        stage_vs = [("s%d" % st, lib.Variant(kernel=lib.KERNEL_TILED, tile_m=128, tile_n=128, tile_k=32,
-                                            stages=st, loader=lib.LOADER_DIRECT, waves_m=2, waves_n=2))
-                    for st in (2, 3, 4)] + [("default", None)]
-        for name, sw in inputs.workloads().items():
-            if not name.startswith("bf16_sweep"):
-                continue
-            a, b = sw.operands()
-            a, b = a.to(dev), b.to(dev)
-            c = torch.empty((sw.M, sw.N), dtype=torch.float32, device=dev)
-            ideal_ms = 1e3 * metrics.roofline_time(sw.M, sw.N, sw.K, 2, 4, PEAK_TFLOPS["bf16"] * 1e12,
-                                                   PEAK_HBM_GBS * 1e9)
-            for label, v in stage_vs:
-                per, _ = time_plan(lib, torch, sw, a, b, c, v, max(10, args.steps // 2), 5)
-                eager_ms = sorted(per)[len(per) // 2]
-                ms, same = time_graph(lib, torch, a, b, c, v)
-                if not same:
-                    raise RuntimeError("graph replay of %s (%s) did not reproduce the eager result" % (name, label))
-                kname = lib.plan_for(sw.M, sw.N, sw.K, lib.BF16, sw.K, sw.N, sw.N, v).name
-                print(json.dumps({"mode": "sweep", "workload": name, "plan": label, "kernel": kname,
-                                  "median_ms": ms, "eager_median_ms": eager_ms, "tflops": sw.flops / ms / 1e9,
-                                  "eager_tflops": sw.flops / eager_ms / 1e9,
-                                  "frac_peak": sw.flops / ms / 1e9 / PEAK_TFLOPS["bf16"],
-                                  "frac_roofline": ideal_ms / ms}), flush=True)
-            del a, b, c
+        run_sweep(torch, lib, dev, args)
 
     if args.soak:
         soak(torch, lib, w, A, B, C, args.soak)

@@ -79,7 +79,8 @@ typedef enum tgemm_dtype {
 /* LDS layouts (GEMM page, section 8.5). */
 #define TGEMM_LDS_PLAIN 1
 #define TGEMM_LDS_XOR 2          /* 16-byte chunk index XOR-swizzled by row; for the fp32
-                                    kernels: each lane's outputs split in quarters 32 apart */
+                                    kernels: the rows of transposed A padded (conflict-free
+                                    A writes) */
 #define TGEMM_LDS_XOR_POISON 3   /* debug form of TGEMM_LDS_XOR for the direct-loader ring:
                                     each lane fills the 16 LDS bytes a direct copy will
                                     write with all-ones bytes (bf16 NaN, int8 -1) and waits
@@ -89,10 +90,9 @@ typedef enum tgemm_dtype {
                                     C.  Same results as TGEMM_LDS_XOR when the ring is
                                     correct; slower.  Only chosen when requested. */
 
-/* Access width of global loads, LDS writes and LDS fragment reads
- * (GEMM page, section 7: 128-bit vector accesses).  For the fp32 kernels it
- * selects the A fragment read: WIDE = A transposed in LDS, two 16-byte reads;
- * NARROW = A row-major in LDS, eight 4-byte reads. */
+/* Access width of global loads and LDS writes (GEMM page, section 7:
+ * 128-bit vector accesses); fragment reads have their own field below (the
+ * narrow matrix-core rung reads 4 bytes at a time). */
 #define TGEMM_ACCESS_WIDE 1      /* 16-byte accesses */
 #define TGEMM_ACCESS_NARROW 2    /* 4-byte global loads / LDS accesses */
 
@@ -110,6 +110,27 @@ typedef enum tgemm_dtype {
 #define TGEMM_COPY_SPREAD 2      /* part of them there, the rest spread over the K steps of the
                                     next slice (fewer memory instructions between any two
                                     matrix instructions; a shorter lead for the rest) */
+
+/* How operand fragments are read out of LDS (the LDS -> register ladder of
+ * the SM80 ablation plan, section 1.1).  Matrix-core kernels: the A fragment
+ * (16 bytes of one row per lane) as four 4-byte, two 8-byte or one 16-byte
+ * ds_read; the B fragment (one column per lane, K-contiguous, out of
+ * N-contiguous LDS rows) by one element read per K value, or (TR) by two
+ * transposing reads ds_read_b64_tr_b16 (bf16) / ds_read_b64_tr_b8 (int8).
+ * fp32 kernels report B128 (A transposed in LDS, 16-byte reads) or B32. */
+#define TGEMM_READ_B32 1         /* A: 4 x ds_read_b32; B: element reads */
+#define TGEMM_READ_B64 2         /* A: 2 x ds_read_b64; B: element reads */
+#define TGEMM_READ_B128 3        /* A: 1 x ds_read_b128; B: element reads */
+#define TGEMM_READ_TR 4          /* A: 1 x ds_read_b128; B: 2 transposing reads (16-byte kernels' default) */
+#define TGEMM_READ_KVEC 5        /* fp32: A row-major in LDS, 16-byte reads along K (4 k steps each) */
+
+/* Which outputs a lane of the fp32 kernels owns (GEMM page, sections 7.4 and
+ * 8.5); matrix-core kernels report BLOCKS. */
+#define TGEMM_LANES_BLOCKS 1     /* one contiguous TM x TN block, lanes row-major on the wave's 8 x 8 grid */
+#define TGEMM_LANES_QUARTERS 2   /* 4 x 4 quarters 32 rows / columns apart (scheme 4: sub-block split) */
+#define TGEMM_LANES_ZORDER 3     /* contiguous blocks, lanes in Z order (scheme 3: each 16-lane group
+                                    covers a 4 x 4 square of the lane grid) */
+#define TGEMM_LANES_ZQUARTERS 4  /* both */
 
 /* Workgroup order (GEMM page, section 2.3). */
 #define TGEMM_ORDER_ROW_MAJOR (-1)
@@ -136,6 +157,8 @@ typedef struct tgemm_variant {
                            VECTOR: the operands of every matrix instruction swapped, C^T = B^T A^T,
                            so each lane holds four consecutive columns: 16-byte stores) */
     int32_t copy_sched; /* TGEMM_COPY_* (matrix-core direct loader; other kernels report BURST) */
+    int32_t frag_read;  /* TGEMM_READ_* */
+    int32_t lane_map;   /* TGEMM_LANES_* */
 } tgemm_variant;
 
 typedef struct tgemm_plan tgemm_plan;

@@ -299,10 +299,16 @@ def test_guard_follows_global_load_width_for_every_variant():
     # N = 257 leaves a partial 16-byte chunk at the end of every B row: every
     # tiled variant that loads B in chunks must guard B (found on the fp32
     # rung whose A-fragment access is narrow but whose B loads are 16 bytes)
+    # (the fp32 rungs with 4-byte global loads read one element at a time,
+    # each checked against N, and need no guard)
     for dtype in (tl.F32, tl.BF16, tl.I8):
         for v in tl.variants(dtype):
             info = tl.Plan(129, 257, 40, dtype, variant=v).info()
-            if info.variant.kernel == tl.KERNEL_TILED:
+            if info.variant.kernel != tl.KERNEL_TILED:
+                continue
+            if dtype == tl.F32 and info.variant.access == tl.ACCESS_NARROW:
+                assert info.b_guarded == 0, info.name.decode()
+            else:
                 assert info.b_guarded == 1, info.name.decode()
 
 
@@ -339,3 +345,22 @@ def test_run_ws_without_workspace_falls_back_to_run():
     # M = 0: both return before touching the device
     p = tl.Plan(0, 16, 16, tl.BF16)
     p.run_ws_ptr(0, 0, 0, 0, 0)
+
+
+def test_ladders_select_distinct_kernels():
+    # every rung of the ablation ladders resolves to its own kernel (no two
+    # rungs time the same code), except where a rung repeats another on
+    # purpose (A4 = R7s3: the fragment-read ladder ends on the 3-slot kernel)
+    from tiled_software_pipelined_amd import inputs, ladders
+    for dtype, rungs in ladders.LADDERS.items():
+        code = {"f32": tl.F32, "bf16": tl.BF16, "i8": tl.I8}[dtype]
+        w = inputs.workloads()[ladders.LADDER_WORKLOAD[dtype]]
+        names = {}
+        for r in rungs:
+            v = None if r.fields is None else tl.Variant(**r.fields)
+            names.setdefault(tl.Plan(w.M, w.N, w.K, code, variant=v).name, []).append(r.label)
+        dup = {k: v for k, v in names.items() if len(v) > 1}
+        assert all(set(v) == {"R7s3", "A4"} for v in dup.values()), dup
+        for r in rungs:
+            if r.base is not None:
+                assert r.base in [x.label for x in rungs], r.label

@@ -40,6 +40,16 @@ void register_bf16(void (*add)(const KernelEntry&)) {
     add(mfma_entry<T, 128, 128, 32, 2, 2, 1, LD_VGPR, LY_PLAIN, AC_WIDE, FR_REUSE, 2>(1));
     add(mfma_entry<T, 128, 128, 32, 2, 2, 1, LD_VGPR, LY_PLAIN, AC_NARROW, FR_REUSE, 2>(1));
     add(mfma_entry<T, 128, 128, 32, 2, 2, 1, LD_VGPR, LY_PLAIN, AC_NARROW, FR_PER_MMA, 2>(1));
+    // 16-byte global loads and LDS writes with the narrow rung's 4-byte
+    // fragment reads: the global-load width and the fragment-read width are
+    // separate rungs
+    add(mfma_entry<T, 128, 128, 32, 2, 2, 1, LD_VGPR, LY_PLAIN, AC_WIDE, FR_REUSE, 2, 0, CST_MFMA, false, RD_B32>(1));
+    // the fragment-read ladder on the direct loader, 3 slots, XOR layout:
+    // A by 4 / 8 / 16-byte reads with B by element reads (then the
+    // transposing B reads: the 3-slot kernel above)
+    add(mfma_entry<T, 128, 128, 32, 2, 2, 3, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2, 0, CST_MFMA, false, RD_B32>(1));
+    add(mfma_entry<T, 128, 128, 32, 2, 2, 3, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2, 0, CST_MFMA, false, RD_B64>(1));
+    add(mfma_entry<T, 128, 128, 32, 2, 2, 3, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2, 0, CST_MFMA, false, RD_B128>(1));
     add(naive_entry<1>());
     // unlisted: thin products (N <= 16) and split-plan remainders
     add(thin_entry<1, 1>());

@@ -21,7 +21,19 @@ void register_i8(void (*add)(const KernelEntry&)) {
     // half the compute units
     add(mfma_entry<T, 128, 64, 64, 2, 2, 4, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2>(2));
     add(mfma_entry<T, 64, 128, 64, 2, 2, 4, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2>(2));
+    // the 128 x 128 x 64 ladder below the 1-slot direct kernel, one change per
+    // step: per-instruction 4-byte fragment reads -> fragment reuse ->
+    // 16-byte global loads / LDS writes -> 16-byte and transposing fragment
+    // reads -> XOR layout
+    add(mfma_entry<T, 128, 128, 64, 2, 2, 1, LD_VGPR, LY_XOR, AC_WIDE, FR_REUSE, 2>(2));
+    add(mfma_entry<T, 128, 128, 64, 2, 2, 1, LD_VGPR, LY_PLAIN, AC_WIDE, FR_REUSE, 2>(2));
+    add(mfma_entry<T, 128, 128, 64, 2, 2, 1, LD_VGPR, LY_PLAIN, AC_WIDE, FR_REUSE, 2, 0, CST_MFMA, false, RD_B32>(2));
+    add(mfma_entry<T, 128, 128, 64, 2, 2, 1, LD_VGPR, LY_PLAIN, AC_NARROW, FR_REUSE, 2>(2));
     add(mfma_entry<T, 128, 128, 64, 2, 2, 1, LD_VGPR, LY_PLAIN, AC_NARROW, FR_PER_MMA, 2>(2));
+    // the fragment-read ladder on the direct loader, 3 slots, XOR layout
+    add(mfma_entry<T, 128, 128, 64, 2, 2, 3, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2, 0, CST_MFMA, false, RD_B32>(2));
+    add(mfma_entry<T, 128, 128, 64, 2, 2, 3, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2, 0, CST_MFMA, false, RD_B64>(2));
+    add(mfma_entry<T, 128, 128, 64, 2, 2, 3, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2, 0, CST_MFMA, false, RD_B128>(2));
     add(naive_entry<2>());
     // unlisted: thin products (N <= 16) and split-plan remainders
     add(thin_entry<2, 1>());

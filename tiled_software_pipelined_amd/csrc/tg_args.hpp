@@ -60,6 +60,8 @@ struct KernelEntry {
     int tail_ok;     // handles K not a multiple of bk
     int waves_per_simd;  // occupancy the kernel is compiled for (its registers allow at least this)
     int copy_sched;  // TGEMM_COPY_BURST / TGEMM_COPY_SPREAD (direct loader; others report BURST)
+    int frag_read;   // TGEMM_READ_*: how fragments come out of LDS
+    int lane_map;    // TGEMM_LANES_*: outputs of a lane (fp32 kernels; others report BLOCKS)
     KernelFn fn;
     char name[96];
 };

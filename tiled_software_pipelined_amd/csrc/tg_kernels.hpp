@@ -22,10 +22,10 @@ static const char* dtype_tag(int dt) { return dt == 0 ? "f32" : dt == 1 ? "bf16"
 // SHIFT: which operands the kernel reads from rows that are not 16-byte
 // aligned (bit 0 A, bit 1 B).  Such kernels are unlisted fallbacks.
 template <class Tr, int BM, int BN, int BK, int WM, int WN, int S, int LD, int LY, int AC, int FR,
-          int WAVES, int SHIFT = 0, int CST = CST_MFMA, bool SPREAD = false>
+          int WAVES, int SHIFT = 0, int CST = CST_MFMA, bool SPREAD = false, int FREAD = RD_AUTO>
 KernelEntry mfma_entry(int dtype) {
     static_assert(!SPREAD || LD == LD_DIRECT, "spread copies: the direct loader");
-    typedef MfmaGemm<Tr, BM, BN, BK, WM, WN, S, LD, LY, AC, FR, SHIFT, CST, SPREAD> K;
+    typedef MfmaGemm<Tr, BM, BN, BK, WM, WN, S, LD, LY, AC, FR, SHIFT, CST, SPREAD, FREAD> K;
     KernelEntry e{};
     e.dtype = dtype;
     e.family = FAM_TILED;
@@ -41,6 +41,8 @@ KernelEntry mfma_entry(int dtype) {
     e.wn = WN;
     e.store = CST == CST_SWAP ? 1 : 2;  // TGEMM_STORE_VECTOR / TGEMM_STORE_SCALAR
     e.copy_sched = SPREAD ? 2 : 1;      // TGEMM_COPY_SPREAD / TGEMM_COPY_BURST
+    e.lane_map = 1;
+    e.frag_read = K::FREAD;             // TGEMM_READ_* (same values as FragRead)
     e.gload_bytes = AC == AC_WIDE ? 16 : 4;
     e.threads = K::NT;
     e.lds_bytes = K::LDS_BYTES;
@@ -50,12 +52,14 @@ KernelEntry mfma_entry(int dtype) {
     e.tail_ok = 1;
     e.waves_per_simd = WAVES;
     e.fn = gemm_kernel<K, WAVES>;
-    snprintf(e.name, sizeof e.name, "%s_t%dx%dx%d_w%dx%d_s%d_%s_%s_%s_%s%s%s%s", dtype_tag(dtype), BM, BN,
+    snprintf(e.name, sizeof e.name, "%s_t%dx%dx%d_w%dx%d_s%d_%s_%s_%s_%s%s%s%s%s", dtype_tag(dtype), BM, BN,
              BK, WM, WN, S, LD == LD_DIRECT ? "direct" : "vgpr",
              LY == LY_XOR ? "xor" : LY == LY_XOR_POISON ? "xorpoison" : "plain",
              AC == AC_WIDE ? "wide" : "narrow", FR == FR_REUSE ? "reuse" : "permma",
              SHIFT == 1 ? "_shiftA" : SHIFT == 2 ? "_shiftB" : SHIFT == 3 ? "_shiftAB" : "",
-             CST == CST_SWAP ? "_vst" : "", SPREAD ? "_spread" : "");
+             CST == CST_SWAP ? "_vst" : "", SPREAD ? "_spread" : "",
+             FREAD == RD_AUTO ? "" : FREAD == RD_B32 ? "_rd32" : FREAD == RD_B64 ? "_rd64" :
+             FREAD == RD_B128 ? "_rd128" : "_rdtr");
     return e;
 }
 
@@ -84,6 +88,8 @@ KernelEntry naive_entry() {
     e.tail_ok = 1;
     e.waves_per_simd = 4;
     e.copy_sched = 1;
+    e.frag_read = 1;  // no LDS: element loads straight from memory
+    e.lane_map = 1;
     e.fn = gemm_kernel<K, 4>;
     snprintf(e.name, sizeof e.name, "%s_naive", dtype_tag(DT));
     return e;
@@ -117,16 +123,21 @@ KernelEntry thin_entry() {
     e.tail_ok = 1;
     e.waves_per_simd = 2;
     e.copy_sched = 1;
+    e.frag_read = 3;  // A streamed in 16-byte pieces
+    e.lane_map = 1;
     e.fn = gemm_kernel<K, 2>;
     snprintf(e.name, sizeof e.name, "%s_thin_n%d", dtype_tag(DT), NB);
     return e;
 }
 
-// fp32 ladder rungs: access / frag fields encode TRANS_A and QUARTERS, the
-// layout field VEC_STORE (see inst_f32.hip).
-template <int S, bool TA, bool QU, bool VS, int BK = 8, int TILE = 128, int TILE_N = TILE>
-KernelEntry f32_entry() {
-    typedef F32Gemm<S, TA, QU, VS, BK, TILE, TILE_N> K;
+// fp32 kernels (tg_f32.hpp), by flag set.  Variant fields: loader, access
+// (global load width), frag (register reuse), frag_read (A's fragment: 4-byte
+// reads of row-major A, 16-byte reads of transposed A, or 16-byte reads along
+// K), lds_layout (PLAIN, or XOR for the padded rows of transposed A),
+// lane_map (contiguous blocks, 4 x 4 quarters, Z-order lanes) and store.
+template <int S, int FLAGS, int BK = 8, int TILE = 128, int TILE_N = TILE>
+KernelEntry f32_flags_entry() {
+    typedef F32Gemm<S, FLAGS, BK, TILE, TILE_N> K;
     // 8 x 8 outputs per lane take ~140 registers (3 waves per SIMD); 4 x 4
     // take few enough for 4
     constexpr int WAVES = TILE == 128 ? 2 : 4;  // 8 x 16 outputs per lane: 2 as well
@@ -137,26 +148,38 @@ KernelEntry f32_entry() {
     e.bn = K::BN;
     e.bk = K::BK;
     e.stages = S;
-    e.loader = LD_VGPR;
-    e.layout = QU ? LY_XOR : LY_PLAIN;    // conflict-free quarters vs contiguous blocks
-    e.access = TA ? AC_WIDE : AC_NARROW;  // A fragment: 16-byte reads of transposed A vs 4-byte reads
-    e.frag = FR_REUSE;
-    e.store = VS ? 1 : 2;                 // TGEMM_STORE_VECTOR / TGEMM_STORE_SCALAR
-    e.gload_bytes = 16;                   // A and B always loaded as float4
+    e.loader = K::DIRECT ? LD_DIRECT : LD_VGPR;
+    e.layout = K::PAD_A ? LY_XOR : LY_PLAIN;
+    e.access = K::WIDE_G ? AC_WIDE : AC_NARROW;
+    e.frag = K::REUSE ? FR_REUSE : FR_PER_MMA;
+    e.frag_read = K::TRANS_A ? RD_B128 : K::AKVEC ? 5 : RD_B32;  // 5: TGEMM_READ_KVEC
+    e.lane_map = K::QUARTERS ? (K::ZORDER ? 4 : 2) : (K::ZORDER ? 3 : 1);
+    e.store = K::VEC_STORE ? 1 : 2;      // TGEMM_STORE_VECTOR / TGEMM_STORE_SCALAR
+    e.copy_sched = 1;
+    e.gload_bytes = K::WIDE_G ? 16 : 4;
     e.wm = 2;
     e.wn = 2;
     e.threads = K::NT;
     e.lds_bytes = K::LDS_BYTES;
-    e.loads_per_stage = K::N_LD;
-    e.shift_mask = 3;  // its own guarded element loads
+    e.loads_per_stage = K::WIDE_G ? K::N_LD : K::EA + K::EB;
+    e.shift_mask = K::DIRECT ? 0 : 3;  // register-staged kernels have their own guarded element loads
     e.listed = 1;
     e.tail_ok = 1;
     e.waves_per_simd = WAVES;
-    e.copy_sched = 1;
     e.fn = gemm_kernel<K, WAVES>;
-    snprintf(e.name, sizeof e.name, "f32_t%dx%dx%d_w2x2_s%d_%s_%s_%s", TILE, TILE_N, BK, S, TA ? "transA" : "rowA",
-             QU ? "quarters" : "blocks", VS ? "vecstore" : "scalarstore");
+    snprintf(e.name, sizeof e.name, "f32_t%dx%dx%d_w2x2_s%d_%s_%s_%s%s_%s%s_%s", TILE, TILE_N, BK, S,
+             K::DIRECT ? "direct" : "vgpr", K::WIDE_G ? "g16" : "g4",
+             K::TRANS_A ? "transA" : K::AKVEC ? "kvecA" : "rowA", K::PAD_A ? "_pad" : "",
+             K::QUARTERS ? (K::ZORDER ? "zquarters" : "quarters") : (K::ZORDER ? "zorder" : "blocks"),
+             K::REUSE ? "" : "_permfma", K::VEC_STORE ? "vecstore" : "scalarstore");
     return e;
+}
+
+// The production form: transposed A with padded rows, quarters, 16-byte C
+// stores (flags of the fully switched-on ladder), at S stages.
+template <int S, int BK = 8, int TILE = 128, int TILE_N = TILE>
+KernelEntry f32_entry() {
+    return f32_flags_entry<S, F_TRANS_A | F_PAD_A | F_QUARTERS | F_VEC_STORE, BK, TILE, TILE_N>();
 }
 
 }  // namespace tg

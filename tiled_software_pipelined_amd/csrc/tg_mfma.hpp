@@ -77,11 +77,21 @@ struct TraitsI8 {
 // each.
 enum CStore { CST_MFMA = 0, CST_SWAP = 1 };
 
+// How the operand fragments come out of LDS (the LDS -> register ladder of
+// the SM80 ablation plan, section 1.1, on this GPU's instructions): the A
+// fragment (16 bytes of one row per lane) as four 4-byte, two 8-byte or one
+// 16-byte read; the B fragment (one column, K-contiguous per lane, from the
+// N-contiguous LDS rows) as one element read per K value, or as two
+// transposing ds_read_b64_tr_b16 / _tr_b8 reads.  RD_AUTO: RD_TR for 16-byte
+// accesses, RD_B32 for the narrow rung.
+enum FragRead { RD_AUTO = 0, RD_B32 = 1, RD_B64 = 2, RD_B128 = 3, RD_TR = 4 };
+
 // SPREAD (direct loader): issue each slice's copies in two parts, the
 // second spread over the K steps of the following slice, instead of all of
 // them right after the slice's barrier (see N1 below).
 template <class Tr, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int LOADER,
-          int LAYOUT, int ACCESS, int FRAG, int SHIFT = 0, int CST = CST_MFMA, bool SPREAD = false>
+          int LAYOUT, int ACCESS, int FRAG, int SHIFT = 0, int CST = CST_MFMA, bool SPREAD = false,
+          int FREAD_ = RD_AUTO>
 struct MfmaGemm {
     typedef typename Tr::T T;
     typedef typename Tr::Out Out;
@@ -117,6 +127,7 @@ struct MfmaGemm {
     static constexpr bool XOR = LAYOUT == LY_XOR || LAYOUT == LY_XOR_POISON;
     static constexpr bool POISON = LAYOUT == LY_XOR_POISON;
     static constexpr bool WIDE = ACCESS == AC_WIDE;
+    static constexpr int FREAD = FREAD_ != RD_AUTO ? FREAD_ : (WIDE ? RD_TR : RD_B32);
     static constexpr bool DIRECT = LOADER == LD_DIRECT;
     // narrow (4-byte) accesses
     static constexpr int A_DW = BM * KB / 4 / NT;  // A dwords per thread per slice
@@ -133,6 +144,7 @@ struct MfmaGemm {
     static_assert(N_LD * (STAGES > 2 ? STAGES - 2 : 0) <= 63, "vmcnt range");
     static_assert(!POISON || (DIRECT && STAGES >= 2), "poisoned slots: the direct-loader ring");
     static_assert(SHIFT == 0 || (LOADER == LD_VGPR && WIDE), "shifted loads: register-staged, 16-byte chunks");
+    static_assert(WIDE || FREAD == RD_B32, "the narrow rung reads 4 bytes at a time");
     // Shifted chunks complete their pairs from the neighbouring lane after
     // the multiply when the staged registers are few (the extra block and
     // shift per chunk then fit); with more chunks per thread the pair is
@@ -452,60 +464,69 @@ struct MfmaGemm {
 
     // ---- fragments -----------------------------------------------------------
     // A fragment of 32 x 32 tile row block at `row0`, K step s: lane l holds
-    // row row0 + l%32, bytes [16 (l/32), +16) of the step's 32-byte K span.
+    // row row0 + l%32, bytes [16 (l/32), +16) of the step's 32-byte K span:
+    // one 16-byte read, or (RD_B64 / RD_B32) two 8-byte or four 4-byte reads
+    // of the same bytes (volatile, so that they are not merged).
     __device__ static __forceinline__ i32x4 read_a(const TG_LDS char* slot, int row0, int s, int lane) {
         const int row = row0 + (lane & 31);
         const int c = 2 * s + (lane >> 5);
-        if constexpr (WIDE) {
-            return *reinterpret_cast<const TG_LDS i32x4*>(slot + row * KB + a_chunk(row, c) * 16);
+        const TG_LDS char* p = slot + row * KB + a_chunk(row, c) * 16;
+        if constexpr (FREAD == RD_B32) {
+            const volatile TG_LDS int32_t* q = reinterpret_cast<const volatile TG_LDS int32_t*>(p);
+            return i32x4{q[0], q[1], q[2], q[3]};
+        } else if constexpr (FREAD == RD_B64) {
+            const volatile TG_LDS i32x2* q = reinterpret_cast<const volatile TG_LDS i32x2*>(p);
+            const i32x2 lo = q[0], hi = q[1];
+            return i32x4{lo.x, lo.y, hi.x, hi.y};
         } else {
-            const volatile TG_LDS int32_t* p =
-                reinterpret_cast<const volatile TG_LDS int32_t*>(slot + row * KB + c * 16);
-            return i32x4{p[0], p[1], p[2], p[3]};
+            return *reinterpret_cast<const TG_LDS i32x4*>(p);
         }
     }
 
     // B fragment of the 32-column block at `col0`, K step s: lane l holds
-    // column col0 + l%32 and K rows s*MK + (MK/2)(l/32) + e.  Transposing
-    // reads: in each 16-lane group, input lane j points at row kb + j/(8/ESZ)
-    // and 8 bytes of columns; output lane i receives column nb + i of 8/ESZ
-    // consecutive rows.
-    // Half h (0: first, 1: second 8/ESZ K rows of the lane's run) of the B
-    // fragment: one transposing read.
+    // column col0 + l%32 and K rows s*MK + (MK/2)(l/32) + e.  Half h (0:
+    // first, 1: second 8/ESZ K rows of the lane's run).  RD_TR: one
+    // transposing read - in each 16-lane group, input lane j points at row
+    // kb + j/(8/ESZ) and 8 bytes of columns; output lane i receives column
+    // nb + i of 8/ESZ consecutive rows.  Otherwise 8/ESZ element reads of
+    // the lane's own column (volatile, one per K row).
     __device__ static __forceinline__ i32x2 read_b_half(const TG_LDS char* bslot, int col0, int s, int lane,
                                                         int h) {
-        const int grp = lane >> 4, j = lane & 15;
-        const int nb = col0 + 16 * (grp & 1);
-        if constexpr (ESZ == 2) {
-            const int row = s * 16 + 8 * (grp >> 1) + (j >> 2) + 4 * h;
-            const int byte = (nb + 4 * (j & 3)) * 2;
-            const int c = byte >> 4, w = byte & 15;
-            const TG_LDS char* p = bslot + row * NB + b_chunk(row, c) * 16 + w;
-            return __builtin_bit_cast(i32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((TG_LDS i16x4*)(p)));
+        if constexpr (FREAD == RD_TR) {
+            const int grp = lane >> 4, j = lane & 15;
+            const int nb = col0 + 16 * (grp & 1);
+            if constexpr (ESZ == 2) {
+                const int row = s * 16 + 8 * (grp >> 1) + (j >> 2) + 4 * h;
+                const int byte = (nb + 4 * (j & 3)) * 2;
+                const int c = byte >> 4, w = byte & 15;
+                const TG_LDS char* p = bslot + row * NB + b_chunk(row, c) * 16 + w;
+                return __builtin_bit_cast(i32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((TG_LDS i16x4*)(p)));
+            } else {
+                const int row = s * 32 + 16 * (grp >> 1) + (j >> 1) + 8 * h;
+                const int byte = nb + 8 * (j & 1);
+                const int c = byte >> 4, w = byte & 15;
+                const TG_LDS char* p = bslot + row * NB + b_chunk(row, c) * 16 + w;
+                return __builtin_amdgcn_ds_read_tr8_b64_v2i32((TG_LDS i32x2*)(p));
+            }
         } else {
-            const int row = s * 32 + 16 * (grp >> 1) + (j >> 1) + 8 * h;
-            const int byte = nb + 8 * (j & 1);
-            const int c = byte >> 4, w = byte & 15;
-            const TG_LDS char* p = bslot + row * NB + b_chunk(row, c) * 16 + w;
-            return __builtin_amdgcn_ds_read_tr8_b64_v2i32((TG_LDS i32x2*)(p));
+            constexpr int PER = 8 / ESZ;  // K rows per half
+            const int col = col0 + (lane & 31);
+            const int kb = s * Tr::MK + (Tr::MK / 2) * (lane >> 5) + PER * h;
+            const int c = col / CE, w = (col % CE) * ESZ;
+            union { i32x2 v; T e[PER]; } u;
+#pragma unroll
+            for (int e = 0; e < PER; ++e) {
+                const int row = kb + e;
+                u.e[e] = *reinterpret_cast<const volatile TG_LDS T*>(bslot + row * NB + b_chunk(row, c) * 16 + w);
+            }
+            return u.v;
         }
     }
 
     __device__ static __forceinline__ i32x4 read_b(const TG_LDS char* bslot, int col0, int s, int lane) {
-        if constexpr (WIDE) {
-            const i32x2 lo = read_b_half(bslot, col0, s, lane, 0);
-            const i32x2 hi = read_b_half(bslot, col0, s, lane, 1);
-            return i32x4{lo.x, lo.y, hi.x, hi.y};
-        } else {
-            constexpr int PER = 16 / ESZ;  // K values per lane
-            union { i32x4 v; T e[PER]; } u;
-            const int col = col0 + (lane & 31);
-            const int kb = s * Tr::MK + PER * (lane >> 5);
-            const volatile TG_LDS T* base = reinterpret_cast<const volatile TG_LDS T*>(bslot);
-#pragma unroll
-            for (int e = 0; e < PER; ++e) u.e[e] = base[(kb + e) * BN + col];
-            return u.v;
-        }
+        const i32x2 lo = read_b_half(bslot, col0, s, lane, 0);
+        const i32x2 hi = read_b_half(bslot, col0, s, lane, 1);
+        return i32x4{lo.x, lo.y, hi.x, hi.y};
     }
 
     struct Frags {

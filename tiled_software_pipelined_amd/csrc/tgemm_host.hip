@@ -96,7 +96,8 @@ bool matches(const KernelEntry& e, const tgemm_variant& v) {
            field_ok(v.stages, e.stages) && field_ok(v.loader, e.loader) &&
            field_ok(v.lds_layout, e.layout) && field_ok(v.access, e.access) && field_ok(v.frag, e.frag) &&
            field_ok(v.waves_m, e.wm) && field_ok(v.waves_n, e.wn) && field_ok(v.store, e.store) &&
-           field_ok(v.copy_sched, e.copy_sched);
+           field_ok(v.copy_sched, e.copy_sched) && field_ok(v.frag_read, e.frag_read) &&
+           field_ok(v.lane_map, e.lane_map);
 }
 
 const KernelEntry* find_entry(int dtype, const tgemm_variant& v) {
@@ -279,6 +280,8 @@ void entry_to_variant(const KernelEntry& e, int32_t wg_group, tgemm_variant* v) 
     v->waves_n = e.wn;
     v->store = e.store;
     v->copy_sched = e.copy_sched;
+    v->frag_read = e.frag_read;
+    v->lane_map = e.lane_map;
 }
 
 // Per-device gfx950 check, cached.
@@ -368,7 +371,7 @@ tgemm_plan* make_plan(int64_t M, int64_t N, int64_t K, int32_t dtype, int64_t ld
     bool default_plan = false;
     if (v.kernel == TGEMM_KERNEL_AUTO && v.tile_m == 0 && v.tile_n == 0 && v.tile_k == 0 && v.stages == 0 &&
         v.loader == 0 && v.lds_layout == 0 && v.access == 0 && v.frag == 0 && v.waves_m == 0 &&
-        v.waves_n == 0 && v.store == 0 && v.copy_sched == 0) {
+        v.waves_n == 0 && v.store == 0 && v.copy_sched == 0 && v.frag_read == 0 && v.lane_map == 0) {
         e = default_entry(dtype, M, N, K, false);
         default_plan = true;
     } else {
@@ -388,6 +391,8 @@ tgemm_plan* make_plan(int64_t M, int64_t N, int64_t K, int32_t dtype, int64_t ld
         r.stages = 2;
         r.store = 0;
         r.copy_sched = 0;
+        r.frag_read = 0;
+        r.lane_map = 0;
         r.wg_group = 0;
         const KernelEntry* rs = find_entry(dtype, r);
         e = rs ? rs : default_entry(dtype, M, N, K, true);

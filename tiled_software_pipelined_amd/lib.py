@@ -31,6 +31,8 @@ ACCESS_WIDE, ACCESS_NARROW = 1, 2
 FRAG_REUSE, FRAG_PER_MMA = 1, 2
 STORE_VECTOR, STORE_SCALAR = 1, 2
 COPY_BURST, COPY_SPREAD = 1, 2
+READ_B32, READ_B64, READ_B128, READ_TR, READ_KVEC = 1, 2, 3, 4, 5
+LANES_BLOCKS, LANES_QUARTERS, LANES_ZORDER, LANES_ZQUARTERS = 1, 2, 3, 4
 ORDER_ROW_MAJOR = -1
 
 
@@ -38,7 +40,7 @@ class Variant(ctypes.Structure):
     """Mirror of ``tgemm_variant``; zero fields mean "default"."""
     _fields_ = [(n, ctypes.c_int32) for n in (
         "kernel", "tile_m", "tile_n", "tile_k", "stages", "loader", "lds_layout", "access", "frag",
-        "wg_group", "waves_m", "waves_n", "store", "copy_sched")]
+        "wg_group", "waves_m", "waves_n", "store", "copy_sched", "frag_read", "lane_map")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
