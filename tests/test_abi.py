@@ -244,7 +244,9 @@ def test_thin_products_use_the_thin_kernel():
         for N, ldb, width in [(1, 1, 1), (7, 7, 8), (16, 17, 16), (3, 64, 4)]:
             info = tl.Plan(4096, N, 4096, dtype, ldb=ldb).info()
             assert b"thin" in info.name and info.n_main == N, (dtype, N, ldb)
-            assert info.variant.tile_n == width and info.grid == 4096 // (8 if width == 16 else 16)
+            # rows per workgroup: 4 waves of 1 row (width <= 2), 2 rows (16), 4 rows
+            rows = 4 if width <= 2 else 8 if width == 16 else 16
+            assert info.variant.tile_n == width and info.variant.tile_m == rows and info.grid == 4096 // rows
         assert b"thin" not in tl.Plan(4096, 16, 4096, dtype, ldb=32).info().name
         assert b"thin" not in tl.Plan(4096, 17, 4096, dtype, ldb=17).info().name
     # fp32 keeps its one-fma-chain-per-output kernel
@@ -325,6 +327,9 @@ def test_workspace_bytes(dtype, esz):
     # repacked rows are rounded up to whole 128-byte lines
     bytes_a = _ru(M * _ru(K * esz, 128), 256)
     bytes_b = _ru(K * _ru(N * esz, 128), 256)
+    # the matrix-core plans split off the last column (the thin kernel): the
+    # repack also writes that column of B densely, K elements
+    bytes_b += _ru(K * esz, 256) if dtype != tl.F32 else 0
     a_al = (K * esz) % 16 == 0
     # leading dimensions: B rows (N = 4097) are never aligned; A rows at K = 4104 are for bf16 / fp32
     assert p.workspace_bytes(al, al) == (0 if a_al else bytes_a) + bytes_b

@@ -4,13 +4,16 @@
 namespace tg {
 
 void register_f32(void (*add)(const KernelEntry&)) {
-    // production: every rung on, 16-deep K slices (interleaved against 8:
-    // 4096^3 1509 vs 1546 us, 2048^3 309 vs 339, 1024^3 156 vs 171; 32-deep
-    // slices were no faster and take 170 VGPRs)
+    // production: every rung on, Z-order lanes (4096^3: 1467 against 1479 us
+    // with row-major lanes, interleaved), 16-deep K slices (interleaved
+    // against 8: 4096^3 1509 vs 1546 us, 2048^3 309 vs 339, 1024^3 156 vs
+    // 171; 32-deep slices were no faster and take 170 VGPRs)
+    add(f32_flags_entry<2, F_TRANS_A | F_PAD_A | F_QUARTERS | F_ZORDER | F_VEC_STORE, 16>());
     add(f32_entry<2, 16>());
     add(f32_entry<2>());
     // 64 x 64 tiles (4 x 4 outputs per lane) for grids that would leave most
     // SIMDs idle on 128 x 128 tiles
+    add(f32_flags_entry<2, F_TRANS_A | F_PAD_A | F_QUARTERS | F_ZORDER | F_VEC_STORE, 16, 64>());
     add(f32_entry<2, 16, 64>());
     add(f32_entry<2, 16, 128, 256>());
     add(f32_entry<2, 32, 64>());
@@ -46,6 +49,7 @@ void register_f32(void (*add)(const KernelEntry&)) {
     add(f32_flags_entry<2, F_AKVEC | F_QUARTERS | F_VEC_STORE | F_DIRECT, 16>());
     add(f32_flags_entry<3, F_AKVEC | F_QUARTERS | F_VEC_STORE | F_DIRECT, 16>());
     add(f32_flags_entry<4, F_AKVEC | F_QUARTERS | F_VEC_STORE | F_DIRECT, 16>());
+    add(f32_flags_entry<2, F_TRANS_A | F_PAD_A | F_QUARTERS | F_ZORDER | F_VEC_STORE, 16, 128, 256>());
     add(naive_entry<0>());
 }
 

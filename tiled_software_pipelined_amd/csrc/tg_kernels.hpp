@@ -121,11 +121,11 @@ KernelEntry thin_entry() {
     e.shift_mask = 3;  // element loads wherever a row is not aligned
     e.listed = 0;
     e.tail_ok = 1;
-    e.waves_per_simd = 2;
+    e.waves_per_simd = K::WAVES;
     e.copy_sched = 1;
     e.frag_read = 3;  // A streamed in 16-byte pieces
     e.lane_map = 1;
-    e.fn = gemm_kernel<K, 2>;
+    e.fn = gemm_kernel<K, K::WAVES>;
     snprintf(e.name, sizeof e.name, "%s_thin_n%d", dtype_tag(DT), NB);
     return e;
 }

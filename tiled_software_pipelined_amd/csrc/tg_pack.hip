@@ -17,9 +17,12 @@ namespace tg {
 // one 16-byte chunk of a destination row: the two aligned 16-byte blocks of
 // the source that cover it, funnel-shifted; byte loads where that pair would
 // leave the source's valid bytes [src, src + (rows-1) ld_s + row_bytes).
-// Bytes of the destination row past row_bytes are written as zero.
+// Bytes of the destination row past row_bytes are written as zero.  With
+// `compact`, the thread whose chunk holds bytes [col_beg, col_beg +
+// col_bytes) of the row also writes them to compact[r * col_bytes ..].
 __global__ __launch_bounds__(256) void pack_rows(const char* src, char* dst, int64_t rows, int64_t row_bytes,
-                                                 int64_t ld_s, int64_t ld_d) {
+                                                 int64_t ld_s, int64_t ld_d, char* compact, int64_t col_beg,
+                                                 int64_t col_bytes) {
     const int64_t cpr = ld_d / 16;
     const int64_t total = rows * cpr;
     const uintptr_t beg = reinterpret_cast<uintptr_t>(src);
@@ -51,17 +54,27 @@ __global__ __launch_bounds__(256) void pack_rows(const char* src, char* dst, int
             }
         }
         *reinterpret_cast<i32x4*>(dst + r * ld_d + off) = v;
+        if (compact && off + 16 > col_beg && off < col_beg + col_bytes) {
+            union { i32x4 v; char b[16]; } u;
+            u.v = v;
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                const int64_t c = off + t - col_beg;
+                if (c >= 0 && c < col_bytes) compact[r * col_bytes + c] = u.b[t];
+            }
+        }
     }
 }
 
 hipError_t launch_pack(const void* src, void* dst, int64_t rows, int64_t row_bytes, int64_t ld_s, int64_t ld_d,
-                       hipStream_t stream) {
+                       hipStream_t stream, void* compact, int64_t col_beg, int64_t col_bytes) {
     const int64_t total = rows * (ld_d / 16);
     if (total <= 0) return hipSuccess;
     const int64_t want = (total + 255) / 256;
     const unsigned blocks = (unsigned)(want < 8192 ? want : 8192);
     hipLaunchKernelGGL(pack_rows, dim3(blocks), dim3(256), 0, stream, static_cast<const char*>(src),
-                       static_cast<char*>(dst), rows, row_bytes, ld_s, ld_d);
+                       static_cast<char*>(dst), rows, row_bytes, ld_s, ld_d, static_cast<char*>(compact), col_beg,
+                       col_bytes);
     return hipGetLastError();
 }
 

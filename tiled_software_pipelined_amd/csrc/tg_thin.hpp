@@ -30,25 +30,35 @@
 
 namespace tg {
 
-template <int DT, int NB>  // DT 1: bf16 -> fp32, 2: int8 -> int32; NB: columns computed (>= N)
+// DT 1: bf16 -> fp32, 2: int8 -> int32; NB: columns computed (>= N); ROWS_ /
+// V_: rows of C per wave and sub-chunks per chunk (0: by NB)
+template <int DT, int NB, int ROWS_ = 0, int V_ = 0>
 struct ThinGemm {
     static_assert(NB >= 1 && NB <= THIN_N_MAX && (NB & (NB - 1)) == 0, "NB: a power of two up to 16");
     typedef typename std::conditional<DT == 1, uint16_t, int8_t>::type T;
     typedef typename std::conditional<DT == 1, float, int32_t>::type Acc;
     static constexpr int NT = 256;
-    static constexpr int ROWS = NB >= 16 ? 2 : 4;  // rows of C per wave (fewer for 16 columns: registers)
+    // rows of C per wave: one for the narrowest products (more workgroups,
+    // four waves per SIMD to keep A in flight; 4095 x 1 x 4104 bf16: 9.7 us
+    // against 11.6 with 4 rows), fewer for 16 columns (registers)
+    static constexpr int ROWS = ROWS_ ? ROWS_ : (NB <= 2 ? 1 : NB >= 16 ? 2 : 4);
+    // waves per SIMD the kernel is compiled for
+    static constexpr int WAVES = NB <= 2 ? 4 : 2;
     static constexpr int BM = ROWS * (NT / 64);  // rows per workgroup
     static constexpr int BN = NB;
     static constexpr int ESZ = sizeof(T);
     static constexpr int KE = 8;                 // consecutive k per lane per sub-chunk
-    static constexpr int V = NB <= 2 ? 4 : NB <= 8 ? 2 : 1;  // sub-chunks per chunk (registers)
+    // sub-chunks per chunk (registers: V x ROWS pieces of A per lane; 9 of 512
+    // cover K up to 4608 in one chunk)
+    static constexpr int V = V_ ? V_ : (NB <= 2 ? 9 : NB <= 8 ? 2 : 1);
     static constexpr int KS = 64 * KE;           // k per sub-chunk
     static constexpr int KC = V * KS;            // k per chunk
     // LDS: the chunk's B rows, NB elements each, as V x 64 runs of KE rows
-    // (run r = sub-chunk r / 64, lane r % 64); every run is followed by 16
-    // bytes of padding so that lanes reading their own rows at the same
-    // offset fall on different banks
-    static constexpr int LANE_ELEMS = KE * NB + 16 / ESZ;
+    // (run r = sub-chunk r / 64, lane r % 64), each lane's run read back as
+    // 16-byte pieces: runs are padded to an odd number of 16-byte pieces, so
+    // that the 16 lanes of one read fall on distinct banks
+    static constexpr int RUN_PIECES = (KE * NB * ESZ + 15) / 16;
+    static constexpr int LANE_ELEMS = (RUN_PIECES | 1) * 16 / ESZ;
     static constexpr int SLOT_ELEMS = V * 64 * LANE_ELEMS;
     static constexpr int BPT = KC * NB / NT;  // B elements each thread stages per chunk
     // with B rows in whole aligned 16-byte pieces: pieces per row, per thread
@@ -147,14 +157,35 @@ struct ThinGemm {
     }
 
     // Sub-chunk v of the chunk in `slot` times this lane's A elements of it.
+    // The lane's KE x NB block of B is contiguous in LDS (16-byte aligned):
+    // read as 16-byte (8-byte) pieces, not element by element.
+    static constexpr int BLK_BYTES = KE * NB * ESZ;
+    static constexpr int BLK_WORDS = BLK_BYTES / 4;
     __device__ static __forceinline__ void multiply(Acc (&acc)[ROWS][NB], const AVec (&av)[ROWS],
                                                     const TG_LDS T* slot, int v, int lane) {
         const TG_LDS T* mine = slot + (v * 64 + lane) * LANE_ELEMS;
+        uint32_t w[BLK_WORDS];
+        if constexpr (BLK_BYTES % 16 == 0) {
+#pragma unroll
+            for (int q = 0; q < BLK_BYTES / 16; ++q) {
+                const i32x4 x = reinterpret_cast<const TG_LDS i32x4*>(mine)[q];
+                w[4 * q] = x.x; w[4 * q + 1] = x.y; w[4 * q + 2] = x.z; w[4 * q + 3] = x.w;
+            }
+        } else {
+            static_assert(BLK_BYTES == 8, "int8, one column: 8 bytes");
+            const i32x2 x = reinterpret_cast<const TG_LDS i32x2*>(mine)[0];
+            w[0] = x.x; w[1] = x.y;
+        }
 #pragma unroll
         for (int e = 0; e < KE; ++e) {
             Acc b[NB];
 #pragma unroll
-            for (int j = 0; j < NB; ++j) b[j] = widen(mine[e * NB + j]);
+            for (int j = 0; j < NB; ++j) {
+                const int idx = e * NB + j;  // element of the block
+                const uint32_t word = w[idx / (4 / ESZ)];
+                if constexpr (DT == 1) b[j] = __uint_as_float((idx & 1) ? (word & 0xffff0000u) : (word << 16));
+                else b[j] = (int32_t)(word << (24 - 8 * (idx & 3))) >> 24;
+            }
 #pragma unroll
             for (int i = 0; i < ROWS; ++i) {
                 const Acc a = elem(av[i], e);
@@ -199,11 +230,16 @@ struct ThinGemm {
         else store_b(slot, r);
     }
 
-    // WIDE: A rows are 16-byte (int8: 8-byte) aligned.  The whole chunks then
-    // take one wide load per row and sub-chunk, all V sub-chunks of chunk c+1
-    // in flight while chunk c is multiplied (each sub-chunk's registers are
-    // refilled as soon as they are used); the partial last chunk, and every
-    // chunk of unaligned rows, take element loads one sub-chunk at a time.
+    // WIDE: A rows are 16-byte (int8: 8-byte) aligned, so a lane's 8
+    // elements of a row that lie inside K take one wide load (element loads
+    // with zero fill otherwise).  Before the first wait, the chunk-0 loads of
+    // B and then of every sub-chunk of A are all in flight; B is staged into
+    // LDS (waiting only for its own loads, issued first), and each
+    // sub-chunk's A registers are refilled with the next chunk's as soon as
+    // they have been multiplied, while that chunk's B is staged into the
+    // other slot: the register-staged double buffer of the GEMM page,
+    // section 9, one barrier per chunk.  Sub-chunks that start at or past K
+    // hold only zeros and are not multiplied.
     template <bool BVEC, bool WIDE>
     __device__ static __forceinline__ void run_k(const GemmArgs& g, TG_LDS T* slots) {
         typedef typename std::conditional<BVEC, i32x4[BVPT], T[BPT]>::type BRegs;
@@ -220,54 +256,28 @@ struct ThinGemm {
             for (int j = 0; j < NB; ++j) acc[i][j] = Acc(0);
 
         const int chunks = (g.K + KC - 1) / KC;
-        const int full = WIDE ? g.K / KC : 0;  // chunks on the wide path
+        AVec av[V][ROWS];
         {
             BRegs b;
             load_b_any<BVEC>(b, g, 0);
+#pragma unroll
+            for (int v = 0; v < V; ++v)
+                if (v * KS < g.K) load_a(av[v], rowp, v * KS + lane * KE, g.K, WIDE);
             store_b_any<BVEC>(slots, b);
             wait_lds_then_barrier();
         }
-        int c = 0;
-        if (WIDE && full > 0) {
-            AVec av[V][ROWS];
-#pragma unroll
-            for (int v = 0; v < V; ++v)
-#pragma unroll
-                for (int i = 0; i < ROWS; ++i)
-                    av[v][i] = *reinterpret_cast<const AVec*>(rowp[i] + v * KS + lane * KE);
-            for (; c < full; ++c) {
-                const bool more_b = c + 1 < chunks, more_a = c + 1 < full;
-                const TG_LDS T* cur = slots + (c & 1) * SLOT_ELEMS;
-                const int k_next = (c + 1) * KC + lane * KE;
-                BRegs b;
-                if (more_b) load_b_any<BVEC>(b, g, (c + 1) * KC);
-#pragma unroll
-                for (int v = 0; v < V; ++v) {
-                    multiply(acc, av[v], cur, v, lane);
-                    if (more_a) {
-#pragma unroll
-                        for (int i = 0; i < ROWS; ++i)
-                            av[v][i] = *reinterpret_cast<const AVec*>(rowp[i] + k_next + v * KS);
-                    }
-                }
-                if (more_b) store_b_any<BVEC>(slots + ((c + 1) & 1) * SLOT_ELEMS, b);
-                wait_lds_then_barrier();
-            }
-        }
-        for (; c < chunks; ++c) {
-            const bool more_b = c + 1 < chunks;
+        for (int c = 0; c < chunks; ++c) {
+            const bool more = c + 1 < chunks;
             const TG_LDS T* cur = slots + (c & 1) * SLOT_ELEMS;
             BRegs b;
-            if (more_b) load_b_any<BVEC>(b, g, (c + 1) * KC);
-            // sub-chunks that start at or past K hold only zeros: skipped
-            const int vs = min(V, (g.K - c * KC + KS - 1) / KS);
-#pragma nounroll
-            for (int v = 0; v < vs; ++v) {
-                AVec t[ROWS];
-                load_a(t, rowp, c * KC + v * KS + lane * KE, g.K, WIDE);
-                multiply(acc, t, cur, v, lane);
+            if (more) load_b_any<BVEC>(b, g, (c + 1) * KC);
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                if (c * KC + v * KS < g.K) multiply(acc, av[v], cur, v, lane);
+                if (more && (c + 1) * KC + v * KS < g.K)
+                    load_a(av[v], rowp, (c + 1) * KC + v * KS + lane * KE, g.K, WIDE);
             }
-            if (more_b) store_b_any<BVEC>(slots + ((c + 1) & 1) * SLOT_ELEMS, b);
+            if (more) store_b_any<BVEC>(slots + ((c + 1) & 1) * SLOT_ELEMS, b);
             wait_lds_then_barrier();
         }
 

@@ -29,6 +29,8 @@ struct tgemm_plan {
     tgemm_plan* packed;           // default plans: the same product on operands repacked with
                                   // 16-byte aligned rows (gemm_run_ws), else NULL
     int64_t lda_p, ldb_p;         // leading dimensions of `packed`
+    tgemm_plan* rem_compact;      // packed split plans: the thin remainder reading B's last
+                                  // N - n_main columns from a contiguous K x r copy (ldb = r)
 };
 
 namespace {
@@ -443,6 +445,7 @@ tgemm_plan* make_plan(int64_t M, int64_t N, int64_t K, int32_t dtype, int64_t ld
     p->n_main = N;
     p->rem = nullptr;
     p->packed = nullptr;
+    p->rem_compact = nullptr;
     p->lda_p = lda;
     p->ldb_p = ldb;
     if (is_default) *is_default = default_plan;
@@ -527,6 +530,19 @@ tgemm_plan* gemm_plan_variant(int64_t M, int64_t N, int64_t K, int32_t dtype, in
     p->packed = q;
     p->lda_p = lda_p;
     p->ldb_p = ldb_p;
+    if (q->rem) {
+        // the repack also writes the remainder's columns of B as a
+        // contiguous K x r block: the thin kernel then reads B as a dense
+        // vector instead of one cache line per element (4095 x 1 x 4104 bf16:
+        // 11.9 against 13.9 us)
+        const int64_t r = N - q->n_main;
+        tgemm_plan* c = make_plan(M, r, K, dtype, lda_p, r, ldc, nullptr, nullptr);
+        if (c && c->entry == q->rem->entry) {
+            p->rem_compact = c;
+        } else {
+            gemm_destroy(c);
+        }
+    }
     g_err.clear();
     return p;
 }
@@ -540,6 +556,7 @@ void gemm_destroy(tgemm_plan* plan) {
     if (!plan) return;
     gemm_destroy(plan->rem);
     gemm_destroy(plan->packed);
+    gemm_destroy(plan->rem_compact);
     delete plan;
 }
 
@@ -691,6 +708,7 @@ static int64_t pack_need(const tgemm_plan* p, const void* A, const void* B, int*
     int64_t need = 0;
     if (ma) need += (p->M * p->lda_p * esz + 255) / 256 * 256;
     if (mb) need += (p->K * p->ldb_p * esz + 255) / 256 * 256;
+    if (mb && p->rem_compact) need += (p->K * p->rem_compact->N * esz + 255) / 256 * 256;
     *mask = (ma ? 1 : 0) | (mb ? 2 : 0);
     return need;
 }
@@ -733,15 +751,27 @@ int gemm_run_ws(const tgemm_plan* p, const void* A, const void* B, void* C, void
         a = ws;
         ws += (p->M * p->lda_p * esz + 255) / 256 * 256;
     }
+    char* compact = nullptr;
     if (mask & 2) {
-        const hipError_t err = tg::launch_pack(B, ws, p->K, p->N * esz, p->ldb * esz, p->ldb_p * esz, s);
+        const int64_t packed_bytes = (p->K * p->ldb_p * esz + 255) / 256 * 256;
+        if (p->rem_compact) compact = ws + packed_bytes;
+        const int64_t r = p->rem_compact ? p->rem_compact->N : 0;
+        const hipError_t err = tg::launch_pack(B, ws, p->K, p->N * esz, p->ldb * esz, p->ldb_p * esz, s, compact,
+                                               (p->N - r) * esz, r * esz);
         if (err != hipSuccess) {
             set_err("repack of B failed: %s", hipGetErrorString(err));
             return TGEMM_E_HIP;
         }
         b = ws;
     }
-    return gemm_run(p->packed, a, b, C, stream);
+    if (!compact) return gemm_run(p->packed, a, b, C, stream);
+    // the main part on the repacked operands, then the remainder's columns
+    // from the contiguous block, on the same stream
+    tgemm_plan main_part = *p->packed;
+    main_part.rem = nullptr;
+    const int rc2 = gemm_run(&main_part, a, b, C, stream);
+    if (rc2 != TGEMM_OK) return rc2;
+    return gemm_run(p->rem_compact, a, compact, static_cast<char*>(C) + p->packed->n_main * 4, stream);
 }
 
 }  // extern "C"

@@ -109,7 +109,10 @@ def _simt() -> list:
              dict(q, stages=2, loader=2, frag_read=5)),
         Rung("S10s3", "+ 3 slots (GEMM page 10.2: multi-stage)", dict(q, stages=3, loader=2, frag_read=5)),
         Rung("S10s4", "+ 4 slots", dict(q, stages=4, loader=2, frag_read=5)),
-        Rung("P8", "S8 with 16-deep slices: the default plan", None, base="S8"),
+        Rung("P8", "S8 with 16-deep slices",
+             dict(t, tile_k=16, stages=2, loader=1, lds_layout=2, access=1, frag=1, frag_read=3, lane_map=2,
+                  store=1), base="S8"),
+        Rung("P8z", "+ Z-order lanes: the default plan", None),
         Rung("P8k", "P8 with A row-major read along K", dict(q, tile_k=16, stages=2, loader=1, frag_read=5),
              base="P8"),
         Rung("P9", "+ direct copies, 2 slots", dict(q, tile_k=16, stages=2, loader=2, frag_read=5)),
