@@ -219,19 +219,20 @@ def mfma_ceiling(torch, lib, dtype, source, reps=None, workgroups=256, launches=
     kind = lib.RATE_PROBE_KINDS.index(dtype)
     nbytes = workgroups * lib.RATE_PROBE_THREADS * 8 * 16
     if source == "random":
-        kinds = {"bf16": ("bf16_normal", 2), "i8": ("i8_uniform", 1), "f32": ("f32_uniform", 4)}
+        kinds = {"bf16": ("bf16_normal", 2), "i8": ("i8_uniform", 1), "f32": ("f32_uniform", 4),
+                 "bf16_lds": ("bf16_normal", 2), "bf16_lds_dma": ("bf16_normal", 2)}
         kname, esz = kinds[dtype]
         ops = inputs.operand(kname, nbytes // esz // 2048, 2048, 77 + kind)
     else:
-        tdt = {"bf16": torch.bfloat16, "i8": torch.int8, "f32": torch.float32}[dtype]
-        esz = {"bf16": 2, "i8": 1, "f32": 4}[dtype]
+        tdt = {"i8": torch.int8, "f32": torch.float32}.get(dtype, torch.bfloat16)
+        esz = {"i8": 1, "f32": 4}.get(dtype, 2)
         ops = torch.full((nbytes // esz,), 1 if source == "ones" else 0, dtype=tdt)
     ops = ops.contiguous().view(-1).to("cuda:0")
     out = torch.empty(workgroups * lib.RATE_PROBE_THREADS, dtype=torch.int32, device="cuda:0")
     clocks = torch.empty(2 * workgroups, dtype=torch.int64, device="cuda:0")
     per_iter = float(lib.RATE_PROBE_OPS_PER_INST[dtype]) * 16 * 4 * workgroups  # ops per loop iteration
     # about 20 ms per launch at the datasheet peak
-    reps = reps or max(1, int(20e-3 * PEAK_TFLOPS[dtype] * 1e12 / per_iter))
+    reps = reps or max(1, int(20e-3 * PEAK_TFLOPS[dtype[:4] if dtype.startswith("bf16") else dtype] * 1e12 / per_iter))
     lib.mfma_rate_probe(kind, max(1, reps // 10), ops, out, clocks)
     torch.cuda.synchronize()
     ms, ghz = [], []
@@ -650,6 +651,8 @@ def main():
                     help="GEMM and matrix-core probe back to back for S seconds each, with socket "
                          "power and shader clocks sampled by amd-smi")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-mix-probe", action="store_true",
+                    help="skip the data-movement ceiling probes of the bf16 line")
     ap.add_argument("--probe-last", action="store_true",
                     help="run the ceiling probe after the timed region instead of before the warmup "
                          "(the timed region then starts from whatever clock state the warmup leaves)")
@@ -671,11 +674,15 @@ def main():
     if args.mfma_probe:
         cases = [(dt, src, 256, 1) for dt in ("bf16", "i8") for src in ("random", "ones", "zeros")]
         cases += [("f32", src, wgs, w) for src in ("random", "ones") for w, wgs in F32_PROBE_WAVES.items()]
+        # the default bf16 kernel's matrix stream at its 2 waves per SIMD:
+        # bare, + its LDS fragment reads, + its direct copies (random operands)
+        cases += [(dt, "random", 512, 2) for dt in ("bf16", "bf16_lds", "bf16_lds_dma")]
         for dt, src, wgs, waves in cases:
             rate, ghz, ms = mfma_ceiling(torch, lib, dt, src, workgroups=wgs)
+            peak = PEAK_TFLOPS["bf16" if dt.startswith("bf16") else dt]
             print(json.dumps({"mode": "mfma_probe", "dtype": dt, "operands": src, "waves_per_simd": waves,
                               "rate": round(rate, 1), "unit": "TOP/s" if dt == "i8" else "TFLOP/s",
-                              "frac_peak": round(rate / PEAK_TFLOPS[dt], 4), "clock_ghz": round(ghz, 3),
+                              "frac_peak": round(rate / peak, 4), "clock_ghz": round(ghz, 3),
                               "median_ms": round(ms, 3)}), flush=True)
         return
 
@@ -804,6 +811,22 @@ def main():
             "value": round(rate, 1), "clock_ghz": round(ghz, 3), "frac": round(achieved / rate, 4),
             "source": "%s rate probe, random %s operands, no memory traffic; run %s the warmup steps" % (
                 unit, w.dtype, "after the timed region" if args.probe_last else "before")}
+    if w.dtype == "bf16" and not args.calib_copy and not args.no_mix_probe:
+        # the same matrix stream with the default kernel's on-chip data
+        # movement and nothing else (no barrier, no C store): what the power
+        # budget leaves once the LDS fragment reads and the direct copies are
+        # paid for (the rate probe's kinds 3 and 4, 2 waves per SIMD)
+        lds, ghz_l, _ = mfma_ceiling(torch, lib, "bf16_lds", "random", workgroups=512)
+        mix, ghz_m, _ = mfma_ceiling(torch, lib, "bf16_lds_dma", "random", workgroups=512)
+        bare, ghz_b, _ = mfma_ceiling(torch, lib, "bf16", "random", workgroups=512)
+        rec["roofline"]["data_movement_ceiling"] = {
+            "bare_2w": round(bare, 1), "bare_2w_ghz": round(ghz_b, 3),
+            "with_lds_reads": round(lds, 1), "with_lds_reads_ghz": round(ghz_l, 3),
+            "with_lds_reads_and_copies": round(mix, 1), "with_lds_reads_and_copies_ghz": round(ghz_m, 3),
+            "frac": round(achieved / mix, 4),
+            "source": "rate probe kinds 0 / 3 / 4 at 2 waves per SIMD, random bf16 operands: the default "
+                      "kernel's matrix stream bare, with its LDS fragment reads, and with its direct "
+                      "global->LDS copies as well; run after the timed region"}
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(w, A_cpu, B_cpu)
     print(json.dumps(rec), flush=True)

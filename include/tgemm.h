@@ -350,6 +350,18 @@ int tgemm_lds_read_probe(int32_t kind, int32_t pattern, int32_t reps, int32_t wo
  *   kind 1: v_mfma_i32_32x32x32_i8   (65536 ops per wave instruction)
  *   kind 2: v_fmac_f32, the fp32 vector fused multiply-add (128 flops per
  *           wave instruction), the ALU of the fp32 path
+ *   kind 3: the bf16 matrix stream of the default 256 x 256 x 64 GEMM
+ *           kernel's 128 x 64 wave tile, with its LDS fragment reads: per K
+ *           step 8 matrix instructions on 4 A and 2 B fragments while the
+ *           next step's are read (4 ds_read_b128, 4 ds_read_b64_tr_b16, one
+ *           after each matrix instruction) from 16 KiB of LDS filled with the
+ *           workgroup's first 16 KiB of operand bytes; 2 K steps per
+ *           iteration; no barrier, no memory traffic (32768 flops per
+ *           matrix instruction)
+ *   kind 4: kind 3 plus that kernel's direct global -> LDS copies, 2 per K
+ *           step per wave (global_load_lds_dwordx4, 1 KiB each) from the
+ *           workgroup's 32 KiB of operand bytes into another 16 KiB of LDS
+ *           that no read touches
  * Launches `workgroups` workgroups of 256 threads (4 waves, one per SIMD
  * while workgroups <= 256 compute units) on `stream`.  Thread t (global
  * index workgroup * 256 + thread) loads operands[8t .. 8t+3] (16 bytes each)
@@ -372,9 +384,13 @@ int tgemm_lds_read_probe(int32_t kind, int32_t pattern, int32_t reps, int32_t wo
  * real-time ticks (s_memrealtime) that wave 0 of workgroup w spent in the
  * loop.  operands (workgroups * 256 * 8 16-byte entries), out (workgroups *
  * 256 uint32) and clocks (2 * workgroups uint64) are device memory owned by
- * the caller.  Returns TGEMM_OK, TGEMM_E_ARG (kind outside 0..2, reps < 0,
- * workgroups < 1), TGEMM_E_NULL, TGEMM_E_ALIGN (operands not 16-byte, out
- * not 4-byte or clocks not 8-byte aligned) or TGEMM_E_HIP (launch failed). */
+ * the caller.  Kinds 3 and 4 are built for 2 waves per SIMD (2 workgroups
+ * per compute unit at workgroups = 512); their out[t] = fp32 bits of the sum
+ * of the thread's 128 accumulator values (the same for both kinds: the
+ * copies land where no read looks).  Returns TGEMM_OK, TGEMM_E_ARG (kind
+ * outside 0..4, reps < 0, workgroups < 1), TGEMM_E_NULL, TGEMM_E_ALIGN
+ * (operands not 16-byte, out not 4-byte or clocks not 8-byte aligned) or
+ * TGEMM_E_HIP (launch failed). */
 int tgemm_mfma_rate_probe(int32_t kind, int32_t reps, int32_t workgroups, const void* operands, uint32_t* out,
                           uint64_t* clocks, void* stream);
 

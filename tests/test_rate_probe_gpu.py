@@ -12,6 +12,8 @@ import numpy as np
 import pytest
 import torch
 
+from tiled_software_pipelined_amd import inputs
+
 pytestmark = pytest.mark.gpu
 
 tl = None
@@ -111,8 +113,39 @@ def test_rate_probe_rejects_bad_arguments():
     clocks = torch.empty(2, dtype=torch.int64, device="cuda:0")
     ops = torch.empty(256 * 8 * 8, dtype=torch.int16, device="cuda:0")
     with pytest.raises(Exception):
-        tl.mfma_rate_probe(3, 1, ops, out, clocks)
+        tl.mfma_rate_probe(5, 1, ops, out, clocks)
     with pytest.raises(Exception):
         tl.mfma_rate_probe(0, -1, ops, out, clocks)
     with pytest.raises(ValueError):
         tl.mfma_rate_probe(0, 1, ops[:-8], out, clocks)
+
+
+@pytest.mark.parametrize("kind", [3, 4])
+def test_mix_probe_all_ones(kind):
+    # all-ones bf16 operands: every matrix instruction adds K = 16 to each
+    # accumulator value; 8 accumulators x 16 values, 2 K steps per iteration
+    # -> every thread's sum is 128 x 16 x 2 x reps (exact in fp32)
+    wgs, reps = 512, 40
+    ops = torch.full((wgs * 256 * 8 * 8,), 1.0, dtype=torch.bfloat16, device="cuda:0")
+    out = torch.empty(wgs * 256, dtype=torch.int32, device="cuda:0")
+    clocks = torch.empty(2 * wgs, dtype=torch.int64, device="cuda:0")
+    tl.mfma_rate_probe(kind, reps, ops, out, clocks)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.float32)
+    assert (got == np.float32(128 * 16 * 2 * reps)).all(), got[:4]
+
+
+def test_mix_probe_copies_do_not_change_the_sums():
+    # random operands: kinds 3 and 4 read the same LDS bytes (the copies land
+    # in a region no read touches), so their sums agree bit for bit
+    wgs, reps = 512, 20
+    ops = inputs.operand("bf16_normal", wgs * 256 * 8, 8, 91).reshape(-1).cuda()
+    outs = []
+    for kind in (3, 4):
+        out = torch.empty(wgs * 256, dtype=torch.int32, device="cuda:0")
+        clocks = torch.empty(2 * wgs, dtype=torch.int64, device="cuda:0")
+        tl.mfma_rate_probe(kind, reps, ops, out, clocks)
+        torch.cuda.synchronize()
+        outs.append(out.cpu())
+    assert torch.equal(outs[0], outs[1])
+    assert np.isfinite(outs[0].numpy().view(np.float32)).all()

@@ -234,6 +234,106 @@ void fma_rate_probe(const i32x4* operands, uint32_t* out, uint64_t* clocks, int 
     }
 }
 
+// The bf16 matrix-core stream of the default 256 x 256 x 64 GEMM kernel
+// with its on-chip data movement added step by step, no barrier and no C
+// store: where the clock the power budget allows goes between the bare
+// matrix instructions (mfma_rate_probe) and the GEMM.  Per wave and K step,
+// as in that kernel's 128 x 64 wave tile: 8 matrix instructions on 4 A and 2
+// B fragments; the next step's fragments are read from LDS meanwhile (4 x
+// ds_read_b128 for A, 4 x ds_read_b64_tr_b16 for B, one read after each
+// matrix instruction), so the matrix instructions consume LDS data.  DMA
+// adds the direct global -> LDS copies at the kernel's rate, 8 per 32 matrix
+// instructions per wave (2 per loop iteration), from the workgroup's operand
+// bytes (L2-resident) into an LDS region the reads never touch.  One loop
+// iteration is two K steps (16 matrix instructions, as in the rate probe).
+constexpr int MIX_READ_BYTES = 16384;  // LDS the fragments are read from
+constexpr int MIX_DMA_BYTES = 16384;   // LDS the copies land in
+
+template <bool DMA>
+__global__ __launch_bounds__(RATE_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void mfma_mix_probe(const i32x4* operands, uint32_t* out, uint64_t* clocks, int reps) {
+    __shared__ __attribute__((aligned(1024))) char lds_raw[MIX_READ_BYTES + MIX_DMA_BYTES];
+    TG_LDS char* lds = (TG_LDS char*)(lds_raw);
+    const int64_t t = (int64_t)blockIdx.x * RATE_THREADS + threadIdx.x;
+    const i32x4* wg_ops = operands + (int64_t)blockIdx.x * RATE_THREADS * 8;
+    // the read region: the workgroup's first 16 KiB of operand bytes
+    for (int i = threadIdx.x; i < MIX_READ_BYTES / 16; i += RATE_THREADS)
+        *reinterpret_cast<TG_LDS i32x4*>(lds + 16 * i) = wg_ops[i];
+    __syncthreads();
+    const int lane = lane_id(), wave = wave_id();
+    // lane offsets of the reads: A fragment f of step s at 1 KiB-aligned
+    // rows of the read region (16 B per lane, conflict-free); B halves at
+    // 8 B per lane
+    const uint32_t rbase = (uint32_t)(uintptr_t)lds;
+    const uint32_t dbase = rbase + MIX_READ_BYTES;
+    i32x4 a[2][4], b[2][2];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) a[0][f] = *reinterpret_cast<const TG_LDS i32x4*>(lds + 1024 * f + 16 * lane);
+#pragma unroll
+    for (int f = 0; f < 2; ++f) b[0][f] = *reinterpret_cast<const TG_LDS i32x4*>(lds + 4096 + 1024 * f + 16 * lane);
+    f32x16 acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+    const char* src = reinterpret_cast<const char*>(wg_ops);
+    const uint64_t c0 = __builtin_amdgcn_s_memtime();
+    const uint64_t w0 = __builtin_amdgcn_s_memrealtime();
+    for (int it = 0; it < reps; ++it) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            const int cur = st, nxt = st ^ 1;
+            // the step's read window rotates through the region
+            const uint32_t win = (uint32_t)(((it * 2 + st + 1) & 3) * 4096);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int i = k >> 1, j = k & 1;
+                acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[cur][i]),
+                                                                 __builtin_bit_cast(bf16x8, b[cur][j]), acc[k], 0,
+                                                                 0, 0);
+                if (k < 4) {
+                    a[nxt][k] = *reinterpret_cast<const TG_LDS i32x4*>(lds + win + 1024 * k + 16 * lane);
+                } else {
+                    const int f = (k - 4) >> 1, h = (k - 4) & 1;
+                    const TG_LDS char* pb = lds + ((win + 2048) & (MIX_READ_BYTES - 1)) + 1024 * f + 512 * h + 8 * lane;
+                    const i32x2 v = __builtin_bit_cast(
+                        i32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((TG_LDS i16x4*)(pb)));
+                    if (h == 0) {
+                        b[nxt][f].x = v.x;
+                        b[nxt][f].y = v.y;
+                    } else {
+                        b[nxt][f].z = v.x;
+                        b[nxt][f].w = v.y;
+                    }
+                }
+                if (DMA && (k == 3 || k == 7)) {
+                    // copy (it * 4 + st * 2 + k / 4) of this wave: 1 KiB from the
+                    // workgroup's operand bytes into the copy region
+                    const int n = it * 4 + st * 2 + (k >> 2);
+                    const uint32_t lds_dst = dbase + (uint32_t)(((n * 4 + wave) & 15) * 1024);
+                    const uint32_t voff = (uint32_t)(((n * 4 + wave) & 31) * 1024 + 16 * lane);
+                    copy16_to_lds(lds_dst, voff, src);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (DMA) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        }
+    }
+    if (DMA) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const uint64_t c1 = __builtin_amdgcn_s_memtime();
+    const uint64_t w1 = __builtin_amdgcn_s_memrealtime();
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sum += acc[i][r];
+    out[t] = __builtin_bit_cast(uint32_t, sum);
+    if (threadIdx.x == 0) {
+        clocks[2 * blockIdx.x] = c1 - c0;
+        clocks[2 * blockIdx.x + 1] = w1 - w0;
+    }
+}
+
 }  // namespace tg
 
 extern "C" int tgemm_lds_read_probe(int32_t kind, int32_t pattern, int32_t reps, int32_t workgroups, uint32_t* out,
@@ -252,11 +352,12 @@ extern "C" int tgemm_lds_read_probe(int32_t kind, int32_t pattern, int32_t reps,
 
 extern "C" int tgemm_mfma_rate_probe(int32_t kind, int32_t reps, int32_t workgroups, const void* operands,
                                      uint32_t* out, uint64_t* clocks, void* stream) {
-    if (kind < 0 || kind > 2 || reps < 0 || workgroups < 1) return TGEMM_E_ARG;
+    if (kind < 0 || kind > 4 || reps < 0 || workgroups < 1) return TGEMM_E_ARG;
     if (!operands || !out || !clocks) return TGEMM_E_NULL;
     if ((uintptr_t)operands % 16 || (uintptr_t)out % 4 || (uintptr_t)clocks % 8) return TGEMM_E_ALIGN;
-    static void (*const fns[3])(const tg::i32x4*, uint32_t*, uint64_t*, int) = {
-        tg::mfma_rate_probe<0>, tg::mfma_rate_probe<1>, tg::fma_rate_probe};
+    static void (*const fns[5])(const tg::i32x4*, uint32_t*, uint64_t*, int) = {
+        tg::mfma_rate_probe<0>, tg::mfma_rate_probe<1>, tg::fma_rate_probe, tg::mfma_mix_probe<false>,
+        tg::mfma_mix_probe<true>};
     const tg::i32x4* ops = static_cast<const tg::i32x4*>(operands);
     void* args[] = {&ops, &out, &clocks, &reps};
     const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(fns[kind]), dim3((unsigned)workgroups),

@@ -151,9 +151,13 @@ def lds_read_probe(kind: int, pattern: int, reps: int, out):
     return out
 
 
-RATE_PROBE_KINDS = ("bf16", "i8", "f32")
+# kinds of tgemm_mfma_rate_probe: the bare bf16 / int8 matrix instruction, the
+# fp32 FMA, and the bf16 matrix stream of the default GEMM kernel with its LDS
+# fragment reads, then also its direct global->LDS copies
+RATE_PROBE_KINDS = ("bf16", "i8", "f32", "bf16_lds", "bf16_lds_dma")
 RATE_PROBE_THREADS = 256
-RATE_PROBE_OPS_PER_INST = {"bf16": 2 * 32 * 32 * 16, "i8": 2 * 32 * 32 * 32, "f32": 2 * 64}
+RATE_PROBE_OPS_PER_INST = {"bf16": 2 * 32 * 32 * 16, "i8": 2 * 32 * 32 * 32, "f32": 2 * 64,
+                           "bf16_lds": 2 * 32 * 32 * 16, "bf16_lds_dma": 2 * 32 * 32 * 16}
 
 
 def mfma_rate_probe(kind: int, reps: int, operands, out, clocks):

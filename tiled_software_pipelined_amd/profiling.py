@@ -44,7 +44,7 @@ OCC_FILE = "occupancy.json"
 
 def _bench_cmd(args, steps, warmup, calib=False):
     cmd = ["python3", os.path.join(ROOT, "bench.py"), "--workload", args.workload, "--steps",
-           str(steps), "--warmup", str(warmup), "--no-cpu"]
+           str(steps), "--warmup", str(warmup), "--no-cpu", "--no-mix-probe"]
     if args.variant:
         cmd += ["--variant", args.variant]
     if calib:
