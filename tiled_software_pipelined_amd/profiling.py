@@ -36,6 +36,7 @@ GROUPS = [
     ["FETCH_SIZE"],
     ["WRITE_SIZE"],
     ["TCC_HIT_sum", "TCC_MISS_sum"],
+    ["SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_ANY", "SQ_INSTS_SALU"],
 ]
 CALIB_MIB = 256
 # the main kernel's workgroups per compute unit, from the HIP runtime
@@ -372,6 +373,12 @@ def render(args, cmds, res):
         if "SQ_LDS_BANK_CONFLICT" in c and c.get("SQ_LDS_IDX_ACTIVE"):
             lines.append("| SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE | %.3f |" % (
                 c["SQ_LDS_BANK_CONFLICT"] / c["SQ_LDS_IDX_ACTIVE"]))
+        if c.get("SQ_ACTIVE_INST_VALU") is not None and c.get("SQ_BUSY_CU_CYCLES"):
+            lines.append("| SQ_ACTIVE_INST_VALU / (4 SIMDs x SQ_BUSY_CU_CYCLES) (vector-ALU issue) | %.3f |" % (
+                c["SQ_ACTIVE_INST_VALU"] / (4.0 * c["SQ_BUSY_CU_CYCLES"])))
+        if c.get("SQ_INSTS_VALU") is not None:
+            lines.append("| SQ_INSTS_VALU / SQ_INSTS_LDS per dispatch | %.4g / %s |" % (
+                c["SQ_INSTS_VALU"], "%.4g" % c["SQ_INSTS_LDS"] if "SQ_INSTS_LDS" in c else "-"))
         if c.get("TCC_HIT_sum") is not None and c.get("TCC_MISS_sum") is not None:
             tot = c["TCC_HIT_sum"] + c["TCC_MISS_sum"]
             if tot:
