@@ -70,15 +70,6 @@ typedef enum tgemm_dtype {
 #define TGEMM_KERNEL_AUTO 0      /* let the plan choose (the default) */
 #define TGEMM_KERNEL_NAIVE 1     /* one thread per C element, no LDS (section 3.1) */
 #define TGEMM_KERNEL_TILED 2     /* LDS block tiling + register / matrix-core tiles */
-/* Persistent matrix-core kernel (bf16 / int8): one workgroup per compute
- * unit walks several tiles with one copy ring and two accumulator sets, and
- * writes each tile's C block during the next tile's first `c_slices`
- * slices (the prologue / steady loop / epilogue overlap of the "流水化 GPU
- * 内核" skill, Step 3, applied to the C write).  Whole tiles only: M, N, K
- * multiples of tile_m, tile_n, tile_k, K / tile_k >= c_slices + 2, operand
- * rows 16-byte aligned; gemm_plan_variant fails otherwise.  Only selected by
- * this value (never by AUTO with other fields). */
-#define TGEMM_KERNEL_PERSISTENT 3
 
 /* Global -> LDS loaders (the "流水化 GPU 内核" skill, Step 2: register-staged
  * vs asynchronous copy). */
@@ -168,11 +159,6 @@ typedef struct tgemm_variant {
     int32_t copy_sched; /* TGEMM_COPY_* (matrix-core direct loader; other kernels report BURST) */
     int32_t frag_read;  /* TGEMM_READ_* */
     int32_t lane_map;   /* TGEMM_LANES_* */
-    int32_t c_slices;   /* TGEMM_KERNEL_PERSISTENT: slices of the next tile over which a tile's C
-                           write is spread (4 or 8); other kernels report 0 */
-    int32_t workgroups; /* TGEMM_KERNEL_PERSISTENT: workgroups to launch (0: as many as the
-                           device's compute units hold at the kernel's occupancy, at most one
-                           per tile); each walks every workgroups-th tile.  Other kernels: 0 */
 } tgemm_variant;
 
 typedef struct tgemm_plan tgemm_plan;

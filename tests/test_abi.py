@@ -132,15 +132,12 @@ def test_variants_enumerate(dtype):
     vs = tl.variants(dtype)
     assert len(vs) >= 3
     kinds = {v.kernel for v in vs}
-    assert kinds == ({tl.KERNEL_NAIVE, tl.KERNEL_TILED} if dtype == tl.F32 else
-                     {tl.KERNEL_NAIVE, tl.KERNEL_TILED, tl.KERNEL_PERSISTENT})
+    assert kinds == {tl.KERNEL_NAIVE, tl.KERNEL_TILED}
     for v in vs:
-        # the persistent kernel takes whole tiles and at least c_slices + 2 slices
-        K = 512 if v.kernel != tl.KERNEL_PERSISTENT else v.tile_k * (v.c_slices + 2)
-        p = tl.Plan(512, 512, K, dtype, variant=v)
+        p = tl.Plan(512, 512, 512, dtype, variant=v)
         got = p.info().variant
         for f in ("kernel", "tile_m", "tile_n", "tile_k", "stages", "loader", "lds_layout", "access", "frag",
-                  "waves_m", "waves_n", "store", "c_slices"):
+                  "waves_m", "waves_n", "store"):
             assert getattr(got, f) == getattr(v, f)
 
 
@@ -308,8 +305,6 @@ def test_guard_follows_global_load_width_for_every_variant():
     # each checked against N, and need no guard)
     for dtype in (tl.F32, tl.BF16, tl.I8):
         for v in tl.variants(dtype):
-            if v.kernel == tl.KERNEL_PERSISTENT:
-                continue  # rejects ragged shapes (test_persistent_plan_checks)
             info = tl.Plan(129, 257, 40, dtype, variant=v).info()
             if info.variant.kernel != tl.KERNEL_TILED:
                 continue
@@ -374,35 +369,3 @@ def test_ladders_select_distinct_kernels():
         for r in rungs:
             if r.base is not None:
                 assert r.base in [x.label for x in rungs], r.label
-
-
-@pytest.mark.parametrize("dtype", [tl.BF16, tl.I8])
-def test_persistent_plan_checks(dtype):
-    vs = [v for v in tl.variants(dtype) if v.kernel == tl.KERNEL_PERSISTENT]
-    assert vs
-    for v in vs:
-        bk = v.tile_k
-        K = bk * (v.c_slices + 2)
-        info = tl.Plan(768, 1024, K, dtype, variant=v).info()
-        assert info.variant.kernel == tl.KERNEL_PERSISTENT and info.variant.c_slices == v.c_slices
-        assert "persist_c%d" % v.c_slices in info.name.decode()
-        # 24 tiles: one workgroup per tile (the device holds more), or as requested
-        assert info.grid == 24
-        w = tl.Variant(**dict(v.as_dict(), workgroups=5))
-        info = tl.Plan(768, 1024, K, dtype, variant=w).info()
-        assert info.grid == 5 and info.variant.workgroups == 5
-        assert tl.Plan(768, 1024, K, dtype, variant=w).clock_slots() >= tl.CLOCK_VALUES * 5
-        # whole tiles, enough slices, aligned rows; anything else is refused
-        for (M, N, KK, lda, ldb) in [(768 + 1, 1024, K, K, 1024), (768, 1024 + 16, K, K, 1024 + 16),
-                                     (768, 1024, K + 1, K + 1, 1024), (768, 1024, K - bk, K - bk, 1024),
-                                     (768, 1024, K, K + 1, 1024), (768, 1024, K, K, 1024 + 1)]:
-            with pytest.raises(tl.TgemmError):
-                tl.Plan(M, N, KK, dtype, lda, ldb, N, variant=v)
-        with pytest.raises(tl.TgemmError):
-            tl.Plan(768, 1024, K, dtype, variant=tl.Variant(**dict(v.as_dict(), workgroups=-1)))
-    # never by the AUTO kernel field, whatever the other fields say
-    with pytest.raises(tl.TgemmError):
-        tl.Plan(768, 1024, 4096, dtype, variant=tl.Variant(c_slices=4))
-    if dtype == tl.BF16:
-        auto = tl.Variant(tile_m=256, tile_n=128, tile_k=64, stages=2, loader=tl.LOADER_DIRECT)
-        assert "persist" not in tl.Plan(768, 1024, 4096, dtype, variant=auto).name

@@ -79,8 +79,6 @@ def _assert_parity(C, A, B, dtype):
 def _variants(dtype, tiled_only=False):
     out = []
     for v in tl.variants(DT[dtype]):
-        if v.kernel == tl.KERNEL_PERSISTENT:
-            continue  # whole tiles only: tests/test_persist_gpu.py
         if tiled_only and v.kernel != tl.KERNEL_TILED:
             continue
         out.append(v)

@@ -83,12 +83,6 @@ void register_bf16(void (*add)(const KernelEntry&)) {
     add(mfma_entry<T, 256, 256, 64, 2, 2, 2, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 1, 0, CST_SWAP, true>(1));
     add(mfma_entry<T, 256, 256, 32, 2, 4, 4, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2, 0, CST_MFMA, true>(1));
     add(mfma_entry<T, 256, 256, 64, 2, 4, 2, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2, 0, CST_MFMA, true>(1));
-    // persistent, the C write of each tile spread over 4 / 8 slices of
-    // the next (TGEMM_KERNEL_PERSISTENT)
-    add(persist_entry<T, 256, 128, 64, 4, 2, 4>(1));
-    add(persist_entry<T, 256, 128, 64, 4, 2, 8>(1));
-    add(persist_entry<T, 128, 256, 64, 2, 4, 4>(1));
-    add(persist_entry<T, 128, 256, 64, 2, 4, 8>(1));
 }
 
 }  // namespace tg

@@ -62,12 +62,6 @@ void register_i8(void (*add)(const KernelEntry&)) {
     add(mfma_entry<T, 256, 256, 64, 2, 2, 4, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 1, 0, CST_SWAP, true>(2));
     add(mfma_entry<T, 256, 256, 128, 2, 4, 2, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2, 0, CST_MFMA, true>(2));
     add(mfma_entry<T, 256, 256, 64, 2, 4, 4, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2, 0, CST_MFMA, true>(2));
-    // persistent, the C write of each tile spread over 4 / 8 slices of
-    // the next (TGEMM_KERNEL_PERSISTENT)
-    add(persist_entry<T, 256, 128, 128, 4, 2, 4>(2));
-    add(persist_entry<T, 256, 128, 128, 4, 2, 8>(2));
-    add(persist_entry<T, 128, 256, 128, 2, 4, 4>(2));
-    add(persist_entry<T, 128, 256, 128, 2, 4, 8>(2));
 }
 
 }  // namespace tg

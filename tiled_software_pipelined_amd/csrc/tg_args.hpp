@@ -32,9 +32,7 @@ constexpr int CLOCK_VALUES = 6;
 // Widest N the thin kernel (and the remainder of a split plan) takes.
 constexpr int THIN_N_MAX = 16;
 
-// FAM_PERSIST: the persistent matrix-core kernel (tg_persist.hpp); its grid is
-// one workgroup per compute unit, not one per tile
-enum Family { FAM_NAIVE = 1, FAM_TILED = 2, FAM_THIN = 3, FAM_PERSIST = 4 };
+enum Family { FAM_NAIVE = 1, FAM_TILED = 2, FAM_THIN = 3 };
 enum Loader { LD_VGPR = 1, LD_DIRECT = 2 };
 // LY_XOR_POISON: LY_XOR plus a debug fill of every LDS chunk with all-ones
 // bytes just before its direct copy is issued (see MfmaGemm::issue_direct_one)
@@ -64,9 +62,6 @@ struct KernelEntry {
     int copy_sched;  // TGEMM_COPY_BURST / TGEMM_COPY_SPREAD (direct loader; others report BURST)
     int frag_read;   // TGEMM_READ_*: how fragments come out of LDS
     int lane_map;    // TGEMM_LANES_*: outputs of a lane (fp32 kernels; others report BLOCKS)
-    int c_slices;    // persistent kernel: slices of the next tile a tile's C write is spread
-                     // over (0: the write follows the tile's own K loop)
-    int min_slices;  // persistent kernel: K / bk it needs at least (0: any)
     KernelFn fn;
     char name[96];
 };

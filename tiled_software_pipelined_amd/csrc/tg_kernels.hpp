@@ -5,7 +5,6 @@
 
 #include "tg_f32.hpp"
 #include "tg_mfma.hpp"
-#include "tg_persist.hpp"
 #include "tg_thin.hpp"
 
 namespace tg {
@@ -61,45 +60,6 @@ KernelEntry mfma_entry(int dtype) {
              CST == CST_SWAP ? "_vst" : "", SPREAD ? "_spread" : "",
              FREAD == RD_AUTO ? "" : FREAD == RD_B32 ? "_rd32" : FREAD == RD_B64 ? "_rd64" :
              FREAD == RD_B128 ? "_rd128" : "_rdtr");
-    return e;
-}
-
-// The persistent kernel with the overlapped C write (tg_persist.hpp): 2
-// slots, direct copies, XOR layout, 16-byte C stores; listed, but only a
-// request for TGEMM_KERNEL_PERSISTENT (or the planner) selects it.
-template <class Tr, int BM, int BN, int BK, int WM, int WN, int CSL>
-KernelEntry persist_entry(int dtype) {
-    typedef PersistGemm<Tr, BM, BN, BK, WM, WN, CSL> K;
-    KernelEntry e{};
-    e.dtype = dtype;
-    e.family = FAM_PERSIST;
-    e.bm = BM;
-    e.bn = BN;
-    e.bk = BK;
-    e.stages = 2;
-    e.loader = LD_DIRECT;
-    e.layout = LY_XOR;
-    e.access = AC_WIDE;
-    e.frag = FR_REUSE;
-    e.wm = WM;
-    e.wn = WN;
-    e.store = 1;  // TGEMM_STORE_VECTOR
-    e.copy_sched = 1;
-    e.lane_map = 1;
-    e.frag_read = K::FREAD;
-    e.c_slices = CSL;
-    e.min_slices = K::MIN_SLICES;
-    e.gload_bytes = 16;
-    e.threads = K::NT;
-    e.lds_bytes = K::LDS_BYTES;
-    e.loads_per_stage = K::N_LD;
-    e.shift_mask = 0;
-    e.listed = 1;
-    e.tail_ok = 0;
-    e.waves_per_simd = 2;
-    e.fn = gemm_kernel<K, 2>;
-    snprintf(e.name, sizeof e.name, "%s_t%dx%dx%d_w%dx%d_s2_direct_xor_wide_reuse_vst_persist_c%d",
-             dtype_tag(dtype), BM, BN, BK, WM, WN, CSL);
     return e;
 }
 

@@ -29,7 +29,6 @@ struct tgemm_plan {
     tgemm_plan* packed;           // default plans: the same product on operands repacked with
                                   // 16-byte aligned rows (gemm_run_ws), else NULL
     int64_t lda_p, ldb_p;         // leading dimensions of `packed`
-    int32_t workgroups;           // persistent kernel: requested grid (0: fill the device)
     tgemm_plan* rem_compact;      // packed split plans: the thin remainder reading B's last
                                   // N - n_main columns from a contiguous K x r copy (ldb = r)
 };
@@ -95,9 +94,6 @@ bool field_ok(int want, int have) { return want == 0 || want == have; }
 bool matches(const KernelEntry& e, const tgemm_variant& v) {
     if (v.kernel == TGEMM_KERNEL_NAIVE && e.family != tg::FAM_NAIVE) return false;
     if (v.kernel == TGEMM_KERNEL_TILED && e.family != tg::FAM_TILED) return false;
-    // the persistent kernel only by name
-    if ((v.kernel == TGEMM_KERNEL_PERSISTENT) != (e.family == tg::FAM_PERSIST)) return false;
-    if (!field_ok(v.c_slices, e.c_slices)) return false;
     return field_ok(v.tile_m, e.bm) && field_ok(v.tile_n, e.bn) && field_ok(v.tile_k, e.bk) &&
            field_ok(v.stages, e.stages) && field_ok(v.loader, e.loader) &&
            field_ok(v.lds_layout, e.layout) && field_ok(v.access, e.access) && field_ok(v.frag, e.frag) &&
@@ -288,42 +284,6 @@ void entry_to_variant(const KernelEntry& e, int32_t wg_group, tgemm_variant* v) 
     v->copy_sched = e.copy_sched;
     v->frag_read = e.frag_read;
     v->lane_map = e.lane_map;
-    v->c_slices = e.c_slices;
-    if (e.family == tg::FAM_PERSIST) v->kernel = TGEMM_KERNEL_PERSISTENT;
-}
-
-// Shape and leading-dimension conditions of the persistent kernel (whole
-// tiles, enough slices per tile, 16-byte aligned operand rows); NULL when
-// they hold, else what fails.
-const char* persist_unfit(const KernelEntry& e, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb) {
-    if (e.family != tg::FAM_PERSIST) return nullptr;
-    if (M % e.bm || N % e.bn || K % e.bk) return "M, N and K must be multiples of the tile";
-    if (K / e.bk < e.min_slices) return "K / tile_k is below the kernel's minimum (c_slices + 2)";
-    const int esz = elem_size(e.dtype);
-    if ((lda * esz) % 16 || (ldb * esz) % 16) return "operand rows must be 16-byte aligned";
-    return nullptr;
-}
-
-// Workgroups of a persistent kernel on the current device: as many as fit
-// at the kernel's occupancy on every compute unit (256 on MI355X, the value
-// used when no device answers), never more than there are tiles.
-int64_t persist_grid(const KernelEntry& e, int64_t tiles, int32_t requested) {
-    if (requested > 0) return tiles < requested ? tiles : requested;
-    static int cus[64];
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
-        if (!cus[dev] && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-            n > 0)
-            cus[dev] = n;
-        n = cus[dev];
-    }
-    if (n <= 0) {
-        (void)hipGetLastError();
-        n = 256;
-    }
-    const int64_t per_cu = (int64_t)4 * e.waves_per_simd / (e.threads / 64);
-    const int64_t g = n * (per_cu > 0 ? per_cu : 1);
-    return tiles < g ? tiles : g;
 }
 
 // Per-device gfx950 check, cached.
@@ -409,16 +369,11 @@ tgemm_plan* make_plan(int64_t M, int64_t N, int64_t K, int32_t dtype, int64_t ld
         set_err("wg_group must be -1, 0 or positive");
         return nullptr;
     }
-    if (v.workgroups < 0) {
-        set_err("workgroups must be 0 or positive");
-        return nullptr;
-    }
     const KernelEntry* e = nullptr;
     bool default_plan = false;
     if (v.kernel == TGEMM_KERNEL_AUTO && v.tile_m == 0 && v.tile_n == 0 && v.tile_k == 0 && v.stages == 0 &&
         v.loader == 0 && v.lds_layout == 0 && v.access == 0 && v.frag == 0 && v.waves_m == 0 &&
-        v.waves_n == 0 && v.store == 0 && v.copy_sched == 0 && v.frag_read == 0 && v.lane_map == 0 &&
-        v.c_slices == 0 && v.workgroups == 0) {
+        v.waves_n == 0 && v.store == 0 && v.copy_sched == 0 && v.frag_read == 0 && v.lane_map == 0) {
         e = default_entry(dtype, M, N, K, false);
         default_plan = true;
     } else {
@@ -426,11 +381,6 @@ tgemm_plan* make_plan(int64_t M, int64_t N, int64_t K, int32_t dtype, int64_t ld
     }
     if (!e) {
         set_err("no compiled variant matches the request (see gemm_variant_get)");
-        return nullptr;
-    }
-    if (const char* why = persist_unfit(*e, M, N, K, lda, ldb)) {
-        set_err("%s: %s (M=%lld N=%lld K=%lld lda=%lld ldb=%lld)", e->name, why, (long long)M, (long long)N,
-                (long long)K, (long long)lda, (long long)ldb);
         return nullptr;
     }
     if (!direct_fits(*e, lda, ldb)) {
@@ -498,7 +448,6 @@ tgemm_plan* make_plan(int64_t M, int64_t N, int64_t K, int32_t dtype, int64_t ld
     p->rem_compact = nullptr;
     p->lda_p = lda;
     p->ldb_p = ldb;
-    p->workgroups = e->family == tg::FAM_PERSIST ? v.workgroups : 0;
     if (is_default) *is_default = default_plan;
     g_err.clear();
     return p;
@@ -684,11 +633,9 @@ int run_impl(const tgemm_plan* p, const void* A, const void* B, void* C, uint64_
     g.a_guard = ga;
     g.b_guard = gb;
     g.c_stream = (uintptr_t)C % 128 == 0 && (p->ldc * 4) % 128 == 0;
-    const int64_t tiles = (int64_t)g.tiles_m * g.tiles_n;
-    const int64_t grid = e->family == tg::FAM_PERSIST ? persist_grid(*e, tiles, p->workgroups) : tiles;
-    if (clocks && (e->family == tg::FAM_TILED || e->family == tg::FAM_PERSIST)) {
+    if (clocks && e->family == tg::FAM_TILED) {
         // the kernel that runs decides the count (a fallback's tile may differ)
-        const int64_t need = tg::CLOCK_VALUES * grid;
+        const int64_t need = tg::CLOCK_VALUES * (int64_t)g.tiles_m * g.tiles_n;
         if (need > clocks_len) {
             set_err("clock buffer holds %lld values, %s needs %lld", (long long)clocks_len, e->name,
                     (long long)need);
@@ -698,7 +645,7 @@ int run_impl(const tgemm_plan* p, const void* A, const void* B, void* C, uint64_
     }
     void* args[] = {&g};
     const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(e->fn),
-                                           dim3((unsigned)grid), dim3(e->threads), args, 0, s);
+                                           dim3((unsigned)(g.tiles_m * g.tiles_n)), dim3(e->threads), args, 0, s);
     if (err != hipSuccess) {
         set_err("launch of %s failed: %s", e->name, hipGetErrorString(err));
         return TGEMM_E_HIP;
@@ -723,7 +670,7 @@ int64_t gemm_clock_slots(const tgemm_plan* p) {
     int64_t most = 0;
     for (int m = 0; m < 4; ++m) {
         const KernelEntry* e = m == 0 ? p->entry : p->fallback[m];
-        if (!e || (e->family != tg::FAM_TILED && e->family != tg::FAM_PERSIST)) continue;
+        if (!e || e->family != tg::FAM_TILED) continue;
         const int64_t n = tg::CLOCK_VALUES * ((p->M + e->bm - 1) / e->bm) * ((p->n_main + e->bn - 1) / e->bn);
         if (n > most) most = n;
     }
@@ -908,9 +855,7 @@ int gemm_plan_get_info(const tgemm_plan* p, tgemm_plan_info* info) {
     info->ldc = p->ldc;
     info->dtype = p->dtype;
     entry_to_variant(e, p->wg_group, &info->variant);
-    const int64_t tiles = ((p->M + e.bm - 1) / e.bm) * ((p->n_main + e.bn - 1) / e.bn);
-    info->grid = (int32_t)(e.family == tg::FAM_PERSIST ? persist_grid(e, tiles, p->workgroups) : tiles);
-    info->variant.workgroups = p->workgroups;
+    info->grid = (int32_t)(((p->M + e.bm - 1) / e.bm) * ((p->n_main + e.bn - 1) / e.bn));
     info->n_main = p->n_main;
     if (p->rem) snprintf(info->rem_name, sizeof info->rem_name, "%s", p->rem->entry->name);
     if (p->packed) snprintf(info->packed_name, sizeof info->packed_name, "%s", p->packed->entry->name);

@@ -24,7 +24,7 @@ ERRORS = {-1: "TGEMM_E_ARG", -2: "TGEMM_E_NULL", -3: "TGEMM_E_ALIGN", -4: "TGEMM
           -5: "TGEMM_E_VARIANT", -6: "TGEMM_E_HIP"}
 
 # variant field values (include/tgemm.h)
-KERNEL_AUTO, KERNEL_NAIVE, KERNEL_TILED, KERNEL_PERSISTENT = 0, 1, 2, 3
+KERNEL_AUTO, KERNEL_NAIVE, KERNEL_TILED = 0, 1, 2
 LOADER_VGPR, LOADER_DIRECT = 1, 2
 LDS_PLAIN, LDS_XOR, LDS_XOR_POISON = 1, 2, 3
 ACCESS_WIDE, ACCESS_NARROW = 1, 2
@@ -40,8 +40,7 @@ class Variant(ctypes.Structure):
     """Mirror of ``tgemm_variant``; zero fields mean "default"."""
     _fields_ = [(n, ctypes.c_int32) for n in (
         "kernel", "tile_m", "tile_n", "tile_k", "stages", "loader", "lds_layout", "access", "frag",
-        "wg_group", "waves_m", "waves_n", "store", "copy_sched", "frag_read", "lane_map", "c_slices",
-        "workgroups")]
+        "wg_group", "waves_m", "waves_n", "store", "copy_sched", "frag_read", "lane_map")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
