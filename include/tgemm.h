@@ -209,10 +209,14 @@ const char* tgemm_last_error(void);
  * then the plan's product runs on the copies with the direct global->LDS
  * loader.  Padding the misaligned operand is the pages' remedy besides a
  * guarded narrow loader (the "流水化 GPU 内核" skill's pitfall list; the SM80
- * ablation plan, section 1.4, note 2).  The result meets the same accuracy
- * as gemm_run's; it is the same bit for bit wherever both paths use
- * matrix-core or fp32 tiles (every such kernel accumulates each output in
- * increasing k), and may differ in the last bits on columns that one path
+ * ablation plan, section 1.4, note 2).  For a split plan (the last N mod
+ * tile <= 16 columns on the thin kernel) the repack of B and the thin
+ * product of those columns run as one launch (both memory-bound and
+ * independent; the thin part reads its columns of B in place), before the
+ * main part.  The result meets the same accuracy as gemm_run's; it is the
+ * same bit for bit wherever both paths use matrix-core or fp32 tiles (every
+ * such kernel accumulates each output in increasing k) or both use the thin
+ * kernel, and may differ in the last bits on columns that only one path
  * gives to the thin kernel.
  *
  * gemm_workspace_bytes returns the bytes this needs for these pointers: 0

@@ -160,3 +160,37 @@ def test_binding_uses_workspace_by_default():
     ok, rep = check(C1.cpu().numpy(), C_ref, S, "bf16", K)
     assert ok, rep
     assert np.isfinite(C1.cpu().numpy()).all()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "i8"])
+@pytest.mark.parametrize("r", [1, 2, 3, 5, 8, 13, 16])
+@pytest.mark.parametrize("a_off", [0, 1])
+def test_split_plan_repack_fused_with_thin_columns(dtype, r, a_off):
+    # 2048 x (2048 + r): 256 whole 128 x 128 tiles plus r columns for the
+    # thin kernel.  B's rows (ldb = N + 1) are never 16-byte aligned, so
+    # gemm_run_ws repacks B in one launch with the thin product of the last
+    # r columns (which reads those columns of B in place), then runs the
+    # main part; with a_off = 1 A is repacked first and the thin part reads
+    # the repacked A.  Same bits as gemm_run (the thin kernel's per-lane
+    # order of k does not depend on its rows per wave or sub-chunks), and
+    # the oracle's values (K = 264: a partial last slice).
+    M, N, K = 2048, 2048 + r, 264
+    A = inputs.operand(KIND[dtype], M, K, 300 + r)
+    B = inputs.operand(KIND[dtype], K, N, 400 + r)
+    lda, ldb = K + a_off, N + 1
+    Ad, Bd = _exact_view(A, lda, a_off), _exact_view(B, ldb, 0)
+    plan = tl.Plan(M, N, K, DT[dtype], lda, ldb, N)
+    info = plan.info()
+    print("split", dtype, r, a_off, info.name.decode(), info.rem_name.decode(), info.packed_name.decode(),
+          flush=True)
+    need = plan.workspace_bytes(Ad.data_ptr(), Bd.data_ptr())
+    buf, base = _workspace(need)
+    got = _run(plan, Ad, Bd, M, N, dtype, base, need)
+    ref = _run(plan, Ad, Bd, M, N, dtype)
+    C_ref, S = oracle.gemm(inputs.as_oracle_array(A), inputs.as_oracle_array(B), dtype)
+    ok, rep = check(got.numpy(), C_ref, S, dtype, K)
+    assert ok, rep
+    if dtype == "i8":
+        assert np.array_equal(got.numpy().astype(np.int64), C_ref)
+    assert torch.equal(got, ref), (dtype, r, a_off)
+    del buf

@@ -5,6 +5,7 @@
 
 #include "tg_f32.hpp"
 #include "tg_mfma.hpp"
+#include "tg_pack.hpp"
 #include "tg_thin.hpp"
 
 namespace tg {
@@ -95,6 +96,18 @@ KernelEntry naive_entry() {
     return e;
 }
 
+// The repack of B and the thin product of the remainder columns in one
+// launch: workgroups [0, thin_blocks) compute C's remainder columns (Thin),
+// the others repack.  The thin workgroups come first, so that their longer
+// streams of A start before the repack's many short workgroups.
+template <class Thin, int WAVES>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES, WAVES)))
+void pack_thin_kernel(PackArgs pk, GemmArgs g, int thin_blocks) {
+    static_assert(Thin::NT == 256, "one block size for both roles");
+    if ((int)blockIdx.x < thin_blocks) Thin::run_block(g, blockIdx.x);
+    else pack_chunks(pk, (int64_t)blockIdx.x - thin_blocks, (int64_t)gridDim.x - thin_blocks);
+}
+
 // The thin-N kernel (N <= NB <= THIN_N_MAX, bf16 / int8): unlisted, chosen
 // by the planner for thin products and for the narrow remainder of a split
 // plan (the smallest NB that covers N).
@@ -126,6 +139,14 @@ KernelEntry thin_entry() {
     e.frag_read = 3;  // A streamed in 16-byte pieces
     e.lane_map = 1;
     e.fn = gemm_kernel<K, K::WAVES>;
+    // fused with the repack of B, the thin kernel reads B's remainder
+    // columns in place, one element per row of B (the repack is writing the
+    // aligned copy meanwhile): four rows of C per wave (two where more would
+    // not fit in the registers), so that each workgroup's reads of those
+    // columns serve 16 (8) rows of C
+    typedef ThinGemm<DT, NB, (NB == 2 || NB >= 16) ? 2 : 4, NB == 1 ? 4 : NB <= 8 ? 2 : 1> F;
+    e.pack_thin = pack_thin_kernel<F, F::WAVES>;
+    e.pack_thin_bm = F::BM;
     snprintf(e.name, sizeof e.name, "%s_thin_n%d", dtype_tag(DT), NB);
     return e;
 }

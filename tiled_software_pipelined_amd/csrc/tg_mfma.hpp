@@ -664,22 +664,31 @@ struct MfmaGemm {
                                         wave);
     }
 
+    // Matrix-core K steps of the partial last slice (K - full BK > 0 values).
+    __device__ static __forceinline__ int tail_steps(const GemmArgs& g, int full) {
+        return (g.K - full * BK + Tr::MK - 1) / Tr::MK;
+    }
+
     // Multiply one slice held in `slot` into the accumulators.  With
     // fragment reuse the reads are software-pipelined one K step ahead
     // (register double buffer, "4.1 CUDA GEMM算子性能优化" section 9.2): the
     // fragments of step s+1 are requested before the matrix-core work of
     // step s, which hides the LDS latency behind it.  (The register-staged
     // loops and the K tail use this; the direct ring's steady state runs
-    // slice_direct, which also interleaves the copies.)
+    // slice_direct, which also interleaves the copies.)  `ksteps`: the K
+    // steps that hold data (the partial last slice of a K that is not a
+    // multiple of BK is zero past K: its remaining K steps would only add
+    // zero products, so they are skipped).
     __device__ static __forceinline__ void compute(const TG_LDS char* slot, Acc (&acc)[FM][FN],
-                                                   int wm0, int wn0, int lane) {
+                                                   int wm0, int wn0, int lane, int ksteps = KSUB) {
         const TG_LDS char* bslot = slot + A_BYTES;
         if constexpr (FRAG == FR_REUSE) {
             Frags f[2];
             read_frags(f[0], slot, 0, wm0, wn0, lane);
 #pragma unroll
             for (int s = 0; s < KSUB; ++s) {
-                if (s + 1 < KSUB) read_frags(f[(s + 1) & 1], slot, s + 1, wm0, wn0, lane);
+                if (s >= ksteps) break;
+                if (s + 1 < KSUB && s + 1 < ksteps) read_frags(f[(s + 1) & 1], slot, s + 1, wm0, wn0, lane);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
@@ -691,6 +700,7 @@ struct MfmaGemm {
         }
 #pragma unroll
         for (int s = 0; s < KSUB; ++s) {
+            if (s >= ksteps) break;
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -741,7 +751,7 @@ struct MfmaGemm {
                 load_regs(r, g, m0, n0, full * BK);
                 store_regs(smem, r);
                 wait_lds_then_barrier();
-                compute(smem, acc, wm0, wn0, lane);
+                compute(smem, acc, wm0, wn0, lane, tail_steps(g, full));
             }
         } else {
             if (full == 0) {
@@ -750,7 +760,7 @@ struct MfmaGemm {
                     load_regs(r, g, m0, n0, 0);
                     store_regs(smem, r);
                     wait_lds_then_barrier();
-                    compute(smem, acc, wm0, wn0, lane);
+                    compute(smem, acc, wm0, wn0, lane, tail_steps(g, full));
                 }
                 return;
             }
@@ -784,7 +794,7 @@ struct MfmaGemm {
                 wait_lds_then_barrier();
                 ++t;
             }
-            compute(smem + (t & 1) * SLOT, acc, wm0, wn0, lane);
+            compute(smem + (t & 1) * SLOT, acc, wm0, wn0, lane, full < tiles ? tail_steps(g, full) : KSUB);
         }
     }
 
@@ -909,7 +919,7 @@ struct MfmaGemm {
                     load_regs(r, g, m0, n0, full * BK);
                     store_regs(smem, r);
                     wait_lds_then_barrier();
-                    compute(smem, acc, wm0, wn0, lane);
+                    compute(smem, acc, wm0, wn0, lane, tail_steps(g, full));
                 }
             } else {
             // Prologue: slices 0 .. STAGES-2 in flight; once slice 0 is in
@@ -971,7 +981,7 @@ struct MfmaGemm {
                 load_regs(r, g, m0, n0, full * BK);
                 store_regs(smem + (full % STAGES) * SLOT, r);
                 wait_lds_then_barrier();
-                compute(smem + (full % STAGES) * SLOT, acc, wm0, wn0, lane);
+                compute(smem + (full % STAGES) * SLOT, acc, wm0, wn0, lane, tail_steps(g, full));
             }
             }
         } else {

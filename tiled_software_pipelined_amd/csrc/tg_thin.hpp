@@ -198,7 +198,10 @@ struct ThinGemm {
         }
     }
 
-    __device__ static __forceinline__ void run(const GemmArgs& g) {
+    __device__ static __forceinline__ void run(const GemmArgs& g) { run_block(g, blockIdx.x); }
+
+    // The rows of C of workgroup `block` (rows block * BM ..).
+    __device__ static __forceinline__ void run_block(const GemmArgs& g, int block) {
         __shared__ __attribute__((aligned(16))) T lds[2 * SLOT_ELEMS];
         TG_LDS T* slots = (TG_LDS T*)(lds);
         // B in 16-byte pieces when its rows allow it (b_guard == 0 means
@@ -207,13 +210,13 @@ struct ThinGemm {
         const bool a_wide = g.a_guard == 0;
         if constexpr (BV > 0) {
             if (g.b_guard == 0) {
-                if (a_wide) run_k<true, true>(g, slots);
-                else run_k<true, false>(g, slots);
+                if (a_wide) run_k<true, true>(g, slots, block);
+                else run_k<true, false>(g, slots, block);
                 return;
             }
         }
-        if (a_wide) run_k<false, true>(g, slots);
-        else run_k<false, false>(g, slots);
+        if (a_wide) run_k<false, true>(g, slots, block);
+        else run_k<false, false>(g, slots, block);
     }
 
     // The chunk's B block (zero past K and N) into `slot`.
@@ -241,11 +244,11 @@ struct ThinGemm {
     // section 9, one barrier per chunk.  Sub-chunks that start at or past K
     // hold only zeros and are not multiplied.
     template <bool BVEC, bool WIDE>
-    __device__ static __forceinline__ void run_k(const GemmArgs& g, TG_LDS T* slots) {
+    __device__ static __forceinline__ void run_k(const GemmArgs& g, TG_LDS T* slots, int block) {
         typedef typename std::conditional<BVEC, i32x4[BVPT], T[BPT]>::type BRegs;
         const T* A = static_cast<const T*>(g.A);
         const int lane = lane_id(), wave = wave_id();
-        const int r0 = blockIdx.x * BM + wave * ROWS;
+        const int r0 = block * BM + wave * ROWS;
         const T* rowp[ROWS];
 #pragma unroll
         for (int i = 0; i < ROWS; ++i) rowp[i] = A + (int64_t)min(r0 + i, g.M - 1) * g.lda;

@@ -29,8 +29,6 @@ struct tgemm_plan {
     tgemm_plan* packed;           // default plans: the same product on operands repacked with
                                   // 16-byte aligned rows (gemm_run_ws), else NULL
     int64_t lda_p, ldb_p;         // leading dimensions of `packed`
-    tgemm_plan* rem_compact;      // packed split plans: the thin remainder reading B's last
-                                  // N - n_main columns from a contiguous K x r copy (ldb = r)
 };
 
 namespace {
@@ -445,7 +443,6 @@ tgemm_plan* make_plan(int64_t M, int64_t N, int64_t K, int32_t dtype, int64_t ld
     p->n_main = N;
     p->rem = nullptr;
     p->packed = nullptr;
-    p->rem_compact = nullptr;
     p->lda_p = lda;
     p->ldb_p = ldb;
     if (is_default) *is_default = default_plan;
@@ -530,19 +527,6 @@ tgemm_plan* gemm_plan_variant(int64_t M, int64_t N, int64_t K, int32_t dtype, in
     p->packed = q;
     p->lda_p = lda_p;
     p->ldb_p = ldb_p;
-    if (q->rem) {
-        // the repack also writes the remainder's columns of B as a
-        // contiguous K x r block: the thin kernel then reads B as a dense
-        // vector instead of one cache line per element (4095 x 1 x 4104 bf16:
-        // 11.9 against 13.9 us)
-        const int64_t r = N - q->n_main;
-        tgemm_plan* c = make_plan(M, r, K, dtype, lda_p, r, ldc, nullptr, nullptr);
-        if (c && c->entry == q->rem->entry) {
-            p->rem_compact = c;
-        } else {
-            gemm_destroy(c);
-        }
-    }
     g_err.clear();
     return p;
 }
@@ -556,7 +540,6 @@ void gemm_destroy(tgemm_plan* plan) {
     if (!plan) return;
     gemm_destroy(plan->rem);
     gemm_destroy(plan->packed);
-    gemm_destroy(plan->rem_compact);
     delete plan;
 }
 
@@ -708,7 +691,6 @@ static int64_t pack_need(const tgemm_plan* p, const void* A, const void* B, int*
     int64_t need = 0;
     if (ma) need += (p->M * p->lda_p * esz + 255) / 256 * 256;
     if (mb) need += (p->K * p->ldb_p * esz + 255) / 256 * 256;
-    if (mb && p->rem_compact) need += (p->K * p->rem_compact->N * esz + 255) / 256 * 256;
     *mask = (ma ? 1 : 0) | (mb ? 2 : 0);
     return need;
 }
@@ -743,7 +725,8 @@ int gemm_run_ws(const tgemm_plan* p, const void* A, const void* B, void* C, void
     const void* a = A;
     const void* b = B;
     if (mask & 1) {
-        const hipError_t err = tg::launch_pack(A, ws, p->M, p->K * esz, p->lda * esz, p->lda_p * esz, s);
+        const tg::PackArgs pa{static_cast<const char*>(A), ws, p->M, p->K * esz, p->lda * esz, p->lda_p * esz};
+        const hipError_t err = tg::launch_pack(pa, s);
         if (err != hipSuccess) {
             set_err("repack of A failed: %s", hipGetErrorString(err));
             return TGEMM_E_HIP;
@@ -751,27 +734,63 @@ int gemm_run_ws(const tgemm_plan* p, const void* A, const void* B, void* C, void
         a = ws;
         ws += (p->M * p->lda_p * esz + 255) / 256 * 256;
     }
-    char* compact = nullptr;
-    if (mask & 2) {
-        const int64_t packed_bytes = (p->K * p->ldb_p * esz + 255) / 256 * 256;
-        if (p->rem_compact) compact = ws + packed_bytes;
-        const int64_t r = p->rem_compact ? p->rem_compact->N : 0;
-        const hipError_t err = tg::launch_pack(B, ws, p->K, p->N * esz, p->ldb * esz, p->ldb_p * esz, s, compact,
-                                               (p->N - r) * esz, r * esz);
+    if (!(mask & 2)) return gemm_run(p->packed, a, b, C, stream);
+    const tg::PackArgs pb{static_cast<const char*>(B), ws, p->K, p->N * esz, p->ldb * esz, p->ldb_p * esz};
+    b = ws;
+    // the thin kernel with the fewest columns that cover the remainder
+    // (whatever the repacked plan's own remainder kernel is)
+    const KernelEntry* thin = nullptr;
+    if (p->packed->rem) {
+        const int64_t rcols = p->N - p->packed->n_main;
+        for (const KernelEntry& e : g_reg[p->dtype])
+            if (e.family == tg::FAM_THIN && e.pack_thin && e.bn >= rcols && (!thin || e.bn < thin->bn)) thin = &e;
+    }
+    if (!thin) {
+        const hipError_t err = tg::launch_pack(pb, s);
         if (err != hipSuccess) {
             set_err("repack of B failed: %s", hipGetErrorString(err));
             return TGEMM_E_HIP;
         }
-        b = ws;
+        return gemm_run(p->packed, a, b, C, stream);
     }
-    if (!compact) return gemm_run(p->packed, a, b, C, stream);
-    // the main part on the repacked operands, then the remainder's columns
-    // from the contiguous block, on the same stream
+    // A split plan: the repack of B and the thin product of the last
+    // N - n_main columns in one launch (both memory-bound, independent: the
+    // thin part reads those columns of B in place), then the main part on
+    // the repacked operands, on the same stream.
+    const KernelEntry& te = *thin;
+    const int64_t r = p->N - p->packed->n_main;
+    const int64_t lda_used = (mask & 1) ? p->lda_p : p->lda;
+    tg::GemmArgs g{};
+    g.A = a;
+    g.B = static_cast<const char*>(B) + p->packed->n_main * esz;
+    g.C = static_cast<char*>(C) + p->packed->n_main * 4;
+    g.M = (int32_t)p->M;
+    g.N = (int32_t)r;
+    g.K = (int32_t)p->K;
+    g.tiles_m = (int32_t)((p->M + te.pack_thin_bm - 1) / te.pack_thin_bm);
+    g.tiles_n = 1;
+    g.lda = lda_used;
+    g.ldb = p->ldb;
+    g.ldc = p->ldc;
+    int32_t ga = 0, gb = 0;
+    ld_guards(te, r, lda_used, p->ldb, &ga, &gb);
+    const int bytes = access_bytes(te);
+    g.a_guard = ga || (bytes && (uintptr_t)g.A % bytes);
+    g.b_guard = gb || (bytes && (uintptr_t)g.B % bytes);
+    const int64_t thin_blocks = g.tiles_m;
+    const int64_t blocks = thin_blocks + tg::pack_blocks(pb);
+    tg::PackArgs pk = pb;
+    int tb = (int)thin_blocks;
+    void* args[] = {&pk, &g, &tb};
+    const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(te.pack_thin), dim3((unsigned)blocks),
+                                           dim3(256), args, 0, s);
+    if (err != hipSuccess) {
+        set_err("launch of the repack of B with %s failed: %s", te.name, hipGetErrorString(err));
+        return TGEMM_E_HIP;
+    }
     tgemm_plan main_part = *p->packed;
     main_part.rem = nullptr;
-    const int rc2 = gemm_run(&main_part, a, b, C, stream);
-    if (rc2 != TGEMM_OK) return rc2;
-    return gemm_run(p->rem_compact, a, compact, static_cast<char*>(C) + p->packed->n_main * 4, stream);
+    return gemm_run(&main_part, a, b, C, stream);
 }
 
 }  // extern "C"
