@@ -244,8 +244,8 @@ def test_thin_products_use_the_thin_kernel():
         for N, ldb, width in [(1, 1, 1), (7, 7, 8), (16, 17, 16), (3, 64, 4)]:
             info = tl.Plan(4096, N, 4096, dtype, ldb=ldb).info()
             assert b"thin" in info.name and info.n_main == N, (dtype, N, ldb)
-            # rows per workgroup: 4 waves of 1 row (width <= 2), 2 rows (16), 4 rows
-            rows = 4 if width <= 2 else 8 if width == 16 else 16
+            # rows per workgroup: 4 waves of 1 row (width 1, 2 and 16), else 4 rows
+            rows = 4 if width <= 2 or width == 16 else 16
             assert info.variant.tile_n == width and info.variant.tile_m == rows and info.grid == 4096 // rows
         assert b"thin" not in tl.Plan(4096, 16, 4096, dtype, ldb=32).info().name
         assert b"thin" not in tl.Plan(4096, 17, 4096, dtype, ldb=17).info().name

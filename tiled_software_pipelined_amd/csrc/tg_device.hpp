@@ -129,6 +129,23 @@ __device__ __forceinline__ i32x4 funnel16(i32x4 x, i32x4 y, uint32_t sh) {
     return out;
 }
 
+// Guarded loads.  Written as `ok ? *p : 0`, the compiler turns the select
+// into a branch around the load (a load is costly enough to skip), and every
+// such branch ends with a wait for all of the wave's outstanding loads, so a
+// run of guarded loads becomes a chain of memory round trips.  load_or_zero
+// instead always loads once, from p or from a zero-filled device array,
+// which keeps every load of the run in flight together.  The array is never
+// written, and is not const, so that the compiler cannot fold its value
+// back into a select.
+static __device__ __attribute__((aligned(16))) int32_t g_zeros[4];
+
+template <class T>
+__device__ __forceinline__ T load_or_zero(const T* p, bool ok) {
+    static_assert(sizeof(T) <= sizeof(g_zeros), "at most 16 bytes");
+    const T* src = ok ? p : reinterpret_cast<const T*>(g_zeros);
+    return *src;
+}
+
 __device__ __forceinline__ int wave_id() {
     return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }

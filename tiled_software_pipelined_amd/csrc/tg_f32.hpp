@@ -132,13 +132,13 @@ struct F32Gemm {
                 const int p = q * NT + threadIdx.x;
                 const int kc = k0 + p % BK;
                 const float* rowp = A + (int64_t)min(m0 + p / BK, g.M - 1) * g.lda;
-                r.ae[q] = kc < g.K ? rowp[kc] : 0.0f;
+                r.ae[q] = load_or_zero(rowp + kc, kc < g.K);
             }
 #pragma unroll
             for (int q = 0; q < EB; ++q) {
                 const int p = q * NT + threadIdx.x;
                 const int gk = k0 + p / BN, nc = n0 + p % BN;
-                r.be[q] = (gk < g.K && nc < g.N) ? B[(int64_t)gk * g.ldb + nc] : 0.0f;
+                r.be[q] = load_or_zero(B + (int64_t)gk * g.ldb + nc, gk < g.K && nc < g.N);
             }
             return;
         }
@@ -151,7 +151,7 @@ struct F32Gemm {
                 r.a[q] = *reinterpret_cast<const f32x4*>(rowp + kc);
             } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) r.a[q][e] = kc + e < g.K ? rowp[kc + e] : 0.0f;
+                for (int e = 0; e < 4; ++e) r.a[q][e] = load_or_zero(rowp + kc + e, kc + e < g.K);
             }
         }
 #pragma unroll
@@ -164,7 +164,7 @@ struct F32Gemm {
             } else {
                 const float* rowp = B + (int64_t)min(gk, g.K - 1) * g.ldb;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) r.b[q][e] = (gk < g.K && nc + e < g.N) ? rowp[nc + e] : 0.0f;
+                for (int e = 0; e < 4; ++e) r.b[q][e] = load_or_zero(rowp + nc + e, gk < g.K && nc + e < g.N);
             }
         }
     }

@@ -144,7 +144,7 @@ KernelEntry thin_entry() {
     // aligned copy meanwhile): four rows of C per wave (two where more would
     // not fit in the registers), so that each workgroup's reads of those
     // columns serve 16 (8) rows of C
-    typedef ThinGemm<DT, NB, (NB == 2 || NB >= 16) ? 2 : 4, NB == 1 ? 4 : NB <= 8 ? 2 : 1> F;
+    typedef ThinGemm<DT, NB, NB == 2 ? 2 : NB >= 16 ? 1 : 4, NB == 1 ? 4 : NB <= 8 ? 2 : 1> F;
     e.pack_thin = pack_thin_kernel<F, F::WAVES>;
     e.pack_thin_bm = F::BM;
     snprintf(e.name, sizeof e.name, "%s_thin_n%d", dtype_tag(DT), NB);

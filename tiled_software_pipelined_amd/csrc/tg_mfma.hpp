@@ -180,13 +180,17 @@ struct MfmaGemm {
     // the mode of a first or last whole slice
     static constexpr int edge_mode(int m) { return m == LM_SHIFTED ? LM_SHIFTED_EDGE : m; }
     // Elements [start, start + CE) of one row, zero where index >= limit.
+    // The scheduling fence keeps the compiler from computing the addresses
+    // of every chunk's element loads up front (64-bit each, they would not
+    // fit in the registers); the loads of all chunks still overlap.
     __device__ static __forceinline__ i32x4 load_chunk_guarded(const T* rowp, int start, int limit) {
         union { i32x4 v; T e[CE]; } u;
 #pragma unroll
         for (int e = 0; e < CE; ++e) {
             const int idx = start + e;
-            u.e[e] = idx < limit ? rowp[idx] : T(0);
+            u.e[e] = load_or_zero(rowp + idx, idx < limit);
         }
+        __builtin_amdgcn_sched_barrier(0);
         return u.v;
     }
 
@@ -219,7 +223,7 @@ struct MfmaGemm {
         }
         union { i32x4 v; T e[CE]; } u;
 #pragma unroll
-        for (int e = 0; e < CE; ++e) u.e[e] = a + (e + 1) * ESZ <= end ? p[e] : T(0);
+        for (int e = 0; e < CE; ++e) u.e[e] = load_or_zero(p + e, a + (e + 1) * ESZ <= end);
         return u.v;
     }
 
@@ -339,7 +343,7 @@ struct MfmaGemm {
                 } else {
                     union { int32_t v; T e[EPD]; } u;
 #pragma unroll
-                    for (int e = 0; e < EPD; ++e) u.e[e] = kc + e < g.K ? rowp[kc + e] : T(0);
+                    for (int e = 0; e < EPD; ++e) u.e[e] = load_or_zero(rowp + kc + e, kc + e < g.K);
                     r.ad[q] = u.v;
                 }
             }
@@ -355,7 +359,7 @@ struct MfmaGemm {
                     union { int32_t v; T e[EPD]; } u;
                     const T* rowp = B + (int64_t)gk * g.ldb;
 #pragma unroll
-                    for (int e = 0; e < EPD; ++e) u.e[e] = (gk < g.K && nc + e < g.N) ? rowp[nc + e] : T(0);
+                    for (int e = 0; e < EPD; ++e) u.e[e] = load_or_zero(rowp + nc + e, gk < g.K && nc + e < g.N);
                     r.bd[q] = u.v;
                 }
             }

@@ -35,7 +35,8 @@ __device__ __forceinline__ void pack_chunks(const PackArgs& a, int64_t block, in
             } else {
                 union { i32x4 v; uint8_t b[16]; } u;
 #pragma unroll
-                for (int t = 0; t < 16; ++t) u.b[t] = p + t < end ? *reinterpret_cast<const uint8_t*>(p + t) : 0;
+                for (int t = 0; t < 16; ++t)
+                    u.b[t] = load_or_zero(reinterpret_cast<const uint8_t*>(p + t), p + t < end);
                 v = u.v;
             }
             if (off + 16 > a.row_bytes) {  // the row's last, partial chunk

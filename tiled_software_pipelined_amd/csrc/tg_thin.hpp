@@ -41,9 +41,9 @@ struct ThinGemm {
     // rows of C per wave: one for the narrowest products (more workgroups,
     // four waves per SIMD to keep A in flight; 4095 x 1 x 4104 bf16: 9.7 us
     // against 11.6 with 4 rows), fewer for 16 columns (registers)
-    static constexpr int ROWS = ROWS_ ? ROWS_ : (NB <= 2 ? 1 : NB >= 16 ? 2 : 4);
+    static constexpr int ROWS = ROWS_ ? ROWS_ : (NB <= 2 || NB >= 16 ? 1 : 4);
     // waves per SIMD the kernel is compiled for
-    static constexpr int WAVES = NB <= 2 ? 4 : 2;
+    static constexpr int WAVES = NB == 1 || (NB == 2 && DT == 1) ? 4 : 2;
     static constexpr int BM = ROWS * (NT / 64);  // rows per workgroup
     static constexpr int BN = NB;
     static constexpr int ESZ = sizeof(T);
@@ -97,10 +97,8 @@ struct ThinGemm {
             for (int i = 0; i < ROWS; ++i) {
                 union { AVec v; T e[KE]; } u;
 #pragma unroll
-                for (int e = 0; e < KE; ++e) {
-                    const T x = rowp[i][min(kv + e, K - 1)];  // always a valid address
-                    u.e[e] = kv + e < K ? x : T(0);
-                }
+                for (int e = 0; e < KE; ++e) u.e[e] = load_or_zero(rowp[i] + kv + e, kv + e < K);
+                __builtin_amdgcn_sched_barrier(0);  // one piece's addresses live at a time
                 av[i] = u.v;
             }
         }
@@ -114,8 +112,10 @@ struct ThinGemm {
         for (int q = 0; q < BPT; ++q) {
             const int idx = q * NT + threadIdx.x;
             const int k = kc0 + idx / NB, j = idx % NB;
-            const T x = B[(int64_t)min(k, g.K - 1) * g.ldb + min(j, g.N - 1)];
-            bv[q] = (k < g.K && j < g.N) ? x : T(0);
+            bv[q] = load_or_zero(B + (int64_t)k * g.ldb + j, k < g.K && j < g.N);
+            // at most 8 of these 64-bit addresses live at a time; the loads
+            // of all groups still overlap
+            if ((q & 7) == 7) __builtin_amdgcn_sched_barrier(0);
         }
     }
 
@@ -128,9 +128,8 @@ struct ThinGemm {
             for (int q = 0; q < BVPT; ++q) {
                 const int idx = q * NT + threadIdx.x;
                 const int k = kc0 + idx / BV, p = idx % BV;
-                const i32x4 x =
-                    *reinterpret_cast<const i32x4*>(B + (int64_t)min(k, g.K - 1) * g.ldb + p * (16 / ESZ));
-                bw[q] = k < g.K ? x : i32x4{0, 0, 0, 0};
+                bw[q] = load_or_zero(reinterpret_cast<const i32x4*>(B + (int64_t)k * g.ldb + p * (16 / ESZ)),
+                                     k < g.K);
             }
         }
     }
@@ -164,6 +163,37 @@ struct ThinGemm {
     __device__ static __forceinline__ void multiply(Acc (&acc)[ROWS][NB], const AVec (&av)[ROWS],
                                                     const TG_LDS T* slot, int v, int lane) {
         const TG_LDS T* mine = slot + (v * 64 + lane) * LANE_ELEMS;
+        if constexpr (NB * ESZ >= 16) {
+            // rows of the block in whole 16-byte pieces: one row (k) at a
+            // time, so that only NB values of B are live
+            constexpr int PR = NB * ESZ / 16;  // pieces per row
+#pragma unroll
+            for (int e = 0; e < KE; ++e) {
+                uint32_t w[4 * PR];
+#pragma unroll
+                for (int q = 0; q < PR; ++q) {
+                    const i32x4 x = reinterpret_cast<const TG_LDS i32x4*>(mine)[e * PR + q];
+                    w[4 * q] = x.x; w[4 * q + 1] = x.y; w[4 * q + 2] = x.z; w[4 * q + 3] = x.w;
+                }
+                Acc b[NB];
+#pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    const uint32_t word = w[j / (4 / ESZ)];
+                    if constexpr (DT == 1) b[j] = __uint_as_float((j & 1) ? (word & 0xffff0000u) : (word << 16));
+                    else b[j] = (int32_t)(word << (24 - 8 * (j & 3))) >> 24;
+                }
+#pragma unroll
+                for (int i = 0; i < ROWS; ++i) {
+                    const Acc a = elem(av[i], e);
+#pragma unroll
+                    for (int j = 0; j < NB; ++j) {
+                        if constexpr (DT == 1) acc[i][j] = __builtin_fmaf(a, b[j], acc[i][j]);
+                        else acc[i][j] += a * b[j];
+                    }
+                }
+            }
+            return;
+        }
         uint32_t w[BLK_WORDS];
         if constexpr (BLK_BYTES % 16 == 0) {
 #pragma unroll
