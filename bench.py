@@ -43,6 +43,12 @@ sys.path.insert(0, ROOT)
 # MI355X published dense peaks (TFLOP/s or TOP/s) and HBM bandwidth (GB/s)
 PEAK_TFLOPS = {"bf16": 2500.0, "i8": 5000.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
+# timed regions whose launches take less than this (ms each when launched one
+# by one from Python, about the host's own launch path) are re-timed as one
+# HIP-graph replay of the same steps.  Longer kernels stay eager: replaying
+# graph nodes costs a few microseconds per kernel (bf16 512x4096x4096: 31.0
+# us per launch replayed against 26.5 eager).
+GRAPH_BELOW_MS = 0.02
 METRIC = "GEMM TFLOPS (TOPS int8) and % of MI355X MFMA peak, bf16 M=N=K=4096"
 
 
@@ -102,6 +108,37 @@ def time_region(lib, torch, A, B, C, variant, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return e0.elapsed_time(e1) / steps, wall
+
+
+def time_region_graph(lib, torch, A, B, C, variant, steps):
+    """The timed region as one HIP-graph replay of `steps` launches, for
+    kernels shorter than the host's launch path (a few microseconds): the
+    same bracketing (synchronisation and a HIP event on each side) with no
+    host work between the launches.  Returns (mean ms per launch from the
+    events, wall seconds, whether the replay reproduced the eager C)."""
+    lib.gemm(A, B, out=C, variant=variant)
+    torch.cuda.synchronize()
+    eager = C.clone()
+    side = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for _ in range(steps):
+            lib.gemm(A, B, out=C, variant=variant)
+    graph.replay()  # warm
+    torch.cuda.synchronize()
+    C.zero_()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    same = bool(torch.equal(C, eager))
+    del graph
+    return e0.elapsed_time(e1) / steps, wall, same
 
 
 def time_graph(lib, torch, A, B, C, variant, per_graph=20, replays=10):
@@ -720,7 +757,12 @@ def main():
 
     variant = parse_variant(args.variant, lib)
     ceiling = None
-    if not args.calib_copy and not args.probe_last:
+    # bound by HBM rather than the arithmetic (the roofline's time for the
+    # algorithmic bytes exceeds that for the flops): the thin products
+    esz = {"f32": 4, "bf16": 2, "i8": 1}[w.dtype]
+    hbm_bytes = metrics.algorithmic_bytes(w.M, w.N, w.K, esz, 4)
+    hbm_bound = hbm_bytes / (PEAK_HBM_GBS * 1e9) > w.flops / (PEAK_TFLOPS[w.dtype] * 1e12)
+    if not args.calib_copy and not args.probe_last and not hbm_bound:
         # The rate the arithmetic units sustain on this machine for the
         # workload's operand distribution with no memory traffic at all (the
         # power budget lowers the clock below nominal for random operands;
@@ -732,6 +774,15 @@ def main():
         ceiling = mfma_ceiling(torch, lib, w.dtype, "random",
                                workgroups=256 if w.dtype != "f32" else F32_PROBE_WAVES[8])
     kernel_ms, wall = time_region(lib, torch, A, B, C, variant, args.steps, args.warmup)
+    timing_mode = "eager"
+    eager_ms = kernel_ms
+    if kernel_ms < GRAPH_BELOW_MS:
+        # launched one by one from here the GPU waits on the host between
+        # kernels: time the same steps as one graph replay instead
+        kernel_ms, wall, same = time_region_graph(lib, torch, A, B, C, variant, args.steps)
+        if not same:
+            raise RuntimeError("graph replay did not reproduce the eager result")
+        timing_mode = "hip_graph"
     # after the timed region, one pass with a pair of events around every
     # launch: the per-launch distribution (median, min, max) of that pass
     per, _ = time_plan(lib, torch, w, A, B, C, variant, args.steps, 0)
@@ -770,21 +821,30 @@ def main():
         "roofline": {"bound": "mfma" if w.dtype != "f32" else "alu", "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s" if w.dtype != "i8" else "TOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "algorithmic_bytes": hbm_bytes,
                      "traffic_unit": "bytes per launch between L2 and the memory fabric (FETCH_SIZE + "
                                      "WRITE_SIZE, copy-scaled): L2-miss bytes, which the 256 MB MALL may serve "
                                      "without reaching HBM",
                      "traffic_source": prof["path"] if prof else None,
                      "kernel_ms_mean": round(kernel_ms, 5),
+                     "timing_mode": timing_mode, "eager_kernel_ms_mean": round(eager_ms, 5),
                      "per_launch_ms": {"median": round(per_sorted[len(per_sorted) // 2], 5),
                                        "min": round(per_sorted[0], 5), "max": round(per_sorted[-1], 5),
                                        "launches": len(per_sorted)},
                      "timing": "kernel_ms_mean (used for achieved): HIP events on the launch stream at the two "
-                               "ends of the timed region / steps; per_launch_ms: one further pass of the same "
+                               "ends of the timed region / steps (timing_mode hip_graph: the steps replayed as one "
+                               "HIP graph, for launches shorter than the host's launch path; eager_kernel_ms_mean "
+                               "is the one-by-one figure); per_launch_ms: one further pass of the same "
                                "number of launches with a pair of events around each launch (the events add "
                                "their own commands between kernels, so these are slightly longer)"},
         "cpu_baseline": None,
         "env": env_record(torch, lib, dev),
     }
+    if hbm_bound:
+        # one read of A and B and one write of C per launch at the HBM peak
+        gbps = hbm_bytes / (kernel_ms * 1e-3) / 1e9
+        rec["roofline"].update({"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                "frac": round(gbps / PEAK_HBM_GBS, 4)})
     clk = clocked_rate(torch, lib, plan, A, B, C, variant)
     if clk is not None:
         at_clock = peak * clk["ghz"] / NOMINAL_GHZ
@@ -801,7 +861,7 @@ def main():
                       "end; wg_loop_us / wg_store_us: per-workgroup means of K loop and C write-back; "
                       "last_loop_end_us / last_end_us: from the first start to the last K-loop end / last "
                       "end" % (CLOCKED_LAUNCHES, NOMINAL_GHZ)}
-    if not args.calib_copy:
+    if not args.calib_copy and not hbm_bound:
         if ceiling is None:
             ceiling = mfma_ceiling(torch, lib, w.dtype, "random",
                                    workgroups=256 if w.dtype != "f32" else F32_PROBE_WAVES[8])
@@ -811,7 +871,7 @@ def main():
             "value": round(rate, 1), "clock_ghz": round(ghz, 3), "frac": round(achieved / rate, 4),
             "source": "%s rate probe, random %s operands, no memory traffic; run %s the warmup steps" % (
                 unit, w.dtype, "after the timed region" if args.probe_last else "before")}
-    if w.dtype == "bf16" and not args.calib_copy and not args.no_mix_probe:
+    if w.dtype == "bf16" and not args.calib_copy and not args.no_mix_probe and not hbm_bound:
         # the same matrix stream with the default kernel's on-chip data
         # movement and nothing else (no barrier, no C store): what the power
         # budget leaves once the LDS fragment reads and the direct copies are
