@@ -181,12 +181,19 @@ tgemm_plan* gemm_plan_variant(int64_t M, int64_t N, int64_t K, int32_t dtype,
 
 /* Enqueue C = A x B on `stream` (a hipStream_t; NULL = the null stream) on
  * the current HIP device.  A, B, C are device pointers (or any pointers the
- * device can access) aligned to their element size.  A pointer that is
- * element-aligned but not 16-byte aligned, or a leading dimension whose rows
- * are not 16-byte aligned, makes the run use a register-staged kernel that
- * reads that operand as shifted pairs of aligned 16-byte blocks (slower,
- * same results); so does a leading dimension too large for the direct
- * loader's 32-bit lane offsets (from the plan on).  Nothing outside
+ * device can access) aligned to their element size.  The matrix-core
+ * kernels with the direct global->LDS loader (every bf16 / int8 default for
+ * products wider than 16 columns) and the thin kernel read rows of any
+ * alignment in place: gfx950's 16-byte reads and copies take any byte
+ * address at the rate of aligned ones.  The others (fp32, register-staged
+ * tiles) run, for a pointer that is element-aligned but not 16-byte aligned
+ * or a leading dimension whose rows are not 16-byte aligned, a kernel that
+ * reads that operand in shifted or element pieces (slower, same results);
+ * so does a B whose N is not a whole number of 16-byte pieces, and a leading
+ * dimension too large for the direct loader's 32-bit lane offsets (from the
+ * plan on).  A default plan one column wider than 16 or more whole 256 x 256
+ * tile columns computes that column in the main kernel's K loop; a few more
+ * columns go to the thin kernel after the main launch.  Nothing outside
  * [A, A + ((M-1)*lda + K) elements) or the corresponding range of B is read.
  * C outside its M x N window is not written.  The launch is asynchronous:
  * execution errors surface at the stream's next synchronisation.  Returns
@@ -204,25 +211,25 @@ const char* tgemm_last_error(void);
  * 16-byte aligned (a leading dimension that is not a whole number of
  * 16-byte chunks, or a pointer that is not 16-byte aligned) are first copied
  * on `stream` into the workspace with 16-byte aligned rows (leading
- * dimension rounded up to 8 bf16, 16 int8 or 4 fp32 elements; each copy
- * starts on a 256-byte boundary; the padding columns are written as zero),
- * then the plan's product runs on the copies with the direct global->LDS
- * loader.  Padding the misaligned operand is the pages' remedy besides a
- * guarded narrow loader (the "流水化 GPU 内核" skill's pitfall list; the SM80
- * ablation plan, section 1.4, note 2).  For a split plan (the last N mod
- * tile <= 16 columns on the thin kernel) the repack of B and the thin
- * product of those columns run as one launch (both memory-bound and
- * independent; the thin part reads its columns of B in place), before the
- * main part.  The result meets the same accuracy as gemm_run's; it is the
- * same bit for bit wherever both paths use matrix-core or fp32 tiles (every
- * such kernel accumulates each output in increasing k) or both use the thin
- * kernel, and may differ in the last bits on columns that only one path
- * gives to the thin kernel.
+ * dimension rounded up to whole 128-byte lines; each copy starts on a
+ * 256-byte boundary; the padding columns are written as zero), then the
+ * plan's product runs on the copies.  Only plans whose kernel reads such
+ * rows slowly carry the repack (fp32 plans, and matrix-core plans that fall
+ * back to a register-staged kernel); the direct-loader and thin kernels
+ * read any alignment in place, and their plans ask for no workspace.
+ * Padding the misaligned operand is the pages' remedy besides a guarded
+ * narrow loader (the "流水化 GPU 内核" skill's pitfall list; the SM80
+ * ablation plan, section 1.4, note 2).  The result meets the same accuracy
+ * as gemm_run's; it is the same bit for bit wherever both paths use
+ * matrix-core or fp32 tiles (every such kernel accumulates each output in
+ * increasing k) or both use the thin kernel, and may differ in the last bits
+ * on columns that only one path gives to the thin kernel.
  *
  * gemm_workspace_bytes returns the bytes this needs for these pointers: 0
  * when no operand is misaligned, for K, M or N = 0, and for plans that carry
  * no repack (explicit variants, products with N <= 16, which read their
- * operands about once anyway).  gemm_run_ws behaves exactly like gemm_run
+ * operands about once anyway, and plans on kernels that read any
+ * alignment).  gemm_run_ws behaves exactly like gemm_run
  * when that is 0, when `workspace` is NULL or when `workspace_bytes` is
  * smaller.  The workspace must be 256-byte aligned (TGEMM_E_ALIGN otherwise),
  * must not overlap A, B or C, and must stay allocated until the stream has
@@ -257,13 +264,16 @@ typedef struct tgemm_plan_info {
     int32_t threads;         /* threads per workgroup */
     int32_t lds_bytes;       /* LDS per workgroup */
     int32_t loads_per_stage; /* global->LDS instructions per wave per stage */
-    int32_t a_guarded;       /* A rows are not 16-byte aligned: a register-staged kernel with
-                                shifted loads reads A (pointer alignment is checked per run) */
-    int32_t b_guarded;       /* the same for B (also when N is not a whole number of 16-byte chunks) */
+    int32_t a_guarded;       /* A rows are not 16-byte aligned and the kernel needs them aligned: a
+                                kernel with shifted loads reads A (pointers are checked per run);
+                                0 for kernels that read any alignment */
+    int32_t b_guarded;       /* the same for B, and whenever N is not a whole number of 16-byte
+                                pieces (the last piece of a B row would cross N) */
     char name[96];           /* kernel name, e.g. "bf16_t256x256x64_w2x4_s2_direct_xor_wide_reuse" */
     int64_t n_main;          /* columns the kernel above covers: N, or for a split plan the first
-                                N - r, the last r (<= 16) going to the thin kernel `rem_name` */
-    char rem_name[96];       /* split plans: the kernel of the last columns; else "" */
+                                N - r, the last r (<= 16) going to `rem_name` */
+    char rem_name[96];       /* split plans: the kernel of the last columns ("<name>_remcol": the
+                                last column in the main kernel's own K loop); else "" */
     char packed_name[96];    /* the kernel gemm_run_ws runs on repacked operands (its plan's
                                 `name`); "" for plans that carry no repack */
     int32_t waves_per_simd;  /* occupancy the kernel is compiled for: its registers (VGPRs + AGPRs,

@@ -191,23 +191,31 @@ def test_default_choice_by_shape():
     assert (f.variant.tile_m, f.variant.tile_k, f.grid) == (128, 16, 1024)
 
 
-def test_unaligned_leading_dimension_uses_guarded_register_loader():
-    # ragged workload: B rows of 4097 bf16 = 8194 bytes are not 16-byte aligned
-    info = tl.Plan(4095, 4097, 4104, tl.BF16).info()
-    assert info.b_guarded == 1 and info.a_guarded == 0
-    assert info.variant.loader == tl.LOADER_VGPR
-    # split: the first 4096 columns on 256 x 256 tiles (one round of 256
-    # workgroups; 4097 columns would need 272 of them, or 1056 of 128 x 128),
-    # the last column on the thin kernel
-    assert (info.variant.tile_m, info.variant.tile_n) == (256, 256)
-    assert info.grid == 16 * 16 and info.n_main == 4096
-    assert b"thin" in info.rem_name
-    # a small unaligned problem keeps a small register-staged tile
+def test_unaligned_rows_are_read_in_place():
+    # ragged workload: B rows of 4097 bf16 = 8194 bytes are not 16-byte
+    # aligned.  The direct loader's copies read 16 bytes from any byte
+    # address, so the plan keeps the direct-loader kernel, unguarded.
+    for dtype in (tl.BF16, tl.I8):
+        info = tl.Plan(4095, 4097, 4104, dtype).info()
+        assert info.b_guarded == 0 and info.a_guarded == 0
+        assert info.variant.loader == tl.LOADER_DIRECT
+        # split: the first 4096 columns on 256 x 256 tiles (one round of 256
+        # workgroups; 4097 columns would need 272 of them, or 1056 of
+        # 128 x 128), the last column in the same K loop (the kernel's twin)
+        assert (info.variant.tile_m, info.variant.tile_n) == (256, 256)
+        assert info.grid == 16 * 16 and info.n_main == 4096
+        assert info.rem_name == info.name + b"_remcol"
+    # rows and pointers of any alignment with whole 16-byte pieces per row
+    info = tl.Plan(4096, 4096, 4096, tl.BF16, lda=4097, ldb=4097).info()
+    assert info.variant.loader == tl.LOADER_DIRECT and info.a_guarded == 0 and info.b_guarded == 0
+    # N not a whole number of 16-byte pieces (the last piece of a B row
+    # would cross N): a small problem keeps a small register-staged tile
     for dtype in (tl.BF16, tl.I8):
         v = tl.Plan(150, 131, 101, dtype).info().variant
         assert v.loader == tl.LOADER_VGPR and (v.tile_m, v.tile_n) == (128, 128), dtype
-    # an explicit direct-loader request falls back to the register-staged
-    # kernel with the same tile and wave grid
+    # an explicit direct-loader request on N = 4097 (no split for explicit
+    # variants) falls back to the register-staged kernel with the same tile
+    # and wave grid
     req = tl.Variant(kernel=tl.KERNEL_TILED, tile_m=256, tile_n=256, tile_k=64, waves_n=4,
                      loader=tl.LOADER_DIRECT)
     v = tl.Plan(4095, 4097, 4104, tl.BF16, variant=req).info().variant
@@ -221,33 +229,41 @@ def test_default_tile_follows_the_round_model():
     for (M, N, want) in [(4096, 4096, 256), (5120, 5120, 256), (3072, 3072, 256), (4096, 4352, 128),
                          (4096, 4608, 128)]:
         assert tl.Plan(M, N, 4096, tl.BF16).info().variant.tile_m == want, (M, N)
-    # unaligned B: 4096^2 keeps the 256 x 256 register-staged kernel
+    # unaligned B rows: 4096^2 keeps the 256 x 256 direct-loader kernel
     big = tl.Plan(4096, 4096, 4096, tl.BF16, ldb=4097).info()
-    assert big.b_guarded == 1 and big.variant.tile_m == 256 and big.variant.loader == tl.LOADER_VGPR
+    assert big.b_guarded == 0 and big.variant.tile_m == 256 and big.variant.loader == tl.LOADER_DIRECT
     # 4096 x 4097 splits off its last column (272 big tiles or 1056 small
-    # ones would need a second round); with a padded, aligned ldb the main
-    # part is the direct-loader kernel
-    info = tl.Plan(4096, 4097, 4096, tl.BF16).info()
-    assert info.b_guarded == 1 and info.variant.tile_m == 256 and info.n_main == 4096
-    info = tl.Plan(4096, 4097, 4096, tl.BF16, ldb=4104).info()
-    assert info.n_main == 4096 and info.variant.loader == tl.LOADER_DIRECT and b"thin" in info.rem_name
+    # ones would need a second round) into the main kernel's K loop, with B
+    # rows aligned or not
+    for ldb in (4097, 4104):
+        info = tl.Plan(4096, 4097, 4096, tl.BF16, ldb=ldb).info()
+        assert info.b_guarded == 0 and info.variant.tile_m == 256 and info.n_main == 4096
+        assert info.variant.loader == tl.LOADER_DIRECT and info.rem_name.endswith(b"_remcol")
+    # three last columns: the thin kernel after the main part
+    info = tl.Plan(4096, 4099, 4096, tl.BF16).info()
+    assert info.n_main == 4096 and b"thin" in info.rem_name
+    # fewer than 16 tile columns (a tile's rows would not all have a
+    # workgroup for the last column): the thin kernel
+    info = tl.Plan(8192, 2049, 4096, tl.BF16).info()
+    assert info.n_main == 2048 and b"thin" in info.rem_name, info.rem_name
     # 4096 x 4352 leaves no thin remainder: no split
     info = tl.Plan(4096, 4352, 4096, tl.BF16).info()
     assert info.n_main == 4352 and info.rem_name == b""
 
 
 def test_thin_products_use_the_thin_kernel():
-    # N <= 16 with rows the direct loader cannot read (N not a whole number of
-    # 16-byte pieces, or an unaligned ldb): the thin kernel of the smallest
-    # width that covers N; with aligned rows the direct-loader tile
+    # N <= 16 where the direct loader cannot read B (N not a whole number of
+    # 16-byte pieces): the thin kernel of the smallest width that covers N;
+    # otherwise the direct-loader tile, whatever the rows' alignment
     for dtype in (tl.BF16, tl.I8):
-        for N, ldb, width in [(1, 1, 1), (7, 7, 8), (16, 17, 16), (3, 64, 4)]:
+        for N, ldb, width in [(1, 1, 1), (7, 7, 8), (3, 64, 4), (9, 9, 16)]:
             info = tl.Plan(4096, N, 4096, dtype, ldb=ldb).info()
             assert b"thin" in info.name and info.n_main == N, (dtype, N, ldb)
             # rows per workgroup: 4 waves of 1 row (width 1, 2 and 16), else 4 rows
             rows = 4 if width <= 2 or width == 16 else 16
             assert info.variant.tile_n == width and info.variant.tile_m == rows and info.grid == 4096 // rows
         assert b"thin" not in tl.Plan(4096, 16, 4096, dtype, ldb=32).info().name
+        assert b"thin" not in tl.Plan(4096, 16, 4096, dtype, ldb=17).info().name
         assert b"thin" not in tl.Plan(4096, 17, 4096, dtype, ldb=17).info().name
     # fp32 keeps its one-fma-chain-per-output kernel
     assert b"thin" not in tl.Plan(4096, 4, 4096, tl.F32).info().name
@@ -324,7 +340,14 @@ def test_workspace_bytes(dtype, esz):
     al = 1 << 20
     M, N, K = 4095, 4097, 4104
     p = tl.Plan(M, N, K, dtype, K, N, N)
-    # repacked rows are rounded up to whole 128-byte lines
+    if dtype != tl.F32:
+        # the matrix-core plans read rows and pointers of any alignment in
+        # place: nothing to repack
+        for a, b in ((al, al), (al + esz, al), (al, al + esz), (al + 1, al + 3)):
+            assert p.workspace_bytes(a, b) == 0
+        assert tl.Plan(1024, 1024, 512, dtype).workspace_bytes(al, al + esz) == 0
+        return
+    # fp32: repacked rows are rounded up to whole 128-byte lines
     bytes_a = _ru(M * _ru(K * esz, 128), 256)
     bytes_b = _ru(K * _ru(N * esz, 128), 256)
     a_al = (K * esz) % 16 == 0

@@ -38,8 +38,10 @@ def test_default_large_tiles_fill_a_compute_unit_alone():
 
 
 def test_packed_form_of_a_misaligned_plan():
-    # ldb = 4097: gemm_run runs the register-staged kernel, gemm_run_ws the
-    # direct one on the repacked operand; both are 256 x 256 tiles
-    p = tl.Plan(4095, 4097, 4104, tl.BF16)
+    # fp32 with ldb = 4097: gemm_run runs the guarded kernel, gemm_run_ws the
+    # same tile on the repacked operand; bf16 reads the rows in place and has
+    # no repacked form
+    p = tl.Plan(4095, 4097, 4104, tl.F32)
     assert p.info().packed_name
-    assert p.occupancy(packed=False) == 1 and p.occupancy(packed=True) == 1
+    assert p.occupancy(packed=False) >= 1 and p.occupancy(packed=True) >= 1
+    assert tl.Plan(4095, 4097, 4104, tl.BF16).info().packed_name == b""

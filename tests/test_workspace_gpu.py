@@ -1,5 +1,8 @@
 """GPU: gemm_run_ws repacks operands whose rows are not 16-byte aligned into
-the caller's workspace and gives the same product as gemm_run.
+the caller's workspace where the plan's kernel needs aligned rows (the fp32
+kernels, and matrix-core plans whose B rows end in a partial 16-byte piece),
+and gives the same product as gemm_run.  Plans whose kernels read rows of any
+alignment (the direct-copy tiles, the thin kernel) need no workspace.
 
 int8 and fp32 must agree bit for bit with gemm_run (exact / one fma chain
 per output in increasing k on every kernel); bf16 too on shapes whose plans
@@ -71,6 +74,7 @@ CASES = [  # M, N, K, lda - K, ldb - N, A offset, B offset (elements)
     (257, 208, 331, 0, 3, 0, 1),
     (130, 1000, 96, 2, 0, 1, 0),
     (512, 264, 517, 5, 7, 3, 5),
+    (260, 333, 150, 2, 1, 1, 3),
 ]
 
 
@@ -84,8 +88,10 @@ def test_workspace_matches_run_and_oracle(dtype, case):
     Ad, Bd = _exact_view(A, lda, oa), _exact_view(B, ldb, ob)
     plan = tl.Plan(M, N, K, DT[dtype], lda, ldb, N)
     need = plan.workspace_bytes(Ad.data_ptr(), Bd.data_ptr())
-    assert need > 0
-    print("workspace", dtype, case, need, flush=True)
+    # fp32 kernels need aligned rows; the matrix-core plans only where N is
+    # not a whole number of 16-byte pieces (their fallback kernels)
+    assert (need > 0) == (dtype == "f32" or N % CE[dtype] != 0), (need, plan.info().name)
+    print("workspace", dtype, case, need, plan.info().name.decode(), flush=True)
     ref = _run(plan, Ad, Bd, M, N, dtype)
     buf, base = _workspace(need)
     got = _run(plan, Ad, Bd, M, N, dtype, base, need)
@@ -93,9 +99,10 @@ def test_workspace_matches_run_and_oracle(dtype, case):
     ok, rep = check(got.numpy(), C_ref, S, dtype, K)
     assert ok, rep
     assert torch.equal(got, ref), (dtype, case)
-    # too small: gemm_run's kernels, same result
-    small = _run(plan, Ad, Bd, M, N, dtype, base, need - 1)
-    assert torch.equal(small, ref)
+    if need:
+        # too small: gemm_run's kernels, same result
+        small = _run(plan, Ad, Bd, M, N, dtype, base, need - 1)
+        assert torch.equal(small, ref)
     del buf
 
 
@@ -103,7 +110,7 @@ def test_workspace_matches_run_and_oracle(dtype, case):
 def test_workspace_reused_in_order_and_ldc(dtype):
     # two products share one workspace on one stream; C with a padded,
     # unaligned row stride
-    M, N, K = 384, 392, 260
+    M, N, K = 384, 393, 260
     A1 = inputs.operand(KIND[dtype], M, K, 95)
     B1 = inputs.operand(KIND[dtype], K, N, 96)
     A2 = inputs.operand(KIND[dtype], M, K, 97)
@@ -129,7 +136,7 @@ def test_workspace_reused_in_order_and_ldc(dtype):
 
 
 def test_workspace_must_be_256_byte_aligned():
-    M, N, K = 64, 72, 33
+    M, N, K = 64, 73, 33
     A = inputs.operand("bf16_normal", M, K, 99)
     B = inputs.operand("bf16_normal", K, N, 100)
     Ad, Bd = A.cuda(), B.cuda()
@@ -146,8 +153,9 @@ def test_workspace_must_be_256_byte_aligned():
 
 
 def test_binding_uses_workspace_by_default():
-    # the Python binding repacks through torch's allocator; with
-    # workspace=False it reads the rows in place; same bits (no thin columns)
+    # the Python binding passes a workspace from torch's allocator where the
+    # plan asks for one (here none: the direct-copy tiles read the unaligned
+    # rows in place); with workspace=False never; same bits (no thin columns)
     M, N, K = 600, 776, 1030
     A = inputs.operand("bf16_normal", M, K, 101)
     B = inputs.operand("bf16_normal", K, N, 102)
@@ -165,15 +173,13 @@ def test_binding_uses_workspace_by_default():
 @pytest.mark.parametrize("dtype", ["bf16", "i8"])
 @pytest.mark.parametrize("r", [1, 2, 3, 5, 8, 13, 16])
 @pytest.mark.parametrize("a_off", [0, 1])
-def test_split_plan_repack_fused_with_thin_columns(dtype, r, a_off):
+def test_split_plan_reads_unaligned_rows_in_place(dtype, r, a_off):
     # 2048 x (2048 + r): 256 whole 128 x 128 tiles plus r columns for the
-    # thin kernel.  B's rows (ldb = N + 1) are never 16-byte aligned, so
-    # gemm_run_ws repacks B in one launch with the thin product of the last
-    # r columns (which reads those columns of B in place), then runs the
-    # main part; with a_off = 1 A is repacked first and the thin part reads
-    # the repacked A.  Same bits as gemm_run (the thin kernel's per-lane
-    # order of k does not depend on its rows per wave or sub-chunks), and
-    # the oracle's values (K = 264: a partial last slice).
+    # thin kernel (or, for 8 or 16 columns that are whole 16-byte pieces, a
+    # small direct-copy tile).  B's rows (ldb = N + 1) are never 16-byte
+    # aligned and, with a_off = 1, neither is A's pointer: every kernel reads
+    # them in place, so the plan asks for no workspace and gemm_run_ws is
+    # gemm_run.  The oracle's values (K = 264: a partial last slice).
     M, N, K = 2048, 2048 + r, 264
     A = inputs.operand(KIND[dtype], M, K, 300 + r)
     B = inputs.operand(KIND[dtype], K, N, 400 + r)
@@ -184,6 +190,7 @@ def test_split_plan_repack_fused_with_thin_columns(dtype, r, a_off):
     print("split", dtype, r, a_off, info.name.decode(), info.rem_name.decode(), info.packed_name.decode(),
           flush=True)
     need = plan.workspace_bytes(Ad.data_ptr(), Bd.data_ptr())
+    assert need == 0 and info.n_main == 2048 and info.rem_name
     buf, base = _workspace(need)
     got = _run(plan, Ad, Bd, M, N, dtype, base, need)
     ref = _run(plan, Ad, Bd, M, N, dtype)

@@ -7,7 +7,7 @@ namespace tg {
 void register_bf16(void (*add)(const KernelEntry&)) {
     typedef TraitsBF16 T;
     // production tiles (the 8-wave 256 x 256 x 64 is the default for large shapes)
-    add(mfma_entry<T, 256, 256, 64, 2, 4, 2, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2>(1));
+    add(mfma_entry<T, 256, 256, 64, 2, 4, 2, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2, 0, CST_MFMA, false, RD_AUTO, true>(1));
     add(mfma_entry<T, 256, 256, 64, 2, 2, 2, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 1>(1));
     add(mfma_entry<T, 256, 256, 32, 2, 2, 3, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 1>(1));
     add(mfma_entry<T, 256, 256, 32, 2, 2, 4, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 1>(1));

@@ -6,7 +6,7 @@ namespace tg {
 
 void register_i8(void (*add)(const KernelEntry&)) {
     typedef TraitsI8 T;
-    add(mfma_entry<T, 256, 256, 128, 2, 4, 2, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2>(2));
+    add(mfma_entry<T, 256, 256, 128, 2, 4, 2, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2, 0, CST_MFMA, false, RD_AUTO, true>(2));
     add(mfma_entry<T, 256, 256, 128, 2, 2, 2, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 1>(2));
     add(mfma_entry<T, 256, 256, 128, 2, 2, 2, LD_VGPR, LY_XOR, AC_WIDE, FR_REUSE, 1>(2));
     add(mfma_entry<T, 256, 256, 128, 2, 4, 2, LD_VGPR, LY_XOR, AC_WIDE, FR_REUSE, 2>(2));

@@ -35,10 +35,6 @@ struct PackArgs {
     int64_t rows, row_bytes, ld_s, ld_d;
 };
 
-// The repack of B fused with the thin product of a split plan's remainder
-// columns (workgroups [0, thin_blocks) run the thin kernel, the rest the
-// repack): the two are independent and both memory-bound.
-typedef void (*PackThinFn)(PackArgs, GemmArgs, int);
 
 // Values per workgroup in GemmArgs::clocks (TGEMM_CLOCK_VALUES of the C ABI).
 constexpr int CLOCK_VALUES = 6;
@@ -77,8 +73,7 @@ struct KernelEntry {
     int frag_read;   // TGEMM_READ_*: how fragments come out of LDS
     int lane_map;    // TGEMM_LANES_*: outputs of a lane (fp32 kernels; others report BLOCKS)
     KernelFn fn;
-    PackThinFn pack_thin;  // thin kernels: the fused repack + thin kernel (else NULL)
-    int pack_thin_bm;      // its rows of C per thin workgroup
+    KernelFn rem_fn;       // the twin that also computes column N of an N + 1 wide product (else NULL)
     char name[96];
 };
 

@@ -15,6 +15,7 @@ typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 #define TG_LDS __attribute__((address_space(3)))
 
@@ -107,6 +108,16 @@ __device__ __forceinline__ void copy16_to_lds(uint32_t lds, uint32_t voff, const
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(sl), "v"(voff), "s"(sb)
                  : "m0");
 }
+// The same copy, 4 bytes per lane: lane l's 4 bytes land at lds + 4 l.
+__device__ __forceinline__ void copy4_to_lds(uint32_t lds, uint32_t voff, const void* base) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    const uint64_t sb = ((uint64_t)hi << 32) | lo;
+    const uint32_t sl = __builtin_amdgcn_readfirstlane(lds);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(sl), "v"(voff), "s"(sb)
+                 : "m0");
+}
 #pragma clang diagnostic pop
 
 // Bytes [sh, sh + 16) of the 32-byte pair x | y (x first in memory),
@@ -137,13 +148,24 @@ __device__ __forceinline__ i32x4 funnel16(i32x4 x, i32x4 y, uint32_t sh) {
 // which keeps every load of the run in flight together.  The array is never
 // written, and is not const, so that the compiler cannot fold its value
 // back into a select.
+// 16 bytes from any byte address.  gfx950 global loads take unaligned
+// addresses (one global_load_dwordx4 either way); the copy keeps the
+// compiler from assuming the 16-byte alignment of an i32x4 pointer.
+__device__ __forceinline__ i32x4 load16(const void* p) {
+    i32x4 v;
+    __builtin_memcpy(&v, p, 16);
+    return v;
+}
+
 static __device__ __attribute__((aligned(16))) int32_t g_zeros[4];
 
 template <class T>
 __device__ __forceinline__ T load_or_zero(const T* p, bool ok) {
     static_assert(sizeof(T) <= sizeof(g_zeros), "at most 16 bytes");
     const T* src = ok ? p : reinterpret_cast<const T*>(g_zeros);
-    return *src;
+    T v;
+    __builtin_memcpy(&v, src, sizeof(T));  // any alignment
+    return v;
 }
 
 __device__ __forceinline__ int wave_id() {

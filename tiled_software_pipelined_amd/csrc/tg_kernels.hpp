@@ -5,7 +5,6 @@
 
 #include "tg_f32.hpp"
 #include "tg_mfma.hpp"
-#include "tg_pack.hpp"
 #include "tg_thin.hpp"
 
 namespace tg {
@@ -22,8 +21,11 @@ static const char* dtype_tag(int dt) { return dt == 0 ? "f32" : dt == 1 ? "bf16"
 
 // SHIFT: which operands the kernel reads from rows that are not 16-byte
 // aligned (bit 0 A, bit 1 B).  Such kernels are unlisted fallbacks.
+// WITH_REM: also compile the kernel's twin that computes one more column
+// of C in the same K loop (MfmaGemm's REM), for split plans.
 template <class Tr, int BM, int BN, int BK, int WM, int WN, int S, int LD, int LY, int AC, int FR,
-          int WAVES, int SHIFT = 0, int CST = CST_MFMA, bool SPREAD = false, int FREAD = RD_AUTO>
+          int WAVES, int SHIFT = 0, int CST = CST_MFMA, bool SPREAD = false, int FREAD = RD_AUTO,
+          bool WITH_REM = false>
 KernelEntry mfma_entry(int dtype) {
     static_assert(!SPREAD || LD == LD_DIRECT, "spread copies: the direct loader");
     typedef MfmaGemm<Tr, BM, BN, BK, WM, WN, S, LD, LY, AC, FR, SHIFT, CST, SPREAD, FREAD> K;
@@ -53,6 +55,9 @@ KernelEntry mfma_entry(int dtype) {
     e.tail_ok = 1;
     e.waves_per_simd = WAVES;
     e.fn = gemm_kernel<K, WAVES>;
+    if constexpr (WITH_REM)
+        e.rem_fn = gemm_kernel<MfmaGemm<Tr, BM, BN, BK, WM, WN, S, LD, LY, AC, FR, SHIFT, CST, SPREAD, FREAD, true>,
+                               WAVES>;
     snprintf(e.name, sizeof e.name, "%s_t%dx%dx%d_w%dx%d_s%d_%s_%s_%s_%s%s%s%s%s", dtype_tag(dtype), BM, BN,
              BK, WM, WN, S, LD == LD_DIRECT ? "direct" : "vgpr",
              LY == LY_XOR ? "xor" : LY == LY_XOR_POISON ? "xorpoison" : "plain",
@@ -96,18 +101,6 @@ KernelEntry naive_entry() {
     return e;
 }
 
-// The repack of B and the thin product of the remainder columns in one
-// launch: workgroups [0, thin_blocks) compute C's remainder columns (Thin),
-// the others repack.  The thin workgroups come first, so that their longer
-// streams of A start before the repack's many short workgroups.
-template <class Thin, int WAVES>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES, WAVES)))
-void pack_thin_kernel(PackArgs pk, GemmArgs g, int thin_blocks) {
-    static_assert(Thin::NT == 256, "one block size for both roles");
-    if ((int)blockIdx.x < thin_blocks) Thin::run_block(g, blockIdx.x);
-    else pack_chunks(pk, (int64_t)blockIdx.x - thin_blocks, (int64_t)gridDim.x - thin_blocks);
-}
-
 // The thin-N kernel (N <= NB <= THIN_N_MAX, bf16 / int8): unlisted, chosen
 // by the planner for thin products and for the narrow remainder of a split
 // plan (the smallest NB that covers N).
@@ -139,14 +132,6 @@ KernelEntry thin_entry() {
     e.frag_read = 3;  // A streamed in 16-byte pieces
     e.lane_map = 1;
     e.fn = gemm_kernel<K, K::WAVES>;
-    // fused with the repack of B, the thin kernel reads B's remainder
-    // columns in place, one element per row of B (the repack is writing the
-    // aligned copy meanwhile): four rows of C per wave (two where more would
-    // not fit in the registers), so that each workgroup's reads of those
-    // columns serve 16 (8) rows of C
-    typedef ThinGemm<DT, NB, NB == 2 ? 2 : NB >= 16 ? 1 : 4, NB == 1 ? 4 : NB <= 8 ? 2 : 1> F;
-    e.pack_thin = pack_thin_kernel<F, F::WAVES>;
-    e.pack_thin_bm = F::BM;
     snprintf(e.name, sizeof e.name, "%s_thin_n%d", dtype_tag(DT), NB);
     return e;
 }

@@ -91,7 +91,7 @@ enum FragRead { RD_AUTO = 0, RD_B32 = 1, RD_B64 = 2, RD_B128 = 3, RD_TR = 4 };
 // them right after the slice's barrier (see N1 below).
 template <class Tr, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int LOADER,
           int LAYOUT, int ACCESS, int FRAG, int SHIFT = 0, int CST = CST_MFMA, bool SPREAD = false,
-          int FREAD_ = RD_AUTO>
+          int FREAD_ = RD_AUTO, bool REM = false>
 struct MfmaGemm {
     typedef typename Tr::T T;
     typedef typename Tr::Out Out;
@@ -114,7 +114,11 @@ struct MfmaGemm {
     static constexpr int CB = NB / 16;       // 16-byte chunks per B row
     static constexpr int A_BYTES = BM * KB;
     static constexpr int B_BYTES = BK * NB;
-    static constexpr int SLOT = A_BYTES + B_BYTES;
+    // REM: the last column of C (the one past the grid's N) is computed in
+    // the same K loop (see rem_slice): each slot also holds, for every B row
+    // of the slice, the 4 bytes of that row that end at the column
+    static constexpr int REM_BYTES = REM ? BK * 4 : 0;
+    static constexpr int SLOT = A_BYTES + B_BYTES + REM_BYTES;
     static constexpr int LDS_BYTES = STAGES * SLOT;
     static constexpr int WTM = BM / WAVES_M;
     static constexpr int WTN = BN / WAVES_N;
@@ -145,6 +149,9 @@ struct MfmaGemm {
     static_assert(!POISON || (DIRECT && STAGES >= 2), "poisoned slots: the direct-loader ring");
     static_assert(SHIFT == 0 || (LOADER == LD_VGPR && WIDE), "shifted loads: register-staged, 16-byte chunks");
     static_assert(WIDE || FREAD == RD_B32, "the narrow rung reads 4 bytes at a time");
+    static_assert(!REM || (DIRECT && STAGES == 2 && !SPREAD && CST == CST_MFMA && !POISON && BK % 64 == 0 &&
+                           BK / 64 <= WAVES_M * WAVES_N && KB / 16 == 8),
+                  "in-loop remainder column: the 2-slot direct ring, 8 chunks per A row");
     // Shifted chunks complete their pairs from the neighbouring lane after
     // the multiply when the staged registers are few (the extra block and
     // shift per chunk then fit); with more chunks per thread the pair is
@@ -297,8 +304,9 @@ struct MfmaGemm {
                 } else if constexpr (MODE_A == LM_SHIFTED_EDGE) {
                     r.a[q] = load_chunk_shifted<true>(rowp + kc, a_beg, a_end);
                 } else if ((SHIFT & 1) == 0 && kc + CE <= g.K) {
-                    // K tail, a chunk wholly inside K of a 16-byte aligned row
-                    r.a[q] = *reinterpret_cast<const i32x4*>(rowp + kc);
+                    // K tail, a chunk wholly inside K (rows of any alignment
+                    // in the direct kernels)
+                    r.a[q] = load16(rowp + kc);
                 } else {
                     r.a[q] = load_chunk_guarded(rowp, kc, g.K);
                 }
@@ -324,8 +332,8 @@ struct MfmaGemm {
                 } else if constexpr (MODE_B == LM_SHIFTED_EDGE) {
                     r.b[q] = load_chunk_shifted<true>(rowp + min(nc, g.N - 1), b_beg, b_end);
                 } else if ((SHIFT & 2) == 0 && gk < g.K && nc + CE <= g.N) {
-                    // K tail, a whole chunk of an aligned row that lies inside K
-                    r.b[q] = *reinterpret_cast<const i32x4*>(rowp + nc);
+                    // K tail, a whole chunk that lies inside K and N
+                    r.b[q] = load16(rowp + nc);
                 } else {
                     r.b[q] = gk < g.K ? load_chunk_guarded(rowp, nc, g.N) : i32x4{0, 0, 0, 0};
                 }
@@ -419,6 +427,7 @@ struct MfmaGemm {
     struct DirectOffsets {
         uint32_t a[A_PER];
         uint32_t b[B_PER];
+        uint32_t rem;  // REM: this lane's B row (wave * 64 + lane) of a slice, in bytes
     };
 
     __device__ static __forceinline__ void direct_offsets(DirectOffsets& o, const GemmArgs& g, int m0,
@@ -440,6 +449,7 @@ struct MfmaGemm {
             const int col = min(n0 + c * CE, g.N - CE) - n0;
             o.b[q] = (uint32_t)((int64_t)k * g.ldb * ESZ + col * ESZ);
         }
+        o.rem = REM ? (uint32_t)((int64_t)(wave_id() * 64 + lane_id()) * g.ldb * ESZ) : 0u;
     }
 
     // Issue copy number i (0 <= i < N_LD) of one slice into `slot`.  Lane l
@@ -590,6 +600,7 @@ struct MfmaGemm {
         TG_LDS char* slot;
         const char* ca;
         const char* cb;
+        const char* cc;  // REM: the slice's B rows at the remainder column's dword
     };
 
     // Copies of slice u are issued in two parts.  Part 1, copies [0, N1),
@@ -603,6 +614,83 @@ struct MfmaGemm {
     static constexpr int N2 = N_LD - N1;
     // first copy of part 2 issued in K step s (0 <= s <= KSUB-1)
     __device__ static constexpr int part2_begin(int s) { return KSUB > 1 ? N1 + (s * N2) / (KSUB - 1) : N_LD; }
+
+    // ---- the remainder column (REM) ------------------------------------------
+    // A product one column wider than a whole number of tiles (N = g.N + 1)
+    // gets that last column from the same K loop instead of a second launch,
+    // whose workgroups would each walk B's column, one cache line per row of
+    // B.  With every slice, waves 0 .. BK/64 - 1 copy for each of the slice's
+    // B rows the 4 bytes that end at the column (the column is their last
+    // element, CPD elements per dword) into the slot's REM area, row k at
+    // 4 k.  Workgroup (tm, tn) owns rows tn*16 .. tn*16+15 of its tile for
+    // that column (the host only takes this path when the tile columns cover
+    // every row: BM <= 16 tiles_n); in waves 0 and 1, lane 8 r + c takes row
+    // 8 w + r and the c-th 16-byte chunk (CE values of k) of the slice's A
+    // row, and multiplies it by the column's CE values with the packed dot
+    // instructions (bf16 pairs into fp32, int8 quads into int32).  Each lane
+    // keeps one partial sum over the K loop; the 8 lanes of a row are added
+    // at the end.
+    static constexpr int CPD = 4 / ESZ;  // elements per copied dword
+    __device__ static __forceinline__ void issue_rem(TG_LDS char* slot, const DirectOffsets& o, const char* cc,
+                                                     int wave) {
+        if constexpr (REM) {
+            if (wave < BK / 64) copy4_to_lds((uint32_t)(uintptr_t)(slot + A_BYTES + B_BYTES + wave * 256), o.rem, cc);
+        }
+    }
+
+    // The column's dwords of rows k0 .. k0+BK-1 (the partial last slice):
+    // element loads of any alignment, zero at k >= K.
+    __device__ static __forceinline__ void fill_rem(TG_LDS char* slot, const GemmArgs& g, int k0, int wave,
+                                                    int lane) {
+        if constexpr (REM) {
+            if (wave < BK / 64) {
+                const int k = k0 + wave * 64 + lane;
+                const char* p = static_cast<const char*>(g.B) + ((int64_t)k * g.ldb + g.N + 1 - CPD) * ESZ;
+                uint32_t v = 0;
+                if (k < g.K) __builtin_memcpy(&v, p, 4);
+                *reinterpret_cast<TG_LDS uint32_t*>(slot + A_BYTES + B_BYTES + (wave * 64 + lane) * 4) = v;
+            }
+        }
+    }
+
+    // One slice's share of the remainder column for row `rt` of the tile.
+    __device__ static __forceinline__ void rem_slice(const TG_LDS char* slot, Out& racc, int rt, int lane) {
+        const int c = lane & 7;
+        const i32x4 a = *reinterpret_cast<const TG_LDS i32x4*>(slot + rt * KB + a_chunk(rt, c) * 16);
+        const TG_LDS i32x4* col = reinterpret_cast<const TG_LDS i32x4*>(slot + A_BYTES + B_BYTES + c * CE * 4);
+        if constexpr (ESZ == 2) {
+            // rows 8c .. 8c+7: the column is the high half of each dword;
+            // pair rows 2p, 2p+1 into one dword and take a dot of two
+            const i32x4 b0 = col[0], b1 = col[1];
+            const uint32_t d[8] = {(uint32_t)b0.x, (uint32_t)b0.y, (uint32_t)b0.z, (uint32_t)b0.w,
+                                   (uint32_t)b1.x, (uint32_t)b1.y, (uint32_t)b1.z, (uint32_t)b1.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t pr = __builtin_amdgcn_perm(d[2 * q + 1], d[2 * q], 0x07060302u);
+                racc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, (uint32_t)a[q]),
+                                                       __builtin_bit_cast(bf16x2, pr), racc, false);
+            }
+        } else {
+            // rows 16c .. 16c+15: the column is byte 3 of each dword; gather
+            // rows 4q .. 4q+3 into one dword and take a dot of four
+            uint32_t d[16];
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const i32x4 b = col[h];
+                d[4 * h] = (uint32_t)b.x;
+                d[4 * h + 1] = (uint32_t)b.y;
+                d[4 * h + 2] = (uint32_t)b.z;
+                d[4 * h + 3] = (uint32_t)b.w;
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t lo = __builtin_amdgcn_perm(d[4 * q + 1], d[4 * q], 0x07030703u);
+                const uint32_t hi = __builtin_amdgcn_perm(d[4 * q + 3], d[4 * q + 2], 0x07030703u);
+                const uint32_t v = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+                racc = __builtin_amdgcn_sdot4((int)a[q], (int)v, racc, false);
+            }
+        }
+    }
 
     // Matrix step on `cur` with reads of (rslot, rs) into `nxt` interleaved.
     // BARRIER: before the reads, meet the other waves once this wave's slot
@@ -632,6 +720,7 @@ struct MfmaGemm {
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        if constexpr (REM && BARRIER && DB == 0 && DE > 0) issue_rem(ct.slot, off, ct.cc, wave);
     }
 
     // K steps s .. KSUB-1 of one slice t from `cur_slot`.  PREV: issue part
@@ -897,6 +986,16 @@ struct MfmaGemm {
         const int tiles = (g.K + BK - 1) / BK;
         const int full = g.K / BK;  // slices with no K tail
 
+        // REM: this lane's row of the remainder column and its partial sum
+        Out racc = Out(0);
+        const bool rem_rows = REM && wave < 2 && tn * 16 < BM;  // wave-uniform
+        const int rt = tn * 16 + wave * 8 + (lane >> 3);
+        auto rem_at = [&](const TG_LDS char* slot) {
+            if constexpr (REM) {
+                if (rem_rows) rem_slice(slot, racc, rt, lane);
+            }
+        };
+
         if constexpr (DIRECT) {
             DirectOffsets off;
             direct_offsets(off, g, m0, n0);
@@ -905,8 +1004,11 @@ struct MfmaGemm {
             const char* bbase = static_cast<const char*>(g.B) + (int64_t)n0 * ESZ;
             const int64_t astep = (int64_t)BK * ESZ;          // A base advance per slice
             const int64_t bstep = (int64_t)BK * g.ldb * ESZ;  // B base advance per slice
+            // REM: slice 0's B rows at the dword that ends at column g.N
+            const char* cbase = static_cast<const char*>(g.B) + (int64_t)(g.N + 1 - CPD) * ESZ;
             auto issue_slice = [&](int sl) {
                 issue_direct(smem + (sl % STAGES) * SLOT, off, abase + sl * astep, bbase + sl * bstep, wave);
+                issue_rem(smem + (sl % STAGES) * SLOT, off, cbase + sl * bstep, wave);
             };
             if constexpr (STAGES == 1) {
                 // One slot: the copy of slice t+1 may only start once every
@@ -949,18 +1051,22 @@ struct MfmaGemm {
             // With SPREAD, part 2 of slice t + STAGES - 1's copies is issued
             // during slice t; slice STAGES - 1 was issued whole above.
             auto target = [&](int sl) {
-                return CopyTarget{smem + (sl % STAGES) * SLOT, abase + sl * astep, bbase + sl * bstep};
+                return CopyTarget{smem + (sl % STAGES) * SLOT, abase + sl * astep, bbase + sl * bstep,
+                                  cbase + sl * bstep};
             };
-            const CopyTarget none{smem, abase, bbase};
+            const CopyTarget none{smem, abase, bbase, cbase};
             int t = 0;
             if (STAGES < full) {
+                rem_at(smem);
                 slice_direct<false, true, true>(acc, f, smem, smem + SLOT, STAGES - 2, none, target(STAGES), off,
                                                 wm0, wn0, lane, wave);
-                for (t = 1; t + STAGES < full; ++t)
+                for (t = 1; t + STAGES < full; ++t) {
+                    rem_at(smem + (t % STAGES) * SLOT);
                     slice_direct<SPREAD, true, true>(acc, f, smem + (t % STAGES) * SLOT,
                                                      smem + ((t + 1) % STAGES) * SLOT, STAGES - 2,
                                                      target(t + STAGES - 1), target(t + STAGES), off, wm0, wn0,
                                                      lane, wave);
+                }
                 // the last slice whose part 2 is still to be issued
                 // (t + STAGES == full, so t + 1 < full)
                 if constexpr (SPREAD) {
@@ -970,13 +1076,17 @@ struct MfmaGemm {
                     ++t;
                 }
             }
-            for (; t + 1 < full; ++t)
+            for (; t + 1 < full; ++t) {
+                rem_at(smem + (t % STAGES) * SLOT);
                 slice_direct<false, true, false>(acc, f, smem + (t % STAGES) * SLOT, smem + ((t + 1) % STAGES) * SLOT,
                                                  min(STAGES - 2, full - 2 - t), none, none, off, wm0, wn0, lane,
                                                  wave);
-            if (t < full)
+            }
+            if (t < full) {
+                rem_at(smem + (t % STAGES) * SLOT);
                 slice_direct<false, false, false>(acc, f, smem + (t % STAGES) * SLOT, smem, 0, none, none, off, wm0,
                                                   wn0, lane, wave);
+            }
             if (full < tiles) {
                 // K tail: element loads with zero fill into slot full % STAGES.
                 // No copy is in flight (the last wait drained them) and every
@@ -984,7 +1094,9 @@ struct MfmaGemm {
                 Staged<LM_ELEMENT, LM_ELEMENT> r;
                 load_regs(r, g, m0, n0, full * BK);
                 store_regs(smem + (full % STAGES) * SLOT, r);
+                fill_rem(smem + (full % STAGES) * SLOT, g, full * BK, wave, lane);
                 wait_lds_then_barrier();
+                rem_at(smem + (full % STAGES) * SLOT);
                 compute(smem + (full % STAGES) * SLOT, acc, wm0, wn0, lane, tail_steps(g, full));
             }
             }
@@ -1010,6 +1122,13 @@ struct MfmaGemm {
         } else {
             if (g.c_stream) store_c<true>(C, g, acc, m0 + wm0, n0 + wn0, lane, inside);
             else store_c<false>(C, g, acc, m0 + wm0, n0 + wn0, lane, inside);
+        }
+        if constexpr (REM) {
+            if (rem_rows) {
+#pragma unroll
+                for (int o = 1; o < 8; o <<= 1) racc += __shfl_xor(racc, o, 64);
+                if ((lane & 7) == 0 && m0 + rt < g.M) C[(int64_t)(m0 + rt) * g.ldc + g.N] = racc;
+            }
         }
         clk.finish(g.clocks);
     }

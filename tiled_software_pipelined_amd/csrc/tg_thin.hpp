@@ -31,13 +31,15 @@
 namespace tg {
 
 // DT 1: bf16 -> fp32, 2: int8 -> int32; NB: columns computed (>= N); ROWS_ /
-// V_: rows of C per wave and sub-chunks per chunk (0: by NB)
-template <int DT, int NB, int ROWS_ = 0, int V_ = 0>
+// V_: rows of C per wave and sub-chunks per chunk (0: by NB); NT_: threads
+// per workgroup
+template <int DT, int NB, int ROWS_ = 0, int V_ = 0, int NT_ = 256>
 struct ThinGemm {
     static_assert(NB >= 1 && NB <= THIN_N_MAX && (NB & (NB - 1)) == 0, "NB: a power of two up to 16");
     typedef typename std::conditional<DT == 1, uint16_t, int8_t>::type T;
     typedef typename std::conditional<DT == 1, float, int32_t>::type Acc;
-    static constexpr int NT = 256;
+    static constexpr int NT = NT_;
+    static_assert(NT % 64 == 0 && NT <= 1024, "whole waves");
     // rows of C per wave: one for the narrowest products (more workgroups,
     // four waves per SIMD to keep A in flight; 4095 x 1 x 4104 bf16: 9.7 us
     // against 11.6 with 4 rows), fewer for 16 columns (registers)
@@ -65,6 +67,7 @@ struct ThinGemm {
     static constexpr int BV = NB * ESZ >= 16 ? NB * ESZ / 16 : 0;
     static constexpr int BVPT = BV ? KC * BV / NT : 1;
     static constexpr int LDS_BYTES = 2 * SLOT_ELEMS * ESZ;
+    static_assert((KC * NB) % NT == 0 && (BV == 0 || (KC * BV) % NT == 0), "a chunk's B block in whole rounds");
     typedef typename std::conditional<DT == 1, i32x4, i32x2>::type AVec;
 
     __device__ static __forceinline__ Acc widen(T v) {
@@ -91,7 +94,7 @@ struct ThinGemm {
                                                   bool a_wide) {
         if (a_wide && kv + KE <= K) {
 #pragma unroll
-            for (int i = 0; i < ROWS; ++i) av[i] = *reinterpret_cast<const AVec*>(rowp[i] + kv);
+            for (int i = 0; i < ROWS; ++i) __builtin_memcpy(&av[i], rowp[i] + kv, sizeof(AVec));
         } else {
 #pragma unroll
             for (int i = 0; i < ROWS; ++i) {

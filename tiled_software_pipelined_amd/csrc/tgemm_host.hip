@@ -26,6 +26,8 @@ struct tgemm_plan {
     int32_t a_guard, b_guard;     // leading-dimension based (pointer alignment is checked per run)
     int64_t n_main;               // columns the entry's grid covers (N unless split)
     tgemm_plan* rem;              // split plans: the last N - n_main columns (thin kernel), else NULL
+    bool rem_fused;               // split plans with one last column: the entry's REM twin computes
+                                  // it in the main K loop (`rem` is kept for a fallback kernel)
     tgemm_plan* packed;           // default plans: the same product on operands repacked with
                                   // 16-byte aligned rows (gemm_run_ws), else NULL
     int64_t lda_p, ldb_p;         // leading dimensions of `packed`
@@ -62,6 +64,12 @@ int elem_size(int dtype) { return dtype == TGEMM_F32 ? 4 : dtype == TGEMM_BF16 ?
 // Width of an entry's unguarded global loads (0: it only does element loads).
 int access_bytes(const KernelEntry& e) { return e.gload_bytes; }
 
+// Kernels whose 16-byte reads take any byte address: the direct loader (the
+// global -> LDS copy reads 16 bytes from any address, at the full rate of an
+// aligned one) and the thin kernel (plain 16-byte loads, which gfx950 serves
+// at any address too).  Only element alignment of the pointers is needed.
+bool any_alignment(const KernelEntry& e) { return e.loader == tg::LD_DIRECT || e.family == tg::FAM_THIN; }
+
 // Leading-dimension checks: can every row of the operand be read with
 // `bytes`-wide aligned accesses?  (Pointer alignment is checked at run time.)
 void ld_guards(const KernelEntry& e, int64_t N, int64_t lda, int64_t ldb, int32_t* ga, int32_t* gb) {
@@ -72,9 +80,18 @@ void ld_guards(const KernelEntry& e, int64_t N, int64_t lda, int64_t ldb, int32_
     }
     const int esz = elem_size(e.dtype);
     const int per = bytes / esz;  // elements per access
+    if (any_alignment(e)) {
+        // rows of any alignment; the last chunk of a B row must still end at N
+        *ga = 0;
+        *gb = N % per != 0 || N < per;
+        return;
+    }
     *ga = (lda * esz) % bytes != 0;
     *gb = (ldb * esz) % bytes != 0 || N % per != 0 || N < per;
 }
+
+// Does entry e need 16-byte aligned operand pointers?
+bool needs_aligned_ptrs(const KernelEntry& e) { return access_bytes(e) != 0 && !any_alignment(e); }
 
 // The direct loader addresses each lane's 16 bytes as a wave-uniform base
 // plus a 32-bit byte offset from the slice's first row: up to (BM-1)*lda
@@ -442,6 +459,7 @@ tgemm_plan* make_plan(int64_t M, int64_t N, int64_t K, int32_t dtype, int64_t ld
     p->b_guard = gb;
     p->n_main = N;
     p->rem = nullptr;
+    p->rem_fused = false;
     p->packed = nullptr;
     p->lda_p = lda;
     p->ldb_p = ldb;
@@ -490,6 +508,13 @@ static tgemm_plan* split_plan(int64_t M, int64_t N, int64_t K, int32_t dtype, in
     gemm_destroy(p);
     main->N = N;  // the user's shape; the grid covers n_main
     main->rem = rem;
+    // one last column, and tile columns enough to give every row of a tile
+    // to some workgroup (16 rows each): the main kernel's twin computes it
+    // in its own K loop (bf16 4095 x 4097 x 4104: 125 us against 145 us for
+    // the two launches, whose thin kernel walks B's column once per
+    // workgroup)
+    main->rem_fused = r == 1 && main->entry->rem_fn && 16 * ((N - r + main->entry->bn - 1) / main->entry->bn) >=
+                                                           main->entry->bm;
     g_err.clear();
     return main;
 }
@@ -516,6 +541,11 @@ tgemm_plan* gemm_plan_variant(int64_t M, int64_t N, int64_t K, int32_t dtype, in
     bool is_default = false;
     tgemm_plan* p = split_plan(M, N, K, dtype, lda, ldb, ldc, variant, &is_default);
     if (!p || !is_default || M == 0 || N <= tg::THIN_N_MAX || K == 0) return p;
+    // a kernel that reads rows of any alignment gains nothing from the copy
+    // (bf16 4096^3 with ldb = 4097: 114 us in place against 121 us repacked)
+    int32_t ga = 0, gb = 0;
+    ld_guards(*p->entry, p->n_main, lda, ldb, &ga, &gb);
+    if (any_alignment(*p->entry) && !ga && !gb) return p;
     const int esz = elem_size(dtype);
     const int64_t lda_p = aligned_ld(lda, K, esz), ldb_p = aligned_ld(ldb, N, esz);
     tgemm_plan* q = split_plan(M, N, K, dtype, lda_p, ldb_p, ldc, nullptr, nullptr);
@@ -582,7 +612,7 @@ int run_impl(const tgemm_plan* p, const void* A, const void* B, void* C, uint64_
     const KernelEntry* e = p->entry;
     int32_t ga = p->a_guard, gb = p->b_guard;
     const int bytes = access_bytes(*e);
-    if (bytes) {
+    if (needs_aligned_ptrs(*e)) {
         if ((uintptr_t)A % bytes) ga = 1;
         if ((uintptr_t)B % bytes) gb = 1;
     }
@@ -591,8 +621,9 @@ int run_impl(const tgemm_plan* p, const void* A, const void* B, void* C, uint64_
         int32_t fa = 0, fbg = 0;
         ld_guards(*e, p->n_main, p->lda, p->ldb, &fa, &fbg);
         const int fbytes = access_bytes(*e);
-        ga = fa || (fbytes && (uintptr_t)A % fbytes);
-        gb = fbg || (fbytes && (uintptr_t)B % fbytes);
+        const bool fptr = needs_aligned_ptrs(*e);
+        ga = fa || (fptr && (uintptr_t)A % fbytes);
+        gb = fbg || (fptr && (uintptr_t)B % fbytes);
         if (!accepts(*e, ga, gb)) {
             set_err("no kernel of this plan reads operands at these addresses");
             return TGEMM_E_ALIGN;
@@ -626,14 +657,16 @@ int run_impl(const tgemm_plan* p, const void* A, const void* B, void* C, uint64_
         }
         g.clocks = clocks;
     }
+    // the plan's own kernel computes the last column too (REM twin)
+    const bool fused = p->rem_fused && e == p->entry;
     void* args[] = {&g};
-    const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(e->fn),
+    const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(fused ? e->rem_fn : e->fn),
                                            dim3((unsigned)(g.tiles_m * g.tiles_n)), dim3(e->threads), args, 0, s);
     if (err != hipSuccess) {
         set_err("launch of %s failed: %s", e->name, hipGetErrorString(err));
         return TGEMM_E_HIP;
     }
-    if (p->rem)  // the last N - n_main columns, after the main part on the same stream
+    if (p->rem && !fused)  // the last N - n_main columns, after the main part on the same stream
         return run_impl(p->rem, A, static_cast<const char*>(B) + p->n_main * esz,
                         static_cast<char*>(C) + p->n_main * 4, nullptr, 0, stream);
     return TGEMM_OK;
@@ -734,63 +767,16 @@ int gemm_run_ws(const tgemm_plan* p, const void* A, const void* B, void* C, void
         a = ws;
         ws += (p->M * p->lda_p * esz + 255) / 256 * 256;
     }
-    if (!(mask & 2)) return gemm_run(p->packed, a, b, C, stream);
-    const tg::PackArgs pb{static_cast<const char*>(B), ws, p->K, p->N * esz, p->ldb * esz, p->ldb_p * esz};
-    b = ws;
-    // the thin kernel with the fewest columns that cover the remainder
-    // (whatever the repacked plan's own remainder kernel is)
-    const KernelEntry* thin = nullptr;
-    if (p->packed->rem) {
-        const int64_t rcols = p->N - p->packed->n_main;
-        for (const KernelEntry& e : g_reg[p->dtype])
-            if (e.family == tg::FAM_THIN && e.pack_thin && e.bn >= rcols && (!thin || e.bn < thin->bn)) thin = &e;
-    }
-    if (!thin) {
+    if (mask & 2) {
+        const tg::PackArgs pb{static_cast<const char*>(B), ws, p->K, p->N * esz, p->ldb * esz, p->ldb_p * esz};
         const hipError_t err = tg::launch_pack(pb, s);
         if (err != hipSuccess) {
             set_err("repack of B failed: %s", hipGetErrorString(err));
             return TGEMM_E_HIP;
         }
-        return gemm_run(p->packed, a, b, C, stream);
+        b = ws;
     }
-    // A split plan: the repack of B and the thin product of the last
-    // N - n_main columns in one launch (both memory-bound, independent: the
-    // thin part reads those columns of B in place), then the main part on
-    // the repacked operands, on the same stream.
-    const KernelEntry& te = *thin;
-    const int64_t r = p->N - p->packed->n_main;
-    const int64_t lda_used = (mask & 1) ? p->lda_p : p->lda;
-    tg::GemmArgs g{};
-    g.A = a;
-    g.B = static_cast<const char*>(B) + p->packed->n_main * esz;
-    g.C = static_cast<char*>(C) + p->packed->n_main * 4;
-    g.M = (int32_t)p->M;
-    g.N = (int32_t)r;
-    g.K = (int32_t)p->K;
-    g.tiles_m = (int32_t)((p->M + te.pack_thin_bm - 1) / te.pack_thin_bm);
-    g.tiles_n = 1;
-    g.lda = lda_used;
-    g.ldb = p->ldb;
-    g.ldc = p->ldc;
-    int32_t ga = 0, gb = 0;
-    ld_guards(te, r, lda_used, p->ldb, &ga, &gb);
-    const int bytes = access_bytes(te);
-    g.a_guard = ga || (bytes && (uintptr_t)g.A % bytes);
-    g.b_guard = gb || (bytes && (uintptr_t)g.B % bytes);
-    const int64_t thin_blocks = g.tiles_m;
-    const int64_t blocks = thin_blocks + tg::pack_blocks(pb);
-    tg::PackArgs pk = pb;
-    int tb = (int)thin_blocks;
-    void* args[] = {&pk, &g, &tb};
-    const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(te.pack_thin), dim3((unsigned)blocks),
-                                           dim3(256), args, 0, s);
-    if (err != hipSuccess) {
-        set_err("launch of the repack of B with %s failed: %s", te.name, hipGetErrorString(err));
-        return TGEMM_E_HIP;
-    }
-    tgemm_plan main_part = *p->packed;
-    main_part.rem = nullptr;
-    return gemm_run(&main_part, a, b, C, stream);
+    return gemm_run(p->packed, a, b, C, stream);
 }
 
 }  // extern "C"
@@ -876,7 +862,8 @@ int gemm_plan_get_info(const tgemm_plan* p, tgemm_plan_info* info) {
     entry_to_variant(e, p->wg_group, &info->variant);
     info->grid = (int32_t)(((p->M + e.bm - 1) / e.bm) * ((p->n_main + e.bn - 1) / e.bn));
     info->n_main = p->n_main;
-    if (p->rem) snprintf(info->rem_name, sizeof info->rem_name, "%s", p->rem->entry->name);
+    if (p->rem_fused) snprintf(info->rem_name, sizeof info->rem_name, "%s_remcol", e.name);
+    else if (p->rem) snprintf(info->rem_name, sizeof info->rem_name, "%s", p->rem->entry->name);
     if (p->packed) snprintf(info->packed_name, sizeof info->packed_name, "%s", p->packed->entry->name);
     info->threads = e.threads;
     info->lds_bytes = e.lds_bytes;

@@ -77,8 +77,8 @@ def _find(d, pattern):
 
 def _is_gemm(name):
     # every kernel a plan launches: the tiled / thin kernels, and the operand
-    # repack of gemm_run_ws (alone, or fused with a split plan's thin part)
-    return "gemm_kernel" in name or "pack_rows" in name or "pack_thin_kernel" in name
+    # repack of gemm_run_ws (plans whose kernels need aligned rows)
+    return "gemm_kernel" in name or "pack_rows" in name
 
 
 def _is_copy(name):
