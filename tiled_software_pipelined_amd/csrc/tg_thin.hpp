@@ -8,10 +8,11 @@
 // loads at a time.  This kernel streams A once.  A workgroup owns BM rows of
 // C (ROWS per wave) and walks K in chunks of KC = V x 512: the chunk is V
 // sub-chunks of 512, and in each every lane takes 8 consecutive k, one
-// 16-byte (bf16) or 8-byte (int8) load per row where the row is aligned,
-// element loads otherwise.  The chunk's KC x NB block of B is loaded once per
-// workgroup (element loads from clamped, valid addresses, zero past K and N)
-// and shared through LDS.  The loads of chunk c+1 (A into registers, B into
+// 16-byte (bf16) or 8-byte (int8) load per row at any alignment (element
+// loads only where the 8 would cross K).  The chunk's KC x NB block of B is
+// loaded once per workgroup (element loads from clamped, valid addresses,
+// zero past K and N; whole 16-byte pieces of its rows when N is a whole
+// number of them) and shared through LDS.  The loads of chunk c+1 (A into registers, B into
 // registers then LDS) are issued before chunk c is multiplied - the
 // register-staged double buffer of the GEMM page, section 9 - and one
 // barrier per chunk orders the LDS slots.  With so little arithmetic per
@@ -90,9 +91,8 @@ struct ThinGemm {
 
     // This lane's 8 elements of each of its rows at kv (zero past K): one
     // sub-chunk.
-    __device__ static __forceinline__ void load_a(AVec (&av)[ROWS], const T* const (&rowp)[ROWS], int kv, int K,
-                                                  bool a_wide) {
-        if (a_wide && kv + KE <= K) {
+    __device__ static __forceinline__ void load_a(AVec (&av)[ROWS], const T* const (&rowp)[ROWS], int kv, int K) {
+        if (kv + KE <= K) {
 #pragma unroll
             for (int i = 0; i < ROWS; ++i) __builtin_memcpy(&av[i], rowp[i] + kv, sizeof(AVec));
         } else {
@@ -233,42 +233,38 @@ struct ThinGemm {
 
     __device__ static __forceinline__ void run(const GemmArgs& g) { run_block(g, blockIdx.x); }
 
-    // The rows of C of workgroup `block` (rows block * BM ..).
+    // The rows of C of workgroup `block` (rows block * BM ..).  A in
+    // 16-byte (int8: 8-byte) pieces at any alignment (element loads only
+    // past K); B in whole 16-byte pieces of its rows when N is a whole
+    // number of pieces (b_guard == 0), element by element otherwise.
     __device__ static __forceinline__ void run_block(const GemmArgs& g, int block) {
         __shared__ __attribute__((aligned(16))) T lds[2 * SLOT_ELEMS];
         TG_LDS T* slots = (TG_LDS T*)(lds);
-        // B in 16-byte pieces when its rows allow it (b_guard == 0 means
-        // aligned rows and pointer, and N a whole number of pieces); A in
-        // 16-byte (int8: 8-byte) pieces when its rows are aligned
-        const bool a_wide = g.a_guard == 0;
         if constexpr (BV > 0) {
             if (g.b_guard == 0) {
-                if (a_wide) run_k<true, true>(g, slots, block);
-                else run_k<true, false>(g, slots, block);
+                run_k<true>(g, slots, block);
                 return;
             }
         }
-        if (a_wide) run_k<false, true>(g, slots, block);
-        else run_k<false, false>(g, slots, block);
+        run_k<false>(g, slots, block);
     }
 
-    // The chunk's B block (zero past K and N) into `slot`.
+    // The chunk's B block (zero past K and N) into registers, then `slot`.
     template <bool BVEC>
-    __device__ static __forceinline__ void load_b_any(typename std::conditional<BVEC, i32x4[BVPT], T[BPT]>::type& r,
-                                                      const GemmArgs& g, int kc0) {
+    using BRegsOf = typename std::conditional<BVEC, i32x4[BVPT], T[BPT]>::type;
+    template <bool BVEC>
+    __device__ static __forceinline__ void load_b_any(BRegsOf<BVEC>& r, const GemmArgs& g, int kc0) {
         if constexpr (BVEC) load_b_vec(r, g, kc0);
         else load_b(r, g, kc0);
     }
     template <bool BVEC>
-    __device__ static __forceinline__ void store_b_any(
-        TG_LDS T* slot, const typename std::conditional<BVEC, i32x4[BVPT], T[BPT]>::type& r) {
+    __device__ static __forceinline__ void store_b_any(TG_LDS T* slot, const BRegsOf<BVEC>& r) {
         if constexpr (BVEC) store_b_vec(slot, r);
         else store_b(slot, r);
     }
 
-    // WIDE: A rows are 16-byte (int8: 8-byte) aligned, so a lane's 8
-    // elements of a row that lie inside K take one wide load (element loads
-    // with zero fill otherwise).  Before the first wait, the chunk-0 loads of
+    // A lane's 8 elements of a row that lie inside K take one wide load
+    // (element loads with zero fill otherwise).  Before the first wait, the chunk-0 loads of
     // B and then of every sub-chunk of A are all in flight; B is staged into
     // LDS (waiting only for its own loads, issued first), and each
     // sub-chunk's A registers are refilled with the next chunk's as soon as
@@ -276,9 +272,9 @@ struct ThinGemm {
     // other slot: the register-staged double buffer of the GEMM page,
     // section 9, one barrier per chunk.  Sub-chunks that start at or past K
     // hold only zeros and are not multiplied.
-    template <bool BVEC, bool WIDE>
+    template <bool BVEC>
     __device__ static __forceinline__ void run_k(const GemmArgs& g, TG_LDS T* slots, int block) {
-        typedef typename std::conditional<BVEC, i32x4[BVPT], T[BPT]>::type BRegs;
+        typedef BRegsOf<BVEC> BRegs;
         const T* A = static_cast<const T*>(g.A);
         const int lane = lane_id(), wave = wave_id();
         const int r0 = block * BM + wave * ROWS;
@@ -298,7 +294,7 @@ struct ThinGemm {
             load_b_any<BVEC>(b, g, 0);
 #pragma unroll
             for (int v = 0; v < V; ++v)
-                if (v * KS < g.K) load_a(av[v], rowp, v * KS + lane * KE, g.K, WIDE);
+                if (v * KS < g.K) load_a(av[v], rowp, v * KS + lane * KE, g.K);
             store_b_any<BVEC>(slots, b);
             wait_lds_then_barrier();
         }
@@ -311,7 +307,7 @@ struct ThinGemm {
             for (int v = 0; v < V; ++v) {
                 if (c * KC + v * KS < g.K) multiply(acc, av[v], cur, v, lane);
                 if (more && (c + 1) * KC + v * KS < g.K)
-                    load_a(av[v], rowp, (c + 1) * KC + v * KS + lane * KE, g.K, WIDE);
+                    load_a(av[v], rowp, (c + 1) * KC + v * KS + lane * KE, g.K);
             }
             if (more) store_b_any<BVEC>(slots + ((c + 1) & 1) * SLOT_ELEMS, b);
             wait_lds_then_barrier();
