@@ -256,12 +256,14 @@ def test_thin_products_use_the_thin_kernel():
     # 16-byte pieces): the thin kernel of the smallest width that covers N;
     # otherwise the direct-loader tile, whatever the rows' alignment
     for dtype in (tl.BF16, tl.I8):
-        for N, ldb, width in [(1, 1, 1), (7, 7, 8), (3, 64, 4), (9, 9, 16)]:
+        for N, ldb, width in [(1, 1, 1), (1, 5, 1), (7, 7, 8), (3, 64, 4), (9, 9, 16)]:
             info = tl.Plan(4096, N, 4096, dtype, ldb=ldb).info()
             assert b"thin" in info.name and info.n_main == N, (dtype, N, ldb)
-            # rows per workgroup: 4 waves of 1 row (width 1, 2 and 16), else 4 rows
-            rows = 4 if width <= 2 or width == 16 else 16
+            # rows per workgroup: 16 waves of one row; the contiguous-column
+            # twin (N = 1, ldb = 1) 4 waves of one row
+            rows = 4 if (N, ldb) == (1, 1) else 16
             assert info.variant.tile_n == width and info.variant.tile_m == rows and info.grid == 4096 // rows
+            assert info.name.endswith(b"_col") == ((N, ldb) == (1, 1))
         assert b"thin" not in tl.Plan(4096, 16, 4096, dtype, ldb=32).info().name
         assert b"thin" not in tl.Plan(4096, 16, 4096, dtype, ldb=17).info().name
         assert b"thin" not in tl.Plan(4096, 17, 4096, dtype, ldb=17).info().name

@@ -53,6 +53,7 @@ void register_bf16(void (*add)(const KernelEntry&)) {
     add(naive_entry<1>());
     // unlisted: thin products (N <= 16) and split-plan remainders
     add(thin_entry<1, 1>());
+    add(thin_entry<1, 1, true>());
     add(thin_entry<1, 2>());
     add(thin_entry<1, 4>());
     add(thin_entry<1, 8>());

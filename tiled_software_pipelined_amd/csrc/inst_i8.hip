@@ -37,6 +37,7 @@ void register_i8(void (*add)(const KernelEntry&)) {
     add(naive_entry<2>());
     // unlisted: thin products (N <= 16) and split-plan remainders
     add(thin_entry<2, 1>());
+    add(thin_entry<2, 1, true>());
     add(thin_entry<2, 2>());
     add(thin_entry<2, 4>());
     add(thin_entry<2, 8>());

@@ -74,6 +74,7 @@ struct KernelEntry {
     int lane_map;    // TGEMM_LANES_*: outputs of a lane (fp32 kernels; others report BLOCKS)
     KernelFn fn;
     KernelFn rem_fn;       // the twin that also computes column N of an N + 1 wide product (else NULL)
+    int thin_col;          // thin kernels: 1 = the twin for a contiguous B column (N = 1, ldb = 1)
     char name[96];
 };
 

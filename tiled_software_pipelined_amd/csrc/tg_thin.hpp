@@ -34,26 +34,30 @@ namespace tg {
 // DT 1: bf16 -> fp32, 2: int8 -> int32; NB: columns computed (>= N); ROWS_ /
 // V_: rows of C per wave and sub-chunks per chunk (0: by NB); NT_: threads
 // per workgroup
-template <int DT, int NB, int ROWS_ = 0, int V_ = 0, int NT_ = 256>
+template <int DT, int NB, int ROWS_ = 0, int V_ = 0, int NT_ = 1024>
 struct ThinGemm {
     static_assert(NB >= 1 && NB <= THIN_N_MAX && (NB & (NB - 1)) == 0, "NB: a power of two up to 16");
     typedef typename std::conditional<DT == 1, uint16_t, int8_t>::type T;
     typedef typename std::conditional<DT == 1, float, int32_t>::type Acc;
     static constexpr int NT = NT_;
     static_assert(NT % 64 == 0 && NT <= 1024, "whole waves");
-    // rows of C per wave: one for the narrowest products (more workgroups,
-    // four waves per SIMD to keep A in flight; 4095 x 1 x 4104 bf16: 9.7 us
-    // against 11.6 with 4 rows), fewer for 16 columns (registers)
-    static constexpr int ROWS = ROWS_ ? ROWS_ : (NB <= 2 || NB >= 16 ? 1 : 4);
+    // One row of C per wave, 16 waves per workgroup (one workgroup per CU at
+    // 4 waves per SIMD): the chunk's B block is staged by 1024 threads, so
+    // each holds few of its elements and 9 sub-chunks (K up to 4608 in one
+    // memory round trip) fit the registers up to 4 columns (4095 x N x 4104
+    // bf16, compact B: N = 2 8.8 us, 3 11.5, 8 15.3, 16 24.1 against 12.7,
+    // 16.7, 21.2, 35.4 with 256 threads and 1-4 rows per wave; a strided
+    // column, the remainder of a split plan: N = 1 11.4 against 21.8)
+    static constexpr int ROWS = ROWS_ ? ROWS_ : 1;
     // waves per SIMD the kernel is compiled for
-    static constexpr int WAVES = NB == 1 || (NB == 2 && DT == 1) ? 4 : 2;
+    static constexpr int WAVES = 4;
     static constexpr int BM = ROWS * (NT / 64);  // rows per workgroup
     static constexpr int BN = NB;
     static constexpr int ESZ = sizeof(T);
     static constexpr int KE = 8;                 // consecutive k per lane per sub-chunk
     // sub-chunks per chunk (registers: V x ROWS pieces of A per lane; 9 of 512
     // cover K up to 4608 in one chunk)
-    static constexpr int V = V_ ? V_ : (NB <= 2 ? 9 : NB <= 8 ? 2 : 1);
+    static constexpr int V = V_ ? V_ : (NB <= 4 ? 9 : NB <= 8 ? 4 : 2);
     static constexpr int KS = 64 * KE;           // k per sub-chunk
     static constexpr int KC = V * KS;            // k per chunk
     // LDS: the chunk's B rows, NB elements each, as V x 64 runs of KE rows
@@ -63,12 +67,11 @@ struct ThinGemm {
     static constexpr int RUN_PIECES = (KE * NB * ESZ + 15) / 16;
     static constexpr int LANE_ELEMS = (RUN_PIECES | 1) * 16 / ESZ;
     static constexpr int SLOT_ELEMS = V * 64 * LANE_ELEMS;
-    static constexpr int BPT = KC * NB / NT;  // B elements each thread stages per chunk
+    static constexpr int BPT = (KC * NB + NT - 1) / NT;  // B elements each thread stages per chunk
     // with B rows in whole aligned 16-byte pieces: pieces per row, per thread
     static constexpr int BV = NB * ESZ >= 16 ? NB * ESZ / 16 : 0;
-    static constexpr int BVPT = BV ? KC * BV / NT : 1;
+    static constexpr int BVPT = BV ? (KC * BV + NT - 1) / NT : 1;
     static constexpr int LDS_BYTES = 2 * SLOT_ELEMS * ESZ;
-    static_assert((KC * NB) % NT == 0 && (BV == 0 || (KC * BV) % NT == 0), "a chunk's B block in whole rounds");
     typedef typename std::conditional<DT == 1, i32x4, i32x2>::type AVec;
 
     __device__ static __forceinline__ Acc widen(T v) {
@@ -107,6 +110,13 @@ struct ThinGemm {
         }
     }
 
+    // Is element / piece q*NT + tid of a chunk's B block one of its `total`?
+    // (Every thread's is, but for the last round when NT does not divide it.)
+    template <int TOTAL>
+    __device__ static __forceinline__ bool in_block(int q, int idx) {
+        return (q + 1) * NT <= TOTAL || idx < TOTAL;
+    }
+
     // This thread's share of the chunk's B block: element q*NT + tid is row
     // (q*NT + tid) / NB, column (q*NT + tid) % NB of the chunk.
     __device__ static __forceinline__ void load_b(T (&bv)[BPT], const GemmArgs& g, int kc0) {
@@ -115,7 +125,7 @@ struct ThinGemm {
         for (int q = 0; q < BPT; ++q) {
             const int idx = q * NT + threadIdx.x;
             const int k = kc0 + idx / NB, j = idx % NB;
-            bv[q] = load_or_zero(B + (int64_t)k * g.ldb + j, k < g.K && j < g.N);
+            bv[q] = load_or_zero(B + (int64_t)k * g.ldb + j, in_block<KC * NB>(q, idx) && k < g.K && j < g.N);
             // at most 8 of these 64-bit addresses live at a time; the loads
             // of all groups still overlap
             if ((q & 7) == 7) __builtin_amdgcn_sched_barrier(0);
@@ -132,7 +142,7 @@ struct ThinGemm {
                 const int idx = q * NT + threadIdx.x;
                 const int k = kc0 + idx / BV, p = idx % BV;
                 bw[q] = load_or_zero(reinterpret_cast<const i32x4*>(B + (int64_t)k * g.ldb + p * (16 / ESZ)),
-                                     k < g.K);
+                                     in_block<KC * BV>(q, idx) && k < g.K);
             }
         }
     }
@@ -143,8 +153,9 @@ struct ThinGemm {
             for (int q = 0; q < BVPT; ++q) {
                 const int idx = q * NT + threadIdx.x;
                 const int kk = idx / BV, p = idx % BV;
-                *reinterpret_cast<TG_LDS i32x4*>(slot + (kk / KE) * LANE_ELEMS + (kk % KE) * NB + p * (16 / ESZ)) =
-                    bw[q];
+                if (in_block<KC * BV>(q, idx))
+                    *reinterpret_cast<TG_LDS i32x4*>(slot + (kk / KE) * LANE_ELEMS + (kk % KE) * NB +
+                                                     p * (16 / ESZ)) = bw[q];
             }
         }
     }
@@ -154,7 +165,7 @@ struct ThinGemm {
         for (int q = 0; q < BPT; ++q) {
             const int idx = q * NT + threadIdx.x;
             const int kk = idx / NB, j = idx % NB;
-            slot[(kk / KE) * LANE_ELEMS + (kk % KE) * NB + j] = bv[q];
+            if (in_block<KC * NB>(q, idx)) slot[(kk / KE) * LANE_ELEMS + (kk % KE) * NB + j] = bv[q];
         }
     }
 

@@ -169,7 +169,7 @@ double model_rounds(const KernelEntry& e, int64_t M, int64_t N) {
     return -1.0;
 }
 
-const KernelEntry* default_entry(int dtype, int64_t M, int64_t N, int64_t K, bool guarded) {
+const KernelEntry* default_entry(int dtype, int64_t M, int64_t N, int64_t K, int64_t ldb, bool guarded) {
     tgemm_variant v{};
     v.kernel = TGEMM_KERNEL_TILED;
     auto wgs = [&](int t) { return ((M + t - 1) / t) * ((N + t - 1) / t); };
@@ -194,9 +194,12 @@ const KernelEntry* default_entry(int dtype, int64_t M, int64_t N, int64_t K, boo
         // time: 4096 x 1 x 4096 in 11 us against 95 us).  With aligned rows
         // the direct-loader tiles are as fast or faster (4096 x 16 x 4096:
         // 17.7 us against 23.8).
+        // (one column: the contiguous-column twin exactly when ldb = 1)
         const KernelEntry* best = nullptr;
         for (const KernelEntry& e : g_reg[dtype])
-            if (e.family == tg::FAM_THIN && e.bn >= N && (!best || e.bn < best->bn)) best = &e;
+            if (e.family == tg::FAM_THIN && e.bn >= N && (!best || e.bn < best->bn) &&
+                (N > 1 || (e.thin_col != 0) == (ldb == 1)))
+                best = &e;
         if (best) return best;
     }
     const int64_t short_k = i8 ? 2048 : 1024;
@@ -389,7 +392,7 @@ tgemm_plan* make_plan(int64_t M, int64_t N, int64_t K, int32_t dtype, int64_t ld
     if (v.kernel == TGEMM_KERNEL_AUTO && v.tile_m == 0 && v.tile_n == 0 && v.tile_k == 0 && v.stages == 0 &&
         v.loader == 0 && v.lds_layout == 0 && v.access == 0 && v.frag == 0 && v.waves_m == 0 &&
         v.waves_n == 0 && v.store == 0 && v.copy_sched == 0 && v.frag_read == 0 && v.lane_map == 0) {
-        e = default_entry(dtype, M, N, K, false);
+        e = default_entry(dtype, M, N, K, ldb, false);
         default_plan = true;
     } else {
         e = find_entry(dtype, v);
@@ -412,7 +415,7 @@ tgemm_plan* make_plan(int64_t M, int64_t N, int64_t K, int32_t dtype, int64_t ld
         r.lane_map = 0;
         r.wg_group = 0;
         const KernelEntry* rs = find_entry(dtype, r);
-        e = rs ? rs : default_entry(dtype, M, N, K, true);
+        e = rs ? rs : default_entry(dtype, M, N, K, ldb, true);
         if (!e || !direct_fits(*e, lda, ldb)) {
             set_err("no kernel addresses leading dimensions lda=%lld ldb=%lld", (long long)lda, (long long)ldb);
             return nullptr;
@@ -423,7 +426,7 @@ tgemm_plan* make_plan(int64_t M, int64_t N, int64_t K, int32_t dtype, int64_t ld
     // starts from.  A default plan falls back to the default register-staged
     // choice for the shape, an explicit variant to its nearest relative.
     const KernelEntry* fb[4] = {e, nullptr, nullptr, nullptr};
-    const KernelEntry* base = default_plan ? default_entry(dtype, M, N, K, true) : e;
+    const KernelEntry* base = default_plan ? default_entry(dtype, M, N, K, ldb, true) : e;
     for (int m = 1; m < 4; ++m) {
         fb[m] = guard_capable(accepts(*e, m & 1, m & 2) ? e : base, m & 1, m & 2);
         if (!fb[m]) {
