@@ -189,9 +189,11 @@ tgemm_plan* gemm_plan_variant(int64_t M, int64_t N, int64_t K, int32_t dtype,
  * tiles) run, for a pointer that is element-aligned but not 16-byte aligned
  * or a leading dimension whose rows are not 16-byte aligned, a kernel that
  * reads that operand in shifted or element pieces (slower, same results);
- * so does a B whose N is not a whole number of 16-byte pieces, and a leading
- * dimension too large for the direct loader's 32-bit lane offsets (from the
- * plan on).  A default plan one column wider than 16 or more whole 256 x 256
+ * so does a B narrower than one 16-byte piece per row (when no thin kernel
+ * takes it), and a leading dimension too large for the direct loader's
+ * 32-bit lane offsets (from the plan on).  A B whose N is not a whole number
+ * of 16-byte pieces is read in place by the direct loader as well (its last
+ * row, and a partial last slice, by element loads).  A default plan one column wider than 16 or more whole 256 x 256
  * tile columns computes that column in the main kernel's K loop; a few more
  * columns go to the thin kernel after the main launch.  Nothing outside
  * [A, A + ((M-1)*lda + K) elements) or the corresponding range of B is read.

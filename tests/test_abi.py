@@ -209,17 +209,24 @@ def test_unaligned_rows_are_read_in_place():
     info = tl.Plan(4096, 4096, 4096, tl.BF16, lda=4097, ldb=4097).info()
     assert info.variant.loader == tl.LOADER_DIRECT and info.a_guarded == 0 and info.b_guarded == 0
     # N not a whole number of 16-byte pieces (the last piece of a B row
-    # would cross N): a small problem keeps a small register-staged tile
+    # crosses N): the direct loader reads that piece in place too (guarded:
+    # B's last row through the register tail)
     for dtype in (tl.BF16, tl.I8):
-        v = tl.Plan(150, 131, 101, dtype).info().variant
-        assert v.loader == tl.LOADER_VGPR and (v.tile_m, v.tile_n) == (128, 128), dtype
-    # an explicit direct-loader request on N = 4097 (no split for explicit
-    # variants) falls back to the register-staged kernel with the same tile
-    # and wave grid
+        info = tl.Plan(150, 131, 101, dtype).info()
+        assert info.variant.loader == tl.LOADER_DIRECT and info.b_guarded == 1, dtype
+    # so does an explicit direct-loader request on N = 4097 (no split for
+    # explicit variants)
     req = tl.Variant(kernel=tl.KERNEL_TILED, tile_m=256, tile_n=256, tile_k=64, waves_n=4,
                      loader=tl.LOADER_DIRECT)
-    v = tl.Plan(4095, 4097, 4104, tl.BF16, variant=req).info().variant
-    assert (v.loader, v.tile_m, v.tile_n, v.tile_k, v.waves_m, v.waves_n) == (tl.LOADER_VGPR, 256, 256, 64, 2, 4)
+    info = tl.Plan(4095, 4097, 4104, tl.BF16, variant=req).info()
+    v = info.variant
+    assert (v.loader, v.tile_m, v.tile_n, v.tile_k, v.waves_m, v.waves_n) == (tl.LOADER_DIRECT, 256, 256, 64, 2, 4)
+    assert info.b_guarded == 1
+    # fewer than one whole piece per row: not the direct loader
+    for dtype in (tl.BF16, tl.I8):
+        assert tl.Plan(150, 5, 101, dtype, variant=tl.Variant(kernel=tl.KERNEL_TILED, tile_m=64, tile_n=64,
+                                                              loader=tl.LOADER_DIRECT)).info().variant.loader \
+            == tl.LOADER_VGPR, dtype
 
 
 def test_default_tile_follows_the_round_model():
@@ -252,11 +259,12 @@ def test_default_tile_follows_the_round_model():
 
 
 def test_thin_products_use_the_thin_kernel():
-    # N <= 16 where the direct loader cannot read B (N not a whole number of
-    # 16-byte pieces): the thin kernel of the smallest width that covers N;
-    # otherwise the direct-loader tile, whatever the rows' alignment
+    # N <= 16 where the direct loader cannot read B (fewer than one whole
+    # 16-byte piece per row): the thin kernel of the smallest width that
+    # covers N; otherwise the direct-loader tile, whatever the rows' alignment
     for dtype in (tl.BF16, tl.I8):
-        for N, ldb, width in [(1, 1, 1), (1, 5, 1), (7, 7, 8), (3, 64, 4), (9, 9, 16)]:
+        cases = [(1, 1, 1), (1, 5, 1), (7, 7, 8), (3, 64, 4)] + ([(9, 9, 16)] if dtype == tl.I8 else [])
+        for N, ldb, width in cases:
             info = tl.Plan(4096, N, 4096, dtype, ldb=ldb).info()
             assert b"thin" in info.name and info.n_main == N, (dtype, N, ldb)
             # rows per workgroup: 16 waves of one row; the contiguous-column
@@ -267,6 +275,8 @@ def test_thin_products_use_the_thin_kernel():
         assert b"thin" not in tl.Plan(4096, 16, 4096, dtype, ldb=32).info().name
         assert b"thin" not in tl.Plan(4096, 16, 4096, dtype, ldb=17).info().name
         assert b"thin" not in tl.Plan(4096, 17, 4096, dtype, ldb=17).info().name
+    # bf16 from 8 columns (one whole piece) on: the direct-loader tile
+    assert b"thin" not in tl.Plan(4096, 9, 4096, tl.BF16, ldb=9).info().name
     # fp32 keeps its one-fma-chain-per-output kernel
     assert b"thin" not in tl.Plan(4096, 4, 4096, tl.F32).info().name
 

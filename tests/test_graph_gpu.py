@@ -32,7 +32,8 @@ def _gpu():
 CASES = [
     ("bf16_normal", 512, 384, 328, 0),    # 64 x 64 direct ring, K tail
     ("bf16_normal", 1024, 1024, 512, 0),  # 128 x 128 direct ring
-    ("bf16_normal", 300, 257, 129, 1),    # unaligned rows: repack + direct kernel, or the shift kernel
+    ("bf16_normal", 300, 257, 129, 1),    # unaligned rows and a partial last piece, read in place
+    ("f32_uniform", 130, 77, 65, 1),      # fp32 unaligned rows: repack, or the guarded kernel
     ("i8_uniform", 520, 264, 1000, 0),
     ("f32_uniform", 200, 136, 96, 0),     # vector-FMA path
     ("bf16_normal", 70, 90, 0, 0),        # K = 0: the fill kernel

@@ -88,9 +88,8 @@ def test_workspace_matches_run_and_oracle(dtype, case):
     Ad, Bd = _exact_view(A, lda, oa), _exact_view(B, ldb, ob)
     plan = tl.Plan(M, N, K, DT[dtype], lda, ldb, N)
     need = plan.workspace_bytes(Ad.data_ptr(), Bd.data_ptr())
-    # fp32 kernels need aligned rows; the matrix-core plans only where N is
-    # not a whole number of 16-byte pieces (their fallback kernels)
-    assert (need > 0) == (dtype == "f32" or N % CE[dtype] != 0), (need, plan.info().name)
+    # fp32 kernels need aligned rows; the matrix-core plans read any in place
+    assert (need > 0) == (dtype == "f32"), (need, plan.info().name)
     print("workspace", dtype, case, need, plan.info().name.decode(), flush=True)
     ref = _run(plan, Ad, Bd, M, N, dtype)
     buf, base = _workspace(need)
@@ -106,7 +105,7 @@ def test_workspace_matches_run_and_oracle(dtype, case):
     del buf
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "i8"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i8"])
 def test_workspace_reused_in_order_and_ldc(dtype):
     # two products share one workspace on one stream; C with a padded,
     # unaligned row stride
@@ -137,10 +136,10 @@ def test_workspace_reused_in_order_and_ldc(dtype):
 
 def test_workspace_must_be_256_byte_aligned():
     M, N, K = 64, 73, 33
-    A = inputs.operand("bf16_normal", M, K, 99)
-    B = inputs.operand("bf16_normal", K, N, 100)
+    A = inputs.operand("f32_uniform", M, K, 99)
+    B = inputs.operand("f32_uniform", K, N, 100)
     Ad, Bd = A.cuda(), B.cuda()
-    plan = tl.Plan(M, N, K, 1, K, N, N)
+    plan = tl.Plan(M, N, K, 0, K, N, N)
     need = plan.workspace_bytes(Ad.data_ptr(), Bd.data_ptr())
     assert need > 0
     buf, base = _workspace(need + 256)

@@ -36,8 +36,8 @@ def _padded(t, ld, off):
 
 
 def _case(dtype, M, N, K, lda, ldb, offa, offb, seed):
-    kind = {"bf16": "bf16_normal", "i8": "i8_uniform"}[dtype]
-    code = {"bf16": tl.BF16, "i8": tl.I8}[dtype]
+    kind = {"f32": "f32_uniform", "bf16": "bf16_normal", "i8": "i8_uniform"}[dtype]
+    code = {"f32": tl.F32, "bf16": tl.BF16, "i8": tl.I8}[dtype]
     A = inputs.operand(kind, M, K, seed)
     B = inputs.operand(kind, K, N, seed + 1)
     bufa, Ad = _padded(A, lda, offa)
@@ -63,13 +63,34 @@ def _case(dtype, M, N, K, lda, ldb, offa, offb, seed):
     return need
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "i8"])
-def test_noalloc_matches_caller_workspace_twice(dtype):
-    # first call: B rows misaligned (ldb odd) and A at an odd element offset;
-    # second call, smaller: both operands misaligned by stride
-    n1 = _case(dtype, 1000, 1001, 1000, 1000, 1001, 3, 0, 71)
-    n2 = _case(dtype, 300, 257, 200, 203, 261, 0, 1, 73)
+def test_noalloc_matches_caller_workspace_twice():
+    # fp32, whose kernels need aligned rows and so repack misaligned
+    # operands: first call, B rows misaligned (ldb odd) and A at an odd
+    # element offset; second call, smaller: both operands misaligned by
+    # stride
+    n1 = _case("f32", 1000, 1001, 1000, 1000, 1001, 3, 0, 71)
+    n2 = _case("f32", 300, 257, 200, 203, 261, 0, 1, 73)
     assert n2 < n1
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "i8"])
+def test_noalloc_reads_matrix_core_operands_in_place(dtype):
+    # the matrix-core kernels read misaligned rows in place: no workspace,
+    # gemm_run_noalloc is gemm_run, bit for bit
+    M, N, K, lda, ldb = 300, 257, 200, 203, 261
+    kind = {"bf16": "bf16_normal", "i8": "i8_uniform"}[dtype]
+    bufa, Ad = _padded(inputs.operand(kind, M, K, 75), lda, 1)
+    bufb, Bd = _padded(inputs.operand(kind, K, N, 76), ldb, 3)
+    plan = tl.Plan(M, N, K, {"bf16": tl.BF16, "i8": tl.I8}[dtype], lda, ldb, N)
+    assert plan.workspace_bytes(Ad.data_ptr(), Bd.data_ptr()) == 0
+    out_dtype = torch.int32 if dtype == "i8" else torch.float32
+    C0 = torch.full((M, N), -7, dtype=out_dtype, device="cuda")
+    C1 = torch.full((M, N), -5, dtype=out_dtype, device="cuda")
+    plan.run_ptr(Ad.data_ptr(), Bd.data_ptr(), C0.data_ptr())
+    plan.run_noalloc_ptr(Ad.data_ptr(), Bd.data_ptr(), C1.data_ptr())
+    torch.cuda.synchronize()
+    assert torch.equal(C0, C1)
+    del bufa, bufb
 
 
 def test_noalloc_without_misaligned_operands_is_gemm_run():
@@ -87,11 +108,11 @@ def test_noalloc_without_misaligned_operands_is_gemm_run():
 
 
 def test_noalloc_rejects_a_repack_beyond_its_array():
-    # B (8192 x 4097 bf16) repacked to rows of 4160 elements: 68.2 MB > 64 MiB
+    # B (8192 x 4097 fp32) repacked to rows of 4128 elements: 135 MB > 64 MiB
     M, N, K = 1, 4097, 8192
-    A = torch.zeros((M, K), dtype=torch.bfloat16, device="cuda")
-    B = torch.zeros((K, N), dtype=torch.bfloat16, device="cuda")
-    plan = tl.Plan(M, N, K, tl.BF16)
+    A = torch.zeros((M, K), dtype=torch.float32, device="cuda")
+    B = torch.zeros((K, N), dtype=torch.float32, device="cuda")
+    plan = tl.Plan(M, N, K, tl.F32)
     need = plan.workspace_bytes(A.data_ptr(), B.data_ptr())
     assert need > tl.NOALLOC_MAX_BYTES
     C = torch.full((M, N), -7.0, device="cuda")

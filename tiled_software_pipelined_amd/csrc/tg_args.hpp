@@ -65,7 +65,8 @@ struct KernelEntry {
     int threads;     // threads per workgroup
     int lds_bytes;   // static LDS per workgroup
     int loads_per_stage;  // global->LDS instructions per wave per stage
-    int shift_mask;  // operands it can read from rows that are not 16-byte aligned: bit 0 A, bit 1 B
+    int shift_mask;  // bit 0: reads A rows that are not 16-byte aligned; bit 1: reads B rows that are not
+                     // (the direct loader: B whose N is not a whole number of 16-byte pieces)
     int listed;      // 0: only reached as the fallback of a listed entry for such operands
     int tail_ok;     // handles K not a multiple of bk
     int waves_per_simd;  // occupancy the kernel is compiled for (its registers allow at least this)

@@ -52,7 +52,9 @@ KernelEntry mfma_entry(int dtype) {
     e.threads = K::NT;
     e.lds_bytes = K::LDS_BYTES;
     e.loads_per_stage = AC == AC_WIDE ? K::N_LD : K::A_DW + K::B_DW;
-    e.shift_mask = SHIFT;
+    // the direct loader reads B whose N is not a whole number of 16-byte
+    // chunks (bit 1); register-staged kernels need their SHIFT bits
+    e.shift_mask = SHIFT | (LD == LD_DIRECT && AC == AC_WIDE ? 2 : 0);
     e.listed = SHIFT == 0;
     e.tail_ok = 1;
     e.waves_per_simd = WAVES;

@@ -421,9 +421,16 @@ struct MfmaGemm {
     // slice's (wave-uniform) base address never change along K, so they are
     // computed once: A chunk q of this thread sits at row r, logical chunk c
     // -> r*lda + c*16 bytes from A's slice base (rows past M clamped to the
-    // last row); B chunk q at row k, chunk c -> k*ldb + (column clamped to
-    // the last full chunk) bytes from B's slice base.  The host only picks
-    // this loader when these offsets fit in 32 bits.
+    // last row); B chunk q at row k, chunk c -> k*ldb + column bytes from B's
+    // slice base, where a chunk that starts inside N is read where it is and
+    // one that starts at or past N is clamped to the row's last whole chunk,
+    // or to the tile's first column when that lies further right (its
+    // columns are never stored).  With N not a whole number of chunks
+    // the chunk that crosses N also reads past N, into the row's padding or
+    // the next row: still inside B for every row but the last, which the
+    // kernel never copies (run: the slice holding it goes through the
+    // register tail).  The host only picks this loader when the offsets fit
+    // in 32 bits and N is at least one chunk.
     struct DirectOffsets {
         uint32_t a[A_PER];
         uint32_t b[B_PER];
@@ -446,7 +453,11 @@ struct MfmaGemm {
             const int p = q * NT + tid;
             const int k = p / CB, pc = p % CB;
             const int c = b_chunk(k, pc);
-            const int col = min(n0 + c * CE, g.N - CE) - n0;
+            const int nc = n0 + c * CE;
+            // never left of the tile's first column: the offset is unsigned
+            // (a tile column that starts within a chunk of N has no whole
+            // chunk inside N, and N - CE lies left of it)
+            const int col = (nc < g.N ? nc : max(g.N - CE, n0)) - n0;
             o.b[q] = (uint32_t)((int64_t)k * g.ldb * ESZ + col * ESZ);
         }
         o.rem = REM ? (uint32_t)((int64_t)(wave_id() * 64 + lane_id()) * g.ldb * ESZ) : 0u;
@@ -984,7 +995,12 @@ struct MfmaGemm {
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
         const int tiles = (g.K + BK - 1) / BK;
-        const int full = g.K / BK;  // slices with no K tail
+        // slices with no K tail; for the direct copy, with B's rows ending in
+        // a partial chunk (b_guard) and K a whole number of slices, all but
+        // the last: that slice holds B's last row, whose chunk across N a
+        // copy would read past the end of B, so it goes through the register
+        // tail (element loads) like a partial slice
+        const int full = g.K / BK - ((DIRECT && g.b_guard && g.K % BK == 0 && g.K > 0) ? 1 : 0);
 
         // REM: this lane's row of the remainder column and its partial sum
         Out racc = Out(0);

@@ -124,7 +124,12 @@ const KernelEntry* find_entry(int dtype, const tgemm_variant& v) {
 }
 
 // Can entry e read operands whose rows are not 16-byte aligned (ga: A, gb: B)?
-bool accepts(const KernelEntry& e, bool ga, bool gb) {
+// Can entry e run an N-column product whose operands need these guards (ga:
+// A rows not 16-byte aligned, gb: B rows not aligned or N not a whole
+// number of 16-byte pieces)?  The direct loader takes the partial piece of
+// N but needs at least one whole piece per row.
+bool accepts(const KernelEntry& e, bool ga, bool gb, int64_t N) {
+    if (gb && e.loader == tg::LD_DIRECT && N * elem_size(e.dtype) < 16) return false;
     return (!ga || (e.shift_mask & 1)) && (!gb || (e.shift_mask & 2));
 }
 
@@ -263,18 +268,18 @@ const KernelEntry* default_entry(int dtype, int64_t M, int64_t N, int64_t K, int
 // register-staged kernel with shifted loads for just those operands
 // (registry order puts A-only before B-only before both) with the same tile
 // and wave grid, else the same tile, else the nearest tile in size.
-const KernelEntry* guard_capable(const KernelEntry* e, bool ga, bool gb) {
-    if (accepts(*e, ga, gb)) return e;
+const KernelEntry* guard_capable(const KernelEntry* e, bool ga, bool gb, int64_t N) {
+    if (accepts(*e, ga, gb, N)) return e;
     for (int same_waves = 1; same_waves >= 0; --same_waves)
         for (const KernelEntry& c : g_reg[e->dtype])
-            if (accepts(c, ga, gb) && c.family == e->family && c.bm == e->bm && c.bn == e->bn &&
+            if (accepts(c, ga, gb, N) && c.family == e->family && c.bm == e->bm && c.bn == e->bn &&
                 c.bk == e->bk && c.access == tg::AC_WIDE && c.stages == 2 &&
                 (!same_waves || (c.wm == e->wm && c.wn == e->wn)))
                 return &c;
     const KernelEntry* best = nullptr;
     int best_d = INT_MAX;
     for (const KernelEntry& c : g_reg[e->dtype])
-        if (accepts(c, ga, gb) && c.family == tg::FAM_TILED && c.access == tg::AC_WIDE && c.stages == 2) {
+        if (accepts(c, ga, gb, N) && c.family == tg::FAM_TILED && c.access == tg::AC_WIDE && c.stages == 2) {
             const int d = abs(c.bm - e->bm) + abs(c.bn - e->bn);
             if (d < best_d) {
                 best = &c;
@@ -428,7 +433,7 @@ tgemm_plan* make_plan(int64_t M, int64_t N, int64_t K, int32_t dtype, int64_t ld
     const KernelEntry* fb[4] = {e, nullptr, nullptr, nullptr};
     const KernelEntry* base = default_plan ? default_entry(dtype, M, N, K, ldb, true) : e;
     for (int m = 1; m < 4; ++m) {
-        fb[m] = guard_capable(accepts(*e, m & 1, m & 2) ? e : base, m & 1, m & 2);
+        fb[m] = guard_capable(accepts(*e, m & 1, m & 2, N) ? e : base, m & 1, m & 2, N);
         if (!fb[m]) {
             set_err("variant %s has no fallback for unaligned operands", e->name);
             return nullptr;
@@ -545,10 +550,9 @@ tgemm_plan* gemm_plan_variant(int64_t M, int64_t N, int64_t K, int32_t dtype, in
     tgemm_plan* p = split_plan(M, N, K, dtype, lda, ldb, ldc, variant, &is_default);
     if (!p || !is_default || M == 0 || N <= tg::THIN_N_MAX || K == 0) return p;
     // a kernel that reads rows of any alignment gains nothing from the copy
-    // (bf16 4096^3 with ldb = 4097: 114 us in place against 121 us repacked)
-    int32_t ga = 0, gb = 0;
-    ld_guards(*p->entry, p->n_main, lda, ldb, &ga, &gb);
-    if (any_alignment(*p->entry) && !ga && !gb) return p;
+    // (bf16 4096^3 with ldb = 4097: 114 us in place against 121 us
+    // repacked), and a copy leaves N as it is
+    if (any_alignment(*p->entry)) return p;
     const int esz = elem_size(dtype);
     const int64_t lda_p = aligned_ld(lda, K, esz), ldb_p = aligned_ld(ldb, N, esz);
     tgemm_plan* q = split_plan(M, N, K, dtype, lda_p, ldb_p, ldc, nullptr, nullptr);
@@ -619,7 +623,7 @@ int run_impl(const tgemm_plan* p, const void* A, const void* B, void* C, uint64_
         if ((uintptr_t)A % bytes) ga = 1;
         if ((uintptr_t)B % bytes) gb = 1;
     }
-    if (!accepts(*e, ga, gb)) {
+    if (!accepts(*e, ga, gb, p->n_main)) {
         e = p->fallback[ga | (gb << 1)];
         int32_t fa = 0, fbg = 0;
         ld_guards(*e, p->n_main, p->lda, p->ldb, &fa, &fbg);
@@ -627,7 +631,7 @@ int run_impl(const tgemm_plan* p, const void* A, const void* B, void* C, uint64_
         const bool fptr = needs_aligned_ptrs(*e);
         ga = fa || (fptr && (uintptr_t)A % fbytes);
         gb = fbg || (fptr && (uintptr_t)B % fbytes);
-        if (!accepts(*e, ga, gb)) {
+        if (!accepts(*e, ga, gb, p->n_main)) {
             set_err("no kernel of this plan reads operands at these addresses");
             return TGEMM_E_ALIGN;
         }
