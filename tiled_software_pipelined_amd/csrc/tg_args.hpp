@@ -16,8 +16,8 @@ struct GemmArgs {
     int32_t tiles_m, tiles_n;  // ceil(M / BM), ceil(N / BN)
     int64_t lda, ldb, ldc;
     int32_t wg_group;          // <= 0: row-major workgroup order
-    int32_t a_guard;           // 1: A rows not 16-byte aligned (kernels with shift_mask bit 0)
-    int32_t b_guard;           // 1: B rows not 16-byte aligned or N not a whole number of chunks (bit 1)
+    int32_t a_guard;           // 1: A rows not 16-byte aligned, for a kernel that needs them aligned
+    int32_t b_guard;           // 1: the same for B, or N not a whole number of 16-byte chunks
     int32_t c_stream;          // 1: C rows 128-byte aligned: non-temporal (streaming) C stores
     uint64_t* clocks;          // NULL, or 6 values per workgroup (tiled kernels): shader-clock and
                                // 100 MHz real-time counters at its start, at the end of its

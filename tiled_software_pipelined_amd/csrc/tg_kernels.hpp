@@ -128,11 +128,11 @@ KernelEntry thin_entry() {
     e.frag = FR_REUSE;
     e.wm = K::NT / 64;
     e.wn = 1;
-    e.gload_bytes = 16;  // A rows in whole pieces when 16-byte aligned; B by element
+    e.gload_bytes = 16;  // A in 16-byte (int8: 8-byte) pieces at any alignment; B by element or piece
     e.threads = K::NT;
     e.lds_bytes = K::LDS_BYTES;
     e.loads_per_stage = K::ROWS + K::BPT;
-    e.shift_mask = 3;  // element loads wherever a row is not aligned
+    e.shift_mask = 3;  // any alignment, any N
     e.listed = 0;
     e.tail_ok = 1;
     e.waves_per_simd = K::WAVES;

@@ -33,10 +33,11 @@
 // Edges: rows of A past M and columns of B past N are loaded from a clamped,
 // valid address (they only feed C elements that are never stored); the last,
 // partial K slice is loaded element by element with zero fill (the skill's
-// pitfall list: boundary tiles need a guarded fallback); an operand whose rows
-// are not 16-byte aligned (odd leading dimension, offset pointer) goes through
-// the register-staged loader, each chunk funnel-shifted out of two aligned
-// 16-byte loads.
+// pitfall list: boundary tiles need a guarded fallback).  The direct loader
+// reads rows of any alignment (its copies take any byte address) and a B
+// whose N is not a whole number of chunks (see direct_offsets); the
+// register-staged loader reads unaligned rows in its SHIFT twins, each chunk
+// funnel-shifted out of two aligned 16-byte loads.
 #pragma once
 
 #include "tg_device.hpp"

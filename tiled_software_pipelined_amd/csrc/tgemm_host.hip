@@ -123,7 +123,6 @@ const KernelEntry* find_entry(int dtype, const tgemm_variant& v) {
     return nullptr;
 }
 
-// Can entry e read operands whose rows are not 16-byte aligned (ga: A, gb: B)?
 // Can entry e run an N-column product whose operands need these guards (ga:
 // A rows not 16-byte aligned, gb: B rows not aligned or N not a whole
 // number of 16-byte pieces)?  The direct loader takes the partial piece of
@@ -148,8 +147,10 @@ bool accepts(const KernelEntry& e, bool ga, bool gb, int64_t N) {
 //    unit, each `mid_tile` of a 256 x 256 round.
 // So 4096 x 4096 keeps 256 x 256 (1 vs 4 x 0.33) and 4096 x 4352 (272 big
 // tiles, 1088 small ones) takes 128 x 128 (1.64 vs 5 x 0.33).  With
-// `guarded` (an operand whose rows are not 16-byte aligned) the candidates
-// are the register-staged tiles.  Short K also takes 128 x 128: with one
+// `guarded` (the fallback choice for operands the direct loader cannot take:
+// B narrower than one 16-byte piece, leading dimensions beyond its 32-bit
+// offsets) the candidates are the thin kernel and the register-staged
+// tiles.  Short K also takes 128 x 128: with one
 // round of 256 x 256 tiles every workgroup writes its C tile at the same
 // moment, unoverlapped, and at short K that write is most of the work.
 double big_rounds(int64_t tiles) {
@@ -539,10 +540,11 @@ static int64_t aligned_ld(int64_t ld, int64_t cols, int esz) {
     return (cols * esz + 127) / 128 * 128 / esz;
 }
 
-// A default plan also carries the plan for the same product on operands
-// repacked into 16-byte aligned rows (gemm_run_ws), when that plan runs a
-// tiled kernel on more than THIN_N_MAX columns (for thinner products the
-// product itself moves about as many bytes as the repack would).
+// A default plan whose kernel needs aligned rows also carries the plan for
+// the same product on operands repacked into 16-byte aligned rows
+// (gemm_run_ws), when that plan runs a tiled kernel on more than THIN_N_MAX
+// columns (for thinner products the product itself moves about as many
+// bytes as the repack would).
 tgemm_plan* gemm_plan_variant(int64_t M, int64_t N, int64_t K, int32_t dtype, int64_t lda, int64_t ldb,
                               int64_t ldc, const tgemm_variant* variant) {
     init_registry();

@@ -260,7 +260,8 @@ class Plan:
             raise TgemmError(rc, last_error())
 
     def workspace_bytes(self, A: int, B: int) -> int:
-        """Workspace bytes gemm_run_ws uses to repack misaligned operands at these addresses."""
+        """Workspace bytes gemm_run_ws uses to repack misaligned operands at these
+        addresses (0 where the plan's kernel reads them in place)."""
         return int(_lib.gemm_workspace_bytes(self._h, ctypes.c_void_p(A), ctypes.c_void_p(B)))
 
     def run_ws_ptr(self, A: int, B: int, C: int, ws: int, ws_bytes: int, stream: int = 0) -> None:
@@ -356,10 +357,11 @@ def gemm(A, B, out=None, variant: Variant | None = None, workspace: bool = True)
     or both int8, row-major (row stride may exceed the row length).  Returns
     C (M, N): float32 for float32/bfloat16 inputs, int32 for int8 inputs.
     ``out`` may be a preallocated row-major C (its row stride is used as ldc).
-    With ``workspace`` (default plans only), operands whose rows are not
-    16-byte aligned are repacked into a device buffer taken from torch's
-    allocator on the current stream (gemm_run_ws); otherwise the kernels that
-    read such rows in place run (gemm_run).
+    Operands whose rows are not 16-byte aligned are read in place by the
+    matrix-core kernels.  With ``workspace`` (default plans only), where the
+    plan's kernel needs aligned rows (fp32) they are repacked into a device
+    buffer taken from torch's allocator on the current stream (gemm_run_ws);
+    otherwise a kernel that reads such rows in place runs (gemm_run).
     """
     import torch
     if not (A.is_cuda and B.is_cuda):
