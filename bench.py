@@ -184,7 +184,10 @@ def cpu_model():
 
 def cpu_baseline(w, A_cpu, B_cpu, budget_s=12.0):
     """The oracle (fp64 / int64 triple loop, OpenMP) on a row sample of the
-    same operands: rows are taken until about `budget_s` of CPU work."""
+    same operands: blocks of rows are taken, passing over A again from its
+    first row when the whole product has been done, until about `budget_s`
+    of CPU work.  Products of at most 2 GFLOP are also timed whole on one
+    thread (`single_thread_s`)."""
     import numpy as np
 
     import oracle
@@ -194,22 +197,38 @@ def cpu_baseline(w, A_cpu, B_cpu, budget_s=12.0):
     t = 0.0
     done_rows = 0
     total_t = 0.0
+    start = 0
     while True:
-        Ao = inputs.as_oracle_array(A_cpu[done_rows:done_rows + rows])
+        n = min(rows, w.M - start)
+        Ao = inputs.as_oracle_array(A_cpu[start:start + n])
         t0 = time.perf_counter()
         oracle.gemm(Ao, Bo, w.dtype)
         t = time.perf_counter() - t0
-        done_rows += rows
+        done_rows += n
+        start = (start + n) % w.M
         total_t += t
-        if total_t >= budget_s or done_rows >= w.M:
+        if total_t >= budget_s:
             break
         left = budget_s - total_t
-        rows = int(min(w.M - done_rows, max(8, rows * min(4.0, left / max(t, 1e-3)))))
+        rows = int(max(8, min(w.M, rows * min(4.0, left / max(t, 1e-3)))))
     flops = 2.0 * done_rows * w.N * w.K
-    return {"value": flops / total_t / 1e12, "unit": "TFLOPS" if w.dtype != "i8" else "TOPS",
-            "cores": oracle.num_threads(), "cpu_model": cpu_model(), "kind": "oracle",
-            "sample": "first %d of %d rows of A times all of B (%s %dx%dx%d), %.1f s" % (
-                done_rows, w.M, w.dtype, w.M, w.N, w.K, total_t)}
+    passes = done_rows / w.M
+    sample = ("%.2f passes over all %d rows of A" % (passes, w.M) if passes >= 1 else
+              "first %d of %d rows of A" % (done_rows, w.M))
+    rec = {"value": flops / total_t / 1e12, "unit": "TFLOPS" if w.dtype != "i8" else "TOPS",
+           "cores": oracle.num_threads(), "cpu_model": cpu_model(), "kind": "oracle",
+           "sample": "%s times all of B (%s %dx%dx%d), %.1f s" % (sample, w.dtype, w.M, w.N, w.K, total_t)}
+    if 2.0 * w.M * w.N * w.K <= 2e9:
+        threads = oracle.num_threads()
+        oracle.set_num_threads(1)
+        try:
+            Ao = inputs.as_oracle_array(A_cpu)
+            t0 = time.perf_counter()
+            oracle.gemm(Ao, Bo, w.dtype)
+            rec["single_thread_s"] = round(time.perf_counter() - t0, 4)
+        finally:
+            oracle.set_num_threads(threads)
+    return rec
 
 
 def lds_probe(torch, lib, workgroups=2048, reps=2048, rounds=8, launches=3):
