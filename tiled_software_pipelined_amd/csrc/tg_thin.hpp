@@ -20,9 +20,10 @@
 // keep V times the bytes in flight and take K / KC round trips instead of
 // K / 512.  The lanes' partial sums are added across the wave at the end.
 //
-// Products of two bf16 values are exact in fp32 and are summed in fp32;
-// int8 products are summed exactly in int32.  The order of the fp32 sum
-// differs from a single chain over k (per lane, then across lanes).
+// Products of two bf16 values are exact in fp32 and are summed in fp32, two
+// at a time (v_dot2c_f32_bf16); int8 products four at a time, exactly, in
+// int32 (v_dot4c_i32_i8).  The order of the fp32 sum differs from a single
+// chain over k (per lane in pairs, then across lanes).
 #pragma once
 
 #include <type_traits>
@@ -60,10 +61,12 @@ struct ThinGemm {
     static constexpr int V = V_ ? V_ : (NB <= 4 ? 9 : NB <= 8 ? 4 : 2);
     static constexpr int KS = 64 * KE;           // k per sub-chunk
     static constexpr int KC = V * KS;            // k per chunk
-    // LDS: the chunk's B rows, NB elements each, as V x 64 runs of KE rows
-    // (run r = sub-chunk r / 64, lane r % 64), each lane's run read back as
-    // 16-byte pieces: runs are padded to an odd number of 16-byte pieces, so
-    // that the 16 lanes of one read fall on distinct banks
+    // LDS: the chunk's B block as V x 64 runs of KE rows (run r = sub-chunk
+    // r / 64, lane r % 64), each run column by column (the KE values of
+    // column j at j KE), so that a lane reads a column as one 16-byte (int8:
+    // 8-byte) piece whose dwords pair (quad) consecutive k like its piece of
+    // A; runs are padded to an odd number of 16-byte pieces, so that the 16
+    // lanes of one read fall on distinct banks
     static constexpr int RUN_PIECES = (KE * NB * ESZ + 15) / 16;
     static constexpr int LANE_ELEMS = (RUN_PIECES | 1) * 16 / ESZ;
     static constexpr int SLOT_ELEMS = V * 64 * LANE_ELEMS;
@@ -73,18 +76,6 @@ struct ThinGemm {
     static constexpr int BVPT = BV ? (KC * BV + NT - 1) / NT : 1;
     static constexpr int LDS_BYTES = 2 * SLOT_ELEMS * ESZ;
     typedef typename std::conditional<DT == 1, i32x4, i32x2>::type AVec;
-
-    __device__ static __forceinline__ Acc widen(T v) {
-        if constexpr (DT == 1) return __uint_as_float((uint32_t)v << 16);
-        else return (int32_t)v;
-    }
-
-    // element e (a constant in the unrolled loops) of a lane's A piece
-    __device__ static __forceinline__ Acc elem(const AVec& v, int e) {
-        const uint32_t w = (uint32_t)v[e / (4 / ESZ)];
-        if constexpr (DT == 1) return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
-        else return (int32_t)(w << (24 - 8 * (e & 3))) >> 24;
-    }
 
     __device__ static __forceinline__ Acc wave_sum(Acc v) {
 #pragma unroll
@@ -147,15 +138,21 @@ struct ThinGemm {
         }
     }
 
+    // A piece of CE16 columns of one row goes to CE16 columns of its run.
+    static constexpr int CE16 = 16 / ESZ;
     __device__ static __forceinline__ void store_b_vec(TG_LDS T* slot, const i32x4 (&bw)[BVPT]) {
         if constexpr (BV > 0) {
 #pragma unroll
             for (int q = 0; q < BVPT; ++q) {
                 const int idx = q * NT + threadIdx.x;
                 const int kk = idx / BV, p = idx % BV;
-                if (in_block<KC * BV>(q, idx))
-                    *reinterpret_cast<TG_LDS i32x4*>(slot + (kk / KE) * LANE_ELEMS + (kk % KE) * NB +
-                                                     p * (16 / ESZ)) = bw[q];
+                if (in_block<KC * BV>(q, idx)) {
+                    union { i32x4 v; T e[CE16]; } u;
+                    u.v = bw[q];
+                    TG_LDS T* run = slot + (kk / KE) * LANE_ELEMS + kk % KE;
+#pragma unroll
+                    for (int e = 0; e < CE16; ++e) run[(p * CE16 + e) * KE] = u.e[e];
+                }
             }
         }
     }
@@ -165,80 +162,32 @@ struct ThinGemm {
         for (int q = 0; q < BPT; ++q) {
             const int idx = q * NT + threadIdx.x;
             const int kk = idx / NB, j = idx % NB;
-            if (in_block<KC * NB>(q, idx)) slot[(kk / KE) * LANE_ELEMS + (kk % KE) * NB + j] = bv[q];
+            if (in_block<KC * NB>(q, idx)) slot[(kk / KE) * LANE_ELEMS + j * KE + kk % KE] = bv[q];
         }
     }
 
-    // Sub-chunk v of the chunk in `slot` times this lane's A elements of it.
-    // The lane's KE x NB block of B is contiguous in LDS (16-byte aligned):
-    // read as 16-byte (8-byte) pieces, not element by element.
-    static constexpr int BLK_BYTES = KE * NB * ESZ;
-    static constexpr int BLK_WORDS = BLK_BYTES / 4;
+    // Sub-chunk v of the chunk in `slot` times this lane's A elements of it:
+    // per column one read of its KE values and KE/2 dot products of two bf16
+    // pairs (int8: KE/4 of four-byte quads, exact) with the lane's piece of
+    // each row of A.
     __device__ static __forceinline__ void multiply(Acc (&acc)[ROWS][NB], const AVec (&av)[ROWS],
                                                     const TG_LDS T* slot, int v, int lane) {
         const TG_LDS T* mine = slot + (v * 64 + lane) * LANE_ELEMS;
-        if constexpr (NB * ESZ >= 16) {
-            // rows of the block in whole 16-byte pieces: one row (k) at a
-            // time, so that only NB values of B are live
-            constexpr int PR = NB * ESZ / 16;  // pieces per row
+        constexpr int WORDS = (int)(sizeof(AVec) / 4);
 #pragma unroll
-            for (int e = 0; e < KE; ++e) {
-                uint32_t w[4 * PR];
+        for (int j = 0; j < NB; ++j) {
+            const AVec b = *reinterpret_cast<const TG_LDS AVec*>(mine + j * KE);
 #pragma unroll
-                for (int q = 0; q < PR; ++q) {
-                    const i32x4 x = reinterpret_cast<const TG_LDS i32x4*>(mine)[e * PR + q];
-                    w[4 * q] = x.x; w[4 * q + 1] = x.y; w[4 * q + 2] = x.z; w[4 * q + 3] = x.w;
+            for (int i = 0; i < ROWS; ++i)
+#pragma unroll
+                for (int q = 0; q < WORDS; ++q) {
+                    if constexpr (DT == 1)
+                        acc[i][j] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, (uint32_t)av[i][q]),
+                                                                    __builtin_bit_cast(bf16x2, (uint32_t)b[q]),
+                                                                    acc[i][j], false);
+                    else
+                        acc[i][j] = __builtin_amdgcn_sdot4(av[i][q], b[q], acc[i][j], false);
                 }
-                Acc b[NB];
-#pragma unroll
-                for (int j = 0; j < NB; ++j) {
-                    const uint32_t word = w[j / (4 / ESZ)];
-                    if constexpr (DT == 1) b[j] = __uint_as_float((j & 1) ? (word & 0xffff0000u) : (word << 16));
-                    else b[j] = (int32_t)(word << (24 - 8 * (j & 3))) >> 24;
-                }
-#pragma unroll
-                for (int i = 0; i < ROWS; ++i) {
-                    const Acc a = elem(av[i], e);
-#pragma unroll
-                    for (int j = 0; j < NB; ++j) {
-                        if constexpr (DT == 1) acc[i][j] = __builtin_fmaf(a, b[j], acc[i][j]);
-                        else acc[i][j] += a * b[j];
-                    }
-                }
-            }
-            return;
-        }
-        uint32_t w[BLK_WORDS];
-        if constexpr (BLK_BYTES % 16 == 0) {
-#pragma unroll
-            for (int q = 0; q < BLK_BYTES / 16; ++q) {
-                const i32x4 x = reinterpret_cast<const TG_LDS i32x4*>(mine)[q];
-                w[4 * q] = x.x; w[4 * q + 1] = x.y; w[4 * q + 2] = x.z; w[4 * q + 3] = x.w;
-            }
-        } else {
-            static_assert(BLK_BYTES == 8, "int8, one column: 8 bytes");
-            const i32x2 x = reinterpret_cast<const TG_LDS i32x2*>(mine)[0];
-            w[0] = x.x; w[1] = x.y;
-        }
-#pragma unroll
-        for (int e = 0; e < KE; ++e) {
-            Acc b[NB];
-#pragma unroll
-            for (int j = 0; j < NB; ++j) {
-                const int idx = e * NB + j;  // element of the block
-                const uint32_t word = w[idx / (4 / ESZ)];
-                if constexpr (DT == 1) b[j] = __uint_as_float((idx & 1) ? (word & 0xffff0000u) : (word << 16));
-                else b[j] = (int32_t)(word << (24 - 8 * (idx & 3))) >> 24;
-            }
-#pragma unroll
-            for (int i = 0; i < ROWS; ++i) {
-                const Acc a = elem(av[i], e);
-#pragma unroll
-                for (int j = 0; j < NB; ++j) {
-                    if constexpr (DT == 1) acc[i][j] = __builtin_fmaf(a, b[j], acc[i][j]);
-                    else acc[i][j] += a * b[j];
-                }
-            }
         }
     }
 
