@@ -393,6 +393,25 @@ def test_thin_kernel(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "i8"])
+def test_thin_kernel_rows_per_wave(dtype):
+    # larger M: thin kernels with 2 and 4 rows of C per wave (the planner
+    # keeps about 256 workgroups), M not a multiple of a workgroup's rows,
+    # B's rows in 16-byte pieces that run into the next row (its last row by
+    # element) and element by element, unaligned views on exact buffers
+    cols = [(1, 3), (3, 3), (7, 7)] + ([(13, 13), (9, 11)] if dtype == "i8" else [])
+    for (M, rows) in [(8200, 2), (16500, 4)]:
+        for (N, ldb) in cols:
+            K = 777
+            name = tl.plan_for(M, N, K, DT[dtype], K + 1, ldb, N).info().name.decode()
+            assert name.endswith("_r%d" % rows) and "thin" in name, (M, N, name)
+            A = inputs.operand(KIND[dtype], M, K, 201 + N)
+            B = inputs.operand(KIND[dtype], K, N, 202 + N)
+            print("thin rows", dtype, M, N, K, ldb, name, flush=True)
+            C = _run_views(_exact_device_view(A, K + 1, 1), _exact_device_view(B, ldb, 1), None)
+            _assert_parity(C, A, B, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "i8"])
 def test_split_plans(dtype):
     # the main tiled kernel on the first N - r columns, the thin kernel on
     # the last r, with aligned and unaligned B and exactly sized buffers

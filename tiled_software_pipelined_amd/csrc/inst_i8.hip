@@ -42,6 +42,16 @@ void register_i8(void (*add)(const KernelEntry&)) {
     add(thin_entry<2, 4>());
     add(thin_entry<2, 8>());
     add(thin_entry<2, 16>());
+    add(thin_entry<2, 1, false, 2>());
+    add(thin_entry<2, 2, false, 2>());
+    add(thin_entry<2, 4, false, 2>());
+    add(thin_entry<2, 8, false, 2>());
+    add(thin_entry<2, 16, false, 2>());
+    add(thin_entry<2, 1, false, 4>());
+    add(thin_entry<2, 2, false, 4>());
+    add(thin_entry<2, 4, false, 4>());
+    add(thin_entry<2, 8, false, 4>());
+    add(thin_entry<2, 16, false, 4>());
     // unlisted: the register-staged defaults reading rows that are not
     // 16-byte aligned (A only, B only, both)
     add(mfma_entry<T, 256, 256, 128, 2, 4, 2, LD_VGPR, LY_XOR, AC_WIDE, FR_REUSE, 2, 1>(2));

@@ -111,10 +111,11 @@ KernelEntry naive_entry() {
 // contiguous B column (N = 1, ldb = 1): 256-thread workgroups of 4 rows
 // (4095 x 1 x 4104 bf16: 6.8 us against 7.3 with 1024 threads; with B's
 // column strided the 1024-thread kernel takes 11.4 us against 21.8).
-template <int DT, int NB, bool COL = false>
+// ROWS: rows of C per wave (the planner takes more for larger M).
+template <int DT, int NB, bool COL = false, int ROWS = 1>
 KernelEntry thin_entry() {
-    static_assert(!COL || NB == 1, "the contiguous-column twin has one column");
-    typedef typename std::conditional<COL, ThinGemm<DT, 1, 1, 9, 256>, ThinGemm<DT, NB>>::type K;
+    static_assert(!COL || (NB == 1 && ROWS == 1), "the contiguous-column twin has one column, one row per wave");
+    typedef typename std::conditional<COL, ThinGemm<DT, 1, 1, 9, 256>, ThinGemm<DT, NB, ROWS>>::type K;
     KernelEntry e{};
     e.dtype = DT;
     e.family = FAM_THIN;
@@ -141,7 +142,10 @@ KernelEntry thin_entry() {
     e.lane_map = 1;
     e.fn = gemm_kernel<K, K::WAVES>;
     e.thin_col = COL;
-    snprintf(e.name, sizeof e.name, COL ? "%s_thin_n%d_col" : "%s_thin_n%d", dtype_tag(DT), NB);
+    if (ROWS > 1)
+        snprintf(e.name, sizeof e.name, "%s_thin_n%d_r%d", dtype_tag(DT), NB, ROWS);
+    else
+        snprintf(e.name, sizeof e.name, COL ? "%s_thin_n%d_col" : "%s_thin_n%d", dtype_tag(DT), NB);
     return e;
 }
 

@@ -10,9 +10,12 @@
 // sub-chunks of 512, and in each every lane takes 8 consecutive k, one
 // 16-byte (bf16) or 8-byte (int8) load per row at any alignment (element
 // loads only where the 8 would cross K).  The chunk's KC x NB block of B is
-// loaded once per workgroup (element loads from clamped, valid addresses,
-// zero past K and N; whole 16-byte pieces of its rows when N is a whole
-// number of them) and shared through LDS.  The loads of chunk c+1 (A into registers, B into
+// loaded once per workgroup and shared through LDS: where a row of NB
+// columns is whole 16-byte pieces, by 16-byte loads of each row at any
+// alignment (columns N..NB-1 then hold the next row's first values, which
+// only reach columns of C that are not stored; B's last row, whose pieces
+// could run past the matrix, is loaded element by element once, up front),
+// otherwise element by element from valid addresses, zero past K and N.  The loads of chunk c+1 (A into registers, B into
 // registers then LDS) are issued before chunk c is multiplied - the
 // register-staged double buffer of the GEMM page, section 9 - and one
 // barrier per chunk orders the LDS slots.  With so little arithmetic per
@@ -57,8 +60,16 @@ struct ThinGemm {
     static constexpr int ESZ = sizeof(T);
     static constexpr int KE = 8;                 // consecutive k per lane per sub-chunk
     // sub-chunks per chunk (registers: V x ROWS pieces of A per lane; 9 of 512
-    // cover K up to 4608 in one chunk)
-    static constexpr int V = V_ ? V_ : (NB <= 4 ? 9 : NB <= 8 ? 4 : 2);
+    // cover K up to 4608 in one chunk; int8 pieces are half as wide, so 9
+    // fit up to 8 columns: 4095 x 8 x 4104 9.2 us against 11.4 with 4)
+    // With more rows per wave (for M large enough to keep ~256 workgroups)
+    // the registers hold fewer sub-chunks: 2 rows 4 (2 from 8 bf16 columns),
+    // 4 rows 2 (1); 16384 x N x 4104: bf16 N = 8 45.8 -> 36.7 us with 4 rows,
+    // int8 N = 7 42.1 -> 25.4; 8192 x 8 x 4104 bf16 24.4 -> 20.3 with 2
+    static constexpr bool NARROW = NB <= 4 || (NB <= 8 && ESZ == 1);
+    static constexpr int V = V_ ? V_
+                                : ROWS == 1 ? (NARROW ? 9 : NB <= 8 ? 4 : 2)
+                                            : ROWS == 2 ? (NARROW ? 4 : 2) : (NARROW ? 2 : 1);
     static constexpr int KS = 64 * KE;           // k per sub-chunk
     static constexpr int KC = V * KS;            // k per chunk
     // LDS: the chunk's B block as V x 64 runs of KE rows (run r = sub-chunk
@@ -123,8 +134,9 @@ struct ThinGemm {
         }
     }
 
-    // The same block in 16-byte pieces (B rows aligned, N a whole number of
-    // pieces: N == NB); piece q*NT + tid is row (q*NT + tid) / BV.
+    // The same block in 16-byte pieces of NB columns at any alignment
+    // (NB <= ldb + N: a row's pieces end within the next row), rows below
+    // K - 1 only; piece q*NT + tid is row (q*NT + tid) / BV.
     __device__ static __forceinline__ void load_b_vec(i32x4 (&bw)[BVPT], const GemmArgs& g, int kc0) {
         if constexpr (BV > 0) {
             const T* B = static_cast<const T*>(g.B);
@@ -133,22 +145,43 @@ struct ThinGemm {
                 const int idx = q * NT + threadIdx.x;
                 const int k = kc0 + idx / BV, p = idx % BV;
                 bw[q] = load_or_zero(reinterpret_cast<const i32x4*>(B + (int64_t)k * g.ldb + p * (16 / ESZ)),
-                                     in_block<KC * BV>(q, idx) && k < g.K);
+                                     in_block<KC * BV>(q, idx) && k < g.K - 1);
             }
         }
     }
 
+    // B's last row, columns 0..NB-1, zero past N (element loads, once).
+    struct LastRow {
+        i32x4 v[BV > 0 ? BV : 1];
+    };
+    __device__ static __forceinline__ LastRow load_last_row(const GemmArgs& g) {
+        const T* B = static_cast<const T*>(g.B);
+        union { LastRow r; T e[(BV > 0 ? BV : 1) * 16 / ESZ]; } u;
+#pragma unroll
+        for (int j = 0; j < (BV > 0 ? BV : 1) * 16 / ESZ; ++j)
+            u.e[j] = load_or_zero(B + (int64_t)(g.K - 1) * g.ldb + j, j < g.N);
+        return u.r;
+    }
+
     // A piece of CE16 columns of one row goes to CE16 columns of its run.
+    // kk_last: the chunk row that is B's last row (its pieces from `last`).
     static constexpr int CE16 = 16 / ESZ;
-    __device__ static __forceinline__ void store_b_vec(TG_LDS T* slot, const i32x4 (&bw)[BVPT]) {
+    __device__ static __forceinline__ void store_b_vec(TG_LDS T* slot, const i32x4 (&bw)[BVPT], const LastRow& last,
+                                                       int kk_last) {
         if constexpr (BV > 0) {
 #pragma unroll
             for (int q = 0; q < BVPT; ++q) {
                 const int idx = q * NT + threadIdx.x;
                 const int kk = idx / BV, p = idx % BV;
                 if (in_block<KC * BV>(q, idx)) {
+                    // (selects, not an index: a private array indexed by a
+                    // lane value would be moved to LDS)
+                    i32x4 lv = last.v[0];
+#pragma unroll
+                    for (int t = 1; t < BV; ++t)
+                        if (p == t) lv = last.v[t];
                     union { i32x4 v; T e[CE16]; } u;
-                    u.v = bw[q];
+                    u.v = kk == kk_last ? lv : bw[q];
                     TG_LDS T* run = slot + (kk / KE) * LANE_ELEMS + kk % KE;
 #pragma unroll
                     for (int e = 0; e < CE16; ++e) run[(p * CE16 + e) * KE] = u.e[e];
@@ -195,8 +228,9 @@ struct ThinGemm {
 
     // The rows of C of workgroup `block` (rows block * BM ..).  A in
     // 16-byte (int8: 8-byte) pieces at any alignment (element loads only
-    // past K); B in whole 16-byte pieces of its rows when N is a whole
-    // number of pieces (b_guard == 0), element by element otherwise.
+    // past K); B in 16-byte pieces of its rows where NB columns are whole
+    // pieces and b_guard == 0 (the host's NB <= ldb + N), element by element
+    // otherwise.
     __device__ static __forceinline__ void run_block(const GemmArgs& g, int block) {
         __shared__ __attribute__((aligned(16))) T lds[2 * SLOT_ELEMS];
         TG_LDS T* slots = (TG_LDS T*)(lds);
@@ -218,8 +252,9 @@ struct ThinGemm {
         else load_b(r, g, kc0);
     }
     template <bool BVEC>
-    __device__ static __forceinline__ void store_b_any(TG_LDS T* slot, const BRegsOf<BVEC>& r) {
-        if constexpr (BVEC) store_b_vec(slot, r);
+    __device__ static __forceinline__ void store_b_any(TG_LDS T* slot, const BRegsOf<BVEC>& r, const LastRow& last,
+                                                       int kk_last) {
+        if constexpr (BVEC) store_b_vec(slot, r, last, kk_last);
         else store_b(slot, r);
     }
 
@@ -249,13 +284,15 @@ struct ThinGemm {
 
         const int chunks = (g.K + KC - 1) / KC;
         AVec av[V][ROWS];
+        LastRow last{};
+        if constexpr (BVEC) last = load_last_row(g);
         {
             BRegs b;
             load_b_any<BVEC>(b, g, 0);
 #pragma unroll
             for (int v = 0; v < V; ++v)
                 if (v * KS < g.K) load_a(av[v], rowp, v * KS + lane * KE, g.K);
-            store_b_any<BVEC>(slots, b);
+            store_b_any<BVEC>(slots, b, last, g.K - 1);
             wait_lds_then_barrier();
         }
         for (int c = 0; c < chunks; ++c) {
@@ -269,7 +306,7 @@ struct ThinGemm {
                 if (more && (c + 1) * KC + v * KS < g.K)
                     load_a(av[v], rowp, (c + 1) * KC + v * KS + lane * KE, g.K);
             }
-            if (more) store_b_any<BVEC>(slots + ((c + 1) & 1) * SLOT_ELEMS, b);
+            if (more) store_b_any<BVEC>(slots + ((c + 1) & 1) * SLOT_ELEMS, b, last, g.K - 1 - (c + 1) * KC);
             wait_lds_then_barrier();
         }
 

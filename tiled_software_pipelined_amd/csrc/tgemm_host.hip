@@ -80,6 +80,14 @@ void ld_guards(const KernelEntry& e, int64_t N, int64_t lda, int64_t ldb, int32_
     }
     const int esz = elem_size(e.dtype);
     const int per = bytes / esz;  // elements per access
+    if (e.family == tg::FAM_THIN) {
+        // the thin kernel reads 16-byte pieces of e.bn columns from every B
+        // row but the last (which it loads by element): they stay within
+        // the matrix when e.bn <= ldb + N, reaching at most into the next row
+        *ga = 0;
+        *gb = e.bn > ldb + N;
+        return;
+    }
     if (any_alignment(e)) {
         // rows of any alignment; the last chunk of a B row must still end at N
         *ga = 0;
@@ -200,12 +208,23 @@ const KernelEntry* default_entry(int dtype, int64_t M, int64_t N, int64_t K, int
         // time: 4096 x 1 x 4096 in 11 us against 95 us).  With aligned rows
         // the direct-loader tiles are as fast or faster (4096 x 16 x 4096:
         // 17.7 us against 23.8).
-        // (one column: the contiguous-column twin exactly when ldb = 1)
+        // (one column: the contiguous-column twin exactly when ldb = 1).
+        // Of the kernels of that width, the most rows per workgroup that
+        // still give 256 workgroups (one per compute unit), else the fewest:
+        // every workgroup stages all of B, and fewer, fuller workgroups
+        // stage it less often (16384 x 8 x 4104 bf16: 36.7 us with 64 rows
+        // against 45.8 with 16; 4095 rows keep 16: 11.7 against 15.8 with 32).
         const KernelEntry* best = nullptr;
-        for (const KernelEntry& e : g_reg[dtype])
-            if (e.family == tg::FAM_THIN && e.bn >= N && (!best || e.bn < best->bn) &&
-                (N > 1 || (e.thin_col != 0) == (ldb == 1)))
+        for (const KernelEntry& e : g_reg[dtype]) {
+            if (e.family != tg::FAM_THIN || e.bn < N || (N == 1 && (e.thin_col != 0) != (ldb == 1))) continue;
+            if (!best || e.bn < best->bn) {
                 best = &e;
+                continue;
+            }
+            if (e.bn != best->bn) continue;
+            const bool fills = (M + e.bm - 1) / e.bm >= 256, best_fills = (M + best->bm - 1) / best->bm >= 256;
+            if (fills ? (!best_fills || e.bm > best->bm) : (!best_fills && e.bm < best->bm)) best = &e;
+        }
         if (best) return best;
     }
     const int64_t short_k = i8 ? 2048 : 1024;
