@@ -259,24 +259,27 @@ def test_default_tile_follows_the_round_model():
 
 
 def test_thin_products_use_the_thin_kernel():
-    # N <= 16 where the direct loader cannot read B (fewer than one whole
-    # 16-byte piece per row): the thin kernel of the smallest width that
-    # covers N; otherwise the direct-loader tile, whatever the rows' alignment
+    # N <= 16 (bf16, int8), whatever the rows' alignment: from 2 columns the
+    # matrix-core thin kernel of the smallest width that covers N (bf16 4,
+    # 8, 16; int8 8, 16), one column the vector one (its contiguous-column
+    # twin exactly when ldb = 1); 17 columns and more the tiles
     for dtype in (tl.BF16, tl.I8):
-        cases = [(1, 1, 1), (1, 5, 1), (7, 7, 8), (3, 64, 4)] + ([(9, 9, 16)] if dtype == tl.I8 else [])
+        cases = [(1, 1, 1), (1, 5, 1), (7, 7, 8), (3, 64, 4 if dtype == tl.BF16 else 8), (9, 9, 16), (16, 32, 16),
+                 (16, 17, 16), (8, 8, 8 if dtype == tl.BF16 else 8)]
         for N, ldb, width in cases:
             info = tl.Plan(4096, N, 4096, dtype, ldb=ldb).info()
             assert b"thin" in info.name and info.n_main == N, (dtype, N, ldb)
-            # rows per workgroup: 16 waves of one row; the contiguous-column
-            # twin (N = 1, ldb = 1) 4 waves of one row
+            assert (b"thin_mma" in info.name) == (N >= 2), info.name
+            # rows per workgroup: 16 waves sharing 16 rows (matrix cores) or
+            # holding one row each; the contiguous-column twin 4 waves of one row
             rows = 4 if (N, ldb) == (1, 1) else 16
             assert info.variant.tile_n == width and info.variant.tile_m == rows and info.grid == 4096 // rows
             assert info.name.endswith(b"_col") == ((N, ldb) == (1, 1))
-        assert b"thin" not in tl.Plan(4096, 16, 4096, dtype, ldb=32).info().name
-        assert b"thin" not in tl.Plan(4096, 16, 4096, dtype, ldb=17).info().name
         assert b"thin" not in tl.Plan(4096, 17, 4096, dtype, ldb=17).info().name
-    # bf16 from 8 columns (one whole piece) on: the direct-loader tile
-    assert b"thin" not in tl.Plan(4096, 9, 4096, tl.BF16, ldb=9).info().name
+    # the matrix-core kernel's B pieces of NB columns must end within the
+    # next row (NB <= ldb + N): a single column with ldb = 2 keeps the
+    # vector kernel
+    assert b"thin_n1" in tl.Plan(4096, 1, 4096, tl.BF16, ldb=2).info().name
     # fp32 keeps its one-fma-chain-per-output kernel
     assert b"thin" not in tl.Plan(4096, 4, 4096, tl.F32).info().name
 

@@ -373,9 +373,9 @@ def test_streaming_and_plain_C_stores_agree(dtype):
 
 @pytest.mark.parametrize("dtype", ["bf16", "i8"])
 def test_thin_kernel(dtype):
-    # N <= 16: the thin kernel (rows per wave, lanes along K, a cross-lane
-    # sum) where B's rows hold less than one 16-byte piece, the direct-loader
-    # tile otherwise (whatever the alignment); offset pointers and K tails
+    # N <= 16: the thin kernels (from 2 columns on the matrix cores, one
+    # column on the vector ALUs), whatever the alignment; offset pointers
+    # and K tails
     ce = 8 if dtype == "bf16" else 16
     for (M, N, K) in [(1, 1, 1), (5, 3, 7), (17, 16, 9), (33, 8, 1029), (1000, 1, 4104), (64, 16, 64),
                       (130, 5, 520)]:
@@ -383,9 +383,8 @@ def test_thin_kernel(dtype):
         B = inputs.operand(KIND[dtype], K, N, 102 + K)
         lda_al = (K + ce - 1) // ce * ce
         C_ref, S = _oracle(A, B, dtype)
-        # B rows the direct loader cannot take whole take the thin kernel
-        thin = b"thin" in tl.plan_for(M, N, K, DT[dtype], K + 1, N + 3, N).info().name
-        assert thin == (N < ce), (M, N, K)
+        name = tl.plan_for(M, N, K, DT[dtype], K + 1, N + 3, N).info().name
+        assert b"thin" in name and (b"thin_mma" in name) == (N >= 2), (M, N, K, name)
         for (lda, oa, ldb, ob) in [(lda_al, 0, N, 0), (K + 1, 1, N + 3, 1), (lda_al, ce - 1, N, 0), (K, 0, N, 0)]:
             C = _run_views(_exact_device_view(A, lda, oa), _exact_device_view(B, ldb, ob), None)
             ok, rep = check(C.numpy(), C_ref, S, dtype, K)

@@ -174,8 +174,7 @@ def test_binding_uses_workspace_by_default():
 @pytest.mark.parametrize("a_off", [0, 1])
 def test_split_plan_reads_unaligned_rows_in_place(dtype, r, a_off):
     # 2048 x (2048 + r): 256 whole 128 x 128 tiles plus r columns for the
-    # thin kernel (or, for 8 or 16 columns that are whole 16-byte pieces, a
-    # small direct-copy tile).  B's rows (ldb = N + 1) are never 16-byte
+    # thin kernel.  B's rows (ldb = N + 1) are never 16-byte
     # aligned and, with a_off = 1, neither is A's pointer: every kernel reads
     # them in place, so the plan asks for no workspace and gemm_run_ws is
     # gemm_run.  The oracle's values (K = 264: a partial last slice).

@@ -51,23 +51,21 @@ void register_bf16(void (*add)(const KernelEntry&)) {
     add(mfma_entry<T, 128, 128, 32, 2, 2, 3, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2, 0, CST_MFMA, false, RD_B64>(1));
     add(mfma_entry<T, 128, 128, 32, 2, 2, 3, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2, 0, CST_MFMA, false, RD_B128>(1));
     add(naive_entry<1>());
-    // unlisted: thin products (N <= 16) and split-plan remainders
+    // unlisted: thin products (N <= 16) and split-plan remainders: one
+    // column on the vector ALUs, 2..16 on the matrix cores
     add(thin_entry<1, 1>());
     add(thin_entry<1, 1, true>());
-    add(thin_entry<1, 2>());
-    add(thin_entry<1, 4>());
-    add(thin_entry<1, 8>());
-    add(thin_entry<1, 16>());
     add(thin_entry<1, 1, false, 2>());
-    add(thin_entry<1, 2, false, 2>());
-    add(thin_entry<1, 4, false, 2>());
-    add(thin_entry<1, 8, false, 2>());
-    add(thin_entry<1, 16, false, 2>());
     add(thin_entry<1, 1, false, 4>());
-    add(thin_entry<1, 2, false, 4>());
-    add(thin_entry<1, 4, false, 4>());
-    add(thin_entry<1, 8, false, 4>());
-    add(thin_entry<1, 16, false, 4>());
+    add(thin_mma_entry<1, 4, 1>());
+    add(thin_mma_entry<1, 8, 1>());
+    add(thin_mma_entry<1, 16, 1>());
+    add(thin_mma_entry<1, 4, 2>());
+    add(thin_mma_entry<1, 8, 2>());
+    add(thin_mma_entry<1, 16, 2>());
+    add(thin_mma_entry<1, 4, 4>());
+    add(thin_mma_entry<1, 8, 4>());
+    add(thin_mma_entry<1, 16, 4>());
     // unlisted: the register-staged defaults reading rows that are not
     // 16-byte aligned (A only, B only, both)
     add(mfma_entry<T, 256, 256, 64, 2, 4, 2, LD_VGPR, LY_XOR, AC_WIDE, FR_REUSE, 2, 1>(1));

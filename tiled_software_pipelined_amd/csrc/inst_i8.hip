@@ -35,23 +35,26 @@ void register_i8(void (*add)(const KernelEntry&)) {
     add(mfma_entry<T, 128, 128, 64, 2, 2, 3, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2, 0, CST_MFMA, false, RD_B64>(2));
     add(mfma_entry<T, 128, 128, 64, 2, 2, 3, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2, 0, CST_MFMA, false, RD_B128>(2));
     add(naive_entry<2>());
-    // unlisted: thin products (N <= 16) and split-plan remainders
+    // unlisted: thin products (N <= 16) and split-plan remainders: up to 4
+    // columns on the vector ALUs where B's rows are too short for the
+    // matrix-core kernel's 8-byte pieces (8 > ldb + N), one column always;
+    // otherwise the matrix cores
     add(thin_entry<2, 1>());
-    add(thin_entry<2, 1, true>());
     add(thin_entry<2, 2>());
     add(thin_entry<2, 4>());
-    add(thin_entry<2, 8>());
-    add(thin_entry<2, 16>());
     add(thin_entry<2, 1, false, 2>());
     add(thin_entry<2, 2, false, 2>());
     add(thin_entry<2, 4, false, 2>());
-    add(thin_entry<2, 8, false, 2>());
-    add(thin_entry<2, 16, false, 2>());
     add(thin_entry<2, 1, false, 4>());
     add(thin_entry<2, 2, false, 4>());
     add(thin_entry<2, 4, false, 4>());
-    add(thin_entry<2, 8, false, 4>());
-    add(thin_entry<2, 16, false, 4>());
+    add(thin_entry<2, 1, true>());
+    add(thin_mma_entry<2, 8, 1>());
+    add(thin_mma_entry<2, 16, 1>());
+    add(thin_mma_entry<2, 8, 2>());
+    add(thin_mma_entry<2, 16, 2>());
+    add(thin_mma_entry<2, 8, 4>());
+    add(thin_mma_entry<2, 16, 4>());
     // unlisted: the register-staged defaults reading rows that are not
     // 16-byte aligned (A only, B only, both)
     add(mfma_entry<T, 256, 256, 128, 2, 4, 2, LD_VGPR, LY_XOR, AC_WIDE, FR_REUSE, 2, 1>(2));

@@ -76,6 +76,7 @@ struct KernelEntry {
     KernelFn fn;
     KernelFn rem_fn;       // the twin that also computes column N of an N + 1 wide product (else NULL)
     int thin_col;          // thin kernels: 1 = the twin for a contiguous B column (N = 1, ldb = 1)
+    int thin_mma;          // thin kernels: 1 = on the matrix cores (B rows read as NB-column pieces)
     char name[96];
 };
 

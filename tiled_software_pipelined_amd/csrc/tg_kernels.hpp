@@ -8,6 +8,7 @@
 #include "tg_f32.hpp"
 #include "tg_mfma.hpp"
 #include "tg_thin.hpp"
+#include "tg_thin_mfma.hpp"
 
 namespace tg {
 
@@ -199,6 +200,56 @@ KernelEntry f32_flags_entry() {
 template <int S, int BK = 8, int TILE = 128, int TILE_N = TILE>
 KernelEntry f32_entry() {
     return f32_flags_entry<S, F_TRANS_A | F_PAD_A | F_QUARTERS | F_VEC_STORE, BK, TILE, TILE_N>();
+}
+
+// The matrix-core thin kernel (bf16 NB 4, 8, 16; int8 8, 16): unlisted,
+// preferred by the planner for 2..16 columns whose B rows allow its 8- or
+// 16-byte row pieces (NB <= ldb + N).  RB: 16-row blocks per workgroup (the
+// planner takes the most that still give 256 workgroups).  P, the matrix
+// steps per wave per chunk: as many as two B slots leave room for in LDS,
+// at most 9 (16 x 9 steps of 64 bytes cover K = 4608 bf16 in one chunk);
+// with more row blocks the measured best (x 7 x 4104 bf16, x 9 x 4104
+// int8): 2 blocks 6 bf16 (8192 rows: 15.0 us against 16.2 with 4 or 2), 4
+// int8 (9.5); 4 blocks 1 bf16 (16384 rows: 26.5 us against 35.6 with 2 and
+// 42.0 with 3), 2 int8 (17.7 against 18.3 with 3 and 19.6 with 1).
+template <int DT, int NB, int RB>
+KernelEntry thin_mma_entry() {
+    constexpr int P1 = 163824 / (2048 * NB) < 9 ? 163824 / (2048 * NB) : 9;
+    constexpr int PR = RB == 1 ? 9 : RB == 2 ? (DT == 1 ? 6 : 4) : (DT == 1 ? 1 : 2);
+    constexpr int P = P1 < PR ? P1 : PR;
+    typedef ThinMfma<DT, NB, RB, P> K;
+    static_assert(K::LDS_BYTES <= 163840, "LDS");
+    KernelEntry e{};
+    e.dtype = DT;
+    e.family = FAM_THIN;
+    e.bm = K::BM;
+    e.bn = K::BN;
+    e.bk = K::KC;  // K per chunk
+    e.stages = 2;
+    e.loader = LD_VGPR;
+    e.layout = LY_PLAIN;
+    e.access = AC_WIDE;
+    e.frag = FR_REUSE;
+    e.wm = K::NT / 64;
+    e.wn = 1;
+    e.gload_bytes = 16;  // A in 16-byte pieces at any alignment; B in 8- or 16-byte row pieces
+    e.threads = K::NT;
+    e.lds_bytes = K::LDS_BYTES;
+    e.loads_per_stage = P * RB + K::BPT;
+    e.shift_mask = 3;  // any alignment; B only where NB <= ldb + N (the planner checks)
+    e.listed = 0;
+    e.tail_ok = 1;
+    e.waves_per_simd = K::WAVES;
+    e.copy_sched = 1;
+    e.frag_read = 0;  // transposing reads of B
+    e.lane_map = 1;
+    e.fn = gemm_kernel<K, K::WAVES>;
+    e.thin_mma = 1;
+    if (RB > 1)
+        snprintf(e.name, sizeof e.name, "%s_thin_mma_n%d_r%d", dtype_tag(DT), NB, RB);
+    else
+        snprintf(e.name, sizeof e.name, "%s_thin_mma_n%d", dtype_tag(DT), NB);
+    return e;
 }
 
 }  // namespace tg

@@ -1,7 +1,9 @@
-// Thin-N GEMM (N <= THIN_N_MAX) for bf16 and int8: C = A x B when B has only
-// a few columns - a matrix-vector product in all but name, and the narrow
-// remainder of a split plan (the last N mod BN columns of a shape whose
-// last tile column would otherwise add a nearly empty round of workgroups).
+// Thin-N GEMM on the vector ALUs for bf16 and int8: C = A x B when B has one
+// column (or, int8, up to 4 whose rows are too short for the matrix-core
+// thin kernel's 8-byte pieces) - a matrix-vector product in all but name,
+// and the narrow remainder of a split plan (the last N mod BN columns of a
+// shape whose last tile column would otherwise add a nearly empty round of
+// workgroups).  Wider B goes to tg_thin_mfma.hpp.
 //
 // A tiled kernel is the wrong shape here: a grid of M / 64 workgroups, each
 // running the whole K loop alone on its compute unit, waits on one slice's
@@ -10,12 +12,8 @@
 // sub-chunks of 512, and in each every lane takes 8 consecutive k, one
 // 16-byte (bf16) or 8-byte (int8) load per row at any alignment (element
 // loads only where the 8 would cross K).  The chunk's KC x NB block of B is
-// loaded once per workgroup and shared through LDS: where a row of NB
-// columns is whole 16-byte pieces, by 16-byte loads of each row at any
-// alignment (columns N..NB-1 then hold the next row's first values, which
-// only reach columns of C that are not stored; B's last row, whose pieces
-// could run past the matrix, is loaded element by element once, up front),
-// otherwise element by element from valid addresses, zero past K and N.  The loads of chunk c+1 (A into registers, B into
+// loaded once per workgroup, element by element from valid addresses (zero
+// past K and N), and shared through LDS.  The loads of chunk c+1 (A into registers, B into
 // registers then LDS) are issued before chunk c is multiplied - the
 // register-staged double buffer of the GEMM page, section 9 - and one
 // barrier per chunk orders the LDS slots.  With so little arithmetic per
@@ -42,6 +40,7 @@ template <int DT, int NB, int ROWS_ = 0, int V_ = 0, int NT_ = 1024>
 struct ThinGemm {
     static_assert(NB >= 1 && NB <= THIN_N_MAX && (NB & (NB - 1)) == 0, "NB: a power of two up to 16");
     typedef typename std::conditional<DT == 1, uint16_t, int8_t>::type T;
+    static_assert(NB * sizeof(T) < 16, "B rows of whole 16-byte pieces: the matrix-core thin kernel");
     typedef typename std::conditional<DT == 1, float, int32_t>::type Acc;
     static constexpr int NT = NT_;
     static_assert(NT % 64 == 0 && NT <= 1024, "whole waves");
@@ -60,16 +59,11 @@ struct ThinGemm {
     static constexpr int ESZ = sizeof(T);
     static constexpr int KE = 8;                 // consecutive k per lane per sub-chunk
     // sub-chunks per chunk (registers: V x ROWS pieces of A per lane; 9 of 512
-    // cover K up to 4608 in one chunk; int8 pieces are half as wide, so 9
-    // fit up to 8 columns: 4095 x 8 x 4104 9.2 us against 11.4 with 4)
-    // With more rows per wave (for M large enough to keep ~256 workgroups)
-    // the registers hold fewer sub-chunks: 2 rows 4 (2 from 8 bf16 columns),
-    // 4 rows 2 (1); 16384 x N x 4104: bf16 N = 8 45.8 -> 36.7 us with 4 rows,
-    // int8 N = 7 42.1 -> 25.4; 8192 x 8 x 4104 bf16 24.4 -> 20.3 with 2
-    static constexpr bool NARROW = NB <= 4 || (NB <= 8 && ESZ == 1);
-    static constexpr int V = V_ ? V_
-                                : ROWS == 1 ? (NARROW ? 9 : NB <= 8 ? 4 : 2)
-                                            : ROWS == 2 ? (NARROW ? 4 : 2) : (NARROW ? 2 : 1);
+    // cover K up to 4608 in one chunk).  With more rows per wave (for M
+    // large enough to keep ~256 workgroups) the registers hold fewer: 2
+    // rows 4, 4 rows 2 (16384 x 3 x 4104 bf16 36.1 -> 31.4 us with 4 rows,
+    // 8192 rows 19.3 -> 17.3 with 2)
+    static constexpr int V = V_ ? V_ : ROWS == 1 ? 9 : ROWS == 2 ? 4 : 2;
     static constexpr int KS = 64 * KE;           // k per sub-chunk
     static constexpr int KC = V * KS;            // k per chunk
     // LDS: the chunk's B block as V x 64 runs of KE rows (run r = sub-chunk
@@ -82,9 +76,6 @@ struct ThinGemm {
     static constexpr int LANE_ELEMS = (RUN_PIECES | 1) * 16 / ESZ;
     static constexpr int SLOT_ELEMS = V * 64 * LANE_ELEMS;
     static constexpr int BPT = (KC * NB + NT - 1) / NT;  // B elements each thread stages per chunk
-    // with B rows in whole aligned 16-byte pieces: pieces per row, per thread
-    static constexpr int BV = NB * ESZ >= 16 ? NB * ESZ / 16 : 0;
-    static constexpr int BVPT = BV ? (KC * BV + NT - 1) / NT : 1;
     static constexpr int LDS_BYTES = 2 * SLOT_ELEMS * ESZ;
     typedef typename std::conditional<DT == 1, i32x4, i32x2>::type AVec;
 
@@ -134,62 +125,6 @@ struct ThinGemm {
         }
     }
 
-    // The same block in 16-byte pieces of NB columns at any alignment
-    // (NB <= ldb + N: a row's pieces end within the next row), rows below
-    // K - 1 only; piece q*NT + tid is row (q*NT + tid) / BV.
-    __device__ static __forceinline__ void load_b_vec(i32x4 (&bw)[BVPT], const GemmArgs& g, int kc0) {
-        if constexpr (BV > 0) {
-            const T* B = static_cast<const T*>(g.B);
-#pragma unroll
-            for (int q = 0; q < BVPT; ++q) {
-                const int idx = q * NT + threadIdx.x;
-                const int k = kc0 + idx / BV, p = idx % BV;
-                bw[q] = load_or_zero(reinterpret_cast<const i32x4*>(B + (int64_t)k * g.ldb + p * (16 / ESZ)),
-                                     in_block<KC * BV>(q, idx) && k < g.K - 1);
-            }
-        }
-    }
-
-    // B's last row, columns 0..NB-1, zero past N (element loads, once).
-    struct LastRow {
-        i32x4 v[BV > 0 ? BV : 1];
-    };
-    __device__ static __forceinline__ LastRow load_last_row(const GemmArgs& g) {
-        const T* B = static_cast<const T*>(g.B);
-        union { LastRow r; T e[(BV > 0 ? BV : 1) * 16 / ESZ]; } u;
-#pragma unroll
-        for (int j = 0; j < (BV > 0 ? BV : 1) * 16 / ESZ; ++j)
-            u.e[j] = load_or_zero(B + (int64_t)(g.K - 1) * g.ldb + j, j < g.N);
-        return u.r;
-    }
-
-    // A piece of CE16 columns of one row goes to CE16 columns of its run.
-    // kk_last: the chunk row that is B's last row (its pieces from `last`).
-    static constexpr int CE16 = 16 / ESZ;
-    __device__ static __forceinline__ void store_b_vec(TG_LDS T* slot, const i32x4 (&bw)[BVPT], const LastRow& last,
-                                                       int kk_last) {
-        if constexpr (BV > 0) {
-#pragma unroll
-            for (int q = 0; q < BVPT; ++q) {
-                const int idx = q * NT + threadIdx.x;
-                const int kk = idx / BV, p = idx % BV;
-                if (in_block<KC * BV>(q, idx)) {
-                    // (selects, not an index: a private array indexed by a
-                    // lane value would be moved to LDS)
-                    i32x4 lv = last.v[0];
-#pragma unroll
-                    for (int t = 1; t < BV; ++t)
-                        if (p == t) lv = last.v[t];
-                    union { i32x4 v; T e[CE16]; } u;
-                    u.v = kk == kk_last ? lv : bw[q];
-                    TG_LDS T* run = slot + (kk / KE) * LANE_ELEMS + kk % KE;
-#pragma unroll
-                    for (int e = 0; e < CE16; ++e) run[(p * CE16 + e) * KE] = u.e[e];
-                }
-            }
-        }
-    }
-
     __device__ static __forceinline__ void store_b(TG_LDS T* slot, const T (&bv)[BPT]) {
 #pragma unroll
         for (int q = 0; q < BPT; ++q) {
@@ -226,40 +161,9 @@ struct ThinGemm {
 
     __device__ static __forceinline__ void run(const GemmArgs& g) { run_block(g, blockIdx.x); }
 
-    // The rows of C of workgroup `block` (rows block * BM ..).  A in
-    // 16-byte (int8: 8-byte) pieces at any alignment (element loads only
-    // past K); B in 16-byte pieces of its rows where NB columns are whole
-    // pieces and b_guard == 0 (the host's NB <= ldb + N), element by element
-    // otherwise.
-    __device__ static __forceinline__ void run_block(const GemmArgs& g, int block) {
-        __shared__ __attribute__((aligned(16))) T lds[2 * SLOT_ELEMS];
-        TG_LDS T* slots = (TG_LDS T*)(lds);
-        if constexpr (BV > 0) {
-            if (g.b_guard == 0) {
-                run_k<true>(g, slots, block);
-                return;
-            }
-        }
-        run_k<false>(g, slots, block);
-    }
-
-    // The chunk's B block (zero past K and N) into registers, then `slot`.
-    template <bool BVEC>
-    using BRegsOf = typename std::conditional<BVEC, i32x4[BVPT], T[BPT]>::type;
-    template <bool BVEC>
-    __device__ static __forceinline__ void load_b_any(BRegsOf<BVEC>& r, const GemmArgs& g, int kc0) {
-        if constexpr (BVEC) load_b_vec(r, g, kc0);
-        else load_b(r, g, kc0);
-    }
-    template <bool BVEC>
-    __device__ static __forceinline__ void store_b_any(TG_LDS T* slot, const BRegsOf<BVEC>& r, const LastRow& last,
-                                                       int kk_last) {
-        if constexpr (BVEC) store_b_vec(slot, r, last, kk_last);
-        else store_b(slot, r);
-    }
-
-    // A lane's 8 elements of a row that lie inside K take one wide load
-    // (element loads with zero fill otherwise).  Before the first wait, the chunk-0 loads of
+    // The rows of C of workgroup `block` (rows block * BM ..).  A lane's 8
+    // elements of a row that lie inside K take one wide load (element loads
+    // with zero fill otherwise).  Before the first wait, the chunk-0 loads of
     // B and then of every sub-chunk of A are all in flight; B is staged into
     // LDS (waiting only for its own loads, issued first), and each
     // sub-chunk's A registers are refilled with the next chunk's as soon as
@@ -267,9 +171,9 @@ struct ThinGemm {
     // other slot: the register-staged double buffer of the GEMM page,
     // section 9, one barrier per chunk.  Sub-chunks that start at or past K
     // hold only zeros and are not multiplied.
-    template <bool BVEC>
-    __device__ static __forceinline__ void run_k(const GemmArgs& g, TG_LDS T* slots, int block) {
-        typedef BRegsOf<BVEC> BRegs;
+    __device__ static __forceinline__ void run_block(const GemmArgs& g, int block) {
+        __shared__ __attribute__((aligned(16))) T lds[2 * SLOT_ELEMS];
+        TG_LDS T* slots = (TG_LDS T*)(lds);
         const T* A = static_cast<const T*>(g.A);
         const int lane = lane_id(), wave = wave_id();
         const int r0 = block * BM + wave * ROWS;
@@ -284,29 +188,27 @@ struct ThinGemm {
 
         const int chunks = (g.K + KC - 1) / KC;
         AVec av[V][ROWS];
-        LastRow last{};
-        if constexpr (BVEC) last = load_last_row(g);
         {
-            BRegs b;
-            load_b_any<BVEC>(b, g, 0);
+            T b[BPT];
+            load_b(b, g, 0);
 #pragma unroll
             for (int v = 0; v < V; ++v)
                 if (v * KS < g.K) load_a(av[v], rowp, v * KS + lane * KE, g.K);
-            store_b_any<BVEC>(slots, b, last, g.K - 1);
+            store_b(slots, b);
             wait_lds_then_barrier();
         }
         for (int c = 0; c < chunks; ++c) {
             const bool more = c + 1 < chunks;
             const TG_LDS T* cur = slots + (c & 1) * SLOT_ELEMS;
-            BRegs b;
-            if (more) load_b_any<BVEC>(b, g, (c + 1) * KC);
+            T b[BPT];
+            if (more) load_b(b, g, (c + 1) * KC);
 #pragma unroll
             for (int v = 0; v < V; ++v) {
                 if (c * KC + v * KS < g.K) multiply(acc, av[v], cur, v, lane);
                 if (more && (c + 1) * KC + v * KS < g.K)
                     load_a(av[v], rowp, (c + 1) * KC + v * KS + lane * KE, g.K);
             }
-            if (more) store_b_any<BVEC>(slots + ((c + 1) & 1) * SLOT_ELEMS, b, last, g.K - 1 - (c + 1) * KC);
+            if (more) store_b(slots + ((c + 1) & 1) * SLOT_ELEMS, b);
             wait_lds_then_barrier();
         }
 

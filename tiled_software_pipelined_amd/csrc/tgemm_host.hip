@@ -81,11 +81,12 @@ void ld_guards(const KernelEntry& e, int64_t N, int64_t lda, int64_t ldb, int32_
     const int esz = elem_size(e.dtype);
     const int per = bytes / esz;  // elements per access
     if (e.family == tg::FAM_THIN) {
-        // the thin kernel reads 16-byte pieces of e.bn columns from every B
-        // row but the last (which it loads by element): they stay within
-        // the matrix when e.bn <= ldb + N, reaching at most into the next row
+        // the matrix-core thin kernel reads pieces of e.bn columns from every
+        // B row but the last (which it loads by element): they stay within
+        // the matrix when e.bn <= ldb + N, reaching at most into the next
+        // row (the vector one reads B by element)
         *ga = 0;
-        *gb = e.bn > ldb + N;
+        *gb = e.thin_mma && e.bn > ldb + N;
         return;
     }
     if (any_alignment(e)) {
@@ -154,11 +155,11 @@ bool accepts(const KernelEntry& e, bool ga, bool gb, int64_t N) {
 //  - 128 x 128 (three per unit): ceil(tiles / 256) tiles on the busiest
 //    unit, each `mid_tile` of a 256 x 256 round.
 // So 4096 x 4096 keeps 256 x 256 (1 vs 4 x 0.33) and 4096 x 4352 (272 big
-// tiles, 1088 small ones) takes 128 x 128 (1.64 vs 5 x 0.33).  With
+// tiles, 1088 small ones) takes 128 x 128 (1.64 vs 5 x 0.33).  Products
+// of at most 16 columns (bf16, int8) take the thin kernels.  With
 // `guarded` (the fallback choice for operands the direct loader cannot take:
-// B narrower than one 16-byte piece, leading dimensions beyond its 32-bit
-// offsets) the candidates are the thin kernel and the register-staged
-// tiles.  Short K also takes 128 x 128: with one
+// leading dimensions beyond its 32-bit offsets) the candidates are the
+// register-staged tiles.  Short K also takes 128 x 128: with one
 // round of 256 x 256 tiles every workgroup writes its C tile at the same
 // moment, unoverlapped, and at short K that write is most of the work.
 double big_rounds(int64_t tiles) {
@@ -201,29 +202,33 @@ const KernelEntry* default_entry(int dtype, int64_t M, int64_t N, int64_t K, int
     v.lds_layout = TGEMM_LDS_XOR;
     v.waves_m = 2;
     const bool i8 = dtype == TGEMM_I8;
-    if (N <= tg::THIN_N_MAX && guarded) {
-        // a few columns whose rows cannot go through the direct loader: the
-        // thin kernel with the fewest columns that cover N (the register-
-        // staged tiles would leave each workgroup waiting on one slice at a
-        // time: 4096 x 1 x 4096 in 11 us against 95 us).  With aligned rows
-        // the direct-loader tiles are as fast or faster (4096 x 16 x 4096:
-        // 17.7 us against 23.8).
+    if (N <= tg::THIN_N_MAX) {
+        // a few columns: the thin kernel with the fewest columns that cover
+        // N (a tile would leave each workgroup waiting on one slice at a
+        // time, and compute mostly columns past N: 4096 x 1 x 4096 in 11 us
+        // against 95 us register-staged; 4095 x 8 x 4104 bf16 7.2 us against
+        // 19.5 on the direct loader, 16384 x 16 x 256 5.0 against 7.5; int8
+        // x 16 x 256 loses 0.4-0.6 us at 512-4095 rows)
         // (one column: the contiguous-column twin exactly when ldb = 1).
         // Of the kernels of that width, the most rows per workgroup that
         // still give 256 workgroups (one per compute unit), else the fewest:
         // every workgroup stages all of B, and fewer, fuller workgroups
         // stage it less often (16384 x 8 x 4104 bf16: 36.7 us with 64 rows
         // against 45.8 with 16; 4095 rows keep 16: 11.7 against 15.8 with 32).
+        // The matrix-core kernels first, for 2..16 columns whose B rows take
+        // their NB-column pieces (NB <= ldb + N).
         const KernelEntry* best = nullptr;
+        auto better = [&](const KernelEntry& e) {
+            if (!best) return true;
+            if (e.thin_mma != best->thin_mma) return e.thin_mma > best->thin_mma;
+            if (e.bn != best->bn) return e.bn < best->bn;
+            const bool fills = (M + e.bm - 1) / e.bm >= 256, best_fills = (M + best->bm - 1) / best->bm >= 256;
+            return fills ? (!best_fills || e.bm > best->bm) : (!best_fills && e.bm < best->bm);
+        };
         for (const KernelEntry& e : g_reg[dtype]) {
             if (e.family != tg::FAM_THIN || e.bn < N || (N == 1 && (e.thin_col != 0) != (ldb == 1))) continue;
-            if (!best || e.bn < best->bn) {
-                best = &e;
-                continue;
-            }
-            if (e.bn != best->bn) continue;
-            const bool fills = (M + e.bm - 1) / e.bm >= 256, best_fills = (M + best->bm - 1) / best->bm >= 256;
-            if (fills ? (!best_fills || e.bm > best->bm) : (!best_fills && e.bm < best->bm)) best = &e;
+            if (e.thin_mma && (N < 2 || e.bn > ldb + N)) continue;
+            if (better(e)) best = &e;
         }
         if (best) return best;
     }
@@ -464,6 +469,13 @@ tgemm_plan* make_plan(int64_t M, int64_t N, int64_t K, int32_t dtype, int64_t ld
     if (ga || gb) {
         e = fb[ga | (gb << 1)];
         ld_guards(*e, N, lda, ldb, &ga, &gb);
+    }
+    if (e->thin_mma && gb) {
+        // the matrix-core thin kernel reads NB-column pieces of B's rows,
+        // which with NB > ldb + N could run past the matrix (the planner
+        // never picks it then)
+        set_err("%s cannot read B with ldb=%lld", e->name, (long long)ldb);
+        return nullptr;
     }
     const int64_t tiles_m = (M + e->bm - 1) / e->bm, tiles_n = (N + e->bn - 1) / e->bn;
     if (tiles_m * tiles_n > INT_MAX) {
