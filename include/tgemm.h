@@ -193,10 +193,15 @@ tgemm_plan* gemm_plan_variant(int64_t M, int64_t N, int64_t K, int32_t dtype,
  * takes it), and a leading dimension too large for the direct loader's
  * 32-bit lane offsets (from the plan on).  A B whose N is not a whole number
  * of 16-byte pieces is read in place by the direct loader as well (its last
- * row, and a partial last slice, by element loads).  A default plan one column wider than 16 or more whole 256 x 256
- * tile columns computes that column in the main kernel's K loop; a few more
- * columns go to the thin kernel after the main launch.  Nothing outside
- * [A, A + ((M-1)*lda + K) elements) or the corresponding range of B is read.
+ * row, and a partial last slice, by element loads).  A default bf16 / int8
+ * plan of at most 16 columns runs a thin kernel: from 2 columns on the
+ * matrix cores (16 x 16 output blocks whose columns past N are computed and
+ * dropped; B's rows read as pieces of 4 to 16 columns that may reach into
+ * the next row), one column on the vector ALUs.  A default plan one column
+ * wider than 16 or more whole 256 x 256 tile columns computes that column
+ * in the main kernel's K loop; a few more columns go to a thin kernel after
+ * the main launch.  Nothing outside [A, A + ((M-1)*lda + K) elements) or
+ * the corresponding range of B is read.
  * C outside its M x N window is not written.  The launch is asynchronous:
  * execution errors surface at the stream's next synchronisation.  Returns
  * TGEMM_OK or a TGEMM_E_* code. */
