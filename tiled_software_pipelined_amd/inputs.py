@@ -113,6 +113,8 @@ def workloads() -> dict:
     # the ragged product's last column as a product of its own (a contiguous
     # 4104 x 1 B): the thin kernel, bound by one read of A
     w["bf16_thin_4095x1x4104"] = Workload("bf16_thin_4095x1x4104", "bf16", 4095, 1, 4104, "bf16_uniform", 5300)
+    # eight columns of the same: the matrix-core thin kernel
+    w["bf16_thin_4095x8x4104"] = Workload("bf16_thin_4095x8x4104", "bf16", 4095, 8, 4104, "bf16_uniform", 5400)
     # one GPU's share of bf16 4096^3 split over 8 GPUs by rows of A and C
     w["bf16_msplit_512x4096x4096"] = Workload("bf16_msplit_512x4096x4096", "bf16", 512, 4096, 4096,
                                               "bf16_normal", 5200)
