@@ -439,7 +439,14 @@ def clocked_rate(torch, lib, plan, A, B, C, variant):
                              stream)
     torch.cuda.synchronize()
     nv = lib.CLOCK_VALUES
-    c = clocks.cpu().numpy().view("uint64").reshape(CLOCKED_LAUNCHES, -1, nv)
+    # the buffer is sized for the largest grid among the plan's kernels (a
+    # fallback for unaligned rows may use a smaller tile); the operands here
+    # are the plan's own, so its main kernel ran and only its grid's rows
+    # were written
+    grid = plan.info().grid
+    c = clocks.cpu().numpy().view("uint64").reshape(CLOCKED_LAUNCHES, -1, nv)[:, :grid]
+    if not (c[:, :, 1] > 0).all():
+        raise RuntimeError("clocked run: a workgroup of the grid wrote no clock values")
     ghz = lib.clock_ghz(c)
     wg = c.shape[1]
     xcd = [lib.clock_ghz(c[:, x::8]) if x < wg else None for x in range(8)]

@@ -99,6 +99,7 @@ typedef enum tgemm_dtype {
 /* Register tiling (GEMM page, sections 5-6). */
 #define TGEMM_FRAG_REUSE 1       /* each fragment read once per k step, reused across the wave tile */
 #define TGEMM_FRAG_PER_MMA 2     /* both fragments re-read for every matrix-core instruction */
+#define TGEMM_FRAG_SLICE 3       /* as REUSE, with a whole slice's fragments read one slice ahead (direct loader) */
 
 /* C write-back (the SIMT ladder's coalesced write-back step). */
 #define TGEMM_STORE_VECTOR 1     /* 16-byte row pieces */

@@ -175,12 +175,18 @@ def test_default_choice_by_shape():
     assert tl.Plan(512, 4096, 1024, tl.I8).info().variant.tile_m == 128
     assert tl.Plan(512, 4096, 1024, tl.BF16).info().variant.tile_m == 64
     # long K on the 128 x 128 tile: the deeper ring; on the 64 x 64 tile the
-    # 8-slot ring
+    # 8-slot ring (from K = 1024 bf16, 2048 int8) and whole-slice fragment
+    # read-ahead at every K
     assert tl.Plan(2048, 2048, 4096, tl.BF16).info().variant.stages == 4
     for dtype in (tl.BF16, tl.I8):
         small = tl.Plan(512, 512, 4096, dtype).info().variant
-        assert (small.tile_m, small.stages) == (64, 8), dtype
-        assert tl.Plan(512, 512, 1024, dtype).info().variant.stages == 3
+        assert (small.tile_m, small.stages, small.frag) == (64, 8, tl.FRAG_SLICE), dtype
+        assert tl.Plan(512, 512, 512, dtype).info().variant.stages == 3
+        assert tl.Plan(512, 512, 512, dtype).info().variant.frag == tl.FRAG_SLICE
+    assert tl.Plan(512, 512, 1024, tl.BF16).info().variant.stages == 8
+    assert tl.Plan(512, 512, 1024, tl.I8).info().variant.stages == 3
+    # the larger tiles keep reading one K step ahead
+    assert tl.Plan(2048, 2048, 4096, tl.BF16).info().variant.frag == tl.FRAG_REUSE
     small = tl.Plan(512, 512, 512, tl.BF16).info()
     assert (small.variant.tile_m, small.variant.tile_n) == (64, 64) and small.grid == 64
     # fp32: 64 x 64 tiles while 128 x 128 ones would give one per CU or fewer

@@ -50,6 +50,13 @@ void register_bf16(void (*add)(const KernelEntry&)) {
     add(mfma_entry<T, 128, 128, 32, 2, 2, 3, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2, 0, CST_MFMA, false, RD_B32>(1));
     add(mfma_entry<T, 128, 128, 32, 2, 2, 3, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2, 0, CST_MFMA, false, RD_B64>(1));
     add(mfma_entry<T, 128, 128, 32, 2, 2, 3, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2, 0, CST_MFMA, false, RD_B128>(1));
+    // whole-slice fragment read-ahead for tiles whose waves issue one or two
+    // matrix instructions per K step (small grids)
+    add(mfma_entry<T, 64, 64, 64, 2, 2, 8, LD_DIRECT, LY_XOR, AC_WIDE, FR_SLICE, 4>(1));
+    add(mfma_entry<T, 64, 64, 64, 2, 2, 3, LD_DIRECT, LY_XOR, AC_WIDE, FR_SLICE, 4>(1));
+    add(mfma_entry<T, 128, 64, 32, 2, 2, 4, LD_DIRECT, LY_XOR, AC_WIDE, FR_SLICE, 2>(1));
+    add(mfma_entry<T, 64, 128, 32, 2, 2, 4, LD_DIRECT, LY_XOR, AC_WIDE, FR_SLICE, 2>(1));
+    add(mfma_entry<T, 128, 128, 32, 2, 2, 4, LD_DIRECT, LY_XOR, AC_WIDE, FR_SLICE, 2>(1));
     add(naive_entry<1>());
     // unlisted: thin products (N <= 16) and split-plan remainders: one
     // column on the vector ALUs, 2..16 on the matrix cores

@@ -34,6 +34,13 @@ void register_i8(void (*add)(const KernelEntry&)) {
     add(mfma_entry<T, 128, 128, 64, 2, 2, 3, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2, 0, CST_MFMA, false, RD_B32>(2));
     add(mfma_entry<T, 128, 128, 64, 2, 2, 3, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2, 0, CST_MFMA, false, RD_B64>(2));
     add(mfma_entry<T, 128, 128, 64, 2, 2, 3, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2, 0, CST_MFMA, false, RD_B128>(2));
+    // whole-slice fragment read-ahead for tiles whose waves issue one or two
+    // matrix instructions per K step (small grids)
+    add(mfma_entry<T, 64, 64, 128, 2, 2, 8, LD_DIRECT, LY_XOR, AC_WIDE, FR_SLICE, 4>(2));
+    add(mfma_entry<T, 64, 64, 128, 2, 2, 3, LD_DIRECT, LY_XOR, AC_WIDE, FR_SLICE, 4>(2));
+    add(mfma_entry<T, 128, 64, 64, 2, 2, 4, LD_DIRECT, LY_XOR, AC_WIDE, FR_SLICE, 2>(2));
+    add(mfma_entry<T, 64, 128, 64, 2, 2, 4, LD_DIRECT, LY_XOR, AC_WIDE, FR_SLICE, 2>(2));
+    add(mfma_entry<T, 128, 128, 64, 2, 2, 4, LD_DIRECT, LY_XOR, AC_WIDE, FR_SLICE, 2>(2));
     add(naive_entry<2>());
     // unlisted: thin products (N <= 16) and split-plan remainders: up to 4
     // columns on the vector ALUs where B's rows are too short for the

@@ -48,7 +48,9 @@ enum Loader { LD_VGPR = 1, LD_DIRECT = 2 };
 // bytes just before its direct copy is issued (see MfmaGemm::issue_direct_one)
 enum Layout { LY_PLAIN = 1, LY_XOR = 2, LY_XOR_POISON = 3 };
 enum Access { AC_WIDE = 1, AC_NARROW = 2 };
-enum Frag { FR_REUSE = 1, FR_PER_MMA = 2 };
+// FR_SLICE: FR_REUSE with the fragments of a whole slice read one slice
+// ahead (direct loader; see MfmaGemm::slice_ahead)
+enum Frag { FR_REUSE = 1, FR_PER_MMA = 2, FR_SLICE = 3 };
 
 struct KernelEntry {
     int dtype;       // TGEMM_* dtype

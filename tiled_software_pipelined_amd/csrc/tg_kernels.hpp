@@ -66,7 +66,7 @@ KernelEntry mfma_entry(int dtype) {
     snprintf(e.name, sizeof e.name, "%s_t%dx%dx%d_w%dx%d_s%d_%s_%s_%s_%s%s%s%s%s", dtype_tag(dtype), BM, BN,
              BK, WM, WN, S, LD == LD_DIRECT ? "direct" : "vgpr",
              LY == LY_XOR ? "xor" : LY == LY_XOR_POISON ? "xorpoison" : "plain",
-             AC == AC_WIDE ? "wide" : "narrow", FR == FR_REUSE ? "reuse" : "permma",
+             AC == AC_WIDE ? "wide" : "narrow", FR == FR_REUSE ? "reuse" : FR == FR_SLICE ? "slice" : "permma",
              SHIFT == 1 ? "_shiftA" : SHIFT == 2 ? "_shiftB" : SHIFT == 3 ? "_shiftAB" : "",
              CST == CST_SWAP ? "_vst" : "", SPREAD ? "_spread" : "",
              FREAD == RD_AUTO ? "" : FREAD == RD_B32 ? "_rd32" : FREAD == RD_B64 ? "_rd64" :

@@ -145,7 +145,9 @@ struct MfmaGemm {
     static_assert(!DIRECT || WIDE, "direct loads move 16-byte chunks");
     static_assert(DIRECT || STAGES <= 2, "register-staged loader: 1 or 2 slots");
     static_assert(WIDE || (!XOR && !DIRECT), "narrow accesses use the plain layout");
-    static_assert(FRAG == FR_REUSE || !WIDE, "per-instruction fragment reloads only on the narrow rung");
+    static_assert(FRAG != FR_PER_MMA || !WIDE, "per-instruction fragment reloads only on the narrow rung");
+    static_assert(FRAG != FR_SLICE || (DIRECT && STAGES >= 2 && !SPREAD && !REM && !POISON),
+                  "whole-slice read-ahead: the plain direct-loader ring");
     static_assert(N_LD * (STAGES > 2 ? STAGES - 2 : 0) <= 63, "vmcnt range");
     static_assert(!POISON || (DIRECT && STAGES >= 2), "poisoned slots: the direct-loader ring");
     static_assert(SHIFT == 0 || (LOADER == LD_VGPR && WIDE), "shifted loads: register-staged, 16-byte chunks");
@@ -769,6 +771,44 @@ struct MfmaGemm {
                                         wave);
     }
 
+    // ---- whole-slice read-ahead (FR_SLICE) -------------------------------------
+    // With one or two matrix instructions per K step (32 x 32 or 64 x 32
+    // wave tiles), the instruction issued before a K step's fragment reads
+    // is too short to cover their LDS latency, so every K step would wait
+    // for its own reads.  Here F[s] holds K step s of the slice being
+    // multiplied, and right after step s's matrix instructions the same
+    // registers are refilled with step s of the next slice: each read is
+    // issued a whole slice before its use.  The slice's one barrier follows
+    // step 0's instructions.  By then this wave has read all of its slot
+    // (that happened during the previous slice), so after the barrier no wave
+    // reads the slot any more and the copy of slice t + STAGES may overwrite
+    // it (DMA); and with the wait before it, every wave's copy of slice t+1
+    // has landed, so slice t+1's fragments may be read (NEXT).  Copies of a
+    // slice thus get STAGES - 1 slices to land, as in slice_direct.
+    template <bool NEXT, bool DMA>
+    __device__ static __forceinline__ void slice_ahead(Acc (&acc)[FM][FN], Frags (&F)[KSUB],
+                                                       const TG_LDS char* next_slot, int ahead,
+                                                       const CopyTarget& next, const DirectOffsets& off, int wm0,
+                                                       int wn0, int lane, int wave) {
+        static_assert(NEXT || !DMA, "copies follow the barrier");
+#pragma unroll
+        for (int s = 0; s < KSUB; ++s) {
+#pragma unroll
+            for (int k = 0; k < NM; ++k) {
+                const int i = k / FN, j = k % FN;
+                acc[i][j] = mma(F[s].a[i], F[s].b[j], acc[i][j]);
+            }
+            if constexpr (NEXT) {
+                if (s == 0) wait_slice(ahead);
+                read_frags(F[s], next_slot, s, wm0, wn0, lane);
+            }
+            if constexpr (DMA) {
+                if (s == 0) issue_direct(next.slot, off, next.ca, next.cb, wave);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
     // Matrix-core K steps of the partial last slice (K - full BK > 0 values).
     __device__ static __forceinline__ int tail_steps(const GemmArgs& g, int full) {
         return (g.K - full * BK + Tr::MK - 1) / Tr::MK;
@@ -787,7 +827,7 @@ struct MfmaGemm {
     __device__ static __forceinline__ void compute(const TG_LDS char* slot, Acc (&acc)[FM][FN],
                                                    int wm0, int wn0, int lane, int ksteps = KSUB) {
         const TG_LDS char* bslot = slot + A_BYTES;
-        if constexpr (FRAG == FR_REUSE) {
+        if constexpr (FRAG != FR_PER_MMA) {
             Frags f[2];
             read_frags(f[0], slot, 0, wm0, wn0, lane);
 #pragma unroll
@@ -1044,6 +1084,44 @@ struct MfmaGemm {
                     wait_lds_then_barrier();
                     compute(smem, acc, wm0, wn0, lane, tail_steps(g, full));
                 }
+            } else if constexpr (FRAG == FR_SLICE) {
+            // Prologue as below, then all of slice 0's fragments; slice t
+            // reads slice t+1's fragments and starts slice t + STAGES.
+            auto target = [&](int sl) {
+                return CopyTarget{smem + (sl % STAGES) * SLOT, abase + sl * astep, bbase + sl * bstep,
+                                  cbase + sl * bstep};
+            };
+            const CopyTarget none{smem, abase, bbase, cbase};
+            Frags F[KSUB];
+#pragma unroll
+            for (int s = 0; s < STAGES - 1; ++s)
+                if (s < full) issue_slice(s);
+            if (full > 0) {
+                wait_slice(min(STAGES - 2, full - 1));
+                if (STAGES - 1 < full) issue_slice(STAGES - 1);
+#pragma unroll
+                for (int s = 0; s < KSUB; ++s) read_frags(F[s], smem, s, wm0, wn0, lane);
+            }
+            int t = 0;
+            for (; t + STAGES < full; ++t)
+                slice_ahead<true, true>(acc, F, smem + ((t + 1) % STAGES) * SLOT, STAGES - 2, target(t + STAGES),
+                                        off, wm0, wn0, lane, wave);
+            for (; t + 1 < full; ++t)
+                slice_ahead<true, false>(acc, F, smem + ((t + 1) % STAGES) * SLOT, min(STAGES - 2, full - 2 - t),
+                                         none, off, wm0, wn0, lane, wave);
+            if (t < full) slice_ahead<false, false>(acc, F, smem, 0, none, off, wm0, wn0, lane, wave);
+            if (full < tiles) {
+                // K tail into slot full % STAGES.  Every wave passed the last
+                // barrier (in slice full-2; with one full slice, the
+                // prologue's), by which all had finished reading that slot,
+                // and its wait drained the copies; the last slice reads no
+                // LDS.
+                Staged<LM_ELEMENT, LM_ELEMENT> r;
+                load_regs(r, g, m0, n0, full * BK);
+                store_regs(smem + (full % STAGES) * SLOT, r);
+                wait_lds_then_barrier();
+                compute(smem + (full % STAGES) * SLOT, acc, wm0, wn0, lane, tail_steps(g, full));
+            }
             } else {
             // Prologue: slices 0 .. STAGES-2 in flight; once slice 0 is in
             // LDS (barrier), start slice STAGES-1 and read the fragments of

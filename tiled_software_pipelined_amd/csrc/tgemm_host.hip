@@ -280,10 +280,20 @@ const KernelEntry* default_entry(int dtype, int64_t M, int64_t N, int64_t K, int
     // and from K = 1024 for int8 (2048^2 x 4096 24.3 vs 25.4 us, 6144^2 x
     // 1024 57.0 vs 60.9; equal at 2048^2 x 8192); 3 below
     v.stages = pick == 256 || guarded ? 2 : (pick == 128 && K >= (i8 ? 1024 : 512) ? 4 : 3);
-    // 64 x 64 tiles (grids of about one workgroup per compute unit): an
-    // 8-slot ring from K = 2048 (6-20 % faster than 3 slots at 512^2 x
-    // 2048..8192, 768^2 x 4096 and 512 x 1024 x 8192, timed by graph replay)
-    if (pick == 64 && K >= 2048) v.stages = 8;
+    // 64 x 64 tiles (grids of about one workgroup per compute unit): each
+    // wave issues one matrix instruction per K step, too short to cover the
+    // next step's fragment reads, so the fragments of a whole slice are read
+    // one slice ahead (graph replay, bf16, us, reads one step ahead -> one
+    // slice ahead: 512^2 x 4096 19.0 -> 13.9, x 8192 33.3 -> 27.2, x 1024
+    // 7.5 -> 6.6; 1024^2 x 4096 20.0 -> 17.8; 768^2 x 4096 18.6 -> 15.7; int8
+    // 512^2 x 4096 11.2 -> 8.9, x 8192 18.5 -> 13.5); an 8-slot ring from
+    // 1024 bf16 / 2048 int8 values of K (512^2 x 2048 bf16 8.8 vs 10.3 us
+    // with 3 slots, 1024^2 x 1024 6.9 vs 7.2; int8 512^2 x 1024 5.3 vs 5.1,
+    // x 4096 8.9 vs 10.2), 3 below (512^2 x 512 5.1 vs 5.3)
+    if (pick == 64) {
+        v.frag = TGEMM_FRAG_SLICE;
+        if (K >= (i8 ? 2048 : 1024)) v.stages = 8;
+    }
     v.loader = guarded ? TGEMM_LOADER_VGPR : TGEMM_LOADER_DIRECT;
     return find_entry(dtype, v);
 }
@@ -439,6 +449,7 @@ tgemm_plan* make_plan(int64_t M, int64_t N, int64_t K, int32_t dtype, int64_t ld
         entry_to_variant(*e, 0, &r);
         r.loader = TGEMM_LOADER_VGPR;
         r.stages = 2;
+        if (r.frag == TGEMM_FRAG_SLICE) r.frag = TGEMM_FRAG_REUSE;  // a direct-loader schedule
         r.store = 0;
         r.copy_sched = 0;
         r.frag_read = 0;
