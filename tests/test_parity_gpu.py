@@ -347,10 +347,13 @@ def test_shifted_loads_few_slices(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "i8"])
-def test_streaming_and_plain_C_stores_agree(dtype):
-    # C rows 128-byte aligned take non-temporal stores, others plain ones;
-    # both must write the same values and nothing outside the M x N window
-    M, N, K = 300, 256, 192
+@pytest.mark.parametrize("k_bytes", [384, 4160])
+def test_streaming_and_plain_C_stores_agree(dtype, k_bytes):
+    # C rows 128-byte aligned take non-temporal stores (on 256 x 256 tiles
+    # only when K spans at least 4 KiB per row), others plain ones; both must
+    # write the same values and nothing outside the M x N window
+    M, N = 300, 256
+    K = k_bytes // (1 if dtype == "i8" else 2)
     A = inputs.operand(KIND[dtype], M, K, 81)
     B = inputs.operand(KIND[dtype], K, N, 82)
     Ad, Bd = _to_device(A), _to_device(B)

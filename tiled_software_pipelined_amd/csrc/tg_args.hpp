@@ -18,7 +18,7 @@ struct GemmArgs {
     int32_t wg_group;          // <= 0: row-major workgroup order
     int32_t a_guard;           // 1: A rows not 16-byte aligned, for a kernel that needs them aligned
     int32_t b_guard;           // 1: the same for B, or N not a whole number of 16-byte chunks
-    int32_t c_stream;          // 1: C rows 128-byte aligned: non-temporal (streaming) C stores
+    int32_t c_stream;          // 1: non-temporal C stores (C rows 128-byte aligned; 256 x 256 tiles: K >= 4 KiB per row)
     uint64_t* clocks;          // NULL, or 6 values per workgroup (tiled kernels): shader-clock and
                                // 100 MHz real-time counters at its start, at the end of its
                                // K loop, then at its end

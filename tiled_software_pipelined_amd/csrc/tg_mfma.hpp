@@ -1205,10 +1205,12 @@ struct MfmaGemm {
         // row 8 (r/4) + 4 (l/32) + r%4, column l%32 of that 32 x 32 tile, so
         // each store instruction writes two 128-byte row segments.  C is
         // written once and never re-read here: when its rows are 128-byte
-        // aligned each segment is one whole cache line and the stores are
-        // non-temporal; otherwise every segment straddles two lines, and
-        // ordinary stores let the L2 merge the halves before they reach HBM
-        // (about 20 % faster than streaming the partial lines at 4096^3).
+        // aligned each segment is one whole cache line and, for a long K
+        // loop (g.c_stream, set by the host), the stores are non-temporal;
+        // otherwise ordinary stores, which drain a large C faster where the
+        // write is a big share of the launch, and where every segment
+        // straddles two lines let the L2 merge the halves before they reach
+        // HBM (about 20 % faster than streaming the partial lines at 4096^3).
         clk.loop_end(g.clocks);
         Out* C = static_cast<Out*>(g.C);
         const bool inside = (m0 + BM <= g.M) && (n0 + BN <= g.N);

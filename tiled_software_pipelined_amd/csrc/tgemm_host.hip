@@ -697,7 +697,19 @@ int run_impl(const tgemm_plan* p, const void* A, const void* B, void* C, uint64_
     g.wg_group = p->wg_group > g.tiles_m ? g.tiles_m : p->wg_group;
     g.a_guard = ga;
     g.b_guard = gb;
-    g.c_stream = (uintptr_t)C % 128 == 0 && (p->ldc * 4) % 128 == 0;
+    // Streaming (non-temporal) C stores where C's rows are whole cache lines.
+    // The exception: 256 x 256 tiles with a short K loop, where every
+    // workgroup writes its C at the same time and the write is a large share
+    // of the launch; plain stores drain it faster there (graph replay, us,
+    // streaming vs plain: bf16 4096^2 x 512 27.0 vs 26.3, x 1024 39.8 vs
+    // 38.9, x 2048 64.5 vs 64.9, x 4096 114.4 vs 115.8; int8 x 1024 27.0 vs
+    // 26.6, x 2048 40.8 vs 40.1, x 4096 66.0 vs 66.9; bf16 8192^2 x 512
+    // 100.2 vs 99.5), so those stream from 4 KiB of K per row.  Smaller tiles
+    // run in several rounds, one round's writes under the next one's loops,
+    // and keep streaming (bf16 4096^2 x 256 on 128 x 128 tiles: 20.6 us
+    // streaming, 22.1 plain).
+    const bool big_tile = e->bm * e->bn >= 256 * 256;
+    g.c_stream = (uintptr_t)C % 128 == 0 && (p->ldc * 4) % 128 == 0 && (!big_tile || p->K * esz >= 4096);
     if (clocks && e->family == tg::FAM_TILED) {
         // the kernel that runs decides the count (a fallback's tile may differ)
         const int64_t need = tg::CLOCK_VALUES * (int64_t)g.tiles_m * g.tiles_n;
