@@ -87,6 +87,8 @@ void register_bf16(void (*add)(const KernelEntry&)) {
     add(mfma_entry<T, 128, 128, 32, 2, 2, 4, LD_DIRECT, LY_XOR_POISON, AC_WIDE, FR_REUSE, 2>(1));
     add(mfma_entry<T, 64, 128, 32, 2, 2, 4, LD_DIRECT, LY_XOR_POISON, AC_WIDE, FR_REUSE, 2>(1));
     add(mfma_entry<T, 64, 64, 64, 2, 2, 8, LD_DIRECT, LY_XOR_POISON, AC_WIDE, FR_REUSE, 4>(1));
+    add(mfma_entry<T, 64, 64, 64, 2, 2, 8, LD_DIRECT, LY_XOR_POISON, AC_WIDE, FR_SLICE, 4>(1));
+    add(mfma_entry<T, 64, 64, 64, 2, 2, 3, LD_DIRECT, LY_XOR_POISON, AC_WIDE, FR_SLICE, 4>(1));
     // 16-byte C stores from the swapped product (TGEMM_STORE_VECTOR)
     add(mfma_entry<T, 256, 256, 64, 2, 4, 2, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2, 0, CST_SWAP>(1));
     add(mfma_entry<T, 256, 256, 32, 2, 4, 4, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2, 0, CST_SWAP>(1));

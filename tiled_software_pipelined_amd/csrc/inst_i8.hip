@@ -74,6 +74,7 @@ void register_i8(void (*add)(const KernelEntry&)) {
     add(mfma_entry<T, 256, 256, 128, 2, 4, 2, LD_DIRECT, LY_XOR_POISON, AC_WIDE, FR_REUSE, 2>(2));
     add(mfma_entry<T, 128, 128, 64, 2, 2, 4, LD_DIRECT, LY_XOR_POISON, AC_WIDE, FR_REUSE, 2>(2));
     add(mfma_entry<T, 64, 64, 128, 2, 2, 8, LD_DIRECT, LY_XOR_POISON, AC_WIDE, FR_REUSE, 4>(2));
+    add(mfma_entry<T, 64, 64, 128, 2, 2, 8, LD_DIRECT, LY_XOR_POISON, AC_WIDE, FR_SLICE, 4>(2));
     // 16-byte C stores from the swapped product (TGEMM_STORE_VECTOR)
     add(mfma_entry<T, 256, 256, 128, 2, 4, 2, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2, 0, CST_SWAP>(2));
     add(mfma_entry<T, 256, 256, 64, 2, 4, 4, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2, 0, CST_SWAP>(2));

@@ -146,7 +146,7 @@ struct MfmaGemm {
     static_assert(DIRECT || STAGES <= 2, "register-staged loader: 1 or 2 slots");
     static_assert(WIDE || (!XOR && !DIRECT), "narrow accesses use the plain layout");
     static_assert(FRAG != FR_PER_MMA || !WIDE, "per-instruction fragment reloads only on the narrow rung");
-    static_assert(FRAG != FR_SLICE || (DIRECT && STAGES >= 2 && !SPREAD && !REM && !POISON),
+    static_assert(FRAG != FR_SLICE || (DIRECT && STAGES >= 2 && !SPREAD && !REM),
                   "whole-slice read-ahead: the plain direct-loader ring");
     static_assert(N_LD * (STAGES > 2 ? STAGES - 2 : 0) <= 63, "vmcnt range");
     static_assert(!POISON || (DIRECT && STAGES >= 2), "poisoned slots: the direct-loader ring");
