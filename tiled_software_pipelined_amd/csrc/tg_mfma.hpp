@@ -177,11 +177,15 @@ struct MfmaGemm {
         else return c;
     }
     // B: row k at k*NB.  A transposing read covers (8/ESZ) consecutive rows
-    // per 16-lane group; XOR the chunk index so those rows (and the
-    // neighbouring group's columns) land on distinct banks.
-    static constexpr int B_RPG = 8 / ESZ;  // rows per 16-lane group of one transposing read
+    // per 16-lane group, and each 32 lanes of it (one LDS pass of 256 bytes)
+    // read 16/B_RPG chunks of each of those rows.  Rows that fall on the same
+    // banks - every row, where a row fills a 256-byte window or more; rows
+    // B_RPW apart, where B_RPW rows share a window - get distinct XOR keys in
+    // the bits above those chunks, so the pass touches every bank once.
+    static constexpr int B_RPG = 8 / ESZ;                   // rows per 16-lane group of one transposing read
+    static constexpr int B_RPW = NB >= LDS_WINDOW ? 1 : LDS_WINDOW / NB;  // B rows per 256-byte window
     __device__ static __forceinline__ int b_chunk(int k, int c) {
-        if constexpr (XOR) return c ^ (((k % B_RPG) * (16 / B_RPG)) & (CB - 1));
+        if constexpr (XOR) return c ^ ((((k % B_RPG) / B_RPW) * (16 / B_RPG)) & (CB - 1));
         else return c;
     }
 
