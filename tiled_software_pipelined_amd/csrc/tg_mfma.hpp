@@ -17,7 +17,10 @@
 //              t+1's first fragments
 //
 // so that the global->LDS copy of later slices overlaps the matrix-core work
-// on slice t.  Two loaders are built (the skill's Step 2 choice):
+// on slice t.  Tiles whose waves issue only one or two matrix instructions
+// per K step read a whole slice's fragments one slice ahead instead
+// (FR_SLICE, slice_ahead), with the slice's barrier in its first K step.
+// Two loaders are built (the skill's Step 2 choice):
 //   LD_VGPR   : 16-byte loads into registers, written to LDS after the
 //               multiply of the current slice (register-staged double buffer,
 //               GEMM page section 9.5);
