@@ -316,6 +316,12 @@ def test_huge_leading_dimension_leaves_the_direct_loader():
     # the default plan of a small shape too
     v = tl.Plan(512, 512, 512, tl.BF16, lda=40_000_000).info().variant
     assert v.loader == tl.LOADER_VGPR
+    # the whole-slice read-ahead is a schedule of the direct loader: the
+    # register-staged fallback reads one K step ahead
+    req = tl.Variant(kernel=tl.KERNEL_TILED, tile_m=64, tile_n=64, tile_k=64, stages=8, frag=tl.FRAG_SLICE)
+    assert tl.Plan(512, 512, 4096, tl.BF16, variant=req).info().variant.frag == tl.FRAG_SLICE
+    v = tl.Plan(512, 512, 4096, tl.BF16, lda=40_000_000, variant=req).info().variant
+    assert v.loader == tl.LOADER_VGPR and v.frag == tl.FRAG_REUSE
 
 
 def test_lds_budget_of_stage_ring():
