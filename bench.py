@@ -13,6 +13,8 @@ Extra modes (not used by the default run):
     --ladder     the ablation ladder of the workload's type, one change per rung
                  (TFLOP/s, gain over the rung it changes, bit identity with the
                  default plan; --ladder-summary writes the table)
+    --late-barrier  the default kernel against its late-barrier twin, in sustained
+                 bursts with each one's shader clock (the power-cap measurement)
     --variants   time every compiled variant of the workload's type
     --sweep      the bf16 shape sweep: the 128x128x32 tile with the register-
                  staged loader (2 slots) and the direct loader (1-4 slots), and
@@ -592,6 +594,57 @@ def run_variants(torch, lib, w, A, B, C, args):
                           "frac_peak": w.flops / ms / 1e9 / PEAK_TFLOPS[w.dtype]}), flush=True)
 
 
+def run_late_barrier(torch, lib, w, A, B, C, args, rounds=6, settle=500, timed=300):
+    """The workload's default kernel against its twin with the slice's
+    barrier half-way through the last K step (copy_sched LATE: the cores idle
+    longer there, everything else the same).  Each is timed in sustained
+    bursts, since the shader clock follows the power drawn over many
+    milliseconds: `settle` launches, then `timed` launches between two HIP
+    events, then clocked launches for the kernel's own shader clock; the two
+    alternate for `rounds` rounds.  One JSON line per burst, then one summary
+    line per kernel (medians) with whether the two wrote the same bits."""
+    code = {"f32": lib.F32, "bf16": lib.BF16, "i8": lib.I8}[w.dtype]
+    kinds = [("default", None), ("late barrier", lib.Variant(kernel=lib.KERNEL_TILED, copy_sched=lib.COPY_LATE))]
+    outs = []
+    for _, v in kinds:
+        C.fill_(-7)
+        lib.gemm(A, B, out=C, variant=v)
+        torch.cuda.synchronize()
+        outs.append(C.clone())
+    same = bool(torch.equal(outs[0], outs[1]))
+    del outs
+    stream = torch.cuda.current_stream()
+    res = {label: {"us": [], "ghz": []} for label, _ in kinds}
+    names = {}
+    for r in range(rounds):
+        for label, v in kinds:
+            plan = lib.plan_for(w.M, w.N, w.K, code, w.K, w.N, w.N, v)
+            names[label] = plan.name
+            for _ in range(settle):
+                lib.gemm(A, B, out=C, variant=v)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(timed):
+                lib.gemm(A, B, out=C, variant=v)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / timed
+            clk = clocked_rate(torch, lib, plan, A, B, C, v)
+            res[label]["us"].append(us)
+            res[label]["ghz"].append(clk["ghz"])
+            print(json.dumps({"mode": "late_barrier", "workload": w.name, "round": r, "kernel": plan.name,
+                              "us": round(us, 2), "ghz": round(clk["ghz"], 3)}), flush=True)
+    for label, _ in kinds:
+        us = sorted(res[label]["us"])[len(res[label]["us"]) // 2]
+        ghz = sorted(res[label]["ghz"])[len(res[label]["ghz"]) // 2]
+        print(json.dumps({"mode": "late_barrier_summary", "workload": w.name, "kernel": names[label],
+                          "median_us": round(us, 2), "median_ghz": round(ghz, 3),
+                          "rate": round(w.flops / us / 1e6, 1), "rate_per_ghz": round(w.flops / us / 1e6 / ghz, 1),
+                          "same_bits_as_default": same, "rounds": rounds, "settle": settle, "timed": timed}),
+              flush=True)
+
+
 SWEEP_VARIANTS = [  # (label, loader, stages) on the 128 x 128 x 32 tile, then the default plan
     ("direct_s1", 2, 1), ("vgpr_s2", 1, 2), ("direct_s2", 2, 2), ("direct_s3", 2, 3), ("direct_s4", 2, 4),
     ("default", None, None)]
@@ -698,6 +751,9 @@ def main():
                     help="with --ladder: also write the rung table as Markdown to PATH")
     ap.add_argument("--variants", action="store_true",
                     help="time every compiled variant of the workload's type")
+    ap.add_argument("--late-barrier", action="store_true",
+                    help="the default kernel against its twin with the slice's barrier later in the last K "
+                         "step, each timed in sustained bursts with its shader clock (one JSON line per burst)")
     ap.add_argument("--sweep", action="store_true",
                     help="the bf16 shape sweep by loader and ring depth (one JSON line per cell)")
     ap.add_argument("--sweep-summary", default="", metavar="PATH",
@@ -762,6 +818,9 @@ def main():
         run_ladder(torch, lib, w, A, B, C, args)
     if args.variants:
         run_variants(torch, lib, w, A, B, C, args)
+    if args.late_barrier:
+        run_late_barrier(torch, lib, w, A, B, C, args)
+        return
     if args.sweep:
         run_sweep(torch, lib, dev, args)
 

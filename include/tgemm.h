@@ -111,6 +111,10 @@ typedef enum tgemm_dtype {
 #define TGEMM_COPY_SPREAD 2      /* part of them there, the rest spread over the K steps of the
                                     next slice (fewer memory instructions between any two
                                     matrix instructions; a shorter lead for the rest) */
+#define TGEMM_COPY_LATE 3        /* as BURST, with the slice's barrier (and the copies and reads
+                                    after it) half-way through the last K step's matrix
+                                    instructions instead of after its second: a measurement
+                                    twin of the 256 x 256 defaults */
 
 /* How operand fragments are read out of LDS (the LDS -> register ladder of
  * the SM80 ablation plan, section 1.1).  Matrix-core kernels: the A fragment

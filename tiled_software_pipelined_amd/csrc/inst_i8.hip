@@ -84,6 +84,10 @@ void register_i8(void (*add)(const KernelEntry&)) {
     add(mfma_entry<T, 256, 256, 64, 2, 2, 4, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 1, 0, CST_SWAP, true>(2));
     add(mfma_entry<T, 256, 256, 128, 2, 4, 2, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2, 0, CST_MFMA, true>(2));
     add(mfma_entry<T, 256, 256, 64, 2, 4, 4, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2, 0, CST_MFMA, true>(2));
+    // the default with the slice's barrier later in the last K step
+    // (TGEMM_COPY_LATE): the power-cap measurement's twin
+    add(mfma_entry<T, 256, 256, 128, 2, 4, 2, LD_DIRECT, LY_XOR, AC_WIDE, FR_REUSE, 2, 0, CST_MFMA, false, RD_AUTO,
+                   false, true>(2));
 }
 
 }  // namespace tg

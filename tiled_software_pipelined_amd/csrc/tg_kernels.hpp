@@ -28,10 +28,11 @@ static const char* dtype_tag(int dt) { return dt == 0 ? "f32" : dt == 1 ? "bf16"
 // of C in the same K loop (MfmaGemm's REM), for split plans.
 template <class Tr, int BM, int BN, int BK, int WM, int WN, int S, int LD, int LY, int AC, int FR,
           int WAVES, int SHIFT = 0, int CST = CST_MFMA, bool SPREAD = false, int FREAD = RD_AUTO,
-          bool WITH_REM = false>
+          bool WITH_REM = false, bool LATE = false>
 KernelEntry mfma_entry(int dtype) {
     static_assert(!SPREAD || LD == LD_DIRECT, "spread copies: the direct loader");
-    typedef MfmaGemm<Tr, BM, BN, BK, WM, WN, S, LD, LY, AC, FR, SHIFT, CST, SPREAD, FREAD> K;
+    static_assert(!(SPREAD && LATE) && !(WITH_REM && LATE), "one copy schedule; no remainder twin");
+    typedef MfmaGemm<Tr, BM, BN, BK, WM, WN, S, LD, LY, AC, FR, SHIFT, CST, SPREAD, FREAD, false, LATE> K;
     KernelEntry e{};
     e.dtype = dtype;
     e.family = FAM_TILED;
@@ -46,7 +47,7 @@ KernelEntry mfma_entry(int dtype) {
     e.wm = WM;
     e.wn = WN;
     e.store = CST == CST_SWAP ? 1 : 2;  // TGEMM_STORE_VECTOR / TGEMM_STORE_SCALAR
-    e.copy_sched = SPREAD ? 2 : 1;      // TGEMM_COPY_SPREAD / TGEMM_COPY_BURST
+    e.copy_sched = LATE ? 3 : SPREAD ? 2 : 1;  // TGEMM_COPY_LATE / _SPREAD / _BURST
     e.lane_map = 1;
     e.frag_read = K::FREAD;             // TGEMM_READ_* (same values as FragRead)
     e.gload_bytes = AC == AC_WIDE ? 16 : 4;
@@ -68,7 +69,7 @@ KernelEntry mfma_entry(int dtype) {
              LY == LY_XOR ? "xor" : LY == LY_XOR_POISON ? "xorpoison" : "plain",
              AC == AC_WIDE ? "wide" : "narrow", FR == FR_REUSE ? "reuse" : FR == FR_SLICE ? "slice" : "permma",
              SHIFT == 1 ? "_shiftA" : SHIFT == 2 ? "_shiftB" : SHIFT == 3 ? "_shiftAB" : "",
-             CST == CST_SWAP ? "_vst" : "", SPREAD ? "_spread" : "",
+             CST == CST_SWAP ? "_vst" : "", SPREAD ? "_spread" : LATE ? "_late" : "",
              FREAD == RD_AUTO ? "" : FREAD == RD_B32 ? "_rd32" : FREAD == RD_B64 ? "_rd64" :
              FREAD == RD_B128 ? "_rd128" : "_rdtr");
     return e;

@@ -92,10 +92,14 @@ enum FragRead { RD_AUTO = 0, RD_B32 = 1, RD_B64 = 2, RD_B128 = 3, RD_TR = 4 };
 
 // SPREAD (direct loader): issue each slice's copies in two parts, the
 // second spread over the K steps of the following slice, instead of all of
-// them right after the slice's barrier (see N1 below).
+// them right after the slice's barrier (see N1 below).  LATE (direct
+// loader, steady ring): the slice's barrier, and the copies and reads that
+// follow it, come after half of the last K step's matrix instructions
+// instead of after its second one (a measurement twin: the cores idle
+// longer at the barrier, with everything else the same).
 template <class Tr, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int LOADER,
           int LAYOUT, int ACCESS, int FRAG, int SHIFT = 0, int CST = CST_MFMA, bool SPREAD = false,
-          int FREAD_ = RD_AUTO, bool REM = false>
+          int FREAD_ = RD_AUTO, bool REM = false, bool LATE = false>
 struct MfmaGemm {
     typedef typename Tr::T T;
     typedef typename Tr::Out Out;
@@ -149,6 +153,7 @@ struct MfmaGemm {
     static_assert(DIRECT || STAGES <= 2, "register-staged loader: 1 or 2 slots");
     static_assert(WIDE || (!XOR && !DIRECT), "narrow accesses use the plain layout");
     static_assert(FRAG != FR_PER_MMA || !WIDE, "per-instruction fragment reloads only on the narrow rung");
+    static_assert(!LATE || (DIRECT && STAGES >= 2 && FRAG != FR_SLICE && !REM), "late barrier: the direct ring");
     static_assert(FRAG != FR_SLICE || (DIRECT && STAGES >= 2 && !SPREAD && !REM),
                   "whole-slice read-ahead: the plain direct-loader ring");
     static_assert(N_LD * (STAGES > 2 ? STAGES - 2 : 0) <= 63, "vmcnt range");
@@ -724,7 +729,7 @@ struct MfmaGemm {
                                                  const DirectOffsets& off, int wm0, int wn0, int lane, int wave) {
         // the barrier follows matrix instruction BAR_K; the memory
         // instructions start after it
-        constexpr int BAR_K = (BARRIER && NM >= 8) ? 1 : 0;
+        constexpr int BAR_K = (BARRIER && NM >= 8) ? (LATE ? NM / 2 : 1) : 0;
         static_assert(BAR_K < NM, "barrier inside the K step");
         static_assert(0 <= DB && DB <= DE && DE <= N_LD, "copy range");
         constexpr int NREAD = READS ? NR : 0;

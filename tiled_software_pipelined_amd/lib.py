@@ -30,7 +30,7 @@ LDS_PLAIN, LDS_XOR, LDS_XOR_POISON = 1, 2, 3
 ACCESS_WIDE, ACCESS_NARROW = 1, 2
 FRAG_REUSE, FRAG_PER_MMA, FRAG_SLICE = 1, 2, 3
 STORE_VECTOR, STORE_SCALAR = 1, 2
-COPY_BURST, COPY_SPREAD = 1, 2
+COPY_BURST, COPY_SPREAD, COPY_LATE = 1, 2, 3
 READ_B32, READ_B64, READ_B128, READ_TR, READ_KVEC = 1, 2, 3, 4, 5
 LANES_BLOCKS, LANES_QUARTERS, LANES_ZORDER, LANES_ZQUARTERS = 1, 2, 3, 4
 ORDER_ROW_MAJOR = -1
