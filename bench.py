@@ -15,6 +15,7 @@ Extra modes (not used by the default run):
                  default plan; --ladder-summary writes the table)
     --late-barrier  the default kernel against its late-barrier twin, in sustained
                  bursts with each one's shader clock (the power-cap measurement)
+    --c-stores   the default plan under each C store policy (auto / streaming / plain)
     --variants   time every compiled variant of the workload's type
     --sweep      the bf16 shape sweep: the 128x128x32 tile with the register-
                  staged loader (2 slots) and the direct loader (1-4 slots), and
@@ -645,6 +646,52 @@ def run_late_barrier(torch, lib, w, A, B, C, args, rounds=6, settle=500, timed=3
               flush=True)
 
 
+def run_c_stores(torch, lib, w, A, B, C, per_graph=20, rounds=15):
+    """The workload's default plan under each C store policy (AUTO, STREAM,
+    PLAIN: tgemm_set_c_store_policy), each captured as one HIP graph of
+    `per_graph` launches (the policy is read when a run is enqueued) and
+    replayed round-robin `rounds` times.  One JSON line per policy: the
+    median per-launch time, and whether its C equals AUTO's bit for bit."""
+    policies = [("auto", lib.C_STORES_AUTO), ("stream", lib.C_STORES_STREAM), ("plain", lib.C_STORES_PLAIN)]
+    graphs, outs = {}, {}
+    try:
+        for label, pol in policies:
+            lib.set_c_store_policy(pol)
+            C.fill_(-7)
+            lib.gemm(A, B, out=C)
+            torch.cuda.synchronize()
+            outs[label] = C.clone()
+            g = torch.cuda.CUDAGraph()
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                with torch.cuda.graph(g, stream=s):
+                    for _ in range(per_graph):
+                        lib.gemm(A, B, out=C)
+            graphs[label] = g
+    finally:
+        lib.set_c_store_policy(lib.C_STORES_AUTO)
+    for g in graphs.values():
+        g.replay()
+    torch.cuda.synchronize()
+    times = {label: [] for label in graphs}
+    for _ in range(rounds):
+        for label, g in graphs.items():
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            e1.synchronize()
+            times[label].append(e0.elapsed_time(e1) * 1e3 / per_graph)
+    kname = lib.plan_for(w.M, w.N, w.K, {"f32": lib.F32, "bf16": lib.BF16, "i8": lib.I8}[w.dtype],
+                         w.K, w.N, w.N).name
+    for label, t in times.items():
+        t.sort()
+        print(json.dumps({"mode": "c_stores", "workload": w.name, "kernel": kname, "policy": label,
+                          "median_us": round(t[len(t) // 2], 2), "min_us": round(t[0], 2),
+                          "same_bits_as_auto": bool(torch.equal(outs[label], outs["auto"]))}), flush=True)
+
+
 SWEEP_VARIANTS = [  # (label, loader, stages) on the 128 x 128 x 32 tile, then the default plan
     ("direct_s1", 2, 1), ("vgpr_s2", 1, 2), ("direct_s2", 2, 2), ("direct_s3", 2, 3), ("direct_s4", 2, 4),
     ("default", None, None)]
@@ -751,6 +798,9 @@ def main():
                     help="with --ladder: also write the rung table as Markdown to PATH")
     ap.add_argument("--variants", action="store_true",
                     help="time every compiled variant of the workload's type")
+    ap.add_argument("--c-stores", action="store_true",
+                    help="the default plan under each C store policy (auto, streaming, plain), timed by "
+                         "HIP-graph replay (one JSON line per policy)")
     ap.add_argument("--late-barrier", action="store_true",
                     help="the default kernel against its twin with the slice's barrier later in the last K "
                          "step, each timed in sustained bursts with its shader clock (one JSON line per burst)")
@@ -820,6 +870,9 @@ def main():
         run_variants(torch, lib, w, A, B, C, args)
     if args.late_barrier:
         run_late_barrier(torch, lib, w, A, B, C, args)
+        return
+    if args.c_stores:
+        run_c_stores(torch, lib, w, A, B, C)
         return
     if args.sweep:
         run_sweep(torch, lib, dev, args)

@@ -267,6 +267,22 @@ int gemm_run_ws(const tgemm_plan* plan, const void* A, const void* B, void* C, v
 #define TGEMM_NOALLOC_MAX_BYTES (64LL << 20)
 int gemm_run_noalloc(const tgemm_plan* plan, const void* A, const void* B, void* C, void* stream);
 
+/* C store policy of the matrix-core kernels that write C from the matrix
+ * instruction's layout, process-wide, for measurement (the GEMM page,
+ * section 2: the write-back as part of the roofline).  AUTO, the default:
+ * non-temporal stores where C's pointer and row stride are 128-byte aligned,
+ * except for 256 x 256 tiles with under 4 KiB of K per row, whose launches
+ * write all of C at once and drain it faster with plain stores.  STREAM:
+ * non-temporal wherever C is 128-byte aligned.  PLAIN: ordinary stores.
+ * The results are the same bits under every policy; only the write path
+ * differs.  Read when a run is enqueued; set it between runs, not while
+ * another host thread enqueues.  Returns the previous policy, or
+ * TGEMM_E_ARG for an unknown one. */
+#define TGEMM_C_STORES_AUTO 0
+#define TGEMM_C_STORES_STREAM 1
+#define TGEMM_C_STORES_PLAIN 2
+int tgemm_set_c_store_policy(int policy);
+
 /* What a plan will launch. */
 typedef struct tgemm_plan_info {
     int64_t M, N, K, lda, ldb, ldc;

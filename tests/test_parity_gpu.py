@@ -375,6 +375,39 @@ def test_streaming_and_plain_C_stores_agree(dtype, k_bytes):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "i8"])
+def test_c_store_policies_agree(dtype):
+    # the 256 x 256 tile at a short K (plain stores under AUTO) and a long
+    # one (streaming): every policy writes the same bits, inside the window
+    # only, on line-aligned and unaligned C
+    M, N = 512, 512
+    v = tl.Variant(kernel=tl.KERNEL_TILED, tile_m=256, tile_n=256, waves_n=4, loader=tl.LOADER_DIRECT)
+    out_dtype = torch.int32 if dtype == "i8" else torch.float32
+    try:
+        for K in (256, 4160):
+            A = inputs.operand(KIND[dtype], M, K, 83 + K)
+            B = inputs.operand(KIND[dtype], K, N, 84 + K)
+            Ad, Bd = _to_device(A), _to_device(B)
+            ref = None
+            for policy in (tl.C_STORES_AUTO, tl.C_STORES_STREAM, tl.C_STORES_PLAIN):
+                tl.set_c_store_policy(policy)
+                for ldc, off in [(N, 0), (N + 1, 0), (N, 1)]:
+                    buf = torch.full((off + M * ldc + 64,), -7, dtype=out_dtype, device="cuda")
+                    C = buf.as_strided((M, N), (ldc, 1), off)
+                    tl.gemm(Ad, Bd, out=C, variant=v)
+                    torch.cuda.synchronize()
+                    got = C.cpu().clone()
+                    mask = torch.ones(buf.numel(), dtype=torch.bool)
+                    mask.as_strided((M, N), (ldc, 1), off).fill_(False)
+                    assert (buf.cpu()[mask] == -7).all(), (K, policy, ldc, off)
+                    if ref is None:
+                        ref = got
+                        _assert_parity(got, A, B, dtype)
+                    assert torch.equal(got, ref), (K, policy, ldc, off)
+    finally:
+        tl.set_c_store_policy(tl.C_STORES_AUTO)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "i8"])
 def test_thin_kernel(dtype):
     # N <= 16: the thin kernels (from 2 columns on the matrix cores, one
     # column on the vector ALUs), whatever the alignment; offset pointers

@@ -2,6 +2,7 @@
 // include/tgemm.h).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <climits>
 #include <cstdlib>
 #include <cstdarg>
@@ -344,6 +345,9 @@ void entry_to_variant(const KernelEntry& e, int32_t wg_group, tgemm_variant* v) 
     v->lane_map = e.lane_map;
 }
 
+// TGEMM_C_STORES_*: how the matrix-core kernels write C (tgemm_set_c_store_policy)
+std::atomic<int> g_c_store_policy{TGEMM_C_STORES_AUTO};
+
 // Per-device gfx950 check, cached.
 std::mutex g_arch_mu;
 int g_arch_ok[64];  // 0 unknown, 1 gfx950, -1 other
@@ -388,6 +392,14 @@ extern "C" {
 const char* tgemm_version(void) { return "tgemm 0.1 (gfx950)"; }
 
 const char* tgemm_last_error(void) { return g_err.c_str(); }
+
+int tgemm_set_c_store_policy(int policy) {
+    if (policy != TGEMM_C_STORES_AUTO && policy != TGEMM_C_STORES_STREAM && policy != TGEMM_C_STORES_PLAIN) {
+        set_err("unknown C store policy %d", policy);
+        return TGEMM_E_ARG;
+    }
+    return g_c_store_policy.exchange(policy);
+}
 
 }  // extern "C"
 
@@ -709,7 +721,11 @@ int run_impl(const tgemm_plan* p, const void* A, const void* B, void* C, uint64_
     // and keep streaming (bf16 4096^2 x 256 on 128 x 128 tiles: 20.6 us
     // streaming, 22.1 plain).
     const bool big_tile = e->bm * e->bn >= 256 * 256;
-    g.c_stream = (uintptr_t)C % 128 == 0 && (p->ldc * 4) % 128 == 0 && (!big_tile || p->K * esz >= 4096);
+    const bool lines = (uintptr_t)C % 128 == 0 && (p->ldc * 4) % 128 == 0;
+    const int policy = g_c_store_policy.load(std::memory_order_relaxed);
+    g.c_stream = policy == TGEMM_C_STORES_PLAIN ? 0
+                 : policy == TGEMM_C_STORES_STREAM ? lines
+                 : lines && (!big_tile || p->K * esz >= 4096);
     if (clocks && e->family == tg::FAM_TILED) {
         // the kernel that runs decides the count (a fallback's tile may differ)
         const int64_t need = tg::CLOCK_VALUES * (int64_t)g.tiles_m * g.tiles_n;

@@ -31,6 +31,7 @@ ACCESS_WIDE, ACCESS_NARROW = 1, 2
 FRAG_REUSE, FRAG_PER_MMA, FRAG_SLICE = 1, 2, 3
 STORE_VECTOR, STORE_SCALAR = 1, 2
 COPY_BURST, COPY_SPREAD, COPY_LATE = 1, 2, 3
+C_STORES_AUTO, C_STORES_STREAM, C_STORES_PLAIN = 0, 1, 2
 READ_B32, READ_B64, READ_B128, READ_TR, READ_KVEC = 1, 2, 3, 4, 5
 LANES_BLOCKS, LANES_QUARTERS, LANES_ZORDER, LANES_ZQUARTERS = 1, 2, 3, 4
 ORDER_ROW_MAJOR = -1
@@ -63,7 +64,8 @@ class PlanInfo(ctypes.Structure):
 EXPORTS = ("gemm_plan", "gemm_plan_variant", "gemm_run", "gemm_destroy", "tgemm_last_error",
            "gemm_plan_get_info", "gemm_variant_count", "gemm_variant_get", "tgemm_version",
            "tgemm_lds_read_probe", "tgemm_mfma_rate_probe", "gemm_workspace_bytes", "gemm_run_ws",
-           "gemm_kernel_occupancy", "gemm_clock_slots", "gemm_run_clocked", "gemm_run_noalloc")
+           "gemm_kernel_occupancy", "gemm_clock_slots", "gemm_run_clocked", "gemm_run_noalloc",
+           "tgemm_set_c_store_policy")
 
 
 def _load():
@@ -110,6 +112,8 @@ def _load():
     lib.gemm_run_noalloc.restype = ctypes.c_int
     lib.tgemm_mfma_rate_probe.argtypes = [i32, i32, i32, vp, vp, vp, vp]
     lib.tgemm_mfma_rate_probe.restype = ctypes.c_int
+    lib.tgemm_set_c_store_policy.argtypes = [i32]
+    lib.tgemm_set_c_store_policy.restype = ctypes.c_int
     return lib
 
 
@@ -124,6 +128,15 @@ class TgemmError(RuntimeError):
 
 def last_error() -> str:
     return _lib.tgemm_last_error().decode()
+
+
+def set_c_store_policy(policy: int) -> int:
+    """tgemm_set_c_store_policy: C_STORES_AUTO / _STREAM / _PLAIN for every
+    later run in this process; returns the previous policy."""
+    rc = _lib.tgemm_set_c_store_policy(int(policy))
+    if rc < 0:
+        raise TgemmError(rc, last_error())
+    return rc
 
 
 def version() -> str:
