@@ -420,8 +420,11 @@ def test_ladders_select_distinct_kernels():
 
 def test_c_store_policy_setter():
     # process-wide; returns the previous policy, rejects unknown ones
-    assert tl.set_c_store_policy(tl.C_STORES_PLAIN) == tl.C_STORES_AUTO
-    assert tl.set_c_store_policy(tl.C_STORES_STREAM) == tl.C_STORES_PLAIN
-    with pytest.raises(tl.TgemmError):
-        tl.set_c_store_policy(7)
-    assert tl.set_c_store_policy(tl.C_STORES_AUTO) == tl.C_STORES_STREAM
+    try:
+        assert tl.set_c_store_policy(tl.C_STORES_PLAIN) == tl.C_STORES_AUTO
+        assert tl.set_c_store_policy(tl.C_STORES_STREAM) == tl.C_STORES_PLAIN
+        with pytest.raises(tl.TgemmError):
+            tl.set_c_store_policy(7)
+        assert tl.set_c_store_policy(tl.C_STORES_AUTO) == tl.C_STORES_STREAM
+    finally:
+        tl.set_c_store_policy(tl.C_STORES_AUTO)
