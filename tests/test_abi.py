@@ -159,7 +159,7 @@ def test_default_choice_by_shape():
     # 128 x 128 tiles filling a quarter of the CUs or fewer: 64 x 64
     for dtype in (tl.BF16, tl.I8):
         q = tl.Plan(1024, 1024, 4096, dtype).info()
-        assert (q.variant.tile_m, q.variant.tile_n, q.variant.stages, q.grid) == (64, 64, 8, 256), dtype
+        assert (q.variant.tile_m, q.variant.tile_n, q.variant.stages, q.grid) == (64, 64, 4, 256), dtype
     # one round of 256 x 256 tiles from K = 512 (int8: 1024); several rounds
     # at short K stay on 128 x 128
     for M, K, dt, edge in [(4096, 512, tl.BF16, 256), (4096, 256, tl.BF16, 128), (3072, 512, tl.BF16, 256),
@@ -174,17 +174,17 @@ def test_default_choice_by_shape():
     # int8 from K = 2048 only
     assert tl.Plan(512, 4096, 1024, tl.I8).info().variant.tile_m == 128
     assert tl.Plan(512, 4096, 1024, tl.BF16).info().variant.tile_m == 64
-    # long K on the 128 x 128 tile: the deeper ring; on the 64 x 64 tile the
-    # 8-slot ring (from K = 1024 bf16, 2048 int8) and whole-slice fragment
-    # read-ahead at every K
+    # long K on the 128 x 128 tile: the deeper ring; on the 64 x 64 tile
+    # 128-deep (int8 256) slices in 4 slots from K = 1024 bf16, 2048 int8, and
+    # whole-slice fragment read-ahead at every K
     assert tl.Plan(2048, 2048, 4096, tl.BF16).info().variant.stages == 4
-    for dtype in (tl.BF16, tl.I8):
+    for dtype, bk in ((tl.BF16, 128), (tl.I8, 256)):
         small = tl.Plan(512, 512, 4096, dtype).info().variant
-        assert (small.tile_m, small.stages, small.frag) == (64, 8, tl.FRAG_SLICE), dtype
+        assert (small.tile_m, small.tile_k, small.stages, small.frag) == (64, bk, 4, tl.FRAG_SLICE), dtype
         assert tl.Plan(512, 512, 512, dtype).info().variant.stages == 3
         assert tl.Plan(512, 512, 512, dtype).info().variant.frag == tl.FRAG_SLICE
-    assert tl.Plan(512, 512, 1024, tl.BF16).info().variant.stages == 8
-    assert tl.Plan(512, 512, 1024, tl.I8).info().variant.stages == 3
+    assert (tl.Plan(512, 512, 1024, tl.BF16).info().variant.tile_k, tl.Plan(512, 512, 1024, tl.BF16).info().variant.stages) == (128, 4)
+    assert (tl.Plan(512, 512, 1024, tl.I8).info().variant.tile_k, tl.Plan(512, 512, 1024, tl.I8).info().variant.stages) == (128, 3)
     # the larger tiles keep reading one K step ahead
     assert tl.Plan(2048, 2048, 4096, tl.BF16).info().variant.frag == tl.FRAG_REUSE
     small = tl.Plan(512, 512, 512, tl.BF16).info()

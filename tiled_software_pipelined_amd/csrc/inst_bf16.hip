@@ -54,6 +54,8 @@ void register_bf16(void (*add)(const KernelEntry&)) {
     // matrix instructions per K step (small grids)
     add(mfma_entry<T, 64, 64, 64, 2, 2, 8, LD_DIRECT, LY_XOR, AC_WIDE, FR_SLICE, 4>(1));
     add(mfma_entry<T, 64, 64, 64, 2, 2, 3, LD_DIRECT, LY_XOR, AC_WIDE, FR_SLICE, 4>(1));
+    add(mfma_entry<T, 64, 64, 128, 2, 2, 4, LD_DIRECT, LY_XOR, AC_WIDE, FR_SLICE, 4>(1));
+    add(mfma_entry<T, 64, 64, 128, 2, 2, 3, LD_DIRECT, LY_XOR, AC_WIDE, FR_SLICE, 4>(1));
     add(mfma_entry<T, 128, 64, 32, 2, 2, 4, LD_DIRECT, LY_XOR, AC_WIDE, FR_SLICE, 2>(1));
     add(mfma_entry<T, 64, 128, 32, 2, 2, 4, LD_DIRECT, LY_XOR, AC_WIDE, FR_SLICE, 2>(1));
     add(mfma_entry<T, 128, 128, 32, 2, 2, 4, LD_DIRECT, LY_XOR, AC_WIDE, FR_SLICE, 2>(1));

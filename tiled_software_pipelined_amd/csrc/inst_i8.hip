@@ -38,6 +38,7 @@ void register_i8(void (*add)(const KernelEntry&)) {
     // matrix instructions per K step (small grids)
     add(mfma_entry<T, 64, 64, 128, 2, 2, 8, LD_DIRECT, LY_XOR, AC_WIDE, FR_SLICE, 4>(2));
     add(mfma_entry<T, 64, 64, 128, 2, 2, 3, LD_DIRECT, LY_XOR, AC_WIDE, FR_SLICE, 4>(2));
+    add(mfma_entry<T, 64, 64, 256, 2, 2, 4, LD_DIRECT, LY_XOR, AC_WIDE, FR_SLICE, 4>(2));
     add(mfma_entry<T, 128, 64, 64, 2, 2, 4, LD_DIRECT, LY_XOR, AC_WIDE, FR_SLICE, 2>(2));
     add(mfma_entry<T, 64, 128, 64, 2, 2, 4, LD_DIRECT, LY_XOR, AC_WIDE, FR_SLICE, 2>(2));
     add(mfma_entry<T, 128, 128, 64, 2, 2, 4, LD_DIRECT, LY_XOR, AC_WIDE, FR_SLICE, 2>(2));

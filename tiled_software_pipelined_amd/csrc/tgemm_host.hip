@@ -287,13 +287,20 @@ const KernelEntry* default_entry(int dtype, int64_t M, int64_t N, int64_t K, int
     // one slice ahead (graph replay, bf16, us, reads one step ahead -> one
     // slice ahead: 512^2 x 4096 19.0 -> 13.9, x 8192 33.3 -> 27.2, x 1024
     // 7.5 -> 6.6; 1024^2 x 4096 20.0 -> 17.8; 768^2 x 4096 18.6 -> 15.7; int8
-    // 512^2 x 4096 11.2 -> 8.9, x 8192 18.5 -> 13.5); an 8-slot ring from
-    // 1024 bf16 / 2048 int8 values of K (512^2 x 2048 bf16 8.8 vs 10.3 us
-    // with 3 slots, 1024^2 x 1024 6.9 vs 7.2; int8 512^2 x 1024 5.3 vs 5.1,
-    // x 4096 8.9 vs 10.2), 3 below (512^2 x 512 5.1 vs 5.3)
+    // 512^2 x 4096 11.2 -> 8.9, x 8192 18.5 -> 13.5).  From 1024 bf16 /
+    // 2048 int8 values of K, 128-deep (int8 256) slices in 4 slots: half the
+    // barriers per matrix instruction of 64-deep slices in 8 slots (the same
+    // 128 KiB ring; bf16 512^2 x 1024 6.2 vs 6.6 us, x 2048 8.6 vs 8.8, x
+    // 8192 25.5 vs 27.0, 768^2 x 4096 15.4 vs 15.9, 1024^2 x 4096 17.2 vs
+    // 18.1, 512^2 x 4096 13.5 vs 13.3; int8 512^2 x 2048 6.2 vs 6.6, x 4096
+    // 8.7 vs 9.0, 1024^2 x 4096 11.0 vs 11.7), 64-deep in 3 slots below
+    // (512^2 x 512 5.1 vs 5.3 us with 8)
     if (pick == 64) {
         v.frag = TGEMM_FRAG_SLICE;
-        if (K >= (i8 ? 2048 : 1024)) v.stages = 8;
+        if (K >= (i8 ? 2048 : 1024)) {
+            v.tile_k = i8 ? 256 : 128;
+            v.stages = 4;
+        }
     }
     v.loader = guarded ? TGEMM_LOADER_VGPR : TGEMM_LOADER_DIRECT;
     return find_entry(dtype, v);
